@@ -1,0 +1,387 @@
+"""Pins of the CPU oracle against facts fixed outside the oracle itself.
+
+Each test checks the oracle against a closed form, an invariant, a library
+routine, a brute-force evaluation or a hand-worked case, so that a plausible
+mistake (a dropped term, a wrong sign or index, a transposed operand, an
+off-by-one window or pool) fails at least one of them.
+"""
+
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import scipy.special
+
+import oracle
+from workloads import WORKLOADS, make_decode_inputs
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+
+
+def _closed_form(expr: str) -> float:
+    return float(eval(expr, {"__builtins__": {}}, {"e": math.e}))
+
+
+def _hand_cases():
+    with open(os.path.join(HERE, "golden", "hand_cases.json")) as f:
+        return json.load(f)["cases"]
+
+
+def _hand_inputs(case):
+    keys = np.asarray(case["keys"], dtype=np.float64)
+    n = keys.size
+    q = np.asarray(case["q"], dtype=np.float64)[None, :, :, None]   # [1][n_q][H][1]
+    k = keys[None, :, None]
+    v = (10.0 * np.arange(1, n + 1))[None, :, None]
+    return q, k, v, np.array([n])
+
+
+@pytest.mark.parametrize("case", _hand_cases(), ids=lambda c: c["name"])
+def test_hand_worked_cases(case):
+    q, k, v, ctx = _hand_inputs(case)
+    n_q, tile_q = case["n_q"], case["tile_q"]
+    kt, win = case["k_top"], case["window"]
+    scores, _, _ = oracle.full_attn_scores(q, k, ctx, tile_q=tile_q, sm_scale=1.0)
+    if "importance" in case:
+        want = np.array([_closed_form(x) for x in case["importance"]])
+        np.testing.assert_allclose(scores[0, 0], want, rtol=1e-6)
+    p0 = oracle.query_positions(ctx[0], n_q)[0]
+    assert oracle.pool_end(p0, win) == case["pool_end"]
+    top_idx, top_cnt = oracle.select_topk_window(
+        scores, ctx, n_q=n_q, tile_q=tile_q, k_top=kt, window=win)
+    for t, want_top in enumerate(case["top"]):
+        assert top_cnt[0, t] == len(want_top)
+        assert list(top_idx[0, t, : top_cnt[0, t]]) == want_top
+        assert np.all(top_idx[0, t, top_cnt[0, t]:] == -1)
+    pos = oracle.query_positions(ctx[0], n_q)
+    for i, want_sel in enumerate(case["selection"]):
+        t = i // tile_q
+        sel = oracle.selection_set(top_idx[0, t], top_cnt[0, t], pos[i], win)
+        assert list(sel) == want_sel
+    o, _ = oracle.sparse_attention(q, k, v, ctx, top_idx, top_cnt,
+                                   tile_q=tile_q, window=win, sm_scale=1.0)
+    for i, expr in enumerate(case.get("o", [])):
+        assert o[0, i, 0, 0] == pytest.approx(_closed_form(expr), rel=1e-12)
+    if "o_dense" in case:
+        od, _ = oracle.dense_attention(q, k, v, ctx, sm_scale=1.0)
+        assert od[0, 0, 0, 0] == pytest.approx(_closed_form(case["o_dense"][0]), rel=1e-12)
+
+
+def _rand(rng, *shape, scale=1.0):
+    return rng.standard_normal(shape) * scale
+
+
+def test_importance_sums_to_heads_decode():
+    # Each head's probabilities sum to one, so the summed importance is H.
+    rng = np.random.default_rng(1)
+    q, k = _rand(rng, 3, 1, 5, 16), _rand(rng, 3, 300, 16)
+    ctx = np.array([300, 17, 1])
+    s, _, _ = oracle.full_attn_scores(q, k, ctx, tile_q=1, sm_scale=0.25)
+    for b in range(3):
+        assert s[b, 0, : ctx[b]].astype(np.float64).sum() == pytest.approx(5.0, rel=1e-6)
+        assert np.all(s[b, 0, ctx[b]:] == 0)
+        assert np.all(s[b, 0, : ctx[b]] >= 0) and np.all(s[b, 0] <= 5.0)
+
+
+def test_importance_sums_to_tile_heads_prefill():
+    rng = np.random.default_rng(2)
+    n_q, tile_q, heads = 8, 4, 3
+    q, k = _rand(rng, 1, n_q, heads, 8), _rand(rng, 1, 40, 8)
+    s, _, _ = oracle.full_attn_scores(q, k, np.array([40]), tile_q=tile_q, sm_scale=0.5)
+    for t in range(n_q // tile_q):
+        assert s[0, t].astype(np.float64).sum() == pytest.approx(tile_q * heads, rel=1e-6)
+        # causal: the tile's last query sits at 40 - 8 + 4t + 3; nothing later is seen
+        last = 40 - n_q + t * tile_q + tile_q - 1
+        assert np.all(s[0, t, last + 1:] == 0)
+
+
+def test_identical_keys_give_uniform_importance():
+    # Closed form: equal logits give p = 1/N per head, so I = H/N exactly.
+    rng = np.random.default_rng(3)
+    k = np.tile(rng.standard_normal(128), (4096, 1))[None]
+    q = rng.standard_normal((1, 1, 32, 128))
+    s, _, _ = oracle.full_attn_scores(q, k, np.array([4096]), tile_q=1, sm_scale=1 / math.sqrt(128))
+    assert np.all(s[0, 0] == np.float32(32 / 4096))
+    top, cnt = oracle.select_topk_window(s, [4096], n_q=1, tile_q=1, k_top=1024, window=128)
+    assert cnt[0, 0] == 1024 and np.array_equal(top[0, 0], np.arange(1024))
+
+
+def test_single_head_is_textbook_softmax():
+    # Library routine: scipy's softmax of the scaled logits.
+    rng = np.random.default_rng(4)
+    q, k = rng.standard_normal((1, 1, 1, 32)), rng.standard_normal((1, 700, 32))
+    s, _, lse = oracle.full_attn_scores(q, k, np.array([700]), tile_q=1, sm_scale=0.3)
+    logits = 0.3 * (k[0] @ q[0, 0, 0])
+    np.testing.assert_allclose(s[0, 0], scipy.special.softmax(logits), rtol=2e-7)
+    assert lse[0, 0, 0] == pytest.approx(scipy.special.logsumexp(logits), rel=1e-13)
+
+
+def _brute_force(q, k, v, ctx, n_q, tile_q, k_top, window, scale):
+    """Element-by-element evaluation with Python floats and math.exp."""
+    bsz, _, heads, dim = q.shape
+    out_scores, out_top, out_o = {}, {}, {}
+    for b in range(bsz):
+        n = int(ctx[b])
+        pos = [n - n_q + i for i in range(n_q)]
+        for t in range(n_q // tile_q):
+            imp = [0.0] * n
+            for i in range(t * tile_q, (t + 1) * tile_q):
+                if pos[i] < 0:
+                    continue
+                for h in range(heads):
+                    lg = [scale * sum(float(q[b, i, h, d]) * float(k[b, j, d]) for d in range(dim))
+                          for j in range(pos[i] + 1)]
+                    mx = max(lg)
+                    z = sum(math.exp(x - mx) for x in lg)
+                    for j in range(pos[i] + 1):
+                        imp[j] += math.exp(lg[j] - mx) / z
+            imp32 = [float(np.float32(x)) for x in imp]
+            out_scores[b, t] = imp32
+            pe = max(0, pos[t * tile_q] - window + 1)
+            ranked = sorted(range(pe), key=lambda j: (-imp32[j], j))
+            out_top[b, t] = sorted(ranked[:k_top])
+            for i in range(t * tile_q, (t + 1) * tile_q):
+                if pos[i] < 0:
+                    out_o[b, i] = [[0.0] * dim for _ in range(heads)]
+                    continue
+                sel = out_top[b, t] + list(range(max(0, pos[i] - window + 1), pos[i] + 1))
+                rows = []
+                for h in range(heads):
+                    lg = [scale * sum(float(q[b, i, h, d]) * float(k[b, j, d]) for d in range(dim))
+                          for j in sel]
+                    mx = max(lg)
+                    w = [math.exp(x - mx) for x in lg]
+                    z = sum(w)
+                    rows.append([sum(w[a] * float(v[b, j, d]) for a, j in enumerate(sel)) / z
+                                 for d in range(dim)])
+                out_o[b, i] = rows
+    return out_scores, out_top, out_o
+
+
+@pytest.mark.parametrize("n_q,tile_q", [(1, 1), (4, 2), (6, 3)])
+def test_brute_force_tiny(n_q, tile_q):
+    rng = np.random.default_rng(5 + n_q)
+    bsz, heads, dim, cap = 2, 3, 4, 23
+    q = rng.standard_normal((bsz, n_q, heads, dim))
+    k = rng.standard_normal((bsz, cap, dim))
+    v = rng.standard_normal((bsz, cap, dim))
+    ctx = np.array([23, 11])
+    k_top, window, scale = 5, 3, 0.7
+    s, _, _ = oracle.full_attn_scores(q, k, ctx, tile_q=tile_q, sm_scale=scale)
+    top, cnt = oracle.select_topk_window(s, ctx, n_q=n_q, tile_q=tile_q, k_top=k_top, window=window)
+    o, _ = oracle.sparse_attention(q, k, v, ctx, top, cnt, tile_q=tile_q, window=window, sm_scale=scale)
+    bs, bt, bo = _brute_force(q, k, v, ctx, n_q, tile_q, k_top, window, scale)
+    for (b, t), imp in bs.items():
+        np.testing.assert_array_equal(s[b, t, : ctx[b]], np.asarray(imp, dtype=np.float32))
+        assert list(top[b, t, : cnt[b, t]]) == bt[b, t]
+    for (b, i), rows in bo.items():
+        np.testing.assert_allclose(o[b, i], np.asarray(rows), rtol=1e-12, atol=1e-13)
+
+
+def test_selection_equals_stable_argsort_and_invariants():
+    # Library routine: a stable argsort of -I gives the (I desc, index asc) order.
+    rng = np.random.default_rng(6)
+    w = WORKLOADS["decode_bf16_64k_b16"].replace(batch=3)
+    inp = make_decode_inputs(w, ctx_lens=[5000, 1200, 1100], capacity=5000)
+    s, _, _ = oracle.full_attn_scores(inp["q"], inp["k"], inp["ctx_len"], tile_q=1,
+                                      sm_scale=w.sm_scale)
+    # Quantise some scores so that many exact ties exist.
+    s = (np.round(s * 2e4) / 2e4).astype(np.float32)
+    top, cnt = oracle.select_topk_window(s, inp["ctx_len"], n_q=1, tile_q=1,
+                                         k_top=1024, window=128)
+    for b, n in enumerate(inp["ctx_len"]):
+        pe = n - 128
+        order = np.argsort(-s[b, 0, :pe], kind="stable")
+        want = np.sort(order[: min(1024, pe)])
+        got = top[b, 0, : cnt[b, 0]]
+        assert np.array_equal(got, want)
+        sel = oracle.selection_set(top[b, 0], cnt[b, 0], n - 1, 128)
+        assert sel.size == min(n, 1152)                       # |S| = min(N, K + W)
+        assert np.all(np.diff(sel) > 0)                       # ascending, disjoint
+        assert set(range(n - 128, n)) <= set(sel.tolist())    # window always present
+        assert got.size == 0 or got.max() < pe                # T inside the pool
+    del rng
+
+
+@pytest.mark.parametrize("name", ["decode_f32_4k", "decode_bf16_64k_b16"])
+def test_planted_needles_are_selected(name):
+    w = WORKLOADS[name]
+    n = 4096 if name == "decode_f32_4k" else 8192
+    w = w.replace(batch=2, ctx_len=n)
+    inp = make_decode_inputs(w)
+    s, _, _ = oracle.full_attn_scores(inp["q"], inp["k"], inp["ctx_len"], tile_q=1,
+                                      sm_scale=w.sm_scale)
+    top, cnt = oracle.select_topk_window(s, inp["ctx_len"], n_q=1, tile_q=1,
+                                         k_top=w.k_top, window=w.window)
+    for b in range(2):
+        assert set(inp["planted"][b].tolist()) <= set(top[b, 0, : cnt[b, 0]].tolist())
+
+
+def test_clustered_keys_are_selected():
+    w = WORKLOADS["decode_bf16_256k_b4"].replace(batch=1, ctx_len=65536)
+    inp = make_decode_inputs(w)
+    assert inp["planted"][0].size == 262
+    s, _, _ = oracle.full_attn_scores(inp["q"], inp["k"], inp["ctx_len"], tile_q=1,
+                                      sm_scale=w.sm_scale)
+    top, cnt = oracle.select_topk_window(s, inp["ctx_len"], n_q=1, tile_q=1,
+                                         k_top=1024, window=128)
+    assert set(inp["planted"][0].tolist()) <= set(top[0, 0, : cnt[0, 0]].tolist())
+
+
+def test_budget_covering_pool_gives_dense_attention():
+    # k_top >= |pool| means every key is attended: the textbook softmax.
+    rng = np.random.default_rng(7)
+    q, k, v = rng.standard_normal((2, 1, 4, 8)), rng.standard_normal((2, 50, 8)), rng.standard_normal((2, 50, 8))
+    ctx = np.array([50, 30])
+    s, _, _ = oracle.full_attn_scores(q, k, ctx, tile_q=1, sm_scale=0.4)
+    top, cnt = oracle.select_topk_window(s, ctx, n_q=1, tile_q=1, k_top=64, window=5)
+    o, lse = oracle.sparse_attention(q, k, v, ctx, top, cnt, tile_q=1, window=5, sm_scale=0.4)
+    for b in range(2):
+        n = ctx[b]
+        lg = 0.4 * np.einsum("hd,jd->hj", q[b, 0], k[b, :n])
+        want = scipy.special.softmax(lg, axis=1) @ v[b, :n]
+        np.testing.assert_allclose(o[b, 0], want, rtol=1e-12, atol=1e-14)
+        np.testing.assert_allclose(lse[b, 0], scipy.special.logsumexp(lg, axis=1), rtol=1e-13)
+    od, _ = oracle.dense_attention(q, k, v, ctx, sm_scale=0.4)
+    np.testing.assert_allclose(o, od, rtol=1e-12, atol=1e-14)
+
+
+def test_single_selected_key_returns_its_value():
+    # |S| = 1: the output is exactly that key's value row.
+    rng = np.random.default_rng(8)
+    q, k, v = rng.standard_normal((1, 1, 3, 8)), rng.standard_normal((1, 10, 8)), rng.standard_normal((1, 10, 8))
+    ctx = np.array([10])
+    s, _, _ = oracle.full_attn_scores(q, k, ctx, tile_q=1, sm_scale=1.0)
+    top, cnt = oracle.select_topk_window(s, ctx, n_q=1, tile_q=1, k_top=1, window=0)
+    assert cnt[0, 0] == 1
+    j = int(top[0, 0, 0])
+    assert j == int(np.lexsort((np.arange(10), -s[0, 0]))[0])
+    o, _ = oracle.sparse_attention(q, k, v, ctx, top, cnt, tile_q=1, window=0, sm_scale=1.0)
+    for h in range(3):
+        assert np.array_equal(o[0, 0, h], v[0, j])
+    o1, _ = oracle.sparse_attention(q, k, v, np.array([1]), np.full((1, 1, 1), -1), np.zeros((1, 1), int),
+                                    tile_q=1, window=4, sm_scale=1.0)
+    assert np.array_equal(o1[0, 0, 0], v[0, 0])
+
+
+def test_equal_logits_average_selected_values():
+    rng = np.random.default_rng(9)
+    k = np.zeros((1, 40, 8))
+    q, v = rng.standard_normal((1, 1, 2, 8)), rng.standard_normal((1, 40, 8))
+    ctx = np.array([40])
+    s, _, _ = oracle.full_attn_scores(q, k, ctx, tile_q=1, sm_scale=1.0)
+    top, cnt = oracle.select_topk_window(s, ctx, n_q=1, tile_q=1, k_top=6, window=4)
+    o, _ = oracle.sparse_attention(q, k, v, ctx, top, cnt, tile_q=1, window=4, sm_scale=1.0)
+    sel = list(range(6)) + list(range(36, 40))
+    np.testing.assert_allclose(o[0, 0, 0], v[0, sel].mean(axis=0), rtol=1e-13, atol=1e-15)
+
+
+def test_one_query_tiles_reduce_to_decode():
+    # A prefill group of one query is a decode step at that query's position.
+    rng = np.random.default_rng(10)
+    n_q, heads, dim, n = 5, 3, 8, 60
+    q, k, v = rng.standard_normal((1, n_q, heads, dim)), rng.standard_normal((1, n, dim)), rng.standard_normal((1, n, dim))
+    s, of, lse = oracle.full_attn_scores(q, k, np.array([n]), tile_q=1, sm_scale=0.5, v=v)
+    top, cnt = oracle.select_topk_window(s, [n], n_q=n_q, tile_q=1, k_top=7, window=4)
+    o, _ = oracle.sparse_attention(q, k, v, [n], top, cnt, tile_q=1, window=4, sm_scale=0.5)
+    for i in range(n_q):
+        ni = n - n_q + i + 1
+        sd, ofd, lsed = oracle.full_attn_scores(q[:, i:i + 1], k, np.array([ni]), tile_q=1, sm_scale=0.5, v=v)
+        np.testing.assert_array_equal(sd[0, 0, :ni], s[0, i, :ni])
+        np.testing.assert_allclose(ofd[0, 0], of[0, i], rtol=1e-13)
+        td, cd = oracle.select_topk_window(sd, [ni], n_q=1, tile_q=1, k_top=7, window=4)
+        assert np.array_equal(td[0, 0], top[0, i])
+        od, _ = oracle.sparse_attention(q[:, i:i + 1], k, v, [ni], td, cd, tile_q=1, window=4, sm_scale=0.5)
+        np.testing.assert_allclose(od[0, 0], o[0, i], rtol=1e-13)
+
+
+def test_prefill_group_pool_and_selection_sizes():
+    # |S_i| = min(K, pool) + min(W, P_i + 1) for every query of a group.
+    rng = np.random.default_rng(11)
+    n_q, tile_q, n = 16, 8, 300
+    q, k = rng.standard_normal((1, n_q, 2, 8)), rng.standard_normal((1, n, 8))
+    s, _, _ = oracle.full_attn_scores(q, k, np.array([n]), tile_q=tile_q, sm_scale=0.5)
+    top, cnt = oracle.select_topk_window(s, [n], n_q=n_q, tile_q=tile_q, k_top=100, window=32)
+    pos = oracle.query_positions(n, n_q)
+    for i in range(n_q):
+        t = i // tile_q
+        pe = pos[t * tile_q] - 32 + 1
+        sel = oracle.selection_set(top[0, t], cnt[0, t], pos[i], 32)
+        assert sel.size == min(100, pe) + min(32, pos[i] + 1)
+        assert np.all(np.diff(sel) > 0) and top[0, t, : cnt[0, t]].max() < pe
+
+
+def test_queries_before_the_cache_start_are_empty():
+    q = np.ones((1, 4, 1, 2))
+    k = np.ones((1, 8, 2))
+    v = np.arange(16.0).reshape(1, 8, 2)
+    s, _, lse = oracle.full_attn_scores(q, k, np.array([2]), tile_q=2, sm_scale=1.0)
+    # ctx 2, n_q 4: positions -2, -1, 0, 1; group 0 is empty, group 1 sees keys 0..1
+    assert np.all(s[0, 0] == 0) and np.isneginf(lse[0, :2]).all()
+    assert s[0, 1, :2].sum() == pytest.approx(2.0)
+    top, cnt = oracle.select_topk_window(s, [2], n_q=4, tile_q=2, k_top=3, window=1)
+    o, _ = oracle.sparse_attention(q, k, v, [2], top, cnt, tile_q=2, window=1, sm_scale=1.0)
+    assert np.all(o[0, :2] == 0)
+    assert np.array_equal(o[0, 2, 0], v[0, 0]) and np.array_equal(o[0, 3, 0], v[0, 1])
+
+
+def test_bf16_round_matches_torch_on_fp32_values():
+    # Library routine: torch's fp32 -> bfloat16 conversion rounds to nearest even.
+    torch = pytest.importorskip("torch")
+    rng = np.random.default_rng(12)
+    x = np.concatenate([rng.standard_normal(100000).astype(np.float32) * np.float32(10.0) ** rng.integers(-30, 30, 100000),
+                        np.float32([0.0, -0.0, 1e-40, -3e-39, 3.3e38, -3.4e38])]).astype(np.float32)
+    want = torch.from_numpy(x).to(torch.bfloat16).to(torch.float64).numpy()
+    got = oracle.bf16_round(x.astype(np.float64))
+    np.testing.assert_array_equal(got, want)
+
+
+def test_bf16_round_ties_and_single_rounding():
+    u = 2.0 ** -8                                   # half an ulp of bfloat16 at 1.0
+    assert oracle.bf16_round(1 + u) == 1.0                      # tie -> even
+    assert oracle.bf16_round(1 + 3 * u) == 1 + 4 * u            # tie -> even (up)
+    assert oracle.bf16_round(1 + u + 2.0 ** -30) == 1 + 2 * u   # above the tie: up,
+    # which a detour through fp32 would miss (fp32 drops the 2**-30 first).
+    assert oracle.bf16_round(-(1 + u + 2.0 ** -30)) == -(1 + 2 * u)
+    assert np.isinf(oracle.bf16_round(3.4e38))
+
+
+def test_generator_bf16_bits_match_torch():
+    torch = pytest.importorskip("torch")
+    from workloads import bf16_bits, bf16_bits_to_f32
+    rng = np.random.default_rng(13)
+    x = (rng.standard_normal(50000) * 100).astype(np.float32)
+    bits = bf16_bits(x)
+    want = torch.from_numpy(x).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    np.testing.assert_array_equal(bits, want)
+    np.testing.assert_array_equal(bf16_bits_to_f32(bits),
+                                  torch.from_numpy(x).to(torch.bfloat16).float().numpy())
+
+
+def test_bridge_is_exact_integer_product():
+    # Small integers: every product and sum is exact and representable in
+    # bfloat16, so K and V must equal the integer matrix product.
+    rng = np.random.default_rng(14)
+    h = rng.integers(-3, 4, size=(37, 24))
+    wk = rng.integers(-2, 3, size=(24, 5))
+    wv = rng.integers(-2, 3, size=(24, 5))
+    k, v = oracle.bridge_kv(h.astype(float), wk.astype(float), wv.astype(float), row_chunk=8)
+    want_k = [[sum(int(h[r, c]) * int(wk[c, d]) for c in range(24)) for d in range(5)] for r in range(37)]
+    want_v = [[sum(int(h[r, c]) * int(wv[c, d]) for c in range(24)) for d in range(5)] for r in range(37)]
+    assert np.array_equal(k, np.asarray(want_k, dtype=float))
+    assert np.array_equal(v, np.asarray(want_v, dtype=float))
+
+
+def test_bridge_rounds_the_fp64_product_once():
+    rng = np.random.default_rng(15)
+    h = rng.standard_normal((100, 64))
+    wk, wv = rng.standard_normal((64, 16)), rng.standard_normal((64, 16))
+    k, v = oracle.bridge_kv(h, wk, wv, row_chunk=33)
+    exact_k = h @ wk
+    # within half a bfloat16 ulp of the exact product, and on the bfloat16 grid
+    ulp = 2.0 ** (np.floor(np.log2(np.abs(exact_k))) - 7)
+    assert np.all(np.abs(k - exact_k) <= ulp / 2)
+    assert np.array_equal(oracle.bf16_round(k), k)
+    assert v.shape == (100, 16)
