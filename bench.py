@@ -1,0 +1,211 @@
+"""Decode-step benchmark of the HySparse2 KV Reuse hot path on one MI355X.
+
+One step = one decode step of every sequence of the batch through the whole
+hot path: full-layer scoring (hs2_full_attn_scores), top-1024 + window-128
+selection (hs2_select_topk_window) and the sparse layer
+(hs2_sparse_attn_gather), on the 256k-context workload: batch 4, 32 query
+heads sharing one bf16 K/V head of dim 128, 262,144 cached keys per sequence,
+keys drawn as N(0,1) background plus 0.1% clustered high-similarity keys.
+Inputs are synthetic, seeded and resident in HBM before timing starts.
+
+Prints one JSON line.  value = decoded tokens/s = batch * steps / time.
+Also reported: the step's algorithmic HBM GB/s (K read once, scores written
+and read once, 1,152 gathered K and V rows per sequence), a roofline entry
+for the dominant unit of work (the scoring call, timed with HIP events on
+its own stream), and the CPU oracle timed on a bounded sample.
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+WORKLOAD = "decode_bf16_256k_b4"
+MIB = 1 << 20
+
+
+def algorithmic_bytes(w) -> dict:
+    """Bytes a decode step must move at minimum (bf16 K/V rows of 256 B)."""
+    n, b = w.ctx_len, w.batch
+    row = w.head_dim * (2 if w.dtype == "bf16" else 4)
+    k_stream = b * n * row                      # every key read once
+    scores = b * n * 4                          # importance written once ...
+    pool = b * max(0, n - w.window) * 4         # ... and the pool read once by the selector
+    sel = min(n, w.k_top + w.window)
+    gather = b * sel * 2 * row                  # K and V rows of the selection
+    q_o = b * w.n_heads * w.head_dim * (2 + 4 + 2)
+    return dict(k_stream=k_stream, scores_write=scores, scores_read=pool, gather=gather,
+                q_out=q_o, step=k_stream + scores + pool + gather + q_o,
+                scoring_call=k_stream + scores)
+
+
+def cpu_baseline(w, inp, budget_s: float = 12.0) -> dict:
+    """The oracle as it stands, on whole sequences of the same workload."""
+    import numpy as np
+    from threadpoolctl import threadpool_info
+
+    import oracle
+
+    threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    done, t0 = 0, time.perf_counter()
+    while True:
+        b = done % w.batch
+        sl = slice(b, b + 1)
+        ctx = inp["ctx_len"][sl]
+        s, _, _ = oracle.full_attn_scores(inp["q"][sl], inp["k"][sl], ctx, tile_q=1,
+                                          sm_scale=w.sm_scale)
+        top, cnt = oracle.select_topk_window(s, ctx, n_q=1, tile_q=1, k_top=w.k_top,
+                                             window=w.window)
+        oracle.sparse_attention(inp["q"][sl], inp["k"][sl], inp["v"][sl], ctx, top, cnt,
+                                tile_q=1, window=w.window, sm_scale=w.sm_scale)
+        done += 1
+        if time.perf_counter() - t0 >= budget_s or done >= 4 * w.batch:
+            break
+    dt = time.perf_counter() - t0
+    del np
+    return {"value": done / dt, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{done} whole sequences ({w.ctx_len} keys, {w.n_heads} heads) of the same "
+                      f"workload, one decode step each, fp64 NumPy, {dt:.1f} s"}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--graph", type=int, default=1, help="replay the step as a HIP graph")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(decode shards by sequence with no exchange; see the design notes).",
+              file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+
+    import kv_cache_reuse_hs2_amd as hs2
+    from kv_cache_reuse_hs2_amd.torch_api import (make_buffers, run_scores, run_select,
+                                                  run_sparse, run_step)
+    from workloads import WORKLOADS, make_decode_inputs
+
+    hs2.load()
+    torch.cuda.set_device(0)
+    w = WORKLOADS[WORKLOAD]
+    t_gen = time.perf_counter()
+    inp = make_decode_inputs(w)
+    buf = make_buffers(inp, n_heads=w.n_heads, k_top=w.k_top, window=w.window,
+                       sm_scale=w.sm_scale, dtype=w.dtype)
+    print(f"[bench] inputs ready in {time.perf_counter() - t_gen:.1f} s", file=sys.stderr, flush=True)
+    stream = torch.cuda.current_stream()
+
+    # Per-call timing (eager): HIP events on the stream the kernels run on.
+    calls = {"scores": run_scores, "select": run_select, "sparse": run_sparse}
+    for _ in range(args.warmup):
+        run_step(buf)
+    torch.cuda.synchronize()
+    per_call = {k: [] for k in calls}
+    for _ in range(args.steps):
+        for name, fn in calls.items():
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            fn(buf)
+            e1.record(stream)
+            per_call[name].append((e0, e1))
+    torch.cuda.synchronize()
+    call_ms = {k: float(np.mean([a.elapsed_time(b) for a, b in v])) for k, v in per_call.items()}
+
+    # Whole-step timing: exactly `steps` steps between two synchronisations.
+    graph = None
+    if args.graph:
+        graph = torch.cuda.CUDAGraph()
+        side = torch.cuda.Stream()
+        side.wait_stream(stream)
+        with torch.cuda.stream(side):
+            run_step(buf)
+        stream.wait_stream(side)
+        torch.cuda.synchronize()
+        with torch.cuda.graph(graph):
+            run_step(buf)
+        torch.cuda.synchronize()
+
+    def step():
+        if graph is not None:
+            graph.replay()
+        else:
+            run_step(buf)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0e, t1e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t_wall = time.perf_counter()
+    t0e.record(stream)
+    for _ in range(args.steps):
+        step()
+    t1e.record(stream)
+    torch.cuda.synchronize()
+    wall_ms = (time.perf_counter() - t_wall) * 1e3
+    ms = t0e.elapsed_time(t1e) / args.steps
+
+    ab = algorithmic_bytes(w)
+    tokens_s = w.batch / (ms * 1e-3)
+    step_gbs = ab["step"] / (ms * 1e-3) / 1e9
+    score_gbs = ab["scoring_call"] / (call_ms["scores"] * 1e-3) / 1e9
+    out = {
+        "metric": "sparse-attn decode tokens/s + HBM GB/s (% of peak) at 256k ctx, 1 GPU",
+        "value": round(tokens_s, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": WORKLOAD,
+            "batch": w.batch,
+            "ctx_len": w.ctx_len,
+            "n_heads": w.n_heads,
+            "kv_heads": 1,
+            "head_dim": w.head_dim,
+            "k_top": w.k_top,
+            "window": w.window,
+            "graph": bool(args.graph),
+            "step_algorithmic_MiB": round(ab["step"] / MIB, 2),
+            "step_hbm_GBps": round(step_gbs, 1),
+            "step_hbm_frac": round(step_gbs / HBM_PEAK_GBS, 4),
+            "call_ms": {k: round(v, 5) for k, v in call_ms.items()},
+            "wall_ms_timed_region": round(wall_ms, 3),
+        },
+        "roofline": {
+            "kernel": "hs2_full_attn_scores (K stream: stats pass, reduce, importance pass)",
+            "bound": "hbm",
+            "achieved": round(score_gbs, 1),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(score_gbs / HBM_PEAK_GBS, 4),
+            "traffic": None,
+            "algorithmic_bytes_per_launch": ab["scoring_call"],
+        },
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(w, inp)
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

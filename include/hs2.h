@@ -1,0 +1,179 @@
+/*
+ * hs2.h -- C ABI of libhs2, the MI355X (gfx950) kernels of HySparse2's
+ * inner-level KV Reuse path: token-level sparse attention in which a
+ * full-attention MQA layer scores every cached key, a selector keeps the
+ * top-k keys plus a forced window of the most recent ones, and the sparse
+ * layers that follow attend only to that selection over the same K/V cache.
+ * The KV Bridging projection that builds such a cache from self-decoder
+ * hidden states is exported too.
+ *
+ * Sources: web pages about the preprint "HySparse2: Hybrid Sparse Attention
+ * with Two-Level KV Sharing" (arXiv 2609.26368):
+ *   [Summary] "HySparse2: Hybrid Sparse Attention with Two-Level KV Sharing"
+ *             (academy.dair.ai summary), bullets "KV Bridging", "KV Reuse
+ *             refinements", "Inference cost".
+ *   [Origins] "HySparse2: How Xiaomi Split the Transformer to Fix Agent
+ *             Prefill Costs" (originshq.com), sections "The Self-Decoder and
+ *             Cross-Decoder Split" (projection equations) and "KV Reuse and
+ *             Token-Level Sparse Selection".
+ *   [Wire]    "Xiaomi's HySparse2 targets lower computing demands for
+ *             long-context AI agents" (chinaaiwire.com), "How to interpret
+ *             the results" (MQA).
+ * The pages give the operations in prose only; the calls below are this
+ * library's own interface to them.
+ *
+ * Conventions shared by every call
+ * --------------------------------
+ * - Every tensor argument is a DEVICE pointer owned by the caller; the
+ *   library never allocates, frees or keeps a pointer after returning, and
+ *   never synchronises.  Work is enqueued asynchronously on `stream` (a
+ *   hipStream_t; NULL means the default stream).
+ * - Arguments are validated on the host before anything is enqueued: a call
+ *   that returns an error status has enqueued nothing and written nothing.
+ *   Asynchronous device faults surface at the caller's next synchronisation.
+ * - Every pointer must be 16-byte aligned (HS2_EALIGN otherwise).
+ * - Shapes: B = batch, Q = n_q new queries per sequence, H = query heads,
+ *   D = head_dim = 128, one shared K/V head (MQA, [Summary] "Inference
+ *   cost"; [Wire] "How to interpret the results").  Layouts are row-major:
+ *     q        [B][Q][H][D]      dtype of the descriptor
+ *     k, v     [B][cap][D]       dtype of the descriptor; sequence stride
+ *                                kv_stride ELEMENTS (>= cap*D), row stride D
+ *     ctx_len  int32 [B]         device array: keys held by each sequence,
+ *                                the new queries' own keys included;
+ *                                values are clamped to [0, cap] on device
+ *     scores   f32 [B][Q/tile_q][cap]
+ *     top_idx  int32 [B][Q/tile_q][k_top], top_cnt int32 [B][Q/tile_q]
+ *     o        f32 [B][Q][H][D],  lse f32 [B][Q][H] (natural log)
+ * - Query i of sequence b sits at position P = ctx_len[b] - Q + i; it sees
+ *   keys 0..P (causal).  Queries at negative positions output 0 / -inf.
+ * - Inputs must be finite.  bf16 values are raw bfloat16 bit patterns.
+ * - Calls are reentrant.  A workspace may be shared by calls issued in order
+ *   on one stream, never by calls that can run concurrently.
+ */
+#ifndef HS2_H_
+#define HS2_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#if defined(__GNUC__) || defined(__clang__)
+#define HS2_API __attribute__((visibility("default")))
+#else
+#define HS2_API
+#endif
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef void* hs2_stream_t; /* a hipStream_t */
+
+typedef enum {
+  HS2_OK = 0,
+  HS2_EINVAL = 1,       /* null pointer, bad size or inconsistent shape */
+  HS2_EUNSUPPORTED = 2, /* valid, but outside what the kernels implement */
+  HS2_EALIGN = 3,       /* a pointer is not 16-byte aligned */
+  HS2_EWORKSPACE = 4,   /* workspace smaller than hs2_workspace_size() */
+  HS2_EHIP = 5          /* the HIP runtime reported an error at enqueue */
+} hs2_status;
+
+typedef enum { HS2_F32 = 0, HS2_BF16 = 1 } hs2_dtype;
+
+/* Attention problem shared by the scoring, selection and sparse calls. */
+typedef struct {
+  int batch;      /* B >= 1 */
+  int n_q;        /* new queries per sequence: 1 (decode) or a multiple of tile_q */
+  int n_heads;    /* query heads, 1..32, all sharing one K/V head (MQA) */
+  int head_dim;   /* must be 128 */
+  int tile_q;     /* queries per selection group: 1 (decode) or 64 (prefill) */
+  int k_top;      /* selected keys per group, 0..2048 (1024 in HySparse2) */
+  int window;     /* forced recent-token window, 0..2048 (128 in HySparse2) */
+  int causal;     /* must be 1 */
+  float sm_scale; /* softmax scale, normally 1/sqrt(head_dim) */
+  hs2_dtype dtype;/* storage type of q, k and v */
+} hs2_attn_desc;
+
+/* Bytes of device workspace the three attention calls need for this problem
+ * and cache capacity (one workspace serves all three when they are issued in
+ * order on one stream).  Returns 0 when the descriptor is invalid. */
+HS2_API size_t hs2_workspace_size(const hs2_attn_desc* desc, int kv_capacity);
+
+/*
+ * Full-attention layer scoring ([Origins] "KV Reuse and Token-Level Sparse
+ * Selection": the full layer attends over the whole context and yields the
+ * selection indices besides its KV cache).
+ *
+ * For each query group g (tile_q consecutive queries) of sequence b, writes
+ *   scores[b][g][j] = sum over queries i in g, heads h of p_ihj,   j < ctx_len[b]
+ * where p_ihj = exp(s_ihj - lse_ih), s_ihj = sm_scale * q_ih . k_j, is query
+ * i's softmax probability over its causal range 0..P_i (0 for j > P_i).
+ * Entries j >= ctx_len[b] are not written.  Optional outputs: o_full, the
+ * full layer's own attention output sum_j p_ihj v_j (needs v), and lse.
+ * v may be NULL when o_full is NULL.
+ */
+HS2_API hs2_status hs2_full_attn_scores(const hs2_attn_desc* desc, const void* q,
+                                const void* k, const void* v, int64_t kv_stride,
+                                const int32_t* ctx_len, int kv_capacity,
+                                float* scores, float* o_full, float* lse,
+                                void* ws, size_t ws_bytes, hs2_stream_t stream);
+
+/*
+ * Selector ([Origins] "KV Reuse and Token-Level Sparse Selection"; [Summary]
+ * "KV Reuse refinements"): for each group g of sequence b, with P0 the
+ * position of its first query, the pool is keys [0, max(0, P0 - window + 1))
+ * -- the window keys are kept out of it -- and the selection is the
+ * min(k_top, pool) pool keys of largest score, ties going to the lower index.
+ * Writes them to top_idx[b][g][0..cnt) in ascending index order, pads the
+ * rest with -1 and writes cnt to top_cnt[b][g].  The forced window itself is
+ * implied by each query's position and is not stored.  Scores must be finite
+ * and non-negative (as hs2_full_attn_scores writes them); the result is
+ * exactly determined by the fp32 values given.
+ */
+HS2_API hs2_status hs2_select_topk_window(const hs2_attn_desc* desc, const float* scores,
+                                  const int32_t* ctx_len, int kv_capacity,
+                                  int32_t* top_idx, int32_t* top_cnt,
+                                  void* ws, size_t ws_bytes, hs2_stream_t stream);
+
+/*
+ * Sparse layer ([Origins] "KV Reuse and Token-Level Sparse Selection": the
+ * sparse layers reuse the full layer's indices and read its K/V cache; the
+ * 128 most recent tokens are always part of the selection).  For query i at
+ * position P of group g:
+ *   S_i = top_idx[b][g][0..top_cnt) ++ [max(0, P - window + 1), P]
+ *   o[b][i][h] = sum over j in S_i of softmax_S(sm_scale * q_ih . k_j) v_j
+ * and lse[b][i][h] = log sum over S_i of exp(sm_scale * q_ih . k_j) (lse may
+ * be NULL).  q is the sparse layer's own query.  top_idx/top_cnt must be as
+ * hs2_select_topk_window writes them (ascending, inside the pool).
+ */
+HS2_API hs2_status hs2_sparse_attn_gather(const hs2_attn_desc* desc, const void* q,
+                                  const void* k, const void* v, int64_t kv_stride,
+                                  const int32_t* ctx_len, int kv_capacity,
+                                  const int32_t* top_idx, const int32_t* top_cnt,
+                                  float* o, float* lse, void* ws, size_t ws_bytes,
+                                  hs2_stream_t stream);
+
+/*
+ * KV Bridging ([Origins] "The Self-Decoder and Cross-Decoder Split", first two
+ * equations; [Summary] "KV Bridging"): the K and V of a cross-decoder
+ * full-attention layer are learned projections of a self-decoder
+ * full-attention layer's hidden states:
+ *   k_out[m][:] = bf16(h[m][:] . w_k),  v_out[m][:] = bf16(h[m][:] . w_v)
+ * with fp32 accumulation and round-to-nearest-even.  All bfloat16:
+ *   h [M][d_model] with row stride ldh (elements), w_k/w_v [d_model][head_dim]
+ *   row-major, k_out/v_out [M][head_dim] with row stride ld_kv (elements).
+ * head_dim must be 128; d_model a positive multiple of 64; ldh >= d_model and
+ * ld_kv >= head_dim, both multiples of 8.
+ */
+HS2_API hs2_status hs2_bridge_kv(const uint16_t* h, int64_t ldh, const uint16_t* w_k,
+                         const uint16_t* w_v, uint16_t* k_out, uint16_t* v_out,
+                         int64_t ld_kv, int M, int d_model, int head_dim,
+                         hs2_stream_t stream);
+
+/* Static description of a status code. */
+HS2_API const char* hs2_status_string(hs2_status status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* HS2_H_ */

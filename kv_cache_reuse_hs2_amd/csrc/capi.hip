@@ -1,0 +1,160 @@
+// C ABI entry points of libhs2: host-side validation, then kernel dispatch.
+// Every argument check happens before the first enqueue, so a call that
+// returns an error has enqueued nothing.
+#include <math.h>
+
+#include "hs2_internal.h"
+
+namespace hs2 {
+
+hipError_t launch_bridge(const uint16_t* h, int64_t ldh, const uint16_t* w_k, const uint16_t* w_v,
+                         uint16_t* k_out, uint16_t* v_out, int64_t ld_kv, int M, int d_model,
+                         hipStream_t st);
+
+namespace {
+
+bool misaligned(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) != 0; }
+
+hs2_status check_desc(const hs2_attn_desc* d) {
+  if (d == nullptr) return HS2_EINVAL;
+  if (d->batch < 1 || d->n_q < 1 || d->n_heads < 1 || d->head_dim < 1 || d->tile_q < 1)
+    return HS2_EINVAL;
+  if (d->k_top < 0 || d->window < 0) return HS2_EINVAL;
+  if (d->n_q % d->tile_q != 0) return HS2_EINVAL;
+  if (!(d->sm_scale > 0.f) || !isfinite(d->sm_scale)) return HS2_EINVAL;
+  if (d->dtype != HS2_F32 && d->dtype != HS2_BF16) return HS2_EINVAL;
+  if (d->head_dim != kHeadDim || d->n_heads > kMaxHeads) return HS2_EUNSUPPORTED;
+  if (d->k_top > kMaxTop || d->window > kMaxWindow) return HS2_EUNSUPPORTED;
+  if (d->causal != 1) return HS2_EUNSUPPORTED;
+  // Decode: one query per sequence.  (Query groups of 64 are the prefill layout.)
+  const bool decode = d->n_q == 1 && d->tile_q == 1;
+  if (!decode) return HS2_EUNSUPPORTED;
+  return HS2_OK;
+}
+
+hs2_status check_cache(const hs2_attn_desc* d, int64_t kv_stride, int cap) {
+  if (cap < 1) return HS2_EINVAL;
+  if (kv_stride < (int64_t)cap * kHeadDim) return HS2_EINVAL;
+  if (kv_stride % 8 != 0) return HS2_EALIGN;  // keeps every row 16-byte aligned
+  (void)d;
+  return HS2_OK;
+}
+
+size_t needed_ws(const hs2_attn_desc& d, int cap) {
+  size_t n = score_ws(d, cap).bytes;
+  n = n > select_ws(d, cap).bytes ? n : select_ws(d, cap).bytes;
+  n = n > sparse_ws(d).bytes ? n : sparse_ws(d).bytes;
+  return n;
+}
+
+hs2_status check_ws(const hs2_attn_desc& d, int cap, const void* ws, size_t ws_bytes) {
+  const size_t need = needed_ws(d, cap);
+  if (ws_bytes < need) return HS2_EWORKSPACE;
+  if (need > 0 && ws == nullptr) return HS2_EINVAL;
+  if (misaligned(ws)) return HS2_EALIGN;
+  return HS2_OK;
+}
+
+hs2_status launched(hipError_t e) { return e == hipSuccess ? HS2_OK : HS2_EHIP; }
+
+}  // namespace
+}  // namespace hs2
+
+using namespace hs2;
+
+extern "C" {
+
+size_t hs2_workspace_size(const hs2_attn_desc* desc, int kv_capacity) {
+  if (check_desc(desc) != HS2_OK || kv_capacity < 1) return 0;
+  return needed_ws(*desc, kv_capacity);
+}
+
+hs2_status hs2_full_attn_scores(const hs2_attn_desc* desc, const void* q, const void* k,
+                                const void* v, int64_t kv_stride, const int32_t* ctx_len,
+                                int kv_capacity, float* scores, float* o_full, float* lse,
+                                void* ws, size_t ws_bytes, hs2_stream_t stream) {
+  hs2_status s = check_desc(desc);
+  if (s != HS2_OK) return s;
+  if (q == nullptr || k == nullptr || ctx_len == nullptr || scores == nullptr) return HS2_EINVAL;
+  if (o_full != nullptr) {
+    if (v == nullptr) return HS2_EINVAL;
+    return HS2_EUNSUPPORTED;  // the decode scorer streams K only
+  }
+  if ((s = check_cache(desc, kv_stride, kv_capacity)) != HS2_OK) return s;
+  if (misaligned(q) || misaligned(k) || misaligned(v) || misaligned(ctx_len) ||
+      misaligned(scores) || misaligned(lse))
+    return HS2_EALIGN;
+  if ((s = check_ws(*desc, kv_capacity, ws, ws_bytes)) != HS2_OK) return s;
+  (void)hipGetLastError();
+  return launched(launch_score_decode(*desc, q, k, kv_stride, ctx_len, kv_capacity, scores, lse,
+                                      static_cast<char*>(ws),
+                                      static_cast<hipStream_t>(stream)));
+}
+
+hs2_status hs2_select_topk_window(const hs2_attn_desc* desc, const float* scores,
+                                  const int32_t* ctx_len, int kv_capacity, int32_t* top_idx,
+                                  int32_t* top_cnt, void* ws, size_t ws_bytes,
+                                  hs2_stream_t stream) {
+  hs2_status s = check_desc(desc);
+  if (s != HS2_OK) return s;
+  if (scores == nullptr || ctx_len == nullptr || top_cnt == nullptr) return HS2_EINVAL;
+  if (top_idx == nullptr && desc->k_top > 0) return HS2_EINVAL;
+  if (kv_capacity < 1) return HS2_EINVAL;
+  if (misaligned(scores) || misaligned(ctx_len) || misaligned(top_idx) || misaligned(top_cnt))
+    return HS2_EALIGN;
+  if ((s = check_ws(*desc, kv_capacity, ws, ws_bytes)) != HS2_OK) return s;
+  (void)hipGetLastError();
+  return launched(launch_select(*desc, scores, ctx_len, kv_capacity, top_idx, top_cnt,
+                                static_cast<char*>(ws), static_cast<hipStream_t>(stream)));
+}
+
+hs2_status hs2_sparse_attn_gather(const hs2_attn_desc* desc, const void* q, const void* k,
+                                  const void* v, int64_t kv_stride, const int32_t* ctx_len,
+                                  int kv_capacity, const int32_t* top_idx,
+                                  const int32_t* top_cnt, float* o, float* lse, void* ws,
+                                  size_t ws_bytes, hs2_stream_t stream) {
+  hs2_status s = check_desc(desc);
+  if (s != HS2_OK) return s;
+  if (q == nullptr || k == nullptr || v == nullptr || ctx_len == nullptr || top_cnt == nullptr ||
+      o == nullptr)
+    return HS2_EINVAL;
+  if (top_idx == nullptr && desc->k_top > 0) return HS2_EINVAL;
+  if ((s = check_cache(desc, kv_stride, kv_capacity)) != HS2_OK) return s;
+  if (misaligned(q) || misaligned(k) || misaligned(v) || misaligned(ctx_len) ||
+      misaligned(top_idx) || misaligned(top_cnt) || misaligned(o) || misaligned(lse))
+    return HS2_EALIGN;
+  if ((s = check_ws(*desc, kv_capacity, ws, ws_bytes)) != HS2_OK) return s;
+  (void)hipGetLastError();
+  return launched(launch_sparse(*desc, q, k, v, kv_stride, ctx_len, kv_capacity, top_idx, top_cnt,
+                                o, lse, static_cast<char*>(ws),
+                                static_cast<hipStream_t>(stream)));
+}
+
+hs2_status hs2_bridge_kv(const uint16_t* h, int64_t ldh, const uint16_t* w_k, const uint16_t* w_v,
+                         uint16_t* k_out, uint16_t* v_out, int64_t ld_kv, int M, int d_model,
+                         int head_dim, hs2_stream_t stream) {
+  if (h == nullptr || w_k == nullptr || w_v == nullptr || k_out == nullptr || v_out == nullptr)
+    return HS2_EINVAL;
+  if (M < 1 || d_model < 1 || head_dim < 1 || ldh < d_model || ld_kv < head_dim) return HS2_EINVAL;
+  if (head_dim != kHeadDim || d_model % 64 != 0) return HS2_EUNSUPPORTED;
+  if (ldh % 8 != 0 || ld_kv % 8 != 0) return HS2_EALIGN;
+  if (misaligned(h) || misaligned(w_k) || misaligned(w_v) || misaligned(k_out) || misaligned(v_out))
+    return HS2_EALIGN;
+  (void)hipGetLastError();
+  return launched(launch_bridge(h, ldh, w_k, w_v, k_out, v_out, ld_kv, M, d_model,
+                                static_cast<hipStream_t>(stream)));
+}
+
+const char* hs2_status_string(hs2_status status) {
+  switch (status) {
+    case HS2_OK: return "HS2_OK: success";
+    case HS2_EINVAL: return "HS2_EINVAL: null pointer, bad size or inconsistent shape";
+    case HS2_EUNSUPPORTED: return "HS2_EUNSUPPORTED: valid arguments outside what the kernels implement";
+    case HS2_EALIGN: return "HS2_EALIGN: pointer or stride not 16-byte aligned";
+    case HS2_EWORKSPACE: return "HS2_EWORKSPACE: workspace smaller than hs2_workspace_size()";
+    case HS2_EHIP: return "HS2_EHIP: the HIP runtime reported an error while enqueuing";
+  }
+  return "unknown hs2_status";
+}
+
+}  // extern "C"

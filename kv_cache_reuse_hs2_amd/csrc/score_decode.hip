@@ -1,0 +1,304 @@
+// Full-attention scoring for a decode step (one query per sequence).
+//
+// The full layer of a hybrid block attends over the whole context and, from
+// that attention, yields the token selection the sparse layers reuse
+// ("HySparse2: How Xiaomi Split the Transformer to Fix Agent Prefill Costs",
+// section "KV Reuse and Token-Level Sparse Selection").  The per-key
+// importance is the softmax probability summed over all query heads:
+//   I[j] = sum_h 2^(x_hj - L_h),  x_hj = (sm_scale*log2 e) * q_h.k_j,
+//   L_h  = log2 sum_j 2^(x_hj)    (base-2 log-sum-exp of head h).
+// L_h needs every key before any I[j] exists, so the K cache is streamed
+// twice: pass 1 writes per-chunk (max, sum) per head, a reduction forms L_h,
+// and pass 2 recomputes the logits and writes I.  Pass 2 walks the chunks in
+// the reverse order of pass 1 so that its reads hit what the memory-side
+// cache still holds from pass 1.
+//
+// bf16 path: one wave computes a 32-key x 32-head logit tile with eight
+// v_mfma_f32_32x32x16_bf16 (K = 128 = 8 x 16).  Each lane loads 16 B of a key
+// row per MFMA step straight from HBM (lane%32 = key, lane/32 = which 8
+// dims of the 16-dim step).  Pass 1 takes K as the A operand so that a lane
+// holds one head over 16 keys (per-head max/sum are in-lane); pass 2 takes
+// K as the B operand so that a lane holds one key over 16 heads (the head
+// sum is in-lane plus one cross-half add).
+//
+// fp32 path: a VALU dot-product kernel, one key per thread.
+#include "hs2_internal.h"
+
+namespace hs2 {
+namespace {
+
+typedef __bf16 bf16x8_t __attribute__((__vector_size__(8 * sizeof(__bf16))));
+typedef float f32x16_t __attribute__((__vector_size__(16 * sizeof(float))));
+
+__device__ __forceinline__ bf16x8_t as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8_t, v); }
+
+constexpr int kWaves = 4;
+constexpr int kF32Chunk = 256;   // keys per workgroup in the fp32 kernels (score_chunk_keys)
+
+// Merge two (max, sum) pairs of base-2 softmax statistics.
+__device__ __forceinline__ void merge_ml(float& m, float& l, float m2, float l2) {
+  const float mn = fmaxf(m, m2);
+  if (mn == -INFINITY) return;  // both empty
+  l = l * fast_exp2(m - mn) + l2 * fast_exp2(m2 - mn);
+  m = mn;
+}
+
+__device__ __forceinline__ void load_q_bf16(const uint16_t* qb, int H, int r32, int hh,
+                                            bf16x8_t (&qreg)[8]) {
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    u32x4 v = {0u, 0u, 0u, 0u};
+    if (r32 < H) v = *reinterpret_cast<const u32x4*>(qb + r32 * kHeadDim + 16 * i + 8 * hh);
+    qreg[i] = as_bf16x8(v);
+  }
+}
+
+__device__ __forceinline__ void load_k_block(const uint16_t* kb, int row, int hh, u32x4 (&kr)[8]) {
+  const u32x4* kp = reinterpret_cast<const u32x4*>(kb + (size_t)row * kHeadDim + 8 * hh);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) kr[i] = kp[2 * i];
+}
+
+// Pass 1, bf16: per (sequence, chunk, head) base-2 (max, sum).
+__global__ __launch_bounds__(256) void score_stats_bf16(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, int64_t kv_stride,
+    const int32_t* __restrict__ ctx_len, int cap, int H, float c2,
+    float2* __restrict__ stats, int nchunks) {
+  const int b = blockIdx.y, c = blockIdx.x;
+  const int N = clamp_ctx(ctx_len, b, cap);
+  const int j_begin = c * kScoreChunk;
+  if (j_begin >= N) return;
+  const int j_end = min(N, j_begin + kScoreChunk);
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int r32 = lane & 31, hh = lane >> 5;
+
+  bf16x8_t qreg[8];
+  load_q_bf16(q + (size_t)b * H * kHeadDim, H, r32, hh, qreg);
+  const uint16_t* kb = k + (size_t)b * kv_stride;
+
+  float m_run = -INFINITY, l_run = 0.f;
+  int j0 = j_begin + 32 * wave;
+  u32x4 kr[8], kn[8];
+  if (j0 < j_end) load_k_block(kb, min(j0 + r32, N - 1), hh, kr);
+  while (j0 < j_end) {
+    const int jn = j0 + 32 * kWaves;
+    if (jn < j_end) load_k_block(kb, min(jn + r32, N - 1), hh, kn);
+    f32x16_t acc = {};
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(kr[i]), qreg[i], acc, 0, 0, 0);
+    // acc[r] = logit of key j0 + 8*(r/4) + 4*hh + r%4 for head r32.
+    float x[16];
+    float bm = -INFINITY;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int j = j0 + 8 * (r >> 2) + 4 * hh + (r & 3);
+      x[r] = (j < j_end) ? acc[r] * c2 : -INFINITY;
+      bm = fmaxf(bm, x[r]);
+    }
+    const float m_new = fmaxf(m_run, bm);
+    const float mref = (m_new == -INFINITY) ? 0.f : m_new;
+    float s = l_run * fast_exp2(m_run - mref);
+#pragma unroll
+    for (int r = 0; r < 16; ++r) s += fast_exp2(x[r] - mref);
+    l_run = s;
+    m_run = m_new;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) kr[i] = kn[i];
+    j0 = jn;
+  }
+  // Lanes r32 and r32+32 hold the same head over different keys.
+  merge_ml(m_run, l_run, __shfl_xor(m_run, 32), __shfl_xor(l_run, 32));
+  __shared__ float2 part[kWaves][32];
+  if (hh == 0) part[wave][r32] = make_float2(m_run, l_run);
+  __syncthreads();
+  if (threadIdx.x < 32) {
+    float m = part[0][threadIdx.x].x, l = part[0][threadIdx.x].y;
+#pragma unroll
+    for (int w = 1; w < kWaves; ++w) merge_ml(m, l, part[w][threadIdx.x].x, part[w][threadIdx.x].y);
+    stats[((size_t)b * nchunks + c) * kMaxHeads + threadIdx.x] = make_float2(m, l);
+  }
+}
+
+// Pass 2, bf16: I[j] = sum_h 2^(x_hj - L_h).  Chunks are taken in reverse.
+__global__ __launch_bounds__(256) void score_importance_bf16(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, int64_t kv_stride,
+    const int32_t* __restrict__ ctx_len, int cap, int H, float c2,
+    const float* __restrict__ lse2, float* __restrict__ scores, int64_t score_stride) {
+  const int b = gridDim.y - 1 - blockIdx.y;
+  const int c = gridDim.x - 1 - blockIdx.x;
+  const int N = clamp_ctx(ctx_len, b, cap);
+  const int j_begin = c * kScoreChunk;
+  if (j_begin >= N) return;
+  const int j_end = min(N, j_begin + kScoreChunk);
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int r32 = lane & 31, hh = lane >> 5;
+
+  bf16x8_t qreg[8];
+  load_q_bf16(q + (size_t)b * H * kHeadDim, H, r32, hh, qreg);
+  float L[16];  // lane holds heads 8*(r/4) + 4*hh + r%4
+#pragma unroll
+  for (int r = 0; r < 16; ++r) L[r] = lse2[b * kMaxHeads + 8 * (r >> 2) + 4 * hh + (r & 3)];
+  const uint16_t* kb = k + (size_t)b * kv_stride;
+  float* out = scores + (size_t)b * score_stride;
+
+  int j0 = j_begin + 32 * wave;
+  u32x4 kr[8], kn[8];
+  if (j0 < j_end) load_k_block(kb, min(j0 + r32, N - 1), hh, kr);
+  while (j0 < j_end) {
+    const int jn = j0 + 32 * kWaves;
+    if (jn < j_end) load_k_block(kb, min(jn + r32, N - 1), hh, kn);
+    f32x16_t acc = {};
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qreg[i], as_bf16x8(kr[i]), acc, 0, 0, 0);
+    // acc[r] = logit of head 8*(r/4) + 4*hh + r%4 for key j0 + r32.
+    float imp = 0.f;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) imp += fast_exp2(acc[r] * c2 - L[r]);
+    imp += __shfl_xor(imp, 32);
+    if (hh == 0 && j0 + r32 < j_end) out[j0 + r32] = imp;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) kr[i] = kn[i];
+    j0 = jn;
+  }
+}
+
+// fp32 VALU kernel: MODE 0 writes per-chunk statistics, MODE 1 importance.
+template <int MODE>
+__global__ __launch_bounds__(256) void score_f32(
+    const float* __restrict__ q, const float* __restrict__ k, int64_t kv_stride,
+    const int32_t* __restrict__ ctx_len, int cap, int H, float c2,
+    float2* __restrict__ stats, int nchunks, const float* __restrict__ lse2,
+    float* __restrict__ scores, int64_t score_stride) {
+  const int b = blockIdx.y;
+  const int c = (MODE == 1) ? (gridDim.x - 1 - blockIdx.x) : blockIdx.x;
+  const int N = clamp_ctx(ctx_len, b, cap);
+  const int j_begin = c * kF32Chunk;
+  if (j_begin >= N) return;
+  __shared__ float4 qs[kMaxHeads][kHeadDim / 4];
+  const float* qb = q + (size_t)b * H * kHeadDim;
+  for (int e = threadIdx.x; e < kMaxHeads * kHeadDim / 4; e += blockDim.x) {
+    const int h = e / (kHeadDim / 4), d4 = e % (kHeadDim / 4);
+    qs[h][d4] = h < H ? reinterpret_cast<const float4*>(qb + h * kHeadDim)[d4] : make_float4(0.f, 0.f, 0.f, 0.f);
+  }
+  __syncthreads();
+  const int j = j_begin + threadIdx.x;
+  const bool valid = j < N;
+  const float4* kp = reinterpret_cast<const float4*>(k + (size_t)b * kv_stride + (size_t)min(j, N - 1) * kHeadDim);
+  float acc[kMaxHeads];
+#pragma unroll
+  for (int h = 0; h < kMaxHeads; ++h) acc[h] = 0.f;
+  for (int d4 = 0; d4 < kHeadDim / 4; ++d4) {
+    const float4 kv = kp[d4];
+#pragma unroll
+    for (int h = 0; h < kMaxHeads; ++h) {
+      const float4 qv = qs[h][d4];
+      acc[h] = fmaf(qv.x, kv.x, acc[h]);
+      acc[h] = fmaf(qv.y, kv.y, acc[h]);
+      acc[h] = fmaf(qv.z, kv.z, acc[h]);
+      acc[h] = fmaf(qv.w, kv.w, acc[h]);
+    }
+  }
+  if (MODE == 1) {
+    if (!valid) return;
+    float imp = 0.f;
+#pragma unroll
+    for (int h = 0; h < kMaxHeads; ++h)
+      if (h < H) imp += fast_exp2(acc[h] * c2 - lse2[b * kMaxHeads + h]);
+    scores[(size_t)b * score_stride + j] = imp;
+  } else {
+    __shared__ float red[kWaves][kMaxHeads];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    for (int h = 0; h < kMaxHeads; ++h) {
+      float x = valid ? acc[h] * c2 : -INFINITY;
+      float m = x;
+#pragma unroll
+      for (int o = 32; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o));
+      if (lane == 0) red[wave][h] = m;
+      acc[h] = x;
+    }
+    __syncthreads();
+    __shared__ float bmax[kMaxHeads];
+    if (threadIdx.x < kMaxHeads) {
+      float m = red[0][threadIdx.x];
+      for (int w = 1; w < kWaves; ++w) m = fmaxf(m, red[w][threadIdx.x]);
+      bmax[threadIdx.x] = m;
+    }
+    __syncthreads();
+    for (int h = 0; h < kMaxHeads; ++h) {
+      const float mref = bmax[h] == -INFINITY ? 0.f : bmax[h];
+      float s = fast_exp2(acc[h] - mref);
+#pragma unroll
+      for (int o = 32; o > 0; o >>= 1) s += __shfl_xor(s, o);
+      if (lane == 0) red[wave][h] = s;
+    }
+    __syncthreads();
+    if (threadIdx.x < kMaxHeads) {
+      float l = 0.f;
+      for (int w = 0; w < kWaves; ++w) l += red[w][threadIdx.x];
+      stats[((size_t)b * nchunks + c) * kMaxHeads + threadIdx.x] = make_float2(bmax[threadIdx.x], l);
+    }
+  }
+}
+
+// Per (sequence, head): L_h = max + log2(sum) over the sequence's chunks.
+// Heads beyond H get +inf so that 2^(x - L) vanishes for them.
+__global__ __launch_bounds__(256) void score_reduce(
+    const float2* __restrict__ stats, int nchunks, int chunk, const int32_t* __restrict__ ctx_len,
+    int cap, int H, float* __restrict__ lse2, float* __restrict__ lse_out) {
+  const int b = blockIdx.x;
+  const int N = clamp_ctx(ctx_len, b, cap);
+  const int nc = (N + chunk - 1) / chunk;
+  const int h = threadIdx.x & 31, part = threadIdx.x >> 5;
+  float m = -INFINITY, l = 0.f;
+  for (int c = part; c < nc; c += 8) {
+    const float2 s = stats[((size_t)b * nchunks + c) * kMaxHeads + h];
+    merge_ml(m, l, s.x, s.y);
+  }
+  __shared__ float2 red[8][32];
+  red[part][h] = make_float2(m, l);
+  __syncthreads();
+  if (threadIdx.x < 32) {
+    m = red[0][h].x;
+    l = red[0][h].y;
+    for (int p = 1; p < 8; ++p) merge_ml(m, l, red[p][h].x, red[p][h].y);
+    const float L = (l > 0.f) ? m + log2f(l) : -INFINITY;
+    lse2[b * kMaxHeads + h] = (h < H) ? L : INFINITY;
+    if (lse_out != nullptr && h < H) lse_out[b * H + h] = L * 0.69314718055994531f;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_score_decode(const hs2_attn_desc& d, const void* q, const void* k,
+                               int64_t kv_stride, const int32_t* ctx_len, int cap,
+                               float* scores, float* lse, char* ws, hipStream_t st) {
+  const ScoreWs w = score_ws(d, cap);
+  float2* stats = reinterpret_cast<float2*>(ws + w.stats_off);
+  float* lse2 = reinterpret_cast<float*>(ws + w.lse2_off);
+  const float c2 = d.sm_scale * 1.4426950408889634f;
+  const int chunk = score_chunk_keys(d.dtype);
+  const int nchunks = score_chunks(d, cap);
+  const dim3 grid(nchunks, d.batch);
+  if (d.dtype == HS2_BF16) {
+    score_stats_bf16<<<grid, 256, 0, st>>>(static_cast<const uint16_t*>(q),
+                                           static_cast<const uint16_t*>(k), kv_stride, ctx_len,
+                                           cap, d.n_heads, c2, stats, nchunks);
+    score_reduce<<<d.batch, 256, 0, st>>>(stats, nchunks, chunk, ctx_len, cap, d.n_heads, lse2, lse);
+    score_importance_bf16<<<grid, 256, 0, st>>>(static_cast<const uint16_t*>(q),
+                                                static_cast<const uint16_t*>(k), kv_stride,
+                                                ctx_len, cap, d.n_heads, c2, lse2, scores, cap);
+  } else {
+    score_f32<0><<<grid, 256, 0, st>>>(static_cast<const float*>(q), static_cast<const float*>(k),
+                                       kv_stride, ctx_len, cap, d.n_heads, c2, stats, nchunks,
+                                       nullptr, nullptr, 0);
+    score_reduce<<<d.batch, 256, 0, st>>>(stats, nchunks, chunk, ctx_len, cap, d.n_heads, lse2, lse);
+    score_f32<1><<<grid, 256, 0, st>>>(static_cast<const float*>(q), static_cast<const float*>(k),
+                                       kv_stride, ctx_len, cap, d.n_heads, c2, nullptr, nchunks,
+                                       lse2, scores, cap);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace hs2

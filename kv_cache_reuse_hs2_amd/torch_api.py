@@ -1,0 +1,102 @@
+"""Torch-side plumbing around the C ABI: device buffers and a decode step.
+
+Nothing here computes: it allocates outputs and workspace with torch and
+calls the three libhs2 entry points in order on the current stream.
+"""
+
+from __future__ import annotations
+
+import dataclasses
+
+import numpy as np
+import torch
+
+from . import (HS2_BF16, HS2_F32, hs2_attn_desc, hs2_full_attn_scores, hs2_select_topk_window,
+               hs2_sparse_attn_gather, hs2_workspace_size, make_desc)
+
+
+def to_device(arr: np.ndarray, device="cuda") -> torch.Tensor:
+    """Copy a host array to the device, keeping raw bfloat16 bits as int16."""
+    a = np.ascontiguousarray(arr)
+    if a.dtype == np.uint16:
+        a = a.view(np.int16)
+    return torch.from_numpy(a).to(device)
+
+
+@dataclasses.dataclass
+class DecodeBuffers:
+    """Device inputs and outputs of one decode step (or query-group step)."""
+
+    desc: hs2_attn_desc
+    q: torch.Tensor
+    k: torch.Tensor
+    v: torch.Tensor
+    ctx_len: torch.Tensor
+    cap: int
+    scores: torch.Tensor
+    top_idx: torch.Tensor
+    top_cnt: torch.Tensor
+    o: torch.Tensor
+    lse_full: torch.Tensor
+    lse: torch.Tensor
+    ws: torch.Tensor
+
+    @property
+    def kv_stride(self) -> int:
+        return self.k.shape[1] * self.k.shape[2]
+
+
+def make_buffers(inp: dict, *, n_heads: int, k_top: int, window: int, sm_scale: float,
+                 dtype: str, n_q: int = 1, tile_q: int = 1, device="cuda") -> DecodeBuffers:
+    """Upload generator output (see ``workloads``) and allocate the outputs."""
+    bsz = inp["ctx_len"].shape[0]
+    cap = int(inp["capacity"])
+    desc = make_desc(batch=bsz, n_heads=n_heads, n_q=n_q, tile_q=tile_q, k_top=k_top,
+                     window=window, sm_scale=sm_scale,
+                     dtype=HS2_BF16 if dtype == "bf16" else HS2_F32)
+    tiles = n_q // tile_q
+    nbytes = hs2_workspace_size(desc, cap)
+    if nbytes == 0:
+        raise ValueError("descriptor rejected by hs2_workspace_size")
+    f32 = dict(dtype=torch.float32, device=device)
+    i32 = dict(dtype=torch.int32, device=device)
+    return DecodeBuffers(
+        desc=desc,
+        q=to_device(inp["q_raw"], device),
+        k=to_device(inp["k_raw"], device),
+        v=to_device(inp["v_raw"], device),
+        ctx_len=to_device(inp["ctx_len"].astype(np.int32), device),
+        cap=cap,
+        scores=torch.zeros((bsz, tiles, cap), **f32),
+        top_idx=torch.empty((bsz, tiles, max(k_top, 1)), **i32),
+        top_cnt=torch.empty((bsz, tiles), **i32),
+        o=torch.empty((bsz, n_q, n_heads, 128), **f32),
+        lse_full=torch.empty((bsz, n_q, n_heads), **f32),
+        lse=torch.empty((bsz, n_q, n_heads), **f32),
+        ws=torch.empty(nbytes, dtype=torch.uint8, device=device),
+    )
+
+
+def run_scores(buf: DecodeBuffers, stream=None) -> None:
+    hs2_full_attn_scores(buf.desc, buf.q, buf.k, None, buf.kv_stride, buf.ctx_len, buf.cap,
+                         buf.scores, None, buf.lse_full, buf.ws, stream)
+
+
+def run_select(buf: DecodeBuffers, scores: torch.Tensor | None = None, stream=None) -> None:
+    hs2_select_topk_window(buf.desc, buf.scores if scores is None else scores, buf.ctx_len,
+                           buf.cap, buf.top_idx, buf.top_cnt, buf.ws, stream)
+
+
+def run_sparse(buf: DecodeBuffers, q: torch.Tensor | None = None, top_idx=None, top_cnt=None,
+               stream=None) -> None:
+    hs2_sparse_attn_gather(buf.desc, buf.q if q is None else q, buf.k, buf.v, buf.kv_stride,
+                           buf.ctx_len, buf.cap, buf.top_idx if top_idx is None else top_idx,
+                           buf.top_cnt if top_cnt is None else top_cnt, buf.o, buf.lse, buf.ws,
+                           stream)
+
+
+def run_step(buf: DecodeBuffers, stream=None) -> None:
+    """One pass of the hot path: full-layer scoring, selection, sparse layer."""
+    run_scores(buf, stream)
+    run_select(buf, stream=stream)
+    run_sparse(buf, stream=stream)

@@ -1,0 +1,70 @@
+"""Shared helpers of the GPU parity tests (not a test module).
+
+Tolerances (the bar each GPU test asserts):
+* importance scores: element-wise |gpu - oracle| <= 1e-4 * |oracle| + 1e-30
+  (both sides compute in fp32 or better on identical stored inputs);
+* selection fed the oracle's fp32 scores: bit-exact;
+* selection from GPU scores: every index in the symmetric difference with the
+  oracle's selection is a near-tie, |I_or[j] - tau| <= 1e-4 * tau, tau being
+  the oracle's k-th pool score;
+* sparse outputs: max |gpu - oracle| <= 1e-4 for fp32 storage; for bf16
+  storage max abs <= 2e-2 and relative L2 <= 5e-3;
+* bridge: within one bfloat16 ulp of the oracle's correctly rounded value,
+  relative L2 <= 5e-3.
+"""
+
+from __future__ import annotations
+
+import numpy as np
+
+import oracle
+
+SCORE_RTOL = 1e-4
+SCORE_ATOL = 1e-30
+
+
+def assert_scores_close(gpu: np.ndarray, ref: np.ndarray, ctx_len) -> None:
+    for b, n in enumerate(ctx_len):
+        g = gpu[b, :, :n].astype(np.float64)
+        r = ref[b, :, :n].astype(np.float64)
+        err = np.abs(g - r)
+        bad = err > SCORE_RTOL * np.abs(r) + SCORE_ATOL
+        assert not bad.any(), (
+            f"seq {b}: {bad.sum()} scores off, worst rel "
+            f"{(err / np.maximum(np.abs(r), 1e-30)).max():.3e}")
+
+
+def assert_outputs_close(gpu: np.ndarray, ref: np.ndarray, dtype: str) -> None:
+    gpu = gpu.astype(np.float64)
+    err = np.abs(gpu - ref)
+    if dtype == "f32":
+        assert err.max() <= 1e-4, f"max abs {err.max():.3e}"
+    else:
+        assert err.max() <= 2e-2, f"max abs {err.max():.3e}"
+        den = np.linalg.norm(ref)
+        rel = np.linalg.norm(gpu - ref) / den if den > 0 else np.linalg.norm(gpu)
+        assert rel <= 5e-3, f"rel L2 {rel:.3e}"
+
+
+def assert_selection_near_ties(top_gpu, cnt_gpu, top_or, cnt_or, scores_or, ctx_len, *, n_q,
+                               tile_q, window) -> int:
+    """End-to-end selection check; returns the number of near-tie swaps."""
+    swaps = 0
+    for b in range(top_or.shape[0]):
+        pos = oracle.query_positions(int(ctx_len[b]), n_q)
+        for t in range(top_or.shape[1]):
+            assert cnt_gpu[b, t] == cnt_or[b, t]
+            c = int(cnt_or[b, t])
+            g = top_gpu[b, t, :c]
+            assert np.all(np.diff(g) > 0), "not ascending"
+            pe = oracle.pool_end(pos[t * tile_q], window)
+            assert c == 0 or (g.min() >= 0 and g.max() < pe)
+            assert np.all(top_gpu[b, t, c:] == -1)
+            o = top_or[b, t, :c]
+            diff = np.setxor1d(g, o)
+            if diff.size:
+                imp = scores_or[b, t, :pe].astype(np.float64)
+                tau = np.sort(imp)[::-1][c - 1]
+                assert np.all(np.abs(imp[diff] - tau) <= 1e-4 * tau), "selection differs beyond near-ties"
+                swaps += diff.size // 2
+    return swaps

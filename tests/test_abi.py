@@ -1,0 +1,159 @@
+"""CPU checks of the C ABI: the library loads, exports what include/hs2.h
+declares, and rejects invalid arguments before enqueuing anything.
+
+Only calls that fail host-side validation are made here (their contract is to
+return before any HIP call), so no GPU is needed.  A pointer value such as
+0x1000 below is never dereferenced: the call is rejected first.
+"""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import kv_cache_reuse_hs2_amd as hs2
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "hs2.h")
+
+FAKE = 0x10000  # 16-byte aligned, never dereferenced
+ODD = 0x10004   # misaligned
+
+
+def _declared():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"HS2_API\s+[\w\s\*]+?\b(hs2_\w+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(hs2.LIB_PATH):
+        pytest.fail("libhs2.so is not built; run __graft_entry__.build()")
+    return hs2.load()
+
+
+def test_header_declares_the_binding_exports():
+    assert _declared() == sorted(hs2.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for name in _declared():
+        assert hasattr(lib, name), name
+    # nothing beyond the C API is exported
+    out = os.popen(f"nm -D --defined-only {hs2.LIB_PATH}").read()
+    exported = {l.split()[-1] for l in out.splitlines() if " T " in l}
+    assert {n for n in exported if n.startswith("hs2")} == set(_declared())
+    assert not any("launch" in n for n in exported)
+
+
+def test_status_strings(lib):
+    for code in range(6):
+        s = hs2.hs2_status_string(code)
+        assert s.startswith(["HS2_OK", "HS2_EINVAL", "HS2_EUNSUPPORTED", "HS2_EALIGN",
+                             "HS2_EWORKSPACE", "HS2_EHIP"][code])
+    assert "unknown" in hs2.hs2_status_string(99)
+
+
+def _desc(**kw):
+    base = dict(batch=4, n_heads=32, n_q=1, tile_q=1, k_top=1024, window=128, dtype=hs2.HS2_BF16)
+    base.update(kw)
+    return hs2.make_desc(**base)
+
+
+def test_workspace_size(lib):
+    n = hs2.hs2_workspace_size(_desc(), 262144)
+    assert n > 0
+    # grows with the capacity, is rejected for invalid descriptors
+    assert hs2.hs2_workspace_size(_desc(), 1 << 20) > n
+    assert hs2.hs2_workspace_size(_desc(head_dim=64), 4096) == 0
+    assert hs2.hs2_workspace_size(_desc(), 0) == 0
+    assert lib.hs2_workspace_size(None, 4096) == 0
+
+
+def _scores(desc, *, q=FAKE, k=FAKE, stride=4096 * 128, ctx=FAKE, cap=4096, sc=FAKE, of=None,
+            v=None, lse=None, ws=FAKE, nbytes=1 << 30):
+    return hs2.load().hs2_full_attn_scores(ctypes.byref(desc) if desc is not None else None, q, k,
+                                           v, stride, ctx, cap, sc, of, lse, ws, nbytes, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(head_dim=64), hs2.HS2_EUNSUPPORTED),
+    (dict(n_heads=33), hs2.HS2_EUNSUPPORTED),
+    (dict(n_heads=0), hs2.HS2_EINVAL),
+    (dict(batch=0), hs2.HS2_EINVAL),
+    (dict(k_top=-1), hs2.HS2_EINVAL),
+    (dict(window=-1), hs2.HS2_EINVAL),
+    (dict(k_top=4096), hs2.HS2_EUNSUPPORTED),
+    (dict(n_q=3, tile_q=2), hs2.HS2_EINVAL),
+    (dict(causal=0), hs2.HS2_EUNSUPPORTED),
+    (dict(sm_scale=0.0), hs2.HS2_EINVAL),
+    (dict(sm_scale=float("inf")), hs2.HS2_EINVAL),
+    (dict(dtype=7), hs2.HS2_EINVAL),
+])
+def test_invalid_descriptor(lib, kw, code):
+    assert _scores(_desc(**kw)) == code
+
+
+def test_invalid_pointers_sizes_and_workspace(lib):
+    d = _desc()
+    assert _scores(None) == hs2.HS2_EINVAL
+    assert _scores(d, q=None) == hs2.HS2_EINVAL
+    assert _scores(d, k=None) == hs2.HS2_EINVAL
+    assert _scores(d, ctx=None) == hs2.HS2_EINVAL
+    assert _scores(d, sc=None) == hs2.HS2_EINVAL
+    assert _scores(d, of=FAKE) == hs2.HS2_EINVAL          # o_full needs v
+    assert _scores(d, cap=0) == hs2.HS2_EINVAL
+    assert _scores(d, stride=4095 * 128) == hs2.HS2_EINVAL
+    assert _scores(d, stride=4096 * 128 + 4) == hs2.HS2_EALIGN
+    assert _scores(d, q=ODD) == hs2.HS2_EALIGN
+    assert _scores(d, sc=ODD) == hs2.HS2_EALIGN
+    assert _scores(d, lse=ODD) == hs2.HS2_EALIGN
+    need = hs2.hs2_workspace_size(d, 4096)
+    assert _scores(d, nbytes=need - 1) == hs2.HS2_EWORKSPACE
+    assert _scores(d, ws=None, nbytes=need) == hs2.HS2_EINVAL
+    assert _scores(d, ws=ODD, nbytes=need) == hs2.HS2_EALIGN
+
+
+def test_select_and_sparse_validation(lib):
+    d = _desc()
+    L = hs2.load()
+    need = hs2.hs2_workspace_size(d, 4096)
+    sel = lambda **kw: L.hs2_select_topk_window(  # noqa: E731
+        ctypes.byref(d), kw.get("sc", FAKE), kw.get("ctx", FAKE), kw.get("cap", 4096),
+        kw.get("ti", FAKE), kw.get("tc", FAKE), kw.get("ws", FAKE), kw.get("nb", need), None)
+    assert sel(sc=None) == hs2.HS2_EINVAL
+    assert sel(tc=None) == hs2.HS2_EINVAL
+    assert sel(ti=None) == hs2.HS2_EINVAL
+    assert sel(cap=0) == hs2.HS2_EINVAL
+    assert sel(ti=ODD) == hs2.HS2_EALIGN
+    assert sel(nb=need - 1) == hs2.HS2_EWORKSPACE
+    sp = lambda **kw: L.hs2_sparse_attn_gather(  # noqa: E731
+        ctypes.byref(d), kw.get("q", FAKE), FAKE, kw.get("v", FAKE), kw.get("st", 4096 * 128),
+        FAKE, 4096, FAKE, FAKE, kw.get("o", FAKE), None, FAKE, kw.get("nb", need), None)
+    assert sp(v=None) == hs2.HS2_EINVAL
+    assert sp(o=None) == hs2.HS2_EINVAL
+    assert sp(q=ODD) == hs2.HS2_EALIGN
+    assert sp(st=100) == hs2.HS2_EINVAL
+    assert sp(nb=0) == hs2.HS2_EWORKSPACE
+
+
+def test_bridge_validation(lib):
+    L = hs2.load()
+    br = lambda **kw: L.hs2_bridge_kv(  # noqa: E731
+        kw.get("h", FAKE), kw.get("ldh", 2048), FAKE, FAKE, FAKE, kw.get("vo", FAKE),
+        kw.get("ldkv", 128), kw.get("M", 1024), kw.get("dm", 2048), kw.get("hd", 128), None)
+    assert br(h=None) == hs2.HS2_EINVAL
+    assert br(vo=None) == hs2.HS2_EINVAL
+    assert br(M=0) == hs2.HS2_EINVAL
+    assert br(ldh=1024) == hs2.HS2_EINVAL
+    assert br(hd=64, ldkv=128) == hs2.HS2_EUNSUPPORTED
+    assert br(dm=100, ldh=2048) == hs2.HS2_EUNSUPPORTED
+    assert br(ldh=2052) == hs2.HS2_EALIGN
+    assert br(h=ODD) == hs2.HS2_EALIGN
+
+
+def test_binding_raises_on_error_status(lib):
+    with pytest.raises(hs2.HS2Error) as ei:
+        hs2.hs2_bridge_kv(None, 2048, FAKE, FAKE, FAKE, FAKE, 128, 1024, 2048, stream=0)
+    assert ei.value.status == hs2.HS2_EINVAL
