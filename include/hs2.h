@@ -49,6 +49,7 @@
  * - Inputs must be finite.  bf16 values are raw bfloat16 bit patterns.
  * - Calls are reentrant.  A workspace may be shared by calls issued in order
  *   on one stream, never by calls that can run concurrently.
+ * - kv_capacity is at most 4,194,304 keys (HS2_EUNSUPPORTED beyond).
  */
 #ifndef HS2_H_
 #define HS2_H_
@@ -151,6 +152,23 @@ HS2_API hs2_status hs2_sparse_attn_gather(const hs2_attn_desc* desc, const void*
                                   const int32_t* top_idx, const int32_t* top_cnt,
                                   float* o, float* lse, void* ws, size_t ws_bytes,
                                   hs2_stream_t stream);
+
+/*
+ * One decode step of a hybrid block in a single call: the full layer's
+ * scoring (as hs2_full_attn_scores, with q), the selection (as
+ * hs2_select_topk_window) and the sparse layer (as hs2_sparse_attn_gather,
+ * with q_sparse, or q when q_sparse is NULL).  The outputs are exactly those
+ * of the three calls issued in order with the same workspace; on the bf16
+ * path the scoring pass also builds the selector's first histogram, which
+ * saves the selector one pass over the scores.  lse_full (the full layer's
+ * log-sum-exp) and lse (the sparse layer's) may be NULL.
+ */
+HS2_API hs2_status hs2_decode_step(const hs2_attn_desc* desc, const void* q,
+                                   const void* q_sparse, const void* k, const void* v,
+                                   int64_t kv_stride, const int32_t* ctx_len, int kv_capacity,
+                                   float* scores, float* lse_full, int32_t* top_idx,
+                                   int32_t* top_cnt, float* o, float* lse, void* ws,
+                                   size_t ws_bytes, hs2_stream_t stream);
 
 /*
  * KV Bridging ([Origins] "The Self-Decoder and Cross-Decoder Split", first two

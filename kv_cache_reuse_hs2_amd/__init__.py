@@ -28,6 +28,7 @@ EXPORTS = (
     "hs2_full_attn_scores",
     "hs2_select_topk_window",
     "hs2_sparse_attn_gather",
+    "hs2_decode_step",
     "hs2_bridge_kv",
     "hs2_status_string",
 )
@@ -82,6 +83,9 @@ def load(path: str | None = None):
     lib.hs2_sparse_attn_gather.argtypes = [_desc_p, _vp, _vp, _vp, _i64, _vp, _int, _vp, _vp,
                                            _vp, _vp, _vp, _sz, _vp]
     lib.hs2_sparse_attn_gather.restype = _int
+    lib.hs2_decode_step.argtypes = [_desc_p, _vp, _vp, _vp, _vp, _i64, _vp, _int, _vp, _vp, _vp,
+                                    _vp, _vp, _vp, _vp, _sz, _vp]
+    lib.hs2_decode_step.restype = _int
     lib.hs2_bridge_kv.argtypes = [_vp, _i64, _vp, _vp, _vp, _vp, _i64, _int, _int, _int, _vp]
     lib.hs2_bridge_kv.restype = _int
     lib.hs2_status_string.argtypes = [_int]
@@ -156,6 +160,15 @@ def hs2_sparse_attn_gather(desc, q, k, v, kv_stride, ctx_len, kv_capacity, top_i
                                        _ptr(top_idx), _ptr(top_cnt), _ptr(o), _ptr(lse), _ptr(ws),
                                        _nbytes(ws), _stream(stream))
     _check(st, "hs2_sparse_attn_gather")
+
+
+def hs2_decode_step(desc, q, q_sparse, k, v, kv_stride, ctx_len, kv_capacity, scores, lse_full,
+                    top_idx, top_cnt, o, lse=None, ws=None, stream=None) -> None:
+    st = load().hs2_decode_step(ctypes.byref(desc), _ptr(q), _ptr(q_sparse), _ptr(k), _ptr(v),
+                                int(kv_stride), _ptr(ctx_len), int(kv_capacity), _ptr(scores),
+                                _ptr(lse_full), _ptr(top_idx), _ptr(top_cnt), _ptr(o), _ptr(lse),
+                                _ptr(ws), _nbytes(ws), _stream(stream))
+    _check(st, "hs2_decode_step")
 
 
 def hs2_bridge_kv(h, ldh, w_k, w_v, k_out, v_out, ld_kv, M, d_model, head_dim=128,

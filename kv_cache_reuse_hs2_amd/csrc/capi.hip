@@ -13,6 +13,8 @@ hipError_t launch_bridge(const uint16_t* h, int64_t ldh, const uint16_t* w_k, co
 
 namespace {
 
+constexpr int kMaxSelectCap = 1024 * kSelSlice;  // selector pools up to 4,194,304 keys
+
 bool misaligned(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) != 0; }
 
 hs2_status check_desc(const hs2_attn_desc* d) {
@@ -34,18 +36,14 @@ hs2_status check_desc(const hs2_attn_desc* d) {
 
 hs2_status check_cache(const hs2_attn_desc* d, int64_t kv_stride, int cap) {
   if (cap < 1) return HS2_EINVAL;
+  if (cap > kMaxSelectCap) return HS2_EUNSUPPORTED;
   if (kv_stride < (int64_t)cap * kHeadDim) return HS2_EINVAL;
   if (kv_stride % 8 != 0) return HS2_EALIGN;  // keeps every row 16-byte aligned
   (void)d;
   return HS2_OK;
 }
 
-size_t needed_ws(const hs2_attn_desc& d, int cap) {
-  size_t n = score_ws(d, cap).bytes;
-  n = n > select_ws(d, cap).bytes ? n : select_ws(d, cap).bytes;
-  n = n > sparse_ws(d).bytes ? n : sparse_ws(d).bytes;
-  return n;
-}
+size_t needed_ws(const hs2_attn_desc& d, int cap) { return ws_layout(d, cap).bytes; }
 
 hs2_status check_ws(const hs2_attn_desc& d, int cap, const void* ws, size_t ws_bytes) {
   const size_t need = needed_ws(d, cap);
@@ -65,7 +63,7 @@ using namespace hs2;
 extern "C" {
 
 size_t hs2_workspace_size(const hs2_attn_desc* desc, int kv_capacity) {
-  if (check_desc(desc) != HS2_OK || kv_capacity < 1) return 0;
+  if (check_desc(desc) != HS2_OK || kv_capacity < 1 || kv_capacity > kMaxSelectCap) return 0;
   return needed_ws(*desc, kv_capacity);
 }
 
@@ -86,8 +84,9 @@ hs2_status hs2_full_attn_scores(const hs2_attn_desc* desc, const void* q, const 
     return HS2_EALIGN;
   if ((s = check_ws(*desc, kv_capacity, ws, ws_bytes)) != HS2_OK) return s;
   (void)hipGetLastError();
+  const WsLayout l = ws_layout(*desc, kv_capacity);
   return launched(launch_score_decode(*desc, q, k, kv_stride, ctx_len, kv_capacity, scores, lse,
-                                      static_cast<char*>(ws),
+                                      static_cast<char*>(ws) + l.score, false,
                                       static_cast<hipStream_t>(stream)));
 }
 
@@ -100,12 +99,15 @@ hs2_status hs2_select_topk_window(const hs2_attn_desc* desc, const float* scores
   if (scores == nullptr || ctx_len == nullptr || top_cnt == nullptr) return HS2_EINVAL;
   if (top_idx == nullptr && desc->k_top > 0) return HS2_EINVAL;
   if (kv_capacity < 1) return HS2_EINVAL;
+  if (kv_capacity > kMaxSelectCap) return HS2_EUNSUPPORTED;
   if (misaligned(scores) || misaligned(ctx_len) || misaligned(top_idx) || misaligned(top_cnt))
     return HS2_EALIGN;
   if ((s = check_ws(*desc, kv_capacity, ws, ws_bytes)) != HS2_OK) return s;
   (void)hipGetLastError();
+  const WsLayout l = ws_layout(*desc, kv_capacity);
   return launched(launch_select(*desc, scores, ctx_len, kv_capacity, top_idx, top_cnt,
-                                static_cast<char*>(ws), static_cast<hipStream_t>(stream)));
+                                static_cast<char*>(ws) + l.select, nullptr,
+                                static_cast<hipStream_t>(stream)));
 }
 
 hs2_status hs2_sparse_attn_gather(const hs2_attn_desc* desc, const void* q, const void* k,
@@ -125,9 +127,46 @@ hs2_status hs2_sparse_attn_gather(const hs2_attn_desc* desc, const void* q, cons
     return HS2_EALIGN;
   if ((s = check_ws(*desc, kv_capacity, ws, ws_bytes)) != HS2_OK) return s;
   (void)hipGetLastError();
+  const WsLayout l = ws_layout(*desc, kv_capacity);
   return launched(launch_sparse(*desc, q, k, v, kv_stride, ctx_len, kv_capacity, top_idx, top_cnt,
-                                o, lse, static_cast<char*>(ws),
+                                o, lse, static_cast<char*>(ws) + l.sparse,
                                 static_cast<hipStream_t>(stream)));
+}
+
+hs2_status hs2_decode_step(const hs2_attn_desc* desc, const void* q, const void* q_sparse,
+                           const void* k, const void* v, int64_t kv_stride,
+                           const int32_t* ctx_len, int kv_capacity, float* scores,
+                           float* lse_full, int32_t* top_idx, int32_t* top_cnt, float* o,
+                           float* lse, void* ws, size_t ws_bytes, hs2_stream_t stream) {
+  hs2_status s = check_desc(desc);
+  if (s != HS2_OK) return s;
+  if (q == nullptr || k == nullptr || v == nullptr || ctx_len == nullptr || scores == nullptr ||
+      top_cnt == nullptr || o == nullptr)
+    return HS2_EINVAL;
+  if (top_idx == nullptr && desc->k_top > 0) return HS2_EINVAL;
+  if ((s = check_cache(desc, kv_stride, kv_capacity)) != HS2_OK) return s;
+  if (q_sparse == nullptr) q_sparse = q;
+  if (misaligned(q) || misaligned(q_sparse) || misaligned(k) || misaligned(v) ||
+      misaligned(ctx_len) || misaligned(scores) || misaligned(lse_full) || misaligned(top_idx) ||
+      misaligned(top_cnt) || misaligned(o) || misaligned(lse))
+    return HS2_EALIGN;
+  if ((s = check_ws(*desc, kv_capacity, ws, ws_bytes)) != HS2_OK) return s;
+  (void)hipGetLastError();
+  const WsLayout l = ws_layout(*desc, kv_capacity);
+  char* w = static_cast<char*>(ws);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  // bf16: the scoring pass also builds the selector's histogram.
+  const bool fuse = desc->dtype == HS2_BF16;
+  hipError_t e = launch_score_decode(*desc, q, k, kv_stride, ctx_len, kv_capacity, scores,
+                                     lse_full, w + l.score, fuse, st);
+  if (e != hipSuccess) return HS2_EHIP;
+  const uint32_t* hist =
+      fuse ? reinterpret_cast<const uint32_t*>(w + l.score + score_ws(*desc, kv_capacity).hist_off)
+           : nullptr;
+  e = launch_select(*desc, scores, ctx_len, kv_capacity, top_idx, top_cnt, w + l.select, hist, st);
+  if (e != hipSuccess) return HS2_EHIP;
+  return launched(launch_sparse(*desc, q_sparse, k, v, kv_stride, ctx_len, kv_capacity, top_idx,
+                                top_cnt, o, lse, w + l.sparse, st));
 }
 
 hs2_status hs2_bridge_kv(const uint16_t* h, int64_t ldh, const uint16_t* w_k, const uint16_t* w_v,

@@ -13,13 +13,17 @@ constexpr int kMaxHeads = 32;
 constexpr int kMaxTop = 2048;
 constexpr int kMaxWindow = 2048;
 
-// Keys per workgroup of the decode scoring passes (4 waves x 8 blocks of 32).
-constexpr int kScoreChunk = 1024;
+// Decode scoring, bf16: both passes take 4,096 keys per workgroup (8 waves x
+// 16 blocks of 32 keys).  fp32: 256 keys
+// per workgroup in both passes.
+constexpr int kP1Chunk = 4096;
+constexpr int kP2Chunk = 4096;
+constexpr int kF32Chunk = 256;
 // Keys per workgroup of the sparse gather kernel.
 constexpr int kSparseSeg = 32;
 // Top-k selection: first radix digit = top 12 bits of the orderable key.
 constexpr int kSelBins = 4096;
-constexpr int kSelSlice = 4096;  // pool keys per workgroup of the radix passes
+constexpr int kSelSlice = 4096;  // pool keys per workgroup of the selector passes
 
 // ---------------------------------------------------------------------------
 // Small device helpers.
@@ -51,75 +55,80 @@ __device__ __forceinline__ int clamp_ctx(const int32_t* ctx_len, int b, int cap)
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 // ---------------------------------------------------------------------------
-// Workspace layout.  Every call lays its scratch out from the start of the
-// caller's workspace; hs2_workspace_size() returns the maximum over calls.
+// Workspace layout.  The three calls use disjoint regions (scoring, selection,
+// sparse, in this order), so a selector histogram left by the scoring pass of
+// the fused decode step survives until the selection reads it.
+
+inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+inline int score_chunk1(hs2_dtype dt) { return dt == HS2_BF16 ? kP1Chunk : kF32Chunk; }
+inline int score_nchunks1(const hs2_attn_desc& d, int cap) {
+  const int c = score_chunk1(d.dtype);
+  return (cap + c - 1) / c;
+}
 
 struct ScoreWs {
-  size_t stats_off;   // float2 [B][nchunks][32]  (max, sum) per chunk & head, base 2
-  size_t lse2_off;    // float  [B][32]            per-head log2-sum-exp (+inf pad)
+  size_t stats_off;  // float2 [B][nchunks1][32]  (max, sum) per chunk & head, base 2
+  size_t lse2_off;   // float  [B][32]             per-head log2-sum-exp (fp32 path)
+  size_t hist_off;   // uint32 [B][kSelBins]       selector histogram (fused step)
   size_t bytes;
 };
 
 struct SelectWs {
-  size_t hist_off;    // uint32 [R][kSelBins]
-  size_t ctr_off;     // uint32 [R][4]   greater count, candidate count
-  size_t greater_off; // int32  [R][kMaxTop]
-  size_t cand_off;    // uint2  [R][cap] (key, index)
+  size_t hist_off;    // uint32 [R][kSelBins]            (standalone selection)
+  size_t cnt_off;     // uint32 [R][nslices]             entries kept per slice
+  size_t list_off;    // uint2  [R][nslices][kSelSlice]  (key, index), index order
   size_t bytes;
 };
 
 struct SparseWs {
-  size_t part_off;    // float [B*n_q][nseg][H][D]  partial outputs
-  size_t ml_off;      // float2 [B*n_q][nseg][H]   partial (max, sum), natural log
+  size_t part_off;    // float  [B*n_q][nseg][H][D]  partial outputs
+  size_t ml_off;      // float2 [B*n_q][nseg][H]     partial (max, sum), natural log
   size_t bytes;
 };
-
-inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
-
-// Keys per workgroup of the decode scoring passes for each storage type.
-inline int score_chunk_keys(hs2_dtype dt) { return dt == HS2_BF16 ? kScoreChunk : 256; }
-inline int score_chunks(const hs2_attn_desc& d, int cap) {
-  const int c = score_chunk_keys(d.dtype);
-  return (cap + c - 1) / c;
-}
 
 inline ScoreWs score_ws(const hs2_attn_desc& d, int cap) {
   ScoreWs w{};
   size_t off = 0;
   w.stats_off = off;
-  off = align_up(off + sizeof(float) * 2 * (size_t)d.batch * score_chunks(d, cap) * kMaxHeads, 256);
+  off = align_up(off + sizeof(float) * 2 * (size_t)d.batch * score_nchunks1(d, cap) * kMaxHeads, 256);
   w.lse2_off = off;
   off = align_up(off + sizeof(float) * (size_t)d.batch * d.n_q * kMaxHeads, 256);
+  w.hist_off = off;
+  off = align_up(off + sizeof(uint32_t) * (size_t)d.batch * kSelBins, 256);
   w.bytes = off;
   return w;
 }
 
+inline int select_slices(int cap) { return (cap + kSelSlice - 1) / kSelSlice; }
+
 inline SelectWs select_ws(const hs2_attn_desc& d, int cap) {
   SelectWs w{};
   const size_t rows = (size_t)d.batch * (d.n_q / d.tile_q);
+  const size_t ns = select_slices(cap);
   size_t off = 0;
   w.hist_off = off;
   off = align_up(off + sizeof(uint32_t) * rows * kSelBins, 256);
-  w.ctr_off = off;
-  off = align_up(off + sizeof(uint32_t) * rows * 4, 256);
-  w.greater_off = off;
-  off = align_up(off + sizeof(int32_t) * rows * kMaxTop, 256);
-  w.cand_off = off;
-  off = align_up(off + sizeof(uint32_t) * 2 * rows * (size_t)cap, 256);
+  w.cnt_off = off;
+  off = align_up(off + sizeof(uint32_t) * rows * ns, 256);
+  w.list_off = off;
+  off = align_up(off + sizeof(uint32_t) * 2 * rows * ns * kSelSlice, 256);
   w.bytes = off;
   return w;
 }
 
 inline int sparse_segments(const hs2_attn_desc& d) {
-  return (d.k_top + d.window + kSparseSeg - 1) / kSparseSeg;
+  const int n = (d.k_top + d.window + kSparseSeg - 1) / kSparseSeg;
+  return n > 0 ? n : 1;
 }
 
 inline SparseWs sparse_ws(const hs2_attn_desc& d) {
   SparseWs w{};
   const size_t nq = (size_t)d.batch * d.n_q;
-  const size_t nseg = sparse_segments(d) > 0 ? sparse_segments(d) : 1;
+  const size_t nseg = sparse_segments(d);
   size_t off = 0;
   w.part_off = off;
   off = align_up(off + sizeof(float) * nq * nseg * d.n_heads * kHeadDim, 256);
@@ -129,15 +138,36 @@ inline SparseWs sparse_ws(const hs2_attn_desc& d) {
   return w;
 }
 
-// ---------------------------------------------------------------------------
-// Kernel launchers (each returns hipGetLastError() of its launches).
+// Offsets of the three regions inside the caller's workspace.
+struct WsLayout {
+  size_t score, select, sparse, bytes;
+};
 
+inline WsLayout ws_layout(const hs2_attn_desc& d, int cap) {
+  WsLayout l{};
+  l.score = 0;
+  l.select = align_up(score_ws(d, cap).bytes, 256);
+  l.sparse = align_up(l.select + select_ws(d, cap).bytes, 256);
+  l.bytes = align_up(l.sparse + sparse_ws(d).bytes, 256);
+  return l;
+}
+
+// ---------------------------------------------------------------------------
+// Kernel launchers (each returns hipGetLastError() of its launches).  `ws`
+// points at the launcher's own region.
+
+// with_hist: also build the selector histogram of the pool scores in the
+// scoring region (bf16 decode only).
 hipError_t launch_score_decode(const hs2_attn_desc& d, const void* q, const void* k,
                                int64_t kv_stride, const int32_t* ctx_len, int cap,
-                               float* scores, float* lse, char* ws, hipStream_t st);
+                               float* scores, float* lse, char* ws, bool with_hist,
+                               hipStream_t st);
 
+// hist: a ready histogram of the pool scores (from launch_score_decode with
+// with_hist), or null to build one.
 hipError_t launch_select(const hs2_attn_desc& d, const float* scores, const int32_t* ctx_len,
-                         int cap, int32_t* top_idx, int32_t* top_cnt, char* ws, hipStream_t st);
+                         int cap, int32_t* top_idx, int32_t* top_cnt, char* ws,
+                         const uint32_t* hist, hipStream_t st);
 
 hipError_t launch_sparse(const hs2_attn_desc& d, const void* q, const void* k, const void* v,
                          int64_t kv_stride, const int32_t* ctx_len, int cap,

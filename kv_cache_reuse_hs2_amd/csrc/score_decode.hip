@@ -8,20 +8,29 @@
 //   I[j] = sum_h 2^(x_hj - L_h),  x_hj = (sm_scale*log2 e) * q_h.k_j,
 //   L_h  = log2 sum_j 2^(x_hj)    (base-2 log-sum-exp of head h).
 // L_h needs every key before any I[j] exists, so the K cache is streamed
-// twice: pass 1 writes per-chunk (max, sum) per head, a reduction forms L_h,
-// and pass 2 recomputes the logits and writes I.  Pass 2 walks the chunks in
-// the reverse order of pass 1 so that its reads hit what the memory-side
-// cache still holds from pass 1.
+// twice, with the kernel boundary as the only synchronisation (on this chip
+// a release/acquire between workgroups writes back the L2 and costs more
+// than the second read):
+//   pass 1: per 4,096-key chunk, per-head (max, sum);
+//   pass 2: per 4,096-key chunk, each workgroup first folds the chunk
+//           statistics of its sequence into L_h (a few KiB from L2), then
+//           recomputes the logits and writes I; optionally it also adds the
+//           chunk's histogram of score bits (pool keys only) to the
+//           selector's per-sequence histogram.  Pass 2 walks the chunks in
+//           the reverse order of pass 1, so its first reads hit what the
+//           memory-side cache still holds.
 //
 // bf16 path: one wave computes a 32-key x 32-head logit tile with eight
 // v_mfma_f32_32x32x16_bf16 (K = 128 = 8 x 16).  Each lane loads 16 B of a key
-// row per MFMA step straight from HBM (lane%32 = key, lane/32 = which 8
-// dims of the 16-dim step).  Pass 1 takes K as the A operand so that a lane
-// holds one head over 16 keys (per-head max/sum are in-lane); pass 2 takes
-// K as the B operand so that a lane holds one key over 16 heads (the head
-// sum is in-lane plus one cross-half add).
+// row per MFMA step straight from HBM (lane%32 = key, lane/32 = which 8 dims
+// of the 16-dim step) and the next block is prefetched while the current one
+// is in the MFMA.  Pass 1 takes K as the A operand so that a lane holds one
+// head over 16 keys (per-head max/sum are in-lane); pass 2 takes K as the B
+// operand so that a lane holds one key over 16 heads (the head sum is
+// in-lane plus one cross-half add).
 //
-// fp32 path: a VALU dot-product kernel, one key per thread.
+// fp32 path: a VALU dot-product kernel, one key per thread, with a separate
+// reduction kernel.
 #include "hs2_internal.h"
 
 namespace hs2 {
@@ -32,8 +41,8 @@ typedef float f32x16_t __attribute__((__vector_size__(16 * sizeof(float))));
 
 __device__ __forceinline__ bf16x8_t as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8_t, v); }
 
-constexpr int kWaves = 4;
-constexpr int kF32Chunk = 256;   // keys per workgroup in the fp32 kernels (score_chunk_keys)
+constexpr int kP1Waves = 8;
+constexpr int kP2Waves = 8;
 
 // Merge two (max, sum) pairs of base-2 softmax statistics.
 __device__ __forceinline__ void merge_ml(float& m, float& l, float m2, float l2) {
@@ -59,16 +68,24 @@ __device__ __forceinline__ void load_k_block(const uint16_t* kb, int row, int hh
   for (int i = 0; i < 8; ++i) kr[i] = kp[2 * i];
 }
 
-// Pass 1, bf16: per (sequence, chunk, head) base-2 (max, sum).
-__global__ __launch_bounds__(256) void score_stats_bf16(
+// Pass 1, bf16: per (sequence, chunk, head) base-2 (max, sum).  Chunks at or
+// beyond the context write neutral statistics.  The workgroup of chunk 0 also
+// clears the sequence's selector histogram when one is built.
+__global__ __launch_bounds__(64 * kP1Waves) void score_p1_bf16(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, int64_t kv_stride,
-    const int32_t* __restrict__ ctx_len, int cap, int H, float c2,
-    float2* __restrict__ stats, int nchunks) {
+    const int32_t* __restrict__ ctx_len, int cap, int H, float c2, float2* __restrict__ stats,
+    int nchunks, uint32_t* __restrict__ hist) {
   const int b = blockIdx.y, c = blockIdx.x;
   const int N = clamp_ctx(ctx_len, b, cap);
-  const int j_begin = c * kScoreChunk;
-  if (j_begin >= N) return;
-  const int j_end = min(N, j_begin + kScoreChunk);
+  const int j_begin = c * kP1Chunk;
+  float2* st = stats + ((size_t)b * nchunks + c) * kMaxHeads;
+  if (hist != nullptr && c == 0)
+    for (int i = threadIdx.x; i < kSelBins; i += blockDim.x) hist[(size_t)b * kSelBins + i] = 0u;
+  if (j_begin >= N) {
+    if (threadIdx.x < kMaxHeads) st[threadIdx.x] = make_float2(-INFINITY, 0.f);
+    return;
+  }
+  const int j_end = min(N, j_begin + kP1Chunk);
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int r32 = lane & 31, hh = lane >> 5;
 
@@ -81,7 +98,7 @@ __global__ __launch_bounds__(256) void score_stats_bf16(
   u32x4 kr[8], kn[8];
   if (j0 < j_end) load_k_block(kb, min(j0 + r32, N - 1), hh, kr);
   while (j0 < j_end) {
-    const int jn = j0 + 32 * kWaves;
+    const int jn = j0 + 32 * kP1Waves;
     if (jn < j_end) load_k_block(kb, min(jn + r32, N - 1), hh, kn);
     f32x16_t acc = {};
 #pragma unroll
@@ -109,44 +126,80 @@ __global__ __launch_bounds__(256) void score_stats_bf16(
   }
   // Lanes r32 and r32+32 hold the same head over different keys.
   merge_ml(m_run, l_run, __shfl_xor(m_run, 32), __shfl_xor(l_run, 32));
-  __shared__ float2 part[kWaves][32];
+  __shared__ float2 part[kP1Waves][32];
   if (hh == 0) part[wave][r32] = make_float2(m_run, l_run);
   __syncthreads();
   if (threadIdx.x < 32) {
     float m = part[0][threadIdx.x].x, l = part[0][threadIdx.x].y;
 #pragma unroll
-    for (int w = 1; w < kWaves; ++w) merge_ml(m, l, part[w][threadIdx.x].x, part[w][threadIdx.x].y);
-    stats[((size_t)b * nchunks + c) * kMaxHeads + threadIdx.x] = make_float2(m, l);
+    for (int w = 1; w < kP1Waves; ++w) merge_ml(m, l, part[w][threadIdx.x].x, part[w][threadIdx.x].y);
+    st[threadIdx.x] = make_float2(m, l);
   }
 }
 
-// Pass 2, bf16: I[j] = sum_h 2^(x_hj - L_h).  Chunks are taken in reverse.
-__global__ __launch_bounds__(256) void score_importance_bf16(
+// Pass 2, bf16: fold the statistics into L_h, then I[j] = sum_h 2^(x_hj - L_h).
+template <bool kHist>
+__global__ __launch_bounds__(64 * kP2Waves) void score_p2_bf16(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, int64_t kv_stride,
     const int32_t* __restrict__ ctx_len, int cap, int H, float c2,
-    const float* __restrict__ lse2, float* __restrict__ scores, int64_t score_stride) {
+    const float2* __restrict__ stats, int nchunks1, float* __restrict__ scores,
+    int64_t score_stride, float* __restrict__ lse_out, uint32_t* __restrict__ hist, int window) {
   const int b = gridDim.y - 1 - blockIdx.y;
   const int c = gridDim.x - 1 - blockIdx.x;
   const int N = clamp_ctx(ctx_len, b, cap);
-  const int j_begin = c * kScoreChunk;
-  if (j_begin >= N) return;
-  const int j_end = min(N, j_begin + kScoreChunk);
+  const int j_begin = c * kP2Chunk;
+  if (j_begin >= N) {
+    if (lse_out != nullptr && c == 0 && threadIdx.x < H) lse_out[b * H + threadIdx.x] = -INFINITY;
+    return;
+  }
+  const int j_end = min(N, j_begin + kP2Chunk);
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int r32 = lane & 31, hh = lane >> 5;
-
-  bf16x8_t qreg[8];
-  load_q_bf16(q + (size_t)b * H * kHeadDim, H, r32, hh, qreg);
-  float L[16];  // lane holds heads 8*(r/4) + 4*hh + r%4
-#pragma unroll
-  for (int r = 0; r < 16; ++r) L[r] = lse2[b * kMaxHeads + 8 * (r >> 2) + 4 * hh + (r & 3)];
   const uint16_t* kb = k + (size_t)b * kv_stride;
-  float* out = scores + (size_t)b * score_stride;
 
+  // Start the K stream before folding the statistics.
   int j0 = j_begin + 32 * wave;
   u32x4 kr[8], kn[8];
   if (j0 < j_end) load_k_block(kb, min(j0 + r32, N - 1), hh, kr);
+  bf16x8_t qreg[8];
+  load_q_bf16(q + (size_t)b * H * kHeadDim, H, r32, hh, qreg);
+
+  constexpr int kParts = kP2Waves * 2;  // 32-thread groups folding the statistics
+  __shared__ float2 red[kParts][32];
+  __shared__ float s_L[32];
+  __shared__ uint32_t s_hist[kHist ? kSelBins : 1];
+  {
+    const int h = threadIdx.x & 31, part = threadIdx.x >> 5;
+    const int nc = (N + kP1Chunk - 1) / kP1Chunk;
+    const float2* sb = stats + (size_t)b * nchunks1 * kMaxHeads;
+    float m = -INFINITY, l = 0.f;
+    for (int cc = part; cc < nc; cc += kParts) {
+      const float2 v = sb[(size_t)cc * kMaxHeads + h];
+      merge_ml(m, l, v.x, v.y);
+    }
+    red[part][h] = make_float2(m, l);
+    if (kHist)
+      for (int i = threadIdx.x; i < kSelBins; i += blockDim.x) s_hist[i] = 0u;
+    __syncthreads();
+    if (threadIdx.x < 32) {
+      m = red[0][h].x;
+      l = red[0][h].y;
+#pragma unroll
+      for (int p = 1; p < kParts; ++p) merge_ml(m, l, red[p][h].x, red[p][h].y);
+      const float L = (l > 0.f) ? m + log2f(l) : -INFINITY;
+      s_L[h] = (h < H) ? L : INFINITY;  // padded heads contribute 2^-inf = 0
+      if (lse_out != nullptr && c == 0 && h < H) lse_out[b * H + h] = L * 0.69314718055994531f;
+    }
+    __syncthreads();
+  }
+  float L[16];  // lane holds heads 8*(r/4) + 4*hh + r%4
+#pragma unroll
+  for (int r = 0; r < 16; ++r) L[r] = s_L[8 * (r >> 2) + 4 * hh + (r & 3)];
+  float* out = scores + (size_t)b * score_stride;
+  const int pe = N - window;  // decode pool end (keys below it are histogrammed)
+
   while (j0 < j_end) {
-    const int jn = j0 + 32 * kWaves;
+    const int jn = j0 + 32 * kP2Waves;
     if (jn < j_end) load_k_block(kb, min(jn + r32, N - 1), hh, kn);
     f32x16_t acc = {};
 #pragma unroll
@@ -157,10 +210,20 @@ __global__ __launch_bounds__(256) void score_importance_bf16(
 #pragma unroll
     for (int r = 0; r < 16; ++r) imp += fast_exp2(acc[r] * c2 - L[r]);
     imp += __shfl_xor(imp, 32);
-    if (hh == 0 && j0 + r32 < j_end) out[j0 + r32] = imp;
+    const int j = j0 + r32;
+    if (hh == 0 && j < j_end) {
+      out[j] = imp;
+      if (kHist && j < pe) atomicAdd(&s_hist[order_key(imp) >> 20], 1u);
+    }
 #pragma unroll
     for (int i = 0; i < 8; ++i) kr[i] = kn[i];
     j0 = jn;
+  }
+  if (kHist) {
+    __syncthreads();
+    uint32_t* gh = hist + (size_t)b * kSelBins;
+    for (int i = threadIdx.x; i < kSelBins; i += blockDim.x)
+      if (s_hist[i] != 0u) atomicAdd(&gh[i], s_hist[i]);
   }
 }
 
@@ -208,7 +271,7 @@ __global__ __launch_bounds__(256) void score_f32(
       if (h < H) imp += fast_exp2(acc[h] * c2 - lse2[b * kMaxHeads + h]);
     scores[(size_t)b * score_stride + j] = imp;
   } else {
-    __shared__ float red[kWaves][kMaxHeads];
+    __shared__ float red[4][kMaxHeads];
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     for (int h = 0; h < kMaxHeads; ++h) {
       float x = valid ? acc[h] * c2 : -INFINITY;
@@ -222,7 +285,7 @@ __global__ __launch_bounds__(256) void score_f32(
     __shared__ float bmax[kMaxHeads];
     if (threadIdx.x < kMaxHeads) {
       float m = red[0][threadIdx.x];
-      for (int w = 1; w < kWaves; ++w) m = fmaxf(m, red[w][threadIdx.x]);
+      for (int w = 1; w < 4; ++w) m = fmaxf(m, red[w][threadIdx.x]);
       bmax[threadIdx.x] = m;
     }
     __syncthreads();
@@ -236,20 +299,20 @@ __global__ __launch_bounds__(256) void score_f32(
     __syncthreads();
     if (threadIdx.x < kMaxHeads) {
       float l = 0.f;
-      for (int w = 0; w < kWaves; ++w) l += red[w][threadIdx.x];
+      for (int w = 0; w < 4; ++w) l += red[w][threadIdx.x];
       stats[((size_t)b * nchunks + c) * kMaxHeads + threadIdx.x] = make_float2(bmax[threadIdx.x], l);
     }
   }
 }
 
-// Per (sequence, head): L_h = max + log2(sum) over the sequence's chunks.
+// fp32 path: per (sequence, head) L_h = max + log2(sum) over the chunks.
 // Heads beyond H get +inf so that 2^(x - L) vanishes for them.
-__global__ __launch_bounds__(256) void score_reduce(
-    const float2* __restrict__ stats, int nchunks, int chunk, const int32_t* __restrict__ ctx_len,
-    int cap, int H, float* __restrict__ lse2, float* __restrict__ lse_out) {
+__global__ __launch_bounds__(256) void score_reduce_f32(
+    const float2* __restrict__ stats, int nchunks, const int32_t* __restrict__ ctx_len, int cap,
+    int H, float* __restrict__ lse2, float* __restrict__ lse_out) {
   const int b = blockIdx.x;
   const int N = clamp_ctx(ctx_len, b, cap);
-  const int nc = (N + chunk - 1) / chunk;
+  const int nc = (N + kF32Chunk - 1) / kF32Chunk;
   const int h = threadIdx.x & 31, part = threadIdx.x >> 5;
   float m = -INFINITY, l = 0.f;
   for (int c = part; c < nc; c += 8) {
@@ -273,30 +336,37 @@ __global__ __launch_bounds__(256) void score_reduce(
 
 hipError_t launch_score_decode(const hs2_attn_desc& d, const void* q, const void* k,
                                int64_t kv_stride, const int32_t* ctx_len, int cap,
-                               float* scores, float* lse, char* ws, hipStream_t st) {
+                               float* scores, float* lse, char* ws, bool with_hist,
+                               hipStream_t st) {
   const ScoreWs w = score_ws(d, cap);
   float2* stats = reinterpret_cast<float2*>(ws + w.stats_off);
-  float* lse2 = reinterpret_cast<float*>(ws + w.lse2_off);
   const float c2 = d.sm_scale * 1.4426950408889634f;
-  const int chunk = score_chunk_keys(d.dtype);
-  const int nchunks = score_chunks(d, cap);
-  const dim3 grid(nchunks, d.batch);
+  const int nchunks1 = score_nchunks1(d, cap);
   if (d.dtype == HS2_BF16) {
-    score_stats_bf16<<<grid, 256, 0, st>>>(static_cast<const uint16_t*>(q),
-                                           static_cast<const uint16_t*>(k), kv_stride, ctx_len,
-                                           cap, d.n_heads, c2, stats, nchunks);
-    score_reduce<<<d.batch, 256, 0, st>>>(stats, nchunks, chunk, ctx_len, cap, d.n_heads, lse2, lse);
-    score_importance_bf16<<<grid, 256, 0, st>>>(static_cast<const uint16_t*>(q),
-                                                static_cast<const uint16_t*>(k), kv_stride,
-                                                ctx_len, cap, d.n_heads, c2, lse2, scores, cap);
+    uint32_t* hist = with_hist ? reinterpret_cast<uint32_t*>(ws + w.hist_off) : nullptr;
+    const auto* qq = static_cast<const uint16_t*>(q);
+    const auto* kk = static_cast<const uint16_t*>(k);
+    score_p1_bf16<<<dim3(nchunks1, d.batch), 64 * kP1Waves, 0, st>>>(
+        qq, kk, kv_stride, ctx_len, cap, d.n_heads, c2, stats, nchunks1, hist);
+    const dim3 g2((cap + kP2Chunk - 1) / kP2Chunk, d.batch);
+    if (with_hist)
+      score_p2_bf16<true><<<g2, 64 * kP2Waves, 0, st>>>(qq, kk, kv_stride, ctx_len, cap,
+                                                        d.n_heads, c2, stats, nchunks1, scores,
+                                                        cap, lse, hist, d.window);
+    else
+      score_p2_bf16<false><<<g2, 64 * kP2Waves, 0, st>>>(qq, kk, kv_stride, ctx_len, cap,
+                                                         d.n_heads, c2, stats, nchunks1, scores,
+                                                         cap, lse, nullptr, d.window);
   } else {
-    score_f32<0><<<grid, 256, 0, st>>>(static_cast<const float*>(q), static_cast<const float*>(k),
-                                       kv_stride, ctx_len, cap, d.n_heads, c2, stats, nchunks,
-                                       nullptr, nullptr, 0);
-    score_reduce<<<d.batch, 256, 0, st>>>(stats, nchunks, chunk, ctx_len, cap, d.n_heads, lse2, lse);
-    score_f32<1><<<grid, 256, 0, st>>>(static_cast<const float*>(q), static_cast<const float*>(k),
-                                       kv_stride, ctx_len, cap, d.n_heads, c2, nullptr, nchunks,
-                                       lse2, scores, cap);
+    float* lse2 = reinterpret_cast<float*>(ws + w.lse2_off);
+    const dim3 grid(nchunks1, d.batch);
+    const auto* qf = static_cast<const float*>(q);
+    const auto* kf = static_cast<const float*>(k);
+    score_f32<0><<<grid, 256, 0, st>>>(qf, kf, kv_stride, ctx_len, cap, d.n_heads, c2, stats,
+                                       nchunks1, nullptr, nullptr, 0);
+    score_reduce_f32<<<d.batch, 256, 0, st>>>(stats, nchunks1, ctx_len, cap, d.n_heads, lse2, lse);
+    score_f32<1><<<grid, 256, 0, st>>>(qf, kf, kv_stride, ctx_len, cap, d.n_heads, c2, nullptr,
+                                       nchunks1, lse2, scores, cap);
   }
   return hipGetLastError();
 }

@@ -8,128 +8,259 @@
 //   S = top_idx[g][0..cnt) ++ [max(0, P - window + 1), P]
 //   o_h = sum_{j in S} softmax_S(sm_scale * q_h.k_j) v_j
 //
-// The selection (at most k_top + window keys) is split into 32-key segments;
-// one workgroup gathers a segment's K and V rows into LDS, computes the
-// 32 x H logits and its local softmax, and writes a partial (max, sum, o).
-// A second kernel merges the partials of each query in segment order, so the
-// result does not depend on scheduling.
+// The selection (at most k_top + window keys) is cut into segments; one
+// workgroup gathers a segment's K and V rows and writes a partial
+// (max, sum, o) per head in base 2; sparse_combine merges the partials of a
+// query in segment order, so results do not depend on scheduling.
+//
+// bf16: 128-key segments, one wave per 32 keys.  QK^T is eight
+// v_mfma_f32_32x32x16_bf16 with the gathered K rows as the A operand (a lane
+// reads 16 contiguous bytes of one row per step), so each lane owns one head
+// over 16 keys and the wave's softmax statistics stay in-lane.  The
+// probabilities feed the PV product straight from those registers (A operand,
+// keys in the order the QK^T result holds them), split into a bf16 high and
+// low part so that the sum keeps about fp32 accuracy; V is transposed
+// through LDS into the matching B layout.  The four waves are merged in LDS in
+// a fixed order.
+// fp32: 32-key segments on VALU.
 #include "hs2_internal.h"
 
 namespace hs2 {
 namespace {
 
-template <typename T>
-__device__ __forceinline__ float ld_elem(const T* p, int i);
-template <>
-__device__ __forceinline__ float ld_elem<float>(const float* p, int i) { return p[i]; }
-template <>
-__device__ __forceinline__ float ld_elem<uint16_t>(const uint16_t* p, int i) { return bf16_to_f32(p[i]); }
+typedef __bf16 bf16x8_t __attribute__((__vector_size__(8 * sizeof(__bf16))));
+typedef float f32x16_t __attribute__((__vector_size__(16 * sizeof(float))));
 
-// Load 16 consecutive elements starting at p (16-B aligned) as fp32.
-template <typename T>
-__device__ __forceinline__ void load16(const T* p, float* dst);
-template <>
-__device__ __forceinline__ void load16<float>(const float* p, float* dst) {
-  const float4* s = reinterpret_cast<const float4*>(p);
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const float4 v = s[i];
-    dst[4 * i] = v.x;
-    dst[4 * i + 1] = v.y;
-    dst[4 * i + 2] = v.z;
-    dst[4 * i + 3] = v.w;
+__device__ __forceinline__ bf16x8_t as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8_t, v); }
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.69314718055994531f;
+
+// Selection-set geometry of one query.
+struct QueryGeom {
+  int N, cnt, wlo, S;
+};
+
+__device__ __forceinline__ QueryGeom query_geom(const int32_t* ctx_len, const int32_t* top_cnt,
+                                                int cap, int b, int i, int g, int tiles, int n_q,
+                                                int k_top, int window) {
+  QueryGeom q{};
+  q.N = clamp_ctx(ctx_len, b, cap);
+  const int P = q.N - n_q + i;
+  int wcnt = 0;
+  if (P >= 0) {
+    int c = top_cnt[b * tiles + g];
+    q.cnt = c < 0 ? 0 : (c > k_top ? k_top : c);
+    q.wlo = max(0, P - window + 1);
+    wcnt = P - q.wlo + 1;
   }
+  q.S = q.cnt + wcnt;
+  return q;
 }
-template <>
-__device__ __forceinline__ void load16<uint16_t>(const uint16_t* p, float* dst) {
-  const u32x4* s = reinterpret_cast<const u32x4*>(p);
+
+// Key index of selection position p (0 <= p < S), clamped into the cache for
+// memory safety (selector output is always inside it).
+__device__ __forceinline__ int sel_key(const QueryGeom& q, const int32_t* top_row, int p) {
+  int idx = p < q.cnt ? top_row[p] : q.wlo + (p - q.cnt);
+  return idx < 0 ? 0 : (idx >= q.N ? q.N - 1 : idx);
+}
+
+// ---------------------------------------------------------------------------
+// bf16, MFMA.
+
+constexpr int kSegWaves = 4;
+constexpr int kSegB = 32 * kSegWaves;  // keys per workgroup
+constexpr int kVtPitch = 40;           // bf16 per transposed V row (32 keys + pad)
+
+__global__ __launch_bounds__(64 * kSegWaves) void sparse_partial_bf16(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
+    const uint16_t* __restrict__ v, int64_t kv_stride, const int32_t* __restrict__ ctx_len,
+    int cap, const int32_t* __restrict__ top_idx, const int32_t* __restrict__ top_cnt, int n_q,
+    int tile_q, int k_top, int window, int H, float c2, float* __restrict__ part,
+    float2* __restrict__ ml, int nseg) {
+  const int seg = blockIdx.x, bq = blockIdx.y;
+  const int b = bq / n_q, i = bq % n_q, g = i / tile_q, tiles = n_q / tile_q;
+  const QueryGeom qg = query_geom(ctx_len, top_cnt, cap, b, i, g, tiles, n_q, k_top, window);
+  const int s0 = seg * kSegB;
+  float2* mlo = ml + ((size_t)bq * nseg + seg) * H;
+  if (s0 >= qg.S) {
+    if (threadIdx.x < H) mlo[threadIdx.x] = make_float2(-INFINITY, 0.f);
+    return;
+  }
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int r32 = lane & 31, hh = lane >> 5;
+  const int32_t* top_row = top_idx + (size_t)(b * tiles + g) * k_top;
+  const int pw = s0 + 32 * wave;  // first selection position of this wave
+  const bool wave_live = pw < qg.S;
+  const int idx = (pw + r32 < qg.S) ? sel_key(qg, top_row, pw + r32) : sel_key(qg, top_row, s0);
+  const size_t rowoff = (size_t)b * kv_stride + (size_t)idx * kHeadDim;
+
+  __shared__ uint16_t vt[kSegWaves][kHeadDim][kVtPitch];
+  __shared__ float s_m[kSegWaves][32], s_l[kSegWaves][32];
+  __shared__ float s_o[kSegWaves][32][kHeadDim + 4];
+
+  // Gathered K (A operand) and V rows; Q^T as the B operand.
+  u32x4 kr[8], vr[8];
+  const u32x4* kp = reinterpret_cast<const u32x4*>(k + rowoff + 8 * hh);
+  const u32x4* vp = reinterpret_cast<const u32x4*>(v + rowoff + 64 * hh);
 #pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const u32x4 v = s[i];
+  for (int e = 0; e < 8; ++e) {
+    kr[e] = kp[2 * e];
+    vr[e] = vp[e];
+  }
+  bf16x8_t qreg[8];
+  const uint16_t* qb = q + (size_t)bq * H * kHeadDim;
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      dst[8 * i + 2 * e] = __uint_as_float(v[e] << 16);
-      dst[8 * i + 2 * e + 1] = __uint_as_float(v[e] & 0xFFFF0000u);
+  for (int e = 0; e < 8; ++e) {
+    u32x4 x = {0u, 0u, 0u, 0u};
+    if (r32 < H) x = *reinterpret_cast<const u32x4*>(qb + r32 * kHeadDim + 16 * e + 8 * hh);
+    qreg[e] = as_bf16x8(x);
+  }
+  // V transposed into LDS: vt[wave][d][key], key = r32, d = 64*hh + 8*e + j.
+#pragma unroll
+  for (int e = 0; e < 8; ++e)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      vt[wave][64 * hh + 8 * e + 2 * j][r32] = (uint16_t)(vr[e][j] & 0xFFFFu);
+      vt[wave][64 * hh + 8 * e + 2 * j + 1][r32] = (uint16_t)(vr[e][j] >> 16);
+    }
+
+  f32x16_t acc = {};
+#pragma unroll
+  for (int e = 0; e < 8; ++e)
+    acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(kr[e]), qreg[e], acc, 0, 0, 0);
+  // acc[r]: head r32, key 8*(r/4) + 4*hh + r%4 of this wave's 32.
+  float x[16];
+  float m = -INFINITY;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    const int key = 8 * (r >> 2) + 4 * hh + (r & 3);
+    x[r] = (pw + key < qg.S) ? acc[r] * c2 : -INFINITY;
+    m = fmaxf(m, x[r]);
+  }
+  m = fmaxf(m, __shfl_xor(m, 32));
+  const float mref = (m == -INFINITY) ? 0.f : m;
+  float l = 0.f;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    x[r] = fast_exp2(x[r] - mref);
+    l += x[r];
+  }
+  l += __shfl_xor(l, 32);
+  if (hh == 0) {
+    s_m[wave][r32] = wave_live ? m : -INFINITY;
+    s_l[wave][r32] = wave_live ? l : 0.f;
+  }
+  __syncthreads();
+
+  // P V for this wave's 32 keys: k-step s covers the keys of registers
+  // 8s..8s+7, i.e. {16s + 4hh + 0..3} and {16s + 8 + 4hh + 0..3}.
+  f32x16_t o[4] = {{}, {}, {}, {}};
+#pragma unroll
+  for (int s = 0; s < 2; ++s) {
+    u32x4 ahi, alo;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const float p0 = x[8 * s + 2 * j], p1 = x[8 * s + 2 * j + 1];
+      const uint16_t h0 = f32_to_bf16_rne(p0), h1 = f32_to_bf16_rne(p1);
+      const uint16_t l0 = f32_to_bf16_rne(p0 - bf16_to_f32(h0));
+      const uint16_t l1 = f32_to_bf16_rne(p1 - bf16_to_f32(h1));
+      ahi[j] = (uint32_t)h0 | ((uint32_t)h1 << 16);
+      alo[j] = (uint32_t)l0 | ((uint32_t)l1 << 16);
+    }
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const uint16_t* row = &vt[wave][32 * t + r32][0];
+      const uint2 lo4 = *reinterpret_cast<const uint2*>(row + 16 * s + 4 * hh);
+      const uint2 hi4 = *reinterpret_cast<const uint2*>(row + 16 * s + 8 + 4 * hh);
+      const u32x4 bv = {lo4.x, lo4.y, hi4.x, hi4.y};
+      o[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(ahi), as_bf16x8(bv), o[t], 0, 0, 0);
+      o[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(alo), as_bf16x8(bv), o[t], 0, 0, 0);
     }
   }
+  // o[t][r]: head 8*(r/4) + 4*hh + r%4, dim 32*t + r32, relative to this
+  // wave's max; rescale to the workgroup max and stage for the merge.
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    const int h = 8 * (r >> 2) + 4 * hh + (r & 3);
+    float M = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < kSegWaves; ++w) M = fmaxf(M, s_m[w][h]);
+    const float mw = s_m[wave][h];
+    const float sc = (mw == -INFINITY) ? 0.f : fast_exp2(mw - M);
+#pragma unroll
+    for (int t = 0; t < 4; ++t) s_o[wave][h][32 * t + r32] = o[t][r] * sc;
+  }
+  __syncthreads();
+  // Merge the waves in order.
+  float* po = part + ((size_t)bq * nseg + seg) * H * kHeadDim;
+  for (int e = threadIdx.x; e < 32 * kHeadDim; e += blockDim.x) {
+    const int h = e / kHeadDim, d = e % kHeadDim;
+    if (h >= H) continue;
+    float acc_o = 0.f;
+#pragma unroll
+    for (int w = 0; w < kSegWaves; ++w) acc_o += s_o[w][h][d];
+    po[(size_t)h * kHeadDim + d] = acc_o;
+  }
+  if (threadIdx.x < H) {
+    const int h = threadIdx.x;
+    float M = -INFINITY;
+    for (int w = 0; w < kSegWaves; ++w) M = fmaxf(M, s_m[w][h]);
+    float L = 0.f;
+    for (int w = 0; w < kSegWaves; ++w)
+      if (s_m[w][h] != -INFINITY) L += s_l[w][h] * fast_exp2(s_m[w][h] - M);
+    mlo[h] = make_float2(M, L);
+  }
 }
 
-constexpr int kSeg = kSparseSeg;   // keys per workgroup
+// ---------------------------------------------------------------------------
+// fp32, VALU.
+
+constexpr int kSegF = kSparseSeg;     // keys per workgroup
 constexpr int kKPitch = kHeadDim + 4;  // LDS row pitch of K (bank spread)
 
-template <typename T>
-__global__ __launch_bounds__(256) void sparse_partial(
-    const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v, int64_t kv_stride,
-    const int32_t* __restrict__ ctx_len, int cap, const int32_t* __restrict__ top_idx,
-    const int32_t* __restrict__ top_cnt, int n_q, int tile_q, int k_top, int window, int H,
-    float sm_scale, float* __restrict__ part, float2* __restrict__ ml, int nseg) {
-  const int seg = blockIdx.x;
-  const int bq = blockIdx.y;
-  const int b = bq / n_q, i = bq % n_q, g = i / tile_q;
-  const int tiles = n_q / tile_q;
+__global__ __launch_bounds__(256) void sparse_partial_f32(
+    const float* __restrict__ q, const float* __restrict__ k, const float* __restrict__ v,
+    int64_t kv_stride, const int32_t* __restrict__ ctx_len, int cap,
+    const int32_t* __restrict__ top_idx, const int32_t* __restrict__ top_cnt, int n_q, int tile_q,
+    int k_top, int window, int H, float c2, float* __restrict__ part, float2* __restrict__ ml,
+    int nseg) {
+  const int seg = blockIdx.x, bq = blockIdx.y;
+  const int b = bq / n_q, i = bq % n_q, g = i / tile_q, tiles = n_q / tile_q;
   const int t = threadIdx.x;
-  const int N = clamp_ctx(ctx_len, b, cap);
-  const int P = N - n_q + i;
-  int cnt = 0, wlo = 0, wcnt = 0;
-  if (P >= 0) {
-    cnt = top_cnt[b * tiles + g];
-    cnt = cnt < 0 ? 0 : (cnt > k_top ? k_top : cnt);
-    wlo = max(0, P - window + 1);
-    wcnt = P - wlo + 1;
-  }
-  const int S = cnt + wcnt;
-  const int s0 = seg * kSeg;
+  const QueryGeom qg = query_geom(ctx_len, top_cnt, cap, b, i, g, tiles, n_q, k_top, window);
+  const int s0 = seg * kSegF;
   float2* mlo = ml + ((size_t)bq * nseg + seg) * H;
-  if (s0 >= S) {
+  if (s0 >= qg.S) {
     if (t < H) mlo[t] = make_float2(-INFINITY, 0.f);
     return;
   }
-  const int nk = min(kSeg, S - s0);
-
+  const int nk = min(kSegF, qg.S - s0);
   __shared__ float qs[kMaxHeads][kHeadDim];
-  __shared__ float ks[kSeg][kKPitch];
-  __shared__ float vs[kSeg][kHeadDim];
-  __shared__ float ps[kSeg][kMaxHeads];
-  __shared__ int kidx[kSeg];
-
-  if (t < kSeg) {
-    int idx = 0;
-    if (t < nk) {
-      const int p = s0 + t;
-      idx = p < cnt ? top_idx[(size_t)(b * tiles + g) * k_top + p] : wlo + (p - cnt);
-      idx = idx < 0 ? 0 : (idx >= N ? N - 1 : idx);  // memory safety only
-    }
-    kidx[t] = idx;
-  }
-  const T* qb = q + (size_t)bq * H * kHeadDim;
-  for (int e = t; e < kMaxHeads * kHeadDim / 16; e += blockDim.x) {
-    const int h = e / (kHeadDim / 16), c = (e % (kHeadDim / 16)) * 16;
-    float tmp[16];
-    if (h < H) {
-      load16<T>(qb + h * kHeadDim + c, tmp);
-    } else {
-#pragma unroll
-      for (int x = 0; x < 16; ++x) tmp[x] = 0.f;
-    }
-#pragma unroll
-    for (int x = 0; x < 16; ++x) qs[h][c + x] = tmp[x];
+  __shared__ float ks[kSegF][kKPitch];
+  __shared__ float vs[kSegF][kHeadDim];
+  __shared__ float ps[kSegF][kMaxHeads];
+  __shared__ int kidx[kSegF];
+  const int32_t* top_row = top_idx + (size_t)(b * tiles + g) * k_top;
+  if (t < kSegF) kidx[t] = sel_key(qg, top_row, s0 + (t < nk ? t : 0));
+  const float* qb = q + (size_t)bq * H * kHeadDim;
+  for (int e = t; e < kMaxHeads * kHeadDim / 4; e += blockDim.x) {
+    const int h = e / (kHeadDim / 4), c = (e % (kHeadDim / 4)) * 4;
+    const float4 qv = h < H ? *reinterpret_cast<const float4*>(qb + h * kHeadDim + c)
+                            : make_float4(0.f, 0.f, 0.f, 0.f);
+    *reinterpret_cast<float4*>(&qs[h][c]) = qv;
   }
   __syncthreads();
-  // Gather K and V rows: 32 rows x 8 pieces of 16 elements = 256 pieces each.
   {
     const int row = t >> 3, c = (t & 7) * 16;
-    float tk[16], tv[16];
     const size_t off = (size_t)b * kv_stride + (size_t)kidx[row] * kHeadDim + c;
-    load16<T>(k + off, tk);
-    load16<T>(v + off, tv);
 #pragma unroll
-    for (int x = 0; x < 16; ++x) {
-      ks[row][c + x] = tk[x];
-      vs[row][c + x] = tv[x];
+    for (int x4 = 0; x4 < 4; ++x4) {
+      *reinterpret_cast<float4*>(&ks[row][c + 4 * x4]) = reinterpret_cast<const float4*>(k + off)[x4];
+      *reinterpret_cast<float4*>(&vs[row][c + 4 * x4]) = reinterpret_cast<const float4*>(v + off)[x4];
     }
   }
   __syncthreads();
-  // Logits: thread (key kx, heads hg, hg+8, hg+16, hg+24).
   {
     const int kx = t & 31, hg = t >> 5;
     float acc[4] = {0.f, 0.f, 0.f, 0.f};
@@ -145,23 +276,21 @@ __global__ __launch_bounds__(256) void sparse_partial(
       }
     }
 #pragma unroll
-    for (int u = 0; u < 4; ++u) ps[kx][hg + 8 * u] = (kx < nk) ? acc[u] * sm_scale : -INFINITY;
+    for (int u = 0; u < 4; ++u) ps[kx][hg + 8 * u] = (kx < nk) ? acc[u] * c2 : -INFINITY;
   }
   __syncthreads();
-  // Segment-local softmax per head.
   if (t < kMaxHeads) {
     float m = -INFINITY;
     for (int x = 0; x < nk; ++x) m = fmaxf(m, ps[x][t]);
     float l = 0.f;
-    for (int x = 0; x < kSeg; ++x) {
-      const float p = (x < nk) ? __expf(ps[x][t] - m) : 0.f;
+    for (int x = 0; x < kSegF; ++x) {
+      const float p = (x < nk) ? fast_exp2(ps[x][t] - m) : 0.f;
       ps[x][t] = p;
       l += p;
     }
     if (t < H) mlo[t] = make_float2(m, l);
   }
   __syncthreads();
-  // P V: thread (dim d, heads 16*hh .. 16*hh+15).
   {
     const int d = t & (kHeadDim - 1), hh = t >> 7;
     float o[16];
@@ -178,7 +307,7 @@ __global__ __launch_bounds__(256) void sparse_partial(
         o[u + 3] = fmaf(p.w, vx, o[u + 3]);
       }
     }
-    float* po = part + (((size_t)bq * nseg + seg) * H) * kHeadDim;
+    float* po = part + ((size_t)bq * nseg + seg) * H * kHeadDim;
 #pragma unroll
     for (int u = 0; u < 16; ++u) {
       const int h = 16 * hh + u;
@@ -187,33 +316,38 @@ __global__ __launch_bounds__(256) void sparse_partial(
   }
 }
 
-// Merge the segment partials of each query: o = sum_s e^(m_s-M) o_s / sum_s e^(m_s-M) l_s.
-__global__ __launch_bounds__(256) void sparse_combine(const float* __restrict__ part,
-                                                      const float2* __restrict__ ml, int nseg,
-                                                      int H, float* __restrict__ o,
-                                                      float* __restrict__ lse) {
-  const int bq = blockIdx.x;
-  const int d = threadIdx.x & (kHeadDim - 1), hh = threadIdx.x >> 7;
-  const float2* mlq = ml + (size_t)bq * nseg * H;
-  const float* pq = part + (size_t)bq * nseg * H * kHeadDim;
-  for (int h = hh; h < H; h += 2) {
-    float M = -INFINITY;
-    for (int s = 0; s < nseg; ++s) {
-      const float2 x = mlq[(size_t)s * H + h];
-      if (x.y > 0.f) M = fmaxf(M, x.x);
-    }
-    float den = 0.f, num = 0.f;
-    for (int s = 0; s < nseg; ++s) {
-      const float2 x = mlq[(size_t)s * H + h];
-      if (x.y > 0.f) {
-        const float w = __expf(x.x - M);
-        den = fmaf(w, x.y, den);
-        num = fmaf(w, pq[((size_t)s * H + h) * kHeadDim + d], num);
-      }
-    }
-    o[((size_t)bq * H + h) * kHeadDim + d] = den > 0.f ? num / den : 0.f;
-    if (lse != nullptr && d == 0) lse[(size_t)bq * H + h] = den > 0.f ? M + __logf(den) : -INFINITY;
+// ---------------------------------------------------------------------------
+// Merge the segment partials of one (query, head): o = sum_s 2^(m_s-M) o_s /
+// sum_s 2^(m_s-M) l_s, segments taken in order.  One workgroup per (query,
+// head), one thread per output dimension.
+__global__ __launch_bounds__(kHeadDim) void sparse_combine(const float* __restrict__ part,
+                                                           const float2* __restrict__ ml, int nseg,
+                                                           int H, float* __restrict__ o,
+                                                           float* __restrict__ lse) {
+  const int h = blockIdx.x, bq = blockIdx.y, d = threadIdx.x;
+  const float2* mlq = ml + (size_t)bq * nseg * H + h;
+  const float* pq = part + ((size_t)bq * nseg * H + h) * kHeadDim + d;
+  float M = -INFINITY;
+  for (int s = 0; s < nseg; ++s) {
+    const float2 x = mlq[(size_t)s * H];
+    if (x.y > 0.f) M = fmaxf(M, x.x);
   }
+  // Loads are unconditional so that they can be issued together; a segment
+  // with no keys (l == 0) has no partial output written, and is masked by a
+  // select, never multiplied (its memory may hold anything).
+  float den = 0.f, num = 0.f;
+#pragma unroll 8
+  for (int s = 0; s < nseg; ++s) {
+    const float2 x = mlq[(size_t)s * H];
+    const float pv = pq[(size_t)s * H * kHeadDim];
+    const bool live = x.y > 0.f;
+    const float w = live ? fast_exp2(x.x - M) : 0.f;
+    den = fmaf(w, live ? x.y : 0.f, den);
+    num = live ? fmaf(w, pv, num) : num;
+  }
+  o[((size_t)bq * H + h) * kHeadDim + d] = den > 0.f ? num / den : 0.f;
+  if (lse != nullptr && d == 0)
+    lse[(size_t)bq * H + h] = den > 0.f ? (M + __log2f(den)) * kLn2 : -INFINITY;
 }
 
 }  // namespace
@@ -225,21 +359,24 @@ hipError_t launch_sparse(const hs2_attn_desc& d, const void* q, const void* k, c
   const SparseWs w = sparse_ws(d);
   float* part = reinterpret_cast<float*>(ws + w.part_off);
   float2* ml = reinterpret_cast<float2*>(ws + w.ml_off);
-  int nseg = sparse_segments(d);
-  if (nseg < 1) nseg = 1;
-  const dim3 grid(nseg, d.batch * d.n_q);
+  const float c2 = d.sm_scale * kLog2e;
+  const int sel_max = d.k_top + d.window;
+  int nseg;
   if (d.dtype == HS2_BF16) {
-    sparse_partial<uint16_t><<<grid, 256, 0, st>>>(
+    nseg = sel_max > 0 ? (sel_max + kSegB - 1) / kSegB : 1;
+    sparse_partial_bf16<<<dim3(nseg, d.batch * d.n_q), 64 * kSegWaves, 0, st>>>(
         static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
         static_cast<const uint16_t*>(v), kv_stride, ctx_len, cap, top_idx, top_cnt, d.n_q,
-        d.tile_q, d.k_top, d.window, d.n_heads, d.sm_scale, part, ml, nseg);
+        d.tile_q, d.k_top, d.window, d.n_heads, c2, part, ml, nseg);
   } else {
-    sparse_partial<float><<<grid, 256, 0, st>>>(
+    nseg = sparse_segments(d);
+    sparse_partial_f32<<<dim3(nseg, d.batch * d.n_q), 256, 0, st>>>(
         static_cast<const float*>(q), static_cast<const float*>(k), static_cast<const float*>(v),
         kv_stride, ctx_len, cap, top_idx, top_cnt, d.n_q, d.tile_q, d.k_top, d.window,
-        d.n_heads, d.sm_scale, part, ml, nseg);
+        d.n_heads, c2, part, ml, nseg);
   }
-  sparse_combine<<<d.batch * d.n_q, 256, 0, st>>>(part, ml, nseg, d.n_heads, o, lse);
+  sparse_combine<<<dim3(d.n_heads, d.batch * d.n_q), kHeadDim, 0, st>>>(part, ml, nseg,
+                                                                        d.n_heads, o, lse);
   return hipGetLastError();
 }
 

@@ -11,8 +11,8 @@ import dataclasses
 import numpy as np
 import torch
 
-from . import (HS2_BF16, HS2_F32, hs2_attn_desc, hs2_full_attn_scores, hs2_select_topk_window,
-               hs2_sparse_attn_gather, hs2_workspace_size, make_desc)
+from . import (HS2_BF16, HS2_F32, hs2_attn_desc, hs2_decode_step, hs2_full_attn_scores,
+               hs2_select_topk_window, hs2_sparse_attn_gather, hs2_workspace_size, make_desc)
 
 
 def to_device(arr: np.ndarray, device="cuda") -> torch.Tensor:
@@ -96,7 +96,14 @@ def run_sparse(buf: DecodeBuffers, q: torch.Tensor | None = None, top_idx=None, 
 
 
 def run_step(buf: DecodeBuffers, stream=None) -> None:
-    """One pass of the hot path: full-layer scoring, selection, sparse layer."""
+    """One pass of the hot path as three calls: scoring, selection, sparse layer."""
     run_scores(buf, stream)
     run_select(buf, stream=stream)
     run_sparse(buf, stream=stream)
+
+
+def run_fused_step(buf: DecodeBuffers, q_sparse: torch.Tensor | None = None, stream=None) -> None:
+    """One pass of the hot path through the single-call entry point."""
+    hs2_decode_step(buf.desc, buf.q, q_sparse, buf.k, buf.v, buf.kv_stride, buf.ctx_len, buf.cap,
+                    buf.scores, buf.lse_full, buf.top_idx, buf.top_cnt, buf.o, buf.lse, buf.ws,
+                    stream)

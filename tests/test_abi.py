@@ -138,6 +138,25 @@ def test_select_and_sparse_validation(lib):
     assert sp(nb=0) == hs2.HS2_EWORKSPACE
 
 
+def test_decode_step_validation(lib):
+    d = _desc()
+    L = hs2.load()
+    need = hs2.hs2_workspace_size(d, 4096)
+    st = lambda **kw: L.hs2_decode_step(  # noqa: E731
+        ctypes.byref(d), kw.get("q", FAKE), kw.get("q2", None), FAKE, kw.get("v", FAKE),
+        kw.get("st", 4096 * 128), FAKE, kw.get("cap", 4096), kw.get("sc", FAKE), None,
+        kw.get("ti", FAKE), FAKE, kw.get("o", FAKE), None, FAKE, kw.get("nb", need), None)
+    assert st(v=None) == hs2.HS2_EINVAL
+    assert st(sc=None) == hs2.HS2_EINVAL
+    assert st(o=None) == hs2.HS2_EINVAL
+    assert st(ti=None) == hs2.HS2_EINVAL
+    assert st(q2=ODD) == hs2.HS2_EALIGN
+    assert st(nb=need - 1) == hs2.HS2_EWORKSPACE
+    big = (1 << 22) + 1
+    assert st(cap=big, st=big * 128) == hs2.HS2_EUNSUPPORTED
+    assert hs2.hs2_workspace_size(d, big) == 0
+
+
 def test_bridge_validation(lib):
     L = hs2.load()
     br = lambda **kw: L.hs2_bridge_kv(  # noqa: E731

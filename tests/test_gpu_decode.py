@@ -233,3 +233,47 @@ def test_step_is_deterministic(hs2):
         outs.append((buf.scores.clone(), buf.top_idx.clone(), buf.o.clone()))
     for s, t, o in outs[1:]:
         assert torch.equal(s, outs[0][0]) and torch.equal(t, outs[0][1]) and torch.equal(o, outs[0][2])
+
+
+@pytest.mark.parametrize("name,wname,over,ctx", CASES, ids=[c[0] for c in CASES])
+def test_fused_step_equals_three_calls(hs2, name, wname, over, ctx):
+    # hs2_decode_step must give bit-for-bit the outputs of the three calls.
+    from kv_cache_reuse_hs2_amd.torch_api import run_fused_step, run_step
+
+    w = WORKLOADS[wname].replace(**over)
+    inp = make_decode_inputs(w, ctx_lens=ctx, capacity=max(ctx))
+    buf = _buffers(hs2, inp, w)
+    _say(f"fused vs three calls {name} ctx={ctx}")
+    run_step(buf)
+    torch.cuda.synchronize()
+    ref = [t.clone() for t in (buf.scores, buf.top_idx, buf.top_cnt, buf.o, buf.lse, buf.lse_full)]
+    for t in (buf.scores, buf.top_idx, buf.top_cnt, buf.o, buf.lse, buf.lse_full):
+        t.fill_(7)
+    run_fused_step(buf)
+    torch.cuda.synchronize()
+    got = (buf.scores, buf.top_idx, buf.top_cnt, buf.o, buf.lse, buf.lse_full)
+    for b, n in enumerate(ctx):  # scores beyond a sequence's context are not written
+        assert torch.equal(ref[0][b, :, :n], got[0][b, :, :n])
+    for a, b in zip(ref[1:], got[1:]):
+        assert torch.equal(a, b)
+
+
+def test_fused_step_with_own_sparse_query(hs2):
+    from kv_cache_reuse_hs2_amd.torch_api import run_fused_step, to_device
+
+    w = WORKLOADS["decode_bf16_256k_b4"].replace(batch=2)
+    inp = make_decode_inputs(w, ctx_lens=[12000, 7000], capacity=12000)
+    q2 = make_decode_inputs(w, seed=w.seed + 1, ctx_lens=[12000, 7000], capacity=12000)
+    buf = _buffers(hs2, inp, w)
+    _say("fused step with q_sparse")
+    run_fused_step(buf, q_sparse=to_device(q2["q_raw"]))
+    torch.cuda.synchronize()
+    tg, cg = buf.top_idx.cpu().numpy(), buf.top_cnt.cpu().numpy()
+    ref, _, _ = _oracle_scores(inp, w)
+    top, cnt = oracle.select_topk_window(ref, inp["ctx_len"], n_q=1, tile_q=1, k_top=w.k_top,
+                                         window=w.window)
+    assert_selection_near_ties(tg, cg, top, cnt, ref, inp["ctx_len"], n_q=1, tile_q=1,
+                               window=w.window)
+    o_ref, _ = oracle.sparse_attention(q2["q"], inp["k"], inp["v"], inp["ctx_len"], tg, cg,
+                                       tile_q=1, window=w.window, sm_scale=w.sm_scale)
+    assert_outputs_close(buf.o.cpu().numpy(), o_ref, "bf16")
