@@ -28,9 +28,11 @@ hs2_status check_desc(const hs2_attn_desc* d) {
   if (d->head_dim != kHeadDim || d->n_heads > kMaxHeads) return HS2_EUNSUPPORTED;
   if (d->k_top > kMaxTop || d->window > kMaxWindow) return HS2_EUNSUPPORTED;
   if (d->causal != 1) return HS2_EUNSUPPORTED;
-  // Decode: one query per sequence.  (Query groups of 64 are the prefill layout.)
+  // Decode: one query per sequence.  Chunked prefill: bf16, query tiles of a
+  // multiple of 16 queries (the kernels work on blocks of 16 queries).
   const bool decode = d->n_q == 1 && d->tile_q == 1;
-  if (!decode) return HS2_EUNSUPPORTED;
+  const bool prefill = d->tile_q > 1 && d->tile_q % 16 == 0 && d->dtype == HS2_BF16;
+  if (!decode && !prefill) return HS2_EUNSUPPORTED;
   return HS2_OK;
 }
 
@@ -85,6 +87,10 @@ hs2_status hs2_full_attn_scores(const hs2_attn_desc* desc, const void* q, const 
   if ((s = check_ws(*desc, kv_capacity, ws, ws_bytes)) != HS2_OK) return s;
   (void)hipGetLastError();
   const WsLayout l = ws_layout(*desc, kv_capacity);
+  if (is_prefill(*desc))
+    return launched(launch_prefill_scores(*desc, q, k, kv_stride, ctx_len, kv_capacity, scores,
+                                          lse, static_cast<char*>(ws) + l.score, false,
+                                          static_cast<hipStream_t>(stream)));
   return launched(launch_score_decode(*desc, q, k, kv_stride, ctx_len, kv_capacity, scores, lse,
                                       static_cast<char*>(ws) + l.score, false,
                                       static_cast<hipStream_t>(stream)));
@@ -128,6 +134,9 @@ hs2_status hs2_sparse_attn_gather(const hs2_attn_desc* desc, const void* q, cons
   if ((s = check_ws(*desc, kv_capacity, ws, ws_bytes)) != HS2_OK) return s;
   (void)hipGetLastError();
   const WsLayout l = ws_layout(*desc, kv_capacity);
+  if (is_prefill(*desc))
+    return launched(launch_prefill_sparse(*desc, q, k, v, kv_stride, ctx_len, kv_capacity, top_idx,
+                                          top_cnt, o, lse, static_cast<hipStream_t>(stream)));
   return launched(launch_sparse(*desc, q, k, v, kv_stride, ctx_len, kv_capacity, top_idx, top_cnt,
                                 o, lse, static_cast<char*>(ws) + l.sparse,
                                 static_cast<hipStream_t>(stream)));
@@ -157,14 +166,21 @@ hs2_status hs2_decode_step(const hs2_attn_desc* desc, const void* q, const void*
   hipStream_t st = static_cast<hipStream_t>(stream);
   // bf16: the scoring pass also builds the selector's histogram.
   const bool fuse = desc->dtype == HS2_BF16;
-  hipError_t e = launch_score_decode(*desc, q, k, kv_stride, ctx_len, kv_capacity, scores,
-                                     lse_full, w + l.score, fuse, st);
+  const bool pf = is_prefill(*desc);
+  hipError_t e =
+      pf ? launch_prefill_scores(*desc, q, k, kv_stride, ctx_len, kv_capacity, scores, lse_full,
+                                 w + l.score, fuse, st)
+         : launch_score_decode(*desc, q, k, kv_stride, ctx_len, kv_capacity, scores, lse_full,
+                               w + l.score, fuse, st);
   if (e != hipSuccess) return HS2_EHIP;
-  const uint32_t* hist =
-      fuse ? reinterpret_cast<const uint32_t*>(w + l.score + score_ws(*desc, kv_capacity).hist_off)
-           : nullptr;
+  const size_t hist_off = pf ? prefill_ws(*desc, kv_capacity).hist_off
+                             : score_ws(*desc, kv_capacity).hist_off;
+  const uint32_t* hist = fuse ? reinterpret_cast<const uint32_t*>(w + l.score + hist_off) : nullptr;
   e = launch_select(*desc, scores, ctx_len, kv_capacity, top_idx, top_cnt, w + l.select, hist, st);
   if (e != hipSuccess) return HS2_EHIP;
+  if (pf)
+    return launched(launch_prefill_sparse(*desc, q_sparse, k, v, kv_stride, ctx_len, kv_capacity,
+                                          top_idx, top_cnt, o, lse, st));
   return launched(launch_sparse(*desc, q_sparse, k, v, kv_stride, ctx_len, kv_capacity, top_idx,
                                 top_cnt, o, lse, w + l.sparse, st));
 }

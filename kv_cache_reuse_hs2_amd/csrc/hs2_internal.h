@@ -19,6 +19,8 @@ constexpr int kMaxWindow = 2048;
 constexpr int kP1Chunk = 4096;
 constexpr int kP2Chunk = 4096;
 constexpr int kF32Chunk = 256;
+// Chunked prefill: keys per workgroup of the scoring passes.
+constexpr int kPfSplit = 8192;
 // Keys per workgroup of the sparse gather kernel.
 constexpr int kSparseSeg = 32;
 // Top-k selection: first radix digit = top 12 bits of the orderable key.
@@ -90,6 +92,29 @@ struct SparseWs {
   size_t bytes;
 };
 
+inline bool is_prefill(const hs2_attn_desc& d) { return d.tile_q > 1; }
+
+struct PrefillWs {
+  size_t stats_off;   // float2 [B][nsplit][n_q][32]
+  size_t colsum_off;  // float  [B][n_q/16][cap]
+  size_t hist_off;    // uint32 [B][tiles][kSelBins]
+  size_t bytes;
+};
+
+inline PrefillWs prefill_ws(const hs2_attn_desc& d, int cap) {
+  PrefillWs w{};
+  const size_t nsplit = (cap + kPfSplit - 1) / kPfSplit;
+  size_t off = 0;
+  w.stats_off = off;
+  off = align_up(off + sizeof(float) * 2 * (size_t)d.batch * nsplit * d.n_q * 32, 256);
+  w.colsum_off = off;
+  off = align_up(off + sizeof(float) * (size_t)d.batch * (d.n_q / 16) * cap, 256);
+  w.hist_off = off;
+  off = align_up(off + sizeof(uint32_t) * (size_t)d.batch * (d.n_q / d.tile_q) * kSelBins, 256);
+  w.bytes = off;
+  return w;
+}
+
 inline ScoreWs score_ws(const hs2_attn_desc& d, int cap) {
   ScoreWs w{};
   size_t off = 0;
@@ -146,7 +171,7 @@ struct WsLayout {
 inline WsLayout ws_layout(const hs2_attn_desc& d, int cap) {
   WsLayout l{};
   l.score = 0;
-  l.select = align_up(score_ws(d, cap).bytes, 256);
+  l.select = align_up(is_prefill(d) ? prefill_ws(d, cap).bytes : score_ws(d, cap).bytes, 256);
   l.sparse = align_up(l.select + select_ws(d, cap).bytes, 256);
   l.bytes = align_up(l.sparse + sparse_ws(d).bytes, 256);
   return l;
@@ -168,6 +193,17 @@ hipError_t launch_score_decode(const hs2_attn_desc& d, const void* q, const void
 hipError_t launch_select(const hs2_attn_desc& d, const float* scores, const int32_t* ctx_len,
                          int cap, int32_t* top_idx, int32_t* top_cnt, char* ws,
                          const uint32_t* hist, hipStream_t st);
+
+// Chunked prefill (tile_q > 1, bf16): scoring over query tiles and sparse
+// attention of the tiles' queries.
+hipError_t launch_prefill_scores(const hs2_attn_desc& d, const void* q, const void* k,
+                                 int64_t kv_stride, const int32_t* ctx_len, int cap,
+                                 float* scores, float* lse, char* ws, bool with_hist,
+                                 hipStream_t st);
+hipError_t launch_prefill_sparse(const hs2_attn_desc& d, const void* q, const void* k,
+                                 const void* v, int64_t kv_stride, const int32_t* ctx_len,
+                                 int cap, const int32_t* top_idx, const int32_t* top_cnt,
+                                 float* o, float* lse, hipStream_t st);
 
 hipError_t launch_sparse(const hs2_attn_desc& d, const void* q, const void* k, const void* v,
                          int64_t kv_stride, const int32_t* ctx_len, int cap,

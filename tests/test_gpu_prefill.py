@@ -1,0 +1,137 @@
+"""GPU parity of the chunked-prefill path (query tiles) against the oracle.
+
+Small shapes cover several 8,192-key splits, several tiles, ragged batches,
+padded heads, tiles of 16/32/64 queries and queries that sit before the start
+of the cache.  The 8,192-query prefill over a 131,072-token cache is checked
+on a seeded sample of tiles: the oracle evaluates a tile alone by giving it
+the context that ends at the tile's last query (the tile's queries see exactly
+those keys).
+"""
+
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from gpu_helpers import (assert_outputs_close, assert_scores_close,
+                         assert_selection_near_ties)
+from workloads import WORKLOADS, make_prefill_inputs
+
+pytestmark = pytest.mark.gpu
+
+
+def _say(msg):
+    print(f"[gpu] {msg}", flush=True)
+    sys.stdout.flush()
+
+
+def _run(inp, w, n_q, tile_q, *, fused=False):
+    from kv_cache_reuse_hs2_amd.torch_api import make_buffers, run_fused_step, run_step
+
+    buf = make_buffers(inp, n_heads=w.n_heads, k_top=w.k_top, window=w.window,
+                       sm_scale=w.sm_scale, dtype="bf16", n_q=n_q, tile_q=tile_q)
+    (run_fused_step if fused else run_step)(buf)
+    torch.cuda.synchronize()
+    return buf
+
+
+CASES = [
+    # name, batch, heads, ctx_lens, capacity, n_q, tile_q
+    ("one_tile", 1, 32, [1200], 1200, 64, 64),
+    ("two_tiles_splits", 1, 32, [20000], 20000, 128, 64),
+    ("ragged_batch", 2, 32, [9000, 5000], 9000, 64, 64),
+    ("heads7_tile16", 1, 7, [4000], 4000, 64, 16),
+    ("tile32", 2, 32, [3100, 2600], 3100, 96, 32),
+    ("before_cache_start", 1, 32, [40], 64, 64, 64),
+    ("small_pool", 1, 32, [300], 300, 64, 64),
+]
+
+
+@pytest.mark.parametrize("name,bsz,heads,ctx,cap,n_q,tile_q", CASES, ids=[c[0] for c in CASES])
+def test_prefill_matches_oracle(hs2, name, bsz, heads, ctx, cap, n_q, tile_q):
+    w = WORKLOADS["prefill_bf16_128k_8k"].replace(batch=bsz, n_heads=heads)
+    inp = make_prefill_inputs(w, ctx_lens=ctx, n_q=n_q, capacity=cap)
+    _say(f"prefill {name} ctx={ctx} n_q={n_q} tile={tile_q} H={heads}")
+    buf = _run(inp, w, n_q, tile_q)
+    scores = buf.scores.cpu().numpy()
+    ref, _, lse = oracle.full_attn_scores(inp["q"], inp["k"], inp["ctx_len"], tile_q=tile_q,
+                                          sm_scale=w.sm_scale)
+    assert_scores_close(scores, ref, inp["ctx_len"])
+    got_lse = buf.lse_full.cpu().numpy()
+    fin = np.isfinite(lse)
+    np.testing.assert_allclose(got_lse[fin], lse[fin], rtol=1e-5, atol=1e-5)
+    assert np.all(np.isneginf(got_lse[~fin]))
+    # selection on the GPU's scores vs the oracle's (near-ties only)
+    top, cnt = oracle.select_topk_window(ref, inp["ctx_len"], n_q=n_q, tile_q=tile_q,
+                                         k_top=w.k_top, window=w.window)
+    tg, cg = buf.top_idx.cpu().numpy(), buf.top_cnt.cpu().numpy()
+    assert_selection_near_ties(tg, cg, top, cnt, ref, inp["ctx_len"], n_q=n_q, tile_q=tile_q,
+                               window=w.window)
+    o_ref, lse_ref = oracle.sparse_attention(inp["q"], inp["k"], inp["v"], inp["ctx_len"], tg, cg,
+                                             tile_q=tile_q, window=w.window, sm_scale=w.sm_scale)
+    assert_outputs_close(buf.o.cpu().numpy(), o_ref, "bf16")
+    fin = np.isfinite(lse_ref)
+    np.testing.assert_allclose(buf.lse.cpu().numpy()[fin], lse_ref[fin], rtol=1e-5, atol=1e-5)
+
+
+def test_prefill_select_bit_exact_on_oracle_scores(hs2):
+    from kv_cache_reuse_hs2_amd.torch_api import make_buffers, run_select, to_device
+
+    w = WORKLOADS["prefill_bf16_128k_8k"].replace(batch=2)
+    inp = make_prefill_inputs(w, ctx_lens=[9000, 7000], n_q=128, capacity=9000)
+    ref, _, _ = oracle.full_attn_scores(inp["q"], inp["k"], inp["ctx_len"], tile_q=64,
+                                        sm_scale=w.sm_scale)
+    buf = make_buffers(inp, n_heads=32, k_top=1024, window=128, sm_scale=w.sm_scale,
+                       dtype="bf16", n_q=128, tile_q=64)
+    _say("prefill select on oracle scores")
+    run_select(buf, scores=to_device(ref))
+    torch.cuda.synchronize()
+    top, cnt = oracle.select_topk_window(ref, inp["ctx_len"], n_q=128, tile_q=64, k_top=1024,
+                                         window=128)
+    np.testing.assert_array_equal(buf.top_cnt.cpu().numpy(), cnt)
+    np.testing.assert_array_equal(buf.top_idx.cpu().numpy(), top)
+
+
+def test_prefill_fused_step_equals_three_calls(hs2):
+    w = WORKLOADS["prefill_bf16_128k_8k"].replace(batch=1)
+    inp = make_prefill_inputs(w, ctx_lens=[10000], n_q=128, capacity=10000)
+    _say("prefill fused vs three calls")
+    a = _run(inp, w, 128, 64)
+    b = _run(inp, w, 128, 64, fused=True)
+    assert torch.equal(a.scores[..., :10000], b.scores[..., :10000])
+    for x, y in ((a.top_idx, b.top_idx), (a.top_cnt, b.top_cnt), (a.o, b.o), (a.lse, b.lse)):
+        assert torch.equal(x, y)
+
+
+def test_prefill_full_size_sampled_tiles(hs2):
+    # 8,192 new queries appended to a 131,072-token cache (139,264 keys),
+    # 128 tiles of 64; the oracle checks a seeded sample of tiles.
+    w = WORKLOADS["prefill_bf16_128k_8k"]
+    inp = make_prefill_inputs(w)
+    n_q, tile_q, n = w.n_q, w.tile_q, w.ctx_len
+    _say(f"prefill full size n_q={n_q} ctx={n}")
+    buf = _run(inp, w, n_q, tile_q, fused=True)
+    scores = buf.scores.cpu().numpy()
+    tg, cg, og = buf.top_idx.cpu().numpy(), buf.top_cnt.cpu().numpy(), buf.o.cpu().numpy()
+    rng = np.random.default_rng(33)
+    tiles = sorted(set([0, 1, 63, 64, 126, 127] + list(rng.integers(0, n_q // tile_q, 2))))
+    for t in tiles:
+        q0 = t * tile_q
+        ctx_t = np.array([n - n_q + q0 + tile_q], dtype=np.int32)
+        qs = inp["q"][:, q0:q0 + tile_q]
+        ref, _, _ = oracle.full_attn_scores(qs, inp["k"][:, :ctx_t[0]], ctx_t, tile_q=tile_q,
+                                            sm_scale=w.sm_scale)
+        got = scores[:, t:t + 1, :]
+        assert_scores_close(got, ref, ctx_t)
+        assert np.all(got[0, 0, ctx_t[0]:n] == 0)  # keys after the tile's last query
+        top, cnt = oracle.select_topk_window(ref, ctx_t, n_q=tile_q, tile_q=tile_q,
+                                             k_top=w.k_top, window=w.window)
+        assert_selection_near_ties(tg[:, t:t + 1], cg[:, t:t + 1], top, cnt, ref, ctx_t,
+                                   n_q=tile_q, tile_q=tile_q, window=w.window)
+        o_ref, _ = oracle.sparse_attention(qs, inp["k"][:, :ctx_t[0]], inp["v"][:, :ctx_t[0]],
+                                           ctx_t, tg[:, t:t + 1], cg[:, t:t + 1], tile_q=tile_q,
+                                           window=w.window, sm_scale=w.sm_scale)
+        assert_outputs_close(og[:, q0:q0 + tile_q], o_ref, "bf16")
+        _say(f"tile {t} ok")
