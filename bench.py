@@ -47,6 +47,101 @@ def algorithmic_bytes(w) -> dict:
                 scoring_call=k_stream + scores)
 
 
+def time_events(fn, steps: int, warmup: int) -> float:
+    """Average milliseconds of fn() over `steps` runs, HIP events on the
+    current stream, after `warmup` untimed runs."""
+    import torch
+
+    stream = torch.cuda.current_stream()
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(steps):
+        fn()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / steps
+
+
+def extra_measurements(steps: int, warmup: int) -> dict:
+    """The other shapes of the method, measured the same way (not the headline):
+    batched decode at 64k, chunked prefill of 8,192 queries on a 131,072-token
+    cache, and KV Bridging of 1,048,576 hidden states followed by a decode step
+    over the bridged 1M-token cache."""
+    import torch
+
+    import kv_cache_reuse_hs2_amd as hs2
+    from kv_cache_reuse_hs2_amd.torch_api import make_buffers, run_fused_step
+    from workloads import WORKLOADS, make_decode_inputs, make_prefill_inputs
+
+    out = {}
+    # Batched decode, 16 x 65,536 keys.
+    w = WORKLOADS["decode_bf16_64k_b16"]
+    buf = make_buffers(make_decode_inputs(w), n_heads=w.n_heads, k_top=w.k_top, window=w.window,
+                       sm_scale=w.sm_scale, dtype=w.dtype)
+    ms = time_events(lambda: run_fused_step(buf), steps, warmup)
+    ab = algorithmic_bytes(w)
+    out[w.name] = {"ms_per_step": round(ms, 5), "tokens_per_s": round(w.batch / (ms * 1e-3), 1),
+                   "step_hbm_GBps": round(ab["step"] / (ms * 1e-3) / 1e9, 1)}
+    del buf
+    # Chunked prefill: 8,192 queries, 139,264 keys, tiles of 64.
+    w = WORKLOADS["prefill_bf16_128k_8k"]
+    inp = make_prefill_inputs(w)
+    buf = make_buffers(inp, n_heads=w.n_heads, k_top=w.k_top, window=w.window,
+                       sm_scale=w.sm_scale, dtype=w.dtype, n_q=w.n_q, tile_q=w.tile_q)
+    ms = time_events(lambda: run_fused_step(buf), max(2, steps // 10), 2)
+    pos = [w.ctx_len - w.n_q + i for i in range(w.n_q)]
+    qk_flop = 2.0 * w.n_heads * w.head_dim * sum(p + 1 for p in pos)   # causal QK^T, once
+    sel = w.k_top + w.window
+    sparse_flop = 2.0 * 2.0 * w.n_heads * w.head_dim * w.n_q * sel      # QK^T + PV over 1,152 keys
+    alg = qk_flop + sparse_flop
+    out[w.name] = {"ms_per_step": round(ms, 4), "queries_per_s": round(w.n_q / (ms * 1e-3), 1),
+                   "algorithmic_TFLOP": round(alg / 1e12, 3),
+                   "achieved_TFLOPs": round(alg / (ms * 1e-3) / 1e12, 1),
+                   "mfma_bf16_frac": round(alg / (ms * 1e-3) / 2.5e15, 4),
+                   "note": "algorithmic FLOPs count the causal QK^T once plus the sparse "
+                           "QK^T+PV; the recompute pass is overhead"}
+    del buf, inp
+    # KV Bridging of 1,048,576 x 2048 hidden states, then decode over the cache.
+    w = WORKLOADS["bridge_decode_bf16_1m"]
+    g = torch.Generator(device="cuda").manual_seed(w.seed)
+    m_rows, dm = w.ctx_len, w.d_model
+    h = (torch.randn((m_rows, dm), generator=g, device="cuda") / dm ** 0.5).to(torch.bfloat16)
+    wk = torch.randn((dm, w.head_dim), generator=g, device="cuda").to(torch.bfloat16)
+    wv = torch.randn((dm, w.head_dim), generator=g, device="cuda").to(torch.bfloat16)
+    k = torch.empty((1, m_rows, w.head_dim), dtype=torch.bfloat16, device="cuda")
+    v = torch.empty_like(k)
+    ms_b = time_events(lambda: hs2.hs2_bridge_kv(h, dm, wk, wv, k, v, w.head_dim, m_rows, dm),
+                       max(3, steps // 5), 2)
+    flop = 2.0 * m_rows * dm * 2 * w.head_dim
+    byts = m_rows * dm * 2 + 2 * dm * w.head_dim * 2 + 2 * m_rows * w.head_dim * 2
+    out["bridge_kv_1m_x_2048"] = {
+        "ms": round(ms_b, 4), "achieved_TFLOPs": round(flop / (ms_b * 1e-3) / 1e12, 1),
+        "mfma_bf16_frac": round(flop / (ms_b * 1e-3) / 2.5e15, 4),
+        "hbm_GBps": round(byts / (ms_b * 1e-3) / 1e9, 1),
+        "hbm_frac": round(byts / (ms_b * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+    del h
+    q = torch.randn((1, 1, w.n_heads, w.head_dim), generator=g, device="cuda").to(torch.bfloat16)
+    desc = hs2.make_desc(batch=1, n_heads=w.n_heads, k_top=w.k_top, window=w.window)
+    ctx = torch.tensor([m_rows], dtype=torch.int32, device="cuda")
+    f32 = dict(dtype=torch.float32, device="cuda")
+    scores = torch.empty((1, 1, m_rows), **f32)
+    ti = torch.empty((1, 1, w.k_top), dtype=torch.int32, device="cuda")
+    tc = torch.empty((1, 1), dtype=torch.int32, device="cuda")
+    o = torch.empty((1, 1, w.n_heads, w.head_dim), **f32)
+    ws = torch.empty(hs2.hs2_workspace_size(desc, m_rows), dtype=torch.uint8, device="cuda")
+    step = lambda: hs2.hs2_decode_step(desc, q, None, k, v, m_rows * w.head_dim, ctx, m_rows,  # noqa: E731
+                                       scores, None, ti, tc, o, None, ws)
+    ms = time_events(step, steps, warmup)
+    ab = algorithmic_bytes(w)
+    out["decode_bf16_1m_after_bridge"] = {
+        "ms_per_step": round(ms, 5), "tokens_per_s": round(1 / (ms * 1e-3), 1),
+        "step_hbm_GBps": round(ab["step"] / (ms * 1e-3) / 1e9, 1)}
+    return out
+
+
 def measured_traffic(kernels) -> float | None:
     """HBM bytes per launch of `kernels` from the committed counter summary
     (profiles/<workload>_traffic.json), or None when the kernel sources have
@@ -105,6 +200,8 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--graph", type=int, default=1, help="replay the step as a HIP graph")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--extras", type=int, default=1,
+                    help="also time batched decode, chunked prefill and KV Bridging")
     ap.add_argument("--calibrate", action="store_true",
                     help="after timing, run a plain 256 MiB device copy (torch copy_) so that "
                          "HBM byte counters can be scaled by a kernel of known traffic")
@@ -229,6 +326,9 @@ def main() -> int:
             "algorithmic_bytes_per_launch": ab["scoring_call"],
         },
     }
+    if args.extras:
+        del buf
+        out["extras"] = extra_measurements(args.steps, args.warmup)
     if args.calibrate:
         src = torch.empty(256 * MIB, dtype=torch.uint8, device="cuda").fill_(1)
         dst = torch.empty_like(src)
