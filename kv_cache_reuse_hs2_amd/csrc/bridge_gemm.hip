@@ -8,15 +8,31 @@
 // Self-Decoder and Cross-Decoder Split", first two equations; "HySparse2:
 // Hybrid Sparse Attention with Two-Level KV Sharing", bullet "KV Bridging").
 //
-// One fused GEMM with N = 2 x 128 so that H (the dominant operand) is read
-// once.  A workgroup owns 128 rows x all 256 columns; each of its 4 waves
-// owns 32 rows and accumulates eight 32x32 fp32 tiles with
-// v_mfma_f32_32x32x16_bf16.  H rows feed the MFMA A operand straight from
-// HBM (a lane reads 16 contiguous bytes of one row).  The weights, which
-// every workgroup re-reads from L2, are staged per 64-deep K slice into LDS
-// transposed ([n][k], k contiguous) as bf16 pairs, so the B operand is one
-// 16-byte LDS read per lane; the row pitch of 36 dwords keeps both the
-// staging writes and the operand reads free of bank conflicts.
+// One fused GEMM with N = 2 x 128 so that H, the dominant operand, is read
+// once; with M = 1M and d_model = 2048 it moves about 227 flop per byte,
+// under the bf16 MFMA ridge, so it is bound by the H stream.
+//
+// The weights are static parameters, so they are packed once (bridge_pack)
+// into the exact order in which the MFMA B operand consumes them: per 32-deep
+// stage, per 32-column tile and 16-deep step, 64 lanes x 16 bytes.
+//
+// A workgroup owns 256 rows x all 256 columns; each of its 4 waves owns 64
+// rows (two 32-row tiles) and keeps sixteen 32x32 fp32 accumulators
+// (v_mfma_f32_32x32x16_bf16), so every weight operand read from LDS feeds two
+// MFMAs.  Both operands reach LDS by direct global-to-LDS loads (16 bytes a
+// lane, no registers in between) through a ring of kStages stages: while the
+// MFMAs of one stage run, the operands of the next are read from LDS into
+// registers and the loads of the two after it, plus a newly issued one, are
+// in flight (up to 64 KiB of H per CU).  Each
+// stage holds the 16 KiB packed weight slice, shared by the 4 waves, and each
+// wave's own 64 x 32 slice of H, which that wave loads row-contiguously (16
+// rows x 64 bytes per instruction) with the 16-byte chunks of a row rotated
+// by (row / 4) % 4 so that the operand reads are free of bank conflicts.
+// Waits are explicit (the compiler does not track loads to LDS): they are
+// counted by vmcnt in issue order, so a wave waits until only its younger
+// stages are outstanding, and one barrier per stage both publishes the stage
+// to all waves and retires the slot that the next load overwrites.  The output tile is staged through LDS
+// so that it leaves in 16-byte row stores.
 #include "hs2_internal.h"
 
 namespace hs2 {
@@ -24,92 +40,205 @@ namespace {
 
 typedef __bf16 bf16x8_t __attribute__((__vector_size__(8 * sizeof(__bf16))));
 typedef float f32x16_t __attribute__((__vector_size__(16 * sizeof(float))));
+typedef __attribute__((address_space(3))) void lds_void_t;
 
-constexpr int kBM = 128;         // rows per workgroup
-constexpr int kBN = 256;         // K columns 0..127, V columns 128..255
-constexpr int kBK = 64;          // reduction depth per LDS stage
-constexpr int kPitch = kBK / 2 + 4;  // dwords per transposed weight row
+constexpr int kWaves = 4;
+constexpr int kBM = 64 * kWaves;                 // rows per workgroup
+constexpr int kBN = 256;                         // K columns 0..127, V columns 128..255
+constexpr int kBK = 32;                          // reduction depth per stage
+constexpr int kStages = 4;                       // LDS ring depth
+constexpr int kAhead = kStages;                  // stages issued before the first MFMA
+constexpr int kWStage = kBN * kBK * 2;           // 16 KiB of packed weights per stage
+constexpr int kHWave = 64 * kBK * 2;             // 4 KiB of H per wave per stage
+constexpr int kStageBytes = kWStage + kWaves * kHWave;
+constexpr int kWLoads = kWStage / 1024 / kWaves; // 1 KiB loads per wave per stage
+constexpr int kHLoads = kHWave / 1024;
+constexpr int kLoadsPerStage = kWLoads + kHLoads;
+static_assert(kStages * kStageBytes >= kBM * kBN * 2, "output tile reuses the ring");
 
 __device__ __forceinline__ bf16x8_t as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8_t, v); }
 
-__global__ __launch_bounds__(256) void bridge_gemm(const uint16_t* __restrict__ h, int64_t ldh,
-                                                   const uint16_t* __restrict__ w_k,
-                                                   const uint16_t* __restrict__ w_v,
-                                                   uint16_t* __restrict__ k_out,
-                                                   uint16_t* __restrict__ v_out, int64_t ld_kv,
-                                                   int M, int d_model) {
-  __shared__ uint32_t wt[kBN * kPitch];
+// 16 bytes from global memory to LDS at lds + 16 * lane.
+__device__ __forceinline__ void load_to_lds(const void* src, uint8_t* lds) {
+  __builtin_amdgcn_global_load_lds(src, (lds_void_t*)lds, 16, 0, 0);
+}
+
+// Wait until at most kN loads of this wave are in flight and its LDS reads
+// are done, then meet the other waves.
+template <int kN>
+__device__ __forceinline__ void wait_then_barrier() {
+  static_assert(kN >= 0 && kN < 64, "vmcnt has 6 bits");
+  __builtin_amdgcn_s_waitcnt((kN & 15) | ((kN >> 4) << 14) | (7 << 4));  // lgkmcnt(0)
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+// Issue the loads of stage g into `slot`: this wave's quarter of the weight
+// slice and its own 64 rows of H.
+__device__ __forceinline__ void issue_stage(int g, const uint16_t* w_packed,
+                                            const uint16_t* const (&hsrc)[kHLoads], int wave,
+                                            int lane, uint8_t* slot) {
+  const uint16_t* ws = w_packed + (size_t)g * (kWStage / 2) + (kWLoads * wave) * 512 + lane * 8;
+#pragma unroll
+  for (int j = 0; j < kWLoads; ++j) load_to_lds(ws + j * 512, slot + (kWLoads * wave + j) * 1024);
+  uint8_t* hs = slot + kWStage + wave * kHWave;
+#pragma unroll
+  for (int j = 0; j < kHLoads; ++j) load_to_lds(hsrc[j] + g * kBK, hs + j * 1024);
+}
+
+// The A and B operands of one stage: [16-deep step][m tile] and [step][n tile].
+struct Operands {
+  u32x4 a[2][2], b[2][8];
+};
+
+__device__ __forceinline__ void read_operands(const uint8_t* st, const int (&a_off)[2][2], int lane,
+                                              Operands& o) {
+#pragma unroll
+  for (int s = 0; s < 2; ++s) {
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt) o.a[s][mt] = *reinterpret_cast<const u32x4*>(st + a_off[mt][s]);
+#pragma unroll
+    for (int n = 0; n < 8; ++n)
+      o.b[s][n] = *reinterpret_cast<const u32x4*>(st + ((2 * n + s) * 64 + lane) * 16);
+  }
+}
+
+// Stage `it`, whose operands are in `cur`: wait for stage it+1 (which also
+// retires the slot of stage it, read by every wave), refill that slot with
+// stage it+kAhead, read the operands of stage it+1 into `next`, and run the
+// 32 MFMAs of stage it while those reads are in flight.  Every step issues
+// the same loads, so that the wait counts are constants and the step has no
+// branch: past the last stage the loads repeat it (cache-resident) into a
+// free slot, and the operands read from it are never used.
+__device__ __forceinline__ void bridge_step(int it, int nk, const uint16_t* w_packed,
+                                            const uint16_t* const (&hsrc)[kHLoads], int wave,
+                                            int lane, const int (&a_off)[2][2], uint8_t* lds,
+                                            const Operands& cur, Operands& next,
+                                            f32x16_t (&acc)[2][8]) {
+  // Younger than stage it+1: stages it+2 .. it+kAhead-1.
+  wait_then_barrier<(kAhead - 2) * kLoadsPerStage>();
+  issue_stage(min(it + kAhead, nk - 1), w_packed, hsrc, wave, lane,
+              lds + (it % kStages) * kStageBytes);
+  read_operands(lds + ((it + 1) % kStages) * kStageBytes, a_off, lane, next);
+#pragma unroll
+  for (int s = 0; s < 2; ++s)
+#pragma unroll
+    for (int n = 0; n < 8; ++n)
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt)
+        acc[mt][n] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+            as_bf16x8(cur.a[s][mt]), as_bf16x8(cur.b[s][n]), acc[mt][n], 0, 0, 0);
+}
+
+__global__ __launch_bounds__(64 * kWaves) void bridge_gemm(const uint16_t* __restrict__ h,
+                                                           int64_t ldh,
+                                                           const uint16_t* __restrict__ w_packed,
+                                                           uint16_t* __restrict__ k_out,
+                                                           uint16_t* __restrict__ v_out,
+                                                           int64_t ld_kv, int M, int d_model) {
+  __shared__ __attribute__((aligned(16))) uint8_t lds[kStages * kStageBytes];
   const int t = threadIdx.x;
   const int lane = t & 63, wave = t >> 6;
   const int r32 = lane & 31, hh = lane >> 5;
-  const int m0 = blockIdx.x * kBM + wave * 32;
-  const int row = min(m0 + r32, M - 1);
-  const uint16_t* hrow = h + (size_t)row * ldh + 8 * hh;
+  const int m0 = blockIdx.x * kBM + wave * 64;
 
-  f32x16_t acc[8];
+  // Load j of a stage brings rows 16j + lane/4 of the wave's 64; the lane's
+  // 16-byte chunk is (lane % 4) rotated by the row's (row / 4) % 4.
+  const uint16_t* hsrc[kHLoads];
 #pragma unroll
-  for (int n = 0; n < 8; ++n) acc[n] = (f32x16_t){};
-
-  // Staging assignment: lane -> k pair (t % 32), n block of 8 (t / 32 + 8 * pass).
-  const int kp = t & 31, nb = t >> 5;
-
-  u32x4 a[4];
-#pragma unroll
-  for (int s = 0; s < 4; ++s) a[s] = *reinterpret_cast<const u32x4*>(hrow + 16 * s);
-
-  for (int k0 = 0; k0 < d_model; k0 += kBK) {
-    __syncthreads();
-#pragma unroll
-    for (int pass = 0; pass < 4; ++pass) {
-      const int n0 = (nb + 8 * pass) * 8;  // 0..248
-      const uint16_t* w = n0 < 128 ? w_k : w_v;
-      const int nc = n0 & 127;
-      const u32x4 lo = *reinterpret_cast<const u32x4*>(w + (size_t)(k0 + 2 * kp) * kHeadDim + nc);
-      const u32x4 hi = *reinterpret_cast<const u32x4*>(w + (size_t)(k0 + 2 * kp + 1) * kHeadDim + nc);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        // element 2e and 2e+1 of the 8 columns, paired with the next k row
-        wt[(n0 + 2 * e) * kPitch + kp] = (lo[e] & 0xFFFFu) | (hi[e] << 16);
-        wt[(n0 + 2 * e + 1) * kPitch + kp] = (lo[e] >> 16) | (hi[e] & 0xFFFF0000u);
-      }
-    }
-    __syncthreads();
-    u32x4 an[4];
-    const bool more = k0 + kBK < d_model;
-#pragma unroll
-    for (int s = 0; s < 4; ++s)
-      if (more) an[s] = *reinterpret_cast<const u32x4*>(hrow + k0 + kBK + 16 * s);
-#pragma unroll
-    for (int s = 0; s < 4; ++s) {
-#pragma unroll
-      for (int n = 0; n < 8; ++n) {
-        const u32x4 b = *reinterpret_cast<const u32x4*>(&wt[(n * 32 + r32) * kPitch + 8 * s + 4 * hh]);
-        acc[n] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a[s]), as_bf16x8(b), acc[n], 0, 0, 0);
-      }
-    }
-#pragma unroll
-    for (int s = 0; s < 4; ++s) a[s] = an[s];
+  for (int j = 0; j < kHLoads; ++j) {
+    const int row = 16 * j + (lane >> 2);
+    const int chunk = (lane & 3) ^ ((row >> 2) & 3);
+    hsrc[j] = h + (size_t)min(m0 + row, M - 1) * ldh + 8 * chunk;
   }
-  // acc[n][r]: row m0 + 8*(r/4) + 4*hh + r%4, column 32*n + r32.
+  // Operand reads: A tile mt, step s -> row 32mt + r32, chunk 2s + hh.
+  int a_off[2][2];
 #pragma unroll
-  for (int n = 0; n < 8; ++n) {
-    uint16_t* out = n < 4 ? k_out : v_out;
-    const int col = (n & 3) * 32 + r32;
+  for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int m = m0 + 8 * (r >> 2) + 4 * hh + (r & 3);
-      if (m < M) out[(size_t)m * ld_kv + col] = f32_to_bf16_rne(acc[n][r]);
+    for (int s = 0; s < 2; ++s) {
+      const int row = 32 * mt + r32, chunk = 2 * s + hh;
+      a_off[mt][s] = kWStage + wave * kHWave + 16 * (4 * row + (chunk ^ ((row >> 2) & 3)));
+    }
+
+  f32x16_t acc[2][8];
+#pragma unroll
+  for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+    for (int n = 0; n < 8; ++n) acc[mt][n] = (f32x16_t){};
+
+  const int nk = d_model / kBK;  // even: d_model is a multiple of 64
+#pragma unroll
+  for (int g = 0; g < kAhead; ++g)
+    issue_stage(min(g, nk - 1), w_packed, hsrc, wave, lane, lds + g * kStageBytes);
+  wait_then_barrier<(kAhead - 1) * kLoadsPerStage>();  // stage 0
+  Operands o0, o1;
+  read_operands(lds, a_off, lane, o0);
+  for (int it = 0; it < nk; it += 2) {
+    bridge_step(it, nk, w_packed, hsrc, wave, lane, a_off, lds, o0, o1, acc);
+    bridge_step(it + 1, nk, w_packed, hsrc, wave, lane, a_off, lds, o1, o0, acc);
+  }
+  wait_then_barrier<0>();  // every wave is done with the ring
+
+  // acc[mt][n][r]: row 32mt + 8(r/4) + 4hh + r%4 of the wave, column 32n + r32.
+  // The wave's 64 x 256 bf16 tile (32 KiB) is staged in its own part of the
+  // ring, then leaves as 16-byte pieces, two rows per instruction.
+  uint16_t* tile = reinterpret_cast<uint16_t*>(lds + wave * 64 * kBN * 2);
+#pragma unroll
+  for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+    for (int n = 0; n < 8; ++n)
+#pragma unroll
+      for (int r = 0; r < 16; ++r)
+        tile[(32 * mt + 8 * (r >> 2) + 4 * hh + (r & 3)) * kBN + 32 * n + r32] =
+            f32_to_bf16_rne(acc[mt][n][r]);
+  wait_then_barrier<0>();  // the tiles are in LDS
+#pragma unroll 4
+  for (int it = 0; it < 32; ++it) {
+    const int row = 2 * it + (lane >> 5), piece = lane & 31;
+    const int m = m0 + row;
+    const u32x4 x = *reinterpret_cast<const u32x4*>(&tile[row * kBN + 8 * piece]);
+    if (m < M) {
+      uint16_t* out = (piece < 16 ? k_out : v_out) + (size_t)m * ld_kv + 8 * (piece & 15);
+      *reinterpret_cast<u32x4*>(out) = x;
     }
   }
 }
 
+// w_packed[g][nt][s][lane][e] = W[32g + 16s + 8(lane / 32) + e][32nt + lane % 32]
+// with W = [W_K | W_V] (d_model x 256): the B operand of stage g, column tile
+// nt and 16-deep step s, 16 bytes per lane.
+__global__ __launch_bounds__(256) void bridge_pack(const uint16_t* __restrict__ w_k,
+                                                   const uint16_t* __restrict__ w_v,
+                                                   uint16_t* __restrict__ w_packed, int d_model) {
+  const int idx = blockIdx.x * 256 + threadIdx.x;  // (g, nt, s, lane)
+  if (idx >= d_model * 32) return;
+  const int lane = idx & 63, s = (idx >> 6) & 1, nt = (idx >> 7) & 7, g = idx >> 10;
+  const int n = 32 * nt + (lane & 31);
+  const int k0 = kBK * g + 16 * s + 8 * (lane >> 5);
+  const uint16_t* w = n < kHeadDim ? w_k + n : w_v + (n - kHeadDim);
+  uint32_t p[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e)
+    p[e] = (uint32_t)w[(size_t)(k0 + 2 * e) * kHeadDim] |
+           ((uint32_t)w[(size_t)(k0 + 2 * e + 1) * kHeadDim] << 16);
+  *reinterpret_cast<u32x4*>(w_packed + (size_t)idx * 8) = (u32x4){p[0], p[1], p[2], p[3]};
+}
+
 }  // namespace
 
-hipError_t launch_bridge(const uint16_t* h, int64_t ldh, const uint16_t* w_k, const uint16_t* w_v,
+hipError_t launch_bridge_pack(const uint16_t* w_k, const uint16_t* w_v, uint16_t* w_packed,
+                              int d_model, hipStream_t st) {
+  bridge_pack<<<(d_model * 32 + 255) / 256, 256, 0, st>>>(w_k, w_v, w_packed, d_model);
+  return hipGetLastError();
+}
+
+hipError_t launch_bridge(const uint16_t* h, int64_t ldh, const uint16_t* w_packed,
                          uint16_t* k_out, uint16_t* v_out, int64_t ld_kv, int M, int d_model,
                          hipStream_t st) {
   const int grid = (M + kBM - 1) / kBM;
-  bridge_gemm<<<grid, 256, 0, st>>>(h, ldh, w_k, w_v, k_out, v_out, ld_kv, M, d_model);
+  bridge_gemm<<<grid, 64 * kWaves, 0, st>>>(h, ldh, w_packed, k_out, v_out, ld_kv, M, d_model);
   return hipGetLastError();
 }
 

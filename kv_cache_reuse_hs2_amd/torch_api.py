@@ -1,7 +1,7 @@
 """Torch-side plumbing around the C ABI: device buffers and a decode step.
 
 Nothing here computes: it allocates outputs and workspace with torch and
-calls the three libhs2 entry points in order on the current stream.
+calls the libhs2 entry points in order on the current stream.
 """
 
 from __future__ import annotations
@@ -11,7 +11,8 @@ import dataclasses
 import numpy as np
 import torch
 
-from . import (HS2_BF16, HS2_F32, hs2_attn_desc, hs2_decode_step, hs2_full_attn_scores,
+from . import (HS2_BF16, HS2_F32, hs2_attn_desc, hs2_bridge_pack_weights,
+               hs2_bridge_packed_bytes, hs2_decode_step, hs2_full_attn_scores,
                hs2_select_topk_window, hs2_sparse_attn_gather, hs2_workspace_size, make_desc)
 
 
@@ -107,3 +108,14 @@ def run_fused_step(buf: DecodeBuffers, q_sparse: torch.Tensor | None = None, str
     hs2_decode_step(buf.desc, buf.q, q_sparse, buf.k, buf.v, buf.kv_stride, buf.ctx_len, buf.cap,
                     buf.scores, buf.lse_full, buf.top_idx, buf.top_cnt, buf.o, buf.lse, buf.ws,
                     stream)
+
+
+def pack_bridge_weights(w_k: torch.Tensor, w_v: torch.Tensor, d_model: int,
+                        stream=None) -> torch.Tensor:
+    """Device buffer holding [W_K | W_V] packed for hs2_bridge_kv."""
+    n = hs2_bridge_packed_bytes(d_model)
+    if n == 0:
+        raise ValueError(f"unsupported d_model {d_model}")
+    w_packed = torch.empty(n // 2, dtype=torch.int16, device=w_k.device)
+    hs2_bridge_pack_weights(w_k, w_v, d_model, w_packed, stream=stream)
+    return w_packed

@@ -160,9 +160,10 @@ def test_decode_step_validation(lib):
 def test_bridge_validation(lib):
     L = hs2.load()
     br = lambda **kw: L.hs2_bridge_kv(  # noqa: E731
-        kw.get("h", FAKE), kw.get("ldh", 2048), FAKE, FAKE, FAKE, kw.get("vo", FAKE),
+        kw.get("h", FAKE), kw.get("ldh", 2048), kw.get("wp", FAKE), FAKE, kw.get("vo", FAKE),
         kw.get("ldkv", 128), kw.get("M", 1024), kw.get("dm", 2048), kw.get("hd", 128), None)
     assert br(h=None) == hs2.HS2_EINVAL
+    assert br(wp=None) == hs2.HS2_EINVAL
     assert br(vo=None) == hs2.HS2_EINVAL
     assert br(M=0) == hs2.HS2_EINVAL
     assert br(ldh=1024) == hs2.HS2_EINVAL
@@ -170,9 +171,27 @@ def test_bridge_validation(lib):
     assert br(dm=100, ldh=2048) == hs2.HS2_EUNSUPPORTED
     assert br(ldh=2052) == hs2.HS2_EALIGN
     assert br(h=ODD) == hs2.HS2_EALIGN
+    assert br(wp=ODD) == hs2.HS2_EALIGN
+
+
+def test_bridge_pack_validation(lib):
+    L = hs2.load()
+    pk = lambda **kw: L.hs2_bridge_pack_weights(  # noqa: E731
+        kw.get("wk", FAKE), FAKE, kw.get("dm", 2048), kw.get("hd", 128), kw.get("wp", FAKE), None)
+    assert pk(wk=None) == hs2.HS2_EINVAL
+    assert pk(wp=None) == hs2.HS2_EINVAL
+    assert pk(dm=0) == hs2.HS2_EINVAL
+    assert pk(dm=96) == hs2.HS2_EUNSUPPORTED
+    assert pk(hd=64) == hs2.HS2_EUNSUPPORTED
+    assert pk(wp=ODD) == hs2.HS2_EALIGN
+    # [W_K | W_V] in bfloat16: d_model x 256 x 2 bytes
+    assert hs2.hs2_bridge_packed_bytes(2048) == 2048 * 256 * 2
+    assert hs2.hs2_bridge_packed_bytes(64) == 64 * 256 * 2
+    assert hs2.hs2_bridge_packed_bytes(96) == 0
+    assert hs2.hs2_bridge_packed_bytes(2048, 64) == 0
 
 
 def test_binding_raises_on_error_status(lib):
     with pytest.raises(hs2.HS2Error) as ei:
-        hs2.hs2_bridge_kv(None, 2048, FAKE, FAKE, FAKE, FAKE, 128, 1024, 2048, stream=0)
+        hs2.hs2_bridge_kv(None, 2048, FAKE, FAKE, FAKE, 128, 1024, 2048, stream=0)
     assert ei.value.status == hs2.HS2_EINVAL

@@ -36,7 +36,7 @@ def _check_rows(k_gpu_bits, v_gpu_bits, inp, rows):
 
 def _run(m_rows, d_model, rows=None, ld_kv=128):
     from kv_cache_reuse_hs2_amd import hs2_bridge_kv
-    from kv_cache_reuse_hs2_amd.torch_api import to_device
+    from kv_cache_reuse_hs2_amd.torch_api import pack_bridge_weights, to_device
 
     w = WORKLOADS["bridge_decode_bf16_1m"].replace(d_model=d_model)
     inp = make_bridge_inputs(w, rows=m_rows)
@@ -46,7 +46,8 @@ def _run(m_rows, d_model, rows=None, ld_kv=128):
     v = torch.zeros((m_rows, ld_kv), dtype=torch.int16, device="cuda")
     print(f"[gpu] bridge M={m_rows} d_model={d_model} ld_kv={ld_kv}", flush=True)
     sys.stdout.flush()
-    hs2_bridge_kv(h, d_model, wk, wv, k, v, ld_kv, m_rows, d_model)
+    wp = pack_bridge_weights(wk, wv, d_model)
+    hs2_bridge_kv(h, d_model, wp, k, v, ld_kv, m_rows, d_model)
     torch.cuda.synchronize()
     kb = k.cpu().numpy().view(np.uint16)[:, :128]
     vb = v.cpu().numpy().view(np.uint16)[:, :128]
