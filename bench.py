@@ -116,7 +116,9 @@ def extra_measurements(steps: int, warmup: int) -> dict:
     from kv_cache_reuse_hs2_amd.torch_api import pack_bridge_weights
     wp = pack_bridge_weights(wk, wv, dm)  # once per set of weights, outside the timing
     ms_pack = time_events(lambda: hs2.hs2_bridge_pack_weights(wk, wv, dm, wp), 5, 2)
-    ms_b = time_events(lambda: hs2.hs2_bridge_kv(h, dm, wp, k, v, w.head_dim, m_rows, dm),
+    ms_u = time_events(lambda: hs2.hs2_bridge_kv(h, dm, wk, wv, k, v, w.head_dim, m_rows, dm),
+                       max(3, steps // 5), 2)
+    ms_b = time_events(lambda: hs2.hs2_bridge_kv_packed(h, dm, wp, k, v, w.head_dim, m_rows, dm),
                        max(3, steps // 5), 2)
     flop = 2.0 * m_rows * dm * 2 * w.head_dim
     byts = m_rows * dm * 2 + 2 * dm * w.head_dim * 2 + 2 * m_rows * w.head_dim * 2
@@ -125,7 +127,9 @@ def extra_measurements(steps: int, warmup: int) -> dict:
         "mfma_bf16_frac": round(flop / (ms_b * 1e-3) / 2.5e15, 4),
         "hbm_GBps": round(byts / (ms_b * 1e-3) / 1e9, 1),
         "hbm_frac": round(byts / (ms_b * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
-        "pack_weights_ms": round(ms_pack, 4)}
+        "entry": "hs2_bridge_kv_packed (weights packed once)",
+        "pack_weights_ms": round(ms_pack, 4),
+        "hs2_bridge_kv_ms": round(ms_u, 4)}
     del h
     q = torch.randn((1, 1, w.n_heads, w.head_dim), generator=g, device="cuda").to(torch.bfloat16)
     desc = hs2.make_desc(batch=1, n_heads=w.n_heads, k_top=w.k_top, window=w.window)

@@ -174,9 +174,27 @@ HS2_API hs2_status hs2_decode_step(const hs2_attn_desc* desc, const void* q,
  * KV Bridging ([Origins] "The Self-Decoder and Cross-Decoder Split", first two
  * equations; [Summary] "KV Bridging"): the K and V of a cross-decoder
  * full-attention layer are learned projections of a self-decoder
- * full-attention layer's hidden states.  W_K and W_V are static parameters,
- * so they are packed once into the order in which the projection kernel
- * consumes them, and every projection reads the packed copy.
+ * full-attention layer's hidden states:
+ *   k_out[m][:] = bf16(h[m][:] . w_k),  v_out[m][:] = bf16(h[m][:] . w_v)
+ * for m < M, with fp32 accumulation and one round-to-nearest-even.  All
+ * bfloat16 on the device: h [M][d_model] with row stride ldh (elements),
+ * w_k/w_v [d_model][head_dim] row-major, k_out/v_out [M][head_dim] with row
+ * stride ld_kv (elements); columns past head_dim are not written.  head_dim
+ * must be 128; d_model a positive multiple of 64; ldh >= d_model and
+ * ld_kv >= head_dim, both multiples of 8; pointers 16-byte aligned.
+ * Enqueued on `stream`.
+ */
+HS2_API hs2_status hs2_bridge_kv(const uint16_t* h, int64_t ldh, const uint16_t* w_k,
+                         const uint16_t* w_v, uint16_t* k_out, uint16_t* v_out,
+                         int64_t ld_kv, int M, int d_model, int head_dim,
+                         hs2_stream_t stream);
+
+/*
+ * W_K and W_V are static parameters, so they can be packed once into the
+ * order in which the projection kernel consumes them; hs2_bridge_kv_packed
+ * then streams the packed copy straight into on-chip memory instead of
+ * transposing the weights in every workgroup.  Same results as
+ * hs2_bridge_kv, bit for bit.
  *
  * Bytes of the packed weights for d_model x head_dim projections (0 if the
  * shape is unsupported).
@@ -184,27 +202,17 @@ HS2_API hs2_status hs2_decode_step(const hs2_attn_desc* desc, const void* q,
 HS2_API size_t hs2_bridge_packed_bytes(int d_model, int head_dim);
 
 /*
- * Packs w_k and w_v (bfloat16 [d_model][head_dim] row-major, device) into
- * w_packed (device, hs2_bridge_packed_bytes bytes, 16-byte aligned, owned by
- * the caller), enqueued on `stream`.  head_dim must be 128 and d_model a
- * positive multiple of 64.  The packed layout is private to this library.
+ * Packs w_k and w_v (as for hs2_bridge_kv) into w_packed (device,
+ * hs2_bridge_packed_bytes bytes, 16-byte aligned, owned by the caller),
+ * enqueued on `stream`.  The packed layout is private to this library.
  */
 HS2_API hs2_status hs2_bridge_pack_weights(const uint16_t* w_k, const uint16_t* w_v, int d_model,
                                    int head_dim, uint16_t* w_packed, hs2_stream_t stream);
 
-/*
- * The projection, with fp32 accumulation and one round-to-nearest-even:
- *   k_out[m][:] = bf16(h[m][:] . w_k),  v_out[m][:] = bf16(h[m][:] . w_v)
- * for m < M.  All bfloat16 on the device: h [M][d_model] with row stride ldh
- * (elements), w_packed from hs2_bridge_pack_weights for the same d_model,
- * k_out/v_out [M][head_dim] with row stride ld_kv (elements); columns past
- * head_dim are not written.  head_dim must be 128; d_model a positive
- * multiple of 64; ldh >= d_model and ld_kv >= head_dim, both multiples of 8;
- * pointers 16-byte aligned.  Enqueued on `stream`.
- */
-HS2_API hs2_status hs2_bridge_kv(const uint16_t* h, int64_t ldh, const uint16_t* w_packed,
-                         uint16_t* k_out, uint16_t* v_out, int64_t ld_kv, int M, int d_model,
-                         int head_dim, hs2_stream_t stream);
+/* hs2_bridge_kv with weights packed by hs2_bridge_pack_weights for the same d_model. */
+HS2_API hs2_status hs2_bridge_kv_packed(const uint16_t* h, int64_t ldh, const uint16_t* w_packed,
+                                uint16_t* k_out, uint16_t* v_out, int64_t ld_kv, int M,
+                                int d_model, int head_dim, hs2_stream_t stream);
 
 /* Static description of a status code. */
 HS2_API const char* hs2_status_string(hs2_status status);

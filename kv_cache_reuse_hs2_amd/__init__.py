@@ -29,9 +29,10 @@ EXPORTS = (
     "hs2_select_topk_window",
     "hs2_sparse_attn_gather",
     "hs2_decode_step",
+    "hs2_bridge_kv",
     "hs2_bridge_packed_bytes",
     "hs2_bridge_pack_weights",
-    "hs2_bridge_kv",
+    "hs2_bridge_kv_packed",
     "hs2_status_string",
 )
 
@@ -92,7 +93,9 @@ def load(path: str | None = None):
     lib.hs2_bridge_packed_bytes.restype = _sz
     lib.hs2_bridge_pack_weights.argtypes = [_vp, _vp, _int, _int, _vp, _vp]
     lib.hs2_bridge_pack_weights.restype = _int
-    lib.hs2_bridge_kv.argtypes = [_vp, _i64, _vp, _vp, _vp, _i64, _int, _int, _int, _vp]
+    lib.hs2_bridge_kv.argtypes = [_vp, _i64, _vp, _vp, _vp, _vp, _i64, _int, _int, _int, _vp]
+    lib.hs2_bridge_kv_packed.argtypes = [_vp, _i64, _vp, _vp, _vp, _i64, _int, _int, _int, _vp]
+    lib.hs2_bridge_kv_packed.restype = _int
     lib.hs2_bridge_kv.restype = _int
     lib.hs2_status_string.argtypes = [_int]
     lib.hs2_status_string.restype = ctypes.c_char_p
@@ -187,8 +190,16 @@ def hs2_bridge_pack_weights(w_k, w_v, d_model, w_packed, head_dim=128, stream=No
     _check(st, "hs2_bridge_pack_weights")
 
 
-def hs2_bridge_kv(h, ldh, w_packed, k_out, v_out, ld_kv, M, d_model, head_dim=128,
+def hs2_bridge_kv(h, ldh, w_k, w_v, k_out, v_out, ld_kv, M, d_model, head_dim=128,
                   stream=None) -> None:
-    st = load().hs2_bridge_kv(_ptr(h), int(ldh), _ptr(w_packed), _ptr(k_out), _ptr(v_out),
+    st = load().hs2_bridge_kv(_ptr(h), int(ldh), _ptr(w_k), _ptr(w_v), _ptr(k_out), _ptr(v_out),
                               int(ld_kv), int(M), int(d_model), int(head_dim), _stream(stream))
     _check(st, "hs2_bridge_kv")
+
+
+def hs2_bridge_kv_packed(h, ldh, w_packed, k_out, v_out, ld_kv, M, d_model, head_dim=128,
+                         stream=None) -> None:
+    st = load().hs2_bridge_kv_packed(_ptr(h), int(ldh), _ptr(w_packed), _ptr(k_out), _ptr(v_out),
+                                     int(ld_kv), int(M), int(d_model), int(head_dim),
+                                     _stream(stream))
+    _check(st, "hs2_bridge_kv_packed")

@@ -48,13 +48,32 @@ constexpr int kBN = 256;                         // K columns 0..127, V columns 
 constexpr int kBK = 32;                          // reduction depth per stage
 constexpr int kStages = 4;                       // LDS ring depth
 constexpr int kAhead = kStages;                  // stages issued before the first MFMA
-constexpr int kWStage = kBN * kBK * 2;           // 16 KiB of packed weights per stage
 constexpr int kHWave = 64 * kBK * 2;             // 4 KiB of H per wave per stage
-constexpr int kStageBytes = kWStage + kWaves * kHWave;
-constexpr int kWLoads = kWStage / 1024 / kWaves; // 1 KiB loads per wave per stage
-constexpr int kHLoads = kHWave / 1024;
-constexpr int kLoadsPerStage = kWLoads + kHLoads;
-static_assert(kStages * kStageBytes >= kBM * kBN * 2, "output tile reuses the ring");
+constexpr int kHLoads = kHWave / 1024;           // 1 KiB loads per wave per stage
+constexpr int kWLoads = 4;                       // weight loads per thread (or wave) per stage
+
+// Weight stage layout, [n tile][16-deep step][lane][8 bf16] (the B operand of
+// every MFMA is one 1 KiB block, 16 bytes per lane).  Staged through
+// registers, 16 bytes of padding follow every 16 lanes so that the transposing
+// 4-byte stores spread over the banks; loaded directly, the blocks are dense.
+template <bool kDirect>
+struct WLayout {
+  static constexpr int kGroup = kDirect ? 256 : 272;        // bytes per 16 lanes
+  static constexpr int kBlock = 4 * kGroup;                  // bytes per operand block
+  static constexpr int kStage = 16 * kBlock;                 // 8 n tiles x 2 steps
+  __device__ static int operand(int n, int s, int lane) {
+    return (2 * n + s) * kBlock + (lane >> 4) * kGroup + (lane & 15) * 16;
+  }
+};
+
+template <bool kDirect>
+struct Ring {
+  static constexpr int kWStage = WLayout<kDirect>::kStage;
+  static constexpr int kStageBytes = kWStage + kWaves * kHWave;
+  static constexpr int kBytes = kStages * kStageBytes;
+};
+static_assert(Ring<true>::kBytes >= kBM * kBN * 2 && Ring<false>::kBytes >= kBM * kBN * 2,
+              "output tile reuses the ring");
 
 __device__ __forceinline__ bf16x8_t as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8_t, v); }
 
@@ -63,8 +82,14 @@ __device__ __forceinline__ void load_to_lds(const void* src, uint8_t* lds) {
   __builtin_amdgcn_global_load_lds(src, (lds_void_t*)lds, 16, 0, 0);
 }
 
+template <int kN>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(kN >= 0 && kN < 64, "vmcnt has 6 bits");
+  __builtin_amdgcn_s_waitcnt((kN & 15) | ((kN >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
 // Wait until at most kN loads of this wave are in flight and its LDS reads
-// are done, then meet the other waves.
+// and writes are done, then meet the other waves.
 template <int kN>
 __device__ __forceinline__ void wait_then_barrier() {
   static_assert(kN >= 0 && kN < 64, "vmcnt has 6 bits");
@@ -74,15 +99,56 @@ __device__ __forceinline__ void wait_then_barrier() {
   __builtin_amdgcn_sched_barrier(0);
 }
 
-// Issue the loads of stage g into `slot`: this wave's quarter of the weight
-// slice and its own 64 rows of H.
+// Weights of one stage in registers (the path that transposes W itself):
+// thread t holds rows k0+2kp and k0+2kp+1 (kp = item % 16) of the 8 columns
+// 8 * (item / 16) .. +7, for its two items t and t + 256.
+struct WRegs {
+  u32x4 lo[2], hi[2];
+};
+
+__device__ __forceinline__ void load_w_regs(const uint16_t* w_k, const uint16_t* w_v, int g, int t,
+                                            WRegs& r) {
+#pragma unroll
+  for (int p = 0; p < 2; ++p) {
+    const int item = t + 256 * p, kp = item & 15, n0 = 8 * (item >> 4);
+    const uint16_t* w = (n0 < kHeadDim ? w_k + n0 : w_v + (n0 - kHeadDim)) +
+                        (size_t)(kBK * g + 2 * kp) * kHeadDim;
+    r.lo[p] = *reinterpret_cast<const u32x4*>(w);
+    r.hi[p] = *reinterpret_cast<const u32x4*>(w + kHeadDim);
+  }
+}
+
+// Element (k, n) of a stage goes to operand block (n / 32, k / 16), lane
+// n % 32 + 32 * (k / 8 % 2), position k % 8; rows k and k+1 share a dword.
+__device__ __forceinline__ void store_w_regs(uint8_t* wst, int t, const WRegs& r) {
+#pragma unroll
+  for (int p = 0; p < 2; ++p) {
+    const int item = t + 256 * p, kp = item & 15, n0 = 8 * (item >> 4);
+    const int k = 2 * kp;
+    const int s = k >> 4, half = (k >> 3) & 1, e = k & 7;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int n = n0 + j;
+      const uint32_t lo = r.lo[p][j >> 1], hi = r.hi[p][j >> 1];
+      const uint32_t v = (j & 1) ? ((lo >> 16) | (hi & 0xFFFF0000u)) : ((lo & 0xFFFFu) | (hi << 16));
+      *reinterpret_cast<uint32_t*>(wst + WLayout<false>::operand(n >> 5, s, (n & 31) + 32 * half) +
+                                   2 * e) = v;
+    }
+  }
+}
+
+// Issue the direct loads of stage g: with packed weights, this wave's quarter
+// of the weight stage; always, the wave's own 64 rows of H.
+template <bool kDirect>
 __device__ __forceinline__ void issue_stage(int g, const uint16_t* w_packed,
                                             const uint16_t* const (&hsrc)[kHLoads], int wave,
                                             int lane, uint8_t* slot) {
-  const uint16_t* ws = w_packed + (size_t)g * (kWStage / 2) + (kWLoads * wave) * 512 + lane * 8;
+  if (kDirect) {
+    const uint16_t* ws = w_packed + (size_t)g * 8192 + (kWLoads * wave) * 512 + lane * 8;
 #pragma unroll
-  for (int j = 0; j < kWLoads; ++j) load_to_lds(ws + j * 512, slot + (kWLoads * wave + j) * 1024);
-  uint8_t* hs = slot + kWStage + wave * kHWave;
+    for (int j = 0; j < kWLoads; ++j) load_to_lds(ws + j * 512, slot + (kWLoads * wave + j) * 1024);
+  }
+  uint8_t* hs = slot + Ring<kDirect>::kWStage + wave * kHWave;
 #pragma unroll
   for (int j = 0; j < kHLoads; ++j) load_to_lds(hsrc[j] + g * kBK, hs + j * 1024);
 }
@@ -92,6 +158,7 @@ struct Operands {
   u32x4 a[2][2], b[2][8];
 };
 
+template <bool kDirect>
 __device__ __forceinline__ void read_operands(const uint8_t* st, const int (&a_off)[2][2], int lane,
                                               Operands& o) {
 #pragma unroll
@@ -100,27 +167,39 @@ __device__ __forceinline__ void read_operands(const uint8_t* st, const int (&a_o
     for (int mt = 0; mt < 2; ++mt) o.a[s][mt] = *reinterpret_cast<const u32x4*>(st + a_off[mt][s]);
 #pragma unroll
     for (int n = 0; n < 8; ++n)
-      o.b[s][n] = *reinterpret_cast<const u32x4*>(st + ((2 * n + s) * 64 + lane) * 16);
+      o.b[s][n] = *reinterpret_cast<const u32x4*>(st + WLayout<kDirect>::operand(n, s, lane));
   }
 }
+
+// Loads issued per wave per stage, in this order: the weight loads (to LDS
+// or to registers), then the H loads.
+constexpr int kLoadsPerStage = kWLoads + kHLoads;
 
 // Stage `it`, whose operands are in `cur`: wait for stage it+1 (which also
 // retires the slot of stage it, read by every wave), refill that slot with
 // stage it+kAhead, read the operands of stage it+1 into `next`, and run the
-// 32 MFMAs of stage it while those reads are in flight.  Every step issues
-// the same loads, so that the wait counts are constants and the step has no
+// 32 MFMAs of stage it while those reads are in flight.  Weights staged
+// through registers are loaded at stage it+kAhead's issue and written to LDS
+// one step later (so `wnext` and `wcur` alternate), after a wait that only
+// forces loads which the next step waits for anyway.  Every step issues the
+// same loads, so that the wait counts are constants and the step has no
 // branch: past the last stage the loads repeat it (cache-resident) into a
 // free slot, and the operands read from it are never used.
+template <bool kDirect>
 __device__ __forceinline__ void bridge_step(int it, int nk, const uint16_t* w_packed,
-                                            const uint16_t* const (&hsrc)[kHLoads], int wave,
-                                            int lane, const int (&a_off)[2][2], uint8_t* lds,
-                                            const Operands& cur, Operands& next,
+                                            const uint16_t* w_k, const uint16_t* w_v,
+                                            const uint16_t* const (&hsrc)[kHLoads], int t,
+                                            int wave, int lane, const int (&a_off)[2][2],
+                                            uint8_t* lds, const Operands& cur, Operands& next,
+                                            WRegs& wnext, const WRegs& wcur,
                                             f32x16_t (&acc)[2][8]) {
+  constexpr int kSB = Ring<kDirect>::kStageBytes;
   // Younger than stage it+1: stages it+2 .. it+kAhead-1.
   wait_then_barrier<(kAhead - 2) * kLoadsPerStage>();
-  issue_stage(min(it + kAhead, nk - 1), w_packed, hsrc, wave, lane,
-              lds + (it % kStages) * kStageBytes);
-  read_operands(lds + ((it + 1) % kStages) * kStageBytes, a_off, lane, next);
+  const int g = min(it + kAhead, nk - 1);
+  if (!kDirect) load_w_regs(w_k, w_v, g, t, wnext);
+  issue_stage<kDirect>(g, w_packed, hsrc, wave, lane, lds + (it % kStages) * kSB);
+  read_operands<kDirect>(lds + ((it + 1) % kStages) * kSB, a_off, lane, next);
 #pragma unroll
   for (int s = 0; s < 2; ++s)
 #pragma unroll
@@ -129,15 +208,24 @@ __device__ __forceinline__ void bridge_step(int it, int nk, const uint16_t* w_pa
       for (int mt = 0; mt < 2; ++mt)
         acc[mt][n] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
             as_bf16x8(cur.a[s][mt]), as_bf16x8(cur.b[s][n]), acc[mt][n], 0, 0, 0);
+  if (!kDirect) {
+    // wcur holds stage it+kAhead-1; younger: its H loads and stage it+kAhead.
+    wait_vm<kHLoads + kLoadsPerStage>();
+    store_w_regs(lds + ((it + kAhead - 1) % kStages) * kSB, t, wcur);
+  }
 }
 
+template <bool kDirect>
 __global__ __launch_bounds__(64 * kWaves) void bridge_gemm(const uint16_t* __restrict__ h,
                                                            int64_t ldh,
                                                            const uint16_t* __restrict__ w_packed,
+                                                           const uint16_t* __restrict__ w_k,
+                                                           const uint16_t* __restrict__ w_v,
                                                            uint16_t* __restrict__ k_out,
                                                            uint16_t* __restrict__ v_out,
                                                            int64_t ld_kv, int M, int d_model) {
-  __shared__ __attribute__((aligned(16))) uint8_t lds[kStages * kStageBytes];
+  constexpr int kSB = Ring<kDirect>::kStageBytes;
+  __shared__ __attribute__((aligned(16))) uint8_t lds[Ring<kDirect>::kBytes];
   const int t = threadIdx.x;
   const int lane = t & 63, wave = t >> 6;
   const int r32 = lane & 31, hh = lane >> 5;
@@ -159,7 +247,8 @@ __global__ __launch_bounds__(64 * kWaves) void bridge_gemm(const uint16_t* __res
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
       const int row = 32 * mt + r32, chunk = 2 * s + hh;
-      a_off[mt][s] = kWStage + wave * kHWave + 16 * (4 * row + (chunk ^ ((row >> 2) & 3)));
+      a_off[mt][s] = Ring<kDirect>::kWStage + wave * kHWave +
+                     16 * (4 * row + (chunk ^ ((row >> 2) & 3)));
     }
 
   f32x16_t acc[2][8];
@@ -169,15 +258,38 @@ __global__ __launch_bounds__(64 * kWaves) void bridge_gemm(const uint16_t* __res
     for (int n = 0; n < 8; ++n) acc[mt][n] = (f32x16_t){};
 
   const int nk = d_model / kBK;  // even: d_model is a multiple of 64
+  WRegs w0, w1;
+  if (kDirect) {
 #pragma unroll
-  for (int g = 0; g < kAhead; ++g)
-    issue_stage(min(g, nk - 1), w_packed, hsrc, wave, lane, lds + g * kStageBytes);
+    for (int g = 0; g < kAhead; ++g)
+      issue_stage<true>(min(g, nk - 1), w_packed, hsrc, wave, lane, lds + g * kSB);
+  } else {
+    // Same issue order as the steps (weights, then H, per stage).  Stages
+    // 0..2 are written to LDS here; stage 3 stays in w1 for the first step.
+    static_assert(kAhead == 4, "prologue written for four stages");
+    load_w_regs(w_k, w_v, 0, t, w0);
+    issue_stage<false>(0, w_packed, hsrc, wave, lane, lds);
+    load_w_regs(w_k, w_v, min(1, nk - 1), t, w1);
+    issue_stage<false>(min(1, nk - 1), w_packed, hsrc, wave, lane, lds + kSB);
+    wait_vm<kHLoads + kLoadsPerStage>();
+    store_w_regs(lds, t, w0);
+    wait_vm<kHLoads>();
+    store_w_regs(lds + kSB, t, w1);
+    load_w_regs(w_k, w_v, min(2, nk - 1), t, w0);
+    issue_stage<false>(min(2, nk - 1), w_packed, hsrc, wave, lane, lds + 2 * kSB);
+    load_w_regs(w_k, w_v, min(3, nk - 1), t, w1);
+    issue_stage<false>(min(3, nk - 1), w_packed, hsrc, wave, lane, lds + 3 * kSB);
+    wait_vm<kHLoads + kLoadsPerStage>();
+    store_w_regs(lds + 2 * kSB, t, w0);
+  }
   wait_then_barrier<(kAhead - 1) * kLoadsPerStage>();  // stage 0
   Operands o0, o1;
-  read_operands(lds, a_off, lane, o0);
+  read_operands<kDirect>(lds, a_off, lane, o0);
   for (int it = 0; it < nk; it += 2) {
-    bridge_step(it, nk, w_packed, hsrc, wave, lane, a_off, lds, o0, o1, acc);
-    bridge_step(it + 1, nk, w_packed, hsrc, wave, lane, a_off, lds, o1, o0, acc);
+    bridge_step<kDirect>(it, nk, w_packed, w_k, w_v, hsrc, t, wave, lane, a_off, lds, o0, o1, w0,
+                         w1, acc);
+    bridge_step<kDirect>(it + 1, nk, w_packed, w_k, w_v, hsrc, t, wave, lane, a_off, lds, o1, o0,
+                         w1, w0, acc);
   }
   wait_then_barrier<0>();  // every wave is done with the ring
 
@@ -235,10 +347,15 @@ hipError_t launch_bridge_pack(const uint16_t* w_k, const uint16_t* w_v, uint16_t
 }
 
 hipError_t launch_bridge(const uint16_t* h, int64_t ldh, const uint16_t* w_packed,
-                         uint16_t* k_out, uint16_t* v_out, int64_t ld_kv, int M, int d_model,
-                         hipStream_t st) {
+                         const uint16_t* w_k, const uint16_t* w_v, uint16_t* k_out,
+                         uint16_t* v_out, int64_t ld_kv, int M, int d_model, hipStream_t st) {
   const int grid = (M + kBM - 1) / kBM;
-  bridge_gemm<<<grid, 64 * kWaves, 0, st>>>(h, ldh, w_packed, k_out, v_out, ld_kv, M, d_model);
+  if (w_packed != nullptr)
+    bridge_gemm<true><<<grid, 64 * kWaves, 0, st>>>(h, ldh, w_packed, nullptr, nullptr, k_out,
+                                                    v_out, ld_kv, M, d_model);
+  else
+    bridge_gemm<false><<<grid, 64 * kWaves, 0, st>>>(h, ldh, nullptr, w_k, w_v, k_out, v_out,
+                                                     ld_kv, M, d_model);
   return hipGetLastError();
 }
 

@@ -10,8 +10,8 @@ namespace hs2 {
 hipError_t launch_bridge_pack(const uint16_t* w_k, const uint16_t* w_v, uint16_t* w_packed,
                               int d_model, hipStream_t st);
 hipError_t launch_bridge(const uint16_t* h, int64_t ldh, const uint16_t* w_packed,
-                         uint16_t* k_out, uint16_t* v_out, int64_t ld_kv, int M, int d_model,
-                         hipStream_t st);
+                         const uint16_t* w_k, const uint16_t* w_v, uint16_t* k_out,
+                         uint16_t* v_out, int64_t ld_kv, int M, int d_model, hipStream_t st);
 
 namespace {
 
@@ -58,6 +58,16 @@ hs2_status check_ws(const hs2_attn_desc& d, int cap, const void* ws, size_t ws_b
 }
 
 hs2_status launched(hipError_t e) { return e == hipSuccess ? HS2_OK : HS2_EHIP; }
+
+hs2_status check_bridge(const uint16_t* h, int64_t ldh, uint16_t* k_out, uint16_t* v_out,
+                        int64_t ld_kv, int M, int d_model, int head_dim) {
+  if (h == nullptr || k_out == nullptr || v_out == nullptr) return HS2_EINVAL;
+  if (M < 1 || d_model < 1 || head_dim < 1 || ldh < d_model || ld_kv < head_dim) return HS2_EINVAL;
+  if (head_dim != kHeadDim || d_model % 64 != 0) return HS2_EUNSUPPORTED;
+  if (ldh % 8 != 0 || ld_kv % 8 != 0) return HS2_EALIGN;
+  if (misaligned(h) || misaligned(k_out) || misaligned(v_out)) return HS2_EALIGN;
+  return HS2_OK;
+}
 
 }  // namespace
 }  // namespace hs2
@@ -187,6 +197,30 @@ hs2_status hs2_decode_step(const hs2_attn_desc* desc, const void* q, const void*
                                 top_cnt, o, lse, w + l.sparse, st));
 }
 
+hs2_status hs2_bridge_kv(const uint16_t* h, int64_t ldh, const uint16_t* w_k, const uint16_t* w_v,
+                         uint16_t* k_out, uint16_t* v_out, int64_t ld_kv, int M, int d_model,
+                         int head_dim, hs2_stream_t stream) {
+  if (w_k == nullptr || w_v == nullptr) return HS2_EINVAL;
+  const hs2_status st = check_bridge(h, ldh, k_out, v_out, ld_kv, M, d_model, head_dim);
+  if (st != HS2_OK) return st;
+  if (misaligned(w_k) || misaligned(w_v)) return HS2_EALIGN;
+  (void)hipGetLastError();
+  return launched(launch_bridge(h, ldh, nullptr, w_k, w_v, k_out, v_out, ld_kv, M, d_model,
+                                static_cast<hipStream_t>(stream)));
+}
+
+hs2_status hs2_bridge_kv_packed(const uint16_t* h, int64_t ldh, const uint16_t* w_packed,
+                                uint16_t* k_out, uint16_t* v_out, int64_t ld_kv, int M,
+                                int d_model, int head_dim, hs2_stream_t stream) {
+  if (w_packed == nullptr) return HS2_EINVAL;
+  const hs2_status st = check_bridge(h, ldh, k_out, v_out, ld_kv, M, d_model, head_dim);
+  if (st != HS2_OK) return st;
+  if (misaligned(w_packed)) return HS2_EALIGN;
+  (void)hipGetLastError();
+  return launched(launch_bridge(h, ldh, w_packed, nullptr, nullptr, k_out, v_out, ld_kv, M,
+                                d_model, static_cast<hipStream_t>(stream)));
+}
+
 size_t hs2_bridge_packed_bytes(int d_model, int head_dim) {
   if (d_model < 64 || d_model % 64 != 0 || head_dim != kHeadDim) return 0;
   return (size_t)d_model * 2 * kHeadDim * sizeof(uint16_t);
@@ -200,21 +234,6 @@ hs2_status hs2_bridge_pack_weights(const uint16_t* w_k, const uint16_t* w_v, int
   if (misaligned(w_k) || misaligned(w_v) || misaligned(w_packed)) return HS2_EALIGN;
   (void)hipGetLastError();
   return launched(launch_bridge_pack(w_k, w_v, w_packed, d_model, static_cast<hipStream_t>(stream)));
-}
-
-hs2_status hs2_bridge_kv(const uint16_t* h, int64_t ldh, const uint16_t* w_packed,
-                         uint16_t* k_out, uint16_t* v_out, int64_t ld_kv, int M, int d_model,
-                         int head_dim, hs2_stream_t stream) {
-  if (h == nullptr || w_packed == nullptr || k_out == nullptr || v_out == nullptr)
-    return HS2_EINVAL;
-  if (M < 1 || d_model < 1 || head_dim < 1 || ldh < d_model || ld_kv < head_dim) return HS2_EINVAL;
-  if (head_dim != kHeadDim || d_model % 64 != 0) return HS2_EUNSUPPORTED;
-  if (ldh % 8 != 0 || ld_kv % 8 != 0) return HS2_EALIGN;
-  if (misaligned(h) || misaligned(w_packed) || misaligned(k_out) || misaligned(v_out))
-    return HS2_EALIGN;
-  (void)hipGetLastError();
-  return launched(launch_bridge(h, ldh, w_packed, k_out, v_out, ld_kv, M, d_model,
-                                static_cast<hipStream_t>(stream)));
 }
 
 const char* hs2_status_string(hs2_status status) {

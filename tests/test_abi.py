@@ -157,21 +157,33 @@ def test_decode_step_validation(lib):
     assert hs2.hs2_workspace_size(d, big) == 0
 
 
-def test_bridge_validation(lib):
+@pytest.mark.parametrize("packed", [False, True])
+def test_bridge_validation(lib, packed):
     L = hs2.load()
-    br = lambda **kw: L.hs2_bridge_kv(  # noqa: E731
-        kw.get("h", FAKE), kw.get("ldh", 2048), kw.get("wp", FAKE), FAKE, kw.get("vo", FAKE),
-        kw.get("ldkv", 128), kw.get("M", 1024), kw.get("dm", 2048), kw.get("hd", 128), None)
+
+    def br(**kw):
+        args = (kw.get("h", FAKE), kw.get("ldh", 2048))
+        tail = (kw.get("ko", FAKE), kw.get("vo", FAKE), kw.get("ldkv", 128), kw.get("M", 1024),
+                kw.get("dm", 2048), kw.get("hd", 128), None)
+        if packed:
+            return L.hs2_bridge_kv_packed(*args, kw.get("wk", FAKE), *tail)
+        return L.hs2_bridge_kv(*args, kw.get("wk", FAKE), kw.get("wv", FAKE), *tail)
+
     assert br(h=None) == hs2.HS2_EINVAL
-    assert br(wp=None) == hs2.HS2_EINVAL
+    assert br(wk=None) == hs2.HS2_EINVAL
     assert br(vo=None) == hs2.HS2_EINVAL
     assert br(M=0) == hs2.HS2_EINVAL
     assert br(ldh=1024) == hs2.HS2_EINVAL
+    assert br(ldkv=64) == hs2.HS2_EINVAL
     assert br(hd=64, ldkv=128) == hs2.HS2_EUNSUPPORTED
     assert br(dm=100, ldh=2048) == hs2.HS2_EUNSUPPORTED
     assert br(ldh=2052) == hs2.HS2_EALIGN
     assert br(h=ODD) == hs2.HS2_EALIGN
-    assert br(wp=ODD) == hs2.HS2_EALIGN
+    assert br(wk=ODD) == hs2.HS2_EALIGN
+    assert br(ko=ODD) == hs2.HS2_EALIGN
+    if not packed:
+        assert br(wv=None) == hs2.HS2_EINVAL
+        assert br(wv=ODD) == hs2.HS2_EALIGN
 
 
 def test_bridge_pack_validation(lib):
@@ -193,5 +205,5 @@ def test_bridge_pack_validation(lib):
 
 def test_binding_raises_on_error_status(lib):
     with pytest.raises(hs2.HS2Error) as ei:
-        hs2.hs2_bridge_kv(None, 2048, FAKE, FAKE, FAKE, 128, 1024, 2048, stream=0)
+        hs2.hs2_bridge_kv(None, 2048, FAKE, FAKE, FAKE, FAKE, 128, 1024, 2048, stream=0)
     assert ei.value.status == hs2.HS2_EINVAL

@@ -35,7 +35,7 @@ def _check_rows(k_gpu_bits, v_gpu_bits, inp, rows):
 
 
 def _run(m_rows, d_model, rows=None, ld_kv=128):
-    from kv_cache_reuse_hs2_amd import hs2_bridge_kv
+    from kv_cache_reuse_hs2_amd import hs2_bridge_kv, hs2_bridge_kv_packed
     from kv_cache_reuse_hs2_amd.torch_api import pack_bridge_weights, to_device
 
     w = WORKLOADS["bridge_decode_bf16_1m"].replace(d_model=d_model)
@@ -46,9 +46,14 @@ def _run(m_rows, d_model, rows=None, ld_kv=128):
     v = torch.zeros((m_rows, ld_kv), dtype=torch.int16, device="cuda")
     print(f"[gpu] bridge M={m_rows} d_model={d_model} ld_kv={ld_kv}", flush=True)
     sys.stdout.flush()
+    hs2_bridge_kv(h, d_model, wk, wv, k, v, ld_kv, m_rows, d_model)
+    # The packed-weight entry point gives the same bits.
     wp = pack_bridge_weights(wk, wv, d_model)
-    hs2_bridge_kv(h, d_model, wp, k, v, ld_kv, m_rows, d_model)
+    k2, v2 = torch.zeros_like(k), torch.zeros_like(v)
+    hs2_bridge_kv_packed(h, d_model, wp, k2, v2, ld_kv, m_rows, d_model)
     torch.cuda.synchronize()
+    assert torch.equal(k, k2) and torch.equal(v, v2)
+    del k2, v2
     kb = k.cpu().numpy().view(np.uint16)[:, :128]
     vb = v.cpu().numpy().view(np.uint16)[:, :128]
     if rows is None:
