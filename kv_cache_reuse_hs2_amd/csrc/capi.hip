@@ -187,7 +187,7 @@ hs2_status hs2_decode_step(const hs2_attn_desc* desc, const void* q, const void*
   if (e != hipSuccess) return HS2_EHIP;
   const size_t hist_off = pf ? prefill_ws(*desc, kv_capacity).hist_off
                              : score_ws(*desc, kv_capacity).hist_off;
-  const uint32_t* hist = fuse ? reinterpret_cast<const uint32_t*>(w + l.score + hist_off) : nullptr;
+  uint32_t* hist = fuse ? reinterpret_cast<uint32_t*>(w + l.score + hist_off) : nullptr;
   e = launch_select(*desc, scores, ctx_len, kv_capacity, top_idx, top_cnt, w + l.select, hist, st);
   if (e != hipSuccess) return HS2_EHIP;
   if (pf)

@@ -25,6 +25,9 @@ constexpr int kPfSplit = 8192;
 constexpr int kSparseSeg = 32;
 // Top-k selection: first radix digit = top 12 bits of the orderable key.
 constexpr int kSelBins = 4096;
+// Selector histograms per row: the top 12 key bits of the pool, then the next
+// 12 bits of the keys in the threshold bin (built while filtering).
+constexpr int kHistRow = 2 * kSelBins;
 constexpr int kSelSlice = 4096;  // pool keys per workgroup of the selector passes
 
 // ---------------------------------------------------------------------------
@@ -75,13 +78,14 @@ inline int score_nchunks1(const hs2_attn_desc& d, int cap) {
 struct ScoreWs {
   size_t stats_off;  // float2 [B][nchunks1][32]  (max, sum) per chunk & head, base 2
   size_t lse2_off;   // float  [B][32]             per-head log2-sum-exp (fp32 path)
-  size_t hist_off;   // uint32 [B][kSelBins]       selector histogram (fused step)
+  size_t hist_off;   // uint32 [B][kHistRow]       selector histograms (fused step)
   size_t bytes;
 };
 
 struct SelectWs {
-  size_t hist_off;    // uint32 [R][kSelBins]            (standalone selection)
+  size_t hist_off;    // uint32 [R][kHistRow]            (standalone selection)
   size_t cnt_off;     // uint32 [R][nslices]             entries kept per slice
+  size_t meta_off;    // uint32 [R][4]                   threshold bin, keys above it
   size_t list_off;    // uint2  [R][nslices][kSelSlice]  (key, index), index order
   size_t bytes;
 };
@@ -97,7 +101,7 @@ inline bool is_prefill(const hs2_attn_desc& d) { return d.tile_q > 1; }
 struct PrefillWs {
   size_t stats_off;   // float2 [B][nsplit][n_q][32]
   size_t colsum_off;  // float  [B][n_q/16][cap]
-  size_t hist_off;    // uint32 [B][tiles][kSelBins]
+  size_t hist_off;    // uint32 [B][tiles][kHistRow]
   size_t bytes;
 };
 
@@ -110,7 +114,7 @@ inline PrefillWs prefill_ws(const hs2_attn_desc& d, int cap) {
   w.colsum_off = off;
   off = align_up(off + sizeof(float) * (size_t)d.batch * (d.n_q / 16) * cap, 256);
   w.hist_off = off;
-  off = align_up(off + sizeof(uint32_t) * (size_t)d.batch * (d.n_q / d.tile_q) * kSelBins, 256);
+  off = align_up(off + sizeof(uint32_t) * (size_t)d.batch * (d.n_q / d.tile_q) * kHistRow, 256);
   w.bytes = off;
   return w;
 }
@@ -123,7 +127,7 @@ inline ScoreWs score_ws(const hs2_attn_desc& d, int cap) {
   w.lse2_off = off;
   off = align_up(off + sizeof(float) * (size_t)d.batch * d.n_q * kMaxHeads, 256);
   w.hist_off = off;
-  off = align_up(off + sizeof(uint32_t) * (size_t)d.batch * kSelBins, 256);
+  off = align_up(off + sizeof(uint32_t) * (size_t)d.batch * kHistRow, 256);
   w.bytes = off;
   return w;
 }
@@ -136,9 +140,11 @@ inline SelectWs select_ws(const hs2_attn_desc& d, int cap) {
   const size_t ns = select_slices(cap);
   size_t off = 0;
   w.hist_off = off;
-  off = align_up(off + sizeof(uint32_t) * rows * kSelBins, 256);
+  off = align_up(off + sizeof(uint32_t) * rows * kHistRow, 256);
   w.cnt_off = off;
   off = align_up(off + sizeof(uint32_t) * rows * ns, 256);
+  w.meta_off = off;
+  off = align_up(off + sizeof(uint32_t) * rows * 4, 256);
   w.list_off = off;
   off = align_up(off + sizeof(uint32_t) * 2 * rows * ns * kSelSlice, 256);
   w.bytes = off;
@@ -192,7 +198,7 @@ hipError_t launch_score_decode(const hs2_attn_desc& d, const void* q, const void
 // with_hist), or null to build one.
 hipError_t launch_select(const hs2_attn_desc& d, const float* scores, const int32_t* ctx_len,
                          int cap, int32_t* top_idx, int32_t* top_cnt, char* ws,
-                         const uint32_t* hist, hipStream_t st);
+                         uint32_t* hist, hipStream_t st);
 
 // Chunked prefill (tile_q > 1, bf16): scoring over query tiles and sparse
 // attention of the tiles' queries.

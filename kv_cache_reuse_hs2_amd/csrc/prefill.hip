@@ -282,14 +282,14 @@ __global__ __launch_bounds__(256) void pf_reduce(PfArgs a, float* scores, uint32
   }
   if (kHist) {
     __syncthreads();
-    uint32_t* gh = hist + ((size_t)b * tiles + t) * kSelBins;
+    uint32_t* gh = hist + ((size_t)b * tiles + t) * kHistRow;
     for (int e = threadIdx.x; e < kSelBins; e += blockDim.x)
       if (s_hist[e] != 0u) atomicAdd(&gh[e], s_hist[e]);
   }
 }
 
 __global__ __launch_bounds__(256) void pf_hist_init(uint32_t* hist) {
-  for (int e = threadIdx.x; e < kSelBins; e += blockDim.x) hist[(size_t)blockIdx.x * kSelBins + e] = 0u;
+  for (int e = threadIdx.x; e < kHistRow; e += blockDim.x) hist[(size_t)blockIdx.x * kHistRow + e] = 0u;
 }
 
 // ---------------------------------------------------------------------------
@@ -448,7 +448,7 @@ __global__ __launch_bounds__(64 * kSpWaves) void pf_sparse(PfArgs a) {
 // Workspace of the prefill scoring (inside the scoring region):
 //   stats  float2 [B][nsplit][n_q][32]
 //   colsum float  [B][n_q/16][cap]
-//   hist   uint32 [B][tiles][kSelBins]
+//   hist   uint32 [B][tiles][kHistRow]
 hipError_t launch_prefill_scores(const hs2_attn_desc& d, const void* q, const void* k,
                                  int64_t kv_stride, const int32_t* ctx_len, int cap,
                                  float* scores, float* lse, char* ws, bool with_hist,

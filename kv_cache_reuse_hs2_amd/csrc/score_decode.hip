@@ -80,7 +80,7 @@ __global__ __launch_bounds__(64 * kP1Waves) void score_p1_bf16(
   const int j_begin = c * kP1Chunk;
   float2* st = stats + ((size_t)b * nchunks + c) * kMaxHeads;
   if (hist != nullptr && c == 0)
-    for (int i = threadIdx.x; i < kSelBins; i += blockDim.x) hist[(size_t)b * kSelBins + i] = 0u;
+    for (int i = threadIdx.x; i < kHistRow; i += blockDim.x) hist[(size_t)b * kHistRow + i] = 0u;
   if (j_begin >= N) {
     if (threadIdx.x < kMaxHeads) st[threadIdx.x] = make_float2(-INFINITY, 0.f);
     return;
@@ -221,7 +221,7 @@ __global__ __launch_bounds__(64 * kP2Waves) void score_p2_bf16(
   }
   if (kHist) {
     __syncthreads();
-    uint32_t* gh = hist + (size_t)b * kSelBins;
+    uint32_t* gh = hist + (size_t)b * kHistRow;
     for (int i = threadIdx.x; i < kSelBins; i += blockDim.x)
       if (s_hist[i] != 0u) atomicAdd(&gh[i], s_hist[i]);
   }

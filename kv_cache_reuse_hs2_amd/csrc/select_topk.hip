@@ -18,9 +18,12 @@
 //   sel_filter: every 4,096-key slice finds the threshold bin b0 from the
 //       histogram and keeps its keys whose top bits are >= b0 (all keys
 //       above b0 are selected, fewer than k of them; keys in b0 are
-//       candidates), written in index order to the slice's list.
-//   sel_final: one workgroup per row resolves the remaining 20 key bits over
-//       the candidates, then the lowest indices among exact ties, and writes
+//       candidates), written in index order to the slice's list; it also
+//       adds key bits 19..8 of its keys in b0 to the row's second-level
+//       histogram.
+//   sel_final: one workgroup per row reads both histograms, which fix the
+//       top 24 bits of the threshold, resolves the last 8 bits over the
+//       candidates, then the lowest indices among exact ties, and writes
 //       the winners by an ordered compaction of the concatenated slice
 //       lists, which are in index order already: no sort is needed.
 // Rows whose pool fits the budget skip the radix passes and take the pool.
@@ -120,9 +123,44 @@ __device__ void find_bin_desc(const uint32_t* hist, int nbins, uint32_t need, ui
   __syncthreads();
 }
 
+// find_bin_desc over a histogram held in registers: thread t owns bins
+// [kPer t, kPer t + kPer) (threads past the histogram hold zeros).  res must
+// not be read between this call and the previous use of the same array
+// without a barrier in between.
+template <int kPer>
+__device__ void find_bin_regs(const uint32_t (&v)[kPer], uint32_t need, uint32_t* scratch,
+                              uint32_t* res) {
+  const int t = threadIdx.x;
+  uint32_t local = 0;
+#pragma unroll
+  for (int e = 0; e < kPer; ++e) local += v[e];
+  if (t == 0) {
+    res[0] = 0u;
+    res[1] = 0u;
+  }
+  const uint32_t suf = block_suffix_sum(local, scratch);
+  const uint32_t above = suf - local;
+  if (above < need && need <= suf) {
+    uint32_t cum = above, bin = 0, cab = 0;
+    bool found = false;
+#pragma unroll
+    for (int e = kPer - 1; e >= 0; --e) {
+      if (!found && cum + v[e] >= need) {
+        bin = (uint32_t)e;
+        cab = cum;
+        found = true;
+      }
+      cum += v[e];
+    }
+    res[0] = (uint32_t)t * kPer + bin;
+    res[1] = cab;
+  }
+  __syncthreads();
+}
+
 __global__ __launch_bounds__(256) void sel_init(uint32_t* __restrict__ hist) {
   const int r = blockIdx.x;
-  for (int i = threadIdx.x; i < kSelBins; i += blockDim.x) hist[(size_t)r * kSelBins + i] = 0u;
+  for (int i = threadIdx.x; i < kHistRow; i += blockDim.x) hist[(size_t)r * kHistRow + i] = 0u;
 }
 
 __global__ __launch_bounds__(256) void sel_hist(const float* __restrict__ scores, int cap,
@@ -140,29 +178,31 @@ __global__ __launch_bounds__(256) void sel_hist(const float* __restrict__ scores
   const float* row = scores + (size_t)r * cap;
   for (int j = s0 + threadIdx.x; j < s1; j += blockDim.x) atomicAdd(&h[order_key(row[j]) >> 20], 1u);
   __syncthreads();
-  uint32_t* gh = hist + (size_t)r * kSelBins;
+  uint32_t* gh = hist + (size_t)r * kHistRow;
   for (int i = threadIdx.x; i < kSelBins; i += blockDim.x)
     if (h[i] != 0u) atomicAdd(&gh[i], h[i]);
 }
 
 constexpr int kPer = kSelSlice / 256;  // keys per thread in sel_filter
 
+// Above this many threshold-bin keys in a slice, the second-level histogram
+// is merged in LDS first instead of one global atomic per key.
+constexpr uint32_t kDirectHist2 = 256;
+
 template <bool kVec4>
 __global__ __launch_bounds__(256) void sel_filter(const float* __restrict__ scores, int cap,
                                                   const int32_t* __restrict__ ctx_len, int tiles,
                                                   int n_q, int tile_q, int k_top, int window,
-                                                  const uint32_t* __restrict__ hist,
+                                                  uint32_t* __restrict__ hist,
                                                   uint32_t* __restrict__ cnt,
+                                                  uint32_t* __restrict__ meta,
                                                   uint2* __restrict__ list, int nslices) {
   const int r = blockIdx.y, s = blockIdx.x;
   const RowGeom g = row_geom(ctx_len, cap, r, tiles, n_q, tile_q, k_top, window);
   const int s0 = s * kSelSlice;
   if (g.kk == 0 || g.kk == g.pe || s0 >= g.pe) return;
-  __shared__ uint32_t scratch[8];
-  __shared__ uint32_t res[2];
-  find_bin_desc(hist + (size_t)r * kSelBins, kSelBins, (uint32_t)g.kk, scratch, res);
-  const uint32_t b0 = res[0];
-  // Thread t owns the 16 consecutive keys s0 + 16t .. s0 + 16t + 15.
+  // Thread t owns the 16 consecutive keys s0 + 16t .. s0 + 16t + 15; they are
+  // loaded first so that the loads overlap the threshold search.
   const int j0 = s0 + kPer * threadIdx.x;
   const float* row = scores + (size_t)r * cap;
   uint32_t key[kPer];
@@ -179,16 +219,57 @@ __global__ __launch_bounds__(256) void sel_filter(const float* __restrict__ scor
 #pragma unroll
     for (int e = 0; e < kPer; ++e) key[e] = (j0 + e < g.pe) ? order_key(row[j0 + e]) : 0u;
   }
-  uint32_t keep = 0;
+  __shared__ uint32_t scratch[8];
+  __shared__ uint32_t res[2];
+  __shared__ uint32_t h2[kSelBins];
+  uint32_t* hrow = hist + (size_t)r * kHistRow;
+  static_assert(kSelBins == 16 * 256, "sixteen bins per thread");
+  uint32_t hv[16];
 #pragma unroll
-  for (int e = 0; e < kPer; ++e) keep += (j0 + e < g.pe && (key[e] >> 20) >= b0) ? 1u : 0u;
-  uint32_t total;
+  for (int i = 0; i < 4; ++i) {
+    const u32x4 x = *reinterpret_cast<const u32x4*>(hrow + 16 * threadIdx.x + 4 * i);
+    hv[4 * i] = x.x;
+    hv[4 * i + 1] = x.y;
+    hv[4 * i + 2] = x.z;
+    hv[4 * i + 3] = x.w;
+  }
+  find_bin_regs(hv, (uint32_t)g.kk, scratch, res);
+  const uint32_t b0 = res[0];
+  uint32_t keep = 0, in_b0 = 0;
+#pragma unroll
+  for (int e = 0; e < kPer; ++e) {
+    const bool valid = j0 + e < g.pe;
+    keep += (valid && (key[e] >> 20) >= b0) ? 1u : 0u;
+    in_b0 += (valid && (key[e] >> 20) == b0) ? 1u : 0u;
+  }
+  uint32_t total, total_b0;
   uint32_t pos = block_prefix_sum(keep, scratch, &total);
+  (void)block_prefix_sum(in_b0, scratch, &total_b0);
   uint2* out = list + ((size_t)r * nslices + s) * kSelSlice;
 #pragma unroll
   for (int e = 0; e < kPer; ++e)
     if (j0 + e < g.pe && (key[e] >> 20) >= b0) out[pos++] = make_uint2(key[e], (uint32_t)(j0 + e));
   if (threadIdx.x == 0) cnt[(size_t)r * nslices + s] = total;
+  if (s == 0 && threadIdx.x == 0) {
+    meta[4 * r] = b0;
+    meta[4 * r + 1] = res[1];  // pool keys above bin b0
+  }
+  // Second level: key bits 19..8 of this slice's keys in the threshold bin.
+  uint32_t* g2 = hrow + kSelBins;
+  if (total_b0 <= kDirectHist2) {
+#pragma unroll
+    for (int e = 0; e < kPer; ++e)
+      if (j0 + e < g.pe && (key[e] >> 20) == b0) atomicAdd(&g2[(key[e] >> 8) & 0xFFFu], 1u);
+  } else {
+    for (int i = threadIdx.x; i < kSelBins; i += blockDim.x) h2[i] = 0u;
+    __syncthreads();
+#pragma unroll
+    for (int e = 0; e < kPer; ++e)
+      if (j0 + e < g.pe && (key[e] >> 20) == b0) atomicAdd(&h2[(key[e] >> 8) & 0xFFFu], 1u);
+    __syncthreads();
+    for (int i = threadIdx.x; i < kSelBins; i += blockDim.x)
+      if (h2[i] != 0u) atomicAdd(&g2[i], h2[i]);
+  }
 }
 
 constexpr int kMaxSlices = 1024;  // pools up to 4,194,304 keys
@@ -198,11 +279,12 @@ __global__ __launch_bounds__(1024) void sel_final(const int32_t* __restrict__ ct
                                                   int tiles, int n_q, int tile_q, int k_top,
                                                   int window, const uint32_t* __restrict__ hist,
                                                   const uint32_t* __restrict__ cnt,
+                                                  const uint32_t* __restrict__ meta,
                                                   const uint2* __restrict__ list, int nslices,
                                                   int32_t* __restrict__ top_idx,
                                                   int32_t* __restrict__ top_cnt) {
   const int r = blockIdx.x;
-  const int t = threadIdx.x;
+  const int t = threadIdx.x;  // blockDim.x == 1024
   const RowGeom g = row_geom(ctx_len, cap, r, tiles, n_q, tile_q, k_top, window);
   int32_t* out = top_idx + (size_t)r * k_top;
   if (g.kk == 0 || g.kk == g.pe) {
@@ -210,22 +292,58 @@ __global__ __launch_bounds__(1024) void sel_final(const int32_t* __restrict__ ct
     if (t == 0) top_cnt[r] = g.kk;
     return;
   }
-  __shared__ uint32_t h[kSelBins];
+  // Bits 7..0 of the threshold; then up to 2,048 bins of the tie passes.
+  __shared__ __attribute__((aligned(16))) uint32_t h[2048];
   __shared__ uint32_t pre[kMaxSlices + 1];
-  __shared__ uint32_t scratch[16];
-  __shared__ uint32_t res[2];
-
-  // Offsets of the slice lists; their concatenation is in index order.
+  __shared__ uint32_t chunk_wins[kStage / 64];
+  __shared__ __attribute__((aligned(16))) uint32_t scratch[16];
+  __shared__ uint32_t res_b[2], res_c[2], res[2];
+  const int lane = t & 63, wave = t >> 6;
   const int ns = (g.pe + kSelSlice - 1) / kSelSlice;
-  uint32_t total = 0;
-  {
-    const uint32_t c = (t < ns) ? cnt[(size_t)r * nslices + t] : 0u;
-    const uint32_t p = block_prefix_sum(c, scratch, &total);
-    if (t < ns) pre[t] = p;
-    if (t == 0) pre[ns] = total;
-    __syncthreads();
-  }
   const uint2* lr = list + (size_t)r * nslices * kSelSlice;
+
+  // Everything that does not depend on another load is fetched at once: the
+  // threshold bin b0 that sel_filter found, the second-level histogram (bins
+  // 4t .. 4t+3 per thread), the slice counts, and the head of each slice
+  // list this wave will copy (slices wave + 16u, entries 0..63).
+  const uint32_t* hrow = hist + (size_t)r * kHistRow;
+  static_assert(kSelBins == 4 * 1024, "four bins per thread");
+  const u32x4 x2 = *reinterpret_cast<const u32x4*>(hrow + kSelBins + 4 * t);
+  const uint32_t b0 = meta[4 * r], above0 = meta[4 * r + 1];
+  uint2 head[4];
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const int sl = wave + 16 * u;
+    if (sl < ns) head[u] = lr[(size_t)sl * kSelSlice + lane];
+  }
+  if (t < 256) h[t] = 0u;  // key bits 7..0, counted while staging
+
+  // Slice offsets: one wave scans the counts 64 at a time.
+  if (wave == 0) {
+    uint32_t carry = 0;
+    for (int c0 = 0; c0 < ns; c0 += 64) {
+      const uint32_t c = (c0 + lane < ns) ? cnt[(size_t)r * nslices + c0 + lane] : 0u;
+      uint32_t incl = c;
+#pragma unroll
+      for (int off = 1; off < 64; off <<= 1) {
+        const uint32_t o = __shfl_up(incl, off);
+        if (lane >= off) incl += o;
+      }
+      if (c0 + lane < ns) pre[c0 + lane] = carry + incl - c;
+      carry += __shfl(incl, 63);
+    }
+    if (lane == 0) pre[ns] = carry;
+  }
+
+  // Bits 19..8 of the threshold among the keys of b0.
+  const uint32_t need0 = (uint32_t)g.kk - above0;
+  const uint32_t v2[4] = {x2.x, x2.y, x2.z, x2.w};
+  find_bin_regs(v2, need0, scratch, res_b);  // its barriers also publish pre[]
+  const uint32_t b1 = res_b[0];
+  const uint32_t need1 = need0 - res_b[1];
+  const uint32_t top24 = (b0 << 12) | b1;
+  const uint32_t total = pre[ns];
+
   auto entry_global = [&](uint32_t gi) -> uint2 {
     int lo = 0, hi = ns - 1;  // last slice with pre[s] <= gi
     while (lo < hi) {
@@ -235,46 +353,55 @@ __global__ __launch_bounds__(1024) void sel_final(const int32_t* __restrict__ ct
     }
     return lr[(size_t)lo * kSelSlice + (gi - pre[lo])];
   };
-  // The radix passes below read the list several times: keep it in LDS when
-  // it fits (the usual case: keys above the threshold bin plus that bin).
+  // The list is read twice more: keep it in LDS when it fits (the usual
+  // case: keys above the threshold bin plus that bin).  Each wave copies
+  // whole slices, four at a time so that their loads overlap, and counts key
+  // bits 7..0 of the candidates that match the top 24 bits on the way.
   __shared__ uint2 stage[kStage];
   const bool staged = total <= (uint32_t)kStage;
+  auto put = [&](uint32_t pos, uint2 e) {
+    stage[pos] = e;
+    if ((e.x >> 8) == top24) atomicAdd(&h[e.x & 0xFFu], 1u);
+  };
   if (staged) {
-    for (uint32_t e = t; e < total; e += blockDim.x) stage[e] = entry_global(e);
-    __syncthreads();
+    for (int sl0 = wave; sl0 < ns; sl0 += 64) {
+      uint2 e[4];
+      uint32_t n[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int sl = sl0 + 16 * u;
+        n[u] = sl < ns ? pre[sl + 1] - pre[sl] : 0u;
+        if (sl0 == wave) e[u] = head[u];
+        else if ((uint32_t)lane < n[u]) e[u] = lr[(size_t)sl * kSelSlice + lane];
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int sl = sl0 + 16 * u;
+        if ((uint32_t)lane < n[u]) put(pre[sl] + lane, e[u]);
+        for (uint32_t i = 64 + lane; i < n[u]; i += 64) put(pre[sl] + i, lr[(size_t)sl * kSelSlice + i]);
+      }
+    }
+  } else {
+    for (uint32_t i = t; i < total; i += blockDim.x) {
+      const uint32_t kx = entry_global(i).x;
+      if ((kx >> 8) == top24) atomicAdd(&h[kx & 0xFFu], 1u);
+    }
   }
+  __syncthreads();
   auto entry = [&](uint32_t gi) -> uint2 { return staged ? stage[gi] : entry_global(gi); };
 
-  // Threshold bin b0 and the count above it, as in sel_filter.
-  for (int i = t; i < kSelBins; i += blockDim.x) h[i] = hist[(size_t)r * kSelBins + i];
-  __syncthreads();
-  find_bin_desc(h, kSelBins, (uint32_t)g.kk, scratch, res);
-  const uint32_t b0 = res[0];
-  const uint32_t need0 = (uint32_t)g.kk - res[1];
-
-  // Key bits 19..8 among the candidates (top bits == b0).
-  for (int i = t; i < kSelBins; i += blockDim.x) h[i] = 0u;
-  __syncthreads();
-  for (uint32_t e = t; e < total; e += blockDim.x) {
-    const uint32_t kx = entry(e).x;
-    if ((kx >> 20) == b0) atomicAdd(&h[(kx >> 8) & 0xFFFu], 1u);
-  }
-  __syncthreads();
-  find_bin_desc(h, kSelBins, need0, scratch, res);
-  const uint32_t b1 = res[0];
-  const uint32_t need1 = need0 - res[1];
-  const uint32_t top24 = (b0 << 12) | b1;
   // Key bits 7..0 among the candidates that match the top 24 bits.
-  for (int i = t; i < 256; i += blockDim.x) h[i] = 0u;
-  __syncthreads();
-  for (uint32_t e = t; e < total; e += blockDim.x) {
-    const uint32_t kx = entry(e).x;
-    if ((kx >> 8) == top24) atomicAdd(&h[kx & 0xFFu], 1u);
+  uint32_t v3[4] = {0u, 0u, 0u, 0u};
+  if (t < 64) {
+    const u32x4 x3 = *reinterpret_cast<const u32x4*>(&h[4 * t]);
+    v3[0] = x3.x;
+    v3[1] = x3.y;
+    v3[2] = x3.z;
+    v3[3] = x3.w;
   }
-  __syncthreads();
-  find_bin_desc(h, 256, need1, scratch, res);
-  const uint32_t b2 = res[0];
-  const uint32_t need2 = need1 - res[1];
+  find_bin_regs(v3, need1, scratch, res_c);
+  const uint32_t b2 = res_c[0];
+  const uint32_t need2 = need1 - res_c[1];
   const uint32_t ties = h[b2];
   const uint32_t tau = (top24 << 8) | b2;
   __syncthreads();
@@ -307,21 +434,58 @@ __global__ __launch_bounds__(1024) void sel_final(const int32_t* __restrict__ ct
     idx_thr = prefix;
   }
 
-  // Ordered compaction of the winners.
-  uint32_t base = 0;
-  for (uint32_t r0 = 0; r0 < total; r0 += blockDim.x) {
-    const uint32_t e = r0 + t;
-    bool win = false;
-    uint32_t idx = 0;
-    if (e < total) {
-      const uint2 c = entry(e);
-      win = c.x > tau || (c.x == tau && c.y <= idx_thr);
-      idx = c.y;
+  // Ordered compaction of the winners.  A staged list is cut into 64-entry
+  // chunks, one lane per entry: a ballot counts each chunk's winners, and a
+  // winner's place is the winners of earlier chunks plus those of lower
+  // lanes.  A list left in global memory goes through one block prefix sum
+  // over runs of consecutive entries.
+  auto wins = [&](uint2 c) { return c.x > tau || (c.x == tau && c.y <= idx_thr); };
+  uint32_t base;
+  if (staged) {
+    const int nchunks = (int)((total + 63) / 64);
+    uint64_t mask[kStage / 64 / 16];
+#pragma unroll
+    for (int u = 0; u < kStage / 64 / 16; ++u) {
+      const int ch = wave + 16 * u;
+      const uint32_t e = 64u * ch + lane;
+      const bool w = ch < nchunks && e < total && wins(stage[e]);
+      mask[u] = __ballot(w);
+      if (ch < nchunks && lane == 0) chunk_wins[ch] = (uint32_t)__popcll(mask[u]);
     }
-    uint32_t round_total;
-    const uint32_t pos = base + block_prefix_sum(win ? 1u : 0u, scratch, &round_total);
-    if (win && pos < (uint32_t)k_top) out[pos] = (int32_t)idx;
-    base += round_total;
+    __syncthreads();
+    // Winners of all chunks, and of the chunks before each of this wave's.
+    uint32_t all = 0;
+    for (int c0 = 0; c0 < nchunks; c0 += 64) all += (c0 + lane < nchunks) ? chunk_wins[c0 + lane] : 0u;
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) all += __shfl_xor(all, off);
+    base = all;
+    const uint64_t lower = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+#pragma unroll
+    for (int u = 0; u < kStage / 64 / 16; ++u) {
+      const int ch = wave + 16 * u;
+      if (ch >= nchunks) break;
+      uint32_t before = 0;
+      for (int c0 = 0; c0 < ch; c0 += 64) before += (c0 + lane < ch) ? chunk_wins[c0 + lane] : 0u;
+#pragma unroll
+      for (int off = 32; off >= 1; off >>= 1) before += __shfl_xor(before, off);
+      if ((mask[u] >> lane) & 1ull) {
+        const uint32_t pos = before + (uint32_t)__popcll(mask[u] & lower);
+        if (pos < (uint32_t)k_top) out[pos] = (int32_t)stage[64u * ch + lane].y;
+      }
+    }
+  } else {
+    const uint32_t per = (total + blockDim.x - 1) / blockDim.x;
+    const uint32_t e0 = min(total, t * per), e1 = min(total, e0 + per);
+    uint32_t mine = 0;
+    for (uint32_t e = e0; e < e1; ++e) mine += wins(entry(e)) ? 1u : 0u;
+    uint32_t pos = block_prefix_sum(mine, scratch, &base);
+    for (uint32_t e = e0; e < e1; ++e) {
+      const uint2 c = entry(e);
+      if (wins(c)) {
+        if (pos < (uint32_t)k_top) out[pos] = (int32_t)c.y;
+        ++pos;
+      }
+    }
   }
   for (int i = (int)min(base, (uint32_t)k_top) + t; i < k_top; i += blockDim.x) out[i] = -1;
   if (t == 0) top_cnt[r] = (int32_t)min(base, (uint32_t)k_top);
@@ -331,13 +495,14 @@ __global__ __launch_bounds__(1024) void sel_final(const int32_t* __restrict__ ct
 
 hipError_t launch_select(const hs2_attn_desc& d, const float* scores, const int32_t* ctx_len,
                          int cap, int32_t* top_idx, int32_t* top_cnt, char* ws,
-                         const uint32_t* hist, hipStream_t st) {
+                         uint32_t* hist, hipStream_t st) {
   const SelectWs w = select_ws(d, cap);
   const int tiles = d.n_q / d.tile_q;
   const int rows = d.batch * tiles;
   const int nslices = select_slices(cap);
   uint32_t* own_hist = reinterpret_cast<uint32_t*>(ws + w.hist_off);
   uint32_t* cnt = reinterpret_cast<uint32_t*>(ws + w.cnt_off);
+  uint32_t* meta = reinterpret_cast<uint32_t*>(ws + w.meta_off);
   uint2* list = reinterpret_cast<uint2*>(ws + w.list_off);
   const dim3 grid(nslices, rows);
   if (hist == nullptr) {
@@ -348,12 +513,12 @@ hipError_t launch_select(const hs2_attn_desc& d, const float* scores, const int3
   }
   if (cap % 4 == 0)
     sel_filter<true><<<grid, 256, 0, st>>>(scores, cap, ctx_len, tiles, d.n_q, d.tile_q, d.k_top,
-                                           d.window, hist, cnt, list, nslices);
+                                           d.window, hist, cnt, meta, list, nslices);
   else
     sel_filter<false><<<grid, 256, 0, st>>>(scores, cap, ctx_len, tiles, d.n_q, d.tile_q,
-                                            d.k_top, d.window, hist, cnt, list, nslices);
+                                            d.k_top, d.window, hist, cnt, meta, list, nslices);
   sel_final<<<rows, 1024, 0, st>>>(ctx_len, cap, tiles, d.n_q, d.tile_q, d.k_top, d.window, hist,
-                                   cnt, list, nslices, top_idx, top_cnt);
+                                   cnt, meta, list, nslices, top_idx, top_cnt);
   return hipGetLastError();
 }
 
