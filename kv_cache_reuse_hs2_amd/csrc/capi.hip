@@ -124,7 +124,7 @@ hs2_status hs2_select_topk_window(const hs2_attn_desc* desc, const float* scores
   (void)hipGetLastError();
   const WsLayout l = ws_layout(*desc, kv_capacity);
   return launched(launch_select(*desc, scores, ctx_len, kv_capacity, top_idx, top_cnt,
-                                static_cast<char*>(ws) + l.select, nullptr,
+                                static_cast<char*>(ws) + l.select, nullptr, true,
                                 static_cast<hipStream_t>(stream)));
 }
 
@@ -188,11 +188,18 @@ hs2_status hs2_decode_step(const hs2_attn_desc* desc, const void* q, const void*
   const size_t hist_off = pf ? prefill_ws(*desc, kv_capacity).hist_off
                              : score_ws(*desc, kv_capacity).hist_off;
   uint32_t* hist = fuse ? reinterpret_cast<uint32_t*>(w + l.score + hist_off) : nullptr;
-  e = launch_select(*desc, scores, ctx_len, kv_capacity, top_idx, top_cnt, w + l.select, hist, st);
+  // bf16 decode: the final selection runs inside the sparse layer's kernel.
+  const bool tail = fuse && !pf;
+  e = launch_select(*desc, scores, ctx_len, kv_capacity, top_idx, top_cnt, w + l.select, hist,
+                    !tail, st);
   if (e != hipSuccess) return HS2_EHIP;
   if (pf)
     return launched(launch_prefill_sparse(*desc, q_sparse, k, v, kv_stride, ctx_len, kv_capacity,
                                           top_idx, top_cnt, o, lse, st));
+  if (tail)
+    return launched(launch_decode_tail(*desc, q_sparse, k, v, kv_stride, ctx_len, kv_capacity,
+                                       hist, w + l.select, top_idx, top_cnt, o, lse, w + l.sparse,
+                                       st));
   return launched(launch_sparse(*desc, q_sparse, k, v, kv_stride, ctx_len, kv_capacity, top_idx,
                                 top_cnt, o, lse, w + l.sparse, st));
 }

@@ -195,10 +195,11 @@ hipError_t launch_score_decode(const hs2_attn_desc& d, const void* q, const void
                                hipStream_t st);
 
 // hist: a ready histogram of the pool scores (from launch_score_decode with
-// with_hist), or null to build one.
+// with_hist), or null to build one.  final_stage false: stop after the
+// candidate filter (launch_decode_tail finishes the selection).
 hipError_t launch_select(const hs2_attn_desc& d, const float* scores, const int32_t* ctx_len,
                          int cap, int32_t* top_idx, int32_t* top_cnt, char* ws,
-                         uint32_t* hist, hipStream_t st);
+                         uint32_t* hist, bool final_stage, hipStream_t st);
 
 // Chunked prefill (tile_q > 1, bf16): scoring over query tiles and sparse
 // attention of the tiles' queries.
@@ -215,5 +216,15 @@ hipError_t launch_sparse(const hs2_attn_desc& d, const void* q, const void* k, c
                          int64_t kv_stride, const int32_t* ctx_len, int cap,
                          const int32_t* top_idx, const int32_t* top_cnt, float* o, float* lse,
                          char* ws, hipStream_t st);
+
+// bf16 decode after launch_select(final_stage = false): the final selection
+// (to top_idx/top_cnt) and the sparse layer in one pass over the candidate
+// lists of sel_ws, then the merge of the partials; same results as
+// launch_select's final stage followed by launch_sparse.
+hipError_t launch_decode_tail(const hs2_attn_desc& d, const void* q, const void* k, const void* v,
+                              int64_t kv_stride, const int32_t* ctx_len, int cap,
+                              const uint32_t* hist, const char* sel_ws, int32_t* top_idx,
+                              int32_t* top_cnt, float* o, float* lse, char* sparse_ws,
+                              hipStream_t st);
 
 }  // namespace hs2

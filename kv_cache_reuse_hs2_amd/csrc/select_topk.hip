@@ -27,136 +27,10 @@
 //       the winners by an ordered compaction of the concatenated slice
 //       lists, which are in index order already: no sort is needed.
 // Rows whose pool fits the budget skip the radix passes and take the pool.
-#include "hs2_internal.h"
+#include "select_core.h"
 
 namespace hs2 {
 namespace {
-
-struct RowGeom {
-  int pe;  // pool end (exclusive)
-  int kk;  // keys to select = min(k_top, pe)
-};
-
-__device__ __forceinline__ RowGeom row_geom(const int32_t* ctx_len, int cap, int r, int tiles,
-                                            int n_q, int tile_q, int k_top, int window) {
-  const int b = r / tiles, g = r % tiles;
-  const int N = clamp_ctx(ctx_len, b, cap);
-  const int p0 = N - n_q + g * tile_q;
-  int pe = p0 - window + 1;
-  if (pe < 0) pe = 0;
-  RowGeom w;
-  w.pe = pe;
-  w.kk = min(k_top, pe);
-  return w;
-}
-
-// Inclusive suffix sum of v over the block (all threads call; scratch holds
-// one word per wave).  Returns the sum over threads >= t.
-__device__ __forceinline__ uint32_t block_suffix_sum(uint32_t v, uint32_t* scratch) {
-  const int t = threadIdx.x, lane = t & 63, wave = t >> 6, nw = blockDim.x >> 6;
-  uint32_t s = v;
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const uint32_t o = __shfl_down(s, off);
-    if (lane + off < 64) s += o;
-  }
-  if (lane == 0) scratch[wave] = s;
-  __syncthreads();
-  uint32_t later = 0;
-  for (int w = wave + 1; w < nw; ++w) later += scratch[w];
-  __syncthreads();
-  return s + later;
-}
-
-// Exclusive prefix sum of v over the block; *total gets the block sum.
-__device__ __forceinline__ uint32_t block_prefix_sum(uint32_t v, uint32_t* scratch, uint32_t* total) {
-  const int t = threadIdx.x, lane = t & 63, wave = t >> 6, nw = blockDim.x >> 6;
-  uint32_t s = v;
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const uint32_t o = __shfl_up(s, off);
-    if (lane >= off) s += o;
-  }
-  if (lane == 63) scratch[wave] = s;
-  __syncthreads();
-  uint32_t before = 0, all = 0;
-  for (int w = 0; w < nw; ++w) {
-    if (w < wave) before += scratch[w];
-    all += scratch[w];
-  }
-  __syncthreads();
-  *total = all;
-  return s - v + before;
-}
-
-// Search, from the highest bin down, for the bin where the running count
-// reaches `need` (1 <= need <= total).  Threads [0, nt) own nbins/nt
-// consecutive bins.  res = {bin, count strictly above it}.  All threads call.
-__device__ void find_bin_desc(const uint32_t* hist, int nbins, uint32_t need, uint32_t* scratch,
-                              uint32_t* res) {
-  const int t = threadIdx.x;
-  const int nt = min((int)blockDim.x, nbins);
-  const int per = nbins / nt;
-  uint32_t local = 0;
-  if (t < nt)
-    for (int i = 0; i < per; ++i) local += hist[t * per + i];
-  if (t == 0) {
-    res[0] = 0u;
-    res[1] = 0u;
-  }
-  const uint32_t suf = block_suffix_sum(local, scratch);
-  if (t < nt) {
-    const uint32_t above = suf - local;
-    if (above < need && need <= suf) {
-      uint32_t cum = above;
-      for (int i = per - 1; i >= 0; --i) {
-        const uint32_t c = hist[t * per + i];
-        if (cum + c >= need) {
-          res[0] = t * per + i;
-          res[1] = cum;
-          break;
-        }
-        cum += c;
-      }
-    }
-  }
-  __syncthreads();
-}
-
-// find_bin_desc over a histogram held in registers: thread t owns bins
-// [kPer t, kPer t + kPer) (threads past the histogram hold zeros).  res must
-// not be read between this call and the previous use of the same array
-// without a barrier in between.
-template <int kPer>
-__device__ void find_bin_regs(const uint32_t (&v)[kPer], uint32_t need, uint32_t* scratch,
-                              uint32_t* res) {
-  const int t = threadIdx.x;
-  uint32_t local = 0;
-#pragma unroll
-  for (int e = 0; e < kPer; ++e) local += v[e];
-  if (t == 0) {
-    res[0] = 0u;
-    res[1] = 0u;
-  }
-  const uint32_t suf = block_suffix_sum(local, scratch);
-  const uint32_t above = suf - local;
-  if (above < need && need <= suf) {
-    uint32_t cum = above, bin = 0, cab = 0;
-    bool found = false;
-#pragma unroll
-    for (int e = kPer - 1; e >= 0; --e) {
-      if (!found && cum + v[e] >= need) {
-        bin = (uint32_t)e;
-        cab = cum;
-        found = true;
-      }
-      cum += v[e];
-    }
-    res[0] = (uint32_t)t * kPer + bin;
-    res[1] = cab;
-  }
-  __syncthreads();
-}
 
 __global__ __launch_bounds__(256) void sel_init(uint32_t* __restrict__ hist) {
   const int r = blockIdx.x;
@@ -272,9 +146,6 @@ __global__ __launch_bounds__(256) void sel_filter(const float* __restrict__ scor
   }
 }
 
-constexpr int kMaxSlices = 1024;  // pools up to 4,194,304 keys
-constexpr int kStage = 8192;      // list entries held in LDS by sel_final
-
 __global__ __launch_bounds__(1024) void sel_final(const int32_t* __restrict__ ctx_len, int cap,
                                                   int tiles, int n_q, int tile_q, int k_top,
                                                   int window, const uint32_t* __restrict__ hist,
@@ -283,219 +154,25 @@ __global__ __launch_bounds__(1024) void sel_final(const int32_t* __restrict__ ct
                                                   const uint2* __restrict__ list, int nslices,
                                                   int32_t* __restrict__ top_idx,
                                                   int32_t* __restrict__ top_cnt) {
-  const int r = blockIdx.x;
-  const int t = threadIdx.x;  // blockDim.x == 1024
-  const RowGeom g = row_geom(ctx_len, cap, r, tiles, n_q, tile_q, k_top, window);
-  int32_t* out = top_idx + (size_t)r * k_top;
-  if (g.kk == 0 || g.kk == g.pe) {
-    for (int i = t; i < k_top; i += blockDim.x) out[i] = i < g.kk ? i : -1;
-    if (t == 0) top_cnt[r] = g.kk;
-    return;
-  }
-  // Bits 7..0 of the threshold; then up to 2,048 bins of the tie passes.
   __shared__ __attribute__((aligned(16))) uint32_t h[2048];
   __shared__ uint32_t pre[kMaxSlices + 1];
   __shared__ uint32_t chunk_wins[kStage / 64];
   __shared__ __attribute__((aligned(16))) uint32_t scratch[16];
-  __shared__ uint32_t res_b[2], res_c[2], res[2];
-  const int lane = t & 63, wave = t >> 6;
-  const int ns = (g.pe + kSelSlice - 1) / kSelSlice;
-  const uint2* lr = list + (size_t)r * nslices * kSelSlice;
-
-  // Everything that does not depend on another load is fetched at once: the
-  // threshold bin b0 that sel_filter found, the second-level histogram (bins
-  // 4t .. 4t+3 per thread), the slice counts, and the head of each slice
-  // list this wave will copy (slices wave + 16u, entries 0..63).
-  const uint32_t* hrow = hist + (size_t)r * kHistRow;
-  static_assert(kSelBins == 4 * 1024, "four bins per thread");
-  const u32x4 x2 = *reinterpret_cast<const u32x4*>(hrow + kSelBins + 4 * t);
-  const uint32_t b0 = meta[4 * r], above0 = meta[4 * r + 1];
-  uint2 head[4];
-#pragma unroll
-  for (int u = 0; u < 4; ++u) {
-    const int sl = wave + 16 * u;
-    if (sl < ns) head[u] = lr[(size_t)sl * kSelSlice + lane];
-  }
-  if (t < 256) h[t] = 0u;  // key bits 7..0, counted while staging
-
-  // Slice offsets: one wave scans the counts 64 at a time.
-  if (wave == 0) {
-    uint32_t carry = 0;
-    for (int c0 = 0; c0 < ns; c0 += 64) {
-      const uint32_t c = (c0 + lane < ns) ? cnt[(size_t)r * nslices + c0 + lane] : 0u;
-      uint32_t incl = c;
-#pragma unroll
-      for (int off = 1; off < 64; off <<= 1) {
-        const uint32_t o = __shfl_up(incl, off);
-        if (lane >= off) incl += o;
-      }
-      if (c0 + lane < ns) pre[c0 + lane] = carry + incl - c;
-      carry += __shfl(incl, 63);
-    }
-    if (lane == 0) pre[ns] = carry;
-  }
-
-  // Bits 19..8 of the threshold among the keys of b0.
-  const uint32_t need0 = (uint32_t)g.kk - above0;
-  const uint32_t v2[4] = {x2.x, x2.y, x2.z, x2.w};
-  find_bin_regs(v2, need0, scratch, res_b);  // its barriers also publish pre[]
-  const uint32_t b1 = res_b[0];
-  const uint32_t need1 = need0 - res_b[1];
-  const uint32_t top24 = (b0 << 12) | b1;
-  const uint32_t total = pre[ns];
-
-  auto entry_global = [&](uint32_t gi) -> uint2 {
-    int lo = 0, hi = ns - 1;  // last slice with pre[s] <= gi
-    while (lo < hi) {
-      const int mid = (lo + hi + 1) >> 1;
-      if (pre[mid] <= gi) lo = mid;
-      else hi = mid - 1;
-    }
-    return lr[(size_t)lo * kSelSlice + (gi - pre[lo])];
-  };
-  // The list is read twice more: keep it in LDS when it fits (the usual
-  // case: keys above the threshold bin plus that bin).  Each wave copies
-  // whole slices, four at a time so that their loads overlap, and counts key
-  // bits 7..0 of the candidates that match the top 24 bits on the way.
+  __shared__ uint32_t res[6];
   __shared__ uint2 stage[kStage];
-  const bool staged = total <= (uint32_t)kStage;
-  auto put = [&](uint32_t pos, uint2 e) {
-    stage[pos] = e;
-    if ((e.x >> 8) == top24) atomicAdd(&h[e.x & 0xFFu], 1u);
-  };
-  if (staged) {
-    for (int sl0 = wave; sl0 < ns; sl0 += 64) {
-      uint2 e[4];
-      uint32_t n[4];
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const int sl = sl0 + 16 * u;
-        n[u] = sl < ns ? pre[sl + 1] - pre[sl] : 0u;
-        if (sl0 == wave) e[u] = head[u];
-        else if ((uint32_t)lane < n[u]) e[u] = lr[(size_t)sl * kSelSlice + lane];
-      }
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const int sl = sl0 + 16 * u;
-        if ((uint32_t)lane < n[u]) put(pre[sl] + lane, e[u]);
-        for (uint32_t i = 64 + lane; i < n[u]; i += 64) put(pre[sl] + i, lr[(size_t)sl * kSelSlice + i]);
-      }
-    }
-  } else {
-    for (uint32_t i = t; i < total; i += blockDim.x) {
-      const uint32_t kx = entry_global(i).x;
-      if ((kx >> 8) == top24) atomicAdd(&h[kx & 0xFFu], 1u);
-    }
-  }
-  __syncthreads();
-  auto entry = [&](uint32_t gi) -> uint2 { return staged ? stage[gi] : entry_global(gi); };
-
-  // Key bits 7..0 among the candidates that match the top 24 bits.
-  uint32_t v3[4] = {0u, 0u, 0u, 0u};
-  if (t < 64) {
-    const u32x4 x3 = *reinterpret_cast<const u32x4*>(&h[4 * t]);
-    v3[0] = x3.x;
-    v3[1] = x3.y;
-    v3[2] = x3.z;
-    v3[3] = x3.w;
-  }
-  find_bin_regs(v3, need1, scratch, res_c);
-  const uint32_t b2 = res_c[0];
-  const uint32_t need2 = need1 - res_c[1];
-  const uint32_t ties = h[b2];
-  const uint32_t tau = (top24 << 8) | b2;
-  __syncthreads();
-
-  // Among keys equal to tau keep the need2 lowest indices: radix-select the
-  // need2-th smallest index (digits of 11/10/10 bits, searched from the top
-  // on the reversed digit).
-  uint32_t idx_thr = 0xFFFFFFFFu;
-  if (need2 < ties) {
-    uint32_t prefix = 0, need = need2;
-    for (int p = 0; p < 3; ++p) {
-      const int sh = (p == 0) ? 20 : (p == 1 ? 10 : 0);
-      const uint32_t nb = (p == 0) ? 2048u : 1024u;
-      for (int i = t; i < (int)nb; i += blockDim.x) h[i] = 0u;
-      __syncthreads();
-      for (uint32_t e = t; e < total; e += blockDim.x) {
-        const uint2 c = entry(e);
-        if (c.x != tau) continue;
-        // Index bits above this digit must match the digits already fixed.
-        if (p > 0 && (c.y >> (sh + 10)) != prefix) continue;
-        atomicAdd(&h[nb - 1u - ((c.y >> sh) & (nb - 1u))], 1u);
-      }
-      __syncthreads();
-      find_bin_desc(h, nb, need, scratch, res);
-      const uint32_t dgt = nb - 1u - res[0];
-      need -= res[1];
-      prefix = (p == 0) ? dgt : ((prefix << 10) | dgt);
-      __syncthreads();
-    }
-    idx_thr = prefix;
-  }
-
-  // Ordered compaction of the winners.  A staged list is cut into 64-entry
-  // chunks, one lane per entry: a ballot counts each chunk's winners, and a
-  // winner's place is the winners of earlier chunks plus those of lower
-  // lanes.  A list left in global memory goes through one block prefix sum
-  // over runs of consecutive entries.
-  auto wins = [&](uint2 c) { return c.x > tau || (c.x == tau && c.y <= idx_thr); };
-  uint32_t base;
-  if (staged) {
-    const int nchunks = (int)((total + 63) / 64);
-    uint64_t mask[kStage / 64 / 16];
-#pragma unroll
-    for (int u = 0; u < kStage / 64 / 16; ++u) {
-      const int ch = wave + 16 * u;
-      const uint32_t e = 64u * ch + lane;
-      const bool w = ch < nchunks && e < total && wins(stage[e]);
-      mask[u] = __ballot(w);
-      if (ch < nchunks && lane == 0) chunk_wins[ch] = (uint32_t)__popcll(mask[u]);
-    }
-    __syncthreads();
-    // Winners of all chunks, and of the chunks before each of this wave's.
-    uint32_t all = 0;
-    for (int c0 = 0; c0 < nchunks; c0 += 64) all += (c0 + lane < nchunks) ? chunk_wins[c0 + lane] : 0u;
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) all += __shfl_xor(all, off);
-    base = all;
-    const uint64_t lower = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-#pragma unroll
-    for (int u = 0; u < kStage / 64 / 16; ++u) {
-      const int ch = wave + 16 * u;
-      if (ch >= nchunks) break;
-      uint32_t before = 0;
-      for (int c0 = 0; c0 < ch; c0 += 64) before += (c0 + lane < ch) ? chunk_wins[c0 + lane] : 0u;
-#pragma unroll
-      for (int off = 32; off >= 1; off >>= 1) before += __shfl_xor(before, off);
-      if ((mask[u] >> lane) & 1ull) {
-        const uint32_t pos = before + (uint32_t)__popcll(mask[u] & lower);
-        if (pos < (uint32_t)k_top) out[pos] = (int32_t)stage[64u * ch + lane].y;
-      }
-    }
-  } else {
-    const uint32_t per = (total + blockDim.x - 1) / blockDim.x;
-    const uint32_t e0 = min(total, t * per), e1 = min(total, e0 + per);
-    uint32_t mine = 0;
-    for (uint32_t e = e0; e < e1; ++e) mine += wins(entry(e)) ? 1u : 0u;
-    uint32_t pos = block_prefix_sum(mine, scratch, &base);
-    for (uint32_t e = e0; e < e1; ++e) {
-      const uint2 c = entry(e);
-      if (wins(c)) {
-        if (pos < (uint32_t)k_top) out[pos] = (int32_t)c.y;
-        ++pos;
-      }
-    }
-  }
-  for (int i = (int)min(base, (uint32_t)k_top) + t; i < k_top; i += blockDim.x) out[i] = -1;
-  if (t == 0) top_cnt[r] = (int32_t)min(base, (uint32_t)k_top);
+  const int r = blockIdx.x;
+  const RowGeom g = row_geom(ctx_len, cap, r, tiles, n_q, tile_q, k_top, window);
+  const int n = final_select_row<1024>(r, g, k_top, hist, cnt, meta, list, nslices,
+                                 top_idx + (size_t)r * k_top, nullptr,
+                                 FinalLds{h, pre, chunk_wins, scratch, res, stage});
+  if (threadIdx.x == 0) top_cnt[r] = n;
 }
 
 }  // namespace
 
 hipError_t launch_select(const hs2_attn_desc& d, const float* scores, const int32_t* ctx_len,
                          int cap, int32_t* top_idx, int32_t* top_cnt, char* ws,
-                         uint32_t* hist, hipStream_t st) {
+                         uint32_t* hist, bool final_stage, hipStream_t st) {
   const SelectWs w = select_ws(d, cap);
   const int tiles = d.n_q / d.tile_q;
   const int rows = d.batch * tiles;
@@ -517,7 +194,8 @@ hipError_t launch_select(const hs2_attn_desc& d, const float* scores, const int3
   else
     sel_filter<false><<<grid, 256, 0, st>>>(scores, cap, ctx_len, tiles, d.n_q, d.tile_q,
                                             d.k_top, d.window, hist, cnt, meta, list, nslices);
-  sel_final<<<rows, 1024, 0, st>>>(ctx_len, cap, tiles, d.n_q, d.tile_q, d.k_top, d.window, hist,
+  if (final_stage)
+    sel_final<<<rows, 1024, 0, st>>>(ctx_len, cap, tiles, d.n_q, d.tile_q, d.k_top, d.window, hist,
                                    cnt, meta, list, nslices, top_idx, top_cnt);
   return hipGetLastError();
 }

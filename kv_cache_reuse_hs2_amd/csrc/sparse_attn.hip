@@ -24,6 +24,7 @@
 // a fixed order.
 // fp32: 32-key segments on VALU.
 #include "hs2_internal.h"
+#include "select_core.h"
 
 namespace hs2 {
 namespace {
@@ -72,12 +73,154 @@ constexpr int kSegWaves = 4;
 constexpr int kSegB = 32 * kSegWaves;  // keys per workgroup
 constexpr int kVtPitch = 40;           // bf16 per transposed V row (32 keys + pad)
 
+// LDS of one segment.
+struct SegLds {
+  uint16_t vt[kSegWaves][kHeadDim][kVtPitch];
+  float s_m[kSegWaves][32], s_l[kSegWaves][32];
+  float s_o[kSegWaves][32][kHeadDim + 4];
+};
+
+// Partial of the segment starting at selection position s0 of query bq
+// (sequence b): (max, sum) per head to mlo[H] and o to po[H][D].  Called by
+// every thread of the workgroup; waves 0..kSegWaves-1 gather 32 keys each,
+// any further waves only take part in the barriers and the final merge.
+// key_at(p) gives the cache index of selection position p < qg.S.
+template <typename KeyAt>
+__device__ __forceinline__ void segment_partial_bf16(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
+    const uint16_t* __restrict__ v, int64_t kv_stride, int b, int bq, int H, float c2,
+    const QueryGeom& qg, int s0, KeyAt key_at, SegLds& L, float* __restrict__ po,
+    float2* __restrict__ mlo) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int r32 = lane & 31, hh = lane >> 5;
+  const bool active = wave < kSegWaves;
+  const int pw = s0 + 32 * wave;  // first selection position of this wave
+  const bool wave_live = active && pw < qg.S;
+  float x[16];
+  if (active) {
+    const int idx = key_at((pw + r32 < qg.S) ? pw + r32 : s0);
+    const size_t rowoff = (size_t)b * kv_stride + (size_t)idx * kHeadDim;
+    // Gathered K (A operand) and V rows; Q^T as the B operand.
+    u32x4 kr[8], vr[8];
+    const u32x4* kp = reinterpret_cast<const u32x4*>(k + rowoff + 8 * hh);
+    const u32x4* vp = reinterpret_cast<const u32x4*>(v + rowoff + 64 * hh);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      kr[e] = kp[2 * e];
+      vr[e] = vp[e];
+    }
+    bf16x8_t qreg[8];
+    const uint16_t* qb = q + (size_t)bq * H * kHeadDim;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      u32x4 xq = {0u, 0u, 0u, 0u};
+      if (r32 < H) xq = *reinterpret_cast<const u32x4*>(qb + r32 * kHeadDim + 16 * e + 8 * hh);
+      qreg[e] = as_bf16x8(xq);
+    }
+    // V transposed into LDS: vt[wave][d][key], key = r32, d = 64*hh + 8*e + j.
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        L.vt[wave][64 * hh + 8 * e + 2 * j][r32] = (uint16_t)(vr[e][j] & 0xFFFFu);
+        L.vt[wave][64 * hh + 8 * e + 2 * j + 1][r32] = (uint16_t)(vr[e][j] >> 16);
+      }
+
+    f32x16_t acc = {};
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(kr[e]), qreg[e], acc, 0, 0, 0);
+    // acc[r]: head r32, key 8*(r/4) + 4*hh + r%4 of this wave's 32.
+    float m = -INFINITY;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int key = 8 * (r >> 2) + 4 * hh + (r & 3);
+      x[r] = (pw + key < qg.S) ? acc[r] * c2 : -INFINITY;
+      m = fmaxf(m, x[r]);
+    }
+    m = fmaxf(m, __shfl_xor(m, 32));
+    const float mref = (m == -INFINITY) ? 0.f : m;
+    float l = 0.f;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      x[r] = fast_exp2(x[r] - mref);
+      l += x[r];
+    }
+    l += __shfl_xor(l, 32);
+    if (hh == 0) {
+      L.s_m[wave][r32] = wave_live ? m : -INFINITY;
+      L.s_l[wave][r32] = wave_live ? l : 0.f;
+    }
+  }
+  __syncthreads();
+  if (active) {
+    // P V for this wave's 32 keys: k-step s covers the keys of registers
+    // 8s..8s+7, i.e. {16s + 4hh + 0..3} and {16s + 8 + 4hh + 0..3}.
+    f32x16_t o[4] = {{}, {}, {}, {}};
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      u32x4 ahi, alo;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const float p0 = x[8 * s + 2 * j], p1 = x[8 * s + 2 * j + 1];
+        const uint16_t h0 = f32_to_bf16_rne(p0), h1 = f32_to_bf16_rne(p1);
+        const uint16_t l0 = f32_to_bf16_rne(p0 - bf16_to_f32(h0));
+        const uint16_t l1 = f32_to_bf16_rne(p1 - bf16_to_f32(h1));
+        ahi[j] = (uint32_t)h0 | ((uint32_t)h1 << 16);
+        alo[j] = (uint32_t)l0 | ((uint32_t)l1 << 16);
+      }
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const uint16_t* row = &L.vt[wave][32 * t + r32][0];
+        const uint2 lo4 = *reinterpret_cast<const uint2*>(row + 16 * s + 4 * hh);
+        const uint2 hi4 = *reinterpret_cast<const uint2*>(row + 16 * s + 8 + 4 * hh);
+        const u32x4 bv = {lo4.x, lo4.y, hi4.x, hi4.y};
+        o[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(ahi), as_bf16x8(bv), o[t], 0, 0, 0);
+        o[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(alo), as_bf16x8(bv), o[t], 0, 0, 0);
+      }
+    }
+    // o[t][r]: head 8*(r/4) + 4*hh + r%4, dim 32*t + r32, relative to this
+    // wave's max; rescale to the workgroup max and stage for the merge.
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int h = 8 * (r >> 2) + 4 * hh + (r & 3);
+      float M = -INFINITY;
+#pragma unroll
+      for (int w = 0; w < kSegWaves; ++w) M = fmaxf(M, L.s_m[w][h]);
+      const float mw = L.s_m[wave][h];
+      const float sc = (mw == -INFINITY) ? 0.f : fast_exp2(mw - M);
+#pragma unroll
+      for (int t = 0; t < 4; ++t) L.s_o[wave][h][32 * t + r32] = o[t][r] * sc;
+    }
+  }
+  __syncthreads();
+  // Merge the waves in order.
+  for (int e = threadIdx.x; e < 32 * kHeadDim; e += blockDim.x) {
+    const int h = e / kHeadDim, d = e % kHeadDim;
+    if (h >= H) continue;
+    float acc_o = 0.f;
+#pragma unroll
+    for (int w = 0; w < kSegWaves; ++w) acc_o += L.s_o[w][h][d];
+    po[(size_t)h * kHeadDim + d] = acc_o;
+  }
+  if (threadIdx.x < H) {
+    const int h = threadIdx.x;
+    float M = -INFINITY;
+    for (int w = 0; w < kSegWaves; ++w) M = fmaxf(M, L.s_m[w][h]);
+    float Ls = 0.f;
+    for (int w = 0; w < kSegWaves; ++w)
+      if (L.s_m[w][h] != -INFINITY) Ls += L.s_l[w][h] * fast_exp2(L.s_m[w][h] - M);
+    mlo[h] = make_float2(M, Ls);
+  }
+}
+
 __global__ __launch_bounds__(64 * kSegWaves) void sparse_partial_bf16(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, int64_t kv_stride, const int32_t* __restrict__ ctx_len,
     int cap, const int32_t* __restrict__ top_idx, const int32_t* __restrict__ top_cnt, int n_q,
     int tile_q, int k_top, int window, int H, float c2, float* __restrict__ part,
     float2* __restrict__ ml, int nseg) {
+  __shared__ SegLds lds;
   const int seg = blockIdx.x, bq = blockIdx.y;
   const int b = bq / n_q, i = bq % n_q, g = i / tile_q, tiles = n_q / tile_q;
   const QueryGeom qg = query_geom(ctx_len, top_cnt, cap, b, i, g, tiles, n_q, k_top, window);
@@ -87,130 +230,71 @@ __global__ __launch_bounds__(64 * kSegWaves) void sparse_partial_bf16(
     if (threadIdx.x < H) mlo[threadIdx.x] = make_float2(-INFINITY, 0.f);
     return;
   }
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int r32 = lane & 31, hh = lane >> 5;
   const int32_t* top_row = top_idx + (size_t)(b * tiles + g) * k_top;
-  const int pw = s0 + 32 * wave;  // first selection position of this wave
-  const bool wave_live = pw < qg.S;
-  const int idx = (pw + r32 < qg.S) ? sel_key(qg, top_row, pw + r32) : sel_key(qg, top_row, s0);
-  const size_t rowoff = (size_t)b * kv_stride + (size_t)idx * kHeadDim;
+  segment_partial_bf16(q, k, v, kv_stride, b, bq, H, c2, qg, s0,
+                       [&](int p) { return sel_key(qg, top_row, p); }, lds,
+                       part + ((size_t)bq * nseg + seg) * H * kHeadDim, mlo);
+}
 
-  __shared__ uint16_t vt[kSegWaves][kHeadDim][kVtPitch];
-  __shared__ float s_m[kSegWaves][32], s_l[kSegWaves][32];
-  __shared__ float s_o[kSegWaves][32][kHeadDim + 4];
+// ---------------------------------------------------------------------------
+// Fused decode tail (bf16): the final selection of sequence blockIdx.y and
+// the partial of segment blockIdx.x, in one launch.  Every workgroup of the
+// sequence resolves the same selection from the filter's candidate lists
+// into LDS (the first one also writes top_idx and top_cnt), then gathers its
+// segment exactly as sparse_partial_bf16 would from top_idx.
 
-  // Gathered K (A operand) and V rows; Q^T as the B operand.
-  u32x4 kr[8], vr[8];
-  const u32x4* kp = reinterpret_cast<const u32x4*>(k + rowoff + 8 * hh);
-  const u32x4* vp = reinterpret_cast<const u32x4*>(v + rowoff + 64 * hh);
-#pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    kr[e] = kp[2 * e];
-    vr[e] = vp[e];
-  }
-  bf16x8_t qreg[8];
-  const uint16_t* qb = q + (size_t)bq * H * kHeadDim;
-#pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    u32x4 x = {0u, 0u, 0u, 0u};
-    if (r32 < H) x = *reinterpret_cast<const u32x4*>(qb + r32 * kHeadDim + 16 * e + 8 * hh);
-    qreg[e] = as_bf16x8(x);
-  }
-  // V transposed into LDS: vt[wave][d][key], key = r32, d = 64*hh + 8*e + j.
-#pragma unroll
-  for (int e = 0; e < 8; ++e)
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      vt[wave][64 * hh + 8 * e + 2 * j][r32] = (uint16_t)(vr[e][j] & 0xFFFFu);
-      vt[wave][64 * hh + 8 * e + 2 * j + 1][r32] = (uint16_t)(vr[e][j] >> 16);
-    }
+constexpr int kTailThreads = 512;
 
-  f32x16_t acc = {};
-#pragma unroll
-  for (int e = 0; e < 8; ++e)
-    acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(kr[e]), qreg[e], acc, 0, 0, 0);
-  // acc[r]: head r32, key 8*(r/4) + 4*hh + r%4 of this wave's 32.
-  float x[16];
-  float m = -INFINITY;
-#pragma unroll
-  for (int r = 0; r < 16; ++r) {
-    const int key = 8 * (r >> 2) + 4 * hh + (r & 3);
-    x[r] = (pw + key < qg.S) ? acc[r] * c2 : -INFINITY;
-    m = fmaxf(m, x[r]);
-  }
-  m = fmaxf(m, __shfl_xor(m, 32));
-  const float mref = (m == -INFINITY) ? 0.f : m;
-  float l = 0.f;
-#pragma unroll
-  for (int r = 0; r < 16; ++r) {
-    x[r] = fast_exp2(x[r] - mref);
-    l += x[r];
-  }
-  l += __shfl_xor(l, 32);
-  if (hh == 0) {
-    s_m[wave][r32] = wave_live ? m : -INFINITY;
-    s_l[wave][r32] = wave_live ? l : 0.f;
-  }
-  __syncthreads();
+union TailLds {
+  struct {
+    uint32_t h[2048];
+    uint2 stage[kStage];
+    uint32_t pre[kMaxSlices + 1];
+    uint32_t chunk_wins[kStage / 64];
+    uint32_t scratch[16];
+    uint32_t res[6];
+  } sel;
+  SegLds seg;
+};
 
-  // P V for this wave's 32 keys: k-step s covers the keys of registers
-  // 8s..8s+7, i.e. {16s + 4hh + 0..3} and {16s + 8 + 4hh + 0..3}.
-  f32x16_t o[4] = {{}, {}, {}, {}};
-#pragma unroll
-  for (int s = 0; s < 2; ++s) {
-    u32x4 ahi, alo;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const float p0 = x[8 * s + 2 * j], p1 = x[8 * s + 2 * j + 1];
-      const uint16_t h0 = f32_to_bf16_rne(p0), h1 = f32_to_bf16_rne(p1);
-      const uint16_t l0 = f32_to_bf16_rne(p0 - bf16_to_f32(h0));
-      const uint16_t l1 = f32_to_bf16_rne(p1 - bf16_to_f32(h1));
-      ahi[j] = (uint32_t)h0 | ((uint32_t)h1 << 16);
-      alo[j] = (uint32_t)l0 | ((uint32_t)l1 << 16);
-    }
-#pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      const uint16_t* row = &vt[wave][32 * t + r32][0];
-      const uint2 lo4 = *reinterpret_cast<const uint2*>(row + 16 * s + 4 * hh);
-      const uint2 hi4 = *reinterpret_cast<const uint2*>(row + 16 * s + 8 + 4 * hh);
-      const u32x4 bv = {lo4.x, lo4.y, hi4.x, hi4.y};
-      o[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(ahi), as_bf16x8(bv), o[t], 0, 0, 0);
-      o[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(alo), as_bf16x8(bv), o[t], 0, 0, 0);
-    }
+__global__ __launch_bounds__(kTailThreads) void decode_tail_bf16(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
+    const uint16_t* __restrict__ v, int64_t kv_stride, const int32_t* __restrict__ ctx_len,
+    int cap, int k_top, int window, int H, float c2, const uint32_t* __restrict__ hist,
+    const uint32_t* __restrict__ cnt, const uint32_t* __restrict__ meta,
+    const uint2* __restrict__ list, int nslices, int32_t* __restrict__ top_idx,
+    int32_t* __restrict__ top_cnt, float* __restrict__ part, float2* __restrict__ ml, int nseg) {
+  __shared__ __attribute__((aligned(16))) TailLds lds;
+  __shared__ int32_t win[kMaxTop];
+  const int seg = blockIdx.x, b = blockIdx.y;  // one query per sequence
+  const RowGeom g = row_geom(ctx_len, cap, b, 1, 1, 1, k_top, window);
+  const int n = final_select_row<kTailThreads>(
+      b, g, k_top, hist, cnt, meta, list, nslices, seg == 0 ? top_idx + (size_t)b * k_top : nullptr,
+      win,
+      FinalLds{lds.sel.h, lds.sel.pre, lds.sel.chunk_wins, lds.sel.scratch, lds.sel.res,
+               lds.sel.stage});
+  if (seg == 0 && threadIdx.x == 0) top_cnt[b] = n;
+  // Selection geometry of the query, as query_geom reads it back from top_cnt.
+  QueryGeom qg{};
+  qg.N = clamp_ctx(ctx_len, b, cap);
+  const int P = qg.N - 1;
+  if (P >= 0) {
+    qg.cnt = n;
+    qg.wlo = max(0, P - window + 1);
+    qg.S = n + (P - qg.wlo + 1);
   }
-  // o[t][r]: head 8*(r/4) + 4*hh + r%4, dim 32*t + r32, relative to this
-  // wave's max; rescale to the workgroup max and stage for the merge.
-#pragma unroll
-  for (int r = 0; r < 16; ++r) {
-    const int h = 8 * (r >> 2) + 4 * hh + (r & 3);
-    float M = -INFINITY;
-#pragma unroll
-    for (int w = 0; w < kSegWaves; ++w) M = fmaxf(M, s_m[w][h]);
-    const float mw = s_m[wave][h];
-    const float sc = (mw == -INFINITY) ? 0.f : fast_exp2(mw - M);
-#pragma unroll
-    for (int t = 0; t < 4; ++t) s_o[wave][h][32 * t + r32] = o[t][r] * sc;
+  const int s0 = seg * kSegB;
+  float2* mlo = ml + ((size_t)b * nseg + seg) * H;
+  if (s0 >= qg.S) {
+    if (threadIdx.x < H) mlo[threadIdx.x] = make_float2(-INFINITY, 0.f);
+    return;
   }
-  __syncthreads();
-  // Merge the waves in order.
-  float* po = part + ((size_t)bq * nseg + seg) * H * kHeadDim;
-  for (int e = threadIdx.x; e < 32 * kHeadDim; e += blockDim.x) {
-    const int h = e / kHeadDim, d = e % kHeadDim;
-    if (h >= H) continue;
-    float acc_o = 0.f;
-#pragma unroll
-    for (int w = 0; w < kSegWaves; ++w) acc_o += s_o[w][h][d];
-    po[(size_t)h * kHeadDim + d] = acc_o;
-  }
-  if (threadIdx.x < H) {
-    const int h = threadIdx.x;
-    float M = -INFINITY;
-    for (int w = 0; w < kSegWaves; ++w) M = fmaxf(M, s_m[w][h]);
-    float L = 0.f;
-    for (int w = 0; w < kSegWaves; ++w)
-      if (s_m[w][h] != -INFINITY) L += s_l[w][h] * fast_exp2(s_m[w][h] - M);
-    mlo[h] = make_float2(M, L);
-  }
+  auto key_at = [&](int p) {
+    const int idx = p < qg.cnt ? win[p] : qg.wlo + (p - qg.cnt);
+    return idx < 0 ? 0 : (idx >= qg.N ? qg.N - 1 : idx);
+  };
+  segment_partial_bf16(q, k, v, kv_stride, b, b, H, c2, qg, s0, key_at, lds.seg,
+                       part + ((size_t)b * nseg + seg) * H * kHeadDim, mlo);
 }
 
 // ---------------------------------------------------------------------------
@@ -377,6 +461,28 @@ hipError_t launch_sparse(const hs2_attn_desc& d, const void* q, const void* k, c
   }
   sparse_combine<<<dim3(d.n_heads, d.batch * d.n_q), kHeadDim, 0, st>>>(part, ml, nseg,
                                                                         d.n_heads, o, lse);
+  return hipGetLastError();
+}
+
+hipError_t launch_decode_tail(const hs2_attn_desc& d, const void* q, const void* k, const void* v,
+                              int64_t kv_stride, const int32_t* ctx_len, int cap,
+                              const uint32_t* hist, const char* sel_ws, int32_t* top_idx,
+                              int32_t* top_cnt, float* o, float* lse, char* ws, hipStream_t st) {
+  const SparseWs w = sparse_ws(d);
+  const SelectWs sw = select_ws(d, cap);
+  float* part = reinterpret_cast<float*>(ws + w.part_off);
+  float2* ml = reinterpret_cast<float2*>(ws + w.ml_off);
+  const int sel_max = d.k_top + d.window;
+  const int nseg = sel_max > 0 ? (sel_max + kSegB - 1) / kSegB : 1;
+  decode_tail_bf16<<<dim3(nseg, d.batch), kTailThreads, 0, st>>>(
+      static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
+      static_cast<const uint16_t*>(v), kv_stride, ctx_len, cap, d.k_top, d.window, d.n_heads,
+      d.sm_scale * kLog2e, hist, reinterpret_cast<const uint32_t*>(sel_ws + sw.cnt_off),
+      reinterpret_cast<const uint32_t*>(sel_ws + sw.meta_off),
+      reinterpret_cast<const uint2*>(sel_ws + sw.list_off), select_slices(cap), top_idx, top_cnt,
+      part, ml, nseg);
+  sparse_combine<<<dim3(d.n_heads, d.batch), kHeadDim, 0, st>>>(part, ml, nseg, d.n_heads, o,
+                                                                 lse);
   return hipGetLastError();
 }
 
