@@ -125,6 +125,9 @@ __global__ __launch_bounds__(1024) void pf_stats(PfArgs a) {
     stage_k(kblk, kb, [&](int r) { return min(kb0 + r, j1 - 1); });
     __syncthreads();
     if (P < kb0) continue;  // the whole block is in this query's future
+    // Every key of the block is inside this query's range and the split:
+    // no masks, and the scale folds into one fma per logit (c2 > 0).
+    const bool full = kb0 + kBlk <= j1 && kb0 + kBlk - 1 <= P;
 #pragma unroll
     for (int mt = 0; mt < 2; ++mt) {
       f32x16_t acc = {};
@@ -132,21 +135,33 @@ __global__ __launch_bounds__(1024) void pf_stats(PfArgs a) {
       for (int e = 0; e < 8; ++e)
         acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k_opnd(kblk, 32 * mt + r32, e, hh), qr[e], acc, 0, 0, 0);
       // acc[r]: row (query i, head r32), key kb0 + 32mt + 8(r/4) + 4hh + r%4
-      float x[16];
-      float bm = -INFINITY;
+      if (full) {
+        float bm = acc[0];
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int j = kb0 + 32 * mt + 8 * (r >> 2) + 4 * hh + (r & 3);
-        x[r] = (j < j1 && j <= P) ? acc[r] * a.c2 : -INFINITY;
-        bm = fmaxf(bm, x[r]);
+        for (int r = 1; r < 16; ++r) bm = fmaxf(bm, acc[r]);
+        const float mn = fmaxf(m, bm * a.c2);
+        float sum = l * fast_exp2(m - mn);
+#pragma unroll
+        for (int r = 0; r < 16; ++r) sum += fast_exp2(fmaf(acc[r], a.c2, -mn));
+        l = sum;
+        m = mn;
+      } else {
+        float x[16];
+        float bm = -INFINITY;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int j = kb0 + 32 * mt + 8 * (r >> 2) + 4 * hh + (r & 3);
+          x[r] = (j < j1 && j <= P) ? acc[r] * a.c2 : -INFINITY;
+          bm = fmaxf(bm, x[r]);
+        }
+        const float mn = fmaxf(m, bm);
+        const float mref = (mn == -INFINITY) ? 0.f : mn;
+        float sum = l * fast_exp2(m - mref);
+#pragma unroll
+        for (int r = 0; r < 16; ++r) sum += fast_exp2(x[r] - mref);
+        l = sum;
+        m = mn;
       }
-      const float mn = fmaxf(m, bm);
-      const float mref = (mn == -INFINITY) ? 0.f : mn;
-      float sum = l * fast_exp2(m - mref);
-#pragma unroll
-      for (int r = 0; r < 16; ++r) sum += fast_exp2(x[r] - mref);
-      l = sum;
-      m = mn;
     }
   }
   merge_ml(m, l, __shfl_xor(m, 32), __shfl_xor(l, 32));
@@ -200,47 +215,31 @@ __global__ __launch_bounds__(1024) void pf_colsum(PfArgs a) {
   float L[16];  // rows (heads) 8(r/4) + 4hh + r%4 of this wave's query
 #pragma unroll
   for (int r = 0; r < 16; ++r) L[r] = s_L[wave * 32 + 8 * (r >> 2) + 4 * hh + (r & 3)];
-  u32x4 ones;
-  ones[0] = ones[1] = ones[2] = ones[3] = 0x3F803F80u;  // bf16 1.0 pairs
   const uint16_t* kb = a.k + (size_t)b * a.kv_stride;
   float* out = a.colsum + ((size_t)b * (a.n_q / 16) + rb) * a.cap;
   for (int kb0 = j0; kb0 < j1; kb0 += kBlk) {
     __syncthreads();
     stage_k(kblk, kb, [&](int r) { return min(kb0 + r, j1 - 1); });
     __syncthreads();
+    const bool full = kb0 + kBlk <= j1 && kb0 + kBlk - 1 <= P;
 #pragma unroll
     for (int mt = 0; mt < 2; ++mt) {
       const int j = kb0 + 32 * mt + r32;  // this lane's key
-      const bool valid = j < j1 && j <= P;
-      f32x16_t cs = {};
+      float cs = 0.f;
       if (P >= kb0) {
         f32x16_t acc = {};
 #pragma unroll
         for (int e = 0; e < 8; ++e)
           acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qr[e], k_opnd(kblk, 32 * mt + r32, e, hh), acc, 0, 0, 0);
-        // acc[r]: row (query i, head 8(r/4) + 4hh + r%4), key j.
-        float p[16];
+        // acc[r]: row (query i, head 8(r/4) + 4hh + r%4), key j.  The sum
+        // over the query's 32 head rows: 16 in this lane, 16 in lane ^ 32.
+        // Padded heads have L = +inf, so their p is 0.
 #pragma unroll
-        for (int r = 0; r < 16; ++r) p[r] = valid ? fast_exp2(acc[r] * a.c2 - L[r]) : 0.f;
-        // Column sum over the 32 rows: ones . p, k-steps of 16 rows in the
-        // order the registers hold them (8s..8s+7).
-#pragma unroll
-        for (int ks = 0; ks < 2; ++ks) {
-          u32x4 hi, lo;
-#pragma unroll
-          for (int u = 0; u < 4; ++u) {
-            const float p0 = p[8 * ks + 2 * u], p1 = p[8 * ks + 2 * u + 1];
-            const uint16_t h0 = f32_to_bf16_rne(p0), h1 = f32_to_bf16_rne(p1);
-            hi[u] = (uint32_t)h0 | ((uint32_t)h1 << 16);
-            lo[u] = (uint32_t)f32_to_bf16_rne(p0 - bf16_to_f32(h0)) |
-                    ((uint32_t)f32_to_bf16_rne(p1 - bf16_to_f32(h1)) << 16);
-          }
-          cs = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(ones), as_bf16x8(hi), cs, 0, 0, 0);
-          cs = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(ones), as_bf16x8(lo), cs, 0, 0, 0);
-        }
+        for (int r = 0; r < 16; ++r) cs += fast_exp2(fmaf(acc[r], a.c2, -L[r]));
+        if (!full && !(j < j1 && j <= P)) cs = 0.f;
       }
-      // cs[0] of lanes hh == 0: sum over the wave's 32 rows for key j.
-      if (hh == 0) s_cs[wave][32 * mt + r32] = cs[0];
+      cs += __shfl_xor(cs, 32);
+      if (hh == 0) s_cs[wave][32 * mt + r32] = cs;
     }
     __syncthreads();
     if (threadIdx.x < kBlk) {
