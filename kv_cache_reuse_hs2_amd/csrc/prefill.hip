@@ -79,6 +79,44 @@ __device__ __forceinline__ bf16x8_t k_opnd(const uint8_t* blk, int key, int e, i
   return as_bf16x8(*reinterpret_cast<const u32x4*>(blk + key * kRowB + 32 * e + 16 * hh));
 }
 
+// K blocks of the two scoring passes go through a ring of LDS slots filled by
+// direct global-to-LDS loads (16 bytes a lane, no registers in between), so
+// that the next blocks load while one is in the MFMAs.  A slot holds 64 rows
+// of 256 bytes; the 16-byte chunks of row r are stored rotated by r % 16
+// (chunk c at c ^ (r % 16)), which keeps the operand reads of 16 consecutive
+// rows on distinct banks.  The compiler does not track these loads: a wave
+// waits for its own with an explicit vmcnt, and a barrier then publishes the
+// whole block.
+typedef __attribute__((address_space(3))) void lds_void_t;
+constexpr int kRing = 3;                  // blocks in LDS: one in use, two loading
+constexpr int kSlotB = kBlk * kHeadDim * 2;  // 16 KiB
+
+// 64 rows by 16 waves of a 1024-thread workgroup: wave w moves rows
+// 4w .. 4w+3, lane l the stored chunk l % 16 of row 4w + l / 16.
+template <typename RowOf>
+__device__ __forceinline__ void dma_k_block(uint8_t* slot, const uint16_t* kb, RowOf row_of) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int r = 4 * wave + (lane >> 4);
+  const int c = (lane & 15) ^ (r & 15);
+  __builtin_amdgcn_global_load_lds(kb + (size_t)row_of(r) * kHeadDim + 8 * c,
+                                   (lds_void_t*)(slot + wave * 1024), 16, 0, 0);
+}
+
+__device__ __forceinline__ bf16x8_t k_opnd_ring(const uint8_t* slot, int key, int e, int hh) {
+  return as_bf16x8(*reinterpret_cast<const u32x4*>(
+      slot + key * (kHeadDim * 2) + 16 * ((2 * e + hh) ^ (key & 15))));
+}
+
+// Wait until this wave has at most `younger` (0 or 1) ring loads in flight and
+// its LDS operations are done, then meet the other waves.
+__device__ __forceinline__ void ring_barrier(bool younger) {
+  if (younger) __builtin_amdgcn_s_waitcnt(1 | (7 << 4));  // vmcnt(1) lgkmcnt(0)
+  else __builtin_amdgcn_s_waitcnt(0 | (7 << 4));          // vmcnt(0) lgkmcnt(0)
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
+}
+
 struct PfArgs {
   const uint16_t* q;
   const uint16_t* k;
@@ -115,15 +153,24 @@ __global__ __launch_bounds__(1024) void pf_stats(PfArgs a) {
     if (hh == 0) st[r32] = make_float2(-INFINITY, 0.f);
     return;
   }
-  __shared__ __attribute__((aligned(16))) uint8_t kblk[kBlk * kRowB];
+  __shared__ __attribute__((aligned(16))) uint8_t ring[kRing * kSlotB];
   bf16x8_t qr[8];
   load_q(a.q + ((size_t)b * a.n_q + i) * a.H * kHeadDim, a.H, r32, hh, P >= 0, qr);
   const uint16_t* kb = a.k + (size_t)b * a.kv_stride;
+  const int nblk = (j1 - j0 + kBlk - 1) / kBlk;
+  auto rows_of = [&](int bi) { return [=](int r) { return min(j0 + bi * kBlk + r, j1 - 1); }; };
+  // Q is in registers before the ring starts, so that no later wait for it
+  // has to cover the ring loads.
+  __builtin_amdgcn_s_waitcnt(0 | (7 << 4) | (15 << 8));  // vmcnt(0)
+  dma_k_block(ring, kb, rows_of(0));
+  if (nblk > 1) dma_k_block(ring + kSlotB, kb, rows_of(1));
   float m = -INFINITY, l = 0.f;
-  for (int kb0 = j0; kb0 < j1; kb0 += kBlk) {
-    __syncthreads();
-    stage_k(kblk, kb, [&](int r) { return min(kb0 + r, j1 - 1); });
-    __syncthreads();
+  for (int bi = 0; bi < nblk; ++bi) {
+    // Block bi has landed for every wave; the slot of block bi-1 is free.
+    ring_barrier(bi + 1 < nblk);
+    if (bi + 2 < nblk) dma_k_block(ring + ((bi + 2) % kRing) * kSlotB, kb, rows_of(bi + 2));
+    const uint8_t* kblk = ring + (bi % kRing) * kSlotB;
+    const int kb0 = j0 + bi * kBlk;
     if (P < kb0) continue;  // the whole block is in this query's future
     // Every key of the block is inside this query's range and the split:
     // no masks, and the scale folds into one fma per logit (c2 > 0).
@@ -133,7 +180,7 @@ __global__ __launch_bounds__(1024) void pf_stats(PfArgs a) {
       f32x16_t acc = {};
 #pragma unroll
       for (int e = 0; e < 8; ++e)
-        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k_opnd(kblk, 32 * mt + r32, e, hh), qr[e], acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k_opnd_ring(kblk, 32 * mt + r32, e, hh), qr[e], acc, 0, 0, 0);
       // acc[r]: row (query i, head r32), key kb0 + 32mt + 8(r/4) + 4hh + r%4
       if (full) {
         float bm = acc[0];
@@ -206,9 +253,16 @@ __global__ __launch_bounds__(1024) void pf_colsum(PfArgs a) {
       a.lse_out[((size_t)b * a.n_q + i) * a.H + r32] = -INFINITY;
     return;
   }
-  __shared__ __attribute__((aligned(16))) uint8_t kblk[kBlk * kRowB];
-  __shared__ float s_L[16 * 32];
-  __shared__ float s_cs[16][kBlk];
+  // One LDS object: with several, the compiler tracks the ring loads per
+  // object and waits for all of them before any read of the ring.
+  __shared__ struct __attribute__((aligned(16))) {
+    uint8_t ring[kRing * kSlotB];
+    float s_L[16 * 32];
+    float s_cs[16][kBlk];
+  } sm;
+  uint8_t* ring = sm.ring;
+  float* s_L = sm.s_L;
+  auto& s_cs = sm.s_cs;
   fold_rows(a, b, rb, N, s_L, s == 0);
   bf16x8_t qr[8];
   load_q(a.q + ((size_t)b * a.n_q + i) * a.H * kHeadDim, a.H, r32, hh, P >= 0, qr);
@@ -217,31 +271,47 @@ __global__ __launch_bounds__(1024) void pf_colsum(PfArgs a) {
   for (int r = 0; r < 16; ++r) L[r] = s_L[wave * 32 + 8 * (r >> 2) + 4 * hh + (r & 3)];
   const uint16_t* kb = a.k + (size_t)b * a.kv_stride;
   float* out = a.colsum + ((size_t)b * (a.n_q / 16) + rb) * a.cap;
-  for (int kb0 = j0; kb0 < j1; kb0 += kBlk) {
-    __syncthreads();
-    stage_k(kblk, kb, [&](int r) { return min(kb0 + r, j1 - 1); });
-    __syncthreads();
+  const int nblk = (j1 - j0 + kBlk - 1) / kBlk;
+  auto rows_of = [&](int bi) { return [=](int r) { return min(j0 + bi * kBlk + r, j1 - 1); }; };
+  // Q is in registers before the ring starts, so that no later wait for it
+  // has to cover the ring loads.
+  __builtin_amdgcn_s_waitcnt(0 | (7 << 4) | (15 << 8));  // vmcnt(0)
+  dma_k_block(ring, kb, rows_of(0));
+  if (nblk > 1) dma_k_block(ring + kSlotB, kb, rows_of(1));
+  for (int bi = 0; bi < nblk; ++bi) {
+    // Block bi has landed for every wave; the slot of block bi-1 is free,
+    // and so is s_cs (read by the previous block's final sum).
+    ring_barrier(bi + 1 < nblk);
+    if (bi + 2 < nblk) dma_k_block(ring + ((bi + 2) % kRing) * kSlotB, kb, rows_of(bi + 2));
+    const uint8_t* kblk = ring + (bi % kRing) * kSlotB;
+    const int kb0 = j0 + bi * kBlk;
     const bool full = kb0 + kBlk <= j1 && kb0 + kBlk - 1 <= P;
 #pragma unroll
     for (int mt = 0; mt < 2; ++mt) {
       const int j = kb0 + 32 * mt + r32;  // this lane's key
+      // Computed for every block (a block in the query's future, at most the
+      // last one, is masked to 0), so that the operand reads follow the
+      // barrier in the same straight-line code.
+      f32x16_t acc = {};
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qr[e], k_opnd_ring(kblk, 32 * mt + r32, e, hh), acc, 0, 0, 0);
+      // acc[r]: row (query i, head 8(r/4) + 4hh + r%4), key j.  The sum over
+      // the query's 32 head rows: 16 in this lane, 16 in lane ^ 32.  Padded
+      // heads have L = +inf, so their p is 0.
       float cs = 0.f;
-      if (P >= kb0) {
-        f32x16_t acc = {};
 #pragma unroll
-        for (int e = 0; e < 8; ++e)
-          acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qr[e], k_opnd(kblk, 32 * mt + r32, e, hh), acc, 0, 0, 0);
-        // acc[r]: row (query i, head 8(r/4) + 4hh + r%4), key j.  The sum
-        // over the query's 32 head rows: 16 in this lane, 16 in lane ^ 32.
-        // Padded heads have L = +inf, so their p is 0.
-#pragma unroll
-        for (int r = 0; r < 16; ++r) cs += fast_exp2(fmaf(acc[r], a.c2, -L[r]));
-        if (!full && !(j < j1 && j <= P)) cs = 0.f;
-      }
+      for (int r = 0; r < 16; ++r) cs += fast_exp2(fmaf(acc[r], a.c2, -L[r]));
+      if (!full && !(j < j1 && j <= P)) cs = 0.f;
       cs += __shfl_xor(cs, 32);
       if (hh == 0) s_cs[wave][32 * mt + r32] = cs;
     }
-    __syncthreads();
+    // LDS-only barrier: a full __syncthreads would also wait for the ring
+    // loads in flight.
+    __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0)
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
     if (threadIdx.x < kBlk) {
       const int j = kb0 + threadIdx.x;
       float sum = 0.f;
