@@ -192,11 +192,12 @@ __device__ __forceinline__ void bridge_step(int it, int nk, const uint16_t* w_pa
                                             int wave, int lane, const int (&a_off)[2][2],
                                             uint8_t* lds, const Operands& cur, Operands& next,
                                             WRegs& wnext, const WRegs& wcur,
-                                            f32x16_t (&acc)[2][8]) {
+                                            f32x16_t (&acc)[2][8], int rot) {
   constexpr int kSB = Ring<kDirect>::kStageBytes;
   // Younger than stage it+1: stages it+2 .. it+kAhead-1.
   wait_then_barrier<(kAhead - 2) * kLoadsPerStage>();
-  const int g = min(it + kAhead, nk - 1);
+  int g = min(it + kAhead, nk - 1) + rot;  // rot < nk
+  if (g >= nk) g -= nk;
   if (!kDirect) load_w_regs(w_k, w_v, g, t, wnext);
   issue_stage<kDirect>(g, w_packed, hsrc, wave, lane, lds + (it % kStages) * kSB);
   read_operands<kDirect>(lds + ((it + 1) % kStages) * kSB, a_off, lane, next);
@@ -258,27 +259,37 @@ __global__ __launch_bounds__(64 * kWaves) void bridge_gemm(const uint16_t* __res
     for (int n = 0; n < 8; ++n) acc[mt][n] = (f32x16_t){};
 
   const int nk = d_model / kBK;  // even: d_model is a multiple of 64
+  // Workgroups start their reduction at different k slices (and wrap), so
+  // that at any moment they read different columns of their rows: the
+  // concurrent requests spread over more memory channels than when every
+  // workgroup reads the same 64 bytes of each of its rows.  Stage s of this
+  // workgroup is the k slice phys(s).
+  const int rot = blockIdx.x % nk;
+  auto phys = [&](int s) {
+    const int g = min(s, nk - 1) + rot;
+    return g >= nk ? g - nk : g;
+  };
   WRegs w0, w1;
   if (kDirect) {
 #pragma unroll
     for (int g = 0; g < kAhead; ++g)
-      issue_stage<true>(min(g, nk - 1), w_packed, hsrc, wave, lane, lds + g * kSB);
+      issue_stage<true>(phys(g), w_packed, hsrc, wave, lane, lds + g * kSB);
   } else {
     // Same issue order as the steps (weights, then H, per stage).  Stages
     // 0..2 are written to LDS here; stage 3 stays in w1 for the first step.
     static_assert(kAhead == 4, "prologue written for four stages");
-    load_w_regs(w_k, w_v, 0, t, w0);
-    issue_stage<false>(0, w_packed, hsrc, wave, lane, lds);
-    load_w_regs(w_k, w_v, min(1, nk - 1), t, w1);
-    issue_stage<false>(min(1, nk - 1), w_packed, hsrc, wave, lane, lds + kSB);
+    load_w_regs(w_k, w_v, phys(0), t, w0);
+    issue_stage<false>(phys(0), w_packed, hsrc, wave, lane, lds);
+    load_w_regs(w_k, w_v, phys(1), t, w1);
+    issue_stage<false>(phys(1), w_packed, hsrc, wave, lane, lds + kSB);
     wait_vm<kHLoads + kLoadsPerStage>();
     store_w_regs(lds, t, w0);
     wait_vm<kHLoads>();
     store_w_regs(lds + kSB, t, w1);
-    load_w_regs(w_k, w_v, min(2, nk - 1), t, w0);
-    issue_stage<false>(min(2, nk - 1), w_packed, hsrc, wave, lane, lds + 2 * kSB);
-    load_w_regs(w_k, w_v, min(3, nk - 1), t, w1);
-    issue_stage<false>(min(3, nk - 1), w_packed, hsrc, wave, lane, lds + 3 * kSB);
+    load_w_regs(w_k, w_v, phys(2), t, w0);
+    issue_stage<false>(phys(2), w_packed, hsrc, wave, lane, lds + 2 * kSB);
+    load_w_regs(w_k, w_v, phys(3), t, w1);
+    issue_stage<false>(phys(3), w_packed, hsrc, wave, lane, lds + 3 * kSB);
     wait_vm<kHLoads + kLoadsPerStage>();
     store_w_regs(lds + 2 * kSB, t, w0);
   }
@@ -287,9 +298,9 @@ __global__ __launch_bounds__(64 * kWaves) void bridge_gemm(const uint16_t* __res
   read_operands<kDirect>(lds, a_off, lane, o0);
   for (int it = 0; it < nk; it += 2) {
     bridge_step<kDirect>(it, nk, w_packed, w_k, w_v, hsrc, t, wave, lane, a_off, lds, o0, o1, w0,
-                         w1, acc);
+                         w1, acc, rot);
     bridge_step<kDirect>(it + 1, nk, w_packed, w_k, w_v, hsrc, t, wave, lane, a_off, lds, o1, o0,
-                         w1, w0, acc);
+                         w1, w0, acc, rot);
   }
   wait_then_barrier<0>();  // every wave is done with the ring
 
