@@ -66,6 +66,77 @@ def time_events(fn, steps: int, warmup: int) -> float:
     return e0.elapsed_time(e1) / steps
 
 
+def time_graphs(fn, steps: int, warmup: int) -> float:
+    """Average milliseconds of fn() replayed from HIP graphs of GRAPH_STEPS
+    consecutive calls (as the headline step), HIP events around exactly
+    `steps` calls."""
+    import torch
+
+    stream = torch.cuda.current_stream()
+    per = min(GRAPH_STEPS, steps)
+    graphs = {}
+    for n in {per, 1}:
+        side = torch.cuda.Stream()
+        side.wait_stream(stream)
+        with torch.cuda.stream(side):
+            fn()
+        stream.wait_stream(side)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for _ in range(n):
+                fn()
+        graphs[n] = g
+    torch.cuda.synchronize()
+    for _ in range(warmup):
+        graphs[1].replay()
+    torch.cuda.synchronize()
+    plan = [graphs[per]] * (steps // per) + [graphs[1]] * (steps % per)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for g in plan:
+        g.replay()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / steps
+
+
+def sparse_layer_measurements(steps: int, warmup: int) -> dict:
+    """S sparse layers after the full layer, sharing its selection: the decode
+    step (scoring, selection, first sparse layer) plus S-1 further layers in
+    one gather (hs2_sparse_attn_gather_layers), against S-1 separate
+    hs2_sparse_attn_gather calls."""
+    import numpy as np
+    import torch
+
+    from kv_cache_reuse_hs2_amd.torch_api import (make_buffers, run_fused_step, run_sparse,
+                                                  run_sparse_layers, to_device)
+    from workloads import WORKLOADS, make_decode_inputs
+
+    w = WORKLOADS[WORKLOAD]
+    inp = make_decode_inputs(w)
+    buf = make_buffers(inp, n_heads=w.n_heads, k_top=w.k_top, window=w.window,
+                       sm_scale=w.sm_scale, dtype=w.dtype)
+    rng = np.random.Generator(np.random.PCG64(w.seed + 7))
+    out = {}
+    for n_sparse in (1, 2, 4, 8):
+        extra = n_sparse - 1
+        if extra:
+            q = rng.standard_normal((extra,) + inp["q_raw"].shape, dtype=np.float32)
+            q_layers = to_device(q).to(torch.bfloat16).view(torch.int16)
+            step = lambda: (run_fused_step(buf), run_sparse_layers(buf, q_layers))  # noqa: E731
+            sep = lambda: (run_fused_step(buf),  # noqa: E731
+                           [run_sparse(buf, q=q_layers[i]) for i in range(extra)])
+        else:
+            step = sep = lambda: run_fused_step(buf)  # noqa: E731
+        ms = time_graphs(step, steps, warmup)
+        ms_sep = time_graphs(sep, steps, warmup)
+        out[f"sparse_layers_{n_sparse}"] = {
+            "ms_per_step": round(ms, 5), "tokens_per_s": round(w.batch / (ms * 1e-3), 1),
+            "ms_per_step_separate_calls": round(ms_sep, 5)}
+    return out
+
+
 def extra_measurements(steps: int, warmup: int) -> dict:
     """The other shapes of the method, measured the same way (not the headline):
     batched decode at 64k, chunked prefill of 8,192 queries on a 131,072-token
@@ -349,6 +420,8 @@ def main() -> int:
     if args.extras:
         del buf
         out["extras"] = extra_measurements(args.steps, args.warmup)
+        out["extras"]["decode_bf16_256k_b4_shared_selection"] = sparse_layer_measurements(
+            args.steps, args.warmup)
     if args.calibrate:
         src = torch.empty(256 * MIB, dtype=torch.uint8, device="cuda").fill_(1)
         dst = torch.empty_like(src)

@@ -154,6 +154,28 @@ HS2_API hs2_status hs2_sparse_attn_gather(const hs2_attn_desc* desc, const void*
                                   hs2_stream_t stream);
 
 /*
+ * Several sparse layers after one full layer.  Each full-attention layer
+ * hands its selection and its K/V cache to the sparse layers that follow it
+ * ([Origins] "The Self-Decoder and Cross-Decoder Split", on HySparse's KV
+ * Reuse), so n_layers sparse layers attend over the same rows with their own
+ * queries.  This call gathers every selected K/V row once for all of them.
+ * Decode only (n_q = tile_q = 1) and bf16 only in this build
+ * (HS2_EUNSUPPORTED otherwise); 1 <= n_layers <= 64.  q_layers is bf16
+ * [n_layers][B][H][D], o_layers fp32 [n_layers][B][H][D], lse_layers
+ * (nullable) fp32 [n_layers][B][H].  The results are those of n_layers calls
+ * of hs2_sparse_attn_gather, bit for bit.  The workspace (16-byte aligned)
+ * needs hs2_sparse_layers_workspace_size bytes.
+ */
+HS2_API size_t hs2_sparse_layers_workspace_size(const hs2_attn_desc* desc, int n_layers);
+HS2_API hs2_status hs2_sparse_attn_gather_layers(const hs2_attn_desc* desc, int n_layers,
+                                         const void* q_layers, const void* k, const void* v,
+                                         int64_t kv_stride, const int32_t* ctx_len,
+                                         int kv_capacity, const int32_t* top_idx,
+                                         const int32_t* top_cnt, float* o_layers,
+                                         float* lse_layers, void* ws, size_t ws_bytes,
+                                         hs2_stream_t stream);
+
+/*
  * One decode step of a hybrid block in a single call: the full layer's
  * scoring (as hs2_full_attn_scores, with q), the selection (as
  * hs2_select_topk_window) and the sparse layer (as hs2_sparse_attn_gather,

@@ -28,6 +28,8 @@ EXPORTS = (
     "hs2_full_attn_scores",
     "hs2_select_topk_window",
     "hs2_sparse_attn_gather",
+    "hs2_sparse_layers_workspace_size",
+    "hs2_sparse_attn_gather_layers",
     "hs2_decode_step",
     "hs2_bridge_kv",
     "hs2_bridge_packed_bytes",
@@ -86,6 +88,11 @@ def load(path: str | None = None):
     lib.hs2_sparse_attn_gather.argtypes = [_desc_p, _vp, _vp, _vp, _i64, _vp, _int, _vp, _vp,
                                            _vp, _vp, _vp, _sz, _vp]
     lib.hs2_sparse_attn_gather.restype = _int
+    lib.hs2_sparse_layers_workspace_size.argtypes = [_desc_p, _int]
+    lib.hs2_sparse_layers_workspace_size.restype = _sz
+    lib.hs2_sparse_attn_gather_layers.argtypes = [_desc_p, _int, _vp, _vp, _vp, _i64, _vp, _int,
+                                                  _vp, _vp, _vp, _vp, _vp, _sz, _vp]
+    lib.hs2_sparse_attn_gather_layers.restype = _int
     lib.hs2_decode_step.argtypes = [_desc_p, _vp, _vp, _vp, _vp, _i64, _vp, _int, _vp, _vp, _vp,
                                     _vp, _vp, _vp, _vp, _sz, _vp]
     lib.hs2_decode_step.restype = _int
@@ -169,6 +176,20 @@ def hs2_sparse_attn_gather(desc, q, k, v, kv_stride, ctx_len, kv_capacity, top_i
                                        _ptr(top_idx), _ptr(top_cnt), _ptr(o), _ptr(lse), _ptr(ws),
                                        _nbytes(ws), _stream(stream))
     _check(st, "hs2_sparse_attn_gather")
+
+
+def hs2_sparse_layers_workspace_size(desc, n_layers) -> int:
+    return int(load().hs2_sparse_layers_workspace_size(ctypes.byref(desc), int(n_layers)))
+
+
+def hs2_sparse_attn_gather_layers(desc, n_layers, q_layers, k, v, kv_stride, ctx_len,
+                                  kv_capacity, top_idx, top_cnt, o_layers, lse_layers=None,
+                                  ws=None, stream=None) -> None:
+    st = load().hs2_sparse_attn_gather_layers(
+        ctypes.byref(desc), int(n_layers), _ptr(q_layers), _ptr(k), _ptr(v), int(kv_stride),
+        _ptr(ctx_len), int(kv_capacity), _ptr(top_idx), _ptr(top_cnt), _ptr(o_layers),
+        _ptr(lse_layers), _ptr(ws), _nbytes(ws), _stream(stream))
+    _check(st, "hs2_sparse_attn_gather_layers")
 
 
 def hs2_decode_step(desc, q, q_sparse, k, v, kv_stride, ctx_len, kv_capacity, scores, lse_full,

@@ -16,6 +16,7 @@ hipError_t launch_bridge(const uint16_t* h, int64_t ldh, const uint16_t* w_packe
 namespace {
 
 constexpr int kMaxSelectCap = 1024 * kSelSlice;  // selector pools up to 4,194,304 keys
+constexpr int kMaxLayers = 64;                   // sparse layers per shared selection
 
 bool misaligned(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) != 0; }
 
@@ -152,6 +153,40 @@ hs2_status hs2_sparse_attn_gather(const hs2_attn_desc* desc, const void* q, cons
   return launched(launch_sparse(*desc, q, k, v, kv_stride, ctx_len, kv_capacity, top_idx, top_cnt,
                                 o, lse, static_cast<char*>(ws) + l.sparse,
                                 static_cast<hipStream_t>(stream)));
+}
+
+size_t hs2_sparse_layers_workspace_size(const hs2_attn_desc* desc, int n_layers) {
+  if (check_desc(desc) != HS2_OK || n_layers < 1 || n_layers > kMaxLayers) return 0;
+  return sparse_layers_ws_bytes(*desc, n_layers);
+}
+
+hs2_status hs2_sparse_attn_gather_layers(const hs2_attn_desc* desc, int n_layers,
+                                         const void* q_layers, const void* k, const void* v,
+                                         int64_t kv_stride, const int32_t* ctx_len,
+                                         int kv_capacity, const int32_t* top_idx,
+                                         const int32_t* top_cnt, float* o_layers,
+                                         float* lse_layers, void* ws, size_t ws_bytes,
+                                         hs2_stream_t stream) {
+  hs2_status s = check_desc(desc);
+  if (s != HS2_OK) return s;
+  if (q_layers == nullptr || k == nullptr || v == nullptr || ctx_len == nullptr ||
+      top_cnt == nullptr || o_layers == nullptr)
+    return HS2_EINVAL;
+  if (top_idx == nullptr && desc->k_top > 0) return HS2_EINVAL;
+  if (n_layers < 1) return HS2_EINVAL;
+  if (n_layers > kMaxLayers || is_prefill(*desc) || desc->dtype != HS2_BF16)
+    return HS2_EUNSUPPORTED;
+  if ((s = check_cache(desc, kv_stride, kv_capacity)) != HS2_OK) return s;
+  if (misaligned(q_layers) || misaligned(k) || misaligned(v) || misaligned(ctx_len) ||
+      misaligned(top_idx) || misaligned(top_cnt) || misaligned(o_layers) ||
+      misaligned(lse_layers) || misaligned(ws))
+    return HS2_EALIGN;
+  if (ws_bytes < sparse_layers_ws_bytes(*desc, n_layers)) return HS2_EWORKSPACE;
+  if (ws == nullptr) return HS2_EINVAL;
+  (void)hipGetLastError();
+  return launched(launch_sparse_layers(*desc, n_layers, q_layers, k, v, kv_stride, ctx_len,
+                                       kv_capacity, top_idx, top_cnt, o_layers, lse_layers,
+                                       static_cast<char*>(ws), static_cast<hipStream_t>(stream)));
 }
 
 hs2_status hs2_decode_step(const hs2_attn_desc* desc, const void* q, const void* q_sparse,

@@ -217,6 +217,16 @@ hipError_t launch_sparse(const hs2_attn_desc& d, const void* q, const void* k, c
                          const int32_t* top_idx, const int32_t* top_cnt, float* o, float* lse,
                          char* ws, hipStream_t st);
 
+// Several sparse layers sharing one selection (bf16 decode): each selected
+// K/V row is gathered once for all n_layers queries; q_layers, o_layers and
+// lse_layers are [n_layers][B][H][D] / [n_layers][B][H].
+size_t sparse_layers_ws_bytes(const hs2_attn_desc& d, int n_layers);
+hipError_t launch_sparse_layers(const hs2_attn_desc& d, int n_layers, const void* q_layers,
+                                const void* k, const void* v, int64_t kv_stride,
+                                const int32_t* ctx_len, int cap, const int32_t* top_idx,
+                                const int32_t* top_cnt, float* o_layers, float* lse_layers,
+                                char* ws, hipStream_t st);
+
 // bf16 decode after launch_select(final_stage = false): the final selection
 // (to top_idx/top_cnt) and the sparse layer in one pass over the candidate
 // lists of sel_ws, then the merge of the partials; same results as

@@ -80,17 +80,51 @@ struct SegLds {
   float s_o[kSegWaves][32][kHeadDim + 4];
 };
 
-// Partial of the segment starting at selection position s0 of query bq
-// (sequence b): (max, sum) per head to mlo[H] and o to po[H][D].  Called by
-// every thread of the workgroup; waves 0..kSegWaves-1 gather 32 keys each,
-// any further waves only take part in the barriers and the final merge.
-// key_at(p) gives the cache index of selection position p < qg.S.
+// Gather of the segment starting at selection position s0 (sequence b):
+// waves 0..kSegWaves-1 load 32 keys each, K rows into kr (the A operand of
+// QK^T: lane = key r32, dims 16e + 8hh) and V rows transposed into L.vt
+// (vt[wave][d][key]).  key_at(p) gives the cache index of selection position
+// p < qg.S.  Called by every thread; other waves do nothing.
 template <typename KeyAt>
-__device__ __forceinline__ void segment_partial_bf16(
-    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
-    const uint16_t* __restrict__ v, int64_t kv_stride, int b, int bq, int H, float c2,
-    const QueryGeom& qg, int s0, KeyAt key_at, SegLds& L, float* __restrict__ po,
-    float2* __restrict__ mlo) {
+__device__ __forceinline__ void segment_gather_bf16(const uint16_t* __restrict__ k,
+                                                    const uint16_t* __restrict__ v,
+                                                    int64_t kv_stride, int b,
+                                                    const QueryGeom& qg, int s0, KeyAt key_at,
+                                                    SegLds& L, u32x4 (&kr)[8]) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int r32 = lane & 31, hh = lane >> 5;
+  if (wave >= kSegWaves) return;
+  const int pw = s0 + 32 * wave;  // first selection position of this wave
+  const int idx = key_at((pw + r32 < qg.S) ? pw + r32 : s0);
+  const size_t rowoff = (size_t)b * kv_stride + (size_t)idx * kHeadDim;
+  u32x4 vr[8];
+  const u32x4* kp = reinterpret_cast<const u32x4*>(k + rowoff + 8 * hh);
+  const u32x4* vp = reinterpret_cast<const u32x4*>(v + rowoff + 64 * hh);
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    kr[e] = kp[2 * e];
+    vr[e] = vp[e];
+  }
+  // V transposed into LDS: vt[wave][d][key], key = r32, d = 64*hh + 8*e + j.
+#pragma unroll
+  for (int e = 0; e < 8; ++e)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      L.vt[wave][64 * hh + 8 * e + 2 * j][r32] = (uint16_t)(vr[e][j] & 0xFFFFu);
+      L.vt[wave][64 * hh + 8 * e + 2 * j + 1][r32] = (uint16_t)(vr[e][j] >> 16);
+    }
+}
+
+// Partial of one query over the gathered segment (kr, L.vt): (max, sum) per
+// head to mlo[H] and o to po[H][D]; qb is the query's [H][D] rows.  Called by
+// every thread of the workgroup, after segment_gather_bf16; its barriers also
+// order the gather's LDS writes before the PV reads.  The LDS statistics and
+// partials are free again when it returns.
+__device__ __forceinline__ void segment_query_bf16(const uint16_t* __restrict__ qb, int H,
+                                                   float c2, const QueryGeom& qg, int s0,
+                                                   const u32x4 (&kr)[8], SegLds& L,
+                                                   float* __restrict__ po,
+                                                   float2* __restrict__ mlo) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int r32 = lane & 31, hh = lane >> 5;
   const bool active = wave < kSegWaves;
@@ -98,34 +132,14 @@ __device__ __forceinline__ void segment_partial_bf16(
   const bool wave_live = active && pw < qg.S;
   float x[16];
   if (active) {
-    const int idx = key_at((pw + r32 < qg.S) ? pw + r32 : s0);
-    const size_t rowoff = (size_t)b * kv_stride + (size_t)idx * kHeadDim;
-    // Gathered K (A operand) and V rows; Q^T as the B operand.
-    u32x4 kr[8], vr[8];
-    const u32x4* kp = reinterpret_cast<const u32x4*>(k + rowoff + 8 * hh);
-    const u32x4* vp = reinterpret_cast<const u32x4*>(v + rowoff + 64 * hh);
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      kr[e] = kp[2 * e];
-      vr[e] = vp[e];
-    }
+    // Q^T as the B operand.
     bf16x8_t qreg[8];
-    const uint16_t* qb = q + (size_t)bq * H * kHeadDim;
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       u32x4 xq = {0u, 0u, 0u, 0u};
       if (r32 < H) xq = *reinterpret_cast<const u32x4*>(qb + r32 * kHeadDim + 16 * e + 8 * hh);
       qreg[e] = as_bf16x8(xq);
     }
-    // V transposed into LDS: vt[wave][d][key], key = r32, d = 64*hh + 8*e + j.
-#pragma unroll
-    for (int e = 0; e < 8; ++e)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        L.vt[wave][64 * hh + 8 * e + 2 * j][r32] = (uint16_t)(vr[e][j] & 0xFFFFu);
-        L.vt[wave][64 * hh + 8 * e + 2 * j + 1][r32] = (uint16_t)(vr[e][j] >> 16);
-      }
-
     f32x16_t acc = {};
 #pragma unroll
     for (int e = 0; e < 8; ++e)
@@ -212,6 +226,19 @@ __device__ __forceinline__ void segment_partial_bf16(
       if (L.s_m[w][h] != -INFINITY) Ls += L.s_l[w][h] * fast_exp2(L.s_m[w][h] - M);
     mlo[h] = make_float2(M, Ls);
   }
+  __syncthreads();
+}
+
+// Gather and partial of one query (one sparse layer).
+template <typename KeyAt>
+__device__ __forceinline__ void segment_partial_bf16(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
+    const uint16_t* __restrict__ v, int64_t kv_stride, int b, int bq, int H, float c2,
+    const QueryGeom& qg, int s0, KeyAt key_at, SegLds& L, float* __restrict__ po,
+    float2* __restrict__ mlo) {
+  u32x4 kr[8];
+  segment_gather_bf16(k, v, kv_stride, b, qg, s0, key_at, L, kr);
+  segment_query_bf16(q + (size_t)bq * H * kHeadDim, H, c2, qg, s0, kr, L, po, mlo);
 }
 
 __global__ __launch_bounds__(64 * kSegWaves) void sparse_partial_bf16(
@@ -234,6 +261,39 @@ __global__ __launch_bounds__(64 * kSegWaves) void sparse_partial_bf16(
   segment_partial_bf16(q, k, v, kv_stride, b, bq, H, c2, qg, s0,
                        [&](int p) { return sel_key(qg, top_row, p); }, lds,
                        part + ((size_t)bq * nseg + seg) * H * kHeadDim, mlo);
+}
+
+// ---------------------------------------------------------------------------
+// Several sparse layers after one full layer (bf16 decode): the layers share
+// the selection and the K/V cache, so each workgroup gathers its segment once
+// and runs every layer's query over it.  Partials are laid out as if the
+// layers were extra queries (row l*B + b), so sparse_combine merges them.
+__global__ __launch_bounds__(64 * kSegWaves) void sparse_layers_bf16(
+    const uint16_t* __restrict__ q_layers, const uint16_t* __restrict__ k,
+    const uint16_t* __restrict__ v, int64_t kv_stride, const int32_t* __restrict__ ctx_len,
+    int cap, const int32_t* __restrict__ top_idx, const int32_t* __restrict__ top_cnt, int B,
+    int k_top, int window, int H, float c2, int n_layers, float* __restrict__ part,
+    float2* __restrict__ ml, int nseg) {
+  __shared__ SegLds lds;
+  const int seg = blockIdx.x, b = blockIdx.y;  // one query per sequence
+  const QueryGeom qg = query_geom(ctx_len, top_cnt, cap, b, 0, 0, 1, 1, k_top, window);
+  const int s0 = seg * kSegB;
+  if (s0 >= qg.S) {
+    if (threadIdx.x < H)
+      for (int l = 0; l < n_layers; ++l)
+        ml[((size_t)(l * B + b) * nseg + seg) * H + threadIdx.x] = make_float2(-INFINITY, 0.f);
+    return;
+  }
+  const int32_t* top_row = top_idx + (size_t)b * k_top;
+  u32x4 kr[8];
+  segment_gather_bf16(k, v, kv_stride, b, qg, s0, [&](int p) { return sel_key(qg, top_row, p); },
+                      lds, kr);
+  for (int l = 0; l < n_layers; ++l) {
+    const int row = l * B + b;
+    segment_query_bf16(q_layers + (size_t)row * H * kHeadDim, H, c2, qg, s0, kr, lds,
+                       part + ((size_t)row * nseg + seg) * H * kHeadDim,
+                       ml + ((size_t)row * nseg + seg) * H);
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -483,6 +543,34 @@ hipError_t launch_decode_tail(const hs2_attn_desc& d, const void* q, const void*
       part, ml, nseg);
   sparse_combine<<<dim3(d.n_heads, d.batch), kHeadDim, 0, st>>>(part, ml, nseg, d.n_heads, o,
                                                                  lse);
+  return hipGetLastError();
+}
+
+size_t sparse_layers_ws_bytes(const hs2_attn_desc& d, int n_layers) {
+  const int sel_max = d.k_top + d.window;
+  const size_t nseg = sel_max > 0 ? (sel_max + kSegB - 1) / kSegB : 1;
+  const size_t rows = (size_t)n_layers * d.batch;
+  return align_up(sizeof(float) * rows * nseg * d.n_heads * kHeadDim, 256) +
+         align_up(sizeof(float) * 2 * rows * nseg * d.n_heads, 256);
+}
+
+hipError_t launch_sparse_layers(const hs2_attn_desc& d, int n_layers, const void* q_layers,
+                                const void* k, const void* v, int64_t kv_stride,
+                                const int32_t* ctx_len, int cap, const int32_t* top_idx,
+                                const int32_t* top_cnt, float* o_layers, float* lse_layers,
+                                char* ws, hipStream_t st) {
+  const int sel_max = d.k_top + d.window;
+  const int nseg = sel_max > 0 ? (sel_max + kSegB - 1) / kSegB : 1;
+  const size_t rows = (size_t)n_layers * d.batch;
+  float* part = reinterpret_cast<float*>(ws);
+  float2* ml = reinterpret_cast<float2*>(
+      ws + align_up(sizeof(float) * rows * nseg * d.n_heads * kHeadDim, 256));
+  sparse_layers_bf16<<<dim3(nseg, d.batch), 64 * kSegWaves, 0, st>>>(
+      static_cast<const uint16_t*>(q_layers), static_cast<const uint16_t*>(k),
+      static_cast<const uint16_t*>(v), kv_stride, ctx_len, cap, top_idx, top_cnt, d.batch,
+      d.k_top, d.window, d.n_heads, d.sm_scale * kLog2e, n_layers, part, ml, nseg);
+  sparse_combine<<<dim3(d.n_heads, (int)rows), kHeadDim, 0, st>>>(part, ml, nseg, d.n_heads,
+                                                                 o_layers, lse_layers);
   return hipGetLastError();
 }
 

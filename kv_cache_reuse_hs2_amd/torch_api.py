@@ -13,7 +13,8 @@ import torch
 
 from . import (HS2_BF16, HS2_F32, hs2_attn_desc, hs2_bridge_pack_weights,
                hs2_bridge_packed_bytes, hs2_decode_step, hs2_full_attn_scores,
-               hs2_select_topk_window, hs2_sparse_attn_gather, hs2_workspace_size, make_desc)
+               hs2_select_topk_window, hs2_sparse_attn_gather, hs2_sparse_attn_gather_layers,
+               hs2_sparse_layers_workspace_size, hs2_workspace_size, make_desc)
 
 
 def to_device(arr: np.ndarray, device="cuda") -> torch.Tensor:
@@ -119,3 +120,19 @@ def pack_bridge_weights(w_k: torch.Tensor, w_v: torch.Tensor, d_model: int,
     w_packed = torch.empty(n // 2, dtype=torch.int16, device=w_k.device)
     hs2_bridge_pack_weights(w_k, w_v, d_model, w_packed, stream=stream)
     return w_packed
+
+
+def run_sparse_layers(buf: DecodeBuffers, q_layers: torch.Tensor, stream=None):
+    """The sparse layers that share buf's selection: q_layers [L][B][1][H][D]
+    (bf16 bits); returns (o_layers [L][B][1][H][D], lse_layers [L][B][1][H])."""
+    n_layers = q_layers.shape[0]
+    nbytes = hs2_sparse_layers_workspace_size(buf.desc, n_layers)
+    if nbytes == 0:
+        raise ValueError("descriptor rejected by hs2_sparse_layers_workspace_size")
+    ws = torch.empty(nbytes, dtype=torch.uint8, device=buf.k.device)
+    o = torch.empty((n_layers,) + tuple(buf.o.shape), dtype=torch.float32, device=buf.k.device)
+    lse = torch.empty((n_layers,) + tuple(buf.lse.shape), dtype=torch.float32, device=buf.k.device)
+    hs2_sparse_attn_gather_layers(buf.desc, n_layers, q_layers, buf.k, buf.v, buf.kv_stride,
+                                  buf.ctx_len, buf.cap, buf.top_idx, buf.top_cnt, o, lse, ws,
+                                  stream)
+    return o, lse

@@ -207,3 +207,28 @@ def test_binding_raises_on_error_status(lib):
     with pytest.raises(hs2.HS2Error) as ei:
         hs2.hs2_bridge_kv(None, 2048, FAKE, FAKE, FAKE, FAKE, 128, 1024, 2048, stream=0)
     assert ei.value.status == hs2.HS2_EINVAL
+
+
+def test_sparse_layers_validation(lib):
+    L = hs2.load()
+    d = hs2.make_desc(batch=2, n_heads=32, k_top=1024, window=128)
+    need = hs2.hs2_sparse_layers_workspace_size(d, 4)
+    assert need > 0
+    assert hs2.hs2_sparse_layers_workspace_size(d, 0) == 0
+    assert hs2.hs2_sparse_layers_workspace_size(d, 65) == 0
+
+    def call(desc=d, nl=4, q=FAKE, o=FAKE, ws=FAKE, nb=need, cap=4096, st=4096 * 128):
+        return L.hs2_sparse_attn_gather_layers(ctypes.byref(desc), nl, q, FAKE, FAKE, st, FAKE,
+                                               cap, FAKE, FAKE, o, None, ws, nb, None)
+
+    assert call(q=None) == hs2.HS2_EINVAL
+    assert call(o=None) == hs2.HS2_EINVAL
+    assert call(nl=0) == hs2.HS2_EINVAL
+    assert call(nl=65) == hs2.HS2_EUNSUPPORTED
+    assert call(desc=hs2.make_desc(batch=2, n_heads=32, k_top=1024, window=128,
+                                   dtype=hs2.HS2_F32)) == hs2.HS2_EUNSUPPORTED
+    assert call(desc=hs2.make_desc(batch=1, n_heads=32, n_q=64, tile_q=64, k_top=1024,
+                                   window=128)) == hs2.HS2_EUNSUPPORTED
+    assert call(q=ODD) == hs2.HS2_EALIGN
+    assert call(nb=need - 1) == hs2.HS2_EWORKSPACE
+    assert call(ws=None) == hs2.HS2_EINVAL
