@@ -12,6 +12,8 @@ from .hs2_oracle import (  # noqa: F401
     bf16_round,
     bridge_kv,
     dense_attention,
+    dequant_kv,
+    fp8_e4m3_value,
     full_attn_scores,
     query_positions,
     pool_end,

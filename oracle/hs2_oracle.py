@@ -68,6 +68,8 @@ __all__ = [
     "sparse_attention",
     "dense_attention",
     "bf16_round",
+    "fp8_e4m3_value",
+    "dequant_kv",
     "bridge_kv",
 ]
 
@@ -284,6 +286,32 @@ def bf16_round(x) -> np.ndarray:
     rounded = np.ldexp(np.round(scaled), expo - 8)   # np.round: ties to even
     big = np.abs(rounded) > 3.3895313892515355e38    # largest finite bfloat16
     return np.where(big, np.copysign(np.inf, x), rounded)
+
+
+def fp8_e4m3_value(codes) -> np.ndarray:
+    """Exact values (float64) of FP8 E4M3 bytes, the KV-cache format the
+    pages' cost figures assume ([Origins] "Results": prefill cost with an FP8
+    KV cache; [Wire] "How to interpret the results": the FP8 cache sizes).
+
+    The pages do not spell the encoding out; this is the OCP E4M3 layout: a
+    sign bit, 4 exponent bits with bias 7 and 3 mantissa bits.  Exponent 0
+    holds the subnormals m/8 * 2**-6; S.1111.111 is NaN and there are no
+    infinities, so the largest finite value is 1.75 * 2**8 = 448.
+    """
+    c = np.asarray(codes, dtype=np.uint8).astype(np.int64)
+    sign = c >> 7
+    expo = (c >> 3) & 15
+    mant = c & 7
+    mag = np.where(expo == 0, np.ldexp(mant / 8.0, -6), np.ldexp(1.0 + mant / 8.0, expo - 7))
+    val = np.where(sign == 1, -mag, mag)
+    return np.where((expo == 15) & (mant == 7), np.nan, val)
+
+
+def dequant_kv(codes, scale) -> np.ndarray:
+    """Values of an FP8 K or V cache with one scale per cache: scale * e4m3(x).
+    (The pages give no scaling convention; one fp32 scale per cache is the
+    reading taken.)"""
+    return fp8_e4m3_value(codes) * float(scale)
 
 
 def bridge_kv(h, w_k, w_v, *, row_chunk: int = 8192):

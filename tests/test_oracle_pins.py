@@ -385,3 +385,46 @@ def test_bridge_rounds_the_fp64_product_once():
     assert np.all(np.abs(k - exact_k) <= ulp / 2)
     assert np.array_equal(oracle.bf16_round(k), k)
     assert v.shape == (100, 16)
+
+
+# --- FP8 E4M3 KV cache (the format of the pages' cost figures) ----------------
+
+def test_e4m3_known_codes():
+    # Code points of the OCP E4M3 encoding: zero, the subnormal range, the
+    # smallest normal, 1, 1.5, 2, the largest finite value, NaN.
+    v = oracle.fp8_e4m3_value(np.arange(256, dtype=np.uint8))
+    assert v[0x00] == 0.0 and np.signbit(v[0x80]) and v[0x80] == 0.0
+    assert v[0x01] == 2.0 ** -9 and v[0x07] == 7 * 2.0 ** -9
+    assert v[0x08] == 2.0 ** -6
+    assert v[0x38] == 1.0 and v[0x3C] == 1.5 and v[0x40] == 2.0
+    assert v[0x7E] == 448.0 and v[0xFE] == -448.0
+    assert np.isnan(v[0x7F]) and np.isnan(v[0xFF])
+    assert np.sum(np.isnan(v)) == 2
+
+
+def test_e4m3_is_ordered_and_symmetric():
+    v = oracle.fp8_e4m3_value(np.arange(256, dtype=np.uint8))
+    pos = v[:0x7F]
+    assert np.all(np.diff(pos) > 0)                 # codes 0x00..0x7E ascend
+    assert np.array_equal(v[0x80:0xFF], -pos)       # sign bit mirrors
+    # Steps between neighbouring codes: 2**-9 through the subnormals and the
+    # first binade, then doubling every 8 codes (3 mantissa bits).
+    for c in range(0x7E):
+        e = max(c >> 3, 1)
+        assert pos[c + 1] - pos[c] == 2.0 ** (e - 10), hex(c)
+
+
+def test_e4m3_matches_torch_float8():
+    torch = pytest.importorskip("torch")
+    codes = np.arange(256, dtype=np.uint8)
+    ref = torch.from_numpy(codes).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    got = oracle.fp8_e4m3_value(codes)
+    fin = ~np.isnan(ref)
+    assert np.array_equal(np.isnan(got), ~fin)
+    assert np.array_equal(got[fin], ref[fin])
+
+
+def test_dequant_kv_scales_every_code():
+    codes = np.arange(0, 0x7F, dtype=np.uint8).reshape(1, -1)
+    got = oracle.dequant_kv(codes, np.float32(0.0103))
+    assert np.array_equal(got, oracle.fp8_e4m3_value(codes) * float(np.float32(0.0103)))

@@ -22,7 +22,8 @@ class Workload:
     tile_q: int          # queries per selection group (1 for decode)
     k_top: int
     window: int
-    dtype: str           # "f32" | "bf16": storage type of q, k, v
+    dtype: str           # "f32" | "bf16" | "fp8": storage type of q, k, v (fp8: k, v
+                         # in E4M3 with one scale per cache, q in bf16)
     seed: int
     recipe: str          # "needles" | "clusters" | "plain" | "bridge"
     n_needles: int = 0
@@ -56,6 +57,10 @@ WORKLOADS = {
         "decode_bf16_256k_b4", "decode", batch=4, n_heads=32, head_dim=128,
         ctx_len=262144, n_q=1, tile_q=1, k_top=1024, window=128, dtype="bf16",
         seed=1004, recipe="clusters"),
+    "decode_fp8_256k_b4": Workload(
+        "decode_fp8_256k_b4", "decode", batch=4, n_heads=32, head_dim=128,
+        ctx_len=262144, n_q=1, tile_q=1, k_top=1024, window=128, dtype="fp8",
+        seed=1006, recipe="clusters"),
     "bridge_decode_bf16_1m": Workload(
         "bridge_decode_bf16_1m", "bridge_decode", batch=1, n_heads=32,
         head_dim=128, ctx_len=1048576, n_q=1, tile_q=1, k_top=1024, window=128,
@@ -86,6 +91,19 @@ def _store(x: np.ndarray, dtype: str):
         return x, x
     bits = bf16_bits(x)
     return bf16_bits_to_f32(bits), bits
+
+
+def e4m3_codes(x: np.ndarray) -> tuple[np.ndarray, np.float32]:
+    """Quantise an fp32 array to FP8 E4M3 bytes with one scale: the scale maps
+    the largest magnitude to 448 (the largest finite E4M3 value) and the
+    scaled values are rounded to nearest, ties to even, by torch's float8
+    conversion.  Returns (codes uint8, scale float32)."""
+    import torch
+
+    amax = float(np.max(np.abs(x)))
+    scale = np.float32(amax / 448.0 if amax > 0 else 1.0)
+    t = torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32) / scale)
+    return t.to(torch.float8_e4m3fn).view(torch.uint8).numpy(), scale
 
 
 def _unit(x: np.ndarray) -> np.ndarray:
@@ -126,7 +144,7 @@ def make_decode_inputs(w: Workload, *, seed: int | None = None,
     q = rng.standard_normal((bsz, w.n_q, n_heads, head_dim), dtype=np.float32) * np.float32(scale)
     k = rng.standard_normal((bsz, cap, head_dim), dtype=np.float32) * np.float32(scale)
     v = rng.standard_normal((bsz, cap, head_dim), dtype=np.float32) * np.float32(scale)
-    q_val, q_raw = _store(q, w.dtype)
+    q_val, q_raw = _store(q, "bf16" if w.dtype == "fp8" else w.dtype)
 
     planted = []
     for b in range(bsz):
@@ -155,6 +173,14 @@ def make_decode_inputs(w: Workload, *, seed: int | None = None,
         else:
             planted.append(np.zeros(0, dtype=np.int64))
 
+    if w.dtype == "fp8":
+        # K and V as E4M3 bytes with one scale each; their values are left to
+        # the consumer (the oracle decodes the bytes itself).
+        k_raw, k_scale = e4m3_codes(k)
+        v_raw, v_scale = e4m3_codes(v)
+        return dict(q=q_val, k=None, v=None, q_raw=q_raw, k_raw=k_raw, v_raw=v_raw,
+                    k_scale=k_scale, v_scale=v_scale, ctx_len=ctx_len, planted=planted,
+                    capacity=cap)
     k_val, k_raw = _store(k, w.dtype)
     v_val, v_raw = _store(v, w.dtype)
     return dict(q=q_val, k=k_val, v=v_val, q_raw=q_raw, k_raw=k_raw,
