@@ -35,7 +35,8 @@
  * - Shapes: B = batch, Q = n_q new queries per sequence, H = query heads,
  *   D = head_dim = 128, one shared K/V head (MQA, [Summary] "Inference
  *   cost"; [Wire] "How to interpret the results").  Layouts are row-major:
- *     q        [B][Q][H][D]      dtype of the descriptor
+ *     q        [B][Q][H][D]      dtype of the descriptor (bf16 for
+ *                                HS2_FP8_E4M3)
  *     k, v     [B][cap][D]       dtype of the descriptor; sequence stride
  *                                kv_stride ELEMENTS (>= cap*D), row stride D
  *     ctx_len  int32 [B]         device array: keys held by each sequence,
@@ -46,7 +47,9 @@
  *     o        f32 [B][Q][H][D],  lse f32 [B][Q][H] (natural log)
  * - Query i of sequence b sits at position P = ctx_len[b] - Q + i; it sees
  *   keys 0..P (causal).  Queries at negative positions output 0 / -inf.
- * - Inputs must be finite.  bf16 values are raw bfloat16 bit patterns.
+ * - Inputs must be finite.  bf16 values are raw bfloat16 bit patterns; fp8
+ *   values are raw OCP FP8 E4M3 bytes (1 sign, 4 exponent bits with bias 7,
+ *   3 mantissa bits, subnormals, no infinities; 0x7F/0xFF are NaN).
  * - Calls are reentrant.  A workspace may be shared by calls issued in order
  *   on one stream, never by calls that can run concurrently.
  * - kv_capacity is at most 4,194,304 keys (HS2_EUNSUPPORTED beyond).
@@ -78,7 +81,17 @@ typedef enum {
   HS2_EHIP = 5          /* the HIP runtime reported an error at enqueue */
 } hs2_status;
 
-typedef enum { HS2_F32 = 0, HS2_BF16 = 1 } hs2_dtype;
+/*
+ * Storage types.  HS2_FP8_E4M3 is the FP8 KV cache that the pages' cost
+ * figures assume ([Origins] "Results", prefill cost "(FP8 KV cache)"; [Wire]
+ * "How to interpret the results"), whose scaling the pages do not give: here
+ * K and V are E4M3 bytes with one fp32 scale per cache (desc->k_scale,
+ * desc->v_scale; the value of a byte x is scale * e4m3(x)), q stays bf16
+ * and the arithmetic is that of the bf16 path (every E4M3 value is exact in
+ * bf16).  Decode only (n_q = tile_q = 1; HS2_EUNSUPPORTED otherwise);
+ * kv_stride must be a multiple of 16 (HS2_EALIGN otherwise).
+ */
+typedef enum { HS2_F32 = 0, HS2_BF16 = 1, HS2_FP8_E4M3 = 2 } hs2_dtype;
 
 /* Attention problem shared by the scoring, selection and sparse calls. */
 typedef struct {
@@ -92,6 +105,8 @@ typedef struct {
   int causal;     /* must be 1 */
   float sm_scale; /* softmax scale, normally 1/sqrt(head_dim) */
   hs2_dtype dtype;/* storage type of q, k and v */
+  float k_scale;  /* HS2_FP8_E4M3: scale of the K cache (finite, > 0); else ignored */
+  float v_scale;  /* HS2_FP8_E4M3: scale of the V cache (finite, > 0); else ignored */
 } hs2_attn_desc;
 
 /* Bytes of device workspace the three attention calls need for this problem
@@ -159,8 +174,8 @@ HS2_API hs2_status hs2_sparse_attn_gather(const hs2_attn_desc* desc, const void*
  * ([Origins] "The Self-Decoder and Cross-Decoder Split", on HySparse's KV
  * Reuse), so n_layers sparse layers attend over the same rows with their own
  * queries.  This call gathers every selected K/V row once for all of them.
- * Decode only (n_q = tile_q = 1) and bf16 only in this build
- * (HS2_EUNSUPPORTED otherwise); 1 <= n_layers <= 64.  q_layers is bf16
+ * Decode only (n_q = tile_q = 1), bf16 or E4M3 caches (HS2_EUNSUPPORTED
+ * otherwise); 1 <= n_layers <= 64.  q_layers is bf16
  * [n_layers][B][H][D], o_layers fp32 [n_layers][B][H][D], lse_layers
  * (nullable) fp32 [n_layers][B][H].  The results are those of n_layers calls
  * of hs2_sparse_attn_gather, bit for bit.  The workspace (16-byte aligned)
@@ -181,7 +196,7 @@ HS2_API hs2_status hs2_sparse_attn_gather_layers(const hs2_attn_desc* desc, int 
  * hs2_select_topk_window) and the sparse layer (as hs2_sparse_attn_gather,
  * with q_sparse, or q when q_sparse is NULL).  The outputs are exactly those
  * of the three calls issued in order with the same workspace; on the bf16
- * path the scoring pass also builds the selector's first histogram, which
+ * and E4M3 paths the scoring pass also builds the selector's first histogram, which
  * saves the selector one pass over the scores.  lse_full (the full layer's
  * log-sum-exp) and lse (the sparse layer's) may be NULL.
  */

@@ -21,6 +21,7 @@ LIB_PATH = os.path.join(_PKG, "libhs2.so")
 
 HS2_F32 = 0
 HS2_BF16 = 1
+HS2_FP8_E4M3 = 2
 HS2_OK, HS2_EINVAL, HS2_EUNSUPPORTED, HS2_EALIGN, HS2_EWORKSPACE, HS2_EHIP = range(6)
 
 EXPORTS = (
@@ -53,6 +54,8 @@ class hs2_attn_desc(ctypes.Structure):
         ("causal", ctypes.c_int),
         ("sm_scale", ctypes.c_float),
         ("dtype", ctypes.c_int),
+        ("k_scale", ctypes.c_float),
+        ("v_scale", ctypes.c_float),
     ]
 
 
@@ -111,11 +114,12 @@ def load(path: str | None = None):
 
 
 def make_desc(*, batch, n_heads, n_q=1, tile_q=1, k_top=1024, window=128, sm_scale=None,
-              dtype=HS2_BF16, head_dim=128, causal=1) -> hs2_attn_desc:
+              dtype=HS2_BF16, head_dim=128, causal=1, k_scale=1.0,
+              v_scale=1.0) -> hs2_attn_desc:
     if sm_scale is None:
         sm_scale = head_dim ** -0.5
     return hs2_attn_desc(batch, n_q, n_heads, head_dim, tile_q, k_top, window, causal,
-                         float(sm_scale), int(dtype))
+                         float(sm_scale), int(dtype), float(k_scale), float(v_scale))
 
 
 def _ptr(x) -> int | None:

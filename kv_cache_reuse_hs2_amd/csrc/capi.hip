@@ -27,7 +27,10 @@ hs2_status check_desc(const hs2_attn_desc* d) {
   if (d->k_top < 0 || d->window < 0) return HS2_EINVAL;
   if (d->n_q % d->tile_q != 0) return HS2_EINVAL;
   if (!(d->sm_scale > 0.f) || !isfinite(d->sm_scale)) return HS2_EINVAL;
-  if (d->dtype != HS2_F32 && d->dtype != HS2_BF16) return HS2_EINVAL;
+  if (d->dtype != HS2_F32 && d->dtype != HS2_BF16 && d->dtype != HS2_FP8_E4M3) return HS2_EINVAL;
+  if (d->dtype == HS2_FP8_E4M3 && (!(d->k_scale > 0.f) || !isfinite(d->k_scale) ||
+                                   !(d->v_scale > 0.f) || !isfinite(d->v_scale)))
+    return HS2_EINVAL;
   if (d->head_dim != kHeadDim || d->n_heads > kMaxHeads) return HS2_EUNSUPPORTED;
   if (d->k_top > kMaxTop || d->window > kMaxWindow) return HS2_EUNSUPPORTED;
   if (d->causal != 1) return HS2_EUNSUPPORTED;
@@ -43,7 +46,8 @@ hs2_status check_cache(const hs2_attn_desc* d, int64_t kv_stride, int cap) {
   if (cap < 1) return HS2_EINVAL;
   if (cap > kMaxSelectCap) return HS2_EUNSUPPORTED;
   if (kv_stride < (int64_t)cap * kHeadDim) return HS2_EINVAL;
-  if (kv_stride % 8 != 0) return HS2_EALIGN;  // keeps every row 16-byte aligned
+  // Keeps every row 16-byte aligned (8 bf16 or 16 fp8 elements).
+  if (kv_stride % (d->dtype == HS2_FP8_E4M3 ? 16 : 8) != 0) return HS2_EALIGN;
   (void)d;
   return HS2_OK;
 }
@@ -174,7 +178,7 @@ hs2_status hs2_sparse_attn_gather_layers(const hs2_attn_desc* desc, int n_layers
     return HS2_EINVAL;
   if (top_idx == nullptr && desc->k_top > 0) return HS2_EINVAL;
   if (n_layers < 1) return HS2_EINVAL;
-  if (n_layers > kMaxLayers || is_prefill(*desc) || desc->dtype != HS2_BF16)
+  if (n_layers > kMaxLayers || is_prefill(*desc) || desc->dtype == HS2_F32)
     return HS2_EUNSUPPORTED;
   if ((s = check_cache(desc, kv_stride, kv_capacity)) != HS2_OK) return s;
   if (misaligned(q_layers) || misaligned(k) || misaligned(v) || misaligned(ctx_len) ||
@@ -211,8 +215,8 @@ hs2_status hs2_decode_step(const hs2_attn_desc* desc, const void* q, const void*
   const WsLayout l = ws_layout(*desc, kv_capacity);
   char* w = static_cast<char*>(ws);
   hipStream_t st = static_cast<hipStream_t>(stream);
-  // bf16: the scoring pass also builds the selector's histogram.
-  const bool fuse = desc->dtype == HS2_BF16;
+  // bf16 and E4M3: the scoring pass also builds the selector's histogram.
+  const bool fuse = desc->dtype != HS2_F32;
   const bool pf = is_prefill(*desc);
   hipError_t e =
       pf ? launch_prefill_scores(*desc, q, k, kv_stride, ctx_len, kv_capacity, scores, lse_full,
@@ -223,7 +227,7 @@ hs2_status hs2_decode_step(const hs2_attn_desc* desc, const void* q, const void*
   const size_t hist_off = pf ? prefill_ws(*desc, kv_capacity).hist_off
                              : score_ws(*desc, kv_capacity).hist_off;
   uint32_t* hist = fuse ? reinterpret_cast<uint32_t*>(w + l.score + hist_off) : nullptr;
-  // bf16 decode: the final selection runs inside the sparse layer's kernel.
+  // MFMA decode: the final selection runs inside the sparse layer's kernel.
   const bool tail = fuse && !pf;
   e = launch_select(*desc, scores, ctx_len, kv_capacity, top_idx, top_cnt, w + l.select, hist,
                     !tail, st);

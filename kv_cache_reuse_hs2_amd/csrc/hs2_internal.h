@@ -61,6 +61,39 @@ __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_ex
 
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+
+// Bytes per stored K/V element: E4M3 caches hold one byte per element, the
+// bf16 kernels two.
+template <bool kFp8>
+constexpr int kv_elem_bytes() {
+  return kFp8 ? 1 : 2;
+}
+
+// Eight OCP E4M3 bytes (two little-endian words, lowest byte first) as eight
+// bf16 values in the same order.  Every E4M3 value, subnormals included, is
+// exact in bf16 (3 mantissa bits, exponents 2^-9 .. 2^8), so nothing rounds.
+__device__ __forceinline__ u32x4 e4m3x8_to_bf16x8(uint32_t w0, uint32_t w1) {
+  u32x4 r;
+  r[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, 1.0f, false));
+  r[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, 1.0f, true));
+  r[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, 1.0f, false));
+  r[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, 1.0f, true));
+  return r;
+}
+
+// Head dimensions that lane half hh (lane / 32) feeds to step e (0..7) of a
+// 128-deep contraction on v_mfma_f32_32x32x16_bf16: eight consecutive dims
+// starting at the returned one.  A dot product does not depend on the order
+// of its terms, so both operands only have to agree.  bf16 rows are read as
+// sixteen 16-byte pieces, piece 2e + hh feeding step e; E4M3 rows (128 bytes)
+// as eight 16-byte pieces, piece 2i + hh (dims 32i + 16hh .. +16) feeding
+// steps 2i and 2i + 1.  Either way the two lane halves read neighbouring
+// pieces of a row in the same load instruction.
+template <bool kFp8>
+__device__ __forceinline__ int step_dim(int e, int hh) {
+  return kFp8 ? 32 * (e >> 1) + 16 * hh + 8 * (e & 1) : 16 * e + 8 * hh;
+}
 
 // ---------------------------------------------------------------------------
 // Workspace layout.  The three calls use disjoint regions (scoring, selection,
@@ -69,7 +102,7 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
-inline int score_chunk1(hs2_dtype dt) { return dt == HS2_BF16 ? kP1Chunk : kF32Chunk; }
+inline int score_chunk1(hs2_dtype dt) { return dt == HS2_F32 ? kF32Chunk : kP1Chunk; }
 inline int score_nchunks1(const hs2_attn_desc& d, int cap) {
   const int c = score_chunk1(d.dtype);
   return (cap + c - 1) / c;

@@ -29,6 +29,11 @@
 // operand so that a lane holds one key over 16 heads (the head sum is
 // in-lane plus one cross-half add).
 //
+// E4M3 path: the same kernels read 64 B of a key row per lane and widen the
+// bytes to bf16 in registers (exact), so the MFMA work is unchanged and the
+// HBM stream halves.  The cache scale multiplies the logit scale:
+// sm_scale * q.(s k) = (sm_scale * s) * q.k.
+//
 // fp32 path: a VALU dot-product kernel, one key per thread, with a separate
 // reduction kernel.
 #include "hs2_internal.h"
@@ -52,27 +57,51 @@ __device__ __forceinline__ void merge_ml(float& m, float& l, float m2, float l2)
   m = mn;
 }
 
+// Registers of raw K per lane and 32-key block: 128 B of a bf16 row, 64 B of
+// an E4M3 row.
+template <bool kFp8>
+constexpr int k_regs() {
+  return kFp8 ? 4 : 8;
+}
+
+// Query rows as the MFMA operand of steps 0..7 (dims as step_dim gives).
+template <bool kFp8>
 __device__ __forceinline__ void load_q_bf16(const uint16_t* qb, int H, int r32, int hh,
                                             bf16x8_t (&qreg)[8]) {
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
     u32x4 v = {0u, 0u, 0u, 0u};
-    if (r32 < H) v = *reinterpret_cast<const u32x4*>(qb + r32 * kHeadDim + 16 * i + 8 * hh);
+    if (r32 < H) v = *reinterpret_cast<const u32x4*>(qb + r32 * kHeadDim + step_dim<kFp8>(i, hh));
     qreg[i] = as_bf16x8(v);
   }
 }
 
-__device__ __forceinline__ void load_k_block(const uint16_t* kb, int row, int hh, u32x4 (&kr)[8]) {
-  const u32x4* kp = reinterpret_cast<const u32x4*>(kb + (size_t)row * kHeadDim + 8 * hh);
+// Lane half hh's share of key row `row` (kb: the sequence's cache, bytes):
+// 16-byte pieces 2i + hh of the row.
+template <bool kFp8>
+__device__ __forceinline__ void load_k_block(const char* kb, int row, int hh,
+                                             u32x4 (&kr)[k_regs<kFp8>()]) {
+  const u32x4* kp =
+      reinterpret_cast<const u32x4*>(kb + (size_t)row * kHeadDim * kv_elem_bytes<kFp8>()) + hh;
 #pragma unroll
-  for (int i = 0; i < 8; ++i) kr[i] = kp[2 * i];
+  for (int i = 0; i < k_regs<kFp8>(); ++i) kr[i] = kp[2 * i];
 }
 
-// Pass 1, bf16: per (sequence, chunk, head) base-2 (max, sum).  Chunks at or
-// beyond the context write neutral statistics.  The workgroup of chunk 0 also
-// clears the sequence's selector histogram when one is built.
+// The K operand of MFMA step e (compile-time after unrolling).
+template <bool kFp8>
+__device__ __forceinline__ bf16x8_t k_operand(const u32x4 (&kr)[k_regs<kFp8>()], int e) {
+  if constexpr (kFp8)
+    return as_bf16x8(e4m3x8_to_bf16x8(kr[e >> 1][2 * (e & 1)], kr[e >> 1][2 * (e & 1) + 1]));
+  else
+    return as_bf16x8(kr[e]);
+}
+
+// Pass 1, bf16 or E4M3 K: per (sequence, chunk, head) base-2 (max, sum).
+// Chunks at or beyond the context write neutral statistics.  The workgroup of
+// chunk 0 also clears the sequence's selector histogram when one is built.
+template <bool kFp8>
 __global__ __launch_bounds__(64 * kP1Waves) void score_p1_bf16(
-    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, int64_t kv_stride,
+    const uint16_t* __restrict__ q, const void* __restrict__ k, int64_t kv_stride,
     const int32_t* __restrict__ ctx_len, int cap, int H, float c2, float2* __restrict__ stats,
     int nchunks, uint32_t* __restrict__ hist) {
   const int b = blockIdx.y, c = blockIdx.x;
@@ -90,20 +119,20 @@ __global__ __launch_bounds__(64 * kP1Waves) void score_p1_bf16(
   const int r32 = lane & 31, hh = lane >> 5;
 
   bf16x8_t qreg[8];
-  load_q_bf16(q + (size_t)b * H * kHeadDim, H, r32, hh, qreg);
-  const uint16_t* kb = k + (size_t)b * kv_stride;
+  load_q_bf16<kFp8>(q + (size_t)b * H * kHeadDim, H, r32, hh, qreg);
+  const char* kb = static_cast<const char*>(k) + (size_t)b * kv_stride * kv_elem_bytes<kFp8>();
 
   float m_run = -INFINITY, l_run = 0.f;
   int j0 = j_begin + 32 * wave;
-  u32x4 kr[8], kn[8];
-  if (j0 < j_end) load_k_block(kb, min(j0 + r32, N - 1), hh, kr);
+  u32x4 kr[k_regs<kFp8>()], kn[k_regs<kFp8>()];
+  if (j0 < j_end) load_k_block<kFp8>(kb, min(j0 + r32, N - 1), hh, kr);
   while (j0 < j_end) {
     const int jn = j0 + 32 * kP1Waves;
-    if (jn < j_end) load_k_block(kb, min(jn + r32, N - 1), hh, kn);
+    if (jn < j_end) load_k_block<kFp8>(kb, min(jn + r32, N - 1), hh, kn);
     f32x16_t acc = {};
 #pragma unroll
     for (int i = 0; i < 8; ++i)
-      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(kr[i]), qreg[i], acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k_operand<kFp8>(kr, i), qreg[i], acc, 0, 0, 0);
     // acc[r] = logit of key j0 + 8*(r/4) + 4*hh + r%4 for head r32.
     float x[16];
     float bm = -INFINITY;
@@ -121,7 +150,7 @@ __global__ __launch_bounds__(64 * kP1Waves) void score_p1_bf16(
     l_run = s;
     m_run = m_new;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) kr[i] = kn[i];
+    for (int i = 0; i < k_regs<kFp8>(); ++i) kr[i] = kn[i];
     j0 = jn;
   }
   // Lanes r32 and r32+32 hold the same head over different keys.
@@ -137,10 +166,11 @@ __global__ __launch_bounds__(64 * kP1Waves) void score_p1_bf16(
   }
 }
 
-// Pass 2, bf16: fold the statistics into L_h, then I[j] = sum_h 2^(x_hj - L_h).
-template <bool kHist>
+// Pass 2, bf16 or E4M3 K: fold the statistics into L_h, then
+// I[j] = sum_h 2^(x_hj - L_h).
+template <bool kFp8, bool kHist>
 __global__ __launch_bounds__(64 * kP2Waves) void score_p2_bf16(
-    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, int64_t kv_stride,
+    const uint16_t* __restrict__ q, const void* __restrict__ k, int64_t kv_stride,
     const int32_t* __restrict__ ctx_len, int cap, int H, float c2,
     const float2* __restrict__ stats, int nchunks1, float* __restrict__ scores,
     int64_t score_stride, float* __restrict__ lse_out, uint32_t* __restrict__ hist, int window) {
@@ -155,14 +185,14 @@ __global__ __launch_bounds__(64 * kP2Waves) void score_p2_bf16(
   const int j_end = min(N, j_begin + kP2Chunk);
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int r32 = lane & 31, hh = lane >> 5;
-  const uint16_t* kb = k + (size_t)b * kv_stride;
+  const char* kb = static_cast<const char*>(k) + (size_t)b * kv_stride * kv_elem_bytes<kFp8>();
 
   // Start the K stream before folding the statistics.
   int j0 = j_begin + 32 * wave;
-  u32x4 kr[8], kn[8];
-  if (j0 < j_end) load_k_block(kb, min(j0 + r32, N - 1), hh, kr);
+  u32x4 kr[k_regs<kFp8>()], kn[k_regs<kFp8>()];
+  if (j0 < j_end) load_k_block<kFp8>(kb, min(j0 + r32, N - 1), hh, kr);
   bf16x8_t qreg[8];
-  load_q_bf16(q + (size_t)b * H * kHeadDim, H, r32, hh, qreg);
+  load_q_bf16<kFp8>(q + (size_t)b * H * kHeadDim, H, r32, hh, qreg);
 
   constexpr int kParts = kP2Waves * 2;  // 32-thread groups folding the statistics
   __shared__ float2 red[kParts][32];
@@ -200,11 +230,11 @@ __global__ __launch_bounds__(64 * kP2Waves) void score_p2_bf16(
 
   while (j0 < j_end) {
     const int jn = j0 + 32 * kP2Waves;
-    if (jn < j_end) load_k_block(kb, min(jn + r32, N - 1), hh, kn);
+    if (jn < j_end) load_k_block<kFp8>(kb, min(jn + r32, N - 1), hh, kn);
     f32x16_t acc = {};
 #pragma unroll
     for (int i = 0; i < 8; ++i)
-      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qreg[i], as_bf16x8(kr[i]), acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qreg[i], k_operand<kFp8>(kr, i), acc, 0, 0, 0);
     // acc[r] = logit of head 8*(r/4) + 4*hh + r%4 for key j0 + r32.
     float imp = 0.f;
 #pragma unroll
@@ -216,7 +246,7 @@ __global__ __launch_bounds__(64 * kP2Waves) void score_p2_bf16(
       if (kHist && j < pe) atomicAdd(&s_hist[order_key(imp) >> 20], 1u);
     }
 #pragma unroll
-    for (int i = 0; i < 8; ++i) kr[i] = kn[i];
+    for (int i = 0; i < k_regs<kFp8>(); ++i) kr[i] = kn[i];
     j0 = jn;
   }
   if (kHist) {
@@ -332,6 +362,25 @@ __global__ __launch_bounds__(256) void score_reduce_f32(
   }
 }
 
+// Both MFMA passes; hist null: no selector histogram.
+template <bool kFp8>
+void launch_score_mfma(const hs2_attn_desc& d, const void* q, const void* k, int64_t kv_stride,
+                       const int32_t* ctx_len, int cap, float* scores, float* lse, float2* stats,
+                       int nchunks1, float c2, uint32_t* hist, hipStream_t st) {
+  const auto* qq = static_cast<const uint16_t*>(q);
+  score_p1_bf16<kFp8><<<dim3(nchunks1, d.batch), 64 * kP1Waves, 0, st>>>(
+      qq, k, kv_stride, ctx_len, cap, d.n_heads, c2, stats, nchunks1, hist);
+  const dim3 g2((cap + kP2Chunk - 1) / kP2Chunk, d.batch);
+  if (hist != nullptr)
+    score_p2_bf16<kFp8, true><<<g2, 64 * kP2Waves, 0, st>>>(
+        qq, k, kv_stride, ctx_len, cap, d.n_heads, c2, stats, nchunks1, scores, cap, lse, hist,
+        d.window);
+  else
+    score_p2_bf16<kFp8, false><<<g2, 64 * kP2Waves, 0, st>>>(
+        qq, k, kv_stride, ctx_len, cap, d.n_heads, c2, stats, nchunks1, scores, cap, lse, nullptr,
+        d.window);
+}
+
 }  // namespace
 
 hipError_t launch_score_decode(const hs2_attn_desc& d, const void* q, const void* k,
@@ -342,21 +391,14 @@ hipError_t launch_score_decode(const hs2_attn_desc& d, const void* q, const void
   float2* stats = reinterpret_cast<float2*>(ws + w.stats_off);
   const float c2 = d.sm_scale * 1.4426950408889634f;
   const int nchunks1 = score_nchunks1(d, cap);
-  if (d.dtype == HS2_BF16) {
+  if (d.dtype != HS2_F32) {
     uint32_t* hist = with_hist ? reinterpret_cast<uint32_t*>(ws + w.hist_off) : nullptr;
-    const auto* qq = static_cast<const uint16_t*>(q);
-    const auto* kk = static_cast<const uint16_t*>(k);
-    score_p1_bf16<<<dim3(nchunks1, d.batch), 64 * kP1Waves, 0, st>>>(
-        qq, kk, kv_stride, ctx_len, cap, d.n_heads, c2, stats, nchunks1, hist);
-    const dim3 g2((cap + kP2Chunk - 1) / kP2Chunk, d.batch);
-    if (with_hist)
-      score_p2_bf16<true><<<g2, 64 * kP2Waves, 0, st>>>(qq, kk, kv_stride, ctx_len, cap,
-                                                        d.n_heads, c2, stats, nchunks1, scores,
-                                                        cap, lse, hist, d.window);
+    if (d.dtype == HS2_FP8_E4M3)
+      launch_score_mfma<true>(d, q, k, kv_stride, ctx_len, cap, scores, lse, stats, nchunks1,
+                              c2 * d.k_scale, hist, st);
     else
-      score_p2_bf16<false><<<g2, 64 * kP2Waves, 0, st>>>(qq, kk, kv_stride, ctx_len, cap,
-                                                         d.n_heads, c2, stats, nchunks1, scores,
-                                                         cap, lse, nullptr, d.window);
+      launch_score_mfma<false>(d, q, k, kv_stride, ctx_len, cap, scores, lse, stats, nchunks1,
+                               c2, hist, st);
   } else {
     float* lse2 = reinterpret_cast<float*>(ws + w.lse2_off);
     const dim3 grid(nchunks1, d.batch);

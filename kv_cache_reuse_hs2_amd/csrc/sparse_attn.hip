@@ -22,6 +22,9 @@
 // low part so that the sum keeps about fp32 accuracy; V is transposed
 // through LDS into the matching B layout.  The four waves are merged in LDS in
 // a fixed order.
+// E4M3 caches take the same path: the gather widens the bytes to bf16 in
+// registers (exact), the K scale multiplies the logit scale and the V scale
+// the merged output (o is linear in V).
 // fp32: 32-key segments on VALU.
 #include "hs2_internal.h"
 #include "select_core.h"
@@ -81,13 +84,14 @@ struct SegLds {
 };
 
 // Gather of the segment starting at selection position s0 (sequence b):
-// waves 0..kSegWaves-1 load 32 keys each, K rows into kr (the A operand of
-// QK^T: lane = key r32, dims 16e + 8hh) and V rows transposed into L.vt
-// (vt[wave][d][key]).  key_at(p) gives the cache index of selection position
-// p < qg.S.  Called by every thread; other waves do nothing.
-template <typename KeyAt>
-__device__ __forceinline__ void segment_gather_bf16(const uint16_t* __restrict__ k,
-                                                    const uint16_t* __restrict__ v,
+// waves 0..kSegWaves-1 load 32 keys each, K rows into kr as bf16 (the A
+// operand of QK^T: lane = key r32, dims step_dim(e, hh) in step e) and V rows
+// transposed into L.vt (vt[wave][d][key]).  key_at(p) gives the cache index
+// of selection position p < qg.S.  Called by every thread; other waves do
+// nothing.
+template <bool kFp8, typename KeyAt>
+__device__ __forceinline__ void segment_gather_bf16(const void* __restrict__ k,
+                                                    const void* __restrict__ v,
                                                     int64_t kv_stride, int b,
                                                     const QueryGeom& qg, int s0, KeyAt key_at,
                                                     SegLds& L, u32x4 (&kr)[8]) {
@@ -96,14 +100,36 @@ __device__ __forceinline__ void segment_gather_bf16(const uint16_t* __restrict__
   if (wave >= kSegWaves) return;
   const int pw = s0 + 32 * wave;  // first selection position of this wave
   const int idx = key_at((pw + r32 < qg.S) ? pw + r32 : s0);
-  const size_t rowoff = (size_t)b * kv_stride + (size_t)idx * kHeadDim;
-  u32x4 vr[8];
-  const u32x4* kp = reinterpret_cast<const u32x4*>(k + rowoff + 8 * hh);
-  const u32x4* vp = reinterpret_cast<const u32x4*>(v + rowoff + 64 * hh);
+  const size_t rowoff =
+      ((size_t)b * kv_stride + (size_t)idx * kHeadDim) * kv_elem_bytes<kFp8>();
+  const char* krow = static_cast<const char*>(k) + rowoff;
+  const char* vrow = static_cast<const char*>(v) + rowoff;
+  u32x4 vr[8];  // bf16 V of dims 64hh + 8e .. +8
+  if constexpr (kFp8) {
+    // K: pieces 2i + hh (dims 32i + 16hh .. +16); V: dims 64hh + 16i .. +16.
+    const u32x4* kp = reinterpret_cast<const u32x4*>(krow) + hh;
+    const u32x4* vp = reinterpret_cast<const u32x4*>(vrow + 64 * hh);
+    u32x4 kb8[4], vb8[4];
 #pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    kr[e] = kp[2 * e];
-    vr[e] = vp[e];
+    for (int i = 0; i < 4; ++i) {
+      kb8[i] = kp[2 * i];
+      vb8[i] = vp[i];
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      kr[2 * i] = e4m3x8_to_bf16x8(kb8[i][0], kb8[i][1]);
+      kr[2 * i + 1] = e4m3x8_to_bf16x8(kb8[i][2], kb8[i][3]);
+      vr[2 * i] = e4m3x8_to_bf16x8(vb8[i][0], vb8[i][1]);
+      vr[2 * i + 1] = e4m3x8_to_bf16x8(vb8[i][2], vb8[i][3]);
+    }
+  } else {
+    const u32x4* kp = reinterpret_cast<const u32x4*>(krow) + hh;
+    const u32x4* vp = reinterpret_cast<const u32x4*>(vrow + 128 * hh);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      kr[e] = kp[2 * e];
+      vr[e] = vp[e];
+    }
   }
   // V transposed into LDS: vt[wave][d][key], key = r32, d = 64*hh + 8*e + j.
 #pragma unroll
@@ -120,6 +146,7 @@ __device__ __forceinline__ void segment_gather_bf16(const uint16_t* __restrict__
 // every thread of the workgroup, after segment_gather_bf16; its barriers also
 // order the gather's LDS writes before the PV reads.  The LDS statistics and
 // partials are free again when it returns.
+template <bool kFp8>
 __device__ __forceinline__ void segment_query_bf16(const uint16_t* __restrict__ qb, int H,
                                                    float c2, const QueryGeom& qg, int s0,
                                                    const u32x4 (&kr)[8], SegLds& L,
@@ -137,7 +164,8 @@ __device__ __forceinline__ void segment_query_bf16(const uint16_t* __restrict__ 
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       u32x4 xq = {0u, 0u, 0u, 0u};
-      if (r32 < H) xq = *reinterpret_cast<const u32x4*>(qb + r32 * kHeadDim + 16 * e + 8 * hh);
+      if (r32 < H)
+        xq = *reinterpret_cast<const u32x4*>(qb + r32 * kHeadDim + step_dim<kFp8>(e, hh));
       qreg[e] = as_bf16x8(xq);
     }
     f32x16_t acc = {};
@@ -230,20 +258,20 @@ __device__ __forceinline__ void segment_query_bf16(const uint16_t* __restrict__ 
 }
 
 // Gather and partial of one query (one sparse layer).
-template <typename KeyAt>
+template <bool kFp8, typename KeyAt>
 __device__ __forceinline__ void segment_partial_bf16(
-    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
-    const uint16_t* __restrict__ v, int64_t kv_stride, int b, int bq, int H, float c2,
-    const QueryGeom& qg, int s0, KeyAt key_at, SegLds& L, float* __restrict__ po,
-    float2* __restrict__ mlo) {
+    const uint16_t* __restrict__ q, const void* __restrict__ k, const void* __restrict__ v,
+    int64_t kv_stride, int b, int bq, int H, float c2, const QueryGeom& qg, int s0,
+    KeyAt key_at, SegLds& L, float* __restrict__ po, float2* __restrict__ mlo) {
   u32x4 kr[8];
-  segment_gather_bf16(k, v, kv_stride, b, qg, s0, key_at, L, kr);
-  segment_query_bf16(q + (size_t)bq * H * kHeadDim, H, c2, qg, s0, kr, L, po, mlo);
+  segment_gather_bf16<kFp8>(k, v, kv_stride, b, qg, s0, key_at, L, kr);
+  segment_query_bf16<kFp8>(q + (size_t)bq * H * kHeadDim, H, c2, qg, s0, kr, L, po, mlo);
 }
 
+template <bool kFp8>
 __global__ __launch_bounds__(64 * kSegWaves) void sparse_partial_bf16(
-    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
-    const uint16_t* __restrict__ v, int64_t kv_stride, const int32_t* __restrict__ ctx_len,
+    const uint16_t* __restrict__ q, const void* __restrict__ k, const void* __restrict__ v,
+    int64_t kv_stride, const int32_t* __restrict__ ctx_len,
     int cap, const int32_t* __restrict__ top_idx, const int32_t* __restrict__ top_cnt, int n_q,
     int tile_q, int k_top, int window, int H, float c2, float* __restrict__ part,
     float2* __restrict__ ml, int nseg) {
@@ -258,19 +286,20 @@ __global__ __launch_bounds__(64 * kSegWaves) void sparse_partial_bf16(
     return;
   }
   const int32_t* top_row = top_idx + (size_t)(b * tiles + g) * k_top;
-  segment_partial_bf16(q, k, v, kv_stride, b, bq, H, c2, qg, s0,
-                       [&](int p) { return sel_key(qg, top_row, p); }, lds,
+  segment_partial_bf16<kFp8>(q, k, v, kv_stride, b, bq, H, c2, qg, s0,
+                             [&](int p) { return sel_key(qg, top_row, p); }, lds,
                        part + ((size_t)bq * nseg + seg) * H * kHeadDim, mlo);
 }
 
 // ---------------------------------------------------------------------------
-// Several sparse layers after one full layer (bf16 decode): the layers share
+// Several sparse layers after one full layer (decode): the layers share
 // the selection and the K/V cache, so each workgroup gathers its segment once
 // and runs every layer's query over it.  Partials are laid out as if the
 // layers were extra queries (row l*B + b), so sparse_combine merges them.
+template <bool kFp8>
 __global__ __launch_bounds__(64 * kSegWaves) void sparse_layers_bf16(
-    const uint16_t* __restrict__ q_layers, const uint16_t* __restrict__ k,
-    const uint16_t* __restrict__ v, int64_t kv_stride, const int32_t* __restrict__ ctx_len,
+    const uint16_t* __restrict__ q_layers, const void* __restrict__ k,
+    const void* __restrict__ v, int64_t kv_stride, const int32_t* __restrict__ ctx_len,
     int cap, const int32_t* __restrict__ top_idx, const int32_t* __restrict__ top_cnt, int B,
     int k_top, int window, int H, float c2, int n_layers, float* __restrict__ part,
     float2* __restrict__ ml, int nseg) {
@@ -286,11 +315,11 @@ __global__ __launch_bounds__(64 * kSegWaves) void sparse_layers_bf16(
   }
   const int32_t* top_row = top_idx + (size_t)b * k_top;
   u32x4 kr[8];
-  segment_gather_bf16(k, v, kv_stride, b, qg, s0, [&](int p) { return sel_key(qg, top_row, p); },
-                      lds, kr);
+  segment_gather_bf16<kFp8>(k, v, kv_stride, b, qg, s0,
+                            [&](int p) { return sel_key(qg, top_row, p); }, lds, kr);
   for (int l = 0; l < n_layers; ++l) {
     const int row = l * B + b;
-    segment_query_bf16(q_layers + (size_t)row * H * kHeadDim, H, c2, qg, s0, kr, lds,
+    segment_query_bf16<kFp8>(q_layers + (size_t)row * H * kHeadDim, H, c2, qg, s0, kr, lds,
                        part + ((size_t)row * nseg + seg) * H * kHeadDim,
                        ml + ((size_t)row * nseg + seg) * H);
   }
@@ -317,9 +346,10 @@ union TailLds {
   SegLds seg;
 };
 
+template <bool kFp8>
 __global__ __launch_bounds__(kTailThreads) void decode_tail_bf16(
-    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
-    const uint16_t* __restrict__ v, int64_t kv_stride, const int32_t* __restrict__ ctx_len,
+    const uint16_t* __restrict__ q, const void* __restrict__ k, const void* __restrict__ v,
+    int64_t kv_stride, const int32_t* __restrict__ ctx_len,
     int cap, int k_top, int window, int H, float c2, const uint32_t* __restrict__ hist,
     const uint32_t* __restrict__ cnt, const uint32_t* __restrict__ meta,
     const uint2* __restrict__ list, int nslices, int32_t* __restrict__ top_idx,
@@ -353,7 +383,7 @@ __global__ __launch_bounds__(kTailThreads) void decode_tail_bf16(
     const int idx = p < qg.cnt ? win[p] : qg.wlo + (p - qg.cnt);
     return idx < 0 ? 0 : (idx >= qg.N ? qg.N - 1 : idx);
   };
-  segment_partial_bf16(q, k, v, kv_stride, b, b, H, c2, qg, s0, key_at, lds.seg,
+  segment_partial_bf16<kFp8>(q, k, v, kv_stride, b, b, H, c2, qg, s0, key_at, lds.seg,
                        part + ((size_t)b * nseg + seg) * H * kHeadDim, mlo);
 }
 
@@ -461,12 +491,14 @@ __global__ __launch_bounds__(256) void sparse_partial_f32(
 }
 
 // ---------------------------------------------------------------------------
-// Merge the segment partials of one (query, head): o = sum_s 2^(m_s-M) o_s /
-// sum_s 2^(m_s-M) l_s, segments taken in order.  One workgroup per (query,
-// head), one thread per output dimension.
+// Merge the segment partials of one (query, head): o = v_scale * sum_s
+// 2^(m_s-M) o_s / sum_s 2^(m_s-M) l_s, segments taken in order (v_scale is
+// the V cache scale of E4M3 caches, else 1).  One workgroup per (query, head),
+// one thread per output dimension.
 __global__ __launch_bounds__(kHeadDim) void sparse_combine(const float* __restrict__ part,
                                                            const float2* __restrict__ ml, int nseg,
-                                                           int H, float* __restrict__ o,
+                                                           int H, float v_scale,
+                                                           float* __restrict__ o,
                                                            float* __restrict__ lse) {
   const int h = blockIdx.x, bq = blockIdx.y, d = threadIdx.x;
   const float2* mlq = ml + (size_t)bq * nseg * H + h;
@@ -489,9 +521,21 @@ __global__ __launch_bounds__(kHeadDim) void sparse_combine(const float* __restri
     den = fmaf(w, live ? x.y : 0.f, den);
     num = live ? fmaf(w, pv, num) : num;
   }
-  o[((size_t)bq * H + h) * kHeadDim + d] = den > 0.f ? num / den : 0.f;
+  o[((size_t)bq * H + h) * kHeadDim + d] = den > 0.f ? num / den * v_scale : 0.f;
   if (lse != nullptr && d == 0)
     lse[(size_t)bq * H + h] = den > 0.f ? (M + __log2f(den)) * kLn2 : -INFINITY;
+}
+
+// Logit scale in base 2 and output scale of a descriptor (E4M3 caches fold
+// their K scale into the first and V scale into the second).
+float logit_c2(const hs2_attn_desc& d) {
+  return d.sm_scale * kLog2e * (d.dtype == HS2_FP8_E4M3 ? d.k_scale : 1.f);
+}
+float out_scale(const hs2_attn_desc& d) { return d.dtype == HS2_FP8_E4M3 ? d.v_scale : 1.f; }
+
+int mfma_segments(const hs2_attn_desc& d) {
+  const int sel_max = d.k_top + d.window;
+  return sel_max > 0 ? (sel_max + kSegB - 1) / kSegB : 1;
 }
 
 }  // namespace
@@ -503,15 +547,20 @@ hipError_t launch_sparse(const hs2_attn_desc& d, const void* q, const void* k, c
   const SparseWs w = sparse_ws(d);
   float* part = reinterpret_cast<float*>(ws + w.part_off);
   float2* ml = reinterpret_cast<float2*>(ws + w.ml_off);
-  const float c2 = d.sm_scale * kLog2e;
-  const int sel_max = d.k_top + d.window;
+  const float c2 = logit_c2(d);
   int nseg;
-  if (d.dtype == HS2_BF16) {
-    nseg = sel_max > 0 ? (sel_max + kSegB - 1) / kSegB : 1;
-    sparse_partial_bf16<<<dim3(nseg, d.batch * d.n_q), 64 * kSegWaves, 0, st>>>(
-        static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
-        static_cast<const uint16_t*>(v), kv_stride, ctx_len, cap, top_idx, top_cnt, d.n_q,
-        d.tile_q, d.k_top, d.window, d.n_heads, c2, part, ml, nseg);
+  if (d.dtype != HS2_F32) {
+    nseg = mfma_segments(d);
+    const dim3 grid(nseg, d.batch * d.n_q);
+    const auto* qq = static_cast<const uint16_t*>(q);
+    if (d.dtype == HS2_FP8_E4M3)
+      sparse_partial_bf16<true><<<grid, 64 * kSegWaves, 0, st>>>(
+          qq, k, v, kv_stride, ctx_len, cap, top_idx, top_cnt, d.n_q, d.tile_q, d.k_top,
+          d.window, d.n_heads, c2, part, ml, nseg);
+    else
+      sparse_partial_bf16<false><<<grid, 64 * kSegWaves, 0, st>>>(
+          qq, k, v, kv_stride, ctx_len, cap, top_idx, top_cnt, d.n_q, d.tile_q, d.k_top,
+          d.window, d.n_heads, c2, part, ml, nseg);
   } else {
     nseg = sparse_segments(d);
     sparse_partial_f32<<<dim3(nseg, d.batch * d.n_q), 256, 0, st>>>(
@@ -519,8 +568,8 @@ hipError_t launch_sparse(const hs2_attn_desc& d, const void* q, const void* k, c
         kv_stride, ctx_len, cap, top_idx, top_cnt, d.n_q, d.tile_q, d.k_top, d.window,
         d.n_heads, c2, part, ml, nseg);
   }
-  sparse_combine<<<dim3(d.n_heads, d.batch * d.n_q), kHeadDim, 0, st>>>(part, ml, nseg,
-                                                                        d.n_heads, o, lse);
+  sparse_combine<<<dim3(d.n_heads, d.batch * d.n_q), kHeadDim, 0, st>>>(
+      part, ml, nseg, d.n_heads, out_scale(d), o, lse);
   return hipGetLastError();
 }
 
@@ -532,23 +581,27 @@ hipError_t launch_decode_tail(const hs2_attn_desc& d, const void* q, const void*
   const SelectWs sw = select_ws(d, cap);
   float* part = reinterpret_cast<float*>(ws + w.part_off);
   float2* ml = reinterpret_cast<float2*>(ws + w.ml_off);
-  const int sel_max = d.k_top + d.window;
-  const int nseg = sel_max > 0 ? (sel_max + kSegB - 1) / kSegB : 1;
-  decode_tail_bf16<<<dim3(nseg, d.batch), kTailThreads, 0, st>>>(
-      static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
-      static_cast<const uint16_t*>(v), kv_stride, ctx_len, cap, d.k_top, d.window, d.n_heads,
-      d.sm_scale * kLog2e, hist, reinterpret_cast<const uint32_t*>(sel_ws + sw.cnt_off),
-      reinterpret_cast<const uint32_t*>(sel_ws + sw.meta_off),
-      reinterpret_cast<const uint2*>(sel_ws + sw.list_off), select_slices(cap), top_idx, top_cnt,
-      part, ml, nseg);
-  sparse_combine<<<dim3(d.n_heads, d.batch), kHeadDim, 0, st>>>(part, ml, nseg, d.n_heads, o,
-                                                                 lse);
+  const int nseg = mfma_segments(d);
+  const dim3 grid(nseg, d.batch);
+  const auto* qq = static_cast<const uint16_t*>(q);
+  const auto* cnt = reinterpret_cast<const uint32_t*>(sel_ws + sw.cnt_off);
+  const auto* meta = reinterpret_cast<const uint32_t*>(sel_ws + sw.meta_off);
+  const auto* list = reinterpret_cast<const uint2*>(sel_ws + sw.list_off);
+  if (d.dtype == HS2_FP8_E4M3)
+    decode_tail_bf16<true><<<grid, kTailThreads, 0, st>>>(
+        qq, k, v, kv_stride, ctx_len, cap, d.k_top, d.window, d.n_heads, logit_c2(d), hist, cnt,
+        meta, list, select_slices(cap), top_idx, top_cnt, part, ml, nseg);
+  else
+    decode_tail_bf16<false><<<grid, kTailThreads, 0, st>>>(
+        qq, k, v, kv_stride, ctx_len, cap, d.k_top, d.window, d.n_heads, logit_c2(d), hist, cnt,
+        meta, list, select_slices(cap), top_idx, top_cnt, part, ml, nseg);
+  sparse_combine<<<dim3(d.n_heads, d.batch), kHeadDim, 0, st>>>(part, ml, nseg, d.n_heads,
+                                                                 out_scale(d), o, lse);
   return hipGetLastError();
 }
 
 size_t sparse_layers_ws_bytes(const hs2_attn_desc& d, int n_layers) {
-  const int sel_max = d.k_top + d.window;
-  const size_t nseg = sel_max > 0 ? (sel_max + kSegB - 1) / kSegB : 1;
+  const size_t nseg = mfma_segments(d);
   const size_t rows = (size_t)n_layers * d.batch;
   return align_up(sizeof(float) * rows * nseg * d.n_heads * kHeadDim, 256) +
          align_up(sizeof(float) * 2 * rows * nseg * d.n_heads, 256);
@@ -559,18 +612,23 @@ hipError_t launch_sparse_layers(const hs2_attn_desc& d, int n_layers, const void
                                 const int32_t* ctx_len, int cap, const int32_t* top_idx,
                                 const int32_t* top_cnt, float* o_layers, float* lse_layers,
                                 char* ws, hipStream_t st) {
-  const int sel_max = d.k_top + d.window;
-  const int nseg = sel_max > 0 ? (sel_max + kSegB - 1) / kSegB : 1;
+  const int nseg = mfma_segments(d);
   const size_t rows = (size_t)n_layers * d.batch;
   float* part = reinterpret_cast<float*>(ws);
   float2* ml = reinterpret_cast<float2*>(
       ws + align_up(sizeof(float) * rows * nseg * d.n_heads * kHeadDim, 256));
-  sparse_layers_bf16<<<dim3(nseg, d.batch), 64 * kSegWaves, 0, st>>>(
-      static_cast<const uint16_t*>(q_layers), static_cast<const uint16_t*>(k),
-      static_cast<const uint16_t*>(v), kv_stride, ctx_len, cap, top_idx, top_cnt, d.batch,
-      d.k_top, d.window, d.n_heads, d.sm_scale * kLog2e, n_layers, part, ml, nseg);
-  sparse_combine<<<dim3(d.n_heads, (int)rows), kHeadDim, 0, st>>>(part, ml, nseg, d.n_heads,
-                                                                 o_layers, lse_layers);
+  const dim3 grid(nseg, d.batch);
+  const auto* qq = static_cast<const uint16_t*>(q_layers);
+  if (d.dtype == HS2_FP8_E4M3)
+    sparse_layers_bf16<true><<<grid, 64 * kSegWaves, 0, st>>>(
+        qq, k, v, kv_stride, ctx_len, cap, top_idx, top_cnt, d.batch, d.k_top, d.window,
+        d.n_heads, logit_c2(d), n_layers, part, ml, nseg);
+  else
+    sparse_layers_bf16<false><<<grid, 64 * kSegWaves, 0, st>>>(
+        qq, k, v, kv_stride, ctx_len, cap, top_idx, top_cnt, d.batch, d.k_top, d.window,
+        d.n_heads, logit_c2(d), n_layers, part, ml, nseg);
+  sparse_combine<<<dim3(d.n_heads, (int)rows), kHeadDim, 0, st>>>(
+      part, ml, nseg, d.n_heads, out_scale(d), o_layers, lse_layers);
   return hipGetLastError();
 }
 

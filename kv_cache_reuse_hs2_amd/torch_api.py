@@ -11,7 +11,7 @@ import dataclasses
 import numpy as np
 import torch
 
-from . import (HS2_BF16, HS2_F32, hs2_attn_desc, hs2_bridge_pack_weights,
+from . import (HS2_BF16, HS2_F32, HS2_FP8_E4M3, hs2_attn_desc, hs2_bridge_pack_weights,
                hs2_bridge_packed_bytes, hs2_decode_step, hs2_full_attn_scores,
                hs2_select_topk_window, hs2_sparse_attn_gather, hs2_sparse_attn_gather_layers,
                hs2_sparse_layers_workspace_size, hs2_workspace_size, make_desc)
@@ -50,12 +50,18 @@ class DecodeBuffers:
 
 def make_buffers(inp: dict, *, n_heads: int, k_top: int, window: int, sm_scale: float,
                  dtype: str, n_q: int = 1, tile_q: int = 1, device="cuda") -> DecodeBuffers:
-    """Upload generator output (see ``workloads``) and allocate the outputs."""
+    """Upload generator output (see ``workloads``) and allocate the outputs.
+
+    dtype "f32", "bf16" or "fp8" (E4M3 K/V bytes with inp["k_scale"] and
+    inp["v_scale"], bf16 queries)."""
     bsz = inp["ctx_len"].shape[0]
     cap = int(inp["capacity"])
+    code = {"f32": HS2_F32, "bf16": HS2_BF16, "fp8": HS2_FP8_E4M3}[dtype]
+    scales = {}
+    if dtype == "fp8":
+        scales = dict(k_scale=float(inp["k_scale"]), v_scale=float(inp["v_scale"]))
     desc = make_desc(batch=bsz, n_heads=n_heads, n_q=n_q, tile_q=tile_q, k_top=k_top,
-                     window=window, sm_scale=sm_scale,
-                     dtype=HS2_BF16 if dtype == "bf16" else HS2_F32)
+                     window=window, sm_scale=sm_scale, dtype=code, **scales)
     tiles = n_q // tile_q
     nbytes = hs2_workspace_size(desc, cap)
     if nbytes == 0:

@@ -232,3 +232,21 @@ def test_sparse_layers_validation(lib):
     assert call(q=ODD) == hs2.HS2_EALIGN
     assert call(nb=need - 1) == hs2.HS2_EWORKSPACE
     assert call(ws=None) == hs2.HS2_EINVAL
+
+
+def test_fp8_descriptor_validation(lib):
+    fp8 = dict(dtype=hs2.HS2_FP8_E4M3, k_scale=0.01, v_scale=0.02)
+    d = _desc(**fp8)
+    assert hs2.hs2_workspace_size(d, 4096) > 0
+    for bad in (0.0, -1.0, float("inf"), float("nan")):
+        assert _scores(_desc(**dict(fp8, k_scale=bad))) == hs2.HS2_EINVAL
+        assert _scores(_desc(**dict(fp8, v_scale=bad))) == hs2.HS2_EINVAL
+    # scales are ignored for the other storage types
+    assert hs2.hs2_workspace_size(_desc(k_scale=0.0, v_scale=float("nan")), 4096) > 0
+    # decode only
+    assert _scores(_desc(n_q=64, tile_q=64, **fp8)) == hs2.HS2_EUNSUPPORTED
+    assert _scores(_desc(n_q=2, tile_q=1, **fp8)) == hs2.HS2_EUNSUPPORTED
+    # rows of 128 bytes stay 16-byte aligned only with a stride multiple of 16
+    assert _scores(d, stride=4096 * 128 + 8) == hs2.HS2_EALIGN
+    # (bf16 accepts that stride: the call gets as far as the workspace check)
+    assert _scores(_desc(), stride=4096 * 128 + 8, nbytes=0) == hs2.HS2_EWORKSPACE
