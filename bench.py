@@ -34,9 +34,10 @@ MIB = 1 << 20
 
 
 def algorithmic_bytes(w) -> dict:
-    """Bytes a decode step must move at minimum (bf16 K/V rows of 256 B)."""
+    """Bytes a decode step must move at minimum (K/V rows of 256 B in bf16,
+    128 B in E4M3)."""
     n, b = w.ctx_len, w.batch
-    row = w.head_dim * (2 if w.dtype == "bf16" else 4)
+    row = w.head_dim * {"f32": 4, "bf16": 2, "fp8": 1}[w.dtype]
     k_stream = b * n * row                      # every key read once
     scores = b * n * 4                          # importance written once ...
     pool = b * max(0, n - w.window) * 4         # ... and the pool read once by the selector
@@ -135,6 +136,42 @@ def sparse_layer_measurements(steps: int, warmup: int) -> dict:
             "ms_per_step": round(ms, 5), "tokens_per_s": round(w.batch / (ms * 1e-3), 1),
             "ms_per_step_separate_calls": round(ms_sep, 5)}
     return out
+
+
+def fp8_measurements(steps: int, warmup: int) -> dict:
+    """The headline decode step on an FP8 E4M3 K/V cache (same shape, same
+    timing method): the step from HIP graphs and the scoring call alone."""
+    import numpy as np
+    import torch
+
+    from kv_cache_reuse_hs2_amd.torch_api import make_buffers, run_fused_step, run_scores
+    from workloads import WORKLOADS, make_decode_inputs
+
+    w = WORKLOADS["decode_fp8_256k_b4"]
+    buf = make_buffers(make_decode_inputs(w), n_heads=w.n_heads, k_top=w.k_top, window=w.window,
+                       sm_scale=w.sm_scale, dtype=w.dtype)
+    ms = time_graphs(lambda: run_fused_step(buf), steps, warmup)
+    stream = torch.cuda.current_stream()
+    for _ in range(warmup):
+        run_scores(buf)
+    ev = []
+    for _ in range(steps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        run_scores(buf)
+        e1.record(stream)
+        ev.append((e0, e1))
+    torch.cuda.synchronize()
+    ms_sc = float(np.mean([a.elapsed_time(b) for a, b in ev]))
+    ab = algorithmic_bytes(w)
+    sc_gbs = ab["scoring_call"] / (ms_sc * 1e-3) / 1e9
+    return {"ms_per_step": round(ms, 5), "tokens_per_s": round(w.batch / (ms * 1e-3), 1),
+            "step_algorithmic_MiB": round(ab["step"] / MIB, 2),
+            "step_hbm_GBps": round(ab["step"] / (ms * 1e-3) / 1e9, 1),
+            "scoring_call_ms": round(ms_sc, 5),
+            "scoring_call_hbm_GBps": round(sc_gbs, 1),
+            "scoring_call_hbm_frac": round(sc_gbs / HBM_PEAK_GBS, 4),
+            "note": "K and V as E4M3 bytes with one fp32 scale each, bf16 queries"}
 
 
 def extra_measurements(steps: int, warmup: int) -> dict:
@@ -407,13 +444,14 @@ def main() -> int:
             "wall_ms_timed_region": round(wall_ms, 3),
         },
         "roofline": {
-            "kernel": "hs2_full_attn_scores = score_p1_bf16 + score_p2_bf16 (two K streams)",
+            "kernel": "hs2_full_attn_scores = score_p1_bf16<false> + score_p2_bf16<false, false> "
+                      "(two K streams)",
             "bound": "hbm",
             "achieved": round(score_gbs, 1),
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(score_gbs / HBM_PEAK_GBS, 4),
-            "traffic": measured_traffic(["score_p1_bf16", "score_p2_bf16<false>"]),
+            "traffic": measured_traffic(["score_p1_bf16<false>", "score_p2_bf16<false, false>"]),
             "algorithmic_bytes_per_launch": ab["scoring_call"],
         },
     }
@@ -422,6 +460,7 @@ def main() -> int:
         out["extras"] = extra_measurements(args.steps, args.warmup)
         out["extras"]["decode_bf16_256k_b4_shared_selection"] = sparse_layer_measurements(
             args.steps, args.warmup)
+        out["extras"]["decode_fp8_256k_b4"] = fp8_measurements(args.steps, args.warmup)
     if args.calibrate:
         src = torch.empty(256 * MIB, dtype=torch.uint8, device="cuda").fill_(1)
         dst = torch.empty_like(src)
