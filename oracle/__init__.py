@@ -10,6 +10,7 @@ from it.  See ``oracle/hs2_oracle.py`` for the definitions and citations.
 from .hs2_oracle import (  # noqa: F401
     attention_probs,
     bf16_round,
+    block_scores,
     bridge_kv,
     dense_attention,
     dequant_kv,
@@ -17,6 +18,7 @@ from .hs2_oracle import (  # noqa: F401
     full_attn_scores,
     query_positions,
     pool_end,
+    select_topk_blocks,
     select_topk_window,
     selection_set,
     sparse_attention,

@@ -45,6 +45,9 @@ Where the pages are silent the oracle takes these readings:
   even); every other quantity stays fp64.
 * The softmax scale is an explicit argument (1/sqrt(head_dim) in practice);
   no positional encoding is applied to K.
+* HySparse's block-level selection, kept for comparison, ranks aligned
+  blocks of the pool by the fp32 sum of their tokens' importance (pairwise
+  order), ties to the lower block, at the same token budget and window.
 * Query i of a sequence with N cached keys (the new queries' own keys
   included) sits at position N - n_q + i.  A query at a negative position has
   no keys; its output is 0 and its log-sum-exp is -inf.
@@ -64,6 +67,8 @@ __all__ = [
     "attention_probs",
     "full_attn_scores",
     "select_topk_window",
+    "block_scores",
+    "select_topk_blocks",
     "selection_set",
     "sparse_attention",
     "dense_attention",
@@ -201,6 +206,70 @@ def select_topk_window(scores, ctx_len, *, n_q: int, tile_q: int, k_top: int,
             chosen = np.sort(order[: min(k_top, pe)])
             top_idx[b, t, : chosen.size] = chosen
             top_cnt[b, t] = chosen.size
+    return top_idx, top_cnt
+
+
+def block_scores(imp_pool, block: int) -> np.ndarray:
+    """Importance of the aligned blocks of `block` tokens that cover a pool.
+
+    imp_pool: float32 importance of the pool tokens [0, pe).  Block m covers
+    tokens [m*block, (m+1)*block) cut at pe; its importance is the sum of its
+    tokens' importance.  The pages do not say how HySparse ranks its blocks;
+    the summed attention mass is the reading taken, the block analogue of the
+    token importance.  Since the sum then decides which blocks are taken, it
+    is computed in the precision and order of the kernels: fp32 additions in
+    a balanced pairwise tree over the block's `block` slots (slots past the
+    pool hold 0), i.e. level by level, adding slot pairs (0,1), (2,3), ...
+    ``block`` is a power of two.
+    """
+    imp_pool = np.asarray(imp_pool, dtype=np.float32)
+    if block < 1 or block & (block - 1):
+        raise ValueError("block must be a power of two")
+    pe = imp_pool.shape[0]
+    nb = -(-pe // block)
+    x = np.zeros(nb * block, dtype=np.float32)
+    x[:pe] = imp_pool
+    x = x.reshape(nb, block)
+    while x.shape[1] > 1:
+        x = x[:, 0::2] + x[:, 1::2]   # float32 + float32, rounded to nearest even
+    return x[:, 0]
+
+
+def select_topk_blocks(scores, ctx_len, *, n_q: int, tile_q: int, k_top: int, window: int,
+                       block: int):
+    """HySparse's block-level selection, at the same token budget.
+
+    The predecessor design spends the sparse budget on blocks of 64
+    consecutive tokens rather than on single tokens ([Origins] "KV Reuse and
+    Token-Level Sparse Selection"; [Summary] "KV Reuse refinements", the
+    comparison at the same attention budget).  Here: the k_top // block
+    blocks of the pool with the largest ``block_scores`` (ties to the lower
+    block index) are taken, and their pool tokens are reported in ascending
+    order, in the same (top_idx, top_cnt) form as ``select_topk_window``.
+    The pool and the forced window are those of the token-level selector, so
+    the two differ only in granularity.  A block cut by the pool end holds
+    only its pool tokens, so top_cnt can fall below k_top.
+    """
+    if k_top % block:
+        raise ValueError("k_top must be a multiple of block")
+    scores = np.asarray(scores, dtype=np.float32)
+    bsz, n_tiles, _ = scores.shape
+    top_idx = np.full((bsz, n_tiles, k_top), -1, dtype=np.int32)
+    top_cnt = np.zeros((bsz, n_tiles), dtype=np.int32)
+    for b in range(bsz):
+        pos = query_positions(int(ctx_len[b]), n_q)
+        for t in range(n_tiles):
+            pe = pool_end(pos[t * tile_q], window)
+            imp = scores[b, t, :pe]
+            if not np.all(np.isfinite(imp)) or np.any(imp < 0):
+                raise ValueError("importance must be finite and non-negative")
+            bs = block_scores(imp, block)
+            order = np.lexsort((np.arange(bs.size), -bs))   # block score desc, index asc
+            chosen = np.sort(order[: min(k_top // block, bs.size)])
+            toks = [np.arange(m * block, min((m + 1) * block, pe)) for m in chosen]
+            toks = np.concatenate(toks) if toks else np.zeros(0, dtype=np.int64)
+            top_idx[b, t, : toks.size] = toks
+            top_cnt[b, t] = toks.size
     return top_idx, top_cnt
 
 

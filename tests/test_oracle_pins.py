@@ -428,3 +428,98 @@ def test_dequant_kv_scales_every_code():
     codes = np.arange(0, 0x7F, dtype=np.uint8).reshape(1, -1)
     got = oracle.dequant_kv(codes, np.float32(0.0103))
     assert np.array_equal(got, oracle.fp8_e4m3_value(codes) * float(np.float32(0.0103)))
+
+
+# --- Block-level selection (HySparse's 64-token blocks, for comparison) -----
+
+def test_block_scores_exact_sums_and_tree_order():
+    # Sums that fp32 holds exactly come out exact, a cut block counts only its
+    # pool tokens, and the pairwise order is the one stated: with slots
+    # [1, 2^-24, 2^-24, 2^-24] the pairs give 1 + 2^-23, a left-to-right sum 1.
+    x = np.array([1, 2, 3, 4, 5, 6, 7, 8, 9, 10], dtype=np.float32)
+    assert oracle.block_scores(x, 4).tolist() == [10.0, 26.0, 19.0]
+    assert oracle.block_scores(x, 1).tolist() == x.tolist()
+    assert oracle.block_scores(x, 16).tolist() == [55.0]
+    t = np.float32(2.0 ** -24)
+    y = np.array([1.0, t, t, t], dtype=np.float32)
+    assert oracle.block_scores(y, 4)[0] == np.float32(1.0 + 2.0 ** -23)
+    seq = np.float32(0.0)
+    for v in y:
+        seq = np.float32(seq + v)
+    assert seq == np.float32(1.0)
+    # Random values: within the pairwise-sum bound of the exact sum.
+    rng = np.random.default_rng(40)
+    z = rng.random(64 * 50, dtype=np.float32) * np.float32(1e-3)
+    got = oracle.block_scores(z, 64).astype(np.float64)
+    exact = np.array([math.fsum(z[i:i + 64].astype(np.float64)) for i in range(0, z.size, 64)])
+    assert np.all(np.abs(got - exact) <= 6 * 2.0 ** -24 * exact)
+    with pytest.raises(ValueError):
+        oracle.block_scores(x, 3)
+
+
+def test_block_selection_hand_case():
+    # Decode, ctx 12, window 2: pool [0, 10); blocks of 4: {0..3}, {4..7},
+    # {8, 9} (cut by the pool end).  Scores per block: 10, 26, 19.
+    s = np.zeros((1, 1, 12), dtype=np.float32)
+    s[0, 0, :10] = np.arange(1, 11)
+    ctx = np.array([12])
+    top, cnt = oracle.select_topk_blocks(s, ctx, n_q=1, tile_q=1, k_top=4, window=2, block=4)
+    assert cnt.tolist() == [[4]] and top[0, 0].tolist() == [4, 5, 6, 7]
+    top, cnt = oracle.select_topk_blocks(s, ctx, n_q=1, tile_q=1, k_top=8, window=2, block=4)
+    assert cnt.tolist() == [[6]]
+    assert top[0, 0].tolist() == [4, 5, 6, 7, 8, 9, -1, -1]
+    # Equal block scores go to the lower block.
+    s[0, 0, :10] = [1, 1, 1, 1, 2, 1, 1, 0, 2, 2]       # blocks 4, 4, 4
+    top, cnt = oracle.select_topk_blocks(s, ctx, n_q=1, tile_q=1, k_top=8, window=2, block=4)
+    assert top[0, 0].tolist() == [0, 1, 2, 3, 4, 5, 6, 7]
+    # Budget beyond the pool: every pool token once.
+    top, cnt = oracle.select_topk_blocks(s, ctx, n_q=1, tile_q=1, k_top=16, window=2, block=4)
+    assert cnt.tolist() == [[10]] and top[0, 0, :10].tolist() == list(range(10))
+    with pytest.raises(ValueError):
+        oracle.select_topk_blocks(s, ctx, n_q=1, tile_q=1, k_top=6, window=2, block=4)
+
+
+def test_block_size_one_is_token_selection():
+    rng = np.random.default_rng(41)
+    s = rng.integers(0, 6, size=(3, 2, 700)).astype(np.float32) / 8   # many ties
+    ctx = np.array([700, 450, 129])
+    for kw in (dict(n_q=1, tile_q=1), dict(n_q=64, tile_q=32)):
+        n_tiles = kw["n_q"] // kw["tile_q"]
+        a = oracle.select_topk_blocks(s[:, :n_tiles], ctx, k_top=64, window=128, block=1, **kw)
+        b = oracle.select_topk_window(s[:, :n_tiles], ctx, k_top=64, window=128, **kw)
+        assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+
+
+def test_block_selection_brute_force_and_invariants():
+    # Exactly one set of n blocks has every member ahead of every non-member
+    # under (score desc, index asc); it must be the one selected.
+    import itertools
+
+    rng = np.random.default_rng(42)
+    for trial in range(40):
+        block = int(rng.choice([2, 4, 8]))
+        n_sel = int(rng.integers(1, 4))
+        ctx = int(rng.integers(3, 40))
+        window = int(rng.integers(0, 5))
+        s = (rng.integers(0, 4, size=(1, 1, ctx)) / 4).astype(np.float32)
+        top, cnt = oracle.select_topk_blocks(s, np.array([ctx]), n_q=1, tile_q=1,
+                                             k_top=n_sel * block, window=window, block=block)
+        pe = max(0, ctx - window)
+        nb = -(-pe // block)
+        score = [sum(float(v) for v in s[0, 0, m * block:min((m + 1) * block, pe)])
+                 for m in range(nb)]   # small dyadic values: every sum is exact
+        ahead = lambda a, b: score[a] > score[b] or (score[a] == score[b] and a < b)  # noqa: E731
+        sets = [c for c in itertools.combinations(range(nb), min(n_sel, nb))
+                if all(ahead(a, b) for a in c for b in range(nb) if b not in c)]
+        assert len(sets) == 1
+        want = [j for m in sets[0] for j in range(m * block, min((m + 1) * block, pe))]
+        c = int(cnt[0, 0])
+        assert top[0, 0, :c].tolist() == want, trial
+        assert np.all(top[0, 0, c:] == -1)
+
+
+def test_identical_scores_select_the_first_blocks():
+    s = np.full((1, 1, 5000), 0.25, dtype=np.float32)
+    top, cnt = oracle.select_topk_blocks(s, np.array([5000]), n_q=1, tile_q=1, k_top=1024,
+                                         window=128, block=64)
+    assert cnt.tolist() == [[1024]] and top[0, 0].tolist() == list(range(1024))
