@@ -151,6 +151,30 @@ HS2_API hs2_status hs2_select_topk_window(const hs2_attn_desc* desc, const float
                                   void* ws, size_t ws_bytes, hs2_stream_t stream);
 
 /*
+ * Block-level selection, the design HySparse2 replaces ([Origins] "KV Reuse
+ * and Token-Level Sparse Selection": HySparse gives the sparse budget to
+ * blocks of 64 neighbouring tokens; [Summary] "KV Reuse refinements"
+ * compares the two at the same attention budget), for comparisons at equal
+ * budget.  The pool of each row is that of hs2_select_topk_window; it is cut
+ * into aligned blocks of block_size tokens (the last one ends at the pool
+ * end).  A block's importance is the fp32 sum of its tokens' scores, added
+ * as a balanced pairwise tree over its block_size slots (slot pairs (0,1),
+ * (2,3), ... level by level; slots past the pool count 0).  The
+ * k_top / block_size blocks of largest importance are taken (ties to the
+ * lower block) and their pool tokens written to top_idx in ascending order,
+ * -1 padded, with top_cnt their number (below k_top when the cut last block
+ * is taken or the pool is small), in the same form as
+ * hs2_select_topk_window, so hs2_sparse_attn_gather takes them unchanged.
+ * block_size is a power of two, 1..64 (HS2_EINVAL otherwise), dividing k_top
+ * (HS2_EINVAL); at most 65,536 blocks per row (HS2_EUNSUPPORTED beyond).
+ * Other arguments as for hs2_select_topk_window; same workspace size.
+ */
+HS2_API hs2_status hs2_select_topk_blocks(const hs2_attn_desc* desc, int block_size,
+                                          const float* scores, const int32_t* ctx_len,
+                                          int kv_capacity, int32_t* top_idx, int32_t* top_cnt,
+                                          void* ws, size_t ws_bytes, hs2_stream_t stream);
+
+/*
  * Sparse layer ([Origins] "KV Reuse and Token-Level Sparse Selection": the
  * sparse layers reuse the full layer's indices and read its K/V cache; the
  * 128 most recent tokens are always part of the selection).  For query i at
@@ -206,6 +230,21 @@ HS2_API hs2_status hs2_decode_step(const hs2_attn_desc* desc, const void* q,
                                    float* scores, float* lse_full, int32_t* top_idx,
                                    int32_t* top_cnt, float* o, float* lse, void* ws,
                                    size_t ws_bytes, hs2_stream_t stream);
+
+/*
+ * The step of hs2_decode_step with the block-level selection of
+ * hs2_select_topk_blocks in place of the token-level one: scoring, block
+ * selection and the sparse layer, with exactly the outputs of those three
+ * calls issued in order with the same workspace.  Arguments as for
+ * hs2_decode_step and hs2_select_topk_blocks.
+ */
+HS2_API hs2_status hs2_decode_step_blocks(const hs2_attn_desc* desc, int block_size,
+                                          const void* q, const void* q_sparse, const void* k,
+                                          const void* v, int64_t kv_stride,
+                                          const int32_t* ctx_len, int kv_capacity, float* scores,
+                                          float* lse_full, int32_t* top_idx, int32_t* top_cnt,
+                                          float* o, float* lse, void* ws, size_t ws_bytes,
+                                          hs2_stream_t stream);
 
 /*
  * KV Bridging ([Origins] "The Self-Decoder and Cross-Decoder Split", first two

@@ -28,10 +28,12 @@ EXPORTS = (
     "hs2_workspace_size",
     "hs2_full_attn_scores",
     "hs2_select_topk_window",
+    "hs2_select_topk_blocks",
     "hs2_sparse_attn_gather",
     "hs2_sparse_layers_workspace_size",
     "hs2_sparse_attn_gather_layers",
     "hs2_decode_step",
+    "hs2_decode_step_blocks",
     "hs2_bridge_kv",
     "hs2_bridge_packed_bytes",
     "hs2_bridge_pack_weights",
@@ -88,6 +90,8 @@ def load(path: str | None = None):
     lib.hs2_full_attn_scores.restype = _int
     lib.hs2_select_topk_window.argtypes = [_desc_p, _vp, _vp, _int, _vp, _vp, _vp, _sz, _vp]
     lib.hs2_select_topk_window.restype = _int
+    lib.hs2_select_topk_blocks.argtypes = [_desc_p, _int, _vp, _vp, _int, _vp, _vp, _vp, _sz, _vp]
+    lib.hs2_select_topk_blocks.restype = _int
     lib.hs2_sparse_attn_gather.argtypes = [_desc_p, _vp, _vp, _vp, _i64, _vp, _int, _vp, _vp,
                                            _vp, _vp, _vp, _sz, _vp]
     lib.hs2_sparse_attn_gather.restype = _int
@@ -99,6 +103,9 @@ def load(path: str | None = None):
     lib.hs2_decode_step.argtypes = [_desc_p, _vp, _vp, _vp, _vp, _i64, _vp, _int, _vp, _vp, _vp,
                                     _vp, _vp, _vp, _vp, _sz, _vp]
     lib.hs2_decode_step.restype = _int
+    lib.hs2_decode_step_blocks.argtypes = [_desc_p, _int, _vp, _vp, _vp, _vp, _i64, _vp, _int,
+                                           _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]
+    lib.hs2_decode_step_blocks.restype = _int
     lib.hs2_bridge_packed_bytes.argtypes = [_int, _int]
     lib.hs2_bridge_packed_bytes.restype = _sz
     lib.hs2_bridge_pack_weights.argtypes = [_vp, _vp, _int, _int, _vp, _vp]
@@ -173,6 +180,14 @@ def hs2_select_topk_window(desc, scores, ctx_len, kv_capacity, top_idx, top_cnt,
     _check(st, "hs2_select_topk_window")
 
 
+def hs2_select_topk_blocks(desc, block_size, scores, ctx_len, kv_capacity, top_idx, top_cnt,
+                           ws=None, stream=None) -> None:
+    st = load().hs2_select_topk_blocks(ctypes.byref(desc), int(block_size), _ptr(scores),
+                                       _ptr(ctx_len), int(kv_capacity), _ptr(top_idx),
+                                       _ptr(top_cnt), _ptr(ws), _nbytes(ws), _stream(stream))
+    _check(st, "hs2_select_topk_blocks")
+
+
 def hs2_sparse_attn_gather(desc, q, k, v, kv_stride, ctx_len, kv_capacity, top_idx, top_cnt, o,
                            lse=None, ws=None, stream=None) -> None:
     st = load().hs2_sparse_attn_gather(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v),
@@ -203,6 +218,17 @@ def hs2_decode_step(desc, q, q_sparse, k, v, kv_stride, ctx_len, kv_capacity, sc
                                 _ptr(lse_full), _ptr(top_idx), _ptr(top_cnt), _ptr(o), _ptr(lse),
                                 _ptr(ws), _nbytes(ws), _stream(stream))
     _check(st, "hs2_decode_step")
+
+
+def hs2_decode_step_blocks(desc, block_size, q, q_sparse, k, v, kv_stride, ctx_len, kv_capacity,
+                           scores, lse_full, top_idx, top_cnt, o, lse=None, ws=None,
+                           stream=None) -> None:
+    st = load().hs2_decode_step_blocks(ctypes.byref(desc), int(block_size), _ptr(q),
+                                       _ptr(q_sparse), _ptr(k), _ptr(v), int(kv_stride),
+                                       _ptr(ctx_len), int(kv_capacity), _ptr(scores),
+                                       _ptr(lse_full), _ptr(top_idx), _ptr(top_cnt), _ptr(o),
+                                       _ptr(lse), _ptr(ws), _nbytes(ws), _stream(stream))
+    _check(st, "hs2_decode_step_blocks")
 
 
 def hs2_bridge_packed_bytes(d_model, head_dim=128) -> int:

@@ -64,6 +64,35 @@ hs2_status check_ws(const hs2_attn_desc& d, int cap, const void* ws, size_t ws_b
 
 hs2_status launched(hipError_t e) { return e == hipSuccess ? HS2_OK : HS2_EHIP; }
 
+// Block-level selection: block size a power of two up to 64 dividing k_top,
+// at most kMaxBlocks blocks per row (cap >= 1 checked before).
+hs2_status check_block(const hs2_attn_desc* d, int block, int cap) {
+  if (block < 1 || block > 64 || (block & (block - 1)) != 0) return HS2_EINVAL;
+  if (d->k_top % block != 0) return HS2_EINVAL;
+  if (blk_stride(cap, block) > kMaxBlocks) return HS2_EUNSUPPORTED;
+  return HS2_OK;
+}
+
+// Arguments of a whole step (hs2_decode_step and its block-level variant).
+hs2_status check_step(const hs2_attn_desc* desc, const void* q, const void* q_sparse,
+                      const void* k, const void* v, int64_t kv_stride, const int32_t* ctx_len,
+                      int kv_capacity, const float* scores, const float* lse_full,
+                      const int32_t* top_idx, const int32_t* top_cnt, const float* o,
+                      const float* lse, const void* ws, size_t ws_bytes) {
+  hs2_status s = check_desc(desc);
+  if (s != HS2_OK) return s;
+  if (q == nullptr || k == nullptr || v == nullptr || ctx_len == nullptr || scores == nullptr ||
+      top_cnt == nullptr || o == nullptr)
+    return HS2_EINVAL;
+  if (top_idx == nullptr && desc->k_top > 0) return HS2_EINVAL;
+  if ((s = check_cache(desc, kv_stride, kv_capacity)) != HS2_OK) return s;
+  if (misaligned(q) || misaligned(q_sparse) || misaligned(k) || misaligned(v) ||
+      misaligned(ctx_len) || misaligned(scores) || misaligned(lse_full) || misaligned(top_idx) ||
+      misaligned(top_cnt) || misaligned(o) || misaligned(lse))
+    return HS2_EALIGN;
+  return check_ws(*desc, kv_capacity, ws, ws_bytes);
+}
+
 hs2_status check_bridge(const uint16_t* h, int64_t ldh, uint16_t* k_out, uint16_t* v_out,
                         int64_t ld_kv, int M, int d_model, int head_dim) {
   if (h == nullptr || k_out == nullptr || v_out == nullptr) return HS2_EINVAL;
@@ -133,6 +162,27 @@ hs2_status hs2_select_topk_window(const hs2_attn_desc* desc, const float* scores
                                 static_cast<hipStream_t>(stream)));
 }
 
+hs2_status hs2_select_topk_blocks(const hs2_attn_desc* desc, int block_size, const float* scores,
+                                  const int32_t* ctx_len, int kv_capacity, int32_t* top_idx,
+                                  int32_t* top_cnt, void* ws, size_t ws_bytes,
+                                  hs2_stream_t stream) {
+  hs2_status s = check_desc(desc);
+  if (s != HS2_OK) return s;
+  if (scores == nullptr || ctx_len == nullptr || top_cnt == nullptr) return HS2_EINVAL;
+  if (top_idx == nullptr && desc->k_top > 0) return HS2_EINVAL;
+  if (kv_capacity < 1) return HS2_EINVAL;
+  if (kv_capacity > kMaxSelectCap) return HS2_EUNSUPPORTED;
+  if ((s = check_block(desc, block_size, kv_capacity)) != HS2_OK) return s;
+  if (misaligned(scores) || misaligned(ctx_len) || misaligned(top_idx) || misaligned(top_cnt))
+    return HS2_EALIGN;
+  if ((s = check_ws(*desc, kv_capacity, ws, ws_bytes)) != HS2_OK) return s;
+  (void)hipGetLastError();
+  const WsLayout l = ws_layout(*desc, kv_capacity);
+  return launched(launch_select_blocks(*desc, block_size, scores, ctx_len, kv_capacity, top_idx,
+                                       top_cnt, static_cast<char*>(ws) + l.select,
+                                       static_cast<hipStream_t>(stream)));
+}
+
 hs2_status hs2_sparse_attn_gather(const hs2_attn_desc* desc, const void* q, const void* k,
                                   const void* v, int64_t kv_stride, const int32_t* ctx_len,
                                   int kv_capacity, const int32_t* top_idx,
@@ -198,19 +248,10 @@ hs2_status hs2_decode_step(const hs2_attn_desc* desc, const void* q, const void*
                            const int32_t* ctx_len, int kv_capacity, float* scores,
                            float* lse_full, int32_t* top_idx, int32_t* top_cnt, float* o,
                            float* lse, void* ws, size_t ws_bytes, hs2_stream_t stream) {
-  hs2_status s = check_desc(desc);
-  if (s != HS2_OK) return s;
-  if (q == nullptr || k == nullptr || v == nullptr || ctx_len == nullptr || scores == nullptr ||
-      top_cnt == nullptr || o == nullptr)
-    return HS2_EINVAL;
-  if (top_idx == nullptr && desc->k_top > 0) return HS2_EINVAL;
-  if ((s = check_cache(desc, kv_stride, kv_capacity)) != HS2_OK) return s;
   if (q_sparse == nullptr) q_sparse = q;
-  if (misaligned(q) || misaligned(q_sparse) || misaligned(k) || misaligned(v) ||
-      misaligned(ctx_len) || misaligned(scores) || misaligned(lse_full) || misaligned(top_idx) ||
-      misaligned(top_cnt) || misaligned(o) || misaligned(lse))
-    return HS2_EALIGN;
-  if ((s = check_ws(*desc, kv_capacity, ws, ws_bytes)) != HS2_OK) return s;
+  hs2_status s = check_step(desc, q, q_sparse, k, v, kv_stride, ctx_len, kv_capacity, scores,
+                            lse_full, top_idx, top_cnt, o, lse, ws, ws_bytes);
+  if (s != HS2_OK) return s;
   (void)hipGetLastError();
   const WsLayout l = ws_layout(*desc, kv_capacity);
   char* w = static_cast<char*>(ws);
@@ -239,6 +280,38 @@ hs2_status hs2_decode_step(const hs2_attn_desc* desc, const void* q, const void*
     return launched(launch_decode_tail(*desc, q_sparse, k, v, kv_stride, ctx_len, kv_capacity,
                                        hist, w + l.select, top_idx, top_cnt, o, lse, w + l.sparse,
                                        st));
+  return launched(launch_sparse(*desc, q_sparse, k, v, kv_stride, ctx_len, kv_capacity, top_idx,
+                                top_cnt, o, lse, w + l.sparse, st));
+}
+
+hs2_status hs2_decode_step_blocks(const hs2_attn_desc* desc, int block_size, const void* q,
+                                  const void* q_sparse, const void* k, const void* v,
+                                  int64_t kv_stride, const int32_t* ctx_len, int kv_capacity,
+                                  float* scores, float* lse_full, int32_t* top_idx,
+                                  int32_t* top_cnt, float* o, float* lse, void* ws,
+                                  size_t ws_bytes, hs2_stream_t stream) {
+  if (q_sparse == nullptr) q_sparse = q;
+  hs2_status s = check_step(desc, q, q_sparse, k, v, kv_stride, ctx_len, kv_capacity, scores,
+                            lse_full, top_idx, top_cnt, o, lse, ws, ws_bytes);
+  if (s != HS2_OK) return s;
+  if ((s = check_block(desc, block_size, kv_capacity)) != HS2_OK) return s;
+  (void)hipGetLastError();
+  const WsLayout l = ws_layout(*desc, kv_capacity);
+  char* w = static_cast<char*>(ws);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const bool pf = is_prefill(*desc);
+  hipError_t e =
+      pf ? launch_prefill_scores(*desc, q, k, kv_stride, ctx_len, kv_capacity, scores, lse_full,
+                                 w + l.score, false, st)
+         : launch_score_decode(*desc, q, k, kv_stride, ctx_len, kv_capacity, scores, lse_full,
+                               w + l.score, false, st);
+  if (e != hipSuccess) return HS2_EHIP;
+  e = launch_select_blocks(*desc, block_size, scores, ctx_len, kv_capacity, top_idx, top_cnt,
+                           w + l.select, st);
+  if (e != hipSuccess) return HS2_EHIP;
+  if (pf)
+    return launched(launch_prefill_sparse(*desc, q_sparse, k, v, kv_stride, ctx_len, kv_capacity,
+                                          top_idx, top_cnt, o, lse, st));
   return launched(launch_sparse(*desc, q_sparse, k, v, kv_stride, ctx_len, kv_capacity, top_idx,
                                 top_cnt, o, lse, w + l.sparse, st));
 }

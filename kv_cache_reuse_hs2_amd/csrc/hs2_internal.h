@@ -234,6 +234,15 @@ hipError_t launch_select(const hs2_attn_desc& d, const float* scores, const int3
                          int cap, int32_t* top_idx, int32_t* top_cnt, char* ws,
                          uint32_t* hist, bool final_stage, hipStream_t st);
 
+// Block-level selection (blocks of `block` tokens, a power of two <= 64):
+// block sums into the selection region's list area, then one workgroup per
+// row; writes top_idx/top_cnt like launch_select.
+constexpr int kMaxBlocks = 65536;  // blocks per row
+int blk_stride(int cap, int block);
+hipError_t launch_select_blocks(const hs2_attn_desc& d, int block, const float* scores,
+                                const int32_t* ctx_len, int cap, int32_t* top_idx,
+                                int32_t* top_cnt, char* ws, hipStream_t st);
+
 // Chunked prefill (tile_q > 1, bf16): scoring over query tiles and sparse
 // attention of the tiles' queries.
 hipError_t launch_prefill_scores(const hs2_attn_desc& d, const void* q, const void* k,

@@ -12,8 +12,9 @@ import numpy as np
 import torch
 
 from . import (HS2_BF16, HS2_F32, HS2_FP8_E4M3, hs2_attn_desc, hs2_bridge_pack_weights,
-               hs2_bridge_packed_bytes, hs2_decode_step, hs2_full_attn_scores,
-               hs2_select_topk_window, hs2_sparse_attn_gather, hs2_sparse_attn_gather_layers,
+               hs2_bridge_packed_bytes, hs2_decode_step, hs2_decode_step_blocks,
+               hs2_full_attn_scores, hs2_select_topk_blocks, hs2_select_topk_window,
+               hs2_sparse_attn_gather, hs2_sparse_attn_gather_layers,
                hs2_sparse_layers_workspace_size, hs2_workspace_size, make_desc)
 
 
@@ -95,6 +96,12 @@ def run_select(buf: DecodeBuffers, scores: torch.Tensor | None = None, stream=No
                            buf.cap, buf.top_idx, buf.top_cnt, buf.ws, stream)
 
 
+def run_select_blocks(buf: DecodeBuffers, block: int, scores: torch.Tensor | None = None,
+                      stream=None) -> None:
+    hs2_select_topk_blocks(buf.desc, block, buf.scores if scores is None else scores,
+                           buf.ctx_len, buf.cap, buf.top_idx, buf.top_cnt, buf.ws, stream)
+
+
 def run_sparse(buf: DecodeBuffers, q: torch.Tensor | None = None, top_idx=None, top_cnt=None,
                stream=None) -> None:
     hs2_sparse_attn_gather(buf.desc, buf.q if q is None else q, buf.k, buf.v, buf.kv_stride,
@@ -115,6 +122,14 @@ def run_fused_step(buf: DecodeBuffers, q_sparse: torch.Tensor | None = None, str
     hs2_decode_step(buf.desc, buf.q, q_sparse, buf.k, buf.v, buf.kv_stride, buf.ctx_len, buf.cap,
                     buf.scores, buf.lse_full, buf.top_idx, buf.top_cnt, buf.o, buf.lse, buf.ws,
                     stream)
+
+
+def run_fused_step_blocks(buf: DecodeBuffers, block: int, q_sparse: torch.Tensor | None = None,
+                          stream=None) -> None:
+    """One pass of the path with block-level selection, in a single call."""
+    hs2_decode_step_blocks(buf.desc, block, buf.q, q_sparse, buf.k, buf.v, buf.kv_stride,
+                           buf.ctx_len, buf.cap, buf.scores, buf.lse_full, buf.top_idx,
+                           buf.top_cnt, buf.o, buf.lse, buf.ws, stream)
 
 
 def pack_bridge_weights(w_k: torch.Tensor, w_v: torch.Tensor, d_model: int,

@@ -250,3 +250,34 @@ def test_fp8_descriptor_validation(lib):
     assert _scores(d, stride=4096 * 128 + 8) == hs2.HS2_EALIGN
     # (bf16 accepts that stride: the call gets as far as the workspace check)
     assert _scores(_desc(), stride=4096 * 128 + 8, nbytes=0) == hs2.HS2_EWORKSPACE
+
+
+def test_block_selection_validation(lib):
+    L = hs2.load()
+    d = _desc(k_top=1024)
+    need = hs2.hs2_workspace_size(d, 4096)
+
+    def sel(desc=d, block=64, cap=4096, sc=FAKE, ti=FAKE, tc=FAKE, nb=need):
+        return L.hs2_select_topk_blocks(ctypes.byref(desc), block, sc, FAKE, cap, ti, tc, FAKE,
+                                        nb, None)
+
+    for bad in (0, -64, 3, 48, 128):
+        assert sel(block=bad) == hs2.HS2_EINVAL
+    assert sel(desc=_desc(k_top=1000)) == hs2.HS2_EINVAL      # not a multiple of 64
+    assert sel(sc=None) == hs2.HS2_EINVAL
+    assert sel(ti=None) == hs2.HS2_EINVAL
+    assert sel(cap=0) == hs2.HS2_EINVAL
+    assert sel(tc=ODD) == hs2.HS2_EALIGN
+    assert sel(nb=need - 1) == hs2.HS2_EWORKSPACE
+    # at most 65,536 blocks per row
+    big = 65536 * 4 + 1
+    assert sel(block=4, cap=big, nb=1 << 40) == hs2.HS2_EUNSUPPORTED
+
+    def step(block=64, nb=need, v=FAKE, st=4096 * 128):
+        return L.hs2_decode_step_blocks(ctypes.byref(d), block, FAKE, None, FAKE, v, st, FAKE,
+                                        4096, FAKE, None, FAKE, FAKE, FAKE, None, FAKE, nb, None)
+
+    assert step(block=5) == hs2.HS2_EINVAL
+    assert step(v=None) == hs2.HS2_EINVAL
+    assert step(st=100) == hs2.HS2_EINVAL
+    assert step(nb=need - 1) == hs2.HS2_EWORKSPACE

@@ -1,0 +1,143 @@
+"""GPU parity of the block-level selection (HySparse's 64-token blocks).
+
+Fed the same fp32 scores, the GPU block selection must equal the oracle's bit
+for bit: both sum a block's scores in fp32 in the same pairwise order and
+break ties towards the lower block.  The single-call step with block
+selection must equal its three calls, and its sparse output the oracle's on
+the selection it made.
+"""
+
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from gpu_helpers import assert_outputs_close, assert_scores_close
+from workloads import WORKLOADS, make_decode_inputs
+
+pytestmark = pytest.mark.gpu
+
+
+def _say(msg):
+    print(f"[gpu] {msg}", flush=True)
+    sys.stdout.flush()
+
+
+def _select_blocks_on(scores, ctx, *, block, k_top=1024, window=128, n_q=1, tile_q=1):
+    from kv_cache_reuse_hs2_amd import hs2_select_topk_blocks, hs2_workspace_size, make_desc
+    from kv_cache_reuse_hs2_amd.torch_api import to_device
+
+    bsz, tiles, cap = scores.shape
+    d = make_desc(batch=bsz, n_heads=32, n_q=n_q, tile_q=tile_q, k_top=k_top, window=window)
+    ws = torch.empty(hs2_workspace_size(d, cap), dtype=torch.uint8, device="cuda")
+    ti = torch.full((bsz, tiles, max(k_top, 1)), 7, dtype=torch.int32, device="cuda")
+    tc = torch.full((bsz, tiles), 7, dtype=torch.int32, device="cuda")
+    ctx = np.asarray(ctx, dtype=np.int32)
+    hs2_select_topk_blocks(d, block, to_device(scores), to_device(ctx), cap, ti, tc, ws)
+    torch.cuda.synchronize()
+    top, cnt = oracle.select_topk_blocks(scores, ctx, n_q=n_q, tile_q=tile_q, k_top=k_top,
+                                         window=window, block=block)
+    np.testing.assert_array_equal(tc.cpu().numpy(), cnt)
+    if k_top > 0:
+        np.testing.assert_array_equal(ti.cpu().numpy(), top)
+    return top, cnt
+
+
+@pytest.mark.parametrize("block", [64, 32, 16, 1])
+def test_block_select_bit_exact_on_oracle_scores(hs2, block):
+    w = WORKLOADS["decode_bf16_256k_b4"].replace(batch=4)
+    ctx = [40000, 9001, 1153, 130]
+    inp = make_decode_inputs(w, ctx_lens=ctx, capacity=max(ctx))
+    ref, _, _ = oracle.full_attn_scores(inp["q"], inp["k"], inp["ctx_len"], tile_q=1,
+                                        sm_scale=w.sm_scale)
+    _say(f"block select block={block} ctx={ctx}")
+    top, cnt = _select_blocks_on(ref, ctx, block=block)
+    for b, planted in enumerate(inp["planted"]):   # the clustered keys' blocks are taken
+        if block == 1:
+            assert set(planted.tolist()) <= set(top[b, 0, : cnt[b, 0]].tolist())
+
+
+def test_block_select_edge_cases_and_ties(hs2):
+    rng = np.random.default_rng(50)
+    cap = 9000
+    ctx = [0, 1, 128, 129, 192, 1152, 1153, 8999, 9000]
+    s = rng.random((len(ctx), 1, cap), dtype=np.float32)
+    for kw in (dict(block=64), dict(block=64, k_top=0), dict(block=64, window=0),
+               dict(block=64, k_top=2048, window=2048), dict(block=8, k_top=8, window=1),
+               dict(block=2, k_top=6, window=3)):
+        _say(f"block select edge {kw}")
+        _select_blocks_on(s, ctx, **kw)
+    _say("block select ties")
+    few = (rng.integers(0, 3, size=(3, 1, 20000)) / 4).astype(np.float32)
+    _select_blocks_on(few, [20000, 15000, 3001], block=64)
+    _select_blocks_on(few, [20000, 15000, 3001], block=4, k_top=64)
+    eq = np.full((2, 1, 20000), 0.125, dtype=np.float32)
+    top, _ = _select_blocks_on(eq, [20000, 7000], block=64)
+    assert np.array_equal(top[0, 0], np.arange(1024))
+    z = np.zeros((1, 1, 20000), dtype=np.float32)
+    z[0, 0, 19000] = 1.0
+    top, cnt = _select_blocks_on(z, [20000], block=64)
+    assert 19000 in top[0, 0, : cnt[0, 0]].tolist()
+
+
+def test_block_select_prefill_tiles_and_large_rows(hs2):
+    rng = np.random.default_rng(51)
+    s = rng.random((1, 4, 30000), dtype=np.float32)
+    _say("block select prefill tiles")
+    _select_blocks_on(s, [30000], block=64, n_q=256, tile_q=64)
+    _say("block select 1M row")
+    big = rng.random((1, 1, 1 << 20), dtype=np.float32)
+    _select_blocks_on(big, [1 << 20], block=64)
+    _say("block select 4M row, 65,536 blocks")
+    huge = rng.random((1, 1, 1 << 22), dtype=np.float32)
+    _select_blocks_on(huge, [1 << 22], block=64, k_top=2048, window=0)
+
+
+@pytest.mark.parametrize("wname,over,ctx", [
+    ("decode_bf16_256k_b4", dict(batch=2), [20000, 16384]),
+    ("decode_bf16_64k_b16", dict(batch=3, n_heads=7), [9000, 4097, 1152]),
+    ("decode_fp8_256k_b4", dict(batch=2), [12000, 3000]),
+], ids=["bf16_clusters", "bf16_h7", "fp8"])
+def test_block_step_equals_calls_and_oracle(hs2, wname, over, ctx):
+    from kv_cache_reuse_hs2_amd.torch_api import (make_buffers, run_fused_step_blocks,
+                                                  run_scores, run_select_blocks, run_sparse)
+
+    w = WORKLOADS[wname].replace(**over)
+    inp = make_decode_inputs(w, ctx_lens=ctx, capacity=max(ctx))
+    if w.dtype == "fp8":
+        inp["k"] = oracle.dequant_kv(inp["k_raw"], inp["k_scale"])
+        inp["v"] = oracle.dequant_kv(inp["v_raw"], inp["v_scale"])
+    buf = make_buffers(inp, n_heads=w.n_heads, k_top=w.k_top, window=w.window,
+                       sm_scale=w.sm_scale, dtype=w.dtype)
+    _say(f"block step {wname} ctx={ctx}")
+    run_scores(buf)
+    run_select_blocks(buf, 64)
+    run_sparse(buf)
+    torch.cuda.synchronize()
+    three = [t.clone() for t in (buf.scores, buf.top_idx, buf.top_cnt, buf.o, buf.lse)]
+    for t in (buf.scores, buf.top_idx, buf.top_cnt, buf.o, buf.lse):
+        t.fill_(7)
+    run_fused_step_blocks(buf, 64)
+    torch.cuda.synchronize()
+    got = (buf.scores, buf.top_idx, buf.top_cnt, buf.o, buf.lse)
+    for b, n in enumerate(ctx):
+        assert torch.equal(three[0][b, :, :n], got[0][b, :, :n])
+    for a, g in zip(three[1:], got[1:]):
+        assert torch.equal(a, g)
+    # Against the oracle: scores within the bar; the selection exactly the
+    # oracle's on the GPU's own scores; the sparse output on that selection.
+    ref, _, _ = oracle.full_attn_scores(inp["q"], inp["k"], inp["ctx_len"], tile_q=1,
+                                        sm_scale=w.sm_scale)
+    sg = buf.scores.cpu().numpy()
+    assert_scores_close(sg, ref, inp["ctx_len"])
+    for b, n in enumerate(ctx):
+        sg[b, :, n:] = 0.0
+    top, cnt = oracle.select_topk_blocks(sg, inp["ctx_len"], n_q=1, tile_q=1, k_top=w.k_top,
+                                         window=w.window, block=64)
+    np.testing.assert_array_equal(buf.top_cnt.cpu().numpy(), cnt)
+    np.testing.assert_array_equal(buf.top_idx.cpu().numpy(), top)
+    o_ref, _ = oracle.sparse_attention(inp["q"], inp["k"], inp["v"], inp["ctx_len"], top, cnt,
+                                       tile_q=1, window=w.window, sm_scale=w.sm_scale)
+    assert_outputs_close(buf.o.cpu().numpy(), o_ref, w.dtype)
