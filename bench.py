@@ -138,6 +138,38 @@ def sparse_layer_measurements(steps: int, warmup: int) -> dict:
     return out
 
 
+def block_measurements(steps: int, warmup: int) -> dict:
+    """Token-level against block-level (64-token blocks) selection at the same
+    budget on the headline workload: the single-call step of each, and the
+    selection and sparse calls alone (HIP events per call)."""
+    import torch
+
+    from kv_cache_reuse_hs2_amd.torch_api import (make_buffers, run_fused_step,
+                                                  run_fused_step_blocks, run_scores,
+                                                  run_select, run_select_blocks, run_sparse)
+    from workloads import WORKLOADS, make_decode_inputs
+
+    w = WORKLOADS[WORKLOAD]
+    buf = make_buffers(make_decode_inputs(w), n_heads=w.n_heads, k_top=w.k_top, window=w.window,
+                       sm_scale=w.sm_scale, dtype=w.dtype)
+    out = {"block": 64}
+    out["step_ms_token"] = round(time_graphs(lambda: run_fused_step(buf), steps, warmup), 5)
+    out["step_ms_block"] = round(time_graphs(lambda: run_fused_step_blocks(buf, 64), steps,
+                                             warmup), 5)
+    run_scores(buf)
+    out["select_ms_token"] = round(time_events(lambda: run_select(buf), steps, warmup), 5)
+    run_select(buf)
+    out["sparse_ms_token"] = round(time_events(lambda: run_sparse(buf), steps, warmup), 5)
+    out["select_ms_block"] = round(time_events(lambda: run_select_blocks(buf, 64), steps,
+                                               warmup), 5)
+    run_select_blocks(buf, 64)
+    out["sparse_ms_block"] = round(time_events(lambda: run_sparse(buf), steps, warmup), 5)
+    torch.cuda.synchronize()
+    out["selected_rows_block"] = int(buf.top_cnt.sum().item())
+    out["tokens_per_s_block"] = round(w.batch / (out["step_ms_block"] * 1e-3), 1)
+    return out
+
+
 def fp8_measurements(steps: int, warmup: int) -> dict:
     """The headline decode step on an FP8 E4M3 K/V cache (same shape, same
     timing method): the step from HIP graphs and the scoring call alone."""
@@ -444,14 +476,15 @@ def main() -> int:
             "wall_ms_timed_region": round(wall_ms, 3),
         },
         "roofline": {
-            "kernel": "hs2_full_attn_scores = score_p1_bf16<false> + score_p2_bf16<false, false> "
-                      "(two K streams)",
+            "kernel": "hs2_full_attn_scores = score_p1_bf16<false> + "
+                      "score_p2_bf16<false, false, false> (two K streams)",
             "bound": "hbm",
             "achieved": round(score_gbs, 1),
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(score_gbs / HBM_PEAK_GBS, 4),
-            "traffic": measured_traffic(["score_p1_bf16<false>", "score_p2_bf16<false, false>"]),
+            "traffic": measured_traffic(["score_p1_bf16<false>",
+                                         "score_p2_bf16<false, false, false>"]),
             "algorithmic_bytes_per_launch": ab["scoring_call"],
         },
     }
@@ -461,6 +494,8 @@ def main() -> int:
         out["extras"]["decode_bf16_256k_b4_shared_selection"] = sparse_layer_measurements(
             args.steps, args.warmup)
         out["extras"]["decode_fp8_256k_b4"] = fp8_measurements(args.steps, args.warmup)
+        out["extras"]["decode_bf16_256k_b4_block_vs_token"] = block_measurements(args.steps,
+                                                                                 args.warmup)
     if args.calibrate:
         src = torch.empty(256 * MIB, dtype=torch.uint8, device="cuda").fill_(1)
         dst = torch.empty_like(src)

@@ -69,7 +69,7 @@ hs2_status launched(hipError_t e) { return e == hipSuccess ? HS2_OK : HS2_EHIP; 
 hs2_status check_block(const hs2_attn_desc* d, int block, int cap) {
   if (block < 1 || block > 64 || (block & (block - 1)) != 0) return HS2_EINVAL;
   if (d->k_top % block != 0) return HS2_EINVAL;
-  if (blk_stride(cap, block) > kMaxBlocks) return HS2_EUNSUPPORTED;
+  if ((cap + block - 1) / block > kMaxBlocks) return HS2_EUNSUPPORTED;
   return HS2_OK;
 }
 
@@ -179,7 +179,7 @@ hs2_status hs2_select_topk_blocks(const hs2_attn_desc* desc, int block_size, con
   (void)hipGetLastError();
   const WsLayout l = ws_layout(*desc, kv_capacity);
   return launched(launch_select_blocks(*desc, block_size, scores, ctx_len, kv_capacity, top_idx,
-                                       top_cnt, static_cast<char*>(ws) + l.select,
+                                       top_cnt, static_cast<char*>(ws) + l.select, false,
                                        static_cast<hipStream_t>(stream)));
 }
 
@@ -300,14 +300,17 @@ hs2_status hs2_decode_step_blocks(const hs2_attn_desc* desc, int block_size, con
   char* w = static_cast<char*>(ws);
   hipStream_t st = static_cast<hipStream_t>(stream);
   const bool pf = is_prefill(*desc);
+  // MFMA decode: the scoring pass also writes the block selector's piece sums.
+  const bool pieces = !pf && desc->dtype != HS2_F32;
+  const BlockPieces pc = block_pieces(*desc, block_size, kv_capacity, w + l.select);
   hipError_t e =
       pf ? launch_prefill_scores(*desc, q, k, kv_stride, ctx_len, kv_capacity, scores, lse_full,
                                  w + l.score, false, st)
          : launch_score_decode(*desc, q, k, kv_stride, ctx_len, kv_capacity, scores, lse_full,
-                               w + l.score, false, st);
+                               w + l.score, false, st, pieces ? &pc : nullptr);
   if (e != hipSuccess) return HS2_EHIP;
   e = launch_select_blocks(*desc, block_size, scores, ctx_len, kv_capacity, top_idx, top_cnt,
-                           w + l.select, st);
+                           w + l.select, pieces, st);
   if (e != hipSuccess) return HS2_EHIP;
   if (pf)
     return launched(launch_prefill_sparse(*desc, q_sparse, k, v, kv_stride, ctx_len, kv_capacity,

@@ -220,12 +220,22 @@ inline WsLayout ws_layout(const hs2_attn_desc& d, int cap) {
 // Kernel launchers (each returns hipGetLastError() of its launches).  `ws`
 // points at the launcher's own region.
 
+// Piece sums of the pool scores for the block-level selector: out[r][m] =
+// fp32 pairwise sum of the scores of keys [m*piece, (m+1)*piece) of row r
+// (keys past the pool count 0), row stride `stride` floats.
+struct BlockPieces {
+  float* out;
+  int piece;   // min(block, 32)
+  int stride;  // blk_stride(cap, piece)
+};
+
 // with_hist: also build the selector histogram of the pool scores in the
-// scoring region (bf16 decode only).
+// scoring region (MFMA paths only).  pieces (MFMA paths, not with
+// with_hist): also write the block selector's piece sums.
 hipError_t launch_score_decode(const hs2_attn_desc& d, const void* q, const void* k,
                                int64_t kv_stride, const int32_t* ctx_len, int cap,
                                float* scores, float* lse, char* ws, bool with_hist,
-                               hipStream_t st);
+                               hipStream_t st, const BlockPieces* pieces = nullptr);
 
 // hist: a ready histogram of the pool scores (from launch_score_decode with
 // with_hist), or null to build one.  final_stage false: stop after the
@@ -235,13 +245,16 @@ hipError_t launch_select(const hs2_attn_desc& d, const float* scores, const int3
                          uint32_t* hist, bool final_stage, hipStream_t st);
 
 // Block-level selection (blocks of `block` tokens, a power of two <= 64):
-// block sums into the selection region's list area, then one workgroup per
-// row; writes top_idx/top_cnt like launch_select.
+// piece sums (pieces of min(block, 32) keys) in the selection region's list
+// area, then one workgroup per row; writes top_idx/top_cnt like
+// launch_select.  have_pieces: the scoring pass already wrote the piece sums
+// (block_pieces gives where), so they are not recomputed from the scores.
 constexpr int kMaxBlocks = 65536;  // blocks per row
-int blk_stride(int cap, int block);
+int blk_stride(int cap, int piece);
+BlockPieces block_pieces(const hs2_attn_desc& d, int block, int cap, char* sel_ws);
 hipError_t launch_select_blocks(const hs2_attn_desc& d, int block, const float* scores,
                                 const int32_t* ctx_len, int cap, int32_t* top_idx,
-                                int32_t* top_cnt, char* ws, hipStream_t st);
+                                int32_t* top_cnt, char* ws, bool have_pieces, hipStream_t st);
 
 // Chunked prefill (tile_q > 1, bf16): scoring over query tiles and sparse
 // attention of the tiles' queries.

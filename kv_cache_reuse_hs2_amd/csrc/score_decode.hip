@@ -167,13 +167,18 @@ __global__ __launch_bounds__(64 * kP1Waves) void score_p1_bf16(
 }
 
 // Pass 2, bf16 or E4M3 K: fold the statistics into L_h, then
-// I[j] = sum_h 2^(x_hj - L_h).
-template <bool kFp8, bool kHist>
+// I[j] = sum_h 2^(x_hj - L_h).  kHist: also count the pool scores into the
+// selector's first histogram.  kPieces: also write the fp32 sums of the pool
+// scores over aligned pieces of `piece` keys (a power of two <= 32, summed as
+// a pairwise tree by an xor butterfly; keys past the pool count 0) to
+// pieces[b][j / piece], the block importance of the block-level selector.
+template <bool kFp8, bool kHist, bool kPieces>
 __global__ __launch_bounds__(64 * kP2Waves) void score_p2_bf16(
     const uint16_t* __restrict__ q, const void* __restrict__ k, int64_t kv_stride,
     const int32_t* __restrict__ ctx_len, int cap, int H, float c2,
     const float2* __restrict__ stats, int nchunks1, float* __restrict__ scores,
-    int64_t score_stride, float* __restrict__ lse_out, uint32_t* __restrict__ hist, int window) {
+    int64_t score_stride, float* __restrict__ lse_out, uint32_t* __restrict__ hist, int window,
+    float* __restrict__ pieces, int piece, int piece_stride) {
   const int b = gridDim.y - 1 - blockIdx.y;
   const int c = gridDim.x - 1 - blockIdx.x;
   const int N = clamp_ctx(ctx_len, b, cap);
@@ -244,6 +249,12 @@ __global__ __launch_bounds__(64 * kP2Waves) void score_p2_bf16(
     if (hh == 0 && j < j_end) {
       out[j] = imp;
       if (kHist && j < pe) atomicAdd(&s_hist[order_key(imp) >> 20], 1u);
+    }
+    if (kPieces) {
+      float x = j < pe ? imp : 0.f;
+      for (int off = 1; off < piece; off <<= 1) x += __shfl_xor(x, off);
+      if (hh == 0 && (r32 & (piece - 1)) == 0 && j < pe)
+        pieces[(size_t)b * piece_stride + j / piece] = x;
     }
 #pragma unroll
     for (int i = 0; i < k_regs<kFp8>(); ++i) kr[i] = kn[i];
@@ -362,23 +373,28 @@ __global__ __launch_bounds__(256) void score_reduce_f32(
   }
 }
 
-// Both MFMA passes; hist null: no selector histogram.
+// Both MFMA passes; hist null: no selector histogram; pc null: no piece sums.
 template <bool kFp8>
 void launch_score_mfma(const hs2_attn_desc& d, const void* q, const void* k, int64_t kv_stride,
                        const int32_t* ctx_len, int cap, float* scores, float* lse, float2* stats,
-                       int nchunks1, float c2, uint32_t* hist, hipStream_t st) {
+                       int nchunks1, float c2, uint32_t* hist, const BlockPieces* pc,
+                       hipStream_t st) {
   const auto* qq = static_cast<const uint16_t*>(q);
   score_p1_bf16<kFp8><<<dim3(nchunks1, d.batch), 64 * kP1Waves, 0, st>>>(
       qq, k, kv_stride, ctx_len, cap, d.n_heads, c2, stats, nchunks1, hist);
   const dim3 g2((cap + kP2Chunk - 1) / kP2Chunk, d.batch);
   if (hist != nullptr)
-    score_p2_bf16<kFp8, true><<<g2, 64 * kP2Waves, 0, st>>>(
+    score_p2_bf16<kFp8, true, false><<<g2, 64 * kP2Waves, 0, st>>>(
         qq, k, kv_stride, ctx_len, cap, d.n_heads, c2, stats, nchunks1, scores, cap, lse, hist,
-        d.window);
-  else
-    score_p2_bf16<kFp8, false><<<g2, 64 * kP2Waves, 0, st>>>(
+        d.window, nullptr, 1, 0);
+  else if (pc != nullptr)
+    score_p2_bf16<kFp8, false, true><<<g2, 64 * kP2Waves, 0, st>>>(
         qq, k, kv_stride, ctx_len, cap, d.n_heads, c2, stats, nchunks1, scores, cap, lse, nullptr,
-        d.window);
+        d.window, pc->out, pc->piece, pc->stride);
+  else
+    score_p2_bf16<kFp8, false, false><<<g2, 64 * kP2Waves, 0, st>>>(
+        qq, k, kv_stride, ctx_len, cap, d.n_heads, c2, stats, nchunks1, scores, cap, lse, nullptr,
+        d.window, nullptr, 1, 0);
 }
 
 }  // namespace
@@ -386,7 +402,7 @@ void launch_score_mfma(const hs2_attn_desc& d, const void* q, const void* k, int
 hipError_t launch_score_decode(const hs2_attn_desc& d, const void* q, const void* k,
                                int64_t kv_stride, const int32_t* ctx_len, int cap,
                                float* scores, float* lse, char* ws, bool with_hist,
-                               hipStream_t st) {
+                               hipStream_t st, const BlockPieces* pieces) {
   const ScoreWs w = score_ws(d, cap);
   float2* stats = reinterpret_cast<float2*>(ws + w.stats_off);
   const float c2 = d.sm_scale * 1.4426950408889634f;
@@ -395,10 +411,10 @@ hipError_t launch_score_decode(const hs2_attn_desc& d, const void* q, const void
     uint32_t* hist = with_hist ? reinterpret_cast<uint32_t*>(ws + w.hist_off) : nullptr;
     if (d.dtype == HS2_FP8_E4M3)
       launch_score_mfma<true>(d, q, k, kv_stride, ctx_len, cap, scores, lse, stats, nchunks1,
-                              c2 * d.k_scale, hist, st);
+                              c2 * d.k_scale, hist, pieces, st);
     else
       launch_score_mfma<false>(d, q, k, kv_stride, ctx_len, cap, scores, lse, stats, nchunks1,
-                               c2, hist, st);
+                               c2, hist, pieces, st);
   } else {
     float* lse2 = reinterpret_cast<float*>(ws + w.lse2_off);
     const dim3 grid(nchunks1, d.batch);

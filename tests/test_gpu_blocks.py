@@ -99,7 +99,8 @@ def test_block_select_prefill_tiles_and_large_rows(hs2):
     ("decode_bf16_256k_b4", dict(batch=2), [20000, 16384]),
     ("decode_bf16_64k_b16", dict(batch=3, n_heads=7), [9000, 4097, 1152]),
     ("decode_fp8_256k_b4", dict(batch=2), [12000, 3000]),
-], ids=["bf16_clusters", "bf16_h7", "fp8"])
+    ("decode_f32_4k", dict(batch=2), [4096, 1000]),
+], ids=["bf16_clusters", "bf16_h7", "fp8", "f32"])
 def test_block_step_equals_calls_and_oracle(hs2, wname, over, ctx):
     from kv_cache_reuse_hs2_amd.torch_api import (make_buffers, run_fused_step_blocks,
                                                   run_scores, run_select_blocks, run_sparse)
@@ -141,3 +142,35 @@ def test_block_step_equals_calls_and_oracle(hs2, wname, over, ctx):
     o_ref, _ = oracle.sparse_attention(inp["q"], inp["k"], inp["v"], inp["ctx_len"], top, cnt,
                                        tile_q=1, window=w.window, sm_scale=w.sm_scale)
     assert_outputs_close(buf.o.cpu().numpy(), o_ref, w.dtype)
+
+
+def test_block_step_prefill_tiles(hs2):
+    # Chunked prefill with block selection per 64-query tile: one call equals
+    # its three calls, and the selection is the oracle's on the GPU's scores.
+    from kv_cache_reuse_hs2_amd.torch_api import (make_buffers, run_fused_step_blocks,
+                                                  run_scores, run_select_blocks, run_sparse)
+    from workloads import make_prefill_inputs
+
+    w = WORKLOADS["prefill_bf16_128k_8k"].replace(batch=2)
+    ctx = [9000, 5000]
+    inp = make_prefill_inputs(w, ctx_lens=ctx, n_q=128, capacity=9000)
+    buf = make_buffers(inp, n_heads=w.n_heads, k_top=w.k_top, window=w.window,
+                       sm_scale=w.sm_scale, dtype="bf16", n_q=128, tile_q=64)
+    _say(f"block step prefill ctx={ctx}")
+    run_scores(buf)
+    run_select_blocks(buf, 64)
+    run_sparse(buf)
+    torch.cuda.synchronize()
+    three = [t.clone() for t in (buf.scores, buf.top_idx, buf.top_cnt, buf.o, buf.lse)]
+    run_fused_step_blocks(buf, 64)
+    torch.cuda.synchronize()
+    for a, g in zip(three, (buf.scores, buf.top_idx, buf.top_cnt, buf.o, buf.lse)):
+        assert torch.equal(a, g)
+    sg = buf.scores.cpu().numpy()
+    top, cnt = oracle.select_topk_blocks(sg, inp["ctx_len"], n_q=128, tile_q=64, k_top=w.k_top,
+                                         window=w.window, block=64)
+    np.testing.assert_array_equal(buf.top_cnt.cpu().numpy(), cnt)
+    np.testing.assert_array_equal(buf.top_idx.cpu().numpy(), top)
+    o_ref, _ = oracle.sparse_attention(inp["q"], inp["k"], inp["v"], inp["ctx_len"], top, cnt,
+                                       tile_q=64, window=w.window, sm_scale=w.sm_scale)
+    assert_outputs_close(buf.o.cpu().numpy(), o_ref, "bf16")
