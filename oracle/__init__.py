@@ -22,4 +22,5 @@ from .hs2_oracle import (  # noqa: F401
     select_topk_window,
     selection_set,
     sparse_attention,
+    swa_attention,
 )

@@ -72,6 +72,7 @@ __all__ = [
     "selection_set",
     "sparse_attention",
     "dense_attention",
+    "swa_attention",
     "bf16_round",
     "fp8_e4m3_value",
     "dequant_kv",
@@ -314,6 +315,38 @@ def sparse_attention(q, k, v, ctx_len, top_idx, top_cnt, *, tile_q: int,
                 continue
             p, lse[b, i] = attention_probs(q[b, i], k[b, sel], sm_scale)
             o[b, i] = p @ v[b, sel]
+    return o, lse
+
+
+def swa_attention(q, k, v, ctx_len, *, window: int, sm_scale: float):
+    """Sliding-window attention of the self-decoder's SWA layers.
+
+    The self-decoder, the only part of the model that prefill runs, mixes
+    full-attention layers with sliding-window attention layers ([Origins]
+    "The Self-Decoder and Cross-Decoder Split"; [Summary] "KV Bridging").
+    The pages give no window size for those layers, so it is an argument.  A
+    query at position P attends causally to the keys
+    [max(0, P - window + 1), P] of its sequence, one shared K/V head:
+      o = softmax(sm_scale * q . k) v over that range.
+    Returns (o float64 [B][n_q][H][D], lse float64 [B][n_q][H], natural log).
+    """
+    q = _f64(q)
+    k = _f64(k)
+    v = _f64(v)
+    if window < 1:
+        raise ValueError("window must be positive")
+    bsz, n_q, n_heads, head_dim = q.shape
+    o = np.zeros((bsz, n_q, n_heads, head_dim))
+    lse = np.full((bsz, n_q, n_heads), -np.inf)
+    for b in range(bsz):
+        pos = query_positions(int(ctx_len[b]), n_q)
+        for i in range(n_q):
+            if pos[i] < 0:
+                continue
+            lo = max(0, int(pos[i]) - window + 1)
+            keys = np.arange(lo, int(pos[i]) + 1)
+            p, lse[b, i] = attention_probs(q[b, i], k[b, keys], sm_scale)
+            o[b, i] = p @ v[b, keys]
     return o, lse
 
 

@@ -523,3 +523,72 @@ def test_identical_scores_select_the_first_blocks():
     top, cnt = oracle.select_topk_blocks(s, np.array([5000]), n_q=1, tile_q=1, k_top=1024,
                                          window=128, block=64)
     assert cnt.tolist() == [[1024]] and top[0, 0].tolist() == list(range(1024))
+
+
+# --- Sliding-window attention of the self-decoder ----------------------------
+
+def test_swa_hand_case():
+    # D = 1, one head, keys 1..5 (scale 1), values 10..50, window 2: the query
+    # at position 4 sees keys 3 and 4 (values 4 and 5 for k, 40 and 50 for v).
+    k = np.arange(1.0, 6.0)[None, :, None]
+    v = (10.0 * np.arange(1, 6))[None, :, None]
+    q = np.array([[[[1.0]], [[0.5]]]])                   # queries at positions 3, 4
+    o, lse = oracle.swa_attention(q, k, v, np.array([5]), window=2, sm_scale=1.0)
+    # position 3: keys 3, 4 (k = 3, 4) with q = 1; position 4: keys 4, 5 with q = 0.5
+    w3 = np.array([math.exp(3.0), math.exp(4.0)])
+    w4 = np.array([math.exp(2.0), math.exp(2.5)])
+    assert o[0, 0, 0, 0] == pytest.approx((w3 @ [30.0, 40.0]) / w3.sum(), rel=1e-14)
+    assert o[0, 1, 0, 0] == pytest.approx((w4 @ [40.0, 50.0]) / w4.sum(), rel=1e-14)
+    assert lse[0, 0, 0] == pytest.approx(math.log(w3.sum()), rel=1e-14)
+    assert lse[0, 1, 0] == pytest.approx(math.log(w4.sum()), rel=1e-14)
+
+
+def test_swa_wide_window_is_scipy_causal_softmax():
+    rng = np.random.default_rng(60)
+    q = rng.standard_normal((2, 5, 3, 8))
+    k = rng.standard_normal((2, 40, 8))
+    v = rng.standard_normal((2, 40, 8))
+    ctx = np.array([40, 23])
+    o, lse = oracle.swa_attention(q, k, v, ctx, window=10_000, sm_scale=0.3)
+    for b in range(2):
+        for i in range(5):
+            P = ctx[b] - 5 + i
+            for h in range(3):
+                s = 0.3 * k[b, : P + 1] @ q[b, i, h]
+                assert np.allclose(o[b, i, h], scipy.special.softmax(s) @ v[b, : P + 1],
+                                   rtol=1e-12, atol=1e-12)
+                assert lse[b, i, h] == pytest.approx(scipy.special.logsumexp(s), rel=1e-12)
+
+
+def test_swa_window_one_returns_own_value_and_brute_force():
+    rng = np.random.default_rng(61)
+    q = rng.standard_normal((1, 6, 2, 4))
+    k = rng.standard_normal((1, 30, 4))
+    v = rng.standard_normal((1, 30, 4))
+    ctx = np.array([30])
+    o, lse = oracle.swa_attention(q, k, v, ctx, window=1, sm_scale=0.5)
+    for i in range(6):
+        P = 24 + i
+        assert np.array_equal(o[0, i], np.repeat(v[0, P][None], 2, axis=0))
+        assert np.allclose(lse[0, i], 0.5 * q[0, i] @ k[0, P], rtol=1e-14)
+    # brute force with math.exp, window 7
+    o, lse = oracle.swa_attention(q, k, v, ctx, window=7, sm_scale=0.5)
+    for i in range(6):
+        P = 24 + i
+        for h in range(2):
+            ws = [math.exp(0.5 * sum(q[0, i, h, d] * k[0, j, d] for d in range(4)))
+                  for j in range(P - 6, P + 1)]
+            tot = sum(ws)
+            for d in range(4):
+                want = sum(w * v[0, j, d] for w, j in zip(ws, range(P - 6, P + 1))) / tot
+                assert o[0, i, h, d] == pytest.approx(want, rel=1e-12, abs=1e-12)
+            assert lse[0, i, h] == pytest.approx(math.log(tot), rel=1e-12)
+
+
+def test_swa_queries_before_the_cache_start_are_empty():
+    q = np.ones((1, 4, 1, 2))
+    k = np.ones((1, 8, 2))
+    v = np.ones((1, 8, 2))
+    o, lse = oracle.swa_attention(q, k, v, np.array([2]), window=3, sm_scale=1.0)
+    assert np.all(o[0, :2] == 0) and np.all(np.isneginf(lse[0, :2]))
+    assert np.all(o[0, 2:] == 1) and np.all(np.isfinite(lse[0, 2:]))
