@@ -170,6 +170,39 @@ def block_measurements(steps: int, warmup: int) -> dict:
     return out
 
 
+def swa_measurements(steps: int, warmup: int) -> dict:
+    """The self-decoder's sliding-window attention (hs2_swa_attention) over the
+    chunked-prefill shape: 8,192 queries at the end of a 139,264-key cache,
+    32 heads, window 128."""
+    import torch
+
+    import kv_cache_reuse_hs2_amd as hs2
+    from kv_cache_reuse_hs2_amd.torch_api import to_device
+    from workloads import WORKLOADS, make_prefill_inputs
+
+    w = WORKLOADS["prefill_bf16_128k_8k"]
+    inp = make_prefill_inputs(w)
+    window = 128
+    d = hs2.make_desc(batch=1, n_heads=w.n_heads, n_q=w.n_q, tile_q=1, k_top=0, window=window,
+                      sm_scale=w.sm_scale)
+    q, k, v = (to_device(inp[x]) for x in ("q_raw", "k_raw", "v_raw"))
+    ctx = to_device(inp["ctx_len"])
+    o = torch.empty((1, w.n_q, w.n_heads, w.head_dim), dtype=torch.float32, device="cuda")
+    lse = torch.empty((1, w.n_q, w.n_heads), dtype=torch.float32, device="cuda")
+    cap = int(inp["capacity"])
+    ms = time_events(lambda: hs2.hs2_swa_attention(d, q, k, v, cap * w.head_dim, ctx, cap, o, lse),
+                     steps, warmup)
+    nq, hd = w.n_q, w.head_dim
+    byts = nq * w.n_heads * hd * (2 + 4) + nq * w.n_heads * 4 + (nq + window - 1) * hd * 2 * 2
+    flop = 4.0 * w.n_heads * hd * nq * window    # QK^T and PV over each query's window
+    return {"ms": round(ms, 5), "queries_per_s": round(nq / (ms * 1e-3), 1),
+            "hbm_GBps": round(byts / (ms * 1e-3) / 1e9, 1),
+            "hbm_frac": round(byts / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+            "achieved_TFLOPs": round(flop / (ms * 1e-3) / 1e12, 1),
+            "algorithmic_bytes": int(byts), "algorithmic_flop": flop,
+            "note": "q read and fp32 o written once, the band's K and V rows once"}
+
+
 def fp8_measurements(steps: int, warmup: int) -> dict:
     """The headline decode step on an FP8 E4M3 K/V cache (same shape, same
     timing method): the step from HIP graphs and the scoring call alone."""
@@ -496,6 +529,7 @@ def main() -> int:
         out["extras"]["decode_fp8_256k_b4"] = fp8_measurements(args.steps, args.warmup)
         out["extras"]["decode_bf16_256k_b4_block_vs_token"] = block_measurements(args.steps,
                                                                                  args.warmup)
+        out["extras"]["swa_bf16_prefill_8k_w128"] = swa_measurements(args.steps, args.warmup)
     if args.calibrate:
         src = torch.empty(256 * MIB, dtype=torch.uint8, device="cuda").fill_(1)
         dst = torch.empty_like(src)

@@ -247,6 +247,27 @@ HS2_API hs2_status hs2_decode_step_blocks(const hs2_attn_desc* desc, int block_s
                                           hs2_stream_t stream);
 
 /*
+ * Sliding-window attention of the self-decoder.  Prefill runs only the
+ * self-decoder, which mixes full-attention layers with sliding-window
+ * attention layers ([Origins] "The Self-Decoder and Cross-Decoder Split";
+ * [Summary] "KV Bridging"); this is the attention of those SWA layers.  Query
+ * i of sequence b sits at position P = ctx_len[b] - n_q + i and attends to
+ * the keys [max(0, P - window + 1), P] of its sequence:
+ *   o[b][i][h] = sum_j softmax(sm_scale * q_bih . k_j) v_j,
+ *   lse[b][i][h] = log sum_j exp(sm_scale * q_bih . k_j)   (lse may be NULL);
+ * queries at negative positions give 0 and -inf.  desc: batch, n_q >= 1,
+ * n_heads 1..32 sharing one K/V head, head_dim 128, window >= 1 (the pages
+ * give no SWA window size; 128 in the benchmarks), sm_scale, causal = 1,
+ * dtype HS2_BF16 (HS2_EUNSUPPORTED otherwise); tile_q and k_top are not used.
+ * Layouts and alignment as for the other calls (q [B][n_q][H][D] bf16, k/v
+ * [B][cap][D] bf16 with sequence stride kv_stride, o f32 [B][n_q][H][D]).
+ * No workspace.
+ */
+HS2_API hs2_status hs2_swa_attention(const hs2_attn_desc* desc, const void* q, const void* k,
+                                     const void* v, int64_t kv_stride, const int32_t* ctx_len,
+                                     int kv_capacity, float* o, float* lse, hs2_stream_t stream);
+
+/*
  * KV Bridging ([Origins] "The Self-Decoder and Cross-Decoder Split", first two
  * equations; [Summary] "KV Bridging"): the K and V of a cross-decoder
  * full-attention layer are learned projections of a self-decoder

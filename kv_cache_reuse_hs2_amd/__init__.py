@@ -34,6 +34,7 @@ EXPORTS = (
     "hs2_sparse_attn_gather_layers",
     "hs2_decode_step",
     "hs2_decode_step_blocks",
+    "hs2_swa_attention",
     "hs2_bridge_kv",
     "hs2_bridge_packed_bytes",
     "hs2_bridge_pack_weights",
@@ -106,6 +107,8 @@ def load(path: str | None = None):
     lib.hs2_decode_step_blocks.argtypes = [_desc_p, _int, _vp, _vp, _vp, _vp, _i64, _vp, _int,
                                            _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]
     lib.hs2_decode_step_blocks.restype = _int
+    lib.hs2_swa_attention.argtypes = [_desc_p, _vp, _vp, _vp, _i64, _vp, _int, _vp, _vp, _vp]
+    lib.hs2_swa_attention.restype = _int
     lib.hs2_bridge_packed_bytes.argtypes = [_int, _int]
     lib.hs2_bridge_packed_bytes.restype = _sz
     lib.hs2_bridge_pack_weights.argtypes = [_vp, _vp, _int, _int, _vp, _vp]
@@ -229,6 +232,14 @@ def hs2_decode_step_blocks(desc, block_size, q, q_sparse, k, v, kv_stride, ctx_l
                                        _ptr(lse_full), _ptr(top_idx), _ptr(top_cnt), _ptr(o),
                                        _ptr(lse), _ptr(ws), _nbytes(ws), _stream(stream))
     _check(st, "hs2_decode_step_blocks")
+
+
+def hs2_swa_attention(desc, q, k, v, kv_stride, ctx_len, kv_capacity, o, lse=None,
+                      stream=None) -> None:
+    st = load().hs2_swa_attention(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), int(kv_stride),
+                                  _ptr(ctx_len), int(kv_capacity), _ptr(o), _ptr(lse),
+                                  _stream(stream))
+    _check(st, "hs2_swa_attention")
 
 
 def hs2_bridge_packed_bytes(d_model, head_dim=128) -> int:

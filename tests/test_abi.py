@@ -281,3 +281,29 @@ def test_block_selection_validation(lib):
     assert step(v=None) == hs2.HS2_EINVAL
     assert step(st=100) == hs2.HS2_EINVAL
     assert step(nb=need - 1) == hs2.HS2_EWORKSPACE
+
+
+def test_swa_validation(lib):
+    L = hs2.load()
+
+    def call(desc=None, q=FAKE, o=FAKE, lse=None, st=4096 * 128, cap=4096):
+        d = desc if desc is not None else hs2.make_desc(batch=1, n_heads=32, n_q=64, k_top=0,
+                                                         window=128)
+        return L.hs2_swa_attention(ctypes.byref(d), q, FAKE, FAKE, st, FAKE, cap, o, lse, None)
+
+    mk = lambda **kw: hs2.make_desc(**dict(dict(batch=1, n_heads=32, n_q=64, k_top=0,  # noqa: E731
+                                                window=128), **kw))
+    assert L.hs2_swa_attention(None, FAKE, FAKE, FAKE, 4096 * 128, FAKE, 4096, FAKE, None,
+                               None) == hs2.HS2_EINVAL
+    assert call(desc=mk(window=0)) == hs2.HS2_EINVAL
+    assert call(desc=mk(n_q=0)) == hs2.HS2_EINVAL
+    assert call(desc=mk(sm_scale=-1.0)) == hs2.HS2_EINVAL
+    assert call(desc=mk(dtype=hs2.HS2_F32)) == hs2.HS2_EUNSUPPORTED
+    assert call(desc=mk(head_dim=64)) == hs2.HS2_EUNSUPPORTED
+    assert call(desc=mk(n_heads=40)) == hs2.HS2_EUNSUPPORTED
+    assert call(q=None) == hs2.HS2_EINVAL
+    assert call(o=None) == hs2.HS2_EINVAL
+    assert call(cap=0) == hs2.HS2_EINVAL
+    assert call(st=100) == hs2.HS2_EINVAL
+    assert call(st=4096 * 128 + 4) == hs2.HS2_EALIGN
+    assert call(lse=ODD) == hs2.HS2_EALIGN
