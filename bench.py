@@ -187,20 +187,25 @@ def swa_measurements(steps: int, warmup: int) -> dict:
                       sm_scale=w.sm_scale)
     q, k, v = (to_device(inp[x]) for x in ("q_raw", "k_raw", "v_raw"))
     ctx = to_device(inp["ctx_len"])
-    o = torch.empty((1, w.n_q, w.n_heads, w.head_dim), dtype=torch.float32, device="cuda")
     lse = torch.empty((1, w.n_q, w.n_heads), dtype=torch.float32, device="cuda")
     cap = int(inp["capacity"])
-    ms = time_events(lambda: hs2.hs2_swa_attention(d, q, k, v, cap * w.head_dim, ctx, cap, o, lse),
-                     steps, warmup)
     nq, hd = w.n_q, w.head_dim
-    byts = nq * w.n_heads * hd * (2 + 4) + nq * w.n_heads * 4 + (nq + window - 1) * hd * 2 * 2
     flop = 4.0 * w.n_heads * hd * nq * window    # QK^T and PV over each query's window
-    return {"ms": round(ms, 5), "queries_per_s": round(nq / (ms * 1e-3), 1),
-            "hbm_GBps": round(byts / (ms * 1e-3) / 1e9, 1),
-            "hbm_frac": round(byts / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
-            "achieved_TFLOPs": round(flop / (ms * 1e-3) / 1e12, 1),
-            "algorithmic_bytes": int(byts), "algorithmic_flop": flop,
-            "note": "q read and fp32 o written once, the band's K and V rows once"}
+    out = {"window": window, "algorithmic_flop": flop}
+    for name, dt, code, ob in (("bf16_out", torch.bfloat16, hs2.HS2_BF16, 2),
+                               ("f32_out", torch.float32, hs2.HS2_F32, 4)):
+        o = torch.empty((1, nq, w.n_heads, hd), dtype=dt, device="cuda")
+        ms = time_events(lambda: hs2.hs2_swa_attention(d, q, k, v, cap * hd, ctx, cap, o, code,
+                                                       lse), steps, warmup)
+        byts = nq * w.n_heads * hd * (2 + ob) + nq * w.n_heads * 4 + (nq + window - 1) * hd * 4
+        out[name] = {"ms": round(ms, 5), "queries_per_s": round(nq / (ms * 1e-3), 1),
+                     "hbm_GBps": round(byts / (ms * 1e-3) / 1e9, 1),
+                     "hbm_frac": round(byts / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                     "achieved_TFLOPs": round(flop / (ms * 1e-3) / 1e12, 1),
+                     "algorithmic_bytes": int(byts)}
+        del o
+    out["note"] = "q read and o written once, the band's K and V rows once"
+    return out
 
 
 def fp8_measurements(steps: int, warmup: int) -> dict:

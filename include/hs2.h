@@ -260,12 +260,15 @@ HS2_API hs2_status hs2_decode_step_blocks(const hs2_attn_desc* desc, int block_s
  * give no SWA window size; 128 in the benchmarks), sm_scale, causal = 1,
  * dtype HS2_BF16 (HS2_EUNSUPPORTED otherwise); tile_q and k_top are not used.
  * Layouts and alignment as for the other calls (q [B][n_q][H][D] bf16, k/v
- * [B][cap][D] bf16 with sequence stride kv_stride, o f32 [B][n_q][H][D]).
- * No workspace.
+ * [B][cap][D] bf16 with sequence stride kv_stride).  o is [B][n_q][H][D] in
+ * o_dtype: HS2_F32, or HS2_BF16 (rounded to nearest even; the next layer's
+ * input format, half the bytes to write); HS2_EINVAL otherwise.  No
+ * workspace.
  */
 HS2_API hs2_status hs2_swa_attention(const hs2_attn_desc* desc, const void* q, const void* k,
                                      const void* v, int64_t kv_stride, const int32_t* ctx_len,
-                                     int kv_capacity, float* o, float* lse, hs2_stream_t stream);
+                                     int kv_capacity, void* o, hs2_dtype o_dtype, float* lse,
+                                     hs2_stream_t stream);
 
 /*
  * KV Bridging ([Origins] "The Self-Decoder and Cross-Decoder Split", first two

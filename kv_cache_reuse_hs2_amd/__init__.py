@@ -107,7 +107,8 @@ def load(path: str | None = None):
     lib.hs2_decode_step_blocks.argtypes = [_desc_p, _int, _vp, _vp, _vp, _vp, _i64, _vp, _int,
                                            _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]
     lib.hs2_decode_step_blocks.restype = _int
-    lib.hs2_swa_attention.argtypes = [_desc_p, _vp, _vp, _vp, _i64, _vp, _int, _vp, _vp, _vp]
+    lib.hs2_swa_attention.argtypes = [_desc_p, _vp, _vp, _vp, _i64, _vp, _int, _vp, _int, _vp,
+                                      _vp]
     lib.hs2_swa_attention.restype = _int
     lib.hs2_bridge_packed_bytes.argtypes = [_int, _int]
     lib.hs2_bridge_packed_bytes.restype = _sz
@@ -234,11 +235,11 @@ def hs2_decode_step_blocks(desc, block_size, q, q_sparse, k, v, kv_stride, ctx_l
     _check(st, "hs2_decode_step_blocks")
 
 
-def hs2_swa_attention(desc, q, k, v, kv_stride, ctx_len, kv_capacity, o, lse=None,
-                      stream=None) -> None:
+def hs2_swa_attention(desc, q, k, v, kv_stride, ctx_len, kv_capacity, o, o_dtype=HS2_F32,
+                      lse=None, stream=None) -> None:
     st = load().hs2_swa_attention(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), int(kv_stride),
-                                  _ptr(ctx_len), int(kv_capacity), _ptr(o), _ptr(lse),
-                                  _stream(stream))
+                                  _ptr(ctx_len), int(kv_capacity), _ptr(o), int(o_dtype),
+                                  _ptr(lse), _stream(stream))
     _check(st, "hs2_swa_attention")
 
 

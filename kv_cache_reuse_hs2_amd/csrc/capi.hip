@@ -321,7 +321,8 @@ hs2_status hs2_decode_step_blocks(const hs2_attn_desc* desc, int block_size, con
 
 hs2_status hs2_swa_attention(const hs2_attn_desc* desc, const void* q, const void* k,
                              const void* v, int64_t kv_stride, const int32_t* ctx_len,
-                             int kv_capacity, float* o, float* lse, hs2_stream_t stream) {
+                             int kv_capacity, void* o, hs2_dtype o_dtype, float* lse,
+                             hs2_stream_t stream) {
   if (desc == nullptr) return HS2_EINVAL;
   const hs2_attn_desc& d = *desc;
   if (d.batch < 1 || d.n_q < 1 || d.n_heads < 1 || d.head_dim < 1 || d.window < 1)
@@ -332,14 +333,15 @@ hs2_status hs2_swa_attention(const hs2_attn_desc* desc, const void* q, const voi
     return HS2_EUNSUPPORTED;
   if (q == nullptr || k == nullptr || v == nullptr || ctx_len == nullptr || o == nullptr)
     return HS2_EINVAL;
+  if (o_dtype != HS2_F32 && o_dtype != HS2_BF16) return HS2_EINVAL;
   if (kv_capacity < 1 || kv_stride < (int64_t)kv_capacity * kHeadDim) return HS2_EINVAL;
   if (kv_stride % 8 != 0) return HS2_EALIGN;
   if (misaligned(q) || misaligned(k) || misaligned(v) || misaligned(ctx_len) || misaligned(o) ||
       misaligned(lse))
     return HS2_EALIGN;
   (void)hipGetLastError();
-  return launched(launch_swa(d, q, k, v, kv_stride, ctx_len, kv_capacity, o, lse,
-                             static_cast<hipStream_t>(stream)));
+  return launched(launch_swa(d, q, k, v, kv_stride, ctx_len, kv_capacity, o,
+                             o_dtype == HS2_BF16, lse, static_cast<hipStream_t>(stream)));
 }
 
 hs2_status hs2_bridge_kv(const uint16_t* h, int64_t ldh, const uint16_t* w_k, const uint16_t* w_v,

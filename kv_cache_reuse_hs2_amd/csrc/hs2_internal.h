@@ -245,10 +245,10 @@ hipError_t launch_select(const hs2_attn_desc& d, const float* scores, const int3
                          uint32_t* hist, bool final_stage, hipStream_t st);
 
 // Sliding-window attention (the self-decoder's SWA layers), bf16, any n_q:
-// query i at N - n_q + i attends to its last d.window keys.
+// query i at N - n_q + i attends to its last d.window keys; o in bf16 or fp32.
 hipError_t launch_swa(const hs2_attn_desc& d, const void* q, const void* k, const void* v,
-                      int64_t kv_stride, const int32_t* ctx_len, int cap, float* o, float* lse,
-                      hipStream_t st);
+                      int64_t kv_stride, const int32_t* ctx_len, int cap, void* o,
+                      bool bf16_out, float* lse, hipStream_t st);
 
 // Block-level selection (blocks of `block` tokens, a power of two <= 64):
 // piece sums (pieces of min(block, 32) keys) in the selection region's list

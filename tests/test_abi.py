@@ -286,15 +286,18 @@ def test_block_selection_validation(lib):
 def test_swa_validation(lib):
     L = hs2.load()
 
-    def call(desc=None, q=FAKE, o=FAKE, lse=None, st=4096 * 128, cap=4096):
+    def call(desc=None, q=FAKE, o=FAKE, lse=None, st=4096 * 128, cap=4096, odt=hs2.HS2_F32):
         d = desc if desc is not None else hs2.make_desc(batch=1, n_heads=32, n_q=64, k_top=0,
                                                          window=128)
-        return L.hs2_swa_attention(ctypes.byref(d), q, FAKE, FAKE, st, FAKE, cap, o, lse, None)
+        return L.hs2_swa_attention(ctypes.byref(d), q, FAKE, FAKE, st, FAKE, cap, o, odt, lse,
+                                   None)
 
     mk = lambda **kw: hs2.make_desc(**dict(dict(batch=1, n_heads=32, n_q=64, k_top=0,  # noqa: E731
                                                 window=128), **kw))
-    assert L.hs2_swa_attention(None, FAKE, FAKE, FAKE, 4096 * 128, FAKE, 4096, FAKE, None,
+    assert L.hs2_swa_attention(None, FAKE, FAKE, FAKE, 4096 * 128, FAKE, 4096, FAKE, 0, None,
                                None) == hs2.HS2_EINVAL
+    assert call(odt=hs2.HS2_FP8_E4M3) == hs2.HS2_EINVAL
+    assert call(odt=9) == hs2.HS2_EINVAL
     assert call(desc=mk(window=0)) == hs2.HS2_EINVAL
     assert call(desc=mk(n_q=0)) == hs2.HS2_EINVAL
     assert call(desc=mk(sm_scale=-1.0)) == hs2.HS2_EINVAL

@@ -1,7 +1,8 @@
 """GPU parity of the self-decoder's sliding-window attention (hs2_swa_attention).
 
-Outputs are compared with the oracle's fp64 sliding-window attention on the
-same bf16 inputs (the bf16 output bar) and the log-sum-exp to 1e-5.  Shapes
+Outputs (fp32, and bf16 rounded) are compared with the oracle's fp64
+sliding-window attention on the same bf16 inputs (the bf16 output bar) and
+the log-sum-exp to 1e-5.  Shapes
 cover ragged query counts (not multiples of the 8 queries a workgroup
 takes), windows of one key, of 128 and wider than one 64-key tile, windows
 that cover the whole context (dense causal attention), padded heads, queries
@@ -26,7 +27,7 @@ def _say(msg):
     sys.stdout.flush()
 
 
-def _run(inp, w, n_q, window):
+def _run(inp, w, n_q, window, out="f32"):
     import kv_cache_reuse_hs2_amd as hs2
     from kv_cache_reuse_hs2_amd.torch_api import to_device
 
@@ -34,13 +35,14 @@ def _run(inp, w, n_q, window):
     cap = int(inp["capacity"])
     d = hs2.make_desc(batch=bsz, n_heads=w.n_heads, n_q=n_q, tile_q=1, k_top=0, window=window,
                       sm_scale=w.sm_scale)
-    o = torch.full((bsz, n_q, w.n_heads, 128), 7.0, dtype=torch.float32, device="cuda")
+    dt = torch.float32 if out == "f32" else torch.bfloat16
+    o = torch.full((bsz, n_q, w.n_heads, 128), 7.0, dtype=dt, device="cuda")
     lse = torch.full((bsz, n_q, w.n_heads), 7.0, dtype=torch.float32, device="cuda")
     hs2.hs2_swa_attention(d, to_device(inp["q_raw"]), to_device(inp["k_raw"]),
                           to_device(inp["v_raw"]), cap * 128, to_device(inp["ctx_len"]), cap, o,
-                          lse)
+                          hs2.HS2_F32 if out == "f32" else hs2.HS2_BF16, lse)
     torch.cuda.synchronize()
-    return o.cpu().numpy(), lse.cpu().numpy()
+    return o.float().cpu().numpy(), lse.cpu().numpy()
 
 
 CASES = [
@@ -55,12 +57,13 @@ CASES = [
 ]
 
 
+@pytest.mark.parametrize("out", ["f32", "bf16"])
 @pytest.mark.parametrize("name,bsz,heads,ctx,cap,n_q,window", CASES, ids=[c[0] for c in CASES])
-def test_swa_matches_oracle(hs2, name, bsz, heads, ctx, cap, n_q, window):
+def test_swa_matches_oracle(hs2, name, bsz, heads, ctx, cap, n_q, window, out):
     w = WORKLOADS["prefill_bf16_128k_8k"].replace(batch=bsz, n_heads=heads)
     inp = make_prefill_inputs(w, ctx_lens=ctx, n_q=n_q, capacity=cap)
-    _say(f"swa {name} ctx={ctx} n_q={n_q} window={window} H={heads}")
-    o, lse = _run(inp, w, n_q, window)
+    _say(f"swa {name} ctx={ctx} n_q={n_q} window={window} H={heads} out={out}")
+    o, lse = _run(inp, w, n_q, window, out)
     o_ref, lse_ref = oracle.swa_attention(inp["q"], inp["k"], inp["v"], inp["ctx_len"],
                                           window=window, sm_scale=w.sm_scale)
     assert_outputs_close(o, o_ref, "bf16")
@@ -73,14 +76,15 @@ def test_swa_matches_oracle(hs2, name, bsz, heads, ctx, cap, n_q, window):
         assert_outputs_close(o, o_d, "bf16")
 
 
-def test_swa_full_size_sampled(hs2):
+@pytest.mark.parametrize("out", ["f32", "bf16"])
+def test_swa_full_size_sampled(hs2, out):
     # 8,192 queries at positions 131,072.. of a 139,264-key cache, window 128;
     # the oracle evaluates a seeded sample of queries, each alone (one query
     # whose context ends at its own position).
     w = WORKLOADS["prefill_bf16_128k_8k"]
     inp = make_prefill_inputs(w)
-    _say(f"swa full size n_q={w.n_q} ctx={w.ctx_len}")
-    o, lse = _run(inp, w, w.n_q, 128)
+    _say(f"swa full size n_q={w.n_q} ctx={w.ctx_len} out={out}")
+    o, lse = _run(inp, w, w.n_q, 128, out)
     assert np.all(np.isfinite(o))
     rng = np.random.default_rng(70)
     sample = np.concatenate([[0, 1, 7, 8, w.n_q - 1], rng.choice(w.n_q, 27, replace=False)])
