@@ -12,6 +12,7 @@ from .hs2_oracle import (  # noqa: F401
     bf16_round,
     block_scores,
     bridge_kv,
+    bridge_kv_decode,
     dense_attention,
     dequant_kv,
     fp8_e4m3_value,

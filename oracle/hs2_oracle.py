@@ -77,6 +77,7 @@ __all__ = [
     "fp8_e4m3_value",
     "dequant_kv",
     "bridge_kv",
+    "bridge_kv_decode",
 ]
 
 
@@ -436,3 +437,27 @@ def bridge_kv(h, w_k, w_v, *, row_chunk: int = 8192):
         k_out[r0:r0 + row_chunk] = bf16_round(hc @ w_k)
         v_out[r0:r0 + row_chunk] = bf16_round(hc @ w_v)
     return k_out, v_out
+
+
+def bridge_kv_decode(h, w_k, w_v, pos, k_cache, v_cache):
+    """KV Bridging during decode: each sequence's new token gets its
+    cross-decoder K and V row from its self-decoder hidden state.
+
+    Prefill skips the cross-decoder, and the cross-decoder's full-attention
+    caches are built from self-decoder hidden states ([Origins] "The
+    Self-Decoder and Cross-Decoder Split"); a token generated later goes
+    through the self-decoder too, so its rows come from the same projection.
+    h: [B][d_model]; pos: int [B], the cache row of sequence b's token;
+    k_cache, v_cache: [B][cap][head_dim].  Returns copies of the caches with
+    row pos[b] of sequence b set to bridge_kv(h[b]); a pos outside [0, cap)
+    writes nothing.
+    """
+    k_new = np.array(k_cache, dtype=np.float64, copy=True)
+    v_new = np.array(v_cache, dtype=np.float64, copy=True)
+    k_rows, v_rows = bridge_kv(h, w_k, w_v)
+    cap = k_new.shape[1]
+    for b, p in enumerate(np.asarray(pos)):
+        if 0 <= int(p) < cap:
+            k_new[b, int(p)] = k_rows[b]
+            v_new[b, int(p)] = v_rows[b]
+    return k_new, v_new

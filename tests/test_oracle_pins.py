@@ -592,3 +592,25 @@ def test_swa_queries_before_the_cache_start_are_empty():
     o, lse = oracle.swa_attention(q, k, v, np.array([2]), window=3, sm_scale=1.0)
     assert np.all(o[0, :2] == 0) and np.all(np.isneginf(lse[0, :2]))
     assert np.all(o[0, 2:] == 1) and np.all(np.isfinite(lse[0, 2:]))
+
+
+def test_bridge_decode_writes_only_the_token_rows():
+    # Small integers: every product and sum is exact, so the rows are the
+    # integer products (all representable in bf16 here).
+    h = np.array([[1.0, 2.0, 0.0, -1.0], [0.0, 1.0, 1.0, 1.0], [3.0, 0.0, 0.0, 0.0]])
+    w_k = np.arange(8.0).reshape(4, 2)
+    w_v = -np.arange(8.0).reshape(4, 2)
+    k_cache = np.full((3, 5, 2), 9.0)
+    v_cache = np.full((3, 5, 2), -9.0)
+    k_new, v_new = oracle.bridge_kv_decode(h, w_k, w_v, np.array([4, 0, 5]), k_cache, v_cache)
+    assert k_new[0, 4].tolist() == [1 * 0 + 2 * 2 + 0 * 4 - 1 * 6, 1 * 1 + 2 * 3 + 0 * 5 - 1 * 7]
+    assert v_new[0, 4].tolist() == [2.0, 0.0]
+    assert k_new[1, 0].tolist() == [2 + 4 + 6, 3 + 5 + 7]
+    # sequence 2's position is past the cache: nothing written
+    assert np.array_equal(k_new[2], k_cache[2]) and np.array_equal(v_new[2], v_cache[2])
+    untouched = np.ones((3, 5), bool)
+    untouched[0, 4] = untouched[1, 0] = False
+    assert np.all(k_new[untouched] == 9.0) and np.all(v_new[untouched] == -9.0)
+    # the rows equal the bulk projection
+    k_rows, v_rows = oracle.bridge_kv(h, w_k, w_v)
+    assert np.array_equal(k_new[0, 4], k_rows[0]) and np.array_equal(v_new[1, 0], v_rows[1])
