@@ -309,6 +309,17 @@ def extra_measurements(steps: int, warmup: int) -> dict:
         "entry": "hs2_bridge_kv_packed (weights packed once)",
         "pack_weights_ms": round(ms_pack, 4),
         "hs2_bridge_kv_ms": round(ms_u, 4)}
+    # Decode-time bridging: one new token for each of 4 sequences, written at
+    # the end of their caches (the 1M-row K/V above serve as 4 caches of 256k).
+    n_seq, cap_d = 4, m_rows // 4
+    pos_d = torch.full((n_seq,), cap_d - 1, dtype=torch.int32, device="cuda")
+    ms_d = time_events(lambda: hs2.hs2_bridge_kv_decode(h, dm, wp, n_seq, dm, pos_d, k, v,
+                                                        cap_d * w.head_dim, cap_d),
+                       steps, warmup)
+    byts_d = 2 * dm * w.head_dim * 2 + n_seq * dm * 2 + 2 * n_seq * w.head_dim * 2
+    out["bridge_kv_decode_b4_x_2048"] = {
+        "us": round(ms_d * 1e3, 2), "hbm_GBps": round(byts_d / (ms_d * 1e-3) / 1e9, 1),
+        "entry": "hs2_bridge_kv_decode", "algorithmic_bytes": byts_d}
     del h
     q = torch.randn((1, 1, w.n_heads, w.head_dim), generator=g, device="cuda").to(torch.bfloat16)
     desc = hs2.make_desc(batch=1, n_heads=w.n_heads, k_top=w.k_top, window=w.window)

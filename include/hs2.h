@@ -314,6 +314,29 @@ HS2_API hs2_status hs2_bridge_kv_packed(const uint16_t* h, int64_t ldh, const ui
                                 uint16_t* k_out, uint16_t* v_out, int64_t ld_kv, int M,
                                 int d_model, int head_dim, hs2_stream_t stream);
 
+/*
+ * KV Bridging during decode.  A token generated after prefill also runs the
+ * self-decoder, and the cross-decoder's full-attention caches are projections
+ * of the self-decoder's hidden states ([Origins] "The Self-Decoder and
+ * Cross-Decoder Split"), so each sequence's new token gets its K and V rows
+ * from the same projection as in prefill:
+ *   k_cache[r][pos[r]][:] = bf16(h[r][:] . w_k),
+ *   v_cache[r][pos[r]][:] = bf16(h[r][:] . w_v)     for r < rows,
+ * with fp32 accumulation and one round-to-nearest-even.  h: bf16 [rows][d_model]
+ * (row stride ldh elements), row r being sequence r's new token; w_packed:
+ * weights packed by hs2_bridge_pack_weights for this d_model; pos: device
+ * int32 [rows], the cache row of each sequence's token (a value outside
+ * [0, kv_capacity) writes nothing for that sequence); k_cache, v_cache: bf16
+ * [rows][kv_capacity][head_dim] with sequence stride kv_stride elements.  Only
+ * those rows are written.  head_dim 128, d_model a positive multiple of 64
+ * (HS2_EUNSUPPORTED otherwise); ldh >= d_model and kv_stride >=
+ * kv_capacity * 128, both multiples of 8; pointers 16-byte aligned.
+ */
+HS2_API hs2_status hs2_bridge_kv_decode(const uint16_t* h, int64_t ldh, const uint16_t* w_packed,
+                                        int rows, int d_model, int head_dim, const int32_t* pos,
+                                        uint16_t* k_cache, uint16_t* v_cache, int64_t kv_stride,
+                                        int kv_capacity, hs2_stream_t stream);
+
 /* Static description of a status code. */
 HS2_API const char* hs2_status_string(hs2_status status);
 

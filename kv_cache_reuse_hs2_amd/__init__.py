@@ -39,6 +39,7 @@ EXPORTS = (
     "hs2_bridge_packed_bytes",
     "hs2_bridge_pack_weights",
     "hs2_bridge_kv_packed",
+    "hs2_bridge_kv_decode",
     "hs2_status_string",
 )
 
@@ -117,6 +118,9 @@ def load(path: str | None = None):
     lib.hs2_bridge_kv.argtypes = [_vp, _i64, _vp, _vp, _vp, _vp, _i64, _int, _int, _int, _vp]
     lib.hs2_bridge_kv_packed.argtypes = [_vp, _i64, _vp, _vp, _vp, _i64, _int, _int, _int, _vp]
     lib.hs2_bridge_kv_packed.restype = _int
+    lib.hs2_bridge_kv_decode.argtypes = [_vp, _i64, _vp, _int, _int, _int, _vp, _vp, _vp, _i64,
+                                         _int, _vp]
+    lib.hs2_bridge_kv_decode.restype = _int
     lib.hs2_bridge_kv.restype = _int
     lib.hs2_status_string.argtypes = [_int]
     lib.hs2_status_string.restype = ctypes.c_char_p
@@ -266,3 +270,11 @@ def hs2_bridge_kv_packed(h, ldh, w_packed, k_out, v_out, ld_kv, M, d_model, head
                                      int(ld_kv), int(M), int(d_model), int(head_dim),
                                      _stream(stream))
     _check(st, "hs2_bridge_kv_packed")
+
+
+def hs2_bridge_kv_decode(h, ldh, w_packed, rows, d_model, pos, k_cache, v_cache, kv_stride,
+                         kv_capacity, head_dim=128, stream=None) -> None:
+    st = load().hs2_bridge_kv_decode(_ptr(h), int(ldh), _ptr(w_packed), int(rows), int(d_model),
+                                     int(head_dim), _ptr(pos), _ptr(k_cache), _ptr(v_cache),
+                                     int(kv_stride), int(kv_capacity), _stream(stream))
+    _check(st, "hs2_bridge_kv_decode")

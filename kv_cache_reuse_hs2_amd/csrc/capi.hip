@@ -9,6 +9,9 @@ namespace hs2 {
 
 hipError_t launch_bridge_pack(const uint16_t* w_k, const uint16_t* w_v, uint16_t* w_packed,
                               int d_model, hipStream_t st);
+hipError_t launch_bridge_decode(const uint16_t* h, int64_t ldh, const uint16_t* w_packed,
+                                int rows, int d_model, const int32_t* pos, uint16_t* k_cache,
+                                uint16_t* v_cache, int64_t kv_stride, int cap, hipStream_t st);
 hipError_t launch_bridge(const uint16_t* h, int64_t ldh, const uint16_t* w_packed,
                          const uint16_t* w_k, const uint16_t* w_v, uint16_t* k_out,
                          uint16_t* v_out, int64_t ld_kv, int M, int d_model, hipStream_t st);
@@ -317,6 +320,26 @@ hs2_status hs2_decode_step_blocks(const hs2_attn_desc* desc, int block_size, con
                                           top_idx, top_cnt, o, lse, st));
   return launched(launch_sparse(*desc, q_sparse, k, v, kv_stride, ctx_len, kv_capacity, top_idx,
                                 top_cnt, o, lse, w + l.sparse, st));
+}
+
+hs2_status hs2_bridge_kv_decode(const uint16_t* h, int64_t ldh, const uint16_t* w_packed,
+                                int rows, int d_model, int head_dim, const int32_t* pos,
+                                uint16_t* k_cache, uint16_t* v_cache, int64_t kv_stride,
+                                int kv_capacity, hs2_stream_t stream) {
+  if (h == nullptr || w_packed == nullptr || pos == nullptr || k_cache == nullptr ||
+      v_cache == nullptr)
+    return HS2_EINVAL;
+  if (rows < 1 || d_model < 1 || head_dim < 1 || ldh < d_model || kv_capacity < 1)
+    return HS2_EINVAL;
+  if (head_dim != kHeadDim || d_model % 64 != 0) return HS2_EUNSUPPORTED;
+  if (kv_stride < (int64_t)kv_capacity * kHeadDim) return HS2_EINVAL;
+  if (ldh % 8 != 0 || kv_stride % 8 != 0) return HS2_EALIGN;
+  if (misaligned(h) || misaligned(w_packed) || misaligned(pos) || misaligned(k_cache) ||
+      misaligned(v_cache))
+    return HS2_EALIGN;
+  (void)hipGetLastError();
+  return launched(launch_bridge_decode(h, ldh, w_packed, rows, d_model, pos, k_cache, v_cache,
+                                       kv_stride, kv_capacity, static_cast<hipStream_t>(stream)));
 }
 
 hs2_status hs2_swa_attention(const hs2_attn_desc* desc, const void* q, const void* k,

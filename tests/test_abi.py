@@ -310,3 +310,24 @@ def test_swa_validation(lib):
     assert call(st=100) == hs2.HS2_EINVAL
     assert call(st=4096 * 128 + 4) == hs2.HS2_EALIGN
     assert call(lse=ODD) == hs2.HS2_EALIGN
+
+
+def test_bridge_decode_validation(lib):
+    L = hs2.load()
+
+    def call(h=FAKE, ldh=2048, wp=FAKE, rows=4, dm=2048, hd=128, pos=FAKE, kc=FAKE, st=300 * 128,
+             cap=300):
+        return L.hs2_bridge_kv_decode(h, ldh, wp, rows, dm, hd, pos, kc, FAKE, st, cap, None)
+
+    assert call(h=None) == hs2.HS2_EINVAL
+    assert call(wp=None) == hs2.HS2_EINVAL
+    assert call(pos=None) == hs2.HS2_EINVAL
+    assert call(rows=0) == hs2.HS2_EINVAL
+    assert call(ldh=1000) == hs2.HS2_EINVAL
+    assert call(cap=0) == hs2.HS2_EINVAL
+    assert call(st=100) == hs2.HS2_EINVAL
+    assert call(dm=96, ldh=96) == hs2.HS2_EUNSUPPORTED
+    assert call(hd=64) == hs2.HS2_EUNSUPPORTED
+    assert call(ldh=2052) == hs2.HS2_EALIGN
+    assert call(st=300 * 128 + 4) == hs2.HS2_EALIGN
+    assert call(kc=ODD) == hs2.HS2_EALIGN

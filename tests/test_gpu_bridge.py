@@ -80,3 +80,36 @@ def test_bridge_full_rows_sampled(hs2):
     rows = np.unique(np.concatenate([np.arange(256), np.arange(m - 256, m),
                                      rng.integers(0, m, 4096)]))
     _run(m, 2048, rows=rows)
+
+
+@pytest.mark.parametrize("n_seq,d_model", [(4, 2048), (37, 640), (1, 64)])
+def test_bridge_decode_rows(hs2, n_seq, d_model):
+    # One new token per sequence: its K and V rows land at pos[b]; positions
+    # outside the cache write nothing, and every other row is untouched.
+    from kv_cache_reuse_hs2_amd import hs2_bridge_kv_decode
+    from kv_cache_reuse_hs2_amd.torch_api import pack_bridge_weights, to_device
+
+    w = WORKLOADS["bridge_decode_bf16_1m"].replace(d_model=d_model)
+    inp = make_bridge_inputs(w, rows=n_seq)
+    cap = 300
+    rng = np.random.default_rng(80 + n_seq)
+    pos = rng.integers(0, cap, size=n_seq).astype(np.int32)
+    if n_seq > 2:
+        pos[1], pos[2] = -1, cap            # skipped
+    sentinel = 0x7F7F
+    kc = torch.full((n_seq, cap, 128), sentinel, dtype=torch.int16, device="cuda")
+    vc = torch.full((n_seq, cap, 128), sentinel, dtype=torch.int16, device="cuda")
+    wk, wv = to_device(inp["w_k_raw"]), to_device(inp["w_v_raw"])
+    wp = pack_bridge_weights(wk, wv, d_model)
+    print(f"[gpu] bridge decode B={n_seq} d_model={d_model}", flush=True)
+    hs2_bridge_kv_decode(to_device(inp["h_raw"]), d_model, wp, n_seq, d_model, to_device(pos),
+                         kc, vc, cap * 128, cap)
+    torch.cuda.synchronize()
+    kb = kc.cpu().numpy().view(np.uint16)
+    vb = vc.cpu().numpy().view(np.uint16)
+    live = np.array([0 <= p < cap for p in pos])
+    rows = np.nonzero(live)[0]
+    _check_rows(kb[rows, pos[rows]], vb[rows, pos[rows]], inp, rows)
+    mask = np.ones((n_seq, cap), bool)
+    mask[rows, pos[rows]] = False
+    assert np.all(kb[mask] == sentinel) and np.all(vb[mask] == sentinel)
