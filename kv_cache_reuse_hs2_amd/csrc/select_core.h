@@ -186,8 +186,8 @@ __device__ int final_select_row(int r, const RowGeom& g, int k_top,
   // Everything that does not depend on another load is fetched at once: the
   // threshold bin b0 that sel_filter found, the second-level histogram (bins
   // kBinsPer t .. kBinsPer t + kBinsPer - 1 per thread), the slice counts,
-  // and the head of each slice list this wave will copy (slices
-  // wave + kWaves u, entries 0..63).
+  // and the head of each slice list this wave will copy first (slices
+  // wave + kWaves u for u < kHeads, entries 0..63).
   const uint32_t* hrow = hist + (size_t)r * kHistRow;
   uint32_t v2[kBinsPer];
 #pragma unroll
@@ -199,9 +199,10 @@ __device__ int final_select_row(int r, const RowGeom& g, int k_top,
     v2[i + 3] = x2.w;
   }
   const uint32_t b0 = meta[4 * r], above0 = meta[4 * r + 1];
-  uint2 head[4];
+  constexpr int kHeads = 8;
+  uint2 head[kHeads];
 #pragma unroll
-  for (int u = 0; u < 4; ++u) {
+  for (int u = 0; u < kHeads; ++u) {
     const int sl = wave + kWaves * u;
     if (sl < ns) head[u] = lr[(size_t)sl * kSelSlice + lane];
   }
@@ -243,26 +244,27 @@ __device__ int final_select_row(int r, const RowGeom& g, int k_top,
   };
   // The list is read twice more: keep it in LDS when it fits (the usual
   // case: keys above the threshold bin plus that bin).  Each wave copies
-  // whole slices, four at a time so that their loads overlap, and counts key
-  // bits 7..0 of the candidates that match the top 24 bits on the way.
+  // whole slices, kHeads at a time so that their loads overlap (the first
+  // kHeads from the heads loaded above), and counts key bits 7..0 of the
+  // candidates that match the top 24 bits on the way.
   const bool staged = total <= (uint32_t)kStage;
   auto put = [&](uint32_t pos, uint2 e) {
     stage[pos] = e;
     if ((e.x >> 8) == top24) atomicAdd(&h[e.x & 0xFFu], 1u);
   };
   if (staged) {
-    for (int sl0 = wave; sl0 < ns; sl0 += 4 * kWaves) {
-      uint2 e[4];
-      uint32_t n[4];
+    for (int sl0 = wave; sl0 < ns; sl0 += kHeads * kWaves) {
+      uint2 e[kHeads];
+      uint32_t n[kHeads];
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
+      for (int u = 0; u < kHeads; ++u) {
         const int sl = sl0 + kWaves * u;
         n[u] = sl < ns ? pre[sl + 1] - pre[sl] : 0u;
         if (sl0 == wave) e[u] = head[u];
         else if ((uint32_t)lane < n[u]) e[u] = lr[(size_t)sl * kSelSlice + lane];
       }
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
+      for (int u = 0; u < kHeads; ++u) {
         const int sl = sl0 + kWaves * u;
         if ((uint32_t)lane < n[u]) put(pre[sl] + lane, e[u]);
         for (uint32_t i = 64 + lane; i < n[u]; i += 64) put(pre[sl] + i, lr[(size_t)sl * kSelSlice + i]);
@@ -340,21 +342,31 @@ __device__ int final_select_row(int r, const RowGeom& g, int k_top,
       if (ch < nchunks && lane == 0) chunk_wins[ch] = (uint32_t)__popcll(mask[u]);
     }
     __syncthreads();
-    // Winners of all chunks, and of the chunks before each of this wave's.
-    uint32_t all = 0;
-    for (int c0 = 0; c0 < nchunks; c0 += 64) all += (c0 + lane < nchunks) ? chunk_wins[c0 + lane] : 0u;
+    // Winners of the chunks before each chunk: one wave scans the counts in
+    // place (res[0] gets the total; the earlier results there are consumed).
+    if (wave == 0) {
+      uint32_t carry = 0;
+      for (int c0 = 0; c0 < nchunks; c0 += 64) {
+        const uint32_t c = (c0 + lane < nchunks) ? chunk_wins[c0 + lane] : 0u;
+        uint32_t incl = c;
 #pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) all += __shfl_xor(all, off);
-    base = all;
+        for (int off = 1; off < 64; off <<= 1) {
+          const uint32_t o = __shfl_up(incl, off);
+          if (lane >= off) incl += o;
+        }
+        if (c0 + lane < nchunks) chunk_wins[c0 + lane] = carry + incl - c;
+        carry += __shfl(incl, 63);
+      }
+      if (lane == 0) res_b[0] = carry;
+    }
+    __syncthreads();
+    base = res_b[0];
     const uint64_t lower = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
 #pragma unroll
     for (int u = 0; u < kStage / 64 / kWaves; ++u) {
       const int ch = wave + kWaves * u;
       if (ch >= nchunks) break;
-      uint32_t before = 0;
-      for (int c0 = 0; c0 < ch; c0 += 64) before += (c0 + lane < ch) ? chunk_wins[c0 + lane] : 0u;
-#pragma unroll
-      for (int off = 32; off >= 1; off >>= 1) before += __shfl_xor(before, off);
+      const uint32_t before = chunk_wins[ch];
       if ((mask[u] >> lane) & 1ull) {
         const uint32_t pos = before + (uint32_t)__popcll(mask[u] & lower);
         if (pos < (uint32_t)k_top) {
