@@ -491,6 +491,8 @@ __global__ __launch_bounds__(256) void sparse_partial_f32(
 }
 
 // ---------------------------------------------------------------------------
+constexpr int kCombRegs = 32;  // segments sparse_combine holds in registers
+
 // Merge the segment partials of one (query, head): o = v_scale * sum_s
 // 2^(m_s-M) o_s / sum_s 2^(m_s-M) l_s, segments taken in order (v_scale is
 // the V cache scale of E4M3 caches, else 1).  One workgroup per (query, head),
@@ -503,23 +505,46 @@ __global__ __launch_bounds__(kHeadDim) void sparse_combine(const float* __restri
   const int h = blockIdx.x, bq = blockIdx.y, d = threadIdx.x;
   const float2* mlq = ml + (size_t)bq * nseg * H + h;
   const float* pq = part + ((size_t)bq * nseg * H + h) * kHeadDim + d;
-  float M = -INFINITY;
-  for (int s = 0; s < nseg; ++s) {
-    const float2 x = mlq[(size_t)s * H];
-    if (x.y > 0.f) M = fmaxf(M, x.x);
-  }
-  // Loads are unconditional so that they can be issued together; a segment
-  // with no keys (l == 0) has no partial output written, and is masked by a
-  // select, never multiplied (its memory may hold anything).
-  float den = 0.f, num = 0.f;
+  // A segment with no keys (l == 0) has no partial output written, and is
+  // masked by a select, never multiplied (its memory may hold anything).
+  float den = 0.f, num = 0.f, M = -INFINITY;
+  if (nseg <= kCombRegs) {
+    // Every load at once (one memory round trip), then the same arithmetic
+    // as the loop below.
+    float2 x[kCombRegs];
+    float pv[kCombRegs];
+#pragma unroll
+    for (int s = 0; s < kCombRegs; ++s)
+      if (s < nseg) {
+        x[s] = mlq[(size_t)s * H];
+        pv[s] = pq[(size_t)s * H * kHeadDim];
+      }
+#pragma unroll
+    for (int s = 0; s < kCombRegs; ++s)
+      if (s < nseg && x[s].y > 0.f) M = fmaxf(M, x[s].x);
+#pragma unroll
+    for (int s = 0; s < kCombRegs; ++s)
+      if (s < nseg) {
+        const bool live = x[s].y > 0.f;
+        const float w = live ? fast_exp2(x[s].x - M) : 0.f;
+        den = fmaf(w, live ? x[s].y : 0.f, den);
+        num = live ? fmaf(w, pv[s], num) : num;
+      }
+  } else {
+    for (int s = 0; s < nseg; ++s) {
+      const float2 x = mlq[(size_t)s * H];
+      if (x.y > 0.f) M = fmaxf(M, x.x);
+    }
+    // Loads are unconditional so that they can be issued together.
 #pragma unroll 8
-  for (int s = 0; s < nseg; ++s) {
-    const float2 x = mlq[(size_t)s * H];
-    const float pv = pq[(size_t)s * H * kHeadDim];
-    const bool live = x.y > 0.f;
-    const float w = live ? fast_exp2(x.x - M) : 0.f;
-    den = fmaf(w, live ? x.y : 0.f, den);
-    num = live ? fmaf(w, pv, num) : num;
+    for (int s = 0; s < nseg; ++s) {
+      const float2 x = mlq[(size_t)s * H];
+      const float pv = pq[(size_t)s * H * kHeadDim];
+      const bool live = x.y > 0.f;
+      const float w = live ? fast_exp2(x.x - M) : 0.f;
+      den = fmaf(w, live ? x.y : 0.f, den);
+      num = live ? fmaf(w, pv, num) : num;
+    }
   }
   o[((size_t)bq * H + h) * kHeadDim + d] = den > 0.f ? num / den * v_scale : 0.f;
   if (lse != nullptr && d == 0)
