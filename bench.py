@@ -244,6 +244,48 @@ def fp8_measurements(steps: int, warmup: int) -> dict:
             "note": "K and V as E4M3 bytes with one fp32 scale each, bf16 queries"}
 
 
+def full_output_measurements(steps: int, warmup: int) -> dict:
+    """The full-attention layer itself on the headline shape: the scoring call
+    that also writes the layer's own output o_full (K streamed twice, V once),
+    timed per call beside the scoring call without it."""
+    import numpy as np
+    import torch
+
+    from kv_cache_reuse_hs2_amd.torch_api import make_buffers, run_scores, run_scores_full
+    from workloads import WORKLOADS, make_decode_inputs
+
+    w = WORKLOADS["decode_bf16_256k_b4"]
+    buf = make_buffers(make_decode_inputs(w), n_heads=w.n_heads, k_top=w.k_top, window=w.window,
+                       sm_scale=w.sm_scale, dtype=w.dtype)
+    o_full = torch.empty((w.batch, w.n_heads, w.head_dim), dtype=torch.float32, device="cuda")
+    stream = torch.cuda.current_stream()
+    fns = {"scores": lambda: run_scores(buf), "scores_and_o_full": lambda: run_scores_full(buf, o_full)}
+    for _ in range(warmup):
+        for fn in fns.values():
+            fn()
+    ev = {k: [] for k in fns}
+    for _ in range(steps):
+        for name, fn in fns.items():
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            fn()
+            e1.record(stream)
+            ev[name].append((e0, e1))
+    torch.cuda.synchronize()
+    ms = {k: float(np.mean([a.elapsed_time(b) for a, b in v])) for k, v in ev.items()}
+    row = w.head_dim * 2
+    kv_once = 2 * w.batch * w.ctx_len * row + w.batch * w.ctx_len * 4   # K, V, scores
+    moved = 3 * w.batch * w.ctx_len * row + w.batch * w.ctx_len * 4     # K twice, V once
+    t = ms["scores_and_o_full"] * 1e-3
+    return {"scores_us": round(ms["scores"] * 1e3, 2),
+            "scores_and_o_full_us": round(ms["scores_and_o_full"] * 1e3, 2),
+            "bytes_moved_GBps": round(moved / t / 1e9, 1),
+            "bytes_moved_frac": round(moved / t / 1e9 / HBM_PEAK_GBS, 4),
+            "kv_once_GBps": round(kv_once / t / 1e9, 1),
+            "note": "bytes_moved counts K twice and V once (what the kernels read); kv_once "
+                    "counts K and V once, the least a full layer can read"}
+
+
 def extra_measurements(steps: int, warmup: int) -> dict:
     """The other shapes of the method, measured the same way (not the headline):
     batched decode at 64k, chunked prefill of 8,192 queries on a 131,072-token
@@ -546,6 +588,8 @@ def main() -> int:
         out["extras"]["decode_bf16_256k_b4_block_vs_token"] = block_measurements(args.steps,
                                                                                  args.warmup)
         out["extras"]["swa_bf16_prefill_8k_w128"] = swa_measurements(args.steps, args.warmup)
+        out["extras"]["decode_bf16_256k_b4_full_layer"] = full_output_measurements(args.steps,
+                                                                                  args.warmup)
     if args.calibrate:
         src = torch.empty(256 * MIB, dtype=torch.uint8, device="cuda").fill_(1)
         dst = torch.empty_like(src)

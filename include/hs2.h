@@ -123,8 +123,13 @@ HS2_API size_t hs2_workspace_size(const hs2_attn_desc* desc, int kv_capacity);
  *   scores[b][g][j] = sum over queries i in g, heads h of p_ihj,   j < ctx_len[b]
  * where p_ihj = exp(s_ihj - lse_ih), s_ihj = sm_scale * q_ih . k_j, is query
  * i's softmax probability over its causal range 0..P_i (0 for j > P_i).
- * Entries j >= ctx_len[b] are not written.  Optional outputs: o_full, the
- * full layer's own attention output sum_j p_ihj v_j (needs v), and lse.
+ * Entries j >= ctx_len[b] are not written.  Optional outputs: lse, and
+ * o_full, the full layer's own attention output, fp32 [B][n_heads][128]:
+ *   o_full[b][h][:] = sum_j p_hj v_j      (times v_scale for E4M3 caches).
+ * o_full needs v (HS2_EINVAL without it) and is implemented for decode
+ * (tile_q = 1) with bf16 or E4M3 caches (HS2_EUNSUPPORTED otherwise); the
+ * second K pass then also streams V, and the scores are summed over heads in
+ * a different order than without o_full (same values up to rounding).
  * v may be NULL when o_full is NULL.
  */
 HS2_API hs2_status hs2_full_attn_scores(const hs2_attn_desc* desc, const void* q,

@@ -127,15 +127,20 @@ hs2_status hs2_full_attn_scores(const hs2_attn_desc* desc, const void* q, const 
   if (q == nullptr || k == nullptr || ctx_len == nullptr || scores == nullptr) return HS2_EINVAL;
   if (o_full != nullptr) {
     if (v == nullptr) return HS2_EINVAL;
-    return HS2_EUNSUPPORTED;  // the decode scorer streams K only
+    // The full layer's own output: decode on the MFMA paths.
+    if (is_prefill(*desc) || desc->dtype == HS2_F32) return HS2_EUNSUPPORTED;
   }
   if ((s = check_cache(desc, kv_stride, kv_capacity)) != HS2_OK) return s;
   if (misaligned(q) || misaligned(k) || misaligned(v) || misaligned(ctx_len) ||
-      misaligned(scores) || misaligned(lse))
+      misaligned(scores) || misaligned(o_full) || misaligned(lse))
     return HS2_EALIGN;
   if ((s = check_ws(*desc, kv_capacity, ws, ws_bytes)) != HS2_OK) return s;
   (void)hipGetLastError();
   const WsLayout l = ws_layout(*desc, kv_capacity);
+  if (o_full != nullptr)
+    return launched(launch_score_full(*desc, q, k, v, kv_stride, ctx_len, kv_capacity, scores,
+                                      o_full, lse, static_cast<char*>(ws) + l.score,
+                                      static_cast<hipStream_t>(stream)));
   if (is_prefill(*desc))
     return launched(launch_prefill_scores(*desc, q, k, kv_stride, ctx_len, kv_capacity, scores,
                                           lse, static_cast<char*>(ws) + l.score, false,

@@ -59,6 +59,15 @@ __device__ __forceinline__ int clamp_ctx(const int32_t* ctx_len, int b, int cap)
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// Orders one wave's LDS writes before its later LDS reads by other lanes (and
+// those reads before later writes).  The hardware keeps a wave's LDS accesses
+// in order; the fences only stop the compiler from moving them.
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
@@ -112,6 +121,7 @@ struct ScoreWs {
   size_t stats_off;  // float2 [B][nchunks1][32]  (max, sum) per chunk & head, base 2
   size_t lse2_off;   // float  [B][32]             per-head log2-sum-exp (fp32 path)
   size_t hist_off;   // uint32 [B][kHistRow]       selector histograms (fused step)
+  size_t opart_off;  // float  [B][nchunks2][32][128] full-output partials per chunk
   size_t bytes;
 };
 
@@ -161,6 +171,9 @@ inline ScoreWs score_ws(const hs2_attn_desc& d, int cap) {
   off = align_up(off + sizeof(float) * (size_t)d.batch * d.n_q * kMaxHeads, 256);
   w.hist_off = off;
   off = align_up(off + sizeof(uint32_t) * (size_t)d.batch * kHistRow, 256);
+  w.opart_off = off;
+  off = align_up(off + sizeof(float) * (size_t)d.batch * ((cap + kP2Chunk - 1) / kP2Chunk) *
+                           kMaxHeads * kHeadDim, 256);
   w.bytes = off;
   return w;
 }
@@ -219,6 +232,13 @@ inline WsLayout ws_layout(const hs2_attn_desc& d, int cap) {
 // ---------------------------------------------------------------------------
 // Kernel launchers (each returns hipGetLastError() of its launches).  `ws`
 // points at the launcher's own region.
+
+// Decode scoring with the full layer's own output (MFMA paths): the
+// importance as launch_score_decode writes it (to within rounding) and
+// o_full[b][h][:] = sum_j p_hj v_j, also streaming V.
+hipError_t launch_score_full(const hs2_attn_desc& d, const void* q, const void* k, const void* v,
+                             int64_t kv_stride, const int32_t* ctx_len, int cap, float* scores,
+                             float* o_full, float* lse, char* ws, hipStream_t st);
 
 // Piece sums of the pool scores for the block-level selector: out[r][m] =
 // fp32 pairwise sum of the scores of keys [m*piece, (m+1)*piece) of row r

@@ -124,21 +124,19 @@ __global__ __launch_bounds__(64 * kP1Waves) void score_p1_bf16(
 
   float m_run = -INFINITY, l_run = 0.f;
   int j0 = j_begin + 32 * wave;
-  u32x4 kr[k_regs<kFp8>()], kn[k_regs<kFp8>()];
-  if (j0 < j_end) load_k_block<kFp8>(kb, min(j0 + r32, N - 1), hh, kr);
-  while (j0 < j_end) {
-    const int jn = j0 + 32 * kP1Waves;
-    if (jn < j_end) load_k_block<kFp8>(kb, min(jn + r32, N - 1), hh, kn);
+  u32x4 ka[k_regs<kFp8>()], kn[k_regs<kFp8>()];
+  if (j0 < j_end) load_k_block<kFp8>(kb, min(j0 + r32, N - 1), hh, ka);
+  auto block = [&](const u32x4 (&kc)[k_regs<kFp8>()], const int jb) {
     f32x16_t acc = {};
 #pragma unroll
     for (int i = 0; i < 8; ++i)
-      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k_operand<kFp8>(kr, i), qreg[i], acc, 0, 0, 0);
-    // acc[r] = logit of key j0 + 8*(r/4) + 4*hh + r%4 for head r32.
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k_operand<kFp8>(kc, i), qreg[i], acc, 0, 0, 0);
+    // acc[r] = logit of key jb + 8*(r/4) + 4*hh + r%4 for head r32.
     float x[16];
     float bm = -INFINITY;
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      const int j = j0 + 8 * (r >> 2) + 4 * hh + (r & 3);
+      const int j = jb + 8 * (r >> 2) + 4 * hh + (r & 3);
       x[r] = (j < j_end) ? acc[r] * c2 : -INFINITY;
       bm = fmaxf(bm, x[r]);
     }
@@ -149,9 +147,24 @@ __global__ __launch_bounds__(64 * kP1Waves) void score_p1_bf16(
     for (int r = 0; r < 16; ++r) s += fast_exp2(x[r] - mref);
     l_run = s;
     m_run = m_new;
-#pragma unroll
-    for (int i = 0; i < k_regs<kFp8>(); ++i) kr[i] = kn[i];
-    j0 = jn;
+  };
+  // Two register sets used in turn, so the next block's loads stay in flight
+  // while the current block is computed.  The loads are unconditional (past
+  // the end they repeat the current block, which the cache still holds): a
+  // load under a branch, or a copy between the sets, makes the compiler wait
+  // for every load in flight before the next MFMA.
+  constexpr int kStep = 32 * kP1Waves;
+  while (j0 < j_end) {
+    const int j1 = j0 + kStep;
+    load_k_block<kFp8>(kb, min((j1 < j_end ? j1 : j0) + r32, N - 1), hh, kn);
+    __builtin_amdgcn_sched_barrier(0);  // issue the loads before the wait below
+    block(ka, j0);
+    if (j1 >= j_end) break;
+    const int j2 = j1 + kStep;
+    load_k_block<kFp8>(kb, min((j2 < j_end ? j2 : j1) + r32, N - 1), hh, ka);
+    __builtin_amdgcn_sched_barrier(0);
+    block(kn, j1);
+    j0 = j2;
   }
   // Lanes r32 and r32+32 hold the same head over different keys.
   merge_ml(m_run, l_run, __shfl_xor(m_run, 32), __shfl_xor(l_run, 32));
@@ -194,8 +207,8 @@ __global__ __launch_bounds__(64 * kP2Waves) void score_p2_bf16(
 
   // Start the K stream before folding the statistics.
   int j0 = j_begin + 32 * wave;
-  u32x4 kr[k_regs<kFp8>()], kn[k_regs<kFp8>()];
-  if (j0 < j_end) load_k_block<kFp8>(kb, min(j0 + r32, N - 1), hh, kr);
+  u32x4 ka[k_regs<kFp8>()], kn[k_regs<kFp8>()];
+  if (j0 < j_end) load_k_block<kFp8>(kb, min(j0 + r32, N - 1), hh, ka);
   bf16x8_t qreg[8];
   load_q_bf16<kFp8>(q + (size_t)b * H * kHeadDim, H, r32, hh, qreg);
 
@@ -233,19 +246,17 @@ __global__ __launch_bounds__(64 * kP2Waves) void score_p2_bf16(
   float* out = scores + (size_t)b * score_stride;
   const int pe = N - window;  // decode pool end (keys below it are histogrammed)
 
-  while (j0 < j_end) {
-    const int jn = j0 + 32 * kP2Waves;
-    if (jn < j_end) load_k_block<kFp8>(kb, min(jn + r32, N - 1), hh, kn);
+  auto block = [&](const u32x4 (&kc)[k_regs<kFp8>()], const int jb) {
     f32x16_t acc = {};
 #pragma unroll
     for (int i = 0; i < 8; ++i)
-      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qreg[i], k_operand<kFp8>(kr, i), acc, 0, 0, 0);
-    // acc[r] = logit of head 8*(r/4) + 4*hh + r%4 for key j0 + r32.
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qreg[i], k_operand<kFp8>(kc, i), acc, 0, 0, 0);
+    // acc[r] = logit of head 8*(r/4) + 4*hh + r%4 for key jb + r32.
     float imp = 0.f;
 #pragma unroll
     for (int r = 0; r < 16; ++r) imp += fast_exp2(acc[r] * c2 - L[r]);
     imp += __shfl_xor(imp, 32);
-    const int j = j0 + r32;
+    const int j = jb + r32;
     if (hh == 0 && j < j_end) {
       out[j] = imp;
       if (kHist && j < pe) atomicAdd(&s_hist[order_key(imp) >> 20], 1u);
@@ -256,15 +267,248 @@ __global__ __launch_bounds__(64 * kP2Waves) void score_p2_bf16(
       if (hh == 0 && (r32 & (piece - 1)) == 0 && j < pe)
         pieces[(size_t)b * piece_stride + j / piece] = x;
     }
-#pragma unroll
-    for (int i = 0; i < k_regs<kFp8>(); ++i) kr[i] = kn[i];
-    j0 = jn;
+  };
+  // Two register sets used in turn, with unconditional loads, as in pass 1.
+  constexpr int kStep = 32 * kP2Waves;
+  while (j0 < j_end) {
+    const int j1 = j0 + kStep;
+    load_k_block<kFp8>(kb, min((j1 < j_end ? j1 : j0) + r32, N - 1), hh, kn);
+    __builtin_amdgcn_sched_barrier(0);  // issue the loads before the wait below
+    block(ka, j0);
+    if (j1 >= j_end) break;
+    const int j2 = j1 + kStep;
+    load_k_block<kFp8>(kb, min((j2 < j_end ? j2 : j1) + r32, N - 1), hh, ka);
+    __builtin_amdgcn_sched_barrier(0);
+    block(kn, j1);
+    j0 = j2;
   }
   if (kHist) {
     __syncthreads();
     uint32_t* gh = hist + (size_t)b * kHistRow;
     for (int i = threadIdx.x; i < kSelBins; i += blockDim.x)
       if (s_hist[i] != 0u) atomicAdd(&gh[i], s_hist[i]);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Pass 2 with the full layer's own output: besides I[j], each workgroup adds
+// p_hj v_j over its 4,096 keys into a partial O, and full_out_combine sums the
+// partials of a sequence in chunk order (p_hj = 2^(x_hj - L_h) is already
+// normalised, so partials simply add).  Here K is the A operand, so a lane
+// holds one head over 16 keys: O is accumulated transposed, O^T += V^T P^T,
+// with P as bf16 high and low parts and V transposed through the wave's LDS
+// tile; the importance (a sum over heads, i.e. over lanes) goes through a
+// 32 x 32 transpose in LDS.
+constexpr int kFullVt = 40;  // bf16 per transposed V row (32 keys + pad)
+
+struct FullLds {
+  float2 red[kP2Waves * 2][32];
+  float s_L[32];
+  union {
+    struct {
+      uint16_t vt[kP2Waves][kHeadDim][kFullVt];
+      float pt[kP2Waves][32][33];
+    } loop;
+    float merge[kP2Waves / 2][32][kHeadDim + 4];
+  } u;
+};
+
+// V rows are read like K rows (load_k_block: each load instruction covers 32
+// B of 32 rows); group e of the lane's values, widened to bf16, holds dims
+// step_dim(e, hh) .. +8.
+template <bool kFp8>
+__device__ __forceinline__ u32x4 v_dims8(const u32x4 (&vr)[k_regs<kFp8>()], int e) {
+  if constexpr (kFp8)
+    return e4m3x8_to_bf16x8(vr[e >> 1][2 * (e & 1)], vr[e >> 1][2 * (e & 1) + 1]);
+  else
+    return vr[e];
+}
+
+template <bool kFp8>
+__global__ __launch_bounds__(64 * kP2Waves) void score_p2_full(
+    const uint16_t* __restrict__ q, const void* __restrict__ k, const void* __restrict__ v,
+    int64_t kv_stride, const int32_t* __restrict__ ctx_len, int cap, int H, float c2,
+    const float2* __restrict__ stats, int nchunks1, float* __restrict__ scores,
+    int64_t score_stride, float* __restrict__ lse_out, float* __restrict__ o_part,
+    int nchunks2) {
+  __shared__ __attribute__((aligned(16))) FullLds S;
+  const int b = gridDim.y - 1 - blockIdx.y;
+  const int c = gridDim.x - 1 - blockIdx.x;
+  const int N = clamp_ctx(ctx_len, b, cap);
+  const int j_begin = c * kP2Chunk;
+  if (j_begin >= N) {
+    if (lse_out != nullptr && c == 0 && threadIdx.x < H) lse_out[b * H + threadIdx.x] = -INFINITY;
+    return;
+  }
+  const int j_end = min(N, j_begin + kP2Chunk);
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int r32 = lane & 31, hh = lane >> 5;
+  const size_t seq = (size_t)b * kv_stride * kv_elem_bytes<kFp8>();
+  const char* kb = static_cast<const char*>(k) + seq;
+  const char* vb = static_cast<const char*>(v) + seq;
+
+  int j0 = j_begin + 32 * wave;
+  u32x4 kr[k_regs<kFp8>()], vr[k_regs<kFp8>()];
+  if (j0 < j_end) {
+    load_k_block<kFp8>(kb, min(j0 + r32, N - 1), hh, kr);
+    load_k_block<kFp8>(vb, min(j0 + r32, N - 1), hh, vr);
+  }
+  bf16x8_t qreg[8];
+  load_q_bf16<kFp8>(q + (size_t)b * H * kHeadDim, H, r32, hh, qreg);
+  {
+    constexpr int kParts = kP2Waves * 2;
+    const int h = threadIdx.x & 31, part = threadIdx.x >> 5;
+    const int nc = (N + kP1Chunk - 1) / kP1Chunk;
+    const float2* sb = stats + (size_t)b * nchunks1 * kMaxHeads;
+    float m = -INFINITY, l = 0.f;
+    for (int cc = part; cc < nc; cc += kParts) {
+      const float2 x = sb[(size_t)cc * kMaxHeads + h];
+      merge_ml(m, l, x.x, x.y);
+    }
+    S.red[part][h] = make_float2(m, l);
+    __syncthreads();
+    if (threadIdx.x < 32) {
+      m = S.red[0][h].x;
+      l = S.red[0][h].y;
+#pragma unroll
+      for (int p = 1; p < kParts; ++p) merge_ml(m, l, S.red[p][h].x, S.red[p][h].y);
+      const float L = (l > 0.f) ? m + log2f(l) : -INFINITY;
+      S.s_L[h] = (h < H) ? L : INFINITY;  // padded heads get p = 0
+      if (lse_out != nullptr && c == 0 && h < H) lse_out[b * H + h] = L * 0.69314718055994531f;
+    }
+    __syncthreads();
+  }
+  const float Lh = S.s_L[r32];
+  float* out = scores + (size_t)b * score_stride;
+  f32x16_t o[4] = {{}, {}, {}, {}};  // O^T: dims 32t + 8(r/4) + 4hh + r%4, head r32
+  float (*pt)[33] = S.u.loop.pt[wave];
+  uint16_t (*vt)[kFullVt] = S.u.loop.vt[wave];
+  // Each wave's next block is loaded into the same registers as soon as the
+  // QK^T MFMAs and the V transpose have consumed them, so the loads are in
+  // flight during the rest of the block's work.
+  while (j0 < j_end) {
+    const int jn = j0 + 32 * kP2Waves;
+    f32x16_t acc = {};
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k_operand<kFp8>(kr, i), qreg[i], acc, 0, 0,
+                                                    0);
+    // V transposed: vt[d][key r32], d = step_dim(e, hh) + 2j (+ 1).
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const u32x4 x = v_dims8<kFp8>(vr, e);
+      const int d0 = step_dim<kFp8>(e, hh);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        vt[d0 + 2 * j][r32] = (uint16_t)(x[j] & 0xFFFFu);
+        vt[d0 + 2 * j + 1][r32] = (uint16_t)(x[j] >> 16);
+      }
+    }
+    if (jn < j_end) {
+      load_k_block<kFp8>(kb, min(jn + r32, N - 1), hh, kr);
+      load_k_block<kFp8>(vb, min(jn + r32, N - 1), hh, vr);
+    }
+    // acc[r]: head r32, key j0 + 8(r/4) + 4hh + r%4.
+    float p[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int kk = 8 * (r >> 2) + 4 * hh + (r & 3);
+      p[r] = (j0 + kk < j_end) ? fast_exp2(acc[r] * c2 - Lh) : 0.f;
+      pt[r32][kk] = p[r];
+    }
+    wave_lds_sync();  // the two tiles are this wave's alone
+    // I[j] = sum over heads: lane (key r32, half hh) adds heads 16hh .. 16hh + 15.
+    float imp = 0.f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) imp += pt[16 * hh + i][r32];
+    imp += __shfl_xor(imp, 32);
+    if (hh == 0 && j0 + r32 < j_end) out[j0 + r32] = imp;
+    // O^T += V^T P^T; step s takes the keys of registers 8s..8s+7.
+#pragma unroll
+    for (int sp = 0; sp < 2; ++sp) {
+      u32x4 phi, plo;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const float p0 = p[8 * sp + 2 * j], p1 = p[8 * sp + 2 * j + 1];
+        const uint16_t h0 = f32_to_bf16_rne(p0), h1 = f32_to_bf16_rne(p1);
+        const uint16_t l0 = f32_to_bf16_rne(p0 - bf16_to_f32(h0));
+        const uint16_t l1 = f32_to_bf16_rne(p1 - bf16_to_f32(h1));
+        phi[j] = (uint32_t)h0 | ((uint32_t)h1 << 16);
+        plo[j] = (uint32_t)l0 | ((uint32_t)l1 << 16);
+      }
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const uint16_t* vrow = &vt[32 * t + r32][0];
+        const uint2 lo4 = *reinterpret_cast<const uint2*>(vrow + 16 * sp + 4 * hh);
+        const uint2 hi4 = *reinterpret_cast<const uint2*>(vrow + 16 * sp + 8 + 4 * hh);
+        const u32x4 av = {lo4.x, lo4.y, hi4.x, hi4.y};
+        o[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(av), as_bf16x8(phi), o[t], 0,
+                                                       0, 0);
+        o[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(av), as_bf16x8(plo), o[t], 0,
+                                                       0, 0);
+      }
+    }
+    wave_lds_sync();  // reads above before the next block's writes
+    j0 = jn;
+  }
+  // The 8 waves' partials, added in a fixed tree (4 + 4, 2 + 2, 1 + 1).
+  __syncthreads();  // the loop's LDS tiles are reused below
+#pragma unroll
+  for (int half = kP2Waves / 2; half >= 1; half >>= 1) {
+    if (wave >= half && wave < 2 * half) {
+#pragma unroll
+      for (int t = 0; t < 4; ++t)
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          S.u.merge[wave - half][r32][32 * t + 8 * (r >> 2) + 4 * hh + (r & 3)] = o[t][r];
+    }
+    __syncthreads();
+    if (wave < half) {
+#pragma unroll
+      for (int t = 0; t < 4; ++t)
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          o[t][r] += S.u.merge[wave][r32][32 * t + 8 * (r >> 2) + 4 * hh + (r & 3)];
+    }
+    __syncthreads();
+  }
+  if (wave == 0 && r32 < H) {
+    float* dst = o_part + (((size_t)b * nchunks2 + c) * kMaxHeads + r32) * kHeadDim;
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const f32x4 x = {o[t][4 * g], o[t][4 * g + 1], o[t][4 * g + 2], o[t][4 * g + 3]};
+        *reinterpret_cast<f32x4*>(dst + 32 * t + 8 * g + 4 * hh) = x;
+      }
+  }
+}
+
+// o_full[b][h][:] = v_scale * sum of the sequence's chunk partials: thread
+// group g (of 16) adds chunks g, g + 16, ... in order, then group 0 adds the
+// 16 group sums in order.  Four dims per thread.
+constexpr int kCombGroups = 16;
+
+__global__ __launch_bounds__(32 * kCombGroups) void full_out_combine(
+    const float* __restrict__ o_part, int nchunks2, const int32_t* __restrict__ ctx_len, int cap,
+    int H, float v_scale, float* __restrict__ o_full) {
+  __shared__ f32x4 red[kCombGroups][32];
+  const int h = blockIdx.x, b = blockIdx.y;
+  const int d4 = threadIdx.x & 31, g = threadIdx.x >> 5;
+  const int N = clamp_ctx(ctx_len, b, cap);
+  const int nc = (N + kP2Chunk - 1) / kP2Chunk;
+  const f32x4* src =
+      reinterpret_cast<const f32x4*>(o_part + ((size_t)b * nchunks2 * kMaxHeads + h) * kHeadDim) +
+      d4;
+  constexpr size_t kChunkStride = kMaxHeads * kHeadDim / 4;
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  for (int c = g; c < nc; c += kCombGroups) acc += src[(size_t)c * kChunkStride];
+  red[g][d4] = acc;
+  __syncthreads();
+  if (g == 0) {
+#pragma unroll
+    for (int i = 1; i < kCombGroups; ++i) acc += red[i][d4];
+    *reinterpret_cast<f32x4*>(o_full + ((size_t)b * H + h) * kHeadDim + 4 * d4) = acc * v_scale;
   }
 }
 
@@ -398,6 +642,36 @@ void launch_score_mfma(const hs2_attn_desc& d, const void* q, const void* k, int
 }
 
 }  // namespace
+
+hipError_t launch_score_full(const hs2_attn_desc& d, const void* q, const void* k, const void* v,
+                             int64_t kv_stride, const int32_t* ctx_len, int cap, float* scores,
+                             float* o_full, float* lse, char* ws, hipStream_t st) {
+  const ScoreWs w = score_ws(d, cap);
+  float2* stats = reinterpret_cast<float2*>(ws + w.stats_off);
+  float* o_part = reinterpret_cast<float*>(ws + w.opart_off);
+  const bool fp8 = d.dtype == HS2_FP8_E4M3;
+  const float c2 = d.sm_scale * 1.4426950408889634f * (fp8 ? d.k_scale : 1.f);
+  const int nchunks1 = score_nchunks1(d, cap);
+  const int nchunks2 = (cap + kP2Chunk - 1) / kP2Chunk;
+  const auto* qq = static_cast<const uint16_t*>(q);
+  const dim3 g1(nchunks1, d.batch), g2(nchunks2, d.batch);
+  if (fp8) {
+    score_p1_bf16<true><<<g1, 64 * kP1Waves, 0, st>>>(qq, k, kv_stride, ctx_len, cap, d.n_heads,
+                                                      c2, stats, nchunks1, nullptr);
+    score_p2_full<true><<<g2, 64 * kP2Waves, 0, st>>>(qq, k, v, kv_stride, ctx_len, cap,
+                                                      d.n_heads, c2, stats, nchunks1, scores, cap,
+                                                      lse, o_part, nchunks2);
+  } else {
+    score_p1_bf16<false><<<g1, 64 * kP1Waves, 0, st>>>(qq, k, kv_stride, ctx_len, cap, d.n_heads,
+                                                       c2, stats, nchunks1, nullptr);
+    score_p2_full<false><<<g2, 64 * kP2Waves, 0, st>>>(qq, k, v, kv_stride, ctx_len, cap,
+                                                       d.n_heads, c2, stats, nchunks1, scores,
+                                                       cap, lse, o_part, nchunks2);
+  }
+  full_out_combine<<<dim3(d.n_heads, d.batch), 32 * kCombGroups, 0, st>>>(
+      o_part, nchunks2, ctx_len, cap, d.n_heads, fp8 ? d.v_scale : 1.f, o_full);
+  return hipGetLastError();
+}
 
 hipError_t launch_score_decode(const hs2_attn_desc& d, const void* q, const void* k,
                                int64_t kv_stride, const int32_t* ctx_len, int cap,

@@ -91,6 +91,12 @@ def run_scores(buf: DecodeBuffers, stream=None) -> None:
                          buf.scores, None, buf.lse_full, buf.ws, stream)
 
 
+def run_scores_full(buf: DecodeBuffers, o_full: torch.Tensor, stream=None) -> None:
+    """Scoring that also writes the full layer's own output o_full, fp32 [B][H][128]."""
+    hs2_full_attn_scores(buf.desc, buf.q, buf.k, buf.v, buf.kv_stride, buf.ctx_len, buf.cap,
+                         buf.scores, o_full, buf.lse_full, buf.ws, stream)
+
+
 def run_select(buf: DecodeBuffers, scores: torch.Tensor | None = None, stream=None) -> None:
     hs2_select_topk_window(buf.desc, buf.scores if scores is None else scores, buf.ctx_len,
                            buf.cap, buf.top_idx, buf.top_cnt, buf.ws, stream)

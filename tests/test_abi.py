@@ -103,6 +103,12 @@ def test_invalid_pointers_sizes_and_workspace(lib):
     assert _scores(d, ctx=None) == hs2.HS2_EINVAL
     assert _scores(d, sc=None) == hs2.HS2_EINVAL
     assert _scores(d, of=FAKE) == hs2.HS2_EINVAL          # o_full needs v
+    # o_full: decode with bf16 or E4M3 caches only
+    assert _scores(_desc(dtype=hs2.HS2_F32), of=FAKE, v=FAKE) == hs2.HS2_EUNSUPPORTED
+    assert _scores(_desc(batch=1, n_q=64, tile_q=64), of=FAKE, v=FAKE,
+                   stride=(4096 + 64) * 128) == hs2.HS2_EUNSUPPORTED
+    assert _scores(d, of=ODD, v=FAKE) == hs2.HS2_EALIGN
+    assert _scores(d, of=FAKE, v=ODD) == hs2.HS2_EALIGN
     assert _scores(d, cap=0) == hs2.HS2_EINVAL
     assert _scores(d, stride=4095 * 128) == hs2.HS2_EINVAL
     assert _scores(d, stride=4096 * 128 + 4) == hs2.HS2_EALIGN

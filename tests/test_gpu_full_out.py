@@ -1,0 +1,110 @@
+"""GPU parity of the full layer's own output (decode scoring with o_full).
+
+The full-attention layer of a hybrid block produces its attention output
+besides the selection ([Origins] "KV Reuse and Token-Level Sparse
+Selection").  With o_full the second K pass also streams V and accumulates
+sum_j p_hj v_j per 4,096-key chunk; the chunk partials are added in order.
+
+Bar: scores as without o_full (relative 1e-4); o_full max |gpu - oracle| <=
+1e-4 * max|v|.  Both sides use the same stored bf16 (or E4M3-widened) values;
+p enters the MFMA as a bf16 high part plus a bf16 low part (residual below
+2^-17 relative), logits and sums are fp32, so the error is some 1e-5 of the
+largest |v|, a tenth of the bar.
+"""
+
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from gpu_helpers import assert_scores_close
+from workloads import WORKLOADS, make_decode_inputs
+
+pytestmark = pytest.mark.gpu
+
+
+def _say(msg):
+    print(f"[gpu] {msg}", flush=True)
+    sys.stdout.flush()
+
+
+def _check(buf, o_full, inp, w):
+    ref, o_ref, lse = oracle.full_attn_scores(inp["q"], inp["k"], inp["ctx_len"], tile_q=1,
+                                              sm_scale=w.sm_scale, v=inp["v"])
+    assert_scores_close(buf.scores.cpu().numpy(), ref, inp["ctx_len"])
+    np.testing.assert_allclose(buf.lse_full.cpu().numpy(), lse, rtol=1e-5, atol=1e-5)
+    got = o_full.cpu().numpy().astype(np.float64)
+    want = o_ref[:, 0]
+    vmax = max(np.abs(inp["v"]).max(), 1e-30)
+    err = np.abs(got - want)
+    assert err.max() <= 1e-4 * vmax, f"o_full max abs {err.max():.3e} (max|v| {vmax:.3e})"
+
+
+CASES = [
+    ("bf16_ragged", "decode_bf16_64k_b16", dict(batch=3), [9000, 4097, 1152]),
+    ("bf16_h7", "decode_bf16_64k_b16", dict(batch=2, n_heads=7), [5000, 130]),
+    ("bf16_h1_one_key", "decode_bf16_64k_b16", dict(batch=2, n_heads=1), [2049, 1]),
+    ("bf16_clusters", "decode_bf16_256k_b4", dict(batch=2), [20000, 16384]),
+    ("fp8_ragged", "decode_fp8_256k_b4", dict(batch=3), [9000, 4097, 1152]),
+    ("fp8_h5", "decode_fp8_256k_b4", dict(batch=2, n_heads=5), [8193, 33]),
+]
+
+
+@pytest.mark.parametrize("name,wname,over,ctx", CASES, ids=[c[0] for c in CASES])
+def test_full_output_matches_oracle(hs2, name, wname, over, ctx):
+    from kv_cache_reuse_hs2_amd.torch_api import make_buffers, run_scores_full
+
+    w = WORKLOADS[wname].replace(**over)
+    inp = make_decode_inputs(w, ctx_lens=ctx, capacity=max(ctx))
+    if w.dtype == "fp8":
+        inp["k"] = oracle.dequant_kv(inp["k_raw"], inp["k_scale"])
+        inp["v"] = oracle.dequant_kv(inp["v_raw"], inp["v_scale"])
+    buf = make_buffers(inp, n_heads=w.n_heads, k_top=w.k_top, window=w.window,
+                       sm_scale=w.sm_scale, dtype=w.dtype)
+    o_full = torch.full((w.batch, w.n_heads, 128), float("nan"), device="cuda")
+    _say(f"full output {name} ctx={ctx} H={w.n_heads} dtype={w.dtype}")
+    run_scores_full(buf, o_full)
+    torch.cuda.synchronize()
+    _check(buf, o_full, inp, w)
+
+
+def test_full_output_empty_sequence_is_zero(hs2):
+    """A sequence with no keys has no attention mass: o_full 0, lse -inf."""
+    from kv_cache_reuse_hs2_amd.torch_api import make_buffers, run_scores_full
+
+    w = WORKLOADS["decode_bf16_64k_b16"].replace(batch=2)
+    inp = make_decode_inputs(w, ctx_lens=[3000, 3000], capacity=3000)
+    inp["ctx_len"] = np.array([3000, 0], dtype=np.int32)
+    buf = make_buffers(inp, n_heads=w.n_heads, k_top=w.k_top, window=w.window,
+                       sm_scale=w.sm_scale, dtype=w.dtype)
+    o_full = torch.full((w.batch, w.n_heads, 128), float("nan"), device="cuda")
+    _say("full output with an empty sequence")
+    run_scores_full(buf, o_full)
+    torch.cuda.synchronize()
+    got = o_full.cpu().numpy()
+    assert np.all(got[1] == 0.0)
+    assert np.all(np.isneginf(buf.lse_full.cpu().numpy()[1]))
+    _check(buf, o_full, inp, w)
+
+
+def test_scores_with_and_without_full_output_agree(hs2):
+    """The o_full pass sums heads in another order: same scores to rounding."""
+    from kv_cache_reuse_hs2_amd.torch_api import make_buffers, run_scores, run_scores_full
+
+    w = WORKLOADS["decode_bf16_256k_b4"].replace(batch=2)
+    inp = make_decode_inputs(w, ctx_lens=[12345, 8192], capacity=12345)
+    buf = make_buffers(inp, n_heads=w.n_heads, k_top=w.k_top, window=w.window,
+                       sm_scale=w.sm_scale, dtype=w.dtype)
+    _say("scores with and without o_full")
+    run_scores(buf)
+    torch.cuda.synchronize()
+    plain = buf.scores.clone()
+    o_full = torch.empty((w.batch, w.n_heads, 128), device="cuda")
+    run_scores_full(buf, o_full)
+    torch.cuda.synchronize()
+    a = plain.cpu().numpy()[:, :, :].astype(np.float64)
+    bb = buf.scores.cpu().numpy().astype(np.float64)
+    for b, n in enumerate(inp["ctx_len"]):
+        np.testing.assert_allclose(bb[b, :, :n], a[b, :, :n], rtol=2e-6, atol=0)
