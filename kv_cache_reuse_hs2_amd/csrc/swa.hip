@@ -103,11 +103,15 @@ struct SwaState {
 
 __device__ __forceinline__ void load_q_rows(const uint16_t* qrow, int H, bool live, int r32,
                                             int hh, bf16x8_t (&qr)[8]) {
+  // Every lane loads (padded heads repeat head H - 1) and zeroes afterwards:
+  // a load under a branch makes the compiler wait for all loads in flight,
+  // this one included, at the next use of any earlier load.
+  const bool use = live && r32 < H;
+  const uint16_t* src = qrow + min(r32, H - 1) * kHeadDim;
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
-    u32x4 x = {0u, 0u, 0u, 0u};
-    if (live && r32 < H)
-      x = *reinterpret_cast<const u32x4*>(qrow + r32 * kHeadDim + step_dim<false>(e, hh));
+    u32x4 x = *reinterpret_cast<const u32x4*>(src + step_dim<false>(e, hh));
+    if (!use) x = (u32x4){0u, 0u, 0u, 0u};
     qr[e] = as_bf16x8(x);
   }
 }
