@@ -530,6 +530,35 @@ def main() -> int:
     ms_3call, _ = timed(run_step, bool(args.graph))
     ms, wall_ms = timed(run_fused_step, bool(args.graph))
 
+    # Spread of single steps (after the timed region, not part of `value`):
+    # each step replayed alone between two events.
+    def per_step(fn, n):
+        g = capture(fn, 1) if args.graph else None
+        run1 = g.replay if g is not None else (lambda: fn(buf))
+        for _ in range(3):
+            run1()
+        ev = []
+        for _ in range(n):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            run1()
+            e1.record(stream)
+            ev.append((e0, e1))
+        torch.cuda.synchronize()
+        us = np.array([a.elapsed_time(b) * 1e3 for a, b in ev])
+        return {"p10": round(float(np.percentile(us, 10)), 2),
+                "median": round(float(np.median(us)), 2),
+                "p90": round(float(np.percentile(us, 90)), 2), "n": n}
+
+    step_spread = per_step(run_fused_step, max(args.steps, 20))
+    # Measured copy bandwidth of the box (a plain 1 GiB device copy, read +
+    # write bytes), the practical ceiling the step's HBM rate is also set against.
+    src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda").fill_(1)
+    dst = torch.empty_like(src)
+    ms_copy = time_events(lambda: dst.copy_(src), 10, 3)
+    copy_gbs = 2 * (1 << 30) / (ms_copy * 1e-3) / 1e9
+    del src, dst
+
     ab = algorithmic_bytes(w)
     tokens_s = w.batch / (ms * 1e-3)
     step_gbs = ab["step"] / (ms * 1e-3) / 1e9
@@ -565,6 +594,10 @@ def main() -> int:
             "step": "hs2_decode_step (scoring + selection + sparse layer, one call)",
             "ms_per_step_three_calls": round(ms_3call, 5),
             "wall_ms_timed_region": round(wall_ms, 3),
+            "single_step_us": step_spread,
+            "hbm_copy_GBps": round(copy_gbs, 1),
+            "step_hbm_frac_of_copy": round(step_gbs / copy_gbs, 4),
+            "scoring_call_hbm_frac_of_copy": round(score_gbs / copy_gbs, 4),
         },
         "roofline": {
             "kernel": "hs2_full_attn_scores = score_p1_bf16<false> + "
