@@ -69,6 +69,39 @@ def test_hand_worked_cases(case):
         assert od[0, 0, 0, 0] == pytest.approx(_closed_form(case["o_dense"][0]), rel=1e-12)
 
 
+@pytest.mark.parametrize("case", [c for c in _hand_cases() if "o_dense" in c],
+                         ids=lambda c: c["name"])
+def test_full_layer_output_hand_cases(case):
+    # The full layer's own output (full_attn_scores with v) against the
+    # hand-worked dense output of the same case.
+    q, k, v, ctx = _hand_inputs(case)
+    _, o_full, lse = oracle.full_attn_scores(q, k, ctx, tile_q=case["tile_q"], sm_scale=1.0, v=v)
+    assert o_full[0, 0, 0, 0] == pytest.approx(_closed_form(case["o_dense"][0]), rel=1e-12)
+
+
+def test_full_layer_output_invariants():
+    # One visible key: the output is its V row.  Constant V: the output is
+    # that constant (the probabilities sum to one).  Two keys with logits
+    # a and b: the output is the logistic mix of their V rows.
+    rng = np.random.default_rng(11)
+    q, k, v = _rand(rng, 2, 1, 3, 8), _rand(rng, 2, 40, 8), _rand(rng, 2, 40, 8)
+    ctx = np.array([1, 40])
+    _, o, _ = oracle.full_attn_scores(q, k, ctx, tile_q=1, sm_scale=0.3, v=v)
+    np.testing.assert_allclose(o[0, 0], np.broadcast_to(v[0, 0], (3, 8)), rtol=0, atol=0)
+    _, oc, _ = oracle.full_attn_scores(q, k, ctx, tile_q=1, sm_scale=0.3,
+                                       v=np.full_like(v, 2.5))
+    np.testing.assert_allclose(oc[1, 0], 2.5, rtol=1e-14)
+    ctx2 = np.array([2, 2])
+    _, o2, _ = oracle.full_attn_scores(q, k, ctx2, tile_q=1, sm_scale=0.3, v=v)
+    for b in range(2):
+        for h in range(3):
+            a = 0.3 * float(q[b, 0, h] @ k[b, 0])
+            c = 0.3 * float(q[b, 0, h] @ k[b, 1])
+            w0 = scipy.special.expit(a - c)
+            np.testing.assert_allclose(o2[b, 0, h], w0 * v[b, 0] + (1 - w0) * v[b, 1],
+                                       rtol=1e-12)
+
+
 def _rand(rng, *shape, scale=1.0):
     return rng.standard_normal(shape) * scale
 
