@@ -175,14 +175,30 @@ __global__ __launch_bounds__(1024) void pf_stats(PfArgs a) {
     // Every key of the block is inside this query's range and the split:
     // no masks, and the scale folds into one fma per logit (c2 > 0).
     const bool full = kb0 + kBlk <= j1 && kb0 + kBlk - 1 <= P;
+    f32x16_t accs[2] = {{}, {}};
 #pragma unroll
-    for (int mt = 0; mt < 2; ++mt) {
-      f32x16_t acc = {};
+    for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
       for (int e = 0; e < 8; ++e)
-        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k_opnd_ring(kblk, 32 * mt + r32, e, hh), qr[e], acc, 0, 0, 0);
+        accs[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k_opnd_ring(kblk, 32 * mt + r32, e, hh), qr[e], accs[mt], 0, 0, 0);
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt) {
+      const f32x16_t& acc = accs[mt];
       // acc[r]: row (query i, head r32), key kb0 + 32mt + 8(r/4) + 4hh + r%4
-      if (full) {
+      // The running reference m moves only when a logit exceeds it by more
+      // than 64 binades: the block's terms are summed against the current m
+      // (each at most 2^64, so the sum stays finite and keeps fp32 relative
+      // precision), and only a sum above 2^64 (or a first block) takes the
+      // block maximum and rescales.  This saves the 16 max operations per
+      // half on almost every block.
+      float lazy = 0.f;
+      if (full && m != -INFINITY) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) lazy += fast_exp2(fmaf(acc[r], a.c2, -m));
+      }
+      if (full && m != -INFINITY && lazy <= 0x1p64f) {
+        l += lazy;
+      } else if (full) {
         float bm = acc[0];
 #pragma unroll
         for (int r = 1; r < 16; ++r) bm = fmaxf(bm, acc[r]);
@@ -258,7 +274,7 @@ __global__ __launch_bounds__(1024) void pf_colsum(PfArgs a) {
   __shared__ struct __attribute__((aligned(16))) {
     uint8_t ring[kRing * kSlotB];
     float s_L[16 * 32];
-    float s_cs[16][kBlk];
+    float s_cs[2][16][kBlk];
   } sm;
   uint8_t* ring = sm.ring;
   float* s_L = sm.s_L;
@@ -278,24 +294,32 @@ __global__ __launch_bounds__(1024) void pf_colsum(PfArgs a) {
   __builtin_amdgcn_s_waitcnt(0 | (7 << 4) | (15 << 8));  // vmcnt(0)
   dma_k_block(ring, kb, rows_of(0));
   if (nblk > 1) dma_k_block(ring + kSlotB, kb, rows_of(1));
+  auto block_sum = [&](int bj) {
+    if (threadIdx.x < kBlk) {
+      const int j = j0 + bj * kBlk + threadIdx.x;
+      float sum = 0.f;
+#pragma unroll
+      for (int w = 0; w < 16; ++w) sum += s_cs[bj & 1][w][threadIdx.x];
+      if (j < j1) out[j] = sum;
+    }
+  };
   for (int bi = 0; bi < nblk; ++bi) {
-    // Block bi has landed for every wave; the slot of block bi-1 is free,
-    // and so is s_cs (read by the previous block's final sum).
     ring_barrier(bi + 1 < nblk);
     if (bi + 2 < nblk) dma_k_block(ring + ((bi + 2) % kRing) * kSlotB, kb, rows_of(bi + 2));
+    if (bi > 0) block_sum(bi - 1);
     const uint8_t* kblk = ring + (bi % kRing) * kSlotB;
     const int kb0 = j0 + bi * kBlk;
     const bool full = kb0 + kBlk <= j1 && kb0 + kBlk - 1 <= P;
+    f32x16_t accs[2] = {{}, {}};
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        accs[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qr[e], k_opnd_ring(kblk, 32 * mt + r32, e, hh), accs[mt], 0, 0, 0);
 #pragma unroll
     for (int mt = 0; mt < 2; ++mt) {
       const int j = kb0 + 32 * mt + r32;  // this lane's key
-      // Computed for every block (a block in the query's future, at most the
-      // last one, is masked to 0), so that the operand reads follow the
-      // barrier in the same straight-line code.
-      f32x16_t acc = {};
-#pragma unroll
-      for (int e = 0; e < 8; ++e)
-        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qr[e], k_opnd_ring(kblk, 32 * mt + r32, e, hh), acc, 0, 0, 0);
+      const f32x16_t& acc = accs[mt];
       // acc[r]: row (query i, head 8(r/4) + 4hh + r%4), key j.  The sum over
       // the query's 32 head rows: 16 in this lane, 16 in lane ^ 32.  Padded
       // heads have L = +inf, so their p is 0.
@@ -304,22 +328,14 @@ __global__ __launch_bounds__(1024) void pf_colsum(PfArgs a) {
       for (int r = 0; r < 16; ++r) cs += fast_exp2(fmaf(acc[r], a.c2, -L[r]));
       if (!full && !(j < j1 && j <= P)) cs = 0.f;
       cs += __shfl_xor(cs, 32);
-      if (hh == 0) s_cs[wave][32 * mt + r32] = cs;
-    }
-    // LDS-only barrier: a full __syncthreads would also wait for the ring
-    // loads in flight.
-    __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0)
-    __builtin_amdgcn_s_barrier();
-    asm volatile("" ::: "memory");
-    __builtin_amdgcn_sched_barrier(0);
-    if (threadIdx.x < kBlk) {
-      const int j = kb0 + threadIdx.x;
-      float sum = 0.f;
-#pragma unroll
-      for (int w = 0; w < 16; ++w) sum += s_cs[w][threadIdx.x];
-      if (j < j1) out[j] = sum;
+      if (hh == 0) s_cs[bi & 1][wave][32 * mt + r32] = cs;
     }
   }
+  __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0)
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
+  block_sum(nblk - 1);
 }
 
 // I_t[j] = sum over the tile's 16-query blocks (in order) of their column

@@ -76,6 +76,24 @@ def test_prefill_matches_oracle(hs2, name, bsz, heads, ctx, cap, n_q, tile_q):
     np.testing.assert_allclose(buf.lse.cpu().numpy()[fin], lse_ref[fin], rtol=1e-5, atol=1e-5)
 
 
+def test_prefill_large_logits(hs2):
+    """Queries scaled by 64 (exact in bf16): logits span hundreds of binades, so
+    the running maximum of the statistics pass has to move by more than its
+    64-binade slack many times; scores and log-sum-exp still match."""
+    w = WORKLOADS["prefill_bf16_128k_8k"].replace(batch=1, n_heads=32)
+    inp = make_prefill_inputs(w, ctx_lens=[12000], n_q=64, capacity=12000)
+    q = np.asarray(inp["q"], dtype=np.float32) * np.float32(64.0)
+    inp["q"] = q.astype(np.float64)
+    inp["q_raw"] = (q.view(np.uint32) >> 16).astype(np.uint16)
+    _say("prefill large logits")
+    buf = _run(inp, w, 64, 64)
+    ref, _, lse = oracle.full_attn_scores(inp["q"], inp["k"], inp["ctx_len"], tile_q=64,
+                                          sm_scale=w.sm_scale)
+    assert_scores_close(buf.scores.cpu().numpy(), ref, inp["ctx_len"])
+    fin = np.isfinite(lse)
+    np.testing.assert_allclose(buf.lse_full.cpu().numpy()[fin], lse[fin], rtol=1e-5, atol=1e-5)
+
+
 def test_prefill_select_bit_exact_on_oracle_scores(hs2):
     from kv_cache_reuse_hs2_amd.torch_api import make_buffers, run_select, to_device
 
