@@ -2,7 +2,8 @@
 
 Tolerances (the bar each GPU test asserts):
 * importance scores: element-wise |gpu - oracle| <= 1e-4 * |oracle| + 1e-30
-  (both sides compute in fp32 or better on identical stored inputs);
+  and, per sequence and tile, relative L2 error <= 1e-5 (both sides compute
+  in fp32 or better on identical stored inputs);
 * selection fed the oracle's fp32 scores: bit-exact;
 * selection from GPU scores: every index in the symmetric difference with the
   oracle's selection is a near-tie, |I_or[j] - tau| <= 1e-4 * tau, tau being
@@ -22,6 +23,7 @@ import oracle
 
 SCORE_RTOL = 1e-4
 SCORE_ATOL = 1e-30
+SCORE_REL_L2 = 1e-5
 
 
 def assert_scores_close(gpu: np.ndarray, ref: np.ndarray, ctx_len) -> None:
@@ -33,6 +35,11 @@ def assert_scores_close(gpu: np.ndarray, ref: np.ndarray, ctx_len) -> None:
         assert not bad.any(), (
             f"seq {b}: {bad.sum()} scores off, worst rel "
             f"{(err / np.maximum(np.abs(r), 1e-30)).max():.3e}")
+        for t in range(r.shape[0]):
+            den = np.linalg.norm(r[t])
+            if den > 0:
+                rel = np.linalg.norm(g[t] - r[t]) / den
+                assert rel <= SCORE_REL_L2, f"seq {b} tile {t}: relative L2 {rel:.3e}"
 
 
 def assert_outputs_close(gpu: np.ndarray, ref: np.ndarray, dtype: str) -> None:
