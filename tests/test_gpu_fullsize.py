@@ -53,6 +53,7 @@ def _run_full(name, **over):
     torch.cuda.synchronize()
     np.testing.assert_array_equal(buf.top_cnt.cpu().numpy(), cnt)
     np.testing.assert_array_equal(buf.top_idx.cpu().numpy(), top)
+    return w, inp, buf
 
 
 def test_decode_256k_batch4_clusters(hs2):
@@ -66,3 +67,21 @@ def test_decode_64k_batch16_needles(hs2):
 def test_decode_1m_context(hs2):
     # The decode half of the bridge workload: one sequence of 1,048,576 keys.
     _run_full("bridge_decode_bf16_1m", recipe="plain")
+
+
+@pytest.mark.timeout(400)
+def test_decode_max_capacity_4m(hs2):
+    # The largest supported cache: one sequence of 4,194,304 keys (1 GiB of
+    # bf16 K), through the three calls, and the full layer's own output.
+    from kv_cache_reuse_hs2_amd.torch_api import run_scores_full
+
+    w, inp, buf = _run_full("bridge_decode_bf16_1m", recipe="plain", ctx_len=4194304)
+    o_full = torch.empty((1, w.n_heads, 128), device="cuda")
+    print("[gpu] full output at 4,194,304 keys", flush=True)
+    run_scores_full(buf, o_full)
+    torch.cuda.synchronize()
+    ref, o_ref, _ = oracle.full_attn_scores(inp["q"], inp["k"], inp["ctx_len"], tile_q=1,
+                                            sm_scale=w.sm_scale, v=inp["v"])
+    assert_scores_close(buf.scores.cpu().numpy(), ref, inp["ctx_len"])
+    err = np.abs(o_full.cpu().numpy().astype(np.float64) - o_ref[:, 0]).max()
+    assert err <= 1e-4 * np.abs(inp["v"]).max(), f"o_full max abs {err:.3e}"
