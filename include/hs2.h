@@ -127,9 +127,10 @@ HS2_API size_t hs2_workspace_size(const hs2_attn_desc* desc, int kv_capacity);
  * o_full, the full layer's own attention output, fp32 [B][n_heads][128]:
  *   o_full[b][h][:] = sum_j p_hj v_j      (times v_scale for E4M3 caches).
  * o_full needs v (HS2_EINVAL without it) and is implemented for decode
- * (tile_q = 1) with bf16 or E4M3 caches (HS2_EUNSUPPORTED otherwise); the
- * second K pass then also streams V, and the scores are summed over heads in
- * a different order than without o_full (same values up to rounding).
+ * (tile_q = 1; HS2_EUNSUPPORTED for prefill); the second K pass then also
+ * streams V.  With bf16 or E4M3 caches the scores are summed over heads in
+ * a different order than without o_full (same values up to rounding); with
+ * fp32 caches they are the same bits.
  * v may be NULL when o_full is NULL.
  */
 HS2_API hs2_status hs2_full_attn_scores(const hs2_attn_desc* desc, const void* q,

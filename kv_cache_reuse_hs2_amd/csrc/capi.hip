@@ -127,8 +127,8 @@ hs2_status hs2_full_attn_scores(const hs2_attn_desc* desc, const void* q, const 
   if (q == nullptr || k == nullptr || ctx_len == nullptr || scores == nullptr) return HS2_EINVAL;
   if (o_full != nullptr) {
     if (v == nullptr) return HS2_EINVAL;
-    // The full layer's own output: decode on the MFMA paths.
-    if (is_prefill(*desc) || desc->dtype == HS2_F32) return HS2_EUNSUPPORTED;
+    // The full layer's own output: decode only.
+    if (is_prefill(*desc)) return HS2_EUNSUPPORTED;
   }
   if ((s = check_cache(desc, kv_stride, kv_capacity)) != HS2_OK) return s;
   if (misaligned(q) || misaligned(k) || misaligned(v) || misaligned(ctx_len) ||

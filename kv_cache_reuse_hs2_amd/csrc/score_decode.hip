@@ -590,6 +590,78 @@ __global__ __launch_bounds__(256) void score_f32(
   }
 }
 
+// fp32 path with the full layer's own output: workgroup (c, b) takes keys
+// [4096c, 4096c + 4096) in sub-blocks of 256.  Per sub-block a thread owns
+// one key: it computes the 32 logits as score_f32<1> does, writes I[j] (the
+// same arithmetic, so the same bits) and puts p_hj in LDS; then a thread owns
+// output dim t % 128 of heads 16(t / 128) .. + 15 and adds p_hj v_jd over
+// the sub-block's keys in order.  The chunk's partial O goes to o_part[b][c]
+// for full_out_combine, as in the MFMA paths.
+__global__ __launch_bounds__(256) void score_full_f32(
+    const float* __restrict__ q, const float* __restrict__ k, const float* __restrict__ v,
+    int64_t kv_stride, const int32_t* __restrict__ ctx_len, int cap, int H, float c2,
+    const float* __restrict__ lse2, float* __restrict__ scores, int64_t score_stride,
+    float* __restrict__ o_part, int nchunks2) {
+  const int b = blockIdx.y, c = blockIdx.x;
+  const int N = clamp_ctx(ctx_len, b, cap);
+  const int j_begin = c * kP2Chunk;
+  if (j_begin >= N) return;
+  const int j_end = min(N, j_begin + kP2Chunk);
+  __shared__ float4 qs[kMaxHeads][kHeadDim / 4];
+  __shared__ float ps[kMaxHeads][kF32Chunk];
+  const float* qb = q + (size_t)b * H * kHeadDim;
+  for (int e = threadIdx.x; e < kMaxHeads * kHeadDim / 4; e += blockDim.x) {
+    const int h = e / (kHeadDim / 4), d4 = e % (kHeadDim / 4);
+    qs[h][d4] = h < H ? reinterpret_cast<const float4*>(qb + h * kHeadDim)[d4]
+                      : make_float4(0.f, 0.f, 0.f, 0.f);
+  }
+  const float* kb = k + (size_t)b * kv_stride;
+  const float* vb = v + (size_t)b * kv_stride;
+  const int d = threadIdx.x & (kHeadDim - 1), hg = threadIdx.x >> 7;
+  float oacc[16];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) oacc[i] = 0.f;
+  for (int j0 = j_begin; j0 < j_end; j0 += kF32Chunk) {
+    __syncthreads();  // q staged; the previous sub-block's ps read
+    const int j = j0 + threadIdx.x;
+    const bool valid = j < j_end;
+    const float4* kp = reinterpret_cast<const float4*>(kb + (size_t)min(j, N - 1) * kHeadDim);
+    float acc[kMaxHeads];
+#pragma unroll
+    for (int h = 0; h < kMaxHeads; ++h) acc[h] = 0.f;
+    for (int d4 = 0; d4 < kHeadDim / 4; ++d4) {
+      const float4 kv = kp[d4];
+#pragma unroll
+      for (int h = 0; h < kMaxHeads; ++h) {
+        const float4 qv = qs[h][d4];
+        acc[h] = fmaf(qv.x, kv.x, acc[h]);
+        acc[h] = fmaf(qv.y, kv.y, acc[h]);
+        acc[h] = fmaf(qv.z, kv.z, acc[h]);
+        acc[h] = fmaf(qv.w, kv.w, acc[h]);
+      }
+    }
+    float imp = 0.f;
+#pragma unroll
+    for (int h = 0; h < kMaxHeads; ++h) {
+      const float p = (valid && h < H) ? fast_exp2(acc[h] * c2 - lse2[b * kMaxHeads + h]) : 0.f;
+      if (h < H) imp += p;
+      ps[h][threadIdx.x] = p;
+    }
+    if (valid) scores[(size_t)b * score_stride + j] = imp;
+    __syncthreads();
+    const int nk = min(kF32Chunk, j_end - j0);
+    for (int jj = 0; jj < nk; ++jj) {
+      const float x = vb[(size_t)(j0 + jj) * kHeadDim + d];
+#pragma unroll
+      for (int i = 0; i < 16; ++i) oacc[i] = fmaf(ps[16 * hg + i][jj], x, oacc[i]);
+    }
+  }
+  float* dst = o_part + ((size_t)b * nchunks2 + c) * kMaxHeads * kHeadDim + d;
+#pragma unroll
+  for (int i = 0; i < 16; ++i)
+    if (16 * hg + i < H) dst[(size_t)(16 * hg + i) * kHeadDim] = oacc[i];
+}
+
 // fp32 path: per (sequence, head) L_h = max + log2(sum) over the chunks.
 // Heads beyond H get +inf so that 2^(x - L) vanishes for them.
 __global__ __launch_bounds__(256) void score_reduce_f32(
@@ -649,10 +721,26 @@ hipError_t launch_score_full(const hs2_attn_desc& d, const void* q, const void* 
   const ScoreWs w = score_ws(d, cap);
   float2* stats = reinterpret_cast<float2*>(ws + w.stats_off);
   float* o_part = reinterpret_cast<float*>(ws + w.opart_off);
+  const int nchunks2 = (cap + kP2Chunk - 1) / kP2Chunk;
+  if (d.dtype == HS2_F32) {
+    float* lse2 = reinterpret_cast<float*>(ws + w.lse2_off);
+    const int nchunks1 = score_nchunks1(d, cap);
+    const auto* qf = static_cast<const float*>(q);
+    const auto* kf = static_cast<const float*>(k);
+    score_f32<0><<<dim3(nchunks1, d.batch), 256, 0, st>>>(qf, kf, kv_stride, ctx_len, cap,
+                                                          d.n_heads, d.sm_scale * 1.4426950408889634f,
+                                                          stats, nchunks1, nullptr, nullptr, 0);
+    score_reduce_f32<<<d.batch, 256, 0, st>>>(stats, nchunks1, ctx_len, cap, d.n_heads, lse2, lse);
+    score_full_f32<<<dim3(nchunks2, d.batch), 256, 0, st>>>(
+        qf, kf, static_cast<const float*>(v), kv_stride, ctx_len, cap, d.n_heads,
+        d.sm_scale * 1.4426950408889634f, lse2, scores, cap, o_part, nchunks2);
+    full_out_combine<<<dim3(d.n_heads, d.batch), 32 * kCombGroups, 0, st>>>(
+        o_part, nchunks2, ctx_len, cap, d.n_heads, 1.f, o_full);
+    return hipGetLastError();
+  }
   const bool fp8 = d.dtype == HS2_FP8_E4M3;
   const float c2 = d.sm_scale * 1.4426950408889634f * (fp8 ? d.k_scale : 1.f);
   const int nchunks1 = score_nchunks1(d, cap);
-  const int nchunks2 = (cap + kP2Chunk - 1) / kP2Chunk;
   const auto* qq = static_cast<const uint16_t*>(q);
   const dim3 g1(nchunks1, d.batch), g2(nchunks2, d.batch);
   if (fp8) {

@@ -43,6 +43,8 @@ def _check(buf, o_full, inp, w):
 
 
 CASES = [
+    ("f32_4k", "decode_f32_4k", dict(), [4096]),
+    ("f32_ragged_h5", "decode_f32_4k", dict(batch=3, n_heads=5), [3000, 1153, 77]),
     ("bf16_ragged", "decode_bf16_64k_b16", dict(batch=3), [9000, 4097, 1152]),
     ("bf16_h7", "decode_bf16_64k_b16", dict(batch=2, n_heads=7), [5000, 130]),
     ("bf16_h1_one_key", "decode_bf16_64k_b16", dict(batch=2, n_heads=1), [2049, 1]),
@@ -87,6 +89,26 @@ def test_full_output_empty_sequence_is_zero(hs2):
     assert np.all(got[1] == 0.0)
     assert np.all(np.isneginf(buf.lse_full.cpu().numpy()[1]))
     _check(buf, o_full, inp, w)
+
+
+def test_f32_scores_with_full_output_are_the_same_bits(hs2):
+    """The fp32 path computes the importance with the same arithmetic either way."""
+    from kv_cache_reuse_hs2_amd.torch_api import make_buffers, run_scores, run_scores_full
+
+    w = WORKLOADS["decode_f32_4k"].replace(batch=2)
+    inp = make_decode_inputs(w, ctx_lens=[4096, 2500], capacity=4096)
+    buf = make_buffers(inp, n_heads=w.n_heads, k_top=w.k_top, window=w.window,
+                       sm_scale=w.sm_scale, dtype=w.dtype)
+    _say("fp32 scores with and without o_full")
+    run_scores(buf)
+    torch.cuda.synchronize()
+    plain, lse = buf.scores.clone(), buf.lse_full.clone()
+    o_full = torch.empty((w.batch, w.n_heads, 128), device="cuda")
+    run_scores_full(buf, o_full)
+    torch.cuda.synchronize()
+    for b, n in enumerate(inp["ctx_len"]):
+        assert torch.equal(buf.scores[b, :, :n], plain[b, :, :n])
+    assert torch.equal(buf.lse_full, lse)
 
 
 def test_scores_with_and_without_full_output_agree(hs2):
