@@ -29,7 +29,7 @@ def _declared():
 @pytest.fixture(scope="module")
 def lib():
     if not os.path.exists(hs2.LIB_PATH):
-        pytest.fail("libhs2.so is not built; run __graft_entry__.build()")
+        pytest.fail("libhs2.so is not built; run python -m kv_cache_reuse_hs2_amd.build_lib")
     return hs2.load()
 
 
