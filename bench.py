@@ -204,6 +204,19 @@ def swa_measurements(steps: int, warmup: int) -> dict:
                      "achieved_TFLOPs": round(flop / (ms * 1e-3) / 1e12, 1),
                      "algorithmic_bytes": int(byts)}
         del o
+    # A wide window takes the streaming (tiled) kernel.
+    wide = 1024
+    dw = hs2.make_desc(batch=1, n_heads=w.n_heads, n_q=w.n_q, tile_q=1, k_top=0, window=wide,
+                       sm_scale=w.sm_scale)
+    o = torch.empty((1, nq, w.n_heads, hd), dtype=torch.bfloat16, device="cuda")
+    ms = time_events(lambda: hs2.hs2_swa_attention(dw, q, k, v, cap * hd, ctx, cap, o,
+                                                   hs2.HS2_BF16, lse), steps, warmup)
+    flop_w = 4.0 * w.n_heads * hd * nq * wide
+    out["bf16_out_window_1024"] = {"ms": round(ms, 5), "queries_per_s": round(nq / (ms * 1e-3), 1),
+                                   "achieved_TFLOPs": round(flop_w / (ms * 1e-3) / 1e12, 1),
+                                   "mfma_bf16_frac": round(flop_w / (ms * 1e-3) / 2.5e15, 4),
+                                   "kernel": "swa_tiled_bf16 (windows above 129)"}
+    del o
     out["note"] = "q read and o written once, the band's K and V rows once"
     return out
 
