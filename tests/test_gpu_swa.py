@@ -54,6 +54,9 @@ CASES = [
     ("heads7", 2, 7, [1200, 640], 1200, 96, 128),
     ("before_cache_start", 2, 32, [50, 9], 64, 64, 16),
     ("decode", 4, 32, [5000, 129, 128, 1], 5000, 1, 128),
+    ("w129_widest_band", 1, 32, [2000], 2000, 100, 129),
+    ("w130_narrowest_tiled", 1, 32, [2000], 2000, 100, 130),
+    ("heads1", 2, 1, [700, 333], 700, 70, 128),
 ]
 
 
