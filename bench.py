@@ -307,7 +307,8 @@ def extra_measurements(steps: int, warmup: int) -> dict:
     import torch
 
     import kv_cache_reuse_hs2_amd as hs2
-    from kv_cache_reuse_hs2_amd.torch_api import make_buffers, run_fused_step
+    from kv_cache_reuse_hs2_amd.torch_api import (make_buffers, run_fused_step, run_scores,
+                                                  run_scores_full)
     from workloads import WORKLOADS, make_decode_inputs, make_prefill_inputs
 
     out = {}
@@ -337,7 +338,20 @@ def extra_measurements(steps: int, warmup: int) -> dict:
                    "mfma_bf16_frac": round(alg / (ms * 1e-3) / 2.5e15, 4),
                    "note": "algorithmic FLOPs count the causal QK^T once plus the sparse "
                            "QK^T+PV; the recompute pass is overhead"}
-    del buf, inp
+    # The full layer's own output on the same shape: scoring alone, then
+    # scoring with o_full (one more pass over K and V).
+    o_full = torch.empty((1, w.n_q, w.n_heads, w.head_dim), dtype=torch.float32, device="cuda")
+    ms_s = time_events(lambda: run_scores(buf), max(2, steps // 10), 2)
+    ms_f = time_events(lambda: run_scores_full(buf, o_full), max(2, steps // 10), 2)
+    att_flop = 2.0 * qk_flop   # causal QK^T and P.V, once each
+    out[w.name]["full_layer"] = {
+        "scores_ms": round(ms_s, 4), "scores_and_o_full_ms": round(ms_f, 4),
+        "o_full_pass_ms": round(ms_f - ms_s, 4),
+        "attention_TFLOPs": round(att_flop / (ms_f * 1e-3) / 1e12, 1),
+        "o_full_pass_TFLOPs": round(att_flop / ((ms_f - ms_s) * 1e-3) / 1e12, 1),
+        "note": "attention FLOPs count the causal QK^T and P.V once each; the output pass "
+                "recomputes QK^T and multiplies P as a bf16 high and low part"}
+    del buf, inp, o_full
     # KV Bridging of 1,048,576 x 2048 hidden states, then decode over the cache.
     w = WORKLOADS["bridge_decode_bf16_1m"]
     g = torch.Generator(device="cuda").manual_seed(w.seed)

@@ -124,13 +124,14 @@ HS2_API size_t hs2_workspace_size(const hs2_attn_desc* desc, int kv_capacity);
  * where p_ihj = exp(s_ihj - lse_ih), s_ihj = sm_scale * q_ih . k_j, is query
  * i's softmax probability over its causal range 0..P_i (0 for j > P_i).
  * Entries j >= ctx_len[b] are not written.  Optional outputs: lse, and
- * o_full, the full layer's own attention output, fp32 [B][n_heads][128]:
- *   o_full[b][h][:] = sum_j p_hj v_j      (times v_scale for E4M3 caches).
- * o_full needs v (HS2_EINVAL without it) and is implemented for decode
- * (tile_q = 1; HS2_EUNSUPPORTED for prefill); the second K pass then also
- * streams V.  With bf16 or E4M3 caches the scores are summed over heads in
- * a different order than without o_full (same values up to rounding); with
- * fp32 caches they are the same bits.
+ * o_full, the full layer's own attention output, fp32 [B][n_q][n_heads][128]:
+ *   o_full[b][i][h][:] = sum_j p_ihj v_j      (times v_scale for E4M3 caches)
+ * (zero for a query before the cache start).  o_full needs v (HS2_EINVAL
+ * without it).  Decode: the second K pass also streams V, and with bf16 or
+ * E4M3 caches the scores are summed over heads in a different order than
+ * without o_full (same values up to rounding; fp32 caches: the same bits).
+ * Prefill: the scores are the same bits as without o_full, and one more pass
+ * over K and V computes the output from the statistics of the first.
  * v may be NULL when o_full is NULL.
  */
 HS2_API hs2_status hs2_full_attn_scores(const hs2_attn_desc* desc, const void* q,

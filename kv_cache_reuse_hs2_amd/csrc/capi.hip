@@ -125,11 +125,7 @@ hs2_status hs2_full_attn_scores(const hs2_attn_desc* desc, const void* q, const 
   hs2_status s = check_desc(desc);
   if (s != HS2_OK) return s;
   if (q == nullptr || k == nullptr || ctx_len == nullptr || scores == nullptr) return HS2_EINVAL;
-  if (o_full != nullptr) {
-    if (v == nullptr) return HS2_EINVAL;
-    // The full layer's own output: decode only.
-    if (is_prefill(*desc)) return HS2_EUNSUPPORTED;
-  }
+  if (o_full != nullptr && v == nullptr) return HS2_EINVAL;
   if ((s = check_cache(desc, kv_stride, kv_capacity)) != HS2_OK) return s;
   if (misaligned(q) || misaligned(k) || misaligned(v) || misaligned(ctx_len) ||
       misaligned(scores) || misaligned(o_full) || misaligned(lse))
@@ -137,6 +133,17 @@ hs2_status hs2_full_attn_scores(const hs2_attn_desc* desc, const void* q, const 
   if ((s = check_ws(*desc, kv_capacity, ws, ws_bytes)) != HS2_OK) return s;
   (void)hipGetLastError();
   const WsLayout l = ws_layout(*desc, kv_capacity);
+  if (o_full != nullptr && is_prefill(*desc)) {
+    // Scores (and the per-row statistics, kept in the workspace), then the
+    // output pass that reads those statistics.
+    const hipError_t e = launch_prefill_scores(*desc, q, k, kv_stride, ctx_len, kv_capacity,
+                                               scores, lse, static_cast<char*>(ws) + l.score,
+                                               false, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return launched(e);
+    return launched(launch_prefill_out(*desc, q, k, v, kv_stride, ctx_len, kv_capacity, o_full,
+                                       static_cast<char*>(ws) + l.score,
+                                       static_cast<hipStream_t>(stream)));
+  }
   if (o_full != nullptr)
     return launched(launch_score_full(*desc, q, k, v, kv_stride, ctx_len, kv_capacity, scores,
                                       o_full, lse, static_cast<char*>(ws) + l.score,

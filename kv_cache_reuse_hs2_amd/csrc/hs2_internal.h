@@ -284,6 +284,12 @@ hipError_t launch_select_blocks(const hs2_attn_desc& d, int block, const float* 
 
 // Chunked prefill (tile_q > 1, bf16): scoring over query tiles and sparse
 // attention of the tiles' queries.
+// Prefill: the full layer's own output (after launch_prefill_scores, whose
+// statistics it reads from the workspace), fp32 [B][n_q][H][128].
+hipError_t launch_prefill_out(const hs2_attn_desc& d, const void* q, const void* k,
+                              const void* v, int64_t kv_stride, const int32_t* ctx_len, int cap,
+                              float* o_full, char* ws, hipStream_t st);
+
 hipError_t launch_prefill_scores(const hs2_attn_desc& d, const void* q, const void* k,
                                  int64_t kv_stride, const int32_t* ctx_len, int cap,
                                  float* scores, float* lse, char* ws, bool with_hist,

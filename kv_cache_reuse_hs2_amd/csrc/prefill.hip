@@ -234,7 +234,7 @@ __global__ __launch_bounds__(1024) void pf_stats(PfArgs a) {
 // Fold the split statistics of the workgroup's 16 x 32 rows into L (base 2;
 // +inf for padded heads and empty rows so that 2^(x - L) = 0).
 __device__ void fold_rows(const PfArgs& a, int b, int rb, int N, float* s_L, bool write_lse) {
-  const int t = threadIdx.x;  // 1024 threads = 16 queries x 32 heads... x 2 halves
+  const int t = threadIdx.x;  // threads t < 512: one (query, head) row each
   if (t < 16 * 32) {
     const int qi = t >> 5, h = t & 31, i = rb * 16 + qi;
     const int P_last = N - a.n_q + rb * 16 + 15;
@@ -336,6 +336,157 @@ __global__ __launch_bounds__(1024) void pf_colsum(PfArgs a) {
   asm volatile("" ::: "memory");
   __builtin_amdgcn_sched_barrier(0);
   block_sum(nblk - 1);
+}
+
+// ---------------------------------------------------------------------------
+// The full layer's own output, o_full[i][h] = sum_j p_ihj v_j over each
+// query's causal range, exactly normalised with the statistics of pf_stats
+// (p = 2^(x - L), no running rescale).  A 512-thread workgroup owns 8
+// consecutive queries (a wave each) over all their keys, so no partial
+// outputs need merging, and a wave has 256 registers for O (four 32x32
+// fp32 tiles), Q and the logit tile.  K and V blocks of 64 keys come through
+// a ring of LDS slots like the scoring passes (rotated chunk layout); after
+// the block's barrier the workgroup transposes V into vt (wave w: dims
+// 16w .. 16w + 15, lane: key) and a second barrier publishes it.  K is the
+// A operand, so a lane holds one head over 16 keys, which is the B layout of
+// P^T: O^T += V^T P^T with p as a bf16 high and low part (residual below
+// 2^-17 of p).
+constexpr int kOutWaves = 8;
+
+// 64 rows by the 8 waves of a 512-thread workgroup: wave w moves rows
+// 8w .. 8w + 7 in two loads, lane l the stored chunk l % 16 of a row.
+template <typename RowOf>
+__device__ __forceinline__ void dma_block_w8(uint8_t* slot, const uint16_t* base, RowOf row_of) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+#pragma unroll
+  for (int k = 0; k < 2; ++k) {
+    const int r = 8 * wave + 4 * k + (lane >> 4);
+    const int c = (lane & 15) ^ (r & 15);
+    __builtin_amdgcn_global_load_lds(base + (size_t)row_of(r) * kHeadDim + 8 * c,
+                                     (lds_void_t*)(slot + wave * 2048 + k * 1024), 16, 0, 0);
+  }
+}
+
+__global__ __launch_bounds__(512) void pf_out(PfArgs a, float* __restrict__ o_full) {
+  const int b = blockIdx.y;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int r32 = lane & 31, hh = lane >> 5;
+  const int N = clamp_ctx(a.ctx_len, b, a.cap);
+  const int i = blockIdx.x * kOutWaves + wave;
+  const int P = N - a.n_q + i;
+  const int P_last = N - a.n_q + blockIdx.x * kOutWaves + kOutWaves - 1;
+  f32x16_t o[4] = {{}, {}, {}, {}};  // O^T: dims 32t + 8(r/4) + 4hh + r%4, head r32
+  if (P_last >= 0) {
+    __shared__ struct __attribute__((aligned(16))) {
+      uint8_t ring[kRing][2][kSlotB];  // [slot][K, V]
+      uint16_t vt[kHeadDim][kVtP];
+      float s_L[16 * 32];
+    } sm;
+    // Statistics of the enclosing 16-query block; this workgroup is one half.
+    fold_rows(a, b, blockIdx.x >> 1, N, sm.s_L, false);
+    bf16x8_t qr[8];
+    load_q(a.q + ((size_t)b * a.n_q + i) * a.H * kHeadDim, a.H, r32, hh, P >= 0, qr);
+    // +inf for padded heads and queries that see no key, so that p = 0.
+    const float Lh = sm.s_L[((blockIdx.x & 1) * kOutWaves + wave) * 32 + r32];
+    const int j1 = P_last + 1;
+    const uint16_t* kb = a.k + (size_t)b * a.kv_stride;
+    const uint16_t* vb = a.v + (size_t)b * a.kv_stride;
+    const int nblk = (j1 + kBlk - 1) / kBlk;
+    auto issue = [&](int bi) {
+      auto rows = [=](int r) { return min(bi * kBlk + r, j1 - 1); };
+      dma_block_w8(sm.ring[bi % kRing][0], kb, rows);
+      dma_block_w8(sm.ring[bi % kRing][1], vb, rows);
+    };
+    __builtin_amdgcn_s_waitcnt(0 | (7 << 4));  // vmcnt(0) lgkmcnt(0): Q
+    issue(0);
+    if (nblk > 1) issue(1);
+    for (int bi = 0; bi < nblk; ++bi) {
+      // Block bi (four loads per wave) has landed for every wave once the
+      // younger block's four are all that is in flight; the slot of block
+      // bi - 1 and vt are free after the barrier.
+      if (bi + 1 < nblk)
+        __builtin_amdgcn_s_waitcnt(4 | (7 << 4));  // vmcnt(4) lgkmcnt(0)
+      else
+        __builtin_amdgcn_s_waitcnt(0 | (7 << 4));
+      __builtin_amdgcn_s_barrier();
+      asm volatile("" ::: "memory");
+      __builtin_amdgcn_sched_barrier(0);
+      if (bi + 2 < nblk) issue(bi + 2);
+      const uint8_t* ks = sm.ring[bi % kRing][0];
+      const uint8_t* vs = sm.ring[bi % kRing][1];
+      // Key `lane` goes to column vpos (bits 2 and 3 swapped), so that the
+      // eight keys of one MFMA operand sit side by side (see below).
+      const int vpos = (lane & ~12) | ((lane & 4) << 1) | ((lane & 8) >> 1);
+#pragma unroll
+      for (int cc = 0; cc < 2; ++cc) {
+        // Chunk c = 2w + cc (dims 8c .. 8c + 7) of key row `lane`, stored at
+        // chunk position c ^ (lane % 16).
+        const int c = 2 * wave + cc;
+        const u32x4 x = *reinterpret_cast<const u32x4*>(vs + lane * (kHeadDim * 2) +
+                                                         16 * (c ^ (lane & 15)));
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          sm.vt[8 * c + 2 * e][vpos] = (uint16_t)(x[e] & 0xFFFFu);
+          sm.vt[8 * c + 2 * e + 1][vpos] = (uint16_t)(x[e] >> 16);
+        }
+      }
+      __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0)
+      __builtin_amdgcn_s_barrier();
+      asm volatile("" ::: "memory");
+      __builtin_amdgcn_sched_barrier(0);
+      const int kb0 = bi * kBlk;
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt) {
+        f32x16_t acc = {};
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k_opnd_ring(ks, 32 * mt + r32, e, hh),
+                                                        qr[e], acc, 0, 0, 0);
+        // acc[r]: head r32, key kb0 + 32mt + 8(r/4) + 4hh + r%4.  The MFMA
+        // k index 8hh + jj of step sp stands for the lane's p[8sp + jj], key
+        // 32mt + 16sp + 8(jj/4) + 4hh + jj%4, in A (V^T) and B (P^T) alike;
+        // that key's vt column is 32mt + 16sp + 8hh + jj.
+#pragma unroll
+        for (int sp = 0; sp < 2; ++sp) {
+          u32x4 phi, plo;
+#pragma unroll
+          for (int jj = 0; jj < 4; ++jj) {
+            float pp[2];
+#pragma unroll
+            for (int u = 0; u < 2; ++u) {
+              const int r = 8 * sp + 2 * jj + u;
+              const int j = kb0 + 32 * mt + 8 * (r >> 2) + 4 * hh + (r & 3);
+              pp[u] = (j <= P) ? fast_exp2(fmaf(acc[r], a.c2, -Lh)) : 0.f;
+            }
+            const uint16_t h0 = f32_to_bf16_rne(pp[0]), h1 = f32_to_bf16_rne(pp[1]);
+            const uint16_t l0 = f32_to_bf16_rne(pp[0] - bf16_to_f32(h0));
+            const uint16_t l1 = f32_to_bf16_rne(pp[1] - bf16_to_f32(h1));
+            phi[jj] = (uint32_t)h0 | ((uint32_t)h1 << 16);
+            plo[jj] = (uint32_t)l0 | ((uint32_t)l1 << 16);
+          }
+#pragma unroll
+          for (int t = 0; t < 4; ++t) {
+            const u32x4 av =
+                *reinterpret_cast<const u32x4*>(&sm.vt[32 * t + r32][32 * mt + 16 * sp + 8 * hh]);
+            o[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(av), as_bf16x8(phi), o[t],
+                                                           0, 0, 0);
+            o[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(av), as_bf16x8(plo), o[t],
+                                                           0, 0, 0);
+          }
+        }
+      }
+    }
+  }
+  // Queries before the cache start and padded heads have p = 0, so O = 0.
+  if (r32 < a.H) {
+    float* orow = o_full + (((size_t)b * a.n_q + i) * a.H + r32) * kHeadDim;
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+#pragma unroll
+      for (int g = 0; g < 4; ++g)
+        *reinterpret_cast<f32x4*>(orow + 32 * t + 8 * g + 4 * hh) =
+            f32x4{o[t][4 * g], o[t][4 * g + 1], o[t][4 * g + 2], o[t][4 * g + 3]};
+  }
 }
 
 // I_t[j] = sum over the tile's 16-query blocks (in order) of their column
@@ -567,6 +718,28 @@ hipError_t launch_prefill_scores(const hs2_attn_desc& d, const void* q, const vo
   } else {
     pf_reduce<false><<<gr, 256, 0, st>>>(a, scores, nullptr);
   }
+  return hipGetLastError();
+}
+
+hipError_t launch_prefill_out(const hs2_attn_desc& d, const void* q, const void* k,
+                              const void* v, int64_t kv_stride, const int32_t* ctx_len, int cap,
+                              float* o_full, char* ws, hipStream_t st) {
+  const PrefillWs w = prefill_ws(d, cap);
+  PfArgs a{};
+  a.q = static_cast<const uint16_t*>(q);
+  a.k = static_cast<const uint16_t*>(k);
+  a.v = static_cast<const uint16_t*>(v);
+  a.kv_stride = kv_stride;
+  a.ctx_len = ctx_len;
+  a.cap = cap;
+  a.n_q = d.n_q;
+  a.H = d.n_heads;
+  a.tile_q = d.tile_q;
+  a.split = kPfSplit;
+  a.nsplit = (cap + kPfSplit - 1) / kPfSplit;
+  a.c2 = d.sm_scale * 1.4426950408889634f;
+  a.stats = reinterpret_cast<float2*>(ws + w.stats_off);
+  pf_out<<<dim3(d.n_q / kOutWaves, d.batch), 512, 0, st>>>(a, o_full);
   return hipGetLastError();
 }
 

@@ -92,7 +92,8 @@ def run_scores(buf: DecodeBuffers, stream=None) -> None:
 
 
 def run_scores_full(buf: DecodeBuffers, o_full: torch.Tensor, stream=None) -> None:
-    """Scoring that also writes the full layer's own output o_full, fp32 [B][H][128]."""
+    """Scoring that also writes the full layer's own output o_full, fp32
+    [B][n_q][H][128] (decode: n_q = 1, so [B][H][128] is the same memory)."""
     hs2_full_attn_scores(buf.desc, buf.q, buf.k, buf.v, buf.kv_stride, buf.ctx_len, buf.cap,
                          buf.scores, o_full, buf.lse_full, buf.ws, stream)
 

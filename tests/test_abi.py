@@ -103,12 +103,16 @@ def test_invalid_pointers_sizes_and_workspace(lib):
     assert _scores(d, ctx=None) == hs2.HS2_EINVAL
     assert _scores(d, sc=None) == hs2.HS2_EINVAL
     assert _scores(d, of=FAKE) == hs2.HS2_EINVAL          # o_full needs v
-    # o_full: decode only (prefill is unsupported); validation runs first
+    # o_full with every cache type and with prefill: validation still runs
+    # first (none of these calls reaches a kernel)
     f32 = _desc(dtype=hs2.HS2_F32)
     assert _scores(f32, of=FAKE, v=FAKE,
                    nbytes=hs2.hs2_workspace_size(f32, 4096) - 1) == hs2.HS2_EWORKSPACE
-    assert _scores(_desc(batch=1, n_q=64, tile_q=64), of=FAKE, v=FAKE,
-                   stride=(4096 + 64) * 128) == hs2.HS2_EUNSUPPORTED
+    pf = _desc(batch=1, n_q=64, tile_q=64)
+    assert _scores(pf, of=FAKE, stride=(4096 + 64) * 128) == hs2.HS2_EINVAL
+    assert _scores(pf, of=FAKE, v=FAKE, stride=(4096 + 64) * 128,
+                   nbytes=hs2.hs2_workspace_size(pf, 4096) - 1) == hs2.HS2_EWORKSPACE
+    assert _scores(pf, of=ODD, v=FAKE, stride=(4096 + 64) * 128) == hs2.HS2_EALIGN
     assert _scores(d, of=ODD, v=FAKE) == hs2.HS2_EALIGN
     assert _scores(d, of=FAKE, v=ODD) == hs2.HS2_EALIGN
     assert _scores(d, cap=0) == hs2.HS2_EINVAL

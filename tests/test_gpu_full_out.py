@@ -1,9 +1,11 @@
-"""GPU parity of the full layer's own output (decode scoring with o_full).
+"""GPU parity of the full layer's own output (scoring with o_full).
 
 The full-attention layer of a hybrid block produces its attention output
 besides the selection ([Origins] "KV Reuse and Token-Level Sparse
-Selection").  With o_full the second K pass also streams V and accumulates
+Selection").  Decode: the second K pass also streams V and accumulates
 sum_j p_hj v_j per 4,096-key chunk; the chunk partials are added in order.
+Prefill: a third pass over K and V, exactly normalised with the first pass's
+statistics, one workgroup per 8 queries over all their keys.
 
 Bar: scores as without o_full (relative 1e-4); o_full max |gpu - oracle| <=
 1e-4 * max|v|.  Both sides use the same stored bf16 (or E4M3-widened) values;
@@ -20,7 +22,7 @@ import torch
 
 import oracle
 from gpu_helpers import assert_scores_close
-from workloads import WORKLOADS, make_decode_inputs
+from workloads import WORKLOADS, make_decode_inputs, make_prefill_inputs
 
 pytestmark = pytest.mark.gpu
 
@@ -130,3 +132,54 @@ def test_scores_with_and_without_full_output_agree(hs2):
     bb = buf.scores.cpu().numpy().astype(np.float64)
     for b, n in enumerate(inp["ctx_len"]):
         np.testing.assert_allclose(bb[b, :, :n], a[b, :, :n], rtol=2e-6, atol=0)
+
+
+PREFILL_CASES = [
+    # name, batch, heads, ctx_lens, capacity, n_q, tile_q
+    ("one_tile", 1, 32, [1200], 1200, 64, 64),
+    ("two_tiles_splits", 1, 32, [20000], 20000, 128, 64),
+    ("ragged_batch", 2, 32, [9000, 5000], 9000, 64, 64),
+    ("heads7_tile16", 1, 7, [4000], 4000, 64, 16),
+    ("heads1_tile32", 2, 1, [3100, 2600], 3100, 96, 32),
+    ("before_cache_start", 1, 32, [40], 64, 64, 64),
+    ("one_key", 1, 5, [1], 64, 16, 16),
+]
+
+
+def _prefill_buffers(name, bsz, heads, ctx, cap, n_q, tile_q):
+    from kv_cache_reuse_hs2_amd.torch_api import make_buffers
+
+    w = WORKLOADS["prefill_bf16_128k_8k"].replace(batch=bsz, n_heads=heads)
+    inp = make_prefill_inputs(w, ctx_lens=ctx, n_q=n_q, capacity=cap)
+    buf = make_buffers(inp, n_heads=w.n_heads, k_top=w.k_top, window=w.window,
+                       sm_scale=w.sm_scale, dtype="bf16", n_q=n_q, tile_q=tile_q)
+    return w, inp, buf
+
+
+@pytest.mark.parametrize("name,bsz,heads,ctx,cap,n_q,tile_q", PREFILL_CASES,
+                         ids=[c[0] for c in PREFILL_CASES])
+def test_prefill_full_output_matches_oracle(hs2, name, bsz, heads, ctx, cap, n_q, tile_q):
+    from kv_cache_reuse_hs2_amd.torch_api import run_scores, run_scores_full
+
+    w, inp, buf = _prefill_buffers(name, bsz, heads, ctx, cap, n_q, tile_q)
+    _say(f"prefill full output {name} ctx={ctx} n_q={n_q} tile={tile_q} H={heads}")
+    run_scores(buf)
+    torch.cuda.synchronize()
+    plain, plain_lse = buf.scores.clone(), buf.lse_full.clone()
+    o_full = torch.full((bsz, n_q, heads, 128), float("nan"), device="cuda")
+    run_scores_full(buf, o_full)
+    torch.cuda.synchronize()
+    # the scores come from the same passes with or without o_full
+    for b, n in enumerate(inp["ctx_len"]):
+        assert torch.equal(buf.scores[b, :, :n], plain[b, :, :n])
+    assert torch.equal(buf.lse_full, plain_lse)
+    ref, o_ref, lse = oracle.full_attn_scores(inp["q"], inp["k"], inp["ctx_len"], tile_q=tile_q,
+                                              sm_scale=w.sm_scale, v=inp["v"])
+    assert_scores_close(buf.scores.cpu().numpy(), ref, inp["ctx_len"])
+    got = o_full.cpu().numpy().astype(np.float64)
+    vmax = max(np.abs(inp["v"]).max(), 1e-30)
+    err = np.abs(got - o_ref)
+    assert err.max() <= 1e-4 * vmax, f"o_full max abs {err.max():.3e} (max|v| {vmax:.3e})"
+    # queries before the cache start see no key: output exactly 0
+    dead = ~np.isfinite(lse)
+    assert np.all(got[dead] == 0.0)

@@ -104,6 +104,20 @@ def test_full_output_graph_replays(hs2):
                    lambda: run_scores(other))
 
 
+def test_prefill_full_output_graph_replays(hs2):
+    from kv_cache_reuse_hs2_amd.torch_api import make_buffers, run_scores, run_scores_full
+
+    w = WORKLOADS["prefill_bf16_128k_8k"].replace(batch=2)
+    inp = make_prefill_inputs(w, ctx_lens=[9000, 3000], n_q=128, capacity=9000)
+    buf = make_buffers(inp, n_heads=w.n_heads, k_top=w.k_top, window=w.window,
+                       sm_scale=w.sm_scale, dtype="bf16", n_q=128, tile_q=64)
+    _, _, other = _decode_buffers("decode_bf16_256k_b4", dict(batch=1), [3000])
+    o_full = torch.empty((2, 128, w.n_heads, 128), device="cuda")
+    _say("graph replays of prefill scoring with the full layer's output")
+    _check_replays(lambda: run_scores_full(buf, o_full), [buf.scores, buf.lse_full, o_full],
+                   lambda: run_scores(other))
+
+
 def test_prefill_step_graph_replays(hs2):
     from kv_cache_reuse_hs2_amd.torch_api import make_buffers, run_fused_step, run_scores
 
