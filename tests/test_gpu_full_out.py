@@ -183,3 +183,34 @@ def test_prefill_full_output_matches_oracle(hs2, name, bsz, heads, ctx, cap, n_q
     # queries before the cache start see no key: output exactly 0
     dead = ~np.isfinite(lse)
     assert np.all(got[dead] == 0.0)
+
+
+def test_prefill_full_output_full_size_sampled(hs2):
+    """8,192 new queries on a 131,072-token cache (139,264 keys), the shape the
+    benchmark times: a seeded sample of 16-query blocks is checked against the
+    oracle, each with the context that ends at its last query (its queries see
+    exactly those keys)."""
+    from kv_cache_reuse_hs2_amd.torch_api import make_buffers, run_scores_full
+
+    w = WORKLOADS["prefill_bf16_128k_8k"]
+    inp = make_prefill_inputs(w)
+    n_q, n = w.n_q, w.ctx_len
+    buf = make_buffers(inp, n_heads=w.n_heads, k_top=w.k_top, window=w.window,
+                       sm_scale=w.sm_scale, dtype="bf16", n_q=n_q, tile_q=w.tile_q)
+    o_full = torch.full((1, n_q, w.n_heads, 128), float("nan"), device="cuda")
+    _say(f"prefill full output at full size n_q={n_q} ctx={n}")
+    run_scores_full(buf, o_full)
+    torch.cuda.synchronize()
+    got_all = o_full.cpu().numpy()
+    vmax = max(np.abs(inp["v"]).max(), 1e-30)
+    rng = np.random.default_rng(41)
+    blocks = sorted(set([0, 1, 255, 511] + list(rng.integers(0, n_q // 16, 2))))
+    for blk in blocks:
+        q0 = 16 * blk
+        ctx_t = np.array([n - n_q + q0 + 16], dtype=np.int32)
+        _, o_ref, _ = oracle.full_attn_scores(inp["q"][:, q0:q0 + 16], inp["k"][:, :ctx_t[0]],
+                                              ctx_t, tile_q=16, sm_scale=w.sm_scale,
+                                              v=inp["v"][:, :ctx_t[0]])
+        err = np.abs(got_all[:, q0:q0 + 16].astype(np.float64) - o_ref)
+        assert err.max() <= 1e-4 * vmax, f"block {blk}: max abs {err.max():.3e}"
+        _say(f"block {blk} ok")

@@ -114,6 +114,23 @@ def test_prefill_step_padded_cache(hs2):
     _same(_outs(padded), _outs(dense), ctx)
 
 
+def test_prefill_full_output_padded_cache(hs2):
+    from kv_cache_reuse_hs2_amd.torch_api import make_buffers, run_scores_full
+
+    ctx = [7000, 2600]
+    w = WORKLOADS["prefill_bf16_128k_8k"].replace(batch=2)
+    inp = make_prefill_inputs(w, ctx_lens=ctx, n_q=128, capacity=max(ctx))
+    mk = lambda: make_buffers(inp, n_heads=w.n_heads, k_top=w.k_top, window=w.window,  # noqa: E731
+                              sm_scale=w.sm_scale, dtype="bf16", n_q=128, tile_q=64)
+    dense, padded = mk(), _pad_buffers(mk(), ctx)
+    o_d = torch.empty((2, 128, w.n_heads, 128), device="cuda")
+    o_p = torch.empty_like(o_d)
+    _say("prefill scoring with the full layer's output on a padded cache")
+    run_scores_full(dense, o_d)
+    run_scores_full(padded, o_p)
+    _same([padded.scores, padded.lse_full, o_p], [dense.scores, dense.lse_full, o_d], ctx)
+
+
 @pytest.mark.parametrize("window", [128, 300])
 def test_swa_padded_cache(hs2, window):
     import kv_cache_reuse_hs2_amd as h
