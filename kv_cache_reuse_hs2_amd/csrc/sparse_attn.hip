@@ -141,13 +141,31 @@ __device__ __forceinline__ void segment_gather_bf16(const void* __restrict__ k,
     }
 }
 
-// Partial of one query over the gathered segment (kr, L.vt): (max, sum) per
-// head to mlo[H] and o to po[H][D]; qb is the query's [H][D] rows.  Called by
-// every thread of the workgroup, after segment_gather_bf16; its barriers also
-// order the gather's LDS writes before the PV reads.  The LDS statistics and
-// partials are free again when it returns.
+// Q^T of one query as the B operand of QK^T (lane: head r32, dims
+// step_dim(e, hh) in step e; heads >= H and waves past the segment's zero).
+// Loaded by the callers ahead of the gather, so that its round trip overlaps
+// the gather's (or the selection's).
 template <bool kFp8>
-__device__ __forceinline__ void segment_query_bf16(const uint16_t* __restrict__ qb, int H,
+__device__ __forceinline__ void load_q_segment(const uint16_t* __restrict__ qb, int H,
+                                               bf16x8_t (&qreg)[8]) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int r32 = lane & 31, hh = lane >> 5;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    u32x4 xq = {0u, 0u, 0u, 0u};
+    if (wave < kSegWaves && r32 < H)
+      xq = *reinterpret_cast<const u32x4*>(qb + r32 * kHeadDim + step_dim<kFp8>(e, hh));
+    qreg[e] = as_bf16x8(xq);
+  }
+}
+
+// Partial of one query over the gathered segment (kr, L.vt): (max, sum) per
+// head to mlo[H] and o to po[H][D]; qreg holds the query (load_q_segment).
+// Called by every thread of the workgroup, after segment_gather_bf16; its
+// barriers also order the gather's LDS writes before the PV reads.  The LDS
+// statistics and partials are free again when it returns.
+template <bool kFp8>
+__device__ __forceinline__ void segment_query_bf16(const bf16x8_t (&qreg)[8], int H,
                                                    float c2, const QueryGeom& qg, int s0,
                                                    const u32x4 (&kr)[8], SegLds& L,
                                                    float* __restrict__ po,
@@ -159,15 +177,6 @@ __device__ __forceinline__ void segment_query_bf16(const uint16_t* __restrict__ 
   const bool wave_live = active && pw < qg.S;
   float x[16];
   if (active) {
-    // Q^T as the B operand.
-    bf16x8_t qreg[8];
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      u32x4 xq = {0u, 0u, 0u, 0u};
-      if (r32 < H)
-        xq = *reinterpret_cast<const u32x4*>(qb + r32 * kHeadDim + step_dim<kFp8>(e, hh));
-      qreg[e] = as_bf16x8(xq);
-    }
     f32x16_t acc = {};
 #pragma unroll
     for (int e = 0; e < 8; ++e)
@@ -260,12 +269,12 @@ __device__ __forceinline__ void segment_query_bf16(const uint16_t* __restrict__ 
 // Gather and partial of one query (one sparse layer).
 template <bool kFp8, typename KeyAt>
 __device__ __forceinline__ void segment_partial_bf16(
-    const uint16_t* __restrict__ q, const void* __restrict__ k, const void* __restrict__ v,
-    int64_t kv_stride, int b, int bq, int H, float c2, const QueryGeom& qg, int s0,
+    const bf16x8_t (&qreg)[8], const void* __restrict__ k, const void* __restrict__ v,
+    int64_t kv_stride, int b, int H, float c2, const QueryGeom& qg, int s0,
     KeyAt key_at, SegLds& L, float* __restrict__ po, float2* __restrict__ mlo) {
   u32x4 kr[8];
   segment_gather_bf16<kFp8>(k, v, kv_stride, b, qg, s0, key_at, L, kr);
-  segment_query_bf16<kFp8>(q + (size_t)bq * H * kHeadDim, H, c2, qg, s0, kr, L, po, mlo);
+  segment_query_bf16<kFp8>(qreg, H, c2, qg, s0, kr, L, po, mlo);
 }
 
 template <bool kFp8>
@@ -286,9 +295,11 @@ __global__ __launch_bounds__(64 * kSegWaves) void sparse_partial_bf16(
     return;
   }
   const int32_t* top_row = top_idx + (size_t)(b * tiles + g) * k_top;
-  segment_partial_bf16<kFp8>(q, k, v, kv_stride, b, bq, H, c2, qg, s0,
+  bf16x8_t qreg[8];
+  load_q_segment<kFp8>(q + (size_t)bq * H * kHeadDim, H, qreg);
+  segment_partial_bf16<kFp8>(qreg, k, v, kv_stride, b, H, c2, qg, s0,
                              [&](int p) { return sel_key(qg, top_row, p); }, lds,
-                       part + ((size_t)bq * nseg + seg) * H * kHeadDim, mlo);
+                             part + ((size_t)bq * nseg + seg) * H * kHeadDim, mlo);
 }
 
 // ---------------------------------------------------------------------------
@@ -319,9 +330,11 @@ __global__ __launch_bounds__(64 * kSegWaves) void sparse_layers_bf16(
                             [&](int p) { return sel_key(qg, top_row, p); }, lds, kr);
   for (int l = 0; l < n_layers; ++l) {
     const int row = l * B + b;
-    segment_query_bf16<kFp8>(q_layers + (size_t)row * H * kHeadDim, H, c2, qg, s0, kr, lds,
-                       part + ((size_t)row * nseg + seg) * H * kHeadDim,
-                       ml + ((size_t)row * nseg + seg) * H);
+    bf16x8_t qreg[8];
+    load_q_segment<kFp8>(q_layers + (size_t)row * H * kHeadDim, H, qreg);
+    segment_query_bf16<kFp8>(qreg, H, c2, qg, s0, kr, lds,
+                             part + ((size_t)row * nseg + seg) * H * kHeadDim,
+                             ml + ((size_t)row * nseg + seg) * H);
   }
 }
 
@@ -357,6 +370,9 @@ __global__ __launch_bounds__(kTailThreads) void decode_tail_bf16(
   __shared__ __attribute__((aligned(16))) TailLds lds;
   __shared__ int32_t win[kMaxTop];
   const int seg = blockIdx.x, b = blockIdx.y;  // one query per sequence
+  // The query's loads go out first and complete during the selection.
+  bf16x8_t qreg[8];
+  load_q_segment<kFp8>(q + (size_t)b * H * kHeadDim, H, qreg);
   const RowGeom g = row_geom(ctx_len, cap, b, 1, 1, 1, k_top, window);
   const int n = final_select_row<kTailThreads>(
       b, g, k_top, hist, cnt, meta, list, nslices, seg == 0 ? top_idx + (size_t)b * k_top : nullptr,
@@ -383,8 +399,8 @@ __global__ __launch_bounds__(kTailThreads) void decode_tail_bf16(
     const int idx = p < qg.cnt ? win[p] : qg.wlo + (p - qg.cnt);
     return idx < 0 ? 0 : (idx >= qg.N ? qg.N - 1 : idx);
   };
-  segment_partial_bf16<kFp8>(q, k, v, kv_stride, b, b, H, c2, qg, s0, key_at, lds.seg,
-                       part + ((size_t)b * nseg + seg) * H * kHeadDim, mlo);
+  segment_partial_bf16<kFp8>(qreg, k, v, kv_stride, b, H, c2, qg, s0, key_at, lds.seg,
+                             part + ((size_t)b * nseg + seg) * H * kHeadDim, mlo);
 }
 
 // ---------------------------------------------------------------------------
