@@ -312,6 +312,26 @@ def extra_measurements(steps: int, warmup: int) -> dict:
     from workloads import WORKLOADS, make_decode_inputs, make_prefill_inputs
 
     out = {}
+    # The small fp32 case (one sequence of 4,096 keys, 16 heads): latency only.
+    w = WORKLOADS["decode_f32_4k"]
+    buf = make_buffers(make_decode_inputs(w), n_heads=w.n_heads, k_top=w.k_top, window=w.window,
+                       sm_scale=w.sm_scale, dtype=w.dtype)
+    ms = time_events(lambda: run_fused_step(buf), steps, warmup)
+    g = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        run_fused_step(buf)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g):
+        run_fused_step(buf)
+    ms_g = time_events(g.replay, steps, warmup)
+    out[w.name] = {"us_per_step_eager": round(ms * 1e3, 2),
+                   "us_per_step_graph": round(ms_g * 1e3, 2),
+                   "note": "fp32 cache, VALU kernels; a latency figure, no roofline claim "
+                           "(eager: launch-bound from Python; graph: one-step replays)"}
+    del buf, g
     # Batched decode, 16 x 65,536 keys.
     w = WORKLOADS["decode_bf16_64k_b16"]
     buf = make_buffers(make_decode_inputs(w), n_heads=w.n_heads, k_top=w.k_top, window=w.window,

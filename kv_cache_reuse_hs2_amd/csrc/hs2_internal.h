@@ -14,11 +14,13 @@ constexpr int kMaxTop = 2048;
 constexpr int kMaxWindow = 2048;
 
 // Decode scoring, bf16: both passes take 4,096 keys per workgroup (8 waves x
-// 16 blocks of 32 keys).  fp32: 256 keys
-// per workgroup in both passes.
+// 16 blocks of 32 keys).  fp32: one wave of 64 keys per workgroup in both
+// passes (a thread per key), and the fp32 pass with the full layer's output
+// works through 256-key sub-blocks.
 constexpr int kP1Chunk = 4096;
 constexpr int kP2Chunk = 4096;
-constexpr int kF32Chunk = 256;
+constexpr int kF32Chunk = 64;
+constexpr int kF32Sub = 256;
 // Chunked prefill: keys per workgroup of the scoring passes.
 constexpr int kPfSplit = 8192;
 // Keys per workgroup of the sparse gather kernel.

@@ -513,8 +513,11 @@ __global__ __launch_bounds__(32 * kCombGroups) void full_out_combine(
 }
 
 // fp32 VALU kernel: MODE 0 writes per-chunk statistics, MODE 1 importance.
-template <int MODE>
-__global__ __launch_bounds__(256) void score_f32(
+// One wave, a thread per key; kHB >= H heads are computed (8, 16 or 32; the
+// rows past H are zero), each logit as one fma chain over the 128 dims in
+// order, the same chain score_full_f32 runs, so both write the same bits.
+template <int MODE, int kHB>
+__global__ __launch_bounds__(kF32Chunk) void score_f32(
     const float* __restrict__ q, const float* __restrict__ k, int64_t kv_stride,
     const int32_t* __restrict__ ctx_len, int cap, int H, float c2,
     float2* __restrict__ stats, int nchunks, const float* __restrict__ lse2,
@@ -524,9 +527,9 @@ __global__ __launch_bounds__(256) void score_f32(
   const int N = clamp_ctx(ctx_len, b, cap);
   const int j_begin = c * kF32Chunk;
   if (j_begin >= N) return;
-  __shared__ float4 qs[kMaxHeads][kHeadDim / 4];
+  __shared__ float4 qs[kHB][kHeadDim / 4];
   const float* qb = q + (size_t)b * H * kHeadDim;
-  for (int e = threadIdx.x; e < kMaxHeads * kHeadDim / 4; e += blockDim.x) {
+  for (int e = threadIdx.x; e < kHB * kHeadDim / 4; e += blockDim.x) {
     const int h = e / (kHeadDim / 4), d4 = e % (kHeadDim / 4);
     qs[h][d4] = h < H ? reinterpret_cast<const float4*>(qb + h * kHeadDim)[d4] : make_float4(0.f, 0.f, 0.f, 0.f);
   }
@@ -534,13 +537,16 @@ __global__ __launch_bounds__(256) void score_f32(
   const int j = j_begin + threadIdx.x;
   const bool valid = j < N;
   const float4* kp = reinterpret_cast<const float4*>(k + (size_t)b * kv_stride + (size_t)min(j, N - 1) * kHeadDim);
-  float acc[kMaxHeads];
+  float acc[kHB];
 #pragma unroll
-  for (int h = 0; h < kMaxHeads; ++h) acc[h] = 0.f;
+  for (int h = 0; h < kHB; ++h) acc[h] = 0.f;
+  // Unrolled so that a thread's row loads are in flight together (the fma
+  // order is unchanged).
+#pragma unroll 8
   for (int d4 = 0; d4 < kHeadDim / 4; ++d4) {
     const float4 kv = kp[d4];
 #pragma unroll
-    for (int h = 0; h < kMaxHeads; ++h) {
+    for (int h = 0; h < kHB; ++h) {
       const float4 qv = qs[h][d4];
       acc[h] = fmaf(qv.x, kv.x, acc[h]);
       acc[h] = fmaf(qv.y, kv.y, acc[h]);
@@ -552,42 +558,42 @@ __global__ __launch_bounds__(256) void score_f32(
     if (!valid) return;
     float imp = 0.f;
 #pragma unroll
-    for (int h = 0; h < kMaxHeads; ++h)
+    for (int h = 0; h < kHB; ++h)
       if (h < H) imp += fast_exp2(acc[h] * c2 - lse2[b * kMaxHeads + h]);
     scores[(size_t)b * score_stride + j] = imp;
   } else {
-    __shared__ float red[4][kMaxHeads];
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    for (int h = 0; h < kMaxHeads; ++h) {
-      float x = valid ? acc[h] * c2 : -INFINITY;
+    float2* st = stats + ((size_t)b * nchunks + c) * kMaxHeads;
+#pragma unroll
+    for (int h = 0; h < kHB; ++h) {
+      const float x = valid ? acc[h] * c2 : -INFINITY;
       float m = x;
 #pragma unroll
       for (int o = 32; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o));
-      if (lane == 0) red[wave][h] = m;
-      acc[h] = x;
-    }
-    __syncthreads();
-    __shared__ float bmax[kMaxHeads];
-    if (threadIdx.x < kMaxHeads) {
-      float m = red[0][threadIdx.x];
-      for (int w = 1; w < 4; ++w) m = fmaxf(m, red[w][threadIdx.x]);
-      bmax[threadIdx.x] = m;
-    }
-    __syncthreads();
-    for (int h = 0; h < kMaxHeads; ++h) {
-      const float mref = bmax[h] == -INFINITY ? 0.f : bmax[h];
-      float s = fast_exp2(acc[h] - mref);
+      float s = fast_exp2(x - (m == -INFINITY ? 0.f : m));
 #pragma unroll
       for (int o = 32; o > 0; o >>= 1) s += __shfl_xor(s, o);
-      if (lane == 0) red[wave][h] = s;
+      if (threadIdx.x == 0) st[h] = make_float2(m, s);
     }
-    __syncthreads();
-    if (threadIdx.x < kMaxHeads) {
-      float l = 0.f;
-      for (int w = 0; w < 4; ++w) l += red[w][threadIdx.x];
-      stats[((size_t)b * nchunks + c) * kMaxHeads + threadIdx.x] = make_float2(bmax[threadIdx.x], l);
-    }
+    // Heads past the bucket: neutral statistics (never used for a real head).
+    if (threadIdx.x < kMaxHeads - kHB) st[kHB + threadIdx.x] = make_float2(-INFINITY, 0.f);
   }
+}
+
+// The head bucket of H for score_f32.
+template <int MODE>
+void launch_score_f32(dim3 grid, hipStream_t st, const float* q, const float* k,
+                      int64_t kv_stride, const int32_t* ctx_len, int cap, int H, float c2,
+                      float2* stats, int nchunks, const float* lse2, float* scores,
+                      int64_t score_stride) {
+  if (H <= 8)
+    score_f32<MODE, 8><<<grid, kF32Chunk, 0, st>>>(q, k, kv_stride, ctx_len, cap, H, c2, stats,
+                                                   nchunks, lse2, scores, score_stride);
+  else if (H <= 16)
+    score_f32<MODE, 16><<<grid, kF32Chunk, 0, st>>>(q, k, kv_stride, ctx_len, cap, H, c2, stats,
+                                                    nchunks, lse2, scores, score_stride);
+  else
+    score_f32<MODE, 32><<<grid, kF32Chunk, 0, st>>>(q, k, kv_stride, ctx_len, cap, H, c2, stats,
+                                                    nchunks, lse2, scores, score_stride);
 }
 
 // fp32 path with the full layer's own output: workgroup (c, b) takes keys
@@ -608,7 +614,7 @@ __global__ __launch_bounds__(256) void score_full_f32(
   if (j_begin >= N) return;
   const int j_end = min(N, j_begin + kP2Chunk);
   __shared__ float4 qs[kMaxHeads][kHeadDim / 4];
-  __shared__ float ps[kMaxHeads][kF32Chunk];
+  __shared__ float ps[kMaxHeads][kF32Sub];
   const float* qb = q + (size_t)b * H * kHeadDim;
   for (int e = threadIdx.x; e < kMaxHeads * kHeadDim / 4; e += blockDim.x) {
     const int h = e / (kHeadDim / 4), d4 = e % (kHeadDim / 4);
@@ -621,7 +627,7 @@ __global__ __launch_bounds__(256) void score_full_f32(
   float oacc[16];
 #pragma unroll
   for (int i = 0; i < 16; ++i) oacc[i] = 0.f;
-  for (int j0 = j_begin; j0 < j_end; j0 += kF32Chunk) {
+  for (int j0 = j_begin; j0 < j_end; j0 += kF32Sub) {
     __syncthreads();  // q staged; the previous sub-block's ps read
     const int j = j0 + threadIdx.x;
     const bool valid = j < j_end;
@@ -629,6 +635,7 @@ __global__ __launch_bounds__(256) void score_full_f32(
     float acc[kMaxHeads];
 #pragma unroll
     for (int h = 0; h < kMaxHeads; ++h) acc[h] = 0.f;
+#pragma unroll 8
     for (int d4 = 0; d4 < kHeadDim / 4; ++d4) {
       const float4 kv = kp[d4];
 #pragma unroll
@@ -649,7 +656,7 @@ __global__ __launch_bounds__(256) void score_full_f32(
     }
     if (valid) scores[(size_t)b * score_stride + j] = imp;
     __syncthreads();
-    const int nk = min(kF32Chunk, j_end - j0);
+    const int nk = min(kF32Sub, j_end - j0);
     for (int jj = 0; jj < nk; ++jj) {
       const float x = vb[(size_t)(j0 + jj) * kHeadDim + d];
 #pragma unroll
@@ -727,9 +734,8 @@ hipError_t launch_score_full(const hs2_attn_desc& d, const void* q, const void* 
     const int nchunks1 = score_nchunks1(d, cap);
     const auto* qf = static_cast<const float*>(q);
     const auto* kf = static_cast<const float*>(k);
-    score_f32<0><<<dim3(nchunks1, d.batch), 256, 0, st>>>(qf, kf, kv_stride, ctx_len, cap,
-                                                          d.n_heads, d.sm_scale * 1.4426950408889634f,
-                                                          stats, nchunks1, nullptr, nullptr, 0);
+    launch_score_f32<0>(dim3(nchunks1, d.batch), st, qf, kf, kv_stride, ctx_len, cap, d.n_heads,
+                        d.sm_scale * 1.4426950408889634f, stats, nchunks1, nullptr, nullptr, 0);
     score_reduce_f32<<<d.batch, 256, 0, st>>>(stats, nchunks1, ctx_len, cap, d.n_heads, lse2, lse);
     score_full_f32<<<dim3(nchunks2, d.batch), 256, 0, st>>>(
         qf, kf, static_cast<const float*>(v), kv_stride, ctx_len, cap, d.n_heads,
@@ -782,11 +788,11 @@ hipError_t launch_score_decode(const hs2_attn_desc& d, const void* q, const void
     const dim3 grid(nchunks1, d.batch);
     const auto* qf = static_cast<const float*>(q);
     const auto* kf = static_cast<const float*>(k);
-    score_f32<0><<<grid, 256, 0, st>>>(qf, kf, kv_stride, ctx_len, cap, d.n_heads, c2, stats,
-                                       nchunks1, nullptr, nullptr, 0);
+    launch_score_f32<0>(grid, st, qf, kf, kv_stride, ctx_len, cap, d.n_heads, c2, stats,
+                        nchunks1, nullptr, nullptr, 0);
     score_reduce_f32<<<d.batch, 256, 0, st>>>(stats, nchunks1, ctx_len, cap, d.n_heads, lse2, lse);
-    score_f32<1><<<grid, 256, 0, st>>>(qf, kf, kv_stride, ctx_len, cap, d.n_heads, c2, nullptr,
-                                       nchunks1, lse2, scores, cap);
+    launch_score_f32<1>(grid, st, qf, kf, kv_stride, ctx_len, cap, d.n_heads, c2, nullptr,
+                        nchunks1, lse2, scores, cap);
   }
   return hipGetLastError();
 }

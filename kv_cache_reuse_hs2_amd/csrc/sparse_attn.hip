@@ -507,7 +507,7 @@ __global__ __launch_bounds__(256) void sparse_partial_f32(
 }
 
 // ---------------------------------------------------------------------------
-constexpr int kCombRegs = 32;  // segments sparse_combine holds in registers
+constexpr int kCombRegs = 40;  // segments sparse_combine holds in registers
 
 // Merge the segment partials of one (query, head): o = v_scale * sum_s
 // 2^(m_s-M) o_s / sum_s 2^(m_s-M) l_s, segments taken in order (v_scale is
