@@ -507,12 +507,14 @@ __global__ __launch_bounds__(256) void sparse_partial_f32(
 }
 
 // ---------------------------------------------------------------------------
-constexpr int kCombRegs = 40;  // segments sparse_combine holds in registers
+// Segments sparse_combine holds in registers: 16 for the MFMA paths (9
+// segments at the usual budget), 40 for the fp32 path (36).
 
 // Merge the segment partials of one (query, head): o = v_scale * sum_s
 // 2^(m_s-M) o_s / sum_s 2^(m_s-M) l_s, segments taken in order (v_scale is
 // the V cache scale of E4M3 caches, else 1).  One workgroup per (query, head),
 // one thread per output dimension.
+template <int kCombRegs>
 __global__ __launch_bounds__(kHeadDim) void sparse_combine(const float* __restrict__ part,
                                                            const float2* __restrict__ ml, int nseg,
                                                            int H, float v_scale,
@@ -567,6 +569,14 @@ __global__ __launch_bounds__(kHeadDim) void sparse_combine(const float* __restri
     lse[(size_t)bq * H + h] = den > 0.f ? (M + __log2f(den)) * kLn2 : -INFINITY;
 }
 
+void launch_combine(dim3 grid, hipStream_t st, const float* part, const float2* ml, int nseg,
+                    int H, float v_scale, float* o, float* lse) {
+  if (nseg <= 16)
+    sparse_combine<16><<<grid, kHeadDim, 0, st>>>(part, ml, nseg, H, v_scale, o, lse);
+  else
+    sparse_combine<40><<<grid, kHeadDim, 0, st>>>(part, ml, nseg, H, v_scale, o, lse);
+}
+
 // Logit scale in base 2 and output scale of a descriptor (E4M3 caches fold
 // their K scale into the first and V scale into the second).
 float logit_c2(const hs2_attn_desc& d) {
@@ -609,8 +619,8 @@ hipError_t launch_sparse(const hs2_attn_desc& d, const void* q, const void* k, c
         kv_stride, ctx_len, cap, top_idx, top_cnt, d.n_q, d.tile_q, d.k_top, d.window,
         d.n_heads, c2, part, ml, nseg);
   }
-  sparse_combine<<<dim3(d.n_heads, d.batch * d.n_q), kHeadDim, 0, st>>>(
-      part, ml, nseg, d.n_heads, out_scale(d), o, lse);
+  launch_combine(dim3(d.n_heads, d.batch * d.n_q), st, part, ml, nseg, d.n_heads, out_scale(d), o,
+                 lse);
   return hipGetLastError();
 }
 
@@ -636,8 +646,7 @@ hipError_t launch_decode_tail(const hs2_attn_desc& d, const void* q, const void*
     decode_tail_bf16<false><<<grid, kTailThreads, 0, st>>>(
         qq, k, v, kv_stride, ctx_len, cap, d.k_top, d.window, d.n_heads, logit_c2(d), hist, cnt,
         meta, list, select_slices(cap), top_idx, top_cnt, part, ml, nseg);
-  sparse_combine<<<dim3(d.n_heads, d.batch), kHeadDim, 0, st>>>(part, ml, nseg, d.n_heads,
-                                                                 out_scale(d), o, lse);
+  launch_combine(dim3(d.n_heads, d.batch), st, part, ml, nseg, d.n_heads, out_scale(d), o, lse);
   return hipGetLastError();
 }
 
@@ -668,8 +677,8 @@ hipError_t launch_sparse_layers(const hs2_attn_desc& d, int n_layers, const void
     sparse_layers_bf16<false><<<grid, 64 * kSegWaves, 0, st>>>(
         qq, k, v, kv_stride, ctx_len, cap, top_idx, top_cnt, d.batch, d.k_top, d.window,
         d.n_heads, logit_c2(d), n_layers, part, ml, nseg);
-  sparse_combine<<<dim3(d.n_heads, (int)rows), kHeadDim, 0, st>>>(
-      part, ml, nseg, d.n_heads, out_scale(d), o_layers, lse_layers);
+  launch_combine(dim3(d.n_heads, (int)rows), st, part, ml, nseg, d.n_heads, out_scale(d), o_layers,
+                 lse_layers);
   return hipGetLastError();
 }
 
