@@ -177,6 +177,29 @@ def test_sparse_independent_query_and_small_budgets(hs2):
         assert_outputs_close(buf.o.cpu().numpy(), o_ref, "bf16")
 
 
+def test_sparse_f32_budgets(hs2):
+    """fp32 sparse layer at the usual budget (36 segments of 32 keys, merged
+    from registers) and at the largest (128 segments, merged in a loop)."""
+    from kv_cache_reuse_hs2_amd.torch_api import make_buffers, run_sparse, to_device
+
+    w = WORKLOADS["decode_f32_4k"].replace(batch=2)
+    inp = make_decode_inputs(w, ctx_lens=[4096, 1000], capacity=4096)
+    ref, _, _ = _oracle_scores(inp, w)
+    for k_top, window in [(1024, 128), (2048, 2048), (2048, 100)]:
+        top, cnt = oracle.select_topk_window(ref, inp["ctx_len"], n_q=1, tile_q=1, k_top=k_top,
+                                             window=window)
+        buf = make_buffers(inp, n_heads=w.n_heads, k_top=k_top, window=window,
+                           sm_scale=w.sm_scale, dtype="f32")
+        _say(f"fp32 sparse k_top={k_top} window={window}")
+        run_sparse(buf, top_idx=to_device(top), top_cnt=to_device(cnt))
+        torch.cuda.synchronize()
+        o_ref, lse_ref = oracle.sparse_attention(inp["q"], inp["k"], inp["v"], inp["ctx_len"], top,
+                                                 cnt, tile_q=1, window=window,
+                                                 sm_scale=w.sm_scale)
+        assert_outputs_close(buf.o.cpu().numpy(), o_ref, "f32")
+        np.testing.assert_allclose(buf.lse.cpu().numpy(), lse_ref, rtol=1e-5, atol=1e-5)
+
+
 @pytest.mark.parametrize("name,wname,over,ctx", CASES, ids=[c[0] for c in CASES])
 def test_decode_step_end_to_end(hs2, name, wname, over, ctx):
     from kv_cache_reuse_hs2_amd.torch_api import run_step
