@@ -507,13 +507,12 @@ __global__ __launch_bounds__(256) void sparse_partial_f32(
 }
 
 // ---------------------------------------------------------------------------
-// Segments sparse_combine holds in registers: 16 for the MFMA paths (9
-// segments at the usual budget), 40 for the fp32 path (36).
-
 // Merge the segment partials of one (query, head): o = v_scale * sum_s
 // 2^(m_s-M) o_s / sum_s 2^(m_s-M) l_s, segments taken in order (v_scale is
 // the V cache scale of E4M3 caches, else 1).  One workgroup per (query, head),
-// one thread per output dimension.
+// one thread per output dimension.  Up to kCombRegs segments are held in
+// registers (launch_combine picks 16 for the MFMA paths, 9 segments at the
+// usual budget, and 40 for the fp32 path's 36); more go through a loop.
 template <int kCombRegs>
 __global__ __launch_bounds__(kHeadDim) void sparse_combine(const float* __restrict__ part,
                                                            const float2* __restrict__ ml, int nseg,
