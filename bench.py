@@ -480,6 +480,100 @@ def cpu_baseline(w, inp, budget_s: float = 12.0) -> dict:
                       f"workload, one decode step each, fp64 NumPy, {dt:.1f} s"}
 
 
+def cpu_baselines_all(budget_s: float = 8.0) -> dict:
+    """The oracle timed on a bounded sample of every measured shape (host
+    only, nothing on the GPU): whole decode sequences, prefill tiles with the
+    context that ends at each tile, KV Bridging rows, and the sliding-window
+    attention's queries.  Reported beside the GPU figures, never as targets."""
+    import numpy as np
+    from threadpoolctl import threadpool_info
+
+    import oracle
+    from workloads import (WORKLOADS, bf16_bits_to_f32, make_bridge_inputs, make_decode_inputs,
+                           make_prefill_inputs)
+
+    threads = int(max([p.get("num_threads", 1) for p in threadpool_info()] or [1]))
+    out = {"cores": threads}
+
+    def run(fn, n_max):
+        done, t0 = 0, time.perf_counter()
+        while done < n_max:
+            fn(done)
+            done += 1
+            if time.perf_counter() - t0 >= budget_s:
+                break
+        return done, time.perf_counter() - t0
+
+    for name in ("decode_f32_4k", "decode_bf16_64k_b16", "decode_fp8_256k_b4"):
+        w = WORKLOADS[name]
+        inp = make_decode_inputs(w)
+        if w.dtype == "fp8":
+            inp["k"] = oracle.dequant_kv(inp["k_raw"], inp["k_scale"])
+            inp["v"] = oracle.dequant_kv(inp["v_raw"], inp["v_scale"])
+
+        def one(i, w=w, inp=inp):
+            sl = slice(i % w.batch, i % w.batch + 1)
+            ctx = inp["ctx_len"][sl]
+            sc, _, _ = oracle.full_attn_scores(inp["q"][sl], inp["k"][sl], ctx, tile_q=1,
+                                               sm_scale=w.sm_scale)
+            top, cnt = oracle.select_topk_window(sc, ctx, n_q=1, tile_q=1, k_top=w.k_top,
+                                                 window=w.window)
+            oracle.sparse_attention(inp["q"][sl], inp["k"][sl], inp["v"][sl], ctx, top, cnt,
+                                    tile_q=1, window=w.window, sm_scale=w.sm_scale)
+
+        n, dt = run(one, 256)
+        out[name] = {"value": round(n / dt, 3), "unit": "tokens/s",
+                     "sample": f"{n} whole sequences, one decode step each, {dt:.1f} s"}
+        del inp
+    # Prefill: tiles of 64 queries, each with the context ending at its last query.
+    w = WORKLOADS["prefill_bf16_128k_8k"]
+    inp = make_prefill_inputs(w)
+    rng = np.random.default_rng(7)
+    tiles = rng.permutation(w.n_q // w.tile_q)
+
+    def tile(i):
+        t = int(tiles[i])
+        q0, nk = t * w.tile_q, w.ctx_len - w.n_q + (t + 1) * w.tile_q
+        ctx = np.array([nk], dtype=np.int32)
+        qs = inp["q"][:, q0:q0 + w.tile_q]
+        sc, _, _ = oracle.full_attn_scores(qs, inp["k"][:, :nk], ctx, tile_q=w.tile_q,
+                                           sm_scale=w.sm_scale)
+        top, cnt = oracle.select_topk_window(sc, ctx, n_q=w.tile_q, tile_q=w.tile_q,
+                                             k_top=w.k_top, window=w.window)
+        oracle.sparse_attention(qs, inp["k"][:, :nk], inp["v"][:, :nk], ctx, top, cnt,
+                                tile_q=w.tile_q, window=w.window, sm_scale=w.sm_scale)
+
+    n, dt = run(tile, len(tiles))
+    out[w.name] = {"value": round(n * w.tile_q / dt, 2), "unit": "queries/s",
+                   "sample": f"{n} seeded tiles of {w.tile_q} queries (scoring, selection and "
+                             f"sparse layer), {dt:.1f} s"}
+    # Sliding-window attention over the same queries, in blocks of 256.
+    def swa(i):
+        q0 = (i * 256) % w.n_q
+        oracle.swa_attention(inp["q"][:, q0:q0 + 256], inp["k"], inp["v"],
+                             np.array([w.ctx_len - w.n_q + q0 + 256], dtype=np.int32),
+                             window=128, sm_scale=w.sm_scale)
+
+    n, dt = run(swa, w.n_q // 256)
+    out["swa_bf16_prefill_8k_w128"] = {"value": round(n * 256 / dt, 1), "unit": "queries/s",
+                                       "sample": f"{n} blocks of 256 queries, window 128, "
+                                                 f"{dt:.1f} s"}
+    del inp
+    # KV Bridging: 16,384-row blocks of the 1M x 2048 hidden states.
+    wb = WORKLOADS["bridge_decode_bf16_1m"]
+    bi = make_bridge_inputs(wb, rows=16384)
+    h = bf16_bits_to_f32(bi["h_raw"])
+
+    def bridge(i):
+        oracle.bridge_kv(h, bi["w_k"], bi["w_v"])
+
+    n, dt = run(bridge, 64)
+    out["bridge_kv_1m_x_2048"] = {"value": round(n * 16384 / dt, 1), "unit": "rows/s",
+                                  "sample": f"{n} blocks of 16,384 rows, {dt:.1f} s"}
+    del np
+    return out
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -489,6 +583,8 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--extras", type=int, default=1,
                     help="also time batched decode, chunked prefill and KV Bridging")
+    ap.add_argument("--cpu-baselines", action="store_true",
+                    help="time the oracle on a sample of every shape (host only) and exit")
     ap.add_argument("--calibrate", action="store_true",
                     help="after timing, run a plain 256 MiB device copy (torch copy_) so that "
                          "HBM byte counters can be scaled by a kernel of known traffic")
@@ -498,6 +594,9 @@ def main() -> int:
               "(decode shards by sequence with no exchange; see the design notes).",
               file=sys.stderr)
         return 2
+    if args.cpu_baselines:
+        print(json.dumps({"cpu_baselines": cpu_baselines_all()}), flush=True)
+        return 0
 
     import numpy as np
     import torch
