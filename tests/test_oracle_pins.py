@@ -102,6 +102,28 @@ def test_full_layer_output_invariants():
                                        rtol=1e-12)
 
 
+def test_full_layer_output_causal_per_query():
+    # Prefill: query i of a block sits at P_i = N - n_q + i and its output is
+    # the softmax-weighted V over keys 0..P_i only (scipy's softmax over the
+    # scaled logits); a query before the cache start sees no key: output 0
+    # and log-sum-exp -inf.
+    rng = np.random.default_rng(12)
+    n_q, heads, d = 4, 2, 8
+    for n in (6, 2):
+        q, k, v = _rand(rng, 1, n_q, heads, d), _rand(rng, 1, n, d), _rand(rng, 1, n, d)
+        _, o, lse = oracle.full_attn_scores(q, k, np.array([n]), tile_q=n_q, sm_scale=0.5, v=v)
+        for i in range(n_q):
+            p_i = n - n_q + i
+            for h in range(heads):
+                if p_i < 0:
+                    assert np.all(o[0, i, h] == 0.0) and lse[0, i, h] == -np.inf
+                    continue
+                s = 0.5 * (k[0, :p_i + 1] @ q[0, i, h])
+                want = scipy.special.softmax(s) @ v[0, :p_i + 1]
+                np.testing.assert_allclose(o[0, i, h], want, rtol=1e-12, atol=1e-14)
+                assert lse[0, i, h] == pytest.approx(scipy.special.logsumexp(s), rel=1e-13)
+
+
 def _rand(rng, *shape, scale=1.0):
     return rng.standard_normal(shape) * scale
 
