@@ -152,9 +152,10 @@ hs2_status hs2_full_attn_scores(const hs2_attn_desc* desc, const void* q, const 
     return launched(launch_prefill_scores(*desc, q, k, kv_stride, ctx_len, kv_capacity, scores,
                                           lse, static_cast<char*>(ws) + l.score, false,
                                           static_cast<hipStream_t>(stream)));
-  return launched(launch_score_decode(*desc, q, k, kv_stride, ctx_len, kv_capacity, scores, lse,
-                                      static_cast<char*>(ws) + l.score, false,
-                                      static_cast<hipStream_t>(stream)));
+  return launched(launch_score_decode(
+      *desc, q, k, kv_stride, ctx_len, kv_capacity, scores, lse, static_cast<char*>(ws) + l.score,
+      reinterpret_cast<uint64_t*>(static_cast<char*>(ws) + l.sync), false,
+      static_cast<hipStream_t>(stream)));
 }
 
 hs2_status hs2_select_topk_window(const hs2_attn_desc* desc, const float* scores,
@@ -194,7 +195,7 @@ hs2_status hs2_select_topk_blocks(const hs2_attn_desc* desc, int block_size, con
   (void)hipGetLastError();
   const WsLayout l = ws_layout(*desc, kv_capacity);
   return launched(launch_select_blocks(*desc, block_size, scores, ctx_len, kv_capacity, top_idx,
-                                       top_cnt, static_cast<char*>(ws) + l.select, false,
+                                       top_cnt, static_cast<char*>(ws) + l.select,
                                        static_cast<hipStream_t>(stream)));
 }
 
@@ -278,7 +279,7 @@ hs2_status hs2_decode_step(const hs2_attn_desc* desc, const void* q, const void*
       pf ? launch_prefill_scores(*desc, q, k, kv_stride, ctx_len, kv_capacity, scores, lse_full,
                                  w + l.score, fuse, st)
          : launch_score_decode(*desc, q, k, kv_stride, ctx_len, kv_capacity, scores, lse_full,
-                               w + l.score, fuse, st);
+                               w + l.score, reinterpret_cast<uint64_t*>(w + l.sync), fuse, st);
   if (e != hipSuccess) return HS2_EHIP;
   const size_t hist_off = pf ? prefill_ws(*desc, kv_capacity).hist_off
                              : score_ws(*desc, kv_capacity).hist_off;
@@ -315,17 +316,16 @@ hs2_status hs2_decode_step_blocks(const hs2_attn_desc* desc, int block_size, con
   char* w = static_cast<char*>(ws);
   hipStream_t st = static_cast<hipStream_t>(stream);
   const bool pf = is_prefill(*desc);
-  // MFMA decode: the scoring pass also writes the block selector's piece sums.
-  const bool pieces = !pf && desc->dtype != HS2_F32;
-  const BlockPieces pc = block_pieces(*desc, block_size, kv_capacity, w + l.select);
+  // The same scores as hs2_full_attn_scores, then the block sums and the
+  // block selection.
   hipError_t e =
       pf ? launch_prefill_scores(*desc, q, k, kv_stride, ctx_len, kv_capacity, scores, lse_full,
                                  w + l.score, false, st)
          : launch_score_decode(*desc, q, k, kv_stride, ctx_len, kv_capacity, scores, lse_full,
-                               w + l.score, false, st, pieces ? &pc : nullptr);
+                               w + l.score, reinterpret_cast<uint64_t*>(w + l.sync), false, st);
   if (e != hipSuccess) return HS2_EHIP;
   e = launch_select_blocks(*desc, block_size, scores, ctx_len, kv_capacity, top_idx, top_cnt,
-                           w + l.select, pieces, st);
+                           w + l.select, st);
   if (e != hipSuccess) return HS2_EHIP;
   if (pf)
     return launched(launch_prefill_sparse(*desc, q_sparse, k, v, kv_stride, ctx_len, kv_capacity,

@@ -31,6 +31,8 @@ constexpr int kSelBins = 4096;
 // 12 bits of the keys in the threshold bin (built while filtering).
 constexpr int kHistRow = 2 * kSelBins;
 constexpr int kSelSlice = 4096;  // pool keys per workgroup of the selector passes
+// One-pass decode scoring: at most this many workgroups per launch (one per CU).
+constexpr int kOpMaxWg = 256;
 
 // ---------------------------------------------------------------------------
 // Small device helpers.
@@ -121,6 +123,7 @@ inline int score_nchunks1(const hs2_attn_desc& d, int cap) {
 
 struct ScoreWs {
   size_t stats_off;  // float2 [B][nchunks1][32]  (max, sum) per chunk & head, base 2
+  size_t op_off;     // float  [kOpMaxWg][64]      one-pass kernel: (max, sum) per workgroup
   size_t lse2_off;   // float  [B][32]             per-head log2-sum-exp (fp32 path)
   size_t hist_off;   // uint32 [B][kHistRow]       selector histograms (fused step)
   size_t opart_off;  // float  [B][nchunks2][32][128] full-output partials per chunk
@@ -169,6 +172,8 @@ inline ScoreWs score_ws(const hs2_attn_desc& d, int cap) {
   size_t off = 0;
   w.stats_off = off;
   off = align_up(off + sizeof(float) * 2 * (size_t)d.batch * score_nchunks1(d, cap) * kMaxHeads, 256);
+  w.op_off = off;
+  off = align_up(off + sizeof(float) * kOpMaxWg * 64, 256);
   w.lse2_off = off;
   off = align_up(off + sizeof(float) * (size_t)d.batch * d.n_q * kMaxHeads, 256);
   w.hist_off = off;
@@ -217,15 +222,23 @@ inline SparseWs sparse_ws(const hs2_attn_desc& d) {
   return w;
 }
 
-// Offsets of the three regions inside the caller's workspace.
+// Words of the one-pass scoring kernel's barrier: a generation per sequence at
+// word b and a slot per (sequence, workgroup) at word kOpMaxWg * (1 + b) + c,
+// the same positions for every descriptor.
+inline size_t sync_words(const hs2_attn_desc& d) { return (size_t)kOpMaxWg * (1 + d.batch); }
+
+// Offsets of the regions inside the caller's workspace: the barrier words at
+// offset 0 (so that they keep their place whatever the descriptor), then
+// scoring, selection and sparse.
 struct WsLayout {
-  size_t score, select, sparse, bytes;
+  size_t sync, score, select, sparse, bytes;
 };
 
 inline WsLayout ws_layout(const hs2_attn_desc& d, int cap) {
   WsLayout l{};
-  l.score = 0;
-  l.select = align_up(is_prefill(d) ? prefill_ws(d, cap).bytes : score_ws(d, cap).bytes, 256);
+  l.sync = 0;
+  l.score = align_up(sizeof(uint64_t) * sync_words(d), 256);
+  l.select = align_up(l.score + (is_prefill(d) ? prefill_ws(d, cap).bytes : score_ws(d, cap).bytes), 256);
   l.sparse = align_up(l.select + select_ws(d, cap).bytes, 256);
   l.bytes = align_up(l.sparse + sparse_ws(d).bytes, 256);
   return l;
@@ -243,21 +256,32 @@ hipError_t launch_score_full(const hs2_attn_desc& d, const void* q, const void* 
                              float* o_full, float* lse, char* ws, hipStream_t st);
 
 // Piece sums of the pool scores for the block-level selector: out[r][m] =
-// fp32 pairwise sum of the scores of keys [m*piece, (m+1)*piece) of row r
-// (keys past the pool count 0), row stride `stride` floats.
+// fp64 sum of the scores of keys [m*piece, (m+1)*piece) of row r (keys past
+// the pool count 0), row stride `stride` doubles.
 struct BlockPieces {
-  float* out;
+  double* out;
   int piece;   // min(block, 32)
   int stride;  // blk_stride(cap, piece)
 };
 
 // with_hist: also build the selector histogram of the pool scores in the
-// scoring region (MFMA paths only).  pieces (MFMA paths, not with
-// with_hist): also write the block selector's piece sums.
+// scoring region (MFMA paths only).  sync: the barrier words of the workspace
+// (ws_layout().sync); bf16 and E4M3 K take the one-pass kernel when the batch
+// fits the device, two passes otherwise.
 hipError_t launch_score_decode(const hs2_attn_desc& d, const void* q, const void* k,
                                int64_t kv_stride, const int32_t* ctx_len, int cap,
-                               float* scores, float* lse, char* ws, bool with_hist,
-                               hipStream_t st, const BlockPieces* pieces = nullptr);
+                               float* scores, float* lse, char* ws, uint64_t* sync,
+                               bool with_hist, hipStream_t st);
+
+// One-pass decode scoring (bf16 or E4M3 K): workgroups per sequence and keys
+// per workgroup for a device of n_cu CUs; false when the batch does not fit.
+bool onepass_plan(const hs2_attn_desc& d, int cap, int n_cu, int* nwg, int* chunk);
+hipError_t launch_score_onepass(const hs2_attn_desc& d, const void* q, const void* k,
+                                int64_t kv_stride, const int32_t* ctx_len, int cap, int nwg,
+                                int chunk, float c2, float* stats, uint64_t* sync, float* scores,
+                                float* lse, uint32_t* hist, hipStream_t st);
+// Compute units of the current device (cached per device).
+int device_cu_count();
 
 // hist: a ready histogram of the pool scores (from launch_score_decode with
 // with_hist), or null to build one.  final_stage false: stop after the
@@ -275,14 +299,13 @@ hipError_t launch_swa(const hs2_attn_desc& d, const void* q, const void* k, cons
 // Block-level selection (blocks of `block` tokens, a power of two <= 64):
 // piece sums (pieces of min(block, 32) keys) in the selection region's list
 // area, then one workgroup per row; writes top_idx/top_cnt like
-// launch_select.  have_pieces: the scoring pass already wrote the piece sums
-// (block_pieces gives where), so they are not recomputed from the scores.
+// launch_select.
 constexpr int kMaxBlocks = 65536;  // blocks per row
 int blk_stride(int cap, int piece);
 BlockPieces block_pieces(const hs2_attn_desc& d, int block, int cap, char* sel_ws);
 hipError_t launch_select_blocks(const hs2_attn_desc& d, int block, const float* scores,
                                 const int32_t* ctx_len, int cap, int32_t* top_idx,
-                                int32_t* top_cnt, char* ws, bool have_pieces, hipStream_t st);
+                                int32_t* top_cnt, char* ws, hipStream_t st);
 
 // Chunked prefill (tile_q > 1, bf16): scoring over query tiles and sparse
 // attention of the tiles' queries.

@@ -36,65 +36,15 @@
 //
 // fp32 path: a VALU dot-product kernel, one key per thread, with a separate
 // reduction kernel.
-#include "hs2_internal.h"
+#include "score_common.h"
 
 namespace hs2 {
 namespace {
 
-typedef __bf16 bf16x8_t __attribute__((__vector_size__(8 * sizeof(__bf16))));
-typedef float f32x16_t __attribute__((__vector_size__(16 * sizeof(float))));
-
-__device__ __forceinline__ bf16x8_t as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8_t, v); }
+using namespace score;
 
 constexpr int kP1Waves = 8;
 constexpr int kP2Waves = 8;
-
-// Merge two (max, sum) pairs of base-2 softmax statistics.
-__device__ __forceinline__ void merge_ml(float& m, float& l, float m2, float l2) {
-  const float mn = fmaxf(m, m2);
-  if (mn == -INFINITY) return;  // both empty
-  l = l * fast_exp2(m - mn) + l2 * fast_exp2(m2 - mn);
-  m = mn;
-}
-
-// Registers of raw K per lane and 32-key block: 128 B of a bf16 row, 64 B of
-// an E4M3 row.
-template <bool kFp8>
-constexpr int k_regs() {
-  return kFp8 ? 4 : 8;
-}
-
-// Query rows as the MFMA operand of steps 0..7 (dims as step_dim gives).
-template <bool kFp8>
-__device__ __forceinline__ void load_q_bf16(const uint16_t* qb, int H, int r32, int hh,
-                                            bf16x8_t (&qreg)[8]) {
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    u32x4 v = {0u, 0u, 0u, 0u};
-    if (r32 < H) v = *reinterpret_cast<const u32x4*>(qb + r32 * kHeadDim + step_dim<kFp8>(i, hh));
-    qreg[i] = as_bf16x8(v);
-  }
-}
-
-// Lane half hh's share of key row `row` (kb: the sequence's cache, bytes):
-// 16-byte pieces 2i + hh of the row.
-template <bool kFp8>
-__device__ __forceinline__ void load_k_block(const char* kb, int row, int hh,
-                                             u32x4 (&kr)[k_regs<kFp8>()]) {
-  const u32x4* kp =
-      reinterpret_cast<const u32x4*>(kb + (size_t)row * kHeadDim * kv_elem_bytes<kFp8>()) + hh;
-#pragma unroll
-  for (int i = 0; i < k_regs<kFp8>(); ++i) kr[i] = kp[2 * i];
-}
-
-// The K operand of MFMA step e (compile-time after unrolling).
-template <bool kFp8>
-__device__ __forceinline__ bf16x8_t k_operand(const u32x4 (&kr)[k_regs<kFp8>()], int e) {
-  if constexpr (kFp8)
-    return as_bf16x8(e4m3x8_to_bf16x8(kr[e >> 1][2 * (e & 1)], kr[e >> 1][2 * (e & 1) + 1]));
-  else
-    return as_bf16x8(kr[e]);
-}
 
 // Pass 1, bf16 or E4M3 K: per (sequence, chunk, head) base-2 (max, sum).
 // Chunks at or beyond the context write neutral statistics.  The workgroup of
@@ -181,17 +131,14 @@ __global__ __launch_bounds__(64 * kP1Waves) void score_p1_bf16(
 
 // Pass 2, bf16 or E4M3 K: fold the statistics into L_h, then
 // I[j] = sum_h 2^(x_hj - L_h).  kHist: also count the pool scores into the
-// selector's first histogram.  kPieces: also write the fp32 sums of the pool
-// scores over aligned pieces of `piece` keys (a power of two <= 32, summed as
-// a pairwise tree by an xor butterfly; keys past the pool count 0) to
-// pieces[b][j / piece], the block importance of the block-level selector.
-template <bool kFp8, bool kHist, bool kPieces>
+// selector's first histogram.
+template <bool kFp8, bool kHist>
 __global__ __launch_bounds__(64 * kP2Waves) void score_p2_bf16(
     const uint16_t* __restrict__ q, const void* __restrict__ k, int64_t kv_stride,
     const int32_t* __restrict__ ctx_len, int cap, int H, float c2,
     const float2* __restrict__ stats, int nchunks1, float* __restrict__ scores,
-    int64_t score_stride, float* __restrict__ lse_out, uint32_t* __restrict__ hist, int window,
-    float* __restrict__ pieces, int piece, int piece_stride) {
+    int64_t score_stride, float* __restrict__ lse_out, uint32_t* __restrict__ hist,
+    int window) {
   const int b = gridDim.y - 1 - blockIdx.y;
   const int c = gridDim.x - 1 - blockIdx.x;
   const int N = clamp_ctx(ctx_len, b, cap);
@@ -260,12 +207,6 @@ __global__ __launch_bounds__(64 * kP2Waves) void score_p2_bf16(
     if (hh == 0 && j < j_end) {
       out[j] = imp;
       if (kHist && j < pe) atomicAdd(&s_hist[order_key(imp) >> 20], 1u);
-    }
-    if (kPieces) {
-      float x = j < pe ? imp : 0.f;
-      for (int off = 1; off < piece; off <<= 1) x += __shfl_xor(x, off);
-      if (hh == 0 && (r32 & (piece - 1)) == 0 && j < pe)
-        pieces[(size_t)b * piece_stride + j / piece] = x;
     }
   };
   // Two register sets used in turn, with unconditional loads, as in pass 1.
@@ -696,28 +637,23 @@ __global__ __launch_bounds__(256) void score_reduce_f32(
   }
 }
 
-// Both MFMA passes; hist null: no selector histogram; pc null: no piece sums.
+// Both MFMA passes; hist null: no selector histogram.
 template <bool kFp8>
 void launch_score_mfma(const hs2_attn_desc& d, const void* q, const void* k, int64_t kv_stride,
                        const int32_t* ctx_len, int cap, float* scores, float* lse, float2* stats,
-                       int nchunks1, float c2, uint32_t* hist, const BlockPieces* pc,
-                       hipStream_t st) {
+                       int nchunks1, float c2, uint32_t* hist, hipStream_t st) {
   const auto* qq = static_cast<const uint16_t*>(q);
   score_p1_bf16<kFp8><<<dim3(nchunks1, d.batch), 64 * kP1Waves, 0, st>>>(
       qq, k, kv_stride, ctx_len, cap, d.n_heads, c2, stats, nchunks1, hist);
   const dim3 g2((cap + kP2Chunk - 1) / kP2Chunk, d.batch);
   if (hist != nullptr)
-    score_p2_bf16<kFp8, true, false><<<g2, 64 * kP2Waves, 0, st>>>(
+    score_p2_bf16<kFp8, true><<<g2, 64 * kP2Waves, 0, st>>>(
         qq, k, kv_stride, ctx_len, cap, d.n_heads, c2, stats, nchunks1, scores, cap, lse, hist,
-        d.window, nullptr, 1, 0);
-  else if (pc != nullptr)
-    score_p2_bf16<kFp8, false, true><<<g2, 64 * kP2Waves, 0, st>>>(
-        qq, k, kv_stride, ctx_len, cap, d.n_heads, c2, stats, nchunks1, scores, cap, lse, nullptr,
-        d.window, pc->out, pc->piece, pc->stride);
+        d.window);
   else
-    score_p2_bf16<kFp8, false, false><<<g2, 64 * kP2Waves, 0, st>>>(
+    score_p2_bf16<kFp8, false><<<g2, 64 * kP2Waves, 0, st>>>(
         qq, k, kv_stride, ctx_len, cap, d.n_heads, c2, stats, nchunks1, scores, cap, lse, nullptr,
-        d.window, nullptr, 1, 0);
+        d.window);
 }
 
 }  // namespace
@@ -769,20 +705,26 @@ hipError_t launch_score_full(const hs2_attn_desc& d, const void* q, const void* 
 
 hipError_t launch_score_decode(const hs2_attn_desc& d, const void* q, const void* k,
                                int64_t kv_stride, const int32_t* ctx_len, int cap,
-                               float* scores, float* lse, char* ws, bool with_hist,
-                               hipStream_t st, const BlockPieces* pieces) {
+                               float* scores, float* lse, char* ws, uint64_t* sync,
+                               bool with_hist, hipStream_t st) {
   const ScoreWs w = score_ws(d, cap);
   float2* stats = reinterpret_cast<float2*>(ws + w.stats_off);
   const float c2 = d.sm_scale * 1.4426950408889634f;
   const int nchunks1 = score_nchunks1(d, cap);
   if (d.dtype != HS2_F32) {
     uint32_t* hist = with_hist ? reinterpret_cast<uint32_t*>(ws + w.hist_off) : nullptr;
+    int nwg = 0, chunk = 0;
+    if (sync != nullptr && onepass_plan(d, cap, device_cu_count(), &nwg, &chunk))
+      return launch_score_onepass(d, q, k, kv_stride, ctx_len, cap, nwg, chunk,
+                                  d.dtype == HS2_FP8_E4M3 ? c2 * d.k_scale : c2,
+                                  reinterpret_cast<float*>(ws + w.op_off), sync, scores, lse,
+                                  hist, st);
     if (d.dtype == HS2_FP8_E4M3)
       launch_score_mfma<true>(d, q, k, kv_stride, ctx_len, cap, scores, lse, stats, nchunks1,
-                              c2 * d.k_scale, hist, pieces, st);
+                              c2 * d.k_scale, hist, st);
     else
       launch_score_mfma<false>(d, q, k, kv_stride, ctx_len, cap, scores, lse, stats, nchunks1,
-                               c2, hist, pieces, st);
+                               c2, hist, st);
   } else {
     float* lse2 = reinterpret_cast<float*>(ws + w.lse2_off);
     const dim3 grid(nchunks1, d.batch);

@@ -7,19 +7,17 @@
 // Token-Level Sparse Selection"; the paper summary's "KV Reuse refinements"
 // compares the two at the same attention budget).  Here a row's pool
 // [0, pe) is cut into aligned blocks of `block` tokens (the last one cut at
-// pe), a block's importance is the fp32 sum of its tokens' importance in a
-// balanced pairwise order (slot pairs (0,1), (2,3), ... level by level; slots
-// past the pool hold 0), and the k_top / block blocks of largest importance
+// pe), a block's importance is the sum of its tokens' fp32 importance,
+// rounded once to fp32, and the k_top / block blocks of largest importance
 // are taken, ties to the lower block.  Their pool tokens are written in
 // ascending order in the token selector's output form, so the sparse layer
 // runs on them unchanged.
 //
-// Piece sums: the tree over a block of 64 is the sum of the trees over its
-// two halves, so the sums are kept per piece of min(block, 32) keys, which a
-// half-wave butterfly yields (x + partner is the same value on both lanes of
-// a pair, so the butterfly is exactly the pairwise tree).  The decode scoring
-// pass writes them while it has the scores in registers; blk_sums computes
-// them from a score array otherwise.
+// Piece sums: blk_sums adds each piece of min(block, 32) keys in fp64 with a
+// half-wave butterfly, and blk_select adds a 64-key block's two pieces in fp64
+// before the one rounding to fp32.  An fp64 sum of at most 64 fp32 values is
+// exact whenever their exponents span less than about 23 binades, so then the
+// result is the exact sum rounded once, whatever the order of the additions.
 // blk_select: one workgroup per row, the row's block importance held in
 // registers (a contiguous run of blocks per thread).  The threshold is found
 // by an MSB-first radix over d = key - min(key) on the order-preserving
@@ -37,13 +35,13 @@ constexpr int kBlkSumThreads = 256;
 
 __global__ __launch_bounds__(kBlkSumThreads) void blk_sums(
     const float* __restrict__ scores, int cap, const int32_t* __restrict__ ctx_len, int tiles,
-    int n_q, int tile_q, int window, int piece, float* __restrict__ ps, int ps_stride) {
+    int n_q, int tile_q, int window, int piece, double* __restrict__ ps, int ps_stride) {
   const int r = blockIdx.y;
   const RowGeom g = row_geom(ctx_len, cap, r, tiles, n_q, tile_q, 0, window);
   const int j0 = blockIdx.x * kBlkSumThreads;
   if (j0 >= g.pe) return;  // uniform over the workgroup
   const int j = j0 + threadIdx.x;
-  float x = j < g.pe ? scores[(size_t)r * cap + j] : 0.f;
+  double x = j < g.pe ? (double)scores[(size_t)r * cap + j] : 0.0;
   for (int off = 1; off < piece; off <<= 1) x += __shfl_xor(x, off);
   if ((j & (piece - 1)) == 0 && j < g.pe) ps[(size_t)r * ps_stride + j / piece] = x;
 }
@@ -74,11 +72,11 @@ __device__ __forceinline__ void block_min_max(uint32_t& lo, uint32_t& hi, uint32
 
 // One row per workgroup of kThreads; thread t holds blocks
 // [kPer t, kPer t + kPer) in registers (kPer * kThreads >= nb).  Block m's
-// importance is the sum of its pieces 2m and 2m + 1 when block = 2 * piece,
-// else piece m.
+// importance is the fp64 sum of its pieces 2m and 2m + 1 when
+// block = 2 * piece, else piece m, rounded to fp32.
 template <int kThreads, int kPer>
 __global__ __launch_bounds__(kThreads) void blk_select(
-    const float* __restrict__ ps, int ps_stride, const int32_t* __restrict__ ctx_len, int cap,
+    const double* __restrict__ ps, int ps_stride, const int32_t* __restrict__ ctx_len, int cap,
     int tiles, int n_q, int tile_q, int k_top, int window, int block, int piece,
     int32_t* __restrict__ top_idx, int32_t* __restrict__ top_cnt) {
   __shared__ uint32_t hist[4096];
@@ -91,7 +89,7 @@ __global__ __launch_bounds__(kThreads) void blk_select(
   const int pe = g.pe;
   const int nb = (pe + block - 1) / block;
   const int n_sel = min(k_top / block, nb);
-  const float* row = ps + (size_t)r * ps_stride;
+  const double* row = ps + (size_t)r * ps_stride;
 
   // Order keys of this thread's blocks; 0 marks a slot past the row (every
   // real key is at least 0x80000000, the image of +0).
@@ -99,24 +97,21 @@ __global__ __launch_bounds__(kThreads) void blk_select(
   const int m0 = t * kPer;
   if (block == piece) {
 #pragma unroll
-    for (int i = 0; i < kPer; i += 4) {
-      f32x4 v = {0.f, 0.f, 0.f, 0.f};
-      if (m0 + i < nb) v = *reinterpret_cast<const f32x4*>(row + m0 + i);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) key[i + e] = (m0 + i + e < nb) ? order_key(v[e]) : 0u;
+    for (int i = 0; i < kPer; i += 2) {
+      double2 v = make_double2(0.0, 0.0);
+      if (m0 + i < nb) v = *reinterpret_cast<const double2*>(row + m0 + i);
+      key[i] = (m0 + i < nb) ? order_key((float)v.x) : 0u;
+      key[i + 1] = (m0 + i + 1 < nb) ? order_key((float)v.y) : 0u;
     }
   } else {
     // Pieces 2m, 2m + 1; a piece that starts at or past the pool end is 0.
 #pragma unroll
-    for (int i = 0; i < kPer; i += 2) {
+    for (int i = 0; i < kPer; ++i) {
       const int q0 = 2 * (m0 + i);
-      f32x4 v = {0.f, 0.f, 0.f, 0.f};
-      if (m0 + i < nb) v = *reinterpret_cast<const f32x4*>(row + q0);
-#pragma unroll
-      for (int e = 0; e < 4; ++e)
-        if ((q0 + e) * piece >= pe) v[e] = 0.f;
-      key[i] = (m0 + i < nb) ? order_key(v[0] + v[1]) : 0u;
-      key[i + 1] = (m0 + i + 1 < nb) ? order_key(v[2] + v[3]) : 0u;
+      double2 v = make_double2(0.0, 0.0);
+      if (m0 + i < nb) v = *reinterpret_cast<const double2*>(row + q0);
+      if ((q0 + 1) * piece >= pe) v.y = 0.0;
+      key[i] = (m0 + i < nb) ? order_key((float)(v.x + v.y)) : 0u;
     }
   }
 
@@ -197,26 +192,25 @@ __global__ __launch_bounds__(kThreads) void blk_select(
 
 }  // namespace
 
-// Row stride of the piece sums (floats): a multiple of 4 so that rows load
-// as 16-byte vectors.
+// Row stride of the piece sums (doubles): a multiple of 4, so that rows and
+// piece pairs load as 16-byte vectors (the select region's list area holds
+// 8 bytes per pool key, at least this).
 int blk_stride(int cap, int piece) { return ((cap + piece - 1) / piece + 3) / 4 * 4; }
 
 BlockPieces block_pieces(const hs2_attn_desc& d, int block, int cap, char* sel_ws) {
   const int piece = min(block, 32);
-  return BlockPieces{reinterpret_cast<float*>(sel_ws + select_ws(d, cap).list_off), piece,
+  return BlockPieces{reinterpret_cast<double*>(sel_ws + select_ws(d, cap).list_off), piece,
                      blk_stride(cap, piece)};
 }
 
 hipError_t launch_select_blocks(const hs2_attn_desc& d, int block, const float* scores,
                                 const int32_t* ctx_len, int cap, int32_t* top_idx,
-                                int32_t* top_cnt, char* ws, bool have_pieces, hipStream_t st) {
+                                int32_t* top_cnt, char* ws, hipStream_t st) {
   const int tiles = d.n_q / d.tile_q;
   const int rows = d.batch * tiles;
   const BlockPieces pc = block_pieces(d, block, cap, ws);
-  if (!have_pieces)
-    blk_sums<<<dim3((cap + kBlkSumThreads - 1) / kBlkSumThreads, rows), kBlkSumThreads, 0,
-               st>>>(scores, cap, ctx_len, tiles, d.n_q, d.tile_q, d.window, pc.piece, pc.out,
-                     pc.stride);
+  blk_sums<<<dim3((cap + kBlkSumThreads - 1) / kBlkSumThreads, rows), kBlkSumThreads, 0, st>>>(
+      scores, cap, ctx_len, tiles, d.n_q, d.tile_q, d.window, pc.piece, pc.out, pc.stride);
   const int nb_max = (cap + block - 1) / block;
 #define HS2_BLK_SELECT(T, P)                                                                \
   blk_select<T, P><<<rows, T, 0, st>>>(pc.out, pc.stride, ctx_len, cap, tiles, d.n_q, d.tile_q, \

@@ -18,6 +18,7 @@ from .hs2_oracle import (  # noqa: F401
     fp8_e4m3_value,
     full_attn_scores,
     query_positions,
+    round_to_f32,
     pool_end,
     select_topk_blocks,
     select_topk_window,

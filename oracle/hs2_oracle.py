@@ -59,6 +59,8 @@ brute force and hand-worked cases); none is "parity unpinned".
 
 from __future__ import annotations
 
+import math
+
 import numpy as np
 
 __all__ = [
@@ -68,6 +70,7 @@ __all__ = [
     "full_attn_scores",
     "select_topk_window",
     "block_scores",
+    "round_to_f32",
     "select_topk_blocks",
     "selection_set",
     "sparse_attention",
@@ -211,6 +214,33 @@ def select_topk_window(scores, ctx_len, *, n_q: int, tile_q: int, k_top: int,
     return top_idx, top_cnt
 
 
+def round_to_f32(n: int, e: int) -> np.float32:
+    """The float32 nearest to n * 2**e (n >= 0 an integer), ties to even.
+
+    Keeps the top 24 significant bits of n, or fewer where the result falls
+    among the float32 subnormals (whose spacing is 2**-149), and rounds the
+    dropped bits half to even.
+    """
+    if n < 0:
+        raise ValueError("n must be >= 0")
+    if n == 0:
+        return np.float32(0.0)
+    q = max(e + n.bit_length() - 24, -149)   # exponent of the last kept bit
+    if q <= e:
+        m = n << (e - q)
+    else:
+        s = q - e
+        m, r = divmod(n, 1 << s)
+        half = 1 << (s - 1)
+        if r > half or (r == half and m & 1):
+            m += 1
+        if m == 1 << 24:
+            m, q = 1 << 23, q + 1
+    if q + 23 > 127:
+        raise OverflowError("sum beyond the float32 range")
+    return np.float32(math.ldexp(m, q))       # m < 2**24: exact in both formats
+
+
 def block_scores(imp_pool, block: int) -> np.ndarray:
     """Importance of the aligned blocks of `block` tokens that cover a pool.
 
@@ -218,10 +248,11 @@ def block_scores(imp_pool, block: int) -> np.ndarray:
     tokens [m*block, (m+1)*block) cut at pe; its importance is the sum of its
     tokens' importance.  The pages do not say how HySparse ranks its blocks;
     the summed attention mass is the reading taken, the block analogue of the
-    token importance.  Since the sum then decides which blocks are taken, it
-    is computed in the precision and order of the kernels: fp32 additions in
-    a balanced pairwise tree over the block's `block` slots (slots past the
-    pool hold 0), i.e. level by level, adding slot pairs (0,1), (2,3), ...
+    token importance ([Origins] "KV Reuse and Token-Level Sparse Selection":
+    HySparse gives the budget to 64-token blocks).  Since the sum decides which
+    blocks are taken, it is defined exactly: the exact sum of the tokens'
+    float32 values, rounded once to float32 (ties to even).  Every float32 is
+    an integer multiple of 2**-149, so the sum is taken over those integers.
     ``block`` is a power of two.
     """
     imp_pool = np.asarray(imp_pool, dtype=np.float32)
@@ -229,12 +260,12 @@ def block_scores(imp_pool, block: int) -> np.ndarray:
         raise ValueError("block must be a power of two")
     pe = imp_pool.shape[0]
     nb = -(-pe // block)
-    x = np.zeros(nb * block, dtype=np.float32)
-    x[:pe] = imp_pool
-    x = x.reshape(nb, block)
-    while x.shape[1] > 1:
-        x = x[:, 0::2] + x[:, 1::2]   # float32 + float32, rounded to nearest even
-    return x[:, 0]
+    units = imp_pool.astype(np.float64) * 2.0 ** 149   # exact integers in float64
+    out = np.empty(nb, dtype=np.float32)
+    for m in range(nb):
+        n = sum(int(u) for u in units[m * block:min((m + 1) * block, pe)])
+        out[m] = round_to_f32(n, -149)
+    return out
 
 
 def select_topk_blocks(scores, ctx_len, *, n_q: int, tile_q: int, k_top: int, window: int,

@@ -1,8 +1,9 @@
 """GPU parity of the block-level selection (HySparse's 64-token blocks).
 
 Fed the same fp32 scores, the GPU block selection must equal the oracle's bit
-for bit: both sum a block's scores in fp32 in the same pairwise order and
-break ties towards the lower block.  The single-call step with block
+for bit: the oracle takes a block's importance as the exact sum of its fp32
+scores rounded once to fp32; the GPU adds in fp64, which is exact at these
+scores' ranges, and rounds once; both break ties towards the lower block.  The single-call step with block
 selection must equal its three calls, and its sparse output the oracle's on
 the selection it made.
 """
@@ -57,6 +58,24 @@ def test_block_select_bit_exact_on_oracle_scores(hs2, block):
     for b, planted in enumerate(inp["planted"]):   # the clustered keys' blocks are taken
         if block == 1:
             assert set(planted.tolist()) <= set(top[b, 0, : cnt[b, 0]].tolist())
+
+
+def test_block_sums_are_rounded_once(hs2):
+    # Pool [0, 256) in four blocks of 64.  Block 0 holds 1, 2^-24, 2^-24, which
+    # is exactly 1 + 2^-23; block 1 holds 1 + 2^-23.  Rounded once they tie and
+    # the lower block is taken; float32 additions would give block 0 only 1.
+    t = 2.0 ** -24
+    s = np.zeros((2, 1, 384), dtype=np.float32)
+    s[:, 0, [0, 1, 2]] = [1.0, t, t]
+    s[:, 0, 64] = np.float32(1.0 + 2.0 ** -23)
+    # Second row: a block of three subnormals against one of two.
+    s[1, 0, :] = 0.0
+    s[1, 0, [130, 131, 132]] = np.float32(2.0 ** -149)
+    s[1, 0, [200, 201]] = np.float32(2.0 ** -149)
+    _say("block sums rounded once")
+    top, cnt = _select_blocks_on(s, [384, 384], block=64, k_top=64)
+    assert top[0, 0].tolist() == list(range(64))
+    assert top[1, 0].tolist() == list(range(128, 192))
 
 
 def test_block_select_edge_cases_and_ties(hs2):

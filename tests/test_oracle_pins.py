@@ -8,6 +8,7 @@ off-by-one window or pool) fails at least one of them.
 
 import json
 import math
+from fractions import Fraction
 import os
 
 import numpy as np
@@ -479,37 +480,83 @@ def test_e4m3_matches_torch_float8():
     assert np.array_equal(got[fin], ref[fin])
 
 
-def test_dequant_kv_scales_every_code():
-    codes = np.arange(0, 0x7F, dtype=np.uint8).reshape(1, -1)
-    got = oracle.dequant_kv(codes, np.float32(0.0103))
-    assert np.array_equal(got, oracle.fp8_e4m3_value(codes) * float(np.float32(0.0103)))
+def test_dequant_kv_fixed_values():
+    # Printed values of the E4M3 format (bias 7): 0x38 = 1.0, 0x3C = 1.5,
+    # 0x30 = 0.5, 0x08 = 2^-6 (smallest normal), 0x01 = 2^-9 (smallest
+    # subnormal), 0x7E = 448 (largest finite); the sign bit mirrors each.  A byte
+    # x of a cache with scale s stands for s * e4m3(x) (the one-scale-per-cache
+    # reading), computed in float64 from the float32 scale.
+    s = np.float32(0.0103)
+    table = {0x38: 1.0, 0x3C: 1.5, 0x30: 0.5, 0x08: 2.0 ** -6, 0x01: 2.0 ** -9,
+             0x7E: 448.0, 0x00: 0.0}
+    codes = np.array([list(table) + [c | 0x80 for c in table]], dtype=np.uint8)
+    want = [v * float(s) for v in table.values()] + [-v * float(s) for v in table.values()]
+    got = oracle.dequant_kv(codes, s)
+    assert got.dtype == np.float64
+    assert got[0].tolist() == want
+    assert np.signbit(got[0, len(table) - 1 + len(table)])      # 0x80 is -0
+    # Scaling is linear in the scale and exact for powers of two.
+    assert oracle.dequant_kv(np.array([[0x7E]], np.uint8), 0.25)[0, 0] == 112.0
+    assert oracle.dequant_kv(np.array([[0x01]], np.uint8), 2.0 ** 9)[0, 0] == 1.0
 
 
 # --- Block-level selection (HySparse's 64-token blocks, for comparison) -----
 
-def test_block_scores_exact_sums_and_tree_order():
-    # Sums that fp32 holds exactly come out exact, a cut block counts only its
-    # pool tokens, and the pairwise order is the one stated: with slots
-    # [1, 2^-24, 2^-24, 2^-24] the pairs give 1 + 2^-23, a left-to-right sum 1.
+def test_block_scores_are_exact_sums_rounded_once():
+    # A block's importance is the exact sum of its tokens' float32 scores,
+    # rounded once to float32, ties to even.  Sums that float32 holds exactly
+    # come out exact, and a block cut by the pool end counts only its tokens.
     x = np.array([1, 2, 3, 4, 5, 6, 7, 8, 9, 10], dtype=np.float32)
     assert oracle.block_scores(x, 4).tolist() == [10.0, 26.0, 19.0]
     assert oracle.block_scores(x, 1).tolist() == x.tolist()
     assert oracle.block_scores(x, 16).tolist() == [55.0]
     t = np.float32(2.0 ** -24)
-    y = np.array([1.0, t, t, t], dtype=np.float32)
+    # [1, t, t, 0] is exactly 1 + 2^-23, a float32.  Float32 additions left to
+    # right, or in the pairwise tree (1 + t) + (t + 0), give 1 instead, since
+    # 1 + t is a tie that rounds to 1.
+    y = np.array([1.0, t, t, 0.0], dtype=np.float32)
     assert oracle.block_scores(y, 4)[0] == np.float32(1.0 + 2.0 ** -23)
     seq = np.float32(0.0)
     for v in y:
         seq = np.float32(seq + v)
-    assert seq == np.float32(1.0)
-    # Random values: within the pairwise-sum bound of the exact sum.
+    tree = np.float32(np.float32(y[0] + y[1]) + np.float32(y[2] + y[3]))
+    assert seq == tree == np.float32(1.0)
+    # 1 + 3t lies halfway between 1 + 2^-23 (odd significand) and 1 + 2^-22:
+    # the even one.  1 + t lies halfway between 1 and 1 + 2^-23: 1.
+    assert oracle.block_scores(np.array([1.0, t, t, t], np.float32), 4)[0] == \
+        np.float32(1.0 + 2.0 ** -22)
+    assert oracle.block_scores(np.array([1.0, t], np.float32), 2)[0] == np.float32(1.0)
+    # Subnormals add exactly.
+    d = np.float32(2.0 ** -149)
+    assert oracle.block_scores(np.array([d, d, d], np.float32), 4)[0] == np.float32(3 * 2.0 ** -149)
+    # Random scores: where math.fsum is exact (its float64 equals the exact
+    # rational sum), numpy's float64 -> float32 cast is the single rounding.
     rng = np.random.default_rng(40)
-    z = rng.random(64 * 50, dtype=np.float32) * np.float32(1e-3)
-    got = oracle.block_scores(z, 64).astype(np.float64)
-    exact = np.array([math.fsum(z[i:i + 64].astype(np.float64)) for i in range(0, z.size, 64)])
-    assert np.all(np.abs(got - exact) <= 6 * 2.0 ** -24 * exact)
+    z = (rng.random(64 * 50) * 10.0 ** rng.integers(-6, 1, 64 * 50)).astype(np.float32)
+    got = oracle.block_scores(z, 64)
+    checked = 0
+    for m in range(50):
+        blk = z[m * 64:(m + 1) * 64]
+        f = math.fsum(float(v) for v in blk)
+        if Fraction(f) == sum(Fraction(float(v)) for v in blk):
+            assert got[m] == np.float32(f)
+            checked += 1
+    assert checked >= 40
     with pytest.raises(ValueError):
         oracle.block_scores(x, 3)
+
+
+def test_round_to_f32_matches_the_library_cast():
+    # n * 2^e with n < 2^53 is a float64 exactly; numpy's cast to float32 rounds
+    # it once, to nearest even, including into the subnormal range.
+    rng = np.random.default_rng(43)
+    for _ in range(3000):
+        n = int(rng.integers(0, 2 ** 53))
+        e = int(rng.integers(-210, 40))
+        assert oracle.round_to_f32(n, e) == np.float32(math.ldexp(float(n), e)), (n, e)
+    for n, e in ((2 ** 24 + 1, -24), (2 ** 24 + 3, -24), (3, -150), (1, -150), (5, -151)):
+        assert oracle.round_to_f32(n, e) == np.float32(math.ldexp(float(n), e)), (n, e)
+    assert oracle.round_to_f32(0, 0) == np.float32(0.0)
 
 
 def test_block_selection_hand_case():
