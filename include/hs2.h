@@ -254,6 +254,26 @@ HS2_API hs2_status hs2_decode_step_blocks(const hs2_attn_desc* desc, int block_s
                                           hs2_stream_t stream);
 
 /*
+ * hs2_decode_step for callers that cannot allocate device memory: code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc.
+ * Same arguments, results and errors as hs2_decode_step, without ws and
+ * ws_bytes: the step's workspace is a 32 MiB (33,554,432-byte) array that the
+ * library holds in the device memory of each GPU it runs on, until the process
+ * ends.  The call allocates nothing.  It returns HS2_EWORKSPACE (enqueuing
+ * nothing) when hs2_workspace_size(desc, kv_capacity) exceeds 32 MiB.  Every
+ * call on one GPU uses that GPU's same array: calls that can overlap on one
+ * GPU (other streams, other threads) race and must not be issued.  The first
+ * call on a device looks up the array's device address (hipGetSymbolAddress);
+ * make that first call outside stream capture.
+ */
+HS2_API hs2_status hs2_decode_step_noalloc(const hs2_attn_desc* desc, const void* q,
+                                           const void* q_sparse, const void* k, const void* v,
+                                           int64_t kv_stride, const int32_t* ctx_len,
+                                           int kv_capacity, float* scores, float* lse_full,
+                                           int32_t* top_idx, int32_t* top_cnt, float* o,
+                                           float* lse, hs2_stream_t stream);
+
+/*
  * Sliding-window attention of the self-decoder.  Prefill runs only the
  * self-decoder, which mixes full-attention layers with sliding-window
  * attention layers ([Origins] "The Self-Decoder and Cross-Decoder Split";

@@ -34,6 +34,7 @@ EXPORTS = (
     "hs2_sparse_attn_gather_layers",
     "hs2_decode_step",
     "hs2_decode_step_blocks",
+    "hs2_decode_step_noalloc",
     "hs2_swa_attention",
     "hs2_bridge_kv",
     "hs2_bridge_packed_bytes",
@@ -108,6 +109,9 @@ def load(path: str | None = None):
     lib.hs2_decode_step_blocks.argtypes = [_desc_p, _int, _vp, _vp, _vp, _vp, _i64, _vp, _int,
                                            _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]
     lib.hs2_decode_step_blocks.restype = _int
+    lib.hs2_decode_step_noalloc.argtypes = [_desc_p, _vp, _vp, _vp, _vp, _i64, _vp, _int, _vp,
+                                            _vp, _vp, _vp, _vp, _vp, _vp]
+    lib.hs2_decode_step_noalloc.restype = _int
     lib.hs2_swa_attention.argtypes = [_desc_p, _vp, _vp, _vp, _i64, _vp, _int, _vp, _int, _vp,
                                       _vp]
     lib.hs2_swa_attention.restype = _int
@@ -237,6 +241,15 @@ def hs2_decode_step_blocks(desc, block_size, q, q_sparse, k, v, kv_stride, ctx_l
                                        _ptr(lse_full), _ptr(top_idx), _ptr(top_cnt), _ptr(o),
                                        _ptr(lse), _ptr(ws), _nbytes(ws), _stream(stream))
     _check(st, "hs2_decode_step_blocks")
+
+
+def hs2_decode_step_noalloc(desc, q, q_sparse, k, v, kv_stride, ctx_len, kv_capacity, scores,
+                            lse_full, top_idx, top_cnt, o, lse=None, stream=None) -> None:
+    st = load().hs2_decode_step_noalloc(ctypes.byref(desc), _ptr(q), _ptr(q_sparse), _ptr(k),
+                                        _ptr(v), int(kv_stride), _ptr(ctx_len), int(kv_capacity),
+                                        _ptr(scores), _ptr(lse_full), _ptr(top_idx),
+                                        _ptr(top_cnt), _ptr(o), _ptr(lse), _stream(stream))
+    _check(st, "hs2_decode_step_noalloc")
 
 
 def hs2_swa_attention(desc, q, k, v, kv_stride, ctx_len, kv_capacity, o, o_dtype=HS2_F32,

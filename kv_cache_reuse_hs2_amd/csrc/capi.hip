@@ -82,6 +82,19 @@ hs2_status check_step(const hs2_attn_desc* desc, const void* q, const void* q_sp
                       int kv_capacity, const float* scores, const float* lse_full,
                       const int32_t* top_idx, const int32_t* top_cnt, const float* o,
                       const float* lse, const void* ws, size_t ws_bytes) {
+  const hs2_status s = check_step_args(desc, q, q_sparse, k, v, kv_stride, ctx_len, kv_capacity,
+                                       scores, lse_full, top_idx, top_cnt, o, lse);
+  if (s != HS2_OK) return s;
+  return check_ws(*desc, kv_capacity, ws, ws_bytes);
+}
+
+}  // namespace
+
+hs2_status check_step_args(const hs2_attn_desc* desc, const void* q, const void* q_sparse,
+                           const void* k, const void* v, int64_t kv_stride,
+                           const int32_t* ctx_len, int kv_capacity, const float* scores,
+                           const float* lse_full, const int32_t* top_idx,
+                           const int32_t* top_cnt, const float* o, const float* lse) {
   hs2_status s = check_desc(desc);
   if (s != HS2_OK) return s;
   if (q == nullptr || k == nullptr || v == nullptr || ctx_len == nullptr || scores == nullptr ||
@@ -93,8 +106,10 @@ hs2_status check_step(const hs2_attn_desc* desc, const void* q, const void* q_sp
       misaligned(ctx_len) || misaligned(scores) || misaligned(lse_full) || misaligned(top_idx) ||
       misaligned(top_cnt) || misaligned(o) || misaligned(lse))
     return HS2_EALIGN;
-  return check_ws(*desc, kv_capacity, ws, ws_bytes);
+  return HS2_OK;
 }
+
+namespace {
 
 hs2_status check_bridge(const uint16_t* h, int64_t ldh, uint16_t* k_out, uint16_t* v_out,
                         int64_t ld_kv, int M, int d_model, int head_dim) {

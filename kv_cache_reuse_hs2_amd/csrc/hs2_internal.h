@@ -283,6 +283,13 @@ hipError_t launch_score_onepass(const hs2_attn_desc& d, const void* q, const voi
 // Compute units of the current device (cached per device).
 int device_cu_count();
 
+// Host-side checks of hs2_decode_step's arguments other than the workspace.
+hs2_status check_step_args(const hs2_attn_desc* desc, const void* q, const void* q_sparse,
+                           const void* k, const void* v, int64_t kv_stride,
+                           const int32_t* ctx_len, int kv_capacity, const float* scores,
+                           const float* lse_full, const int32_t* top_idx,
+                           const int32_t* top_cnt, const float* o, const float* lse);
+
 // hist: a ready histogram of the pool scores (from launch_score_decode with
 // with_hist), or null to build one.  final_stage false: stop after the
 // candidate filter (launch_decode_tail finishes the selection).

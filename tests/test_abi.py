@@ -343,3 +343,19 @@ def test_bridge_decode_validation(lib):
     assert call(ldh=2052) == hs2.HS2_EALIGN
     assert call(st=300 * 128 + 4) == hs2.HS2_EALIGN
     assert call(kc=ODD) == hs2.HS2_EALIGN
+
+
+def test_noalloc_step_rejects_before_any_hip_call(lib):
+    # A problem whose workspace exceeds the library's 32 MiB array, and invalid
+    # arguments, are refused on the host (fake pointers are never touched).
+    def call(desc, cap=262144, q=FAKE, k=FAKE):
+        return lib.hs2_decode_step_noalloc(ctypes.byref(desc), q, None, k, FAKE, cap * 128, FAKE,
+                                           cap, FAKE, None, FAKE, FAKE, FAKE, None, None)
+
+    big = _desc(batch=16)
+    assert hs2.hs2_workspace_size(big, 262144) > 32 << 20
+    assert call(big) == hs2.HS2_EWORKSPACE
+    assert call(_desc(head_dim=64), cap=4096) == hs2.HS2_EUNSUPPORTED
+    assert call(_desc(), cap=0) == hs2.HS2_EINVAL
+    assert call(_desc(), cap=4096, q=ODD) == hs2.HS2_EALIGN
+    assert call(_desc(), cap=4096, k=None) == hs2.HS2_EINVAL
