@@ -8,11 +8,14 @@ heads sharing one bf16 K/V head of dim 128, 262,144 cached keys per sequence,
 keys drawn as N(0,1) background plus 0.1% clustered high-similarity keys.
 Inputs are synthetic, seeded and resident in HBM before timing starts.
 
-Prints one JSON line.  value = decoded tokens/s = batch * steps / time.
+Prints one JSON line.  value = decoded tokens/s = batch * steps / time, the
+steps cycling over four distinct K/V caches (as a model's full layers would),
+so that no step finds its K left in the memory-side cache by the step before.
 Also reported: the step's algorithmic HBM GB/s (K read once, scores written
 and read once, 1,152 gathered K and V rows per sequence), a roofline entry
 for the dominant unit of work (the scoring call, timed with HIP events on
-its own stream), and the CPU oracle timed on a bounded sample.
+its own stream), one sequence of the last step checked against the oracle,
+and the CPU oracle timed on a bounded sample.
 """
 
 from __future__ import annotations
@@ -29,7 +32,10 @@ if ROOT not in sys.path:
 
 HBM_PEAK_GBS = 8000.0
 WORKLOAD = "decode_bf16_256k_b4"
-GRAPH_STEPS = 10  # decode steps per captured HIP graph
+GRAPH_STEPS = 10  # decode steps per captured HIP graph (extras)
+GRAPH_ROUNDS = 3  # rounds over the four caches per captured HIP graph (headline)
+# The headline scoring call's kernel (bf16 K, no selector histogram).
+SCORE_KERNEL = "score_onepass<false, false, 20>"
 MIB = 1 << 20
 
 
@@ -299,6 +305,35 @@ def full_output_measurements(steps: int, warmup: int) -> dict:
                     "counts K and V once, the least a full layer can read"}
 
 
+def mfma_calibration(steps: int, warmup: int) -> dict:
+    """What a library GEMM (torch.matmul in bf16, hipBLASLt) reaches on this
+    part, on random and on all-zero operands: a square 8192^3 product, and the
+    KV Bridging shape [1,048,576 x 2048] x [2048 x 256] (H times [W_K | W_V])
+    that hs2_bridge_kv_packed computes.  A reference for the MFMA-bound
+    kernels' fractions, not a part of the path."""
+    import torch
+
+    out = {}
+    for name, (m, kk, n) in (("square_8192", (8192, 8192, 8192)),
+                             ("bridge_shape_1m_x_2048_x_256", (1 << 20, 2048, 256))):
+        g = torch.Generator(device="cuda").manual_seed(5)
+        a = torch.randn((m, kk), generator=g, device="cuda").to(torch.bfloat16)
+        b = torch.randn((kk, n), generator=g, device="cuda").to(torch.bfloat16)
+        flop = 2.0 * m * n * kk
+        ms = time_events(lambda: torch.matmul(a, b), max(5, steps // 5), 3)
+        a.zero_()
+        b.zero_()
+        ms0 = time_events(lambda: torch.matmul(a, b), max(5, steps // 5), 3)
+        out[name] = {"ms": round(ms, 4), "TFLOPs": round(flop / (ms * 1e-3) / 1e12, 1),
+                     "mfma_bf16_frac": round(flop / (ms * 1e-3) / 2.5e15, 4),
+                     "ms_zero_operands": round(ms0, 4),
+                     "TFLOPs_zero_operands": round(flop / (ms0 * 1e-3) / 1e12, 1)}
+        del a, b
+    out["note"] = ("torch.matmul bf16 (hipBLASLt); the matrix cores' rate depends on the "
+                   "operand data, so random and zero operands are both given")
+    return out
+
+
 def extra_measurements(steps: int, warmup: int) -> dict:
     """The other shapes of the method, measured the same way (not the headline):
     batched decode at 64k, chunked prefill of 8,192 queries on a 131,072-token
@@ -449,6 +484,41 @@ def measured_traffic(kernels) -> float | None:
     if not all(k in per for k in kernels):
         return None
     return float(sum(per[k] for k in kernels))
+
+
+def oracle_check(w, inp, buf, seq: int = 0) -> dict:
+    """One sequence of the last timed step against the oracle (after the timed
+    region): element-wise relative error of the scores, the selection's
+    difference from the oracle's (only near-ties of the k-th score may
+    differ), and the sparse output's error on the GPU's own selection."""
+    import numpy as np
+
+    import oracle
+
+    sl = slice(seq, seq + 1)
+    ctx = inp["ctx_len"][sl]
+    n = int(ctx[0])
+    s_or, _, _ = oracle.full_attn_scores(inp["q"][sl], inp["k"][sl], ctx, tile_q=1,
+                                         sm_scale=w.sm_scale)
+    s_gpu = buf.scores[sl].cpu().numpy()
+    rel = np.abs(s_gpu[0, 0, :n].astype(np.float64) - s_or[0, 0, :n]) / np.maximum(
+        np.abs(s_or[0, 0, :n]), 1e-30)
+    top_or, cnt_or = oracle.select_topk_window(s_or, ctx, n_q=1, tile_q=1, k_top=w.k_top,
+                                               window=w.window)
+    top = buf.top_idx[sl].cpu().numpy()
+    cnt = buf.top_cnt[sl].cpu().numpy()
+    c = int(cnt_or[0, 0])
+    diff = np.setxor1d(top[0, 0, :c], top_or[0, 0, :c])
+    pe = oracle.pool_end(n - 1, w.window)
+    pool = s_or[0, 0, :pe].astype(np.float64)
+    tau = np.sort(pool)[::-1][c - 1] if c else 0.0
+    near = bool(np.all(np.abs(pool[diff] - tau) <= 1e-4 * tau)) if diff.size else True
+    o_or, _ = oracle.sparse_attention(inp["q"][sl], inp["k"][sl], inp["v"][sl], ctx, top, cnt,
+                                      tile_q=1, window=w.window, sm_scale=w.sm_scale)
+    o_err = float(np.abs(buf.o[sl].cpu().numpy() - o_or).max())
+    return {"sequence": seq, "scores_max_rel_err": float(rel.max()),
+            "top_cnt_equal": bool(cnt[0, 0] == c), "near_tie_swaps": int(diff.size // 2),
+            "swaps_all_near_ties": near, "o_max_abs_err": o_err}
 
 
 def cpu_baseline(w, inp, budget_s: float = 12.0) -> dict:
@@ -616,78 +686,89 @@ def main() -> int:
     print(f"[bench] inputs ready in {time.perf_counter() - t_gen:.1f} s", file=sys.stderr, flush=True)
     stream = torch.cuda.current_stream()
 
+    # Four distinct K/V caches (four full layers' caches, 2 GiB), used in turn,
+    # so that no step finds its K left in the 256 MB memory-side cache by the
+    # step before: in a model each full layer has a cache of its own.
+    rot = [buf] + [make_buffers(inp, n_heads=w.n_heads, k_top=w.k_top, window=w.window,
+                                sm_scale=w.sm_scale, dtype=w.dtype) for _ in range(3)]
+
     # Per-call timing (eager): HIP events on the stream the kernels run on.
     calls = {"scores": run_scores, "select": run_select, "sparse": run_sparse}
-    for _ in range(args.warmup):
-        run_step(buf)
+    for i in range(args.warmup):
+        run_step(rot[i % 4])
     torch.cuda.synchronize()
     per_call = {k: [] for k in calls}
-    for _ in range(args.steps):
+    for i in range(args.steps):
+        bb = rot[i % 4]
         for name, fn in calls.items():
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             e0.record(stream)
-            fn(buf)
+            fn(bb)
             e1.record(stream)
             per_call[name].append((e0, e1))
     torch.cuda.synchronize()
     call_ms = {k: float(np.mean([a.elapsed_time(b) for a, b in v])) for k, v in per_call.items()}
 
-    # Whole-step timing: exactly `steps` steps between two synchronisations.
-    # The step is the single-call decode step (hs2_decode_step) replayed from
-    # HIP graphs that hold GRAPH_STEPS consecutive steps each (a serving loop
-    # captures a whole model step, so the per-replay launch cost is not the
-    # layer's); the remainder runs from a one-step graph.  The same step
-    # issued as three calls is timed beside it.
-    def capture(fn, n):
+    def capture(fn, bufs):
+        """One HIP graph holding fn(b) for each b in bufs, in order."""
         g = torch.cuda.CUDAGraph()
         side = torch.cuda.Stream()
         side.wait_stream(stream)
         with torch.cuda.stream(side):
-            fn(buf)
+            for bb in bufs:
+                fn(bb)
         stream.wait_stream(side)
         torch.cuda.synchronize()
         with torch.cuda.graph(g):
-            for _ in range(n):
-                fn(buf)
+            for bb in bufs:
+                fn(bb)
         torch.cuda.synchronize()
         return g
 
-    def timed(fn, use_graph: bool):
-        if use_graph:
-            per = min(GRAPH_STEPS, args.steps)
-            g_many, g_one = capture(fn, per), capture(fn, 1)
-            plan = [g_many] * (args.steps // per) + [g_one] * (args.steps % per)
-            warm = [g_one] * args.warmup
+    def timed(fn, bufs, n_steps, n_warm):
+        """Milliseconds per step over exactly n_steps steps (after n_warm untimed
+        ones), the steps cycling through bufs: from HIP graphs of GRAPH_ROUNDS
+        rounds (a serving loop captures a whole model step, so the per-replay
+        launch cost is not the layer's) plus one-step graphs for the rest, or
+        eager calls when --graph 0.  Also returns the wall time of the region."""
+        per = GRAPH_ROUNDS * len(bufs)
+        if args.graph:
+            g_many = capture(fn, bufs * GRAPH_ROUNDS)
+            g_one = [capture(fn, [bb]) for bb in bufs]
+            plan = lambda n: [g_many] * (n // per) + [g_one[i % len(bufs)] for i in range(n % per)]  # noqa: E731
             run = lambda gs: [g.replay() for g in gs]  # noqa: E731
         else:
-            plan = [None] * args.steps
-            warm = [None] * args.warmup
-            run = lambda gs: [fn(buf) for _ in gs]  # noqa: E731
-        run(warm)
+            plan = lambda n: [bufs[i % len(bufs)] for i in range(n)]  # noqa: E731
+            run = lambda bs: [fn(bb) for bb in bs]  # noqa: E731
+        run(plan(n_warm))
         torch.cuda.synchronize()
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         t_wall = time.perf_counter()
         e0.record(stream)
-        run(plan)
+        run(plan(n_steps))
         e1.record(stream)
         torch.cuda.synchronize()
-        return e0.elapsed_time(e1) / args.steps, (time.perf_counter() - t_wall) * 1e3
+        return e0.elapsed_time(e1) / n_steps, (time.perf_counter() - t_wall) * 1e3
 
-    ms_3call, _ = timed(run_step, bool(args.graph))
-    ms, wall_ms = timed(run_fused_step, bool(args.graph))
+    # The headline: the single-call step (hs2_decode_step) over the four caches.
+    ms, wall_ms = timed(run_fused_step, rot, args.steps, args.warmup)
+    # Beside it: the same step on one cache only (part of K then comes from the
+    # memory-side cache), and the step issued as three calls over the four caches.
+    ms_same, _ = timed(run_fused_step, [buf], args.steps, args.warmup)
+    ms_3call, _ = timed(run_step, rot, args.steps, args.warmup)
 
     # Spread of single steps (after the timed region, not part of `value`):
-    # each step replayed alone between two events.
+    # each step replayed alone between two events, the caches in turn.
     def per_step(fn, n):
-        g = capture(fn, 1) if args.graph else None
-        run1 = g.replay if g is not None else (lambda: fn(buf))
-        for _ in range(3):
-            run1()
+        gs = [capture(fn, [bb]) for bb in rot] if args.graph else None
+        run1 = [g.replay for g in gs] if gs else [lambda bb=bb: fn(bb) for bb in rot]
+        for i in range(4):
+            run1[i]()
         ev = []
-        for _ in range(n):
+        for i in range(n):
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             e0.record(stream)
-            run1()
+            run1[i % 4]()
             e1.record(stream)
             ev.append((e0, e1))
         torch.cuda.synchronize()
@@ -697,43 +778,8 @@ def main() -> int:
                 "p90": round(float(np.percentile(us, 90)), 2), "n": n}
 
     step_spread = per_step(run_fused_step, max(args.steps, 20))
-
-    # The same step over four distinct caches in turn (four full layers' K/V,
-    # 2 GiB), so that no step finds its cache left in the 256 MB memory-side
-    # cache by the previous step; within a step the second K pass still
-    # re-reads what the first just read, as it would in a model.
-    rot = [buf] + [make_buffers(inp, n_heads=w.n_heads, k_top=w.k_top, window=w.window,
-                                sm_scale=w.sm_scale, dtype=w.dtype) for _ in range(3)]
-
-    def rotating(n_rounds):
-        g = torch.cuda.CUDAGraph()
-        side = torch.cuda.Stream()
-        side.wait_stream(stream)
-        with torch.cuda.stream(side):
-            for bb in rot:
-                run_fused_step(bb)
-        stream.wait_stream(side)
-        torch.cuda.synchronize()
-        with torch.cuda.graph(g):
-            for _ in range(n_rounds):
-                for bb in rot:
-                    run_fused_step(bb)
-        torch.cuda.synchronize()
-        return g
-
-    g_rot = rotating(2)  # 8 steps per replay
-    reps = max(1, args.steps // 8)
-    for _ in range(2):
-        g_rot.replay()
-    torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record(stream)
-    for _ in range(reps):
-        g_rot.replay()
-    e1.record(stream)
-    torch.cuda.synchronize()
-    ms_rot = e0.elapsed_time(e1) / (8 * reps)
-    del g_rot, rot[1:]
+    check = oracle_check(w, inp, buf)
+    del rot[1:]
     # Measured copy bandwidth of the box (a plain 1 GiB device copy, read +
     # write bytes), the practical ceiling the step's HBM rate is also set against.
     src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda").fill_(1)
@@ -768,32 +814,32 @@ def main() -> int:
             "head_dim": w.head_dim,
             "k_top": w.k_top,
             "window": w.window,
+            "step": "hs2_decode_step (scoring + selection + sparse layer, one call), "
+                    "over four distinct K/V caches in turn",
             "graph": bool(args.graph),
-            "graph_steps": min(GRAPH_STEPS, args.steps) if args.graph else 0,
+            "graph_steps": GRAPH_ROUNDS * 4 if args.graph else 0,
             "step_algorithmic_MiB": round(ab["step"] / MIB, 2),
             "step_hbm_GBps": round(step_gbs, 1),
             "step_hbm_frac": round(step_gbs / HBM_PEAK_GBS, 4),
             "call_ms": {k: round(v, 5) for k, v in call_ms.items()},
-            "step": "hs2_decode_step (scoring + selection + sparse layer, one call)",
+            "ms_per_step_same_cache": round(ms_same, 5),
+            "tokens_per_s_same_cache": round(w.batch / (ms_same * 1e-3), 1),
             "ms_per_step_three_calls": round(ms_3call, 5),
             "wall_ms_timed_region": round(wall_ms, 3),
             "single_step_us": step_spread,
-            "ms_per_step_four_caches": round(ms_rot, 5),
-            "tokens_per_s_four_caches": round(w.batch / (ms_rot * 1e-3), 1),
             "hbm_copy_GBps": round(copy_gbs, 1),
             "step_hbm_frac_of_copy": round(step_gbs / copy_gbs, 4),
             "scoring_call_hbm_frac_of_copy": round(score_gbs / copy_gbs, 4),
+            "oracle_check": check,
         },
         "roofline": {
-            "kernel": "hs2_full_attn_scores = score_p1_bf16<false> + "
-                      "score_p2_bf16<false, false, false> (two K streams)",
+            "kernel": f"{SCORE_KERNEL} (hs2_full_attn_scores: K read once)",
             "bound": "hbm",
             "achieved": round(score_gbs, 1),
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(score_gbs / HBM_PEAK_GBS, 4),
-            "traffic": measured_traffic(["score_p1_bf16<false>",
-                                         "score_p2_bf16<false, false, false>"]),
+            "traffic": measured_traffic([SCORE_KERNEL]),
             "algorithmic_bytes_per_launch": ab["scoring_call"],
         },
     }
@@ -808,6 +854,7 @@ def main() -> int:
         out["extras"]["swa_bf16_prefill_8k_w128"] = swa_measurements(args.steps, args.warmup)
         out["extras"]["decode_bf16_256k_b4_full_layer"] = full_output_measurements(args.steps,
                                                                                   args.warmup)
+        out["extras"]["mfma_calibration"] = mfma_calibration(args.steps, args.warmup)
     if args.calibrate:
         src = torch.empty(256 * MIB, dtype=torch.uint8, device="cuda").fill_(1)
         dst = torch.empty_like(src)

@@ -29,7 +29,10 @@
  *   never synchronises.  Work is enqueued asynchronously on `stream` (a
  *   hipStream_t; NULL means the default stream).
  * - Arguments are validated on the host before anything is enqueued: a call
- *   that returns an error status has enqueued nothing and written nothing.
+ *   that returns HS2_EINVAL, HS2_EUNSUPPORTED, HS2_EALIGN or HS2_EWORKSPACE
+ *   has enqueued nothing and written nothing.  HS2_EHIP reports that the HIP
+ *   runtime refused a kernel launch; kernels that the same call launched
+ *   before it may already be enqueued, so the outputs are then undefined.
  *   Asynchronous device faults surface at the caller's next synchronisation.
  * - Every pointer must be 16-byte aligned (HS2_EALIGN otherwise).
  * - Shapes: B = batch, Q = n_q new queries per sequence, H = query heads,
@@ -52,6 +55,13 @@
  *   3 mantissa bits, subnormals, no infinities; 0x7F/0xFF are NaN).
  * - Calls are reentrant.  A workspace may be shared by calls issued in order
  *   on one stream, never by calls that can run concurrently.
+ * - Decode scoring of a bf16 or E4M3 cache (hs2_full_attn_scores without
+ *   o_full, and the decode steps) reads K once with one workgroup on each
+ *   compute unit, and those workgroups wait for one another.  So two such
+ *   calls must not run at the same time on one GPU, whatever their streams
+ *   or workspaces.  Waits are bounded (about 1 s), after which the scores of
+ *   the sequences concerned are NaN.  Batches larger than the GPU's compute
+ *   unit count take a two-pass path with no such wait.
  * - kv_capacity is at most 4,194,304 keys (HS2_EUNSUPPORTED beyond).
  */
 #ifndef HS2_H_
@@ -99,7 +109,8 @@ typedef struct {
   int n_q;        /* new queries per sequence: 1 (decode) or a multiple of tile_q */
   int n_heads;    /* query heads, 1..32, all sharing one K/V head (MQA) */
   int head_dim;   /* must be 128 */
-  int tile_q;     /* queries per selection group: 1 (decode) or 64 (prefill) */
+  int tile_q;     /* queries per selection group: 1 (decode), or a multiple of 16 for
+                     bf16 chunked prefill (64 in the benchmarks) */
   int k_top;      /* selected keys per group, 0..2048 (1024 in HySparse2) */
   int window;     /* forced recent-token window, 0..2048 (128 in HySparse2) */
   int causal;     /* must be 1 */

@@ -21,10 +21,9 @@
 //              keys, so row max/sum stay in-lane; per key split, partial
 //              (max, sum) per row.
 //   pf_colsum: Q as the A operand: a lane owns one key over 16 rows; after
-//              p = 2^(x - L) the column sum over the wave's rows is one more
-//              MFMA against a vector of ones, with p split into a bf16 high
-//              and low part so the sum keeps about fp32 accuracy; the 16
-//              waves are added in a fixed order and written per
+//              p = 2^(x - L) the column sum over the wave's rows is an fp32
+//              sum in the lane plus one add across the two lane halves; the
+//              16 waves are added in a fixed order and written per
 //              (16-query block, key).
 //   pf_reduce: I_t[j] = sum of the tile's 16-query blocks, in order.
 //   pf_sparse: 8 queries per workgroup; gathered keys (the tile's selection,

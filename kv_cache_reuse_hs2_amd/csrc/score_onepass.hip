@@ -59,7 +59,11 @@ namespace {
 
 constexpr int kOpWaves = 4;
 constexpr int kOpThreads = 64 * kOpWaves;
-constexpr int kRegBlocks = 16;  // 32-key tiles per wave kept in registers (even)
+// 32-key tiles per wave kept in registers: the most that compile without
+// spilling (bf16 K needs more registers in flight than E4M3 K, but the
+// compiler's allocation differs between the two).
+constexpr int kOpRegBlocksBf16 = 20;
+constexpr int kOpRegBlocksFp8 = 16;
 constexpr int kLdsBlocks = 9;   // ... kept in LDS
 constexpr float kRefMin = -1e30f;           // reference of a lane that has seen no key
 constexpr float kRescale = 64.f;            // binades a logit may exceed its reference
@@ -69,11 +73,12 @@ constexpr uint64_t kTagMix = 0x9E3779B97F4A7C15ull;
 __device__ __forceinline__ uint64_t slot_tag(uint64_t gen) { return gen ^ kTagMix; }
 
 struct OpLds {
-  union {
-    float4 tile[kOpWaves][kLdsBlocks][4][64];  // kept logit tiles: 16 floats per lane
-    uint32_t hist[kSelBins];                   // phase 2, once the tiles are read
-  } u;
-  float2 red[8][32];  // per-wave statistics (end of phase 1), fold partials (phase 2)
+  float4 tile[kOpWaves][kLdsBlocks][4][64];  // kept logit tiles: 16 floats per lane
+  // Phase 2: the workgroup's histogram of the top 12 bits of its pool scores,
+  // two 16-bit counts per word (bin 2w in the low half of word w); a
+  // workgroup counts at most 4,096 keys, so no count reaches the high half.
+  uint32_t hist16[kSelBins / 2];
+  float2 red[16][32];  // per-wave statistics (end of phase 1), fold partials (phase 2)
   float s_L[32];
   uint64_t tag;
   int wflag[2][kOpWaves];  // barrier polling: per-wave verdicts, by iteration parity
@@ -124,7 +129,7 @@ __device__ __forceinline__ void half_reduce_scatter(const float (&v)[16], const 
   // slot s = 8*b4 + 4*b3 + 2*b2 + b1 = r32 >> 1
 }
 
-template <bool kFp8, bool kHist>
+template <bool kFp8, bool kHist, int kRegBlocks>
 __global__ __launch_bounds__(kOpThreads) __attribute__((amdgpu_waves_per_eu(1, 1))) void
 score_onepass(const uint16_t* __restrict__ q, const void* __restrict__ k, int64_t kv_stride,
               const int32_t* __restrict__ ctx_len, int cap, int H, float c2, int nwg, int chunk,
@@ -137,8 +142,9 @@ score_onepass(const uint16_t* __restrict__ q, const void* __restrict__ k, int64_
   const int j_begin = c * chunk;
   const int j_end = min(N, j_begin + chunk);
   const bool any = j_begin < j_end;  // workgroup-uniform
-  const int nbw = chunk / (32 * kOpWaves);  // blocks per wave (even)
+  const int nbw = chunk / (32 * kOpWaves);  // blocks per wave
   const int nR = nbw - kRegBlocks;          // blocks before the register-kept ones
+  const int nS = nR - kLdsBlocks;           // blocks kept nowhere (read again in phase 2)
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int r32 = lane & 31, hh = lane >> 5;
   uint64_t* const gen_word = sync + b;
@@ -161,10 +167,42 @@ score_onepass(const uint16_t* __restrict__ q, const void* __restrict__ k, int64_
   bf16x8_t qreg[8];
   load_q_bf16<kFp8>(q + (size_t)b * H * kHeadDim, H, r32, hh, qreg);
   // Key rows of local block i of this wave (clamped into the context, so every
-  // load is in bounds; blocks outside [j_begin, j_end) are never computed).
+  // load is in bounds; blocks outside [j_begin, j_end) are never folded).
   auto jb_of = [&](int i) { return j_begin + 32 * (i * kOpWaves + wave); };
   auto row_of = [&](int i) { return min(max(jb_of(i) + r32, 0), N - 1); };
   auto live = [&](int i) { return i >= 0 && jb_of(i) < j_end; };
+
+  // One register set of K, reloaded piece by piece: as soon as an MFMA has
+  // taken a 16-byte piece of the current block, the same piece of the block at
+  // next_row is loaded into its place, so the next block's loads are in flight
+  // while the current one is folded, in the registers of one block.
+  u32x4 kc[k_regs<kFp8>()];
+  auto logits_roll = [&](int next_row) {
+    const u32x4* kp = reinterpret_cast<const u32x4*>(
+                          kb + (size_t)next_row * kHeadDim * kv_elem_bytes<kFp8>()) + hh;
+    f32x16_t acc = {};
+    if constexpr (kFp8) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+            qreg[2 * i], as_bf16x8(e4m3x8_to_bf16x8(kc[i][0], kc[i][1])), acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+            qreg[2 * i + 1], as_bf16x8(e4m3x8_to_bf16x8(kc[i][2], kc[i][3])), acc, 0, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
+        kc[i] = kp[2 * i];
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qreg[e], as_bf16x8(kc[e]), acc, 0, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
+        kc[e] = kp[2 * e];
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+    return acc;
+  };
 
   float mref[16], lsum[16];
 #pragma unroll
@@ -172,80 +210,73 @@ score_onepass(const uint16_t* __restrict__ q, const void* __restrict__ k, int64_
     mref[r] = kRefMin;
     lsum[r] = 0.f;
   }
-  auto logits = [&](const u32x4 (&kc)[k_regs<kFp8>()]) {
-    f32x16_t acc = {};
-#pragma unroll
-    for (int i = 0; i < 8; ++i)
-      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qreg[i], k_operand<kFp8>(kc, i), acc, 0, 0, 0);
-    return acc;
-  };
+  // A kept tile holds e = 2^(x - mref) (the terms of the running sums), so
+  // that phase 2 needs no exponential: 2^(x - L) = e * 2^(mref - L).  If the
+  // references move after the wave has kept tiles (a logit more than 2^6 above
+  // them), the kept values no longer share one scale: the wave then reads all
+  // its blocks again in phase 2 (late_move, wave-uniform).
+  bool kept_any = false, late_move = false;
   auto fold_tile = [&](const f32x16_t& acc, int jb) {
     const bool valid = jb + r32 < j_end;
-    float x[16];
+    float dx[16];
     bool up = false;
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      x[r] = valid ? acc[r] * c2 : -INFINITY;
-      up |= x[r] > mref[r] + kRescale;
+      dx[r] = (valid ? acc[r] * c2 : -INFINITY) - mref[r];
+      up |= dx[r] > kRescale;
     }
     if (__builtin_amdgcn_ballot_w64(up) != 0) {  // rare: move the references up
+      late_move |= kept_any;
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        float bm = x[r];
+        const float x = valid ? acc[r] * c2 : -INFINITY;
+        float bm = x;
 #pragma unroll
         for (int o = 1; o < 32; o <<= 1) bm = fmaxf(bm, __shfl_xor(bm, o));
         const float mn = fmaxf(mref[r], bm);
         lsum[r] *= fast_exp2(mref[r] - mn);
         mref[r] = mn;
+        dx[r] = x - mn;
       }
     }
+    f32x16_t e;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) lsum[r] += fast_exp2(x[r] - mref[r]);
+    for (int r = 0; r < 16; ++r) {
+      e[r] = fast_exp2(dx[r]);
+      lsum[r] += e[r];
+    }
+    return e;
   };
 
   f32x16_t keep[kRegBlocks];
-  u32x4 ka[k_regs<kFp8>()], kn[k_regs<kFp8>()];
-  float4* my_tiles = &S.u.tile[wave][0][0][0];
+  float4* my_tiles = &S.tile[wave][0][0][0];
   if (any) {
     // ---- phase 1 ------------------------------------------------------------
-    // Blocks [0, nR): streamed, the last kLdsBlocks of them kept in LDS; then
-    // kRegBlocks blocks kept in registers.  Two register sets are used in
-    // turn with unconditional loads, so the next block's loads are in flight
-    // while the current one is computed.
-    load_k_block<kFp8>(kb, row_of(nR > 0 ? 0 : nR), hh, ka);
-    auto stream_block = [&](const u32x4 (&kc)[k_regs<kFp8>()], int i) {
-      if (!live(i)) return;
-      const f32x16_t acc = logits(kc);
-      fold_tile(acc, jb_of(i));
-      const int s = i - (nR - kLdsBlocks);
-      if (s >= 0) {
-        float4* t = my_tiles + s * 4 * 64 + lane;
+    // Blocks [0, nR) are folded, the last kLdsBlocks of them kept in LDS; the
+    // next kRegBlocks blocks are folded and kept in registers.  The last
+    // reload fetches the first block to be read again in phase 2.
+    load_k_block<kFp8>(kb, row_of(nR > 0 ? 0 : nR), hh, kc);
+    for (int i = 0; i < nR; ++i) {
+      const f32x16_t acc = logits_roll(row_of(i + 1));
+      if (live(i)) {
+        const f32x16_t e = fold_tile(acc, jb_of(i));
+        const int s = i - nS;
+        if (s >= 0) {
+          float4* t = my_tiles + s * 4 * 64 + lane;
 #pragma unroll
-        for (int p = 0; p < 4; ++p)
-          t[p * 64] = make_float4(acc[4 * p], acc[4 * p + 1], acc[4 * p + 2], acc[4 * p + 3]);
+          for (int p = 0; p < 4; ++p)
+            t[p * 64] = make_float4(e[4 * p], e[4 * p + 1], e[4 * p + 2], e[4 * p + 3]);
+          kept_any = true;
+        }
       }
-    };
-    for (int i = 0; i < nR; i += 2) {
-      load_k_block<kFp8>(kb, row_of(i + 1), hh, kn);
-      __builtin_amdgcn_sched_barrier(0);
-      stream_block(ka, i);
-      load_k_block<kFp8>(kb, row_of(i + 2), hh, ka);
-      __builtin_amdgcn_sched_barrier(0);
-      stream_block(kn, i + 1);
     }
 #pragma unroll
     for (int t = 0; t < kRegBlocks; ++t) {
       const int i = nR + t;
-      if (t + 1 < kRegBlocks) {
-        if (t & 1)
-          load_k_block<kFp8>(kb, row_of(i + 1), hh, ka);
-        else
-          load_k_block<kFp8>(kb, row_of(i + 1), hh, kn);
-      }
-      __builtin_amdgcn_sched_barrier(0);
+      const f32x16_t acc = logits_roll(row_of(min(i + 1, nbw - 1)));
       if (live(i)) {
-        keep[t] = (t & 1) ? logits(kn) : logits(ka);
-        fold_tile(keep[t], jb_of(i));
+        keep[t] = fold_tile(acc, jb_of(i));
+        kept_any = true;
       }
     }
   }
@@ -317,25 +348,43 @@ score_onepass(const uint16_t* __restrict__ q, const void* __restrict__ k, int64_
     }
   }
   // ---- phase 2 --------------------------------------------------------------
-  // Fold the sequence's rows into L_h (coherent loads: the rows come from other
-  // CUs of this launch).
+  // Fold the sequence's rows into L_h with coherent loads (the rows come from
+  // other CUs of this launch).  Thread t takes 16-byte piece t % 16 (heads
+  // 2p, 2p + 1) of rows t / 16, t / 16 + 16, ...; its loads are issued four
+  // at a time, then merged.
   {
-    const int h = threadIdx.x & 31, part = threadIdx.x >> 5;
+    const int pc = threadIdx.x & 15, r0 = threadIdx.x >> 4;
     const __amdgpu_buffer_rsrc_t rs =
         rsrc_of(stats + (size_t)b * nwg * 64, (uint32_t)(nwg * 64 * sizeof(float)));
-    float m = -INFINITY, l = 0.f;
-    for (int cc = part; cc < nwg; cc += 8) {
-      const float2 v = __builtin_bit_cast(
-          float2, __builtin_amdgcn_raw_buffer_load_b64(rs, (cc * 64 + 2 * h) * 4, 0, kSc1));
-      merge_ml(m, l, v.x, v.y);
+    float ma = -INFINITY, la = 0.f, mb = -INFINITY, lb = 0.f;
+    for (int base = r0; base < nwg; base += 4 * 16) {
+      float4 v[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int cc = base + 16 * u;
+        v[u] = cc < nwg ? __builtin_bit_cast(
+                              float4, __builtin_amdgcn_raw_buffer_load_b128(
+                                          rs, (cc * 64 + 4 * pc) * 4, 0, kSc1))
+                        : make_float4(-INFINITY, 0.f, -INFINITY, 0.f);
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        merge_ml(ma, la, v[u].x, v[u].y);
+        merge_ml(mb, lb, v[u].z, v[u].w);
+      }
     }
-    S.red[part][h] = make_float2(m, l);
+    // 16 partials per head pair: in LDS, then one thread per head.
+    float2 (*part)[32] = S.red;  // reused as [16 row groups][16 pieces] of two heads
+    reinterpret_cast<float4*>(&part[0][0])[r0 * 16 + pc] = make_float4(ma, la, mb, lb);
     __syncthreads();
     if (threadIdx.x < 32) {
-      m = S.red[0][h].x;
-      l = S.red[0][h].y;
+      const int h = threadIdx.x, p = h >> 1, second = h & 1;
+      float m = -INFINITY, l = 0.f;
 #pragma unroll
-      for (int p = 1; p < 8; ++p) merge_ml(m, l, S.red[p][h].x, S.red[p][h].y);
+      for (int rr = 0; rr < 16; ++rr) {
+        const float4 v = reinterpret_cast<const float4*>(&part[0][0])[rr * 16 + p];
+        merge_ml(m, l, second ? v.z : v.x, second ? v.w : v.y);
+      }
       const float L = (l > 0.f) ? m + log2f(l) : -INFINITY;
       S.s_L[h] = (h < H) ? L : INFINITY;  // padded heads contribute 2^-inf = 0
       if (lse_out != nullptr && c == 0 && h < H) lse_out[b * H + h] = L * 0.69314718055994531f;
@@ -348,23 +397,59 @@ score_onepass(const uint16_t* __restrict__ q, const void* __restrict__ k, int64_
   for (int r = 0; r < 16; ++r) L[r] = S.s_L[8 * (r >> 2) + 4 * hh + (r & 3)];
   float* out = scores + (size_t)b * score_stride;
   const int pe = N - window;  // decode pool end
-  const int nS = nR - kLdsBlocks;  // blocks that were not kept
-  // Start re-reading the first block that was not kept.
-  if (nS > 0) load_k_block<kFp8>(kb, row_of(0), hh, ka);
+  if (kHist) {
+    for (int i = threadIdx.x; i < kSelBins / 2; i += kOpThreads) S.hist16[i] = 0u;
+    __syncthreads();
+  }
+  // From logits (blocks read again): sum_h 2^(x - L_h).
   auto importance = [&](const f32x16_t& acc) {
     float imp = 0.f;
 #pragma unroll
     for (int r = 0; r < 16; ++r) imp += fast_exp2(acc[r] * c2 - L[r]);
     return imp + __shfl_xor(imp, 32);
   };
-  // LDS-kept tiles first (their scores are held until the histogram is free).
-  float lds_imp[kLdsBlocks];
+  // From kept terms e = 2^(x - mref): sum_h e * 2^(mref_h - L_h).
+  float wt[16];
 #pragma unroll
-  for (int s = 0; s < kLdsBlocks; ++s) {
-    const int i = nR - kLdsBlocks + s;
-    lds_imp[s] = 0.f;
-    if (live(i)) {
-      const float4* t = my_tiles + s * 4 * 64 + lane;
+  for (int r = 0; r < 16; ++r) wt[r] = fast_exp2(mref[r] - L[r]);
+  auto importance_kept = [&](const f32x16_t& e) {
+    float imp = 0.f;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) imp = fmaf(e[r], wt[r], imp);
+    return imp + __shfl_xor(imp, 32);
+  };
+  // After a late move of the references every block of the wave is read again.
+  const int n_re = late_move ? nbw : nS;
+  auto emit = [&](float imp, int jb) {
+    const int j = jb + r32;
+    if (hh == 0 && j < j_end) {
+      out[j] = imp;
+      if (kHist && j < pe) {
+        const uint32_t bin = order_key(imp) >> 20;
+        atomicAdd(&S.hist16[bin >> 1], 1u << (16 * (bin & 1)));
+      }
+    }
+  };
+  // Register-kept tiles first (their registers are then free), then the
+  // LDS-kept ones, then the blocks kept nowhere, read again four at a time
+  // with all their loads in flight together.  The importance of a group of
+  // tiles is computed before any of it is stored, so that the tiles' exp2
+  // chains and cross-half adds overlap.
+  if (!late_move) {
+    float imp[kRegBlocks];
+#pragma unroll
+    for (int t = 0; t < kRegBlocks; ++t) imp[t] = importance_kept(keep[t]);
+#pragma unroll
+    for (int t = 0; t < kRegBlocks; ++t)
+      if (live(nR + t)) emit(imp[t], jb_of(nR + t));
+  }
+  constexpr int kLdsGroup = 3;
+  static_assert(kLdsBlocks % kLdsGroup == 0, "LDS tiles go in groups");
+  for (int s0 = 0; s0 < (late_move ? 0 : kLdsBlocks); s0 += kLdsGroup) {
+    float imp[kLdsGroup];
+#pragma unroll
+    for (int u = 0; u < kLdsGroup; ++u) {
+      const float4* t = my_tiles + (s0 + u) * 4 * 64 + lane;
       f32x16_t acc;
 #pragma unroll
       for (int p = 0; p < 4; ++p) {
@@ -374,50 +459,35 @@ score_onepass(const uint16_t* __restrict__ q, const void* __restrict__ k, int64_
         acc[4 * p + 2] = v.z;
         acc[4 * p + 3] = v.w;
       }
-      lds_imp[s] = importance(acc);
-      const int j = jb_of(i) + r32;
-      if (hh == 0 && j < j_end) out[j] = lds_imp[s];
+      imp[u] = importance_kept(acc);
     }
-  }
-  if (kHist) {
-    __syncthreads();  // every wave has read its tiles
-    for (int i = threadIdx.x; i < kSelBins; i += kOpThreads) S.u.hist[i] = 0u;
-    __syncthreads();
 #pragma unroll
-    for (int s = 0; s < kLdsBlocks; ++s) {
-      const int i = nR - kLdsBlocks + s;
-      const int j = jb_of(i) + r32;
-      if (live(i) && hh == 0 && j < j_end && j < pe)
-        atomicAdd(&S.u.hist[order_key(lds_imp[s]) >> 20], 1u);
-    }
+    for (int u = 0; u < kLdsGroup; ++u)
+      if (live(nS + s0 + u)) emit(imp[u], jb_of(nS + s0 + u));
   }
-  auto emit = [&](float imp, int jb) {
-    const int j = jb + r32;
-    if (hh == 0 && j < j_end) {
-      out[j] = imp;
-      if (kHist && j < pe) atomicAdd(&S.u.hist[order_key(imp) >> 20], 1u);
-    }
-  };
+  for (int i0 = 0; i0 < n_re; i0 += 4) {
+    u32x4 kr[4][k_regs<kFp8>()];
 #pragma unroll
-  for (int t = 0; t < kRegBlocks; ++t) {
-    const int i = nR + t;
-    if (live(i)) emit(importance(keep[t]), jb_of(i));
-  }
-  // Blocks that did not fit: read again.
-  for (int i = 0; i < nS; i += 2) {
-    load_k_block<kFp8>(kb, row_of(i + 1 < nS ? i + 1 : i), hh, kn);
-    __builtin_amdgcn_sched_barrier(0);
-    if (live(i)) emit(importance(logits(ka)), jb_of(i));
-    if (i + 1 >= nS) break;
-    load_k_block<kFp8>(kb, row_of(i + 2 < nS ? i + 2 : i + 1), hh, ka);
-    __builtin_amdgcn_sched_barrier(0);
-    if (live(i + 1)) emit(importance(logits(kn)), jb_of(i + 1));
+    for (int u = 0; u < 4; ++u) load_k_block<kFp8>(kb, row_of(min(i0 + u, n_re - 1)), hh, kr[u]);
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      if (i0 + u >= n_re) break;
+      f32x16_t acc = {};
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qreg[e], k_operand<kFp8>(kr[u], e), acc, 0,
+                                                      0, 0);
+      if (live(i0 + u)) emit(importance(acc), jb_of(i0 + u));
+    }
   }
   if (kHist) {
     __syncthreads();
     uint32_t* gh = hist + (size_t)b * kHistRow;
-    for (int i = threadIdx.x; i < kSelBins; i += kOpThreads)
-      if (S.u.hist[i] != 0u) atomicAdd(&gh[i], S.u.hist[i]);
+    for (int w = threadIdx.x; w < kSelBins / 2; w += kOpThreads) {
+      const uint32_t two = S.hist16[w];
+      if (two & 0xFFFFu) atomicAdd(&gh[2 * w], two & 0xFFFFu);
+      if (two >> 16) atomicAdd(&gh[2 * w + 1], two >> 16);
+    }
   }
 }
 
@@ -455,19 +525,19 @@ hipError_t launch_score_onepass(const hs2_attn_desc& d, const void* q, const voi
   const dim3 grid(d.batch * nwg);
   const bool fp8 = d.dtype == HS2_FP8_E4M3;
   if (fp8 && hist)
-    score_onepass<true, true><<<grid, kOpThreads, 0, st>>>(qq, k, kv_stride, ctx_len, cap,
+    score_onepass<true, true, kOpRegBlocksFp8><<<grid, kOpThreads, 0, st>>>(qq, k, kv_stride, ctx_len, cap,
                                                            d.n_heads, c2, nwg, chunk, stats, sync,
                                                            scores, cap, lse, hist, d.window);
   else if (fp8)
-    score_onepass<true, false><<<grid, kOpThreads, 0, st>>>(qq, k, kv_stride, ctx_len, cap,
+    score_onepass<true, false, kOpRegBlocksFp8><<<grid, kOpThreads, 0, st>>>(qq, k, kv_stride, ctx_len, cap,
                                                             d.n_heads, c2, nwg, chunk, stats,
                                                             sync, scores, cap, lse, hist, d.window);
   else if (hist)
-    score_onepass<false, true><<<grid, kOpThreads, 0, st>>>(qq, k, kv_stride, ctx_len, cap,
+    score_onepass<false, true, kOpRegBlocksBf16><<<grid, kOpThreads, 0, st>>>(qq, k, kv_stride, ctx_len, cap,
                                                             d.n_heads, c2, nwg, chunk, stats,
                                                             sync, scores, cap, lse, hist, d.window);
   else
-    score_onepass<false, false><<<grid, kOpThreads, 0, st>>>(qq, k, kv_stride, ctx_len, cap,
+    score_onepass<false, false, kOpRegBlocksBf16><<<grid, kOpThreads, 0, st>>>(qq, k, kv_stride, ctx_len, cap,
                                                              d.n_heads, c2, nwg, chunk, stats,
                                                              sync, scores, cap, lse, hist,
                                                              d.window);
