@@ -106,7 +106,8 @@ typedef enum { HS2_F32 = 0, HS2_BF16 = 1, HS2_FP8_E4M3 = 2 } hs2_dtype;
 /* Attention problem shared by the scoring, selection and sparse calls. */
 typedef struct {
   int batch;      /* B >= 1 */
-  int n_q;        /* new queries per sequence: 1 (decode) or a multiple of tile_q */
+  int n_q;        /* new queries per sequence: 1 (decode) or a multiple of tile_q;
+                     batch * n_q <= 2^24 (HS2_EUNSUPPORTED beyond) */
   int n_heads;    /* query heads, 1..32, all sharing one K/V head (MQA) */
   int head_dim;   /* must be 128 */
   int tile_q;     /* queries per selection group: 1 (decode), or a multiple of 16 for

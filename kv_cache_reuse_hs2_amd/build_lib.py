@@ -1,7 +1,7 @@
 """Build libhs2.so (gfx950) in-tree with hipcc.
 
 Usage: ``python -m kv_cache_reuse_hs2_amd.build_lib`` or ``build()`` from
-Python.  Each ``csrc/*.hip`` is compiled to an object in parallel, then linked
+Python.  Each ``csrc/*.hip`` and ``csrc/*.cpp`` is compiled to an object in parallel, then linked
 into ``kv_cache_reuse_hs2_amd/libhs2.so``.  Cross-compiles without a GPU.
 """
 
@@ -52,7 +52,8 @@ def _compile(src: str) -> str:
 
 def build(verbose: bool = True) -> str:
     os.makedirs(BUILD, exist_ok=True)
-    sources = sorted(glob.glob(os.path.join(CSRC, "*.hip")))
+    # Kernels and launchers (*.hip) and the host-only argument checks (*.cpp).
+    sources = sorted(glob.glob(os.path.join(CSRC, "*.hip")) + glob.glob(os.path.join(CSRC, "*.cpp")))
     with concurrent.futures.ThreadPoolExecutor(max_workers=min(8, len(sources))) as ex:
         objs = list(ex.map(_compile, sources))
     tmp = LIB + ".tmp"

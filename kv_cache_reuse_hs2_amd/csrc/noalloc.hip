@@ -4,6 +4,7 @@
 #include <mutex>
 
 #include "hs2_internal.h"
+#include "validate.h"
 
 namespace {
 
@@ -43,12 +44,11 @@ hs2_status hs2_decode_step_noalloc(const hs2_attn_desc* desc, const void* q, con
                                    float* lse_full, int32_t* top_idx, int32_t* top_cnt, float* o,
                                    float* lse, hs2_stream_t stream) {
   // Every argument is checked before the runtime is asked for anything.
-  hs2_status s = hs2::check_step_args(desc, q, q_sparse == nullptr ? q : q_sparse, k, v,
-                                      kv_stride, ctx_len, kv_capacity, scores, lse_full, top_idx,
-                                      top_cnt, o, lse);
+  hs2_status s = hs2::validate_step_noalloc(desc, q, q_sparse, k, v, kv_stride, ctx_len,
+                                            kv_capacity, scores, lse_full, top_idx, top_cnt, o,
+                                            lse, kScratchBytes);
   if (s != HS2_OK) return s;
   const size_t need = hs2_workspace_size(desc, kv_capacity);
-  if (need > kScratchBytes) return HS2_EWORKSPACE;
   void* ws = nullptr;
   if ((s = scratch_address(&ws)) != HS2_OK) return s;
   return hs2_decode_step(desc, q, q_sparse, k, v, kv_stride, ctx_len, kv_capacity, scores,

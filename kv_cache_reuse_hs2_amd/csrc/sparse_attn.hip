@@ -73,7 +73,7 @@ __device__ __forceinline__ int sel_key(const QueryGeom& q, const int32_t* top_ro
 // bf16, MFMA.
 
 constexpr int kSegWaves = 4;
-constexpr int kSegB = 32 * kSegWaves;  // keys per workgroup
+static_assert(kSegB == 32 * kSegWaves, "keys per workgroup");
 constexpr int kVtPitch = 40;           // bf16 per transposed V row (32 keys + pad)
 
 // LDS of one segment.
@@ -583,11 +583,6 @@ float logit_c2(const hs2_attn_desc& d) {
 }
 float out_scale(const hs2_attn_desc& d) { return d.dtype == HS2_FP8_E4M3 ? d.v_scale : 1.f; }
 
-int mfma_segments(const hs2_attn_desc& d) {
-  const int sel_max = d.k_top + d.window;
-  return sel_max > 0 ? (sel_max + kSegB - 1) / kSegB : 1;
-}
-
 }  // namespace
 
 hipError_t launch_sparse(const hs2_attn_desc& d, const void* q, const void* k, const void* v,
@@ -647,13 +642,6 @@ hipError_t launch_decode_tail(const hs2_attn_desc& d, const void* q, const void*
         meta, list, select_slices(cap), top_idx, top_cnt, part, ml, nseg);
   launch_combine(dim3(d.n_heads, d.batch), st, part, ml, nseg, d.n_heads, out_scale(d), o, lse);
   return hipGetLastError();
-}
-
-size_t sparse_layers_ws_bytes(const hs2_attn_desc& d, int n_layers) {
-  const size_t nseg = mfma_segments(d);
-  const size_t rows = (size_t)n_layers * d.batch;
-  return align_up(sizeof(float) * rows * nseg * d.n_heads * kHeadDim, 256) +
-         align_up(sizeof(float) * 2 * rows * nseg * d.n_heads, 256);
 }
 
 hipError_t launch_sparse_layers(const hs2_attn_desc& d, int n_layers, const void* q_layers,

@@ -43,8 +43,10 @@ def test_counter_record_is_well_formed():
     rec = json.load(open(path))
     assert rec["workload"] == bench.WORKLOAD
     per = rec["bytes_per_dispatch"]
-    # each scoring pass reads its 256 MiB of K once (no re-reads), give or
-    # take a few percent of other traffic
-    for k in ("score_p1_bf16<false>", "score_p2_bf16<false, false, false>"):
-        assert 256 * MIB <= per[k] <= 1.1 * 256 * MIB
+    # the one-pass scoring kernel reads the 256 MiB of K once and, after its
+    # grid barrier, the blocks it could not keep on chip again (3 of each
+    # wave's 32 blocks at 4,096 keys per workgroup: 9.4 %), give or take a
+    # few percent of other traffic
+    for k in ("score_onepass<false, false, 20>", "score_onepass<false, true, 20>"):
+        assert 256 * MIB * (1 + 3 / 32) <= per[k] <= 1.15 * 256 * MIB
     assert 1.9 <= rec["fetch_scale"] <= 2.1
