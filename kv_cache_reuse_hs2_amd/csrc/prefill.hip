@@ -13,18 +13,21 @@
 // and the tile's queries share one top-k selection (pool [0, P_0 - window + 1)
 // with P_0 the tile's first query) while each keeps its own window.
 //
-// One tiled MFMA core serves the three passes.  A wave owns one query (its
-// heads padded to 32 rows); 16 waves (16 queries) share K blocks of 64 keys
-// staged in LDS with a 272-byte row pitch (conflict-free 16-byte operand
-// reads).  The logit tile uses eight v_mfma_f32_32x32x16_bf16 per 32 keys:
+// One tiled MFMA core serves the scoring passes.  A workgroup owns a block
+// of 16 queries; its 8 waves take two queries each (heads padded to 32
+// rows) and share K blocks of 64 keys staged in LDS by direct-to-LDS loads
+// (rows of 256 bytes, 16-byte chunks XOR-swizzled by row, so that operand
+// reads are conflict-free).  The logit tile uses eight
+// v_mfma_f32_32x32x16_bf16 per 32 keys and query, and each K operand read
+// feeds the MFMAs of both queries:
 //   pf_stats:  K as the A operand: a lane owns one (query, head) row over 16
 //              keys, so row max/sum stay in-lane; per key split, partial
 //              (max, sum) per row.
 //   pf_colsum: Q as the A operand: a lane owns one key over 16 rows; after
-//              p = 2^(x - L) the column sum over the wave's rows is an fp32
-//              sum in the lane plus one add across the two lane halves; the
-//              16 waves are added in a fixed order and written per
-//              (16-query block, key).
+//              p = 2^(x - L) the column sum over the wave's two queries is
+//              an fp32 sum in the lane plus one add across the two lane
+//              halves; the 8 waves are added in a fixed order, kept in LDS
+//              for the split and written per (16-query block, key).
 //   pf_reduce: I_t[j] = sum of the tile's 16-query blocks, in order.
 //   pf_sparse: 8 queries per workgroup; gathered keys (the tile's selection,
 //              then the window band of the block), a statistics pass then a P.V pass on MFMA with V
@@ -87,33 +90,12 @@ __device__ __forceinline__ bf16x8_t k_opnd(const uint8_t* blk, int key, int e, i
 // waits for its own with an explicit vmcnt, and a barrier then publishes the
 // whole block.
 typedef __attribute__((address_space(3))) void lds_void_t;
-constexpr int kRing = 3;                  // blocks in LDS: one in use, two loading
+constexpr int kRing = 3;                  // pf_out: blocks in LDS, one in use, two loading
 constexpr int kSlotB = kBlk * kHeadDim * 2;  // 16 KiB
-
-// 64 rows by 16 waves of a 1024-thread workgroup: wave w moves rows
-// 4w .. 4w+3, lane l the stored chunk l % 16 of row 4w + l / 16.
-template <typename RowOf>
-__device__ __forceinline__ void dma_k_block(uint8_t* slot, const uint16_t* kb, RowOf row_of) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int r = 4 * wave + (lane >> 4);
-  const int c = (lane & 15) ^ (r & 15);
-  __builtin_amdgcn_global_load_lds(kb + (size_t)row_of(r) * kHeadDim + 8 * c,
-                                   (lds_void_t*)(slot + wave * 1024), 16, 0, 0);
-}
 
 __device__ __forceinline__ bf16x8_t k_opnd_ring(const uint8_t* slot, int key, int e, int hh) {
   return as_bf16x8(*reinterpret_cast<const u32x4*>(
       slot + key * (kHeadDim * 2) + 16 * ((2 * e + hh) ^ (key & 15))));
-}
-
-// Wait until this wave has at most `younger` (0 or 1) ring loads in flight and
-// its LDS operations are done, then meet the other waves.
-__device__ __forceinline__ void ring_barrier(bool younger) {
-  if (younger) __builtin_amdgcn_s_waitcnt(1 | (7 << 4));  // vmcnt(1) lgkmcnt(0)
-  else __builtin_amdgcn_s_waitcnt(0 | (7 << 4));          // vmcnt(0) lgkmcnt(0)
-  __builtin_amdgcn_s_barrier();
-  asm volatile("" ::: "memory");
-  __builtin_amdgcn_sched_barrier(0);
 }
 
 struct PfArgs {
@@ -136,98 +118,211 @@ struct PfArgs {
 };
 
 // ---------------------------------------------------------------------------
+// The two scoring passes run 8 waves of two consecutive queries each (a
+// workgroup owns a 16-query block): every K operand read from LDS feeds the
+// MFMAs of both queries, which halves the LDS traffic per FLOP, and the
+// exponentials of one 32-key half are issued between the MFMAs of the next.
+constexpr int kPfWaves = 8;
+constexpr int kPfRing = 3;  // K blocks in LDS: the one in use and two loading
+
+// 64 rows by the 8 waves of a 512-thread workgroup: wave w moves rows
+// 8w .. 8w + 7 in two loads, lane l the stored chunk l % 16 of a row.
+template <typename RowOf>
+__device__ __forceinline__ void dma_block_w8(uint8_t* slot, const uint16_t* base, RowOf row_of) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+#pragma unroll
+  for (int k = 0; k < 2; ++k) {
+    const int r = 8 * wave + 4 * k + (lane >> 4);
+    const int c = (lane & 15) ^ (r & 15);
+    __builtin_amdgcn_global_load_lds(base + (size_t)row_of(r) * kHeadDim + 8 * c,
+                                     (lds_void_t*)(slot + wave * 2048 + k * 1024), 16, 0, 0);
+  }
+}
+
+// Wait until this wave's ring loads of the current block have landed (the
+// younger block's two may still be in flight) and its LDS operations are
+// done, then meet the other waves.  No other global memory operation is
+// outstanding in the loops, so the count covers ring loads only.
+__device__ __forceinline__ void ring_barrier_w8(bool younger) {
+  if (younger) __builtin_amdgcn_s_waitcnt(2 | (7 << 4));  // vmcnt(2) lgkmcnt(0)
+  else __builtin_amdgcn_s_waitcnt(0 | (7 << 4));          // vmcnt(0) lgkmcnt(0)
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+// Per-lane addresses of the lane's eight K operands (steps e) in the first
+// half of a ring slot, as k_opnd_ring computes them for key r32; the second
+// half is 32 rows further.  Formed before the MFMA section (a scheduling
+// barrier keeps their arithmetic out of it).
+__device__ __forceinline__ void k_opnd_ptrs(const uint8_t* slot, int r32, int hh,
+                                            const uint8_t* (&kp)[8]) {
+#pragma unroll
+  for (int e = 0; e < 8; ++e) kp[e] = slot + r32 * (kHeadDim * 2) + 16 * ((2 * e + hh) ^ (r32 & 15));
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+// The logits of one 32-key half (mt) of the K block in a ring slot for the
+// wave's two queries (fp32, unscaled): with K as the A operand (kKA) a lane
+// holds (query, head r32) over 16 keys, with Q as the A operand one key over
+// 16 heads.  `valu(e)` is issued between the MFMAs: the exponentials of the
+// previous half, which then overlap this half's MFMAs.  Without that the
+// per-block workgroup barrier keeps the waves of a SIMD in one phase, all on
+// MFMA and then all on exponentials, and the two pipelines take turns.
+template <bool kKA, typename V>
+__device__ __forceinline__ void half_logits(const uint8_t* const (&kp)[8], int mt,
+                                            const bf16x8_t (&qa)[8], const bf16x8_t (&qb)[8],
+                                            f32x16_t (&acc)[2], V valu) {
+  acc[0] = f32x16_t{};
+  acc[1] = f32x16_t{};
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const bf16x8_t kop =
+        as_bf16x8(*reinterpret_cast<const u32x4*>(kp[e] + mt * 32 * (kHeadDim * 2)));
+    if (kKA) {
+      acc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop, qa[e], acc[0], 0, 0, 0);
+      acc[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop, qb[e], acc[1], 0, 0, 0);
+    } else {
+      acc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[e], kop, acc[0], 0, 0, 0);
+      acc[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qb[e], kop, acc[1], 0, 0, 0);
+    }
+    valu(e);
+  }
+  // Per step: the next step's K operand read, then each MFMA followed by six
+  // VALU operations (fma, exponential and add for two terms), about as long
+  // as the MFMA.  Two MFMAs in a row would stall the wave at the second
+  // (the matrix unit is busy), and its exponentials with it.
+  __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    if (e < 7) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x402, 6, 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x402, 6, 0);
+  }
+}
+
 // Pass 1: partial (max, sum) per (query, head) row over one key split.
-__global__ __launch_bounds__(1024) void pf_stats(PfArgs a) {
+__global__ __launch_bounds__(64 * kPfWaves) void pf_stats(PfArgs a) {
   const int rb = blockIdx.x, s = blockIdx.y, b = blockIdx.z;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int r32 = lane & 31, hh = lane >> 5;
   const int N = clamp_ctx(a.ctx_len, b, a.cap);
-  const int i = rb * 16 + wave;             // this wave's query
-  const int P = N - a.n_q + i;              // its position
+  const int i0 = rb * 16 + 2 * wave;        // this wave's queries i0, i0 + 1
+  const int P0 = N - a.n_q + i0;
   const int P_last = N - a.n_q + rb * 16 + 15;
   const int j0 = s * a.split;
   const int j1 = min(j0 + a.split, P_last + 1);
-  float2* st = a.stats + (((size_t)b * a.nsplit + s) * a.n_q + i) * 32;
+  float2* st = a.stats + (((size_t)b * a.nsplit + s) * a.n_q + i0) * 32;  // two rows of 32
   if (P_last < 0 || j0 >= j1) {
-    if (hh == 0) st[r32] = make_float2(-INFINITY, 0.f);
+    if (hh == 0) {
+      st[r32] = make_float2(-INFINITY, 0.f);
+      st[32 + r32] = make_float2(-INFINITY, 0.f);
+    }
     return;
   }
-  __shared__ __attribute__((aligned(16))) uint8_t ring[kRing * kSlotB];
-  bf16x8_t qr[8];
-  load_q(a.q + ((size_t)b * a.n_q + i) * a.H * kHeadDim, a.H, r32, hh, P >= 0, qr);
+  __shared__ __attribute__((aligned(16))) uint8_t ring[kPfRing * kSlotB];
+  bf16x8_t qa[8], qb[8];
+  const uint16_t* qrow = a.q + ((size_t)b * a.n_q + i0) * a.H * kHeadDim;
+  load_q(qrow, a.H, r32, hh, P0 >= 0, qa);
+  load_q(qrow + a.H * kHeadDim, a.H, r32, hh, P0 + 1 >= 0, qb);
   const uint16_t* kb = a.k + (size_t)b * a.kv_stride;
   const int nblk = (j1 - j0 + kBlk - 1) / kBlk;
   auto rows_of = [&](int bi) { return [=](int r) { return min(j0 + bi * kBlk + r, j1 - 1); }; };
   // Q is in registers before the ring starts, so that no later wait for it
   // has to cover the ring loads.
   __builtin_amdgcn_s_waitcnt(0 | (7 << 4) | (15 << 8));  // vmcnt(0)
-  dma_k_block(ring, kb, rows_of(0));
-  if (nblk > 1) dma_k_block(ring + kSlotB, kb, rows_of(1));
-  float m = -INFINITY, l = 0.f;
-  for (int bi = 0; bi < nblk; ++bi) {
-    // Block bi has landed for every wave; the slot of block bi-1 is free.
-    ring_barrier(bi + 1 < nblk);
-    if (bi + 2 < nblk) dma_k_block(ring + ((bi + 2) % kRing) * kSlotB, kb, rows_of(bi + 2));
-    const uint8_t* kblk = ring + (bi % kRing) * kSlotB;
-    const int kb0 = j0 + bi * kBlk;
-    if (P < kb0) continue;  // the whole block is in this query's future
-    // Every key of the block is inside this query's range and the split:
-    // no masks, and the scale folds into one fma per logit (c2 > 0).
-    const bool full = kb0 + kBlk <= j1 && kb0 + kBlk - 1 <= P;
-    f32x16_t accs[2] = {{}, {}};
+  dma_block_w8(ring, kb, rows_of(0));
+  if (nblk > 1) dma_block_w8(ring + kSlotB, kb, rows_of(1));
+  // acc[q][r]: row (query i0 + q, head r32), key hk0 + 8(r/4) + 4hh + r%4 of
+  // the half starting at hk0.  The running reference m moves only when a
+  // logit exceeds it by more than 64 binades: the half's terms are summed
+  // against the current m while the next half's MFMAs run (each term at
+  // most 2^64, so the sum stays finite and keeps fp32 relative precision);
+  // only a sum above 2^64 (or a first half, or one with masked keys) takes
+  // the exact path below.
+  float m[2] = {-INFINITY, -INFINITY}, l[2] = {0.f, 0.f};
+  auto finish = [&](const f32x16_t (&acc)[2], const float (&lz)[2], int hk0) {
 #pragma unroll
-    for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-      for (int e = 0; e < 8; ++e)
-        accs[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k_opnd_ring(kblk, 32 * mt + r32, e, hh), qr[e], accs[mt], 0, 0, 0);
-#pragma unroll
-    for (int mt = 0; mt < 2; ++mt) {
-      const f32x16_t& acc = accs[mt];
-      // acc[r]: row (query i, head r32), key kb0 + 32mt + 8(r/4) + 4hh + r%4
-      // The running reference m moves only when a logit exceeds it by more
-      // than 64 binades: the block's terms are summed against the current m
-      // (each at most 2^64, so the sum stays finite and keeps fp32 relative
-      // precision), and only a sum above 2^64 (or a first block) takes the
-      // block maximum and rescales.  This saves the 16 max operations per
-      // half on almost every block.
-      float lazy = 0.f;
-      if (full && m != -INFINITY) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) lazy += fast_exp2(fmaf(acc[r], a.c2, -m));
-      }
-      if (full && m != -INFINITY && lazy <= 0x1p64f) {
-        l += lazy;
+    for (int q = 0; q < 2; ++q) {
+      const int P = P0 + q;
+      const bool full = hk0 + 32 <= j1 && hk0 + 31 <= P;
+      if (full && m[q] != -INFINITY && lz[q] <= 0x1p64f) {
+        l[q] += lz[q];
       } else if (full) {
-        float bm = acc[0];
+        float bm = acc[q][0];
 #pragma unroll
-        for (int r = 1; r < 16; ++r) bm = fmaxf(bm, acc[r]);
-        const float mn = fmaxf(m, bm * a.c2);
-        float sum = l * fast_exp2(m - mn);
+        for (int r = 1; r < 16; ++r) bm = fmaxf(bm, acc[q][r]);
+        const float mn = fmaxf(m[q], bm * a.c2);
+        float sum = l[q] * fast_exp2(m[q] - mn);
 #pragma unroll
-        for (int r = 0; r < 16; ++r) sum += fast_exp2(fmaf(acc[r], a.c2, -mn));
-        l = sum;
-        m = mn;
+        for (int r = 0; r < 16; ++r) sum += fast_exp2(fmaf(acc[q][r], a.c2, -mn));
+        l[q] = sum;
+        m[q] = mn;
       } else {
         float x[16];
         float bm = -INFINITY;
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const int j = kb0 + 32 * mt + 8 * (r >> 2) + 4 * hh + (r & 3);
-          x[r] = (j < j1 && j <= P) ? acc[r] * a.c2 : -INFINITY;
+          const int j = hk0 + 8 * (r >> 2) + 4 * hh + (r & 3);
+          x[r] = (j < j1 && j <= P) ? acc[q][r] * a.c2 : -INFINITY;
           bm = fmaxf(bm, x[r]);
         }
-        const float mn = fmaxf(m, bm);
+        const float mn = fmaxf(m[q], bm);
         const float mref = (mn == -INFINITY) ? 0.f : mn;
-        float sum = l * fast_exp2(m - mref);
+        float sum = l[q] * fast_exp2(m[q] - mref);
 #pragma unroll
         for (int r = 0; r < 16; ++r) sum += fast_exp2(x[r] - mref);
-        l = sum;
-        m = mn;
+        l[q] = sum;
+        m[q] = mn;
       }
     }
+  };
+  f32x16_t prev[2] = {{}, {}};
+  int prev_k0 = 0;
+  for (int bi = 0; bi < nblk; ++bi) {
+    // Block bi has landed for every wave; the slot of block bi-1 is free.
+    ring_barrier_w8(bi + 1 < nblk);
+    if (bi + 2 < nblk) dma_block_w8(ring + ((bi + 2) % kPfRing) * kSlotB, kb, rows_of(bi + 2));
+    const uint8_t* kp[8];
+    k_opnd_ptrs(ring + (bi % kPfRing) * kSlotB, r32, hh, kp);
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt) {
+      f32x16_t cur[2];
+      float lz[2] = {0.f, 0.f};
+      half_logits<true>(kp, mt, qa, qb, cur, [&](int e) {
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+          lz[0] += fast_exp2(fmaf(prev[0][2 * e + u], a.c2, -m[0]));
+          lz[1] += fast_exp2(fmaf(prev[1][2 * e + u], a.c2, -m[1]));
+        }
+      });
+      // The sums are needed here, next to the MFMAs (the compiler would
+      // otherwise sink them into the conditional below).
+      asm volatile("" ::"v"(lz[0]), "v"(lz[1]));
+      if (bi > 0 || mt > 0) finish(prev, lz, prev_k0);
+      prev[0] = cur[0];
+      prev[1] = cur[1];
+      prev_k0 = j0 + bi * kBlk + 32 * mt;
+    }
   }
-  merge_ml(m, l, __shfl_xor(m, 32), __shfl_xor(l, 32));
-  if (hh == 0) st[r32] = make_float2(m, l);
+  {
+    float lz[2] = {0.f, 0.f};
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      lz[0] += fast_exp2(fmaf(prev[0][r], a.c2, -m[0]));
+      lz[1] += fast_exp2(fmaf(prev[1][r], a.c2, -m[1]));
+    }
+    finish(prev, lz, prev_k0);
+  }
+  float ma = m[0], la = l[0], mb = m[1], lb = l[1];
+  merge_ml(ma, la, __shfl_xor(ma, 32), __shfl_xor(la, 32));
+  merge_ml(mb, lb, __shfl_xor(mb, 32), __shfl_xor(lb, 32));
+  if (hh == 0) {
+    st[r32] = make_float2(ma, la);
+    st[32 + r32] = make_float2(mb, lb);
+  }
 }
 
 // Fold the split statistics of the workgroup's 16 x 32 rows into L (base 2;
@@ -252,38 +347,50 @@ __device__ void fold_rows(const PfArgs& a, int b, int rb, int N, float* s_L, boo
 }
 
 // Pass 2: per (16-query block, key) column sums of p over the block's rows.
-__global__ __launch_bounds__(1024) void pf_colsum(PfArgs a) {
+__global__ __launch_bounds__(64 * kPfWaves) void pf_colsum(PfArgs a) {
   const int rb = blockIdx.x, s = blockIdx.y, b = blockIdx.z;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int r32 = lane & 31, hh = lane >> 5;
   const int N = clamp_ctx(a.ctx_len, b, a.cap);
-  const int i = rb * 16 + wave;
-  const int P = N - a.n_q + i;
+  const int i0 = rb * 16 + 2 * wave;
+  const int P0 = N - a.n_q + i0, P1 = P0 + 1;
   const int P_last = N - a.n_q + rb * 16 + 15;
   const int j0 = s * a.split;
   const int j1 = min(j0 + a.split, P_last + 1);
   if (P_last < 0 || j0 >= j1) {
     // A block entirely before the cache start sees no key: log-sum-exp -inf.
-    if (P_last < 0 && s == 0 && a.lse_out != nullptr && hh == 0 && r32 < a.H)
-      a.lse_out[((size_t)b * a.n_q + i) * a.H + r32] = -INFINITY;
+    if (P_last < 0 && s == 0 && a.lse_out != nullptr && hh == 0 && r32 < a.H) {
+      a.lse_out[((size_t)b * a.n_q + i0) * a.H + r32] = -INFINITY;
+      a.lse_out[((size_t)b * a.n_q + i0 + 1) * a.H + r32] = -INFINITY;
+    }
     return;
   }
   // One LDS object: with several, the compiler tracks the ring loads per
-  // object and waits for all of them before any read of the ring.
+  // object and waits for all of them before any read of the ring.  The
+  // per-wave column sums rotate over three buffers: a block's second half is
+  // summed after the next block's barrier, and its total is formed after the
+  // barrier after that.  The totals of the split stay in LDS until the end
+  // (no global store inside the loop, whose wait counts only ring loads).
   __shared__ struct __attribute__((aligned(16))) {
-    uint8_t ring[kRing * kSlotB];
+    uint8_t ring[kPfRing * kSlotB];
     float s_L[16 * 32];
-    float s_cs[2][16][kBlk];
+    float s_cs[3][kPfWaves][kBlk];
+    float s_col[kPfSplit];
   } sm;
   uint8_t* ring = sm.ring;
   float* s_L = sm.s_L;
   auto& s_cs = sm.s_cs;
   fold_rows(a, b, rb, N, s_L, s == 0);
-  bf16x8_t qr[8];
-  load_q(a.q + ((size_t)b * a.n_q + i) * a.H * kHeadDim, a.H, r32, hh, P >= 0, qr);
-  float L[16];  // rows (heads) 8(r/4) + 4hh + r%4 of this wave's query
+  bf16x8_t qa[8], qb[8];
+  const uint16_t* qrow = a.q + ((size_t)b * a.n_q + i0) * a.H * kHeadDim;
+  load_q(qrow, a.H, r32, hh, P0 >= 0, qa);
+  load_q(qrow + a.H * kHeadDim, a.H, r32, hh, P1 >= 0, qb);
+  float La[16], Lb[16];  // rows (heads) 8(r/4) + 4hh + r%4 of the two queries
 #pragma unroll
-  for (int r = 0; r < 16; ++r) L[r] = s_L[wave * 32 + 8 * (r >> 2) + 4 * hh + (r & 3)];
+  for (int r = 0; r < 16; ++r) {
+    La[r] = s_L[(2 * wave) * 32 + 8 * (r >> 2) + 4 * hh + (r & 3)];
+    Lb[r] = s_L[(2 * wave + 1) * 32 + 8 * (r >> 2) + 4 * hh + (r & 3)];
+  }
   const uint16_t* kb = a.k + (size_t)b * a.kv_stride;
   float* out = a.colsum + ((size_t)b * (a.n_q / 16) + rb) * a.cap;
   const int nblk = (j1 - j0 + kBlk - 1) / kBlk;
@@ -291,50 +398,70 @@ __global__ __launch_bounds__(1024) void pf_colsum(PfArgs a) {
   // Q is in registers before the ring starts, so that no later wait for it
   // has to cover the ring loads.
   __builtin_amdgcn_s_waitcnt(0 | (7 << 4) | (15 << 8));  // vmcnt(0)
-  dma_k_block(ring, kb, rows_of(0));
-  if (nblk > 1) dma_k_block(ring + kSlotB, kb, rows_of(1));
+  dma_block_w8(ring, kb, rows_of(0));
+  if (nblk > 1) dma_block_w8(ring + kSlotB, kb, rows_of(1));
   auto block_sum = [&](int bj) {
     if (threadIdx.x < kBlk) {
-      const int j = j0 + bj * kBlk + threadIdx.x;
       float sum = 0.f;
 #pragma unroll
-      for (int w = 0; w < 16; ++w) sum += s_cs[bj & 1][w][threadIdx.x];
-      if (j < j1) out[j] = sum;
+      for (int w = 0; w < kPfWaves; ++w) sum += s_cs[bj % 3][w][threadIdx.x];
+      sm.s_col[bj * kBlk + threadIdx.x] = sum;
     }
   };
+  // acc[q][r]: row (query i0 + q, head 8(r/4) + 4hh + r%4), key hk0 + r32 of
+  // the half starting at hk0.  The column sum over the two queries' 32 head
+  // rows: 16 each in this lane, 16 each in lane ^ 32.  Padded heads have
+  // L = +inf, so their p is 0.
+  auto finish = [&](float ca, float cb, int hb, int hmt) {
+    const int j = j0 + hb * kBlk + 32 * hmt + r32;
+    if (!(j < j1 && j <= P0)) ca = 0.f;
+    if (!(j < j1 && j <= P1)) cb = 0.f;
+    float cs = ca + cb;
+    cs += __shfl_xor(cs, 32);
+    if (hh == 0) s_cs[hb % 3][wave][32 * hmt + r32] = cs;
+  };
+  f32x16_t prev[2] = {{}, {}};
   for (int bi = 0; bi < nblk; ++bi) {
-    ring_barrier(bi + 1 < nblk);
-    if (bi + 2 < nblk) dma_k_block(ring + ((bi + 2) % kRing) * kSlotB, kb, rows_of(bi + 2));
-    if (bi > 0) block_sum(bi - 1);
-    const uint8_t* kblk = ring + (bi % kRing) * kSlotB;
-    const int kb0 = j0 + bi * kBlk;
-    const bool full = kb0 + kBlk <= j1 && kb0 + kBlk - 1 <= P;
-    f32x16_t accs[2] = {{}, {}};
-#pragma unroll
-    for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-      for (int e = 0; e < 8; ++e)
-        accs[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qr[e], k_opnd_ring(kblk, 32 * mt + r32, e, hh), accs[mt], 0, 0, 0);
+    ring_barrier_w8(bi + 1 < nblk);
+    if (bi + 2 < nblk) dma_block_w8(ring + ((bi + 2) % kPfRing) * kSlotB, kb, rows_of(bi + 2));
+    if (bi > 1) block_sum(bi - 2);
+    const uint8_t* kp[8];
+    k_opnd_ptrs(ring + (bi % kPfRing) * kSlotB, r32, hh, kp);
 #pragma unroll
     for (int mt = 0; mt < 2; ++mt) {
-      const int j = kb0 + 32 * mt + r32;  // this lane's key
-      const f32x16_t& acc = accs[mt];
-      // acc[r]: row (query i, head 8(r/4) + 4hh + r%4), key j.  The sum over
-      // the query's 32 head rows: 16 in this lane, 16 in lane ^ 32.  Padded
-      // heads have L = +inf, so their p is 0.
-      float cs = 0.f;
+      f32x16_t cur[2];
+      float ca = 0.f, cb = 0.f;
+      half_logits<false>(kp, mt, qa, qb, cur, [&](int e) {
 #pragma unroll
-      for (int r = 0; r < 16; ++r) cs += fast_exp2(fmaf(acc[r], a.c2, -L[r]));
-      if (!full && !(j < j1 && j <= P)) cs = 0.f;
-      cs += __shfl_xor(cs, 32);
-      if (hh == 0) s_cs[bi & 1][wave][32 * mt + r32] = cs;
+        for (int u = 0; u < 2; ++u) {
+          ca += fast_exp2(fmaf(prev[0][2 * e + u], a.c2, -La[2 * e + u]));
+          cb += fast_exp2(fmaf(prev[1][2 * e + u], a.c2, -Lb[2 * e + u]));
+        }
+      });
+      asm volatile("" ::"v"(ca), "v"(cb));  // computed next to the MFMAs
+      if (mt == 1) finish(ca, cb, bi, 0);
+      else if (bi > 0) finish(ca, cb, bi - 1, 1);
+      prev[0] = cur[0];
+      prev[1] = cur[1];
     }
+  }
+  {
+    float ca = 0.f, cb = 0.f;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      ca += fast_exp2(fmaf(prev[0][r], a.c2, -La[r]));
+      cb += fast_exp2(fmaf(prev[1][r], a.c2, -Lb[r]));
+    }
+    finish(ca, cb, nblk - 1, 1);
   }
   __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0)
   __builtin_amdgcn_s_barrier();
   asm volatile("" ::: "memory");
   __builtin_amdgcn_sched_barrier(0);
+  if (nblk > 1) block_sum(nblk - 2);
   block_sum(nblk - 1);
+  __syncthreads();
+  for (int t = threadIdx.x; t < j1 - j0; t += 64 * kPfWaves) out[j0 + t] = sm.s_col[t];
 }
 
 // ---------------------------------------------------------------------------
@@ -351,20 +478,6 @@ __global__ __launch_bounds__(1024) void pf_colsum(PfArgs a) {
 // P^T: O^T += V^T P^T with p as a bf16 high and low part (residual below
 // 2^-17 of p).
 constexpr int kOutWaves = 8;
-
-// 64 rows by the 8 waves of a 512-thread workgroup: wave w moves rows
-// 8w .. 8w + 7 in two loads, lane l the stored chunk l % 16 of a row.
-template <typename RowOf>
-__device__ __forceinline__ void dma_block_w8(uint8_t* slot, const uint16_t* base, RowOf row_of) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-#pragma unroll
-  for (int k = 0; k < 2; ++k) {
-    const int r = 8 * wave + 4 * k + (lane >> 4);
-    const int c = (lane & 15) ^ (r & 15);
-    __builtin_amdgcn_global_load_lds(base + (size_t)row_of(r) * kHeadDim + 8 * c,
-                                     (lds_void_t*)(slot + wave * 2048 + k * 1024), 16, 0, 0);
-  }
-}
 
 __global__ __launch_bounds__(512) void pf_out(PfArgs a, float* __restrict__ o_full) {
   const int b = blockIdx.y;
@@ -706,8 +819,8 @@ hipError_t launch_prefill_scores(const hs2_attn_desc& d, const void* q, const vo
   a.lse_out = lse;
   a.window = d.window;
   const dim3 g(d.n_q / 16, a.nsplit, d.batch);
-  pf_stats<<<g, 1024, 0, st>>>(a);
-  pf_colsum<<<g, 1024, 0, st>>>(a);
+  pf_stats<<<g, 64 * kPfWaves, 0, st>>>(a);
+  pf_colsum<<<g, 64 * kPfWaves, 0, st>>>(a);
   const int tiles = d.n_q / d.tile_q;
   const dim3 gr((cap + 4095) / 4096, tiles, d.batch);
   uint32_t* hist = reinterpret_cast<uint32_t*>(ws + w.hist_off);
@@ -768,3 +881,4 @@ hipError_t launch_prefill_sparse(const hs2_attn_desc& d, const void* q, const vo
 }
 
 }  // namespace hs2
+
