@@ -140,9 +140,9 @@ constexpr int kStage = 8192;      // list entries held in LDS by the final selec
 
 // LDS of the final selection of one row.
 struct FinalLds {
-  uint32_t* h;           // [2048], 16-byte aligned: bits 7..0, then the tie passes
+  uint32_t* h;           // [256], 16-byte aligned: key bits 7..0
   uint32_t* pre;         // [kMaxSlices + 1] slice offsets
-  uint32_t* chunk_wins;  // [kStage / 64]
+  uint32_t* chunk_wins;  // [2 * kStage / 64]: per chunk, candidates above and at the threshold
   uint32_t* scratch;     // [16], 16-byte aligned
   uint32_t* res;         // [6]: three result pairs
   uint2* stage;          // [kStage] the candidate list
@@ -163,31 +163,23 @@ __device__ int final_select_row(int r, const RowGeom& g, int k_top,
   constexpr int kWaves = kThreads / 64;
   constexpr int kBinsPer = kSelBins / kThreads;
   const int t = threadIdx.x;
-  if (g.kk == 0 || g.kk == g.pe) {
-    for (int i = t; i < k_top; i += blockDim.x) {
-      if (out != nullptr) out[i] = i < g.kk ? i : -1;
-      if (win != nullptr && i < g.kk) win[i] = i;
-    }
-    if (win != nullptr) __syncthreads();
-    return g.kk;
-  }
   uint32_t* h = L.h;
   uint32_t* pre = L.pre;
   uint32_t* chunk_wins = L.chunk_wins;
   uint32_t* scratch = L.scratch;
   uint32_t* res_b = L.res;
   uint32_t* res_c = L.res + 2;
-  uint32_t* res = L.res + 4;
   uint2* stage = L.stage;
   const int lane = t & 63, wave = t >> 6;
-  const int ns = (g.pe + kSelSlice - 1) / kSelSlice;
   const uint2* lr = list + (size_t)r * nslices * kSelSlice;
 
-  // Everything that does not depend on another load is fetched at once: the
-  // threshold bin b0 that sel_filter found, the second-level histogram (bins
-  // kBinsPer t .. kBinsPer t + kBinsPer - 1 per thread), the slice counts,
-  // and the head of each slice list this wave will copy first (slices
-  // wave + kWaves u for u < kHeads, entries 0..63).
+  // Everything that does not depend on another load is fetched at once,
+  // before the row geometry (which waits for the sequence length) is used:
+  // the threshold bin b0 that sel_filter found, the second-level histogram
+  // (bins kBinsPer t .. kBinsPer t + kBinsPer - 1 per thread), the first 64
+  // slice counts, and the head of each slice list this wave will copy first
+  // (slices wave + kWaves u for u < kHeads, entries 0..63).  Slices past the
+  // row's pool are in the buffers too; their values are not used.
   const uint32_t* hrow = hist + (size_t)r * kHistRow;
   uint32_t v2[kBinsPer];
 #pragma unroll
@@ -204,15 +196,26 @@ __device__ int final_select_row(int r, const RowGeom& g, int k_top,
 #pragma unroll
   for (int u = 0; u < kHeads; ++u) {
     const int sl = wave + kWaves * u;
-    if (sl < ns) head[u] = lr[(size_t)sl * kSelSlice + lane];
+    if (sl < nslices) head[u] = lr[(size_t)sl * kSelSlice + lane];
   }
+  const uint32_t cnt0 = (wave == 0 && lane < nslices) ? cnt[(size_t)r * nslices + lane] : 0u;
+  if (g.kk == 0 || g.kk == g.pe) {
+    for (int i = t; i < k_top; i += blockDim.x) {
+      if (out != nullptr) out[i] = i < g.kk ? i : -1;
+      if (win != nullptr && i < g.kk) win[i] = i;
+    }
+    if (win != nullptr) __syncthreads();
+    return g.kk;
+  }
+  const int ns = (g.pe + kSelSlice - 1) / kSelSlice;
   for (int i = t; i < 256; i += kThreads) h[i] = 0u;  // key bits 7..0, counted while staging
 
   // Slice offsets: one wave scans the counts 64 at a time.
   if (wave == 0) {
     uint32_t carry = 0;
     for (int c0 = 0; c0 < ns; c0 += 64) {
-      const uint32_t c = (c0 + lane < ns) ? cnt[(size_t)r * nslices + c0 + lane] : 0u;
+      const uint32_t c = (c0 + lane >= ns) ? 0u
+                         : (c0 == 0 ? cnt0 : cnt[(size_t)r * nslices + c0 + lane]);
       uint32_t incl = c;
 #pragma unroll
       for (int off = 1; off < 64; off <<= 1) {
@@ -291,84 +294,81 @@ __device__ int final_select_row(int r, const RowGeom& g, int k_top,
   find_bin_regs(v3, need1, scratch, res_c);
   const uint32_t b2 = res_c[0];
   const uint32_t need2 = need1 - res_c[1];
-  const uint32_t ties = h[b2];
   const uint32_t tau = (top24 << 8) | b2;
   __syncthreads();
 
-  // Among keys equal to tau keep the need2 lowest indices: radix-select the
-  // need2-th smallest index (digits of 11/10/10 bits, searched from the top
-  // on the reversed digit).
-  uint32_t idx_thr = 0xFFFFFFFFu;
-  if (need2 < ties) {
-    uint32_t prefix = 0, need = need2;
-    for (int p = 0; p < 3; ++p) {
-      const int sh = (p == 0) ? 20 : (p == 1 ? 10 : 0);
-      const uint32_t nb = (p == 0) ? 2048u : 1024u;
-      for (int i = t; i < (int)nb; i += blockDim.x) h[i] = 0u;
-      __syncthreads();
-      for (uint32_t e = t; e < total; e += blockDim.x) {
-        const uint2 c = entry(e);
-        if (c.x != tau) continue;
-        // Index bits above this digit must match the digits already fixed.
-        if (p > 0 && (c.y >> (sh + 10)) != prefix) continue;
-        atomicAdd(&h[nb - 1u - ((c.y >> sh) & (nb - 1u))], 1u);
-      }
-      __syncthreads();
-      find_bin_desc(h, nb, need, scratch, res);
-      const uint32_t dgt = nb - 1u - res[0];
-      need -= res[1];
-      prefix = (p == 0) ? dgt : ((prefix << 10) | dgt);
-      __syncthreads();
-    }
-    idx_thr = prefix;
-  }
-
-  // Ordered compaction of the winners.  A staged list is cut into 64-entry
-  // chunks, one lane per entry: a ballot counts each chunk's winners, and a
-  // winner's place is the winners of earlier chunks plus those of lower
-  // lanes.  A list left in global memory goes through one block prefix sum
-  // over runs of consecutive entries.
-  auto wins = [&](uint2 c) { return c.x > tau || (c.x == tau && c.y <= idx_thr); };
+  // Ordered compaction of the winners: every candidate above tau, and of the
+  // candidates equal to tau the need2 first ones, which are those of lowest
+  // index because the list is in index order (slices in order, each in key
+  // order).  A winner's place is the number of winners before it in the
+  // list: those above tau, plus min(need2, candidates equal to tau) before
+  // it.  A staged list is cut into 64-entry chunks, one lane per entry:
+  // ballots count each chunk's candidates above and at tau, one wave scans
+  // the chunk counts, and lanes add the lower lanes of their chunk.  A list
+  // left in global memory goes through two block prefix sums over runs of
+  // consecutive entries.
   uint32_t base;
   if (staged) {
     const int nchunks = (int)((total + 63) / 64);
-    uint64_t mask[kStage / 64 / kWaves];
+    uint32_t* chunk_tau = chunk_wins + kStage / 64;
+    uint64_t mask_a[kStage / 64 / kWaves], mask_t[kStage / 64 / kWaves];
 #pragma unroll
     for (int u = 0; u < kStage / 64 / kWaves; ++u) {
       const int ch = wave + kWaves * u;
       const uint32_t e = 64u * ch + lane;
-      const bool w = ch < nchunks && e < total && wins(stage[e]);
-      mask[u] = __ballot(w);
-      if (ch < nchunks && lane == 0) chunk_wins[ch] = (uint32_t)__popcll(mask[u]);
+      const uint32_t kx = (ch < nchunks && e < total) ? stage[e].x : 0u;
+      const bool valid = ch < nchunks && e < total;
+      mask_a[u] = __ballot(valid && kx > tau);
+      mask_t[u] = __ballot(valid && kx == tau);
+      if (ch < nchunks && lane == 0) {
+        chunk_wins[ch] = (uint32_t)__popcll(mask_a[u]);
+        chunk_tau[ch] = (uint32_t)__popcll(mask_t[u]);
+      }
     }
     __syncthreads();
-    // Winners of the chunks before each chunk: one wave scans the counts in
-    // place (res[0] gets the total; the earlier results there are consumed).
+    // Candidates above and at tau in the chunks before each chunk: one wave
+    // scans both counts in place (res_b gets the totals; the earlier results
+    // there are consumed).
     if (wave == 0) {
-      uint32_t carry = 0;
+      uint32_t carry_a = 0, carry_t = 0;
       for (int c0 = 0; c0 < nchunks; c0 += 64) {
-        const uint32_t c = (c0 + lane < nchunks) ? chunk_wins[c0 + lane] : 0u;
-        uint32_t incl = c;
+        const bool in = c0 + lane < nchunks;
+        const uint32_t ca = in ? chunk_wins[c0 + lane] : 0u;
+        const uint32_t ct = in ? chunk_tau[c0 + lane] : 0u;
+        uint32_t ia = ca, it = ct;
 #pragma unroll
         for (int off = 1; off < 64; off <<= 1) {
-          const uint32_t o = __shfl_up(incl, off);
-          if (lane >= off) incl += o;
+          const uint32_t oa = __shfl_up(ia, off), ot = __shfl_up(it, off);
+          if (lane >= off) {
+            ia += oa;
+            it += ot;
+          }
         }
-        if (c0 + lane < nchunks) chunk_wins[c0 + lane] = carry + incl - c;
-        carry += __shfl(incl, 63);
+        if (in) {
+          chunk_wins[c0 + lane] = carry_a + ia - ca;
+          chunk_tau[c0 + lane] = carry_t + it - ct;
+        }
+        carry_a += __shfl(ia, 63);
+        carry_t += __shfl(it, 63);
       }
-      if (lane == 0) res_b[0] = carry;
+      if (lane == 0) {
+        res_b[0] = carry_a;
+        res_b[1] = carry_t;
+      }
     }
     __syncthreads();
-    base = res_b[0];
+    base = res_b[0] + min(res_b[1], need2);
     const uint64_t lower = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
 #pragma unroll
     for (int u = 0; u < kStage / 64 / kWaves; ++u) {
       const int ch = wave + kWaves * u;
       if (ch >= nchunks) break;
-      const uint32_t before = chunk_wins[ch];
-      if ((mask[u] >> lane) & 1ull) {
-        const uint32_t pos = before + (uint32_t)__popcll(mask[u] & lower);
+      const uint32_t a_before = chunk_wins[ch] + (uint32_t)__popcll(mask_a[u] & lower);
+      const uint32_t t_before = chunk_tau[ch] + (uint32_t)__popcll(mask_t[u] & lower);
+      const bool above = (mask_a[u] >> lane) & 1ull;
+      const bool at = ((mask_t[u] >> lane) & 1ull) && t_before < need2;
+      if (above || at) {
+        const uint32_t pos = a_before + min(t_before, need2);
         if (pos < (uint32_t)k_top) {
           if (out != nullptr) out[pos] = (int32_t)stage[64u * ch + lane].y;
           if (win != nullptr) win[pos] = (int32_t)stage[64u * ch + lane].y;
@@ -378,18 +378,28 @@ __device__ int final_select_row(int r, const RowGeom& g, int k_top,
   } else {
     const uint32_t per = (total + blockDim.x - 1) / blockDim.x;
     const uint32_t e0 = min(total, t * per), e1 = min(total, e0 + per);
-    uint32_t mine = 0;
-    for (uint32_t e = e0; e < e1; ++e) mine += wins(entry(e)) ? 1u : 0u;
-    uint32_t pos = block_prefix_sum(mine, scratch, &base);
+    uint32_t mine_a = 0, mine_t = 0;
+    for (uint32_t e = e0; e < e1; ++e) {
+      const uint32_t kx = entry(e).x;
+      mine_a += kx > tau ? 1u : 0u;
+      mine_t += kx == tau ? 1u : 0u;
+    }
+    uint32_t tot_a, tot_t;
+    uint32_t pa = block_prefix_sum(mine_a, scratch, &tot_a);
+    uint32_t pt = block_prefix_sum(mine_t, scratch, &tot_t);
+    base = tot_a + min(tot_t, need2);
     for (uint32_t e = e0; e < e1; ++e) {
       const uint2 c = entry(e);
-      if (wins(c)) {
+      const bool above = c.x > tau, at = c.x == tau && pt < need2;
+      if (above || at) {
+        const uint32_t pos = pa + min(pt, need2);
         if (pos < (uint32_t)k_top) {
           if (out != nullptr) out[pos] = (int32_t)c.y;
           if (win != nullptr) win[pos] = (int32_t)c.y;
         }
-        ++pos;
       }
+      pa += above ? 1u : 0u;
+      pt += c.x == tau ? 1u : 0u;
     }
   }
   if (out != nullptr)

@@ -154,9 +154,9 @@ __global__ __launch_bounds__(1024) void sel_final(const int32_t* __restrict__ ct
                                                   const uint2* __restrict__ list, int nslices,
                                                   int32_t* __restrict__ top_idx,
                                                   int32_t* __restrict__ top_cnt) {
-  __shared__ __attribute__((aligned(16))) uint32_t h[2048];
+  __shared__ __attribute__((aligned(16))) uint32_t h[256];
   __shared__ uint32_t pre[kMaxSlices + 1];
-  __shared__ uint32_t chunk_wins[kStage / 64];
+  __shared__ uint32_t chunk_wins[2 * kStage / 64];
   __shared__ __attribute__((aligned(16))) uint32_t scratch[16];
   __shared__ uint32_t res[6];
   __shared__ uint2 stage[kStage];

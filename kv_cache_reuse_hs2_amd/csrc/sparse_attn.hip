@@ -349,10 +349,10 @@ constexpr int kTailThreads = 512;
 
 union TailLds {
   struct {
-    uint32_t h[2048];
+    uint32_t h[256];
     uint2 stage[kStage];
     uint32_t pre[kMaxSlices + 1];
-    uint32_t chunk_wins[kStage / 64];
+    uint32_t chunk_wins[2 * kStage / 64];
     uint32_t scratch[16];
     uint32_t res[6];
   } sel;
