@@ -36,6 +36,9 @@ GRAPH_STEPS = 10  # decode steps per captured HIP graph (extras)
 GRAPH_ROUNDS = 3  # rounds over the four caches per captured HIP graph (headline)
 # The headline scoring call's kernel (bf16 K, no selector histogram).
 SCORE_KERNEL = "score_onepass<false, false, 20>"
+# The sources of the headline scoring kernel: its measured traffic is used only
+# while these are unchanged.
+TRAFFIC_SOURCES = ("score_onepass.hip", "score_common.h", "hs2_internal.h", "layout.h")
 MIB = 1 << 20
 
 
@@ -466,8 +469,9 @@ def extra_measurements(steps: int, warmup: int) -> dict:
 
 def measured_traffic(kernels) -> float | None:
     """HBM bytes per launch of `kernels` from the committed counter summary
-    (profiles/<workload>_traffic.json), or None when the kernel sources have
-    changed since those counters were taken."""
+    (profiles/<workload>_traffic.json), or None when the sources the scoring
+    kernel is built from (TRAFFIC_SOURCES) have changed since those counters
+    were taken."""
     import hashlib
 
     path = os.path.join(ROOT, "profiles", f"{WORKLOAD}_traffic.json")
@@ -476,7 +480,7 @@ def measured_traffic(kernels) -> float | None:
     rec = json.load(open(path))
     csrc = os.path.join(ROOT, "kv_cache_reuse_hs2_amd", "csrc")
     h = hashlib.sha256()
-    for name in sorted(os.listdir(csrc)):
+    for name in TRAFFIC_SOURCES:
         h.update(open(os.path.join(csrc, name), "rb").read())
     if h.hexdigest() != rec.get("source_sha256"):
         return None
