@@ -340,7 +340,7 @@ def mfma_calibration(steps: int, warmup: int) -> dict:
 def extra_measurements(steps: int, warmup: int) -> dict:
     """The other shapes of the method, measured the same way (not the headline):
     batched decode at 64k, chunked prefill of 8,192 queries on a 131,072-token
-    cache, and KV Bridging of 1,048,576 hidden states followed by a decode step
+    cache (bf16 and E4M3 K/V), and KV Bridging of 1,048,576 hidden states followed by a decode step
     over the bridged 1M-token cache."""
     import torch
 
@@ -410,6 +410,20 @@ def extra_measurements(steps: int, warmup: int) -> dict:
         "note": "attention FLOPs count the causal QK^T and P.V once each; the output pass "
                 "recomputes QK^T and multiplies P as a bf16 high and low part"}
     del buf, inp, o_full
+    # The same prefill on an E4M3 K/V cache (one scale per cache).
+    w8 = WORKLOADS["prefill_fp8_128k_8k"]
+    inp = make_prefill_inputs(w8)
+    buf = make_buffers(inp, n_heads=w8.n_heads, k_top=w8.k_top, window=w8.window,
+                       sm_scale=w8.sm_scale, dtype="fp8", n_q=w8.n_q, tile_q=w8.tile_q)
+    ms8 = time_events(lambda: run_fused_step(buf), max(2, steps // 10), 2)
+    ms8_s = time_events(lambda: run_scores(buf), max(2, steps // 10), 2)
+    out[w8.name] = {"ms_per_step": round(ms8, 4), "queries_per_s": round(w8.n_q / (ms8 * 1e-3), 1),
+                    "scores_ms": round(ms8_s, 4),
+                    "achieved_TFLOPs": round(alg / (ms8 * 1e-3) / 1e12, 1),
+                    "mfma_bf16_frac": round(alg / (ms8 * 1e-3) / 2.5e15, 4),
+                    "note": "K and V as E4M3 bytes with one fp32 scale each, widened to bf16 "
+                            "(exact) on the way into LDS; same FLOP count as the bf16 prefill"}
+    del buf, inp
     # KV Bridging of 1,048,576 x 2048 hidden states, then decode over the cache.
     w = WORKLOADS["bridge_decode_bf16_1m"]
     g = torch.Generator(device="cuda").manual_seed(w.seed)

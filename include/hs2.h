@@ -98,8 +98,8 @@ typedef enum {
  * K and V are E4M3 bytes with one fp32 scale per cache (desc->k_scale,
  * desc->v_scale; the value of a byte x is scale * e4m3(x)), q stays bf16
  * and the arithmetic is that of the bf16 path (every E4M3 value is exact in
- * bf16).  Decode only (n_q = tile_q = 1; HS2_EUNSUPPORTED otherwise);
- * kv_stride must be a multiple of 16 (HS2_EALIGN otherwise).
+ * bf16).  Decode and chunked prefill; kv_stride must be a multiple of 16
+ * (HS2_EALIGN otherwise).
  */
 typedef enum { HS2_F32 = 0, HS2_BF16 = 1, HS2_FP8_E4M3 = 2 } hs2_dtype;
 
@@ -111,7 +111,7 @@ typedef struct {
   int n_heads;    /* query heads, 1..32, all sharing one K/V head (MQA) */
   int head_dim;   /* must be 128 */
   int tile_q;     /* queries per selection group: 1 (decode), or a multiple of 16 for
-                     bf16 chunked prefill (64 in the benchmarks) */
+                     chunked prefill, bf16 or E4M3 K/V (64 in the benchmarks) */
   int k_top;      /* selected keys per group, 0..2048 (1024 in HySparse2) */
   int window;     /* forced recent-token window, 0..2048 (128 in HySparse2) */
   int causal;     /* must be 1 */

@@ -66,13 +66,25 @@ __device__ __forceinline__ void load_q(const uint16_t* qrow, int H, int r32, int
   }
 }
 
-// Stage 64 K rows (indices from `row_of`) into LDS; each thread moves 16 B.
-template <typename RowOf>
-__device__ __forceinline__ void stage_k(uint8_t* dst, const uint16_t* kb, RowOf row_of) {
-  for (int e = threadIdx.x; e < kBlk * 16; e += blockDim.x) {
-    const int r = e >> 4, c = e & 15;
-    const u32x4 x = *reinterpret_cast<const u32x4*>(kb + (size_t)row_of(r) * kHeadDim + 8 * c);
-    *reinterpret_cast<u32x4*>(dst + r * kRowB + 16 * c) = x;
+// Stage 64 K rows (indices from `row_of`) into LDS as bf16; each thread
+// moves 16 B of a row (E4M3 rows: 16 bytes, widened to 32 B of bf16).
+template <bool kFp8, typename RowOf>
+__device__ __forceinline__ void stage_k(uint8_t* dst, const void* kb, RowOf row_of) {
+  if constexpr (kFp8) {
+    const uint8_t* k8 = static_cast<const uint8_t*>(kb);
+    for (int e = threadIdx.x; e < kBlk * 8; e += blockDim.x) {
+      const int r = e >> 3, c = e & 7;
+      const u32x4 x = *reinterpret_cast<const u32x4*>(k8 + (size_t)row_of(r) * kHeadDim + 16 * c);
+      *reinterpret_cast<u32x4*>(dst + r * kRowB + 32 * c) = e4m3x8_to_bf16x8(x[0], x[1]);
+      *reinterpret_cast<u32x4*>(dst + r * kRowB + 32 * c + 16) = e4m3x8_to_bf16x8(x[2], x[3]);
+    }
+  } else {
+    const uint16_t* k16 = static_cast<const uint16_t*>(kb);
+    for (int e = threadIdx.x; e < kBlk * 16; e += blockDim.x) {
+      const int r = e >> 4, c = e & 15;
+      const u32x4 x = *reinterpret_cast<const u32x4*>(k16 + (size_t)row_of(r) * kHeadDim + 8 * c);
+      *reinterpret_cast<u32x4*>(dst + r * kRowB + 16 * c) = x;
+    }
   }
 }
 
@@ -115,6 +127,7 @@ struct PfArgs {
   int k_top, window;
   float* o;        // [B][n_q][H][D]
   float* lse_sp;   // [B][n_q][H] or null
+  float v_scale;   // scale of the V cache (E4M3), else 1
 };
 
 // ---------------------------------------------------------------------------
@@ -137,6 +150,24 @@ __device__ __forceinline__ void dma_block_w8(uint8_t* slot, const uint16_t* base
     __builtin_amdgcn_global_load_lds(base + (size_t)row_of(r) * kHeadDim + 8 * c,
                                      (lds_void_t*)(slot + wave * 2048 + k * 1024), 16, 0, 0);
   }
+}
+
+// E4M3 caches (one byte per element, 128-byte rows): a block of 64 rows comes
+// through registers instead, thread t of the 512 holding bytes 16(t % 8) ..
+// +15 of row t / 8, and is written widened to bf16 (exact: every E4M3 value
+// is a bf16 value) into the same slot layout as a bf16 block, so that the
+// MFMA code reads both alike.
+template <typename RowOf>
+__device__ __forceinline__ u32x4 load_block_e4m3(const uint8_t* base, RowOf row_of) {
+  const int r = threadIdx.x >> 3, c = threadIdx.x & 7;
+  return *reinterpret_cast<const u32x4*>(base + (size_t)row_of(r) * kHeadDim + 16 * c);
+}
+
+__device__ __forceinline__ void store_block_e4m3(uint8_t* slot, u32x4 x) {
+  const int r = threadIdx.x >> 3, c = threadIdx.x & 7;
+  uint8_t* row = slot + r * (kHeadDim * 2);
+  *reinterpret_cast<u32x4*>(row + 16 * ((2 * c) ^ (r & 15))) = e4m3x8_to_bf16x8(x[0], x[1]);
+  *reinterpret_cast<u32x4*>(row + 16 * ((2 * c + 1) ^ (r & 15))) = e4m3x8_to_bf16x8(x[2], x[3]);
 }
 
 // Wait until this wave's ring loads of the current block have landed (the
@@ -204,6 +235,7 @@ __device__ __forceinline__ void half_logits(const uint8_t* const (&kp)[8], int m
 }
 
 // Pass 1: partial (max, sum) per (query, head) row over one key split.
+template <bool kFp8>
 __global__ __launch_bounds__(64 * kPfWaves) void pf_stats(PfArgs a) {
   const int rb = blockIdx.x, s = blockIdx.y, b = blockIdx.z;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -228,13 +260,20 @@ __global__ __launch_bounds__(64 * kPfWaves) void pf_stats(PfArgs a) {
   load_q(qrow, a.H, r32, hh, P0 >= 0, qa);
   load_q(qrow + a.H * kHeadDim, a.H, r32, hh, P0 + 1 >= 0, qb);
   const uint16_t* kb = a.k + (size_t)b * a.kv_stride;
+  const uint8_t* kb8 = reinterpret_cast<const uint8_t*>(a.k) + (size_t)b * a.kv_stride;
   const int nblk = (j1 - j0 + kBlk - 1) / kBlk;
   auto rows_of = [&](int bi) { return [=](int r) { return min(j0 + bi * kBlk + r, j1 - 1); }; };
   // Q is in registers before the ring starts, so that no later wait for it
   // has to cover the ring loads.
   __builtin_amdgcn_s_waitcnt(0 | (7 << 4) | (15 << 8));  // vmcnt(0)
-  dma_block_w8(ring, kb, rows_of(0));
-  if (nblk > 1) dma_block_w8(ring + kSlotB, kb, rows_of(1));
+  u32x4 pend = {0u, 0u, 0u, 0u};  // E4M3: the rows of the next block, in registers
+  if constexpr (kFp8) {
+    store_block_e4m3(ring, load_block_e4m3(kb8, rows_of(0)));
+    if (nblk > 1) pend = load_block_e4m3(kb8, rows_of(1));
+  } else {
+    dma_block_w8(ring, kb, rows_of(0));
+    if (nblk > 1) dma_block_w8(ring + kSlotB, kb, rows_of(1));
+  }
   // acc[q][r]: row (query i0 + q, head r32), key hk0 + 8(r/4) + 4hh + r%4 of
   // the half starting at hk0.  The running reference m moves only when a
   // logit exceeds it by more than 64 binades: the half's terms are summed
@@ -284,7 +323,14 @@ __global__ __launch_bounds__(64 * kPfWaves) void pf_stats(PfArgs a) {
   for (int bi = 0; bi < nblk; ++bi) {
     // Block bi has landed for every wave; the slot of block bi-1 is free.
     ring_barrier_w8(bi + 1 < nblk);
-    if (bi + 2 < nblk) dma_block_w8(ring + ((bi + 2) % kPfRing) * kSlotB, kb, rows_of(bi + 2));
+    if constexpr (kFp8) {
+      // Block bi+1 goes into the slot of block bi-2 (done before the last
+      // barrier) and is complete in LDS at the next one.
+      if (bi + 1 < nblk) store_block_e4m3(ring + ((bi + 1) % kPfRing) * kSlotB, pend);
+      if (bi + 2 < nblk) pend = load_block_e4m3(kb8, rows_of(bi + 2));
+    } else {
+      if (bi + 2 < nblk) dma_block_w8(ring + ((bi + 2) % kPfRing) * kSlotB, kb, rows_of(bi + 2));
+    }
     const uint8_t* kp[8];
     k_opnd_ptrs(ring + (bi % kPfRing) * kSlotB, r32, hh, kp);
 #pragma unroll
@@ -347,6 +393,7 @@ __device__ void fold_rows(const PfArgs& a, int b, int rb, int N, float* s_L, boo
 }
 
 // Pass 2: per (16-query block, key) column sums of p over the block's rows.
+template <bool kFp8>
 __global__ __launch_bounds__(64 * kPfWaves) void pf_colsum(PfArgs a) {
   const int rb = blockIdx.x, s = blockIdx.y, b = blockIdx.z;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -392,14 +439,21 @@ __global__ __launch_bounds__(64 * kPfWaves) void pf_colsum(PfArgs a) {
     Lb[r] = s_L[(2 * wave + 1) * 32 + 8 * (r >> 2) + 4 * hh + (r & 3)];
   }
   const uint16_t* kb = a.k + (size_t)b * a.kv_stride;
+  const uint8_t* kb8 = reinterpret_cast<const uint8_t*>(a.k) + (size_t)b * a.kv_stride;
   float* out = a.colsum + ((size_t)b * (a.n_q / 16) + rb) * a.cap;
   const int nblk = (j1 - j0 + kBlk - 1) / kBlk;
   auto rows_of = [&](int bi) { return [=](int r) { return min(j0 + bi * kBlk + r, j1 - 1); }; };
   // Q is in registers before the ring starts, so that no later wait for it
   // has to cover the ring loads.
   __builtin_amdgcn_s_waitcnt(0 | (7 << 4) | (15 << 8));  // vmcnt(0)
-  dma_block_w8(ring, kb, rows_of(0));
-  if (nblk > 1) dma_block_w8(ring + kSlotB, kb, rows_of(1));
+  u32x4 pend = {0u, 0u, 0u, 0u};  // E4M3: the rows of the next block, in registers
+  if constexpr (kFp8) {
+    store_block_e4m3(ring, load_block_e4m3(kb8, rows_of(0)));
+    if (nblk > 1) pend = load_block_e4m3(kb8, rows_of(1));
+  } else {
+    dma_block_w8(ring, kb, rows_of(0));
+    if (nblk > 1) dma_block_w8(ring + kSlotB, kb, rows_of(1));
+  }
   auto block_sum = [&](int bj) {
     if (threadIdx.x < kBlk) {
       float sum = 0.f;
@@ -423,7 +477,14 @@ __global__ __launch_bounds__(64 * kPfWaves) void pf_colsum(PfArgs a) {
   f32x16_t prev[2] = {{}, {}};
   for (int bi = 0; bi < nblk; ++bi) {
     ring_barrier_w8(bi + 1 < nblk);
-    if (bi + 2 < nblk) dma_block_w8(ring + ((bi + 2) % kPfRing) * kSlotB, kb, rows_of(bi + 2));
+    if constexpr (kFp8) {
+      // Block bi+1 goes into the slot of block bi-2 (done before the last
+      // barrier) and is complete in LDS at the next one.
+      if (bi + 1 < nblk) store_block_e4m3(ring + ((bi + 1) % kPfRing) * kSlotB, pend);
+      if (bi + 2 < nblk) pend = load_block_e4m3(kb8, rows_of(bi + 2));
+    } else {
+      if (bi + 2 < nblk) dma_block_w8(ring + ((bi + 2) % kPfRing) * kSlotB, kb, rows_of(bi + 2));
+    }
     if (bi > 1) block_sum(bi - 2);
     const uint8_t* kp[8];
     k_opnd_ptrs(ring + (bi % kPfRing) * kSlotB, r32, hh, kp);
@@ -479,6 +540,7 @@ __global__ __launch_bounds__(64 * kPfWaves) void pf_colsum(PfArgs a) {
 // 2^-17 of p).
 constexpr int kOutWaves = 8;
 
+template <bool kFp8>
 __global__ __launch_bounds__(512) void pf_out(PfArgs a, float* __restrict__ o_full) {
   const int b = blockIdx.y;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -503,15 +565,31 @@ __global__ __launch_bounds__(512) void pf_out(PfArgs a, float* __restrict__ o_fu
     const int j1 = P_last + 1;
     const uint16_t* kb = a.k + (size_t)b * a.kv_stride;
     const uint16_t* vb = a.v + (size_t)b * a.kv_stride;
+    const uint8_t* kb8 = reinterpret_cast<const uint8_t*>(a.k) + (size_t)b * a.kv_stride;
+    const uint8_t* vb8 = reinterpret_cast<const uint8_t*>(a.v) + (size_t)b * a.kv_stride;
     const int nblk = (j1 + kBlk - 1) / kBlk;
     auto issue = [&](int bi) {
       auto rows = [=](int r) { return min(bi * kBlk + r, j1 - 1); };
       dma_block_w8(sm.ring[bi % kRing][0], kb, rows);
       dma_block_w8(sm.ring[bi % kRing][1], vb, rows);
     };
+    // E4M3: the K and V rows of the next block, in registers.
+    u32x4 pk = {0u, 0u, 0u, 0u}, pv = {0u, 0u, 0u, 0u};
+    auto load8 = [&](int bi) {
+      auto rows = [=](int r) { return min(bi * kBlk + r, j1 - 1); };
+      pk = load_block_e4m3(kb8, rows);
+      pv = load_block_e4m3(vb8, rows);
+    };
     __builtin_amdgcn_s_waitcnt(0 | (7 << 4));  // vmcnt(0) lgkmcnt(0): Q
-    issue(0);
-    if (nblk > 1) issue(1);
+    if constexpr (kFp8) {
+      load8(0);
+      store_block_e4m3(sm.ring[0][0], pk);
+      store_block_e4m3(sm.ring[0][1], pv);
+      if (nblk > 1) load8(1);
+    } else {
+      issue(0);
+      if (nblk > 1) issue(1);
+    }
     for (int bi = 0; bi < nblk; ++bi) {
       // Block bi (four loads per wave) has landed for every wave once the
       // younger block's four are all that is in flight; the slot of block
@@ -523,7 +601,17 @@ __global__ __launch_bounds__(512) void pf_out(PfArgs a, float* __restrict__ o_fu
       __builtin_amdgcn_s_barrier();
       asm volatile("" ::: "memory");
       __builtin_amdgcn_sched_barrier(0);
-      if (bi + 2 < nblk) issue(bi + 2);
+      if constexpr (kFp8) {
+        // Block bi+1 goes into the slot of block bi-2, done before the last
+        // barrier; the barrier after the V transpose publishes it.
+        if (bi + 1 < nblk) {
+          store_block_e4m3(sm.ring[(bi + 1) % kRing][0], pk);
+          store_block_e4m3(sm.ring[(bi + 1) % kRing][1], pv);
+        }
+        if (bi + 2 < nblk) load8(bi + 2);
+      } else {
+        if (bi + 2 < nblk) issue(bi + 2);
+      }
       const uint8_t* ks = sm.ring[bi % kRing][0];
       const uint8_t* vs = sm.ring[bi % kRing][1];
       // Key `lane` goes to column vpos (bits 2 and 3 swapped), so that the
@@ -597,7 +685,8 @@ __global__ __launch_bounds__(512) void pf_out(PfArgs a, float* __restrict__ o_fu
 #pragma unroll
       for (int g = 0; g < 4; ++g)
         *reinterpret_cast<f32x4*>(orow + 32 * t + 8 * g + 4 * hh) =
-            f32x4{o[t][4 * g], o[t][4 * g + 1], o[t][4 * g + 2], o[t][4 * g + 3]};
+            f32x4{o[t][4 * g] * a.v_scale, o[t][4 * g + 1] * a.v_scale,
+                  o[t][4 * g + 2] * a.v_scale, o[t][4 * g + 3] * a.v_scale};
   }
 }
 
@@ -645,6 +734,7 @@ __global__ __launch_bounds__(256) void pf_hist_init(uint32_t* hist) {
 // block's window band: S_i = T_t ++ [max(0, P_i - W + 1), P_i].
 constexpr int kSpWaves = 8;  // queries per workgroup of the sparse pass
 
+template <bool kFp8>
 __global__ __launch_bounds__(64 * kSpWaves) void pf_sparse(PfArgs a) {
   const int rb = blockIdx.x, b = blockIdx.y;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -683,8 +773,11 @@ __global__ __launch_bounds__(64 * kSpWaves) void pf_sparse(PfArgs a) {
   __shared__ int s_key[kBlk];
   bf16x8_t qr[8];
   load_q(a.q + ((size_t)b * a.n_q + i) * a.H * kHeadDim, a.H, r32, hh, P >= 0, qr);
-  const uint16_t* kb = a.k + (size_t)b * a.kv_stride;
+  const void* kb = kFp8 ? static_cast<const void*>(reinterpret_cast<const uint8_t*>(a.k) +
+                                                   (size_t)b * a.kv_stride)
+                        : static_cast<const void*>(a.k + (size_t)b * a.kv_stride);
   const uint16_t* vb = a.v + (size_t)b * a.kv_stride;
+  const uint8_t* vb8 = reinterpret_cast<const uint8_t*>(a.v) + (size_t)b * a.kv_stride;
 
   // Pass A: row statistics over the list.
   float m = -INFINITY, l = 0.f;
@@ -692,7 +785,7 @@ __global__ __launch_bounds__(64 * kSpWaves) void pf_sparse(PfArgs a) {
     __syncthreads();
     if (threadIdx.x < kBlk) s_key[threadIdx.x] = key_of(min(p0 + (int)threadIdx.x, total - 1));
     __syncthreads();
-    stage_k(kblk, kb, [&](int r) { return s_key[r]; });
+    stage_k<kFp8>(kblk, kb, [&](int r) { return s_key[r]; });
     __syncthreads();
 #pragma unroll
     for (int mt = 0; mt < 2; ++mt) {
@@ -726,15 +819,30 @@ __global__ __launch_bounds__(64 * kSpWaves) void pf_sparse(PfArgs a) {
     __syncthreads();
     if (threadIdx.x < kBlk) s_key[threadIdx.x] = key_of(min(p0 + (int)threadIdx.x, total - 1));
     __syncthreads();
-    stage_k(kblk, kb, [&](int r) { return s_key[r]; });
-    // V block transposed: vt[d][key].
-    for (int e = threadIdx.x; e < kBlk * 16; e += blockDim.x) {
-      const int r = e >> 4, c = e & 15;
-      const u32x4 x = *reinterpret_cast<const u32x4*>(vb + (size_t)s_key[r] * kHeadDim + 8 * c);
+    stage_k<kFp8>(kblk, kb, [&](int r) { return s_key[r]; });
+    // V block transposed: vt[d][key] (E4M3 rows widened to bf16).
+    if constexpr (kFp8) {
+      for (int e = threadIdx.x; e < kBlk * 8; e += blockDim.x) {
+        const int r = e >> 3, c = e & 7;
+        const u32x4 x8 = *reinterpret_cast<const u32x4*>(vb8 + (size_t)s_key[r] * kHeadDim + 16 * c);
+        const u32x4 xs[2] = {e4m3x8_to_bf16x8(x8[0], x8[1]), e4m3x8_to_bf16x8(x8[2], x8[3])};
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        vt[8 * c + 2 * u][r] = (uint16_t)(x[u] & 0xFFFFu);
-        vt[8 * c + 2 * u + 1][r] = (uint16_t)(x[u] >> 16);
+        for (int hf = 0; hf < 2; ++hf)
+#pragma unroll
+          for (int u = 0; u < 4; ++u) {
+            vt[16 * c + 8 * hf + 2 * u][r] = (uint16_t)(xs[hf][u] & 0xFFFFu);
+            vt[16 * c + 8 * hf + 2 * u + 1][r] = (uint16_t)(xs[hf][u] >> 16);
+          }
+      }
+    } else {
+      for (int e = threadIdx.x; e < kBlk * 16; e += blockDim.x) {
+        const int r = e >> 4, c = e & 15;
+        const u32x4 x = *reinterpret_cast<const u32x4*>(vb + (size_t)s_key[r] * kHeadDim + 8 * c);
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          vt[8 * c + 2 * u][r] = (uint16_t)(x[u] & 0xFFFFu);
+          vt[8 * c + 2 * u + 1][r] = (uint16_t)(x[u] >> 16);
+        }
       }
     }
     __syncthreads();
@@ -784,7 +892,8 @@ __global__ __launch_bounds__(64 * kSpWaves) void pf_sparse(PfArgs a) {
       const int h = 8 * (r >> 2) + 4 * hh + (r & 3);
       if (h < a.H)
 #pragma unroll
-        for (int dt = 0; dt < 4; ++dt) orow[(size_t)h * kHeadDim + 32 * dt + r32] = o[dt][r];
+        for (int dt = 0; dt < 4; ++dt)
+          orow[(size_t)h * kHeadDim + 32 * dt + r32] = o[dt][r] * a.v_scale;
     }
     if (a.lse_sp != nullptr && hh == 0 && r32 < a.H)
       a.lse_sp[((size_t)b * a.n_q + i) * a.H + r32] = (l > 0.f) ? (m + log2f(l)) * kLn2 : -INFINITY;
@@ -792,6 +901,15 @@ __global__ __launch_bounds__(64 * kSpWaves) void pf_sparse(PfArgs a) {
 }
 
 }  // namespace
+
+// Logits in base 2 (sm_scale log2(e), times the K cache's scale for E4M3)
+// and the factor of the outputs (the V cache's scale for E4M3).
+static float logit_scale(const hs2_attn_desc& d) {
+  return d.sm_scale * 1.4426950408889634f * (d.dtype == HS2_FP8_E4M3 ? d.k_scale : 1.f);
+}
+static float value_scale(const hs2_attn_desc& d) {
+  return d.dtype == HS2_FP8_E4M3 ? d.v_scale : 1.f;
+}
 
 // Workspace of the prefill scoring (inside the scoring region):
 //   stats  float2 [B][nsplit][n_q][32]
@@ -813,14 +931,19 @@ hipError_t launch_prefill_scores(const hs2_attn_desc& d, const void* q, const vo
   a.tile_q = d.tile_q;
   a.split = kPfSplit;
   a.nsplit = (cap + kPfSplit - 1) / kPfSplit;
-  a.c2 = d.sm_scale * 1.4426950408889634f;
+  a.c2 = logit_scale(d);
   a.stats = reinterpret_cast<float2*>(ws + w.stats_off);
   a.colsum = reinterpret_cast<float*>(ws + w.colsum_off);
   a.lse_out = lse;
   a.window = d.window;
   const dim3 g(d.n_q / 16, a.nsplit, d.batch);
-  pf_stats<<<g, 64 * kPfWaves, 0, st>>>(a);
-  pf_colsum<<<g, 64 * kPfWaves, 0, st>>>(a);
+  if (d.dtype == HS2_FP8_E4M3) {
+    pf_stats<true><<<g, 64 * kPfWaves, 0, st>>>(a);
+    pf_colsum<true><<<g, 64 * kPfWaves, 0, st>>>(a);
+  } else {
+    pf_stats<false><<<g, 64 * kPfWaves, 0, st>>>(a);
+    pf_colsum<false><<<g, 64 * kPfWaves, 0, st>>>(a);
+  }
   const int tiles = d.n_q / d.tile_q;
   const dim3 gr((cap + 4095) / 4096, tiles, d.batch);
   uint32_t* hist = reinterpret_cast<uint32_t*>(ws + w.hist_off);
@@ -849,9 +972,13 @@ hipError_t launch_prefill_out(const hs2_attn_desc& d, const void* q, const void*
   a.tile_q = d.tile_q;
   a.split = kPfSplit;
   a.nsplit = (cap + kPfSplit - 1) / kPfSplit;
-  a.c2 = d.sm_scale * 1.4426950408889634f;
+  a.c2 = logit_scale(d);
+  a.v_scale = value_scale(d);
   a.stats = reinterpret_cast<float2*>(ws + w.stats_off);
-  pf_out<<<dim3(d.n_q / kOutWaves, d.batch), 512, 0, st>>>(a, o_full);
+  if (d.dtype == HS2_FP8_E4M3)
+    pf_out<true><<<dim3(d.n_q / kOutWaves, d.batch), 512, 0, st>>>(a, o_full);
+  else
+    pf_out<false><<<dim3(d.n_q / kOutWaves, d.batch), 512, 0, st>>>(a, o_full);
   return hipGetLastError();
 }
 
@@ -869,14 +996,18 @@ hipError_t launch_prefill_sparse(const hs2_attn_desc& d, const void* q, const vo
   a.n_q = d.n_q;
   a.H = d.n_heads;
   a.tile_q = d.tile_q;
-  a.c2 = d.sm_scale * 1.4426950408889634f;
+  a.c2 = logit_scale(d);
+  a.v_scale = value_scale(d);
   a.top_idx = top_idx;
   a.top_cnt = top_cnt;
   a.k_top = d.k_top;
   a.window = d.window;
   a.o = o;
   a.lse_sp = lse;
-  pf_sparse<<<dim3(d.n_q / kSpWaves, d.batch), 64 * kSpWaves, 0, st>>>(a);
+  if (d.dtype == HS2_FP8_E4M3)
+    pf_sparse<true><<<dim3(d.n_q / kSpWaves, d.batch), 64 * kSpWaves, 0, st>>>(a);
+  else
+    pf_sparse<false><<<dim3(d.n_q / kSpWaves, d.batch), 64 * kSpWaves, 0, st>>>(a);
   return hipGetLastError();
 }
 

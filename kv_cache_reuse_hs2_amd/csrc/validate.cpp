@@ -84,10 +84,11 @@ hs2_status check_desc(const hs2_attn_desc* d) {
   if (d->k_top > kMaxTop || d->window > kMaxWindow) return HS2_EUNSUPPORTED;
   if (d->causal != 1) return HS2_EUNSUPPORTED;
   if ((int64_t)d->batch * d->n_q > kMaxQueryRows) return HS2_EUNSUPPORTED;
-  // Decode: one query per sequence.  Chunked prefill: bf16, query tiles of a
-  // multiple of 16 queries (the kernels work on blocks of 16 queries).
+  // Decode: one query per sequence.  Chunked prefill: bf16 or E4M3 K/V,
+  // query tiles of a multiple of 16 queries (the kernels work on blocks of
+  // 16 queries).
   const bool decode = d->n_q == 1 && d->tile_q == 1;
-  const bool prefill = d->tile_q > 1 && d->tile_q % 16 == 0 && dt == HS2_BF16;
+  const bool prefill = d->tile_q > 1 && d->tile_q % 16 == 0 && (dt == HS2_BF16 || dt == HS2_FP8_E4M3);
   if (!decode && !prefill) return HS2_EUNSUPPORTED;
   return HS2_OK;
 }

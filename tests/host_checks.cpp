@@ -95,7 +95,8 @@ void desc_cases() {
       {"prefill tile 8", [](hs2_attn_desc* d) { d->n_q = 8; d->tile_q = 8; }, HS2_EUNSUPPORTED},
       {"prefill n_q % tile", [](hs2_attn_desc* d) { d->n_q = 100; d->tile_q = 64; }, HS2_EINVAL},
       {"prefill f32", [](hs2_attn_desc* d) { d->n_q = 64; d->tile_q = 64; set_dtype(d, HS2_F32); }, HS2_EUNSUPPORTED},
-      {"prefill fp8", [](hs2_attn_desc* d) { d->n_q = 64; d->tile_q = 64; set_dtype(d, HS2_FP8_E4M3); }, HS2_EUNSUPPORTED},
+      {"prefill fp8", [](hs2_attn_desc* d) { d->n_q = 64; d->tile_q = 64; set_dtype(d, HS2_FP8_E4M3); }, HS2_OK},
+      {"prefill fp8 bad scale", [](hs2_attn_desc* d) { d->n_q = 64; d->tile_q = 64; set_dtype(d, HS2_FP8_E4M3); d->k_scale = 0.f; }, HS2_EINVAL},
       {"prefill rows 2^24", [](hs2_attn_desc* d) { d->batch = 1 << 11; d->n_q = 1 << 13; d->tile_q = 64; }, HS2_OK},
       {"prefill rows 2^25", [](hs2_attn_desc* d) { d->batch = 1 << 12; d->n_q = 1 << 13; d->tile_q = 64; }, HS2_EUNSUPPORTED},
       {"prefill n_q INT_MAX/64*64", [](hs2_attn_desc* d) { d->n_q = INT_MAX / 64 * 64; d->tile_q = 64; }, HS2_EUNSUPPORTED},

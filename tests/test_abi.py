@@ -255,9 +255,10 @@ def test_fp8_descriptor_validation(lib):
         assert _scores(_desc(**dict(fp8, v_scale=bad))) == hs2.HS2_EINVAL
     # scales are ignored for the other storage types
     assert hs2.hs2_workspace_size(_desc(k_scale=0.0, v_scale=float("nan")), 4096) > 0
-    # decode only
-    assert _scores(_desc(n_q=64, tile_q=64, **fp8)) == hs2.HS2_EUNSUPPORTED
+    # decode and chunked prefill (tiles of a multiple of 16 queries)
+    assert hs2.hs2_workspace_size(_desc(n_q=64, tile_q=64, **fp8), 4096) > 0
     assert _scores(_desc(n_q=2, tile_q=1, **fp8)) == hs2.HS2_EUNSUPPORTED
+    assert _scores(_desc(n_q=8, tile_q=8, **fp8)) == hs2.HS2_EUNSUPPORTED
     # rows of 128 bytes stay 16-byte aligned only with a stride multiple of 16
     assert _scores(d, stride=4096 * 128 + 8) == hs2.HS2_EALIGN
     # (bf16 accepts that stride: the call gets as far as the workspace check)

@@ -37,7 +37,7 @@ class Workload:
         return dataclasses.replace(self, **kw)
 
 
-# The five measured shapes.  Sizes follow the contexts the pages use (32k
+# The measured shapes.  Sizes follow the contexts the pages use (32k
 # pretraining, 256k post-training, 1M in the cost analysis) and the 1,024 +
 # 128 selection budget.
 WORKLOADS = {
@@ -57,6 +57,10 @@ WORKLOADS = {
         "decode_bf16_256k_b4", "decode", batch=4, n_heads=32, head_dim=128,
         ctx_len=262144, n_q=1, tile_q=1, k_top=1024, window=128, dtype="bf16",
         seed=1004, recipe="clusters"),
+    "prefill_fp8_128k_8k": Workload(
+        "prefill_fp8_128k_8k", "prefill", batch=1, n_heads=32, head_dim=128,
+        ctx_len=131072 + 8192, n_q=8192, tile_q=64, k_top=1024, window=128,
+        dtype="fp8", seed=1007, recipe="plain"),
     "decode_fp8_256k_b4": Workload(
         "decode_fp8_256k_b4", "decode", batch=4, n_heads=32, head_dim=128,
         ctx_len=262144, n_q=1, tile_q=1, k_top=1024, window=128, dtype="fp8",
