@@ -198,7 +198,12 @@ __device__ int final_select_row(int r, const RowGeom& g, int k_top,
     const int sl = wave + kWaves * u;
     if (sl < nslices) head[u] = lr[(size_t)sl * kSelSlice + lane];
   }
-  const uint32_t cnt0 = (wave == 0 && lane < nslices) ? cnt[(size_t)r * nslices + lane] : 0u;
+  // Wave 0's slice counts, 64 per chunk, for every chunk the buffers hold.
+  constexpr int kCntChunks = kMaxSlices / 64;
+  uint32_t cntv[kCntChunks];
+#pragma unroll
+  for (int c = 0; c < kCntChunks; ++c)
+    cntv[c] = (wave == 0 && 64 * c + lane < nslices) ? cnt[(size_t)r * nslices + 64 * c + lane] : 0u;
   if (g.kk == 0 || g.kk == g.pe) {
     for (int i = t; i < k_top; i += blockDim.x) {
       if (out != nullptr) out[i] = i < g.kk ? i : -1;
@@ -213,9 +218,11 @@ __device__ int final_select_row(int r, const RowGeom& g, int k_top,
   // Slice offsets: one wave scans the counts 64 at a time.
   if (wave == 0) {
     uint32_t carry = 0;
-    for (int c0 = 0; c0 < ns; c0 += 64) {
-      const uint32_t c = (c0 + lane >= ns) ? 0u
-                         : (c0 == 0 ? cnt0 : cnt[(size_t)r * nslices + c0 + lane]);
+#pragma unroll
+    for (int ci = 0; ci < kCntChunks; ++ci) {
+      const int c0 = 64 * ci;
+      if (c0 >= ns) break;
+      const uint32_t c = (c0 + lane >= ns) ? 0u : cntv[ci];
       uint32_t incl = c;
 #pragma unroll
       for (int off = 1; off < 64; off <<= 1) {
@@ -256,21 +263,42 @@ __device__ int final_select_row(int r, const RowGeom& g, int k_top,
     if ((e.x >> 8) == top24) atomicAdd(&h[e.x & 0xFFu], 1u);
   };
   if (staged) {
-    for (int sl0 = wave; sl0 < ns; sl0 += kHeads * kWaves) {
-      uint2 e[kHeads];
-      uint32_t n[kHeads];
+    // Slices wave + kWaves u (u < kHeads): their first 64 entries come from
+    // the heads loaded above, any further ones (rare) by direct loads.
 #pragma unroll
-      for (int u = 0; u < kHeads; ++u) {
-        const int sl = sl0 + kWaves * u;
-        n[u] = sl < ns ? pre[sl + 1] - pre[sl] : 0u;
-        if (sl0 == wave) e[u] = head[u];
-        else if ((uint32_t)lane < n[u]) e[u] = lr[(size_t)sl * kSelSlice + lane];
+    for (int u = 0; u < kHeads; ++u) {
+      const int sl = wave + kWaves * u;
+      if (sl >= ns) break;
+      const uint32_t n = pre[sl + 1] - pre[sl];
+      if ((uint32_t)lane < n) put(pre[sl] + lane, head[u]);
+      for (uint32_t i = 64 + lane; i < n; i += 64) put(pre[sl] + i, lr[(size_t)sl * kSelSlice + i]);
+    }
+    // The slices after those (pools above kHeads kWaves slices): every entry
+    // by its list position, the loads of all of a thread's entries issued
+    // before any is stored; an entry's slice is found by binary search over
+    // the slice offsets.
+    constexpr int kFirst = kHeads * kWaves;
+    if (ns > kFirst) {
+      constexpr int kPerT = kStage / kThreads;
+      const uint32_t p0 = pre[kFirst];
+      uint2 e[kPerT];
+#pragma unroll
+      for (int k = 0; k < kPerT; ++k) {
+        const uint32_t i = p0 + t + (uint32_t)(k * kThreads);
+        if (i < total) {
+          int lo = kFirst, hi = ns - 1;  // last slice with pre[s] <= i
+          while (lo < hi) {
+            const int mid = (lo + hi + 1) >> 1;
+            if (pre[mid] <= i) lo = mid;
+            else hi = mid - 1;
+          }
+          e[k] = lr[(size_t)lo * kSelSlice + (i - pre[lo])];
+        }
       }
 #pragma unroll
-      for (int u = 0; u < kHeads; ++u) {
-        const int sl = sl0 + kWaves * u;
-        if ((uint32_t)lane < n[u]) put(pre[sl] + lane, e[u]);
-        for (uint32_t i = 64 + lane; i < n[u]; i += 64) put(pre[sl] + i, lr[(size_t)sl * kSelSlice + i]);
+      for (int k = 0; k < kPerT; ++k) {
+        const uint32_t i = p0 + t + (uint32_t)(k * kThreads);
+        if (i < total) put(i, e[k]);
       }
     }
   } else {
