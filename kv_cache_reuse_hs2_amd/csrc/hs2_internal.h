@@ -39,6 +39,17 @@ __device__ __forceinline__ int clamp_ctx(const int32_t* ctx_len, int b, int cap)
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// Sums over the two halves of a wave for two values at once, on the VALU
+// (v_permlane32_swap exchanges the upper half of its first operand with the
+// lower half of its second) rather than through the LDS crossbar: lane l < 32
+// gets a[l] + a[l + 32], lane l >= 32 gets b[l - 32] + b[l].  Each sum adds the
+// lower half's value to the upper half's, as a single-value reduction would.
+__device__ __forceinline__ float half_sums2(float a, float b) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(a), __float_as_uint(b), false,
+                                                  false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 // Orders one wave's LDS writes before its later LDS reads by other lanes (and
 // those reads before later writes).  The hardware keeps a wave's LDS accesses
 // in order; the fences only stop the compiler from moving them.

@@ -13,17 +13,23 @@
 // once:
 //
 //   phase 1  each workgroup (one per CU, four waves, one per SIMD with 512
-//            registers each) streams its chunk of the sequence's keys,
-//            computes the 32 x 32 logit tile of every 32-key block on
+//            registers each) streams its share of the sequence's 32-key
+//            blocks, computes the 32 x 32 logit tile of every block on
 //            v_mfma_f32_32x32x16_bf16 and folds it into per-head (max, sum);
-//            the tiles of the chunk's last blocks stay on chip, kRegBlocks
-//            per wave in registers and kLdsBlocks per wave in LDS;
+//            the tiles of its last blocks stay on chip, kRegBlocks per wave
+//            in registers and kLdsBlocks per wave in LDS;
 //   barrier  the workgroup writes its per-head statistics, then waits until
 //            every workgroup of its sequence has written theirs;
 //   phase 2  it folds the sequence's statistics into L_h, turns the kept tiles
-//            into I[j] without touching HBM, re-reads only the keys of its
-//            chunk that did not fit, and (in the fused decode step) adds the
-//            pool scores to the selector's first histogram.
+//            into I[j] without touching HBM, re-reads only its blocks that
+//            did not fit, and (in the fused decode step) adds the pool
+//            scores to the selector's first histogram.
+//
+// Workgroup c of a sequence with nwg workgroups takes blocks c, c + nwg,
+// c + 2 nwg, ... (its four waves in turn), so that at any moment the
+// workgroups of a sequence read neighbouring blocks rather than 1 MiB apart;
+// measured, this narrows the spread of their finishing times, which the
+// barrier turns into waiting.
 //
 // The barrier is a generation count per sequence in the workspace: at entry a
 // workgroup reads the sequence's generation g, after its statistics it sets its
@@ -139,9 +145,7 @@ score_onepass(const uint16_t* __restrict__ q, const void* __restrict__ k, int64_
   __shared__ __attribute__((aligned(16))) OpLds S;
   const int b = blockIdx.x / nwg, c = blockIdx.x - b * nwg;
   const int N = clamp_ctx(ctx_len, b, cap);
-  const int j_begin = c * chunk;
-  const int j_end = min(N, j_begin + chunk);
-  const bool any = j_begin < j_end;  // workgroup-uniform
+  const bool any = 32 * c < N;  // workgroup-uniform: its first block holds keys
   const int nbw = chunk / (32 * kOpWaves);  // blocks per wave
   const int nR = nbw - kRegBlocks;          // blocks before the register-kept ones
   const int nS = nR - kLdsBlocks;           // blocks kept nowhere (read again in phase 2)
@@ -166,11 +170,12 @@ score_onepass(const uint16_t* __restrict__ q, const void* __restrict__ k, int64_
   const char* kb = static_cast<const char*>(k) + (size_t)b * kv_stride * kv_elem_bytes<kFp8>();
   bf16x8_t qreg[8];
   load_q_bf16<kFp8>(q + (size_t)b * H * kHeadDim, H, r32, hh, qreg);
-  // Key rows of local block i of this wave (clamped into the context, so every
-  // load is in bounds; blocks outside [j_begin, j_end) are never folded).
-  auto jb_of = [&](int i) { return j_begin + 32 * (i * kOpWaves + wave); };
+  // First key of local block i of this wave, and the key row lane r32 loads
+  // (clamped into the context, so every load is in bounds; keys at or past N
+  // are never folded or stored).
+  auto jb_of = [&](int i) { return 32 * ((i * kOpWaves + wave) * nwg + c); };
   auto row_of = [&](int i) { return min(max(jb_of(i) + r32, 0), N - 1); };
-  auto live = [&](int i) { return i >= 0 && jb_of(i) < j_end; };
+  auto live = [&](int i) { return i >= 0 && jb_of(i) < N; };
 
   // One register set of K, reloaded piece by piece: as soon as an MFMA has
   // taken a 16-byte piece of the current block, the same piece of the block at
@@ -217,7 +222,7 @@ score_onepass(const uint16_t* __restrict__ q, const void* __restrict__ k, int64_
   // its blocks again in phase 2 (late_move, wave-uniform).
   bool kept_any = false, late_move = false;
   auto fold_tile = [&](const f32x16_t& acc, int jb) {
-    const bool valid = jb + r32 < j_end;
+    const bool valid = jb + r32 < N;
     float dx[16];
     bool up = false;
 #pragma unroll
@@ -248,13 +253,21 @@ score_onepass(const uint16_t* __restrict__ q, const void* __restrict__ k, int64_
     return e;
   };
 
+  // Waves that prefetch block 0 at the end of phase 1: not wave 0, whose
+  // waits for its statistics store and for the barrier would wait for those
+  // loads too (memory operations complete in order), and not the workgroup
+  // that clears the histograms, whose waves wait for their stores before the
+  // barrier.
+  const bool pre0 = nS > 0 && wave != 0 && !(kHist && c == 0);
   f32x16_t keep[kRegBlocks];
   float4* my_tiles = &S.tile[wave][0][0][0];
   if (any) {
     // ---- phase 1 ------------------------------------------------------------
     // Blocks [0, nR) are folded, the last kLdsBlocks of them kept in LDS; the
-    // next kRegBlocks blocks are folded and kept in registers.  The last
-    // reload fetches the first block to be read again in phase 2.
+    // next kRegBlocks blocks are folded and kept in registers.  In the waves
+    // that prefetch (pre0), the last reload fetches block 0, the first to be
+    // read again in phase 2, so that its loads are in flight across the
+    // barrier.
     load_k_block<kFp8>(kb, row_of(nR > 0 ? 0 : nR), hh, kc);
     for (int i = 0; i < nR; ++i) {
       const f32x16_t acc = logits_roll(row_of(i + 1));
@@ -273,7 +286,7 @@ score_onepass(const uint16_t* __restrict__ q, const void* __restrict__ k, int64_
 #pragma unroll
     for (int t = 0; t < kRegBlocks; ++t) {
       const int i = nR + t;
-      const f32x16_t acc = logits_roll(row_of(min(i + 1, nbw - 1)));
+      const f32x16_t acc = logits_roll(row_of(i + 1 < nbw ? i + 1 : (pre0 ? 0 : i)));
       if (live(i)) {
         keep[t] = fold_tile(acc, jb_of(i));
         kept_any = true;
@@ -289,10 +302,16 @@ score_onepass(const uint16_t* __restrict__ q, const void* __restrict__ k, int64_
     const int h = 8 * (s >> 2) + 4 * hh + (s & 3);
     if ((r32 & 1) == 0) S.red[wave][h] = make_float2(m, v);
   }
-  __builtin_amdgcn_s_waitcnt(0);  // this wave's write-through stores are done
+  // The histogram clears are done before the barrier can pass.  (Only that
+  // workgroup waits for its memory operations here: elsewhere the prefetch of
+  // block 0 may still be in flight.)
+  if (kHist && c == 0) __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   float* row = stats + ((size_t)b * nwg + c) * 64;
-  if (wave == 0) {
+  // A branch the compiler knows to be wave-uniform, so that the other waves
+  // jump over the wait below instead of executing it (a wait is a scalar
+  // instruction, carried out whatever the lane mask).
+  if (__builtin_amdgcn_readfirstlane(wave) == 0) {
     if (threadIdx.x < 16) {
       float2 a = S.red[0][2 * threadIdx.x], bb = S.red[0][2 * threadIdx.x + 1];
 #pragma unroll
@@ -343,7 +362,8 @@ score_onepass(const uint16_t* __restrict__ q, const void* __restrict__ k, int64_
       __hip_atomic_store(gen_word, tag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     if (timed_out) {
       float* out = scores + (size_t)b * score_stride;
-      for (int j = j_begin + threadIdx.x; j < j_end; j += kOpThreads) out[j] = __builtin_nanf("");
+      for (int i = 0; i < nbw; ++i)
+        if (hh == 0 && jb_of(i) + r32 < N) out[jb_of(i) + r32] = __builtin_nanf("");
       return;
     }
   }
@@ -401,28 +421,33 @@ score_onepass(const uint16_t* __restrict__ q, const void* __restrict__ k, int64_
     for (int i = threadIdx.x; i < kSelBins / 2; i += kOpThreads) S.hist16[i] = 0u;
     __syncthreads();
   }
-  // From logits (blocks read again): sum_h 2^(x - L_h).
-  auto importance = [&](const f32x16_t& acc) {
+  // This lane's half (16 heads) of a key's importance.  From logits (blocks
+  // read again): sum_h 2^(x - L_h).
+  auto part_logits = [&](const f32x16_t& acc) {
     float imp = 0.f;
 #pragma unroll
     for (int r = 0; r < 16; ++r) imp += fast_exp2(acc[r] * c2 - L[r]);
-    return imp + __shfl_xor(imp, 32);
+    return imp;
   };
   // From kept terms e = 2^(x - mref): sum_h e * 2^(mref_h - L_h).
   float wt[16];
 #pragma unroll
   for (int r = 0; r < 16; ++r) wt[r] = fast_exp2(mref[r] - L[r]);
-  auto importance_kept = [&](const f32x16_t& e) {
+  auto part_kept = [&](const f32x16_t& e) {
     float imp = 0.f;
 #pragma unroll
     for (int r = 0; r < 16; ++r) imp = fmaf(e[r], wt[r], imp);
-    return imp + __shfl_xor(imp, 32);
+    return imp;
   };
   // After a late move of the references every block of the wave is read again.
   const int n_re = late_move ? nbw : nS;
-  auto emit = [&](float imp, int jb) {
-    const int j = jb + r32;
-    if (hh == 0 && j < j_end) {
+  // Scores of two blocks from their halves' partial sums: lanes of half 0
+  // store block ia's keys, lanes of half 1 block ib's (ib < 0: none).
+  auto emit2 = [&](float pa, float pb, int ia, int ib) {
+    const float imp = half_sums2(pa, pb);
+    const int i = hh ? ib : ia;
+    const int j = jb_of(i) + r32;
+    if (i >= 0 && j < N) {
       out[j] = imp;
       if (kHist && j < pe) {
         const uint32_t bin = order_key(imp) >> 20;
@@ -430,26 +455,32 @@ score_onepass(const uint16_t* __restrict__ q, const void* __restrict__ k, int64_
       }
     }
   };
-  // Register-kept tiles first (their registers are then free), then the
-  // LDS-kept ones, then the blocks kept nowhere, read again four at a time
-  // with all their loads in flight together.  The importance of a group of
-  // tiles is computed before any of it is stored, so that the tiles' exp2
-  // chains and cross-half adds overlap.
+  // Register-kept tiles first (their registers are then free); then the loads
+  // of the next blocks to be read again are issued, and the LDS-kept tiles are
+  // turned into scores while they are in flight; then the blocks kept nowhere:
+  // block 0 from the registers phase 1 left it in, the early ones, the rest
+  // four at a time.  The partial sums of a group of tiles are computed before
+  // any of it is stored, so that the tiles' chains overlap.
+  static_assert(kRegBlocks % 2 == 0, "register tiles go in pairs");
   if (!late_move) {
-    float imp[kRegBlocks];
+    float pk[kRegBlocks];
 #pragma unroll
-    for (int t = 0; t < kRegBlocks; ++t) imp[t] = importance_kept(keep[t]);
+    for (int t = 0; t < kRegBlocks; ++t) pk[t] = part_kept(keep[t]);
 #pragma unroll
-    for (int t = 0; t < kRegBlocks; ++t)
-      if (live(nR + t)) emit(imp[t], jb_of(nR + t));
+    for (int t = 0; t < kRegBlocks; t += 2) emit2(pk[t], pk[t + 1], nR + t, nR + t + 1);
   }
-  constexpr int kLdsGroup = 3;
-  static_assert(kLdsBlocks % kLdsGroup == 0, "LDS tiles go in groups");
-  for (int s0 = 0; s0 < (late_move ? 0 : kLdsBlocks); s0 += kLdsGroup) {
-    float imp[kLdsGroup];
+  const int from_kc = pre0 ? 1 : 0;  // kc holds block 0
+  constexpr int kEarly = 3;
+  const int n_early = min(kEarly, n_re - from_kc);
+  u32x4 ke[kEarly][k_regs<kFp8>()];
 #pragma unroll
-    for (int u = 0; u < kLdsGroup; ++u) {
-      const float4* t = my_tiles + (s0 + u) * 4 * 64 + lane;
+  for (int u = 0; u < kEarly; ++u)
+    if (u < n_early) load_k_block<kFp8>(kb, row_of(from_kc + u), hh, ke[u]);
+  if (!late_move) {
+    float pl[kLdsBlocks];
+#pragma unroll
+    for (int u = 0; u < kLdsBlocks; ++u) {
+      const float4* t = my_tiles + u * 4 * 64 + lane;
       f32x16_t acc;
 #pragma unroll
       for (int p = 0; p < 4; ++p) {
@@ -459,27 +490,45 @@ score_onepass(const uint16_t* __restrict__ q, const void* __restrict__ k, int64_
         acc[4 * p + 2] = v.z;
         acc[4 * p + 3] = v.w;
       }
-      imp[u] = importance_kept(acc);
+      pl[u] = part_kept(acc);
     }
 #pragma unroll
-    for (int u = 0; u < kLdsGroup; ++u)
-      if (live(nS + s0 + u)) emit(imp[u], jb_of(nS + s0 + u));
+    for (int u = 0; u < kLdsBlocks; u += 2)
+      emit2(pl[u], u + 1 < kLdsBlocks ? pl[u + 1] : pl[u], nS + u,
+            u + 1 < kLdsBlocks ? nS + u + 1 : -1);
   }
-  for (int i0 = 0; i0 < n_re; i0 += 4) {
+  // Blocks read again, in order, paired as they come (wave-uniform state).
+  float held = 0.f;
+  int held_i = -1;
+  auto reread = [&](const u32x4(&kr)[k_regs<kFp8>()], int i) {
+    f32x16_t acc = {};
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qreg[e], k_operand<kFp8>(kr, e), acc, 0, 0, 0);
+    const float p = part_logits(acc);
+    if (held_i < 0) {
+      held = p;
+      held_i = i;
+    } else {
+      emit2(held, p, held_i, i);
+      held_i = -1;
+    }
+  };
+  if (from_kc) reread(kc, 0);
+#pragma unroll
+  for (int u = 0; u < kEarly; ++u)
+    if (u < n_early) reread(ke[u], from_kc + u);
+  for (int i0 = from_kc + kEarly; i0 < n_re; i0 += 4) {
     u32x4 kr[4][k_regs<kFp8>()];
 #pragma unroll
     for (int u = 0; u < 4; ++u) load_k_block<kFp8>(kb, row_of(min(i0 + u, n_re - 1)), hh, kr[u]);
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
       if (i0 + u >= n_re) break;
-      f32x16_t acc = {};
-#pragma unroll
-      for (int e = 0; e < 8; ++e)
-        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qreg[e], k_operand<kFp8>(kr[u], e), acc, 0,
-                                                      0, 0);
-      if (live(i0 + u)) emit(importance(acc), jb_of(i0 + u));
+      reread(kr[u], i0 + u);
     }
   }
+  if (held_i >= 0) emit2(held, held, held_i, -1);
   if (kHist) {
     __syncthreads();
     uint32_t* gh = hist + (size_t)b * kHistRow;
