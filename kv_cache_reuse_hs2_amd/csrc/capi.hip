@@ -146,23 +146,35 @@ hs2_status hs2_decode_step(const hs2_attn_desc* desc, const void* q, const void*
   const WsLayout l = ws_layout(*desc, kv_capacity);
   char* w = static_cast<char*>(ws);
   hipStream_t st = static_cast<hipStream_t>(stream);
-  // bf16 and E4M3: the scoring pass also builds the selector's histogram.
+  // bf16 and E4M3: the scoring pass also builds the selector's histogram,
+  // and the one-pass decode kernel also runs the selector's candidate filter.
   const bool fuse = desc->dtype != HS2_F32;
   const bool pf = is_prefill(*desc);
+  const SelectWs sw = select_ws(*desc, kv_capacity);
+  FilterArgs filt{};
+  filt.cnt = reinterpret_cast<uint32_t*>(w + l.select + sw.cnt_off);
+  filt.meta = reinterpret_cast<uint32_t*>(w + l.select + sw.meta_off);
+  filt.list = reinterpret_cast<uint2*>(w + l.select + sw.list_off);
+  filt.nslices = select_slices(kv_capacity);
+  filt.k_top = desc->k_top;
+  bool filtered = false;
   hipError_t e =
       pf ? launch_prefill_scores(*desc, q, k, kv_stride, ctx_len, kv_capacity, scores, lse_full,
                                  w + l.score, fuse, st)
          : launch_score_decode(*desc, q, k, kv_stride, ctx_len, kv_capacity, scores, lse_full,
-                               w + l.score, reinterpret_cast<uint64_t*>(w + l.sync), fuse, st);
+                               w + l.score, reinterpret_cast<uint64_t*>(w + l.sync), fuse, st,
+                               fuse ? &filt : nullptr, &filtered);
   if (e != hipSuccess) return HS2_EHIP;
   const size_t hist_off = pf ? prefill_ws(*desc, kv_capacity).hist_off
                              : score_ws(*desc, kv_capacity).hist_off;
   uint32_t* hist = fuse ? reinterpret_cast<uint32_t*>(w + l.score + hist_off) : nullptr;
   // MFMA decode: the final selection runs inside the sparse layer's kernel.
   const bool tail = fuse && !pf;
-  e = launch_select(*desc, scores, ctx_len, kv_capacity, top_idx, top_cnt, w + l.select, hist,
-                    !tail, st);
-  if (e != hipSuccess) return HS2_EHIP;
+  if (!filtered) {
+    e = launch_select(*desc, scores, ctx_len, kv_capacity, top_idx, top_cnt, w + l.select, hist,
+                      !tail, st);
+    if (e != hipSuccess) return HS2_EHIP;
+  }
   if (pf)
     return launched(launch_prefill_sparse(*desc, q_sparse, k, v, kv_stride, ctx_len, kv_capacity,
                                           top_idx, top_cnt, o, lse, st));

@@ -63,6 +63,15 @@ typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 
+// Buffer resource over `bytes` bytes at p: buffer loads past the end return
+// zero and stores past it are dropped.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* p, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), 0, bytes, 0x00020000);
+}
+// Cache policy of buffer accesses to data that other workgroups of the same
+// launch write or read (sc1: coherent at device scope, across the XCDs' L2s).
+constexpr int kSc1 = 16;
+
 // Bytes per stored K/V element: E4M3 caches hold one byte per element, the
 // bf16 kernels two.
 template <bool kFp8>
@@ -115,22 +124,39 @@ struct BlockPieces {
   int stride;  // blk_stride(cap, piece)
 };
 
+// The selector's candidate filter as the one-pass scoring kernel runs it in
+// the fused decode step: the selection region's slice counts, per-row
+// metadata and candidate lists (select_ws), and the budget.
+struct FilterArgs {
+  uint32_t* cnt;
+  uint32_t* meta;
+  uint2* list;
+  int nslices;
+  int k_top;
+};
+
 // with_hist: also build the selector histogram of the pool scores in the
 // scoring region (MFMA paths only).  sync: the barrier words of the workspace
 // (ws_layout().sync); bf16 and E4M3 K take the one-pass kernel when the batch
-// fits the device, two passes otherwise.
+// fits the device, two passes otherwise.  filt (with with_hist): the one-pass
+// kernel also runs the selector's candidate filter, and *filtered says
+// whether it did (false: the two-pass kernels ran; the filter is the
+// caller's).
 hipError_t launch_score_decode(const hs2_attn_desc& d, const void* q, const void* k,
                                int64_t kv_stride, const int32_t* ctx_len, int cap,
                                float* scores, float* lse, char* ws, uint64_t* sync,
-                               bool with_hist, hipStream_t st);
+                               bool with_hist, hipStream_t st, const FilterArgs* filt = nullptr,
+                               bool* filtered = nullptr);
 
 // One-pass decode scoring (bf16 or E4M3 K): workgroups per sequence and keys
 // per workgroup for a device of n_cu CUs; false when the batch does not fit.
+// With filt and hist, the kernel builds the histogram and runs the filter.
 bool onepass_plan(const hs2_attn_desc& d, int cap, int n_cu, int* nwg, int* chunk);
 hipError_t launch_score_onepass(const hs2_attn_desc& d, const void* q, const void* k,
                                 int64_t kv_stride, const int32_t* ctx_len, int cap, int nwg,
                                 int chunk, float c2, float* stats, uint64_t* sync, float* scores,
-                                float* lse, uint32_t* hist, hipStream_t st);
+                                float* lse, uint32_t* hist, const FilterArgs* filt,
+                                hipStream_t st);
 // Compute units of the current device (cached per device).
 int device_cu_count();
 

@@ -157,10 +157,13 @@ inline SparseWs sparse_ws(const hs2_attn_desc& d) {
   return w;
 }
 
-// Words of the one-pass scoring kernel's barrier: a generation per sequence at
-// word b and a slot per (sequence, workgroup) at word kOpMaxWg * (1 + b) + c,
+// Words of the one-pass scoring kernel's barriers: a generation per sequence
+// at word b, and per (sequence, workgroup) a slot of the first barrier at
+// word kOpMaxWg * (1 + 2b) + c and one of the second at kOpMaxWg * (2 + 2b) + c,
 // the same positions for every descriptor.
-inline size_t sync_words(const hs2_attn_desc& d) { return (size_t)kOpMaxWg * (1 + (size_t)d.batch); }
+inline size_t sync_words(const hs2_attn_desc& d) {
+  return (size_t)kOpMaxWg * (1 + 2 * (size_t)d.batch);
+}
 
 // Offsets of the regions inside the caller's workspace: the barrier words at
 // offset 0 (so that they keep their place whatever the descriptor), then

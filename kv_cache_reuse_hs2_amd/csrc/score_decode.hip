@@ -706,7 +706,9 @@ hipError_t launch_score_full(const hs2_attn_desc& d, const void* q, const void* 
 hipError_t launch_score_decode(const hs2_attn_desc& d, const void* q, const void* k,
                                int64_t kv_stride, const int32_t* ctx_len, int cap,
                                float* scores, float* lse, char* ws, uint64_t* sync,
-                               bool with_hist, hipStream_t st) {
+                               bool with_hist, hipStream_t st, const FilterArgs* filt,
+                               bool* filtered) {
+  if (filtered != nullptr) *filtered = false;
   const ScoreWs w = score_ws(d, cap);
   float2* stats = reinterpret_cast<float2*>(ws + w.stats_off);
   const float c2 = d.sm_scale * 1.4426950408889634f;
@@ -714,11 +716,15 @@ hipError_t launch_score_decode(const hs2_attn_desc& d, const void* q, const void
   if (d.dtype != HS2_F32) {
     uint32_t* hist = with_hist ? reinterpret_cast<uint32_t*>(ws + w.hist_off) : nullptr;
     int nwg = 0, chunk = 0;
-    if (sync != nullptr && onepass_plan(d, cap, device_cu_count(), &nwg, &chunk))
+    if (sync != nullptr && onepass_plan(d, cap, device_cu_count(), &nwg, &chunk)) {
+      // The one-pass kernel builds the histogram only together with the filter.
+      if (hist != nullptr && filt == nullptr) return hipErrorInvalidValue;
+      if (filtered != nullptr) *filtered = hist != nullptr;
       return launch_score_onepass(d, q, k, kv_stride, ctx_len, cap, nwg, chunk,
                                   d.dtype == HS2_FP8_E4M3 ? c2 * d.k_scale : c2,
                                   reinterpret_cast<float*>(ws + w.op_off), sync, scores, lse,
-                                  hist, st);
+                                  hist, filt, st);
+    }
     if (d.dtype == HS2_FP8_E4M3)
       launch_score_mfma<true>(d, q, k, kv_stride, ctx_len, cap, scores, lse, stats, nchunks1,
                               c2 * d.k_scale, hist, st);

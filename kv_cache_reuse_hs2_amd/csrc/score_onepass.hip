@@ -23,7 +23,11 @@
 //   phase 2  it folds the sequence's statistics into L_h, turns the kept tiles
 //            into I[j] without touching HBM, re-reads only its blocks that
 //            did not fit, and (in the fused decode step) adds the pool
-//            scores to the selector's first histogram.
+//            scores to the selector's first histogram;
+//   filter   (fused decode step only) after a second barrier, when the
+//            sequence's scores and first-level histogram are complete, the
+//            selector's candidate filter runs on the sequence's 4,096-key
+//            slices c, c + nwg, ... (the same code as the filter kernel).
 //
 // Workgroup c of a sequence with nwg workgroups takes blocks c, c + nwg,
 // c + 2 nwg, ... (its four waves in turn), so that at any moment the
@@ -35,18 +39,21 @@
 // workgroup reads the sequence's generation g, after its statistics it sets its
 // own 64-bit slot to tag(g + 1), and it polls the sequence's slots until all of
 // them hold that tag; workgroup 0 of the sequence then stores g + 1 as the new
-// generation.  No counter has to be reset between calls and a fresh workspace
+// generation.  The second barrier is the same with a second set of slots and
+// a second tag.  No counter has to be reset between calls and a fresh workspace
 // needs no initialisation: a slot written by an earlier call holds the tag of
 // a generation already passed, and the tag is the generation mixed with a
 // fixed 64-bit constant, so other data left in the workspace does not pass for
-// it either.  The words sit at fixed positions (generation b at word b, slot
-// (b, c) at word kOpMaxWg * (1 + b) + c) for every descriptor.  All
+// it either.  The words sit at fixed positions (generation b at word b, slots
+// (b, c) at words kOpMaxWg * (1 + 2b) + c and kOpMaxWg * (2 + 2b) + c) for
+// every descriptor.  All
 // cross-workgroup data goes through write-through stores and coherent loads
 // (sc1), so the L2s of the chip's XCDs need no write-back or invalidation.
 // Every workgroup of the grid must be resident at once: the grid never has more
 // workgroups than the device has CUs, and the LDS use allows one per CU.  Waits
-// are bounded in time; a workgroup that gives up writes NaN scores, so a
-// failure is visible rather than silent.
+// are bounded in time; a workgroup that gives up writes NaN scores (and
+// empty candidate lists for its slices), so a failure is visible rather than
+// silent.
 //
 // Layout of a logit tile (K as the B operand): lane (r32, hh) holds key
 // jb + r32 for heads 8*(r/4) + 4*hh + r%4, r = 0..15, so the sum over heads is
@@ -56,6 +63,7 @@
 // logit exceeds it by more than 2^6, so almost every logit costs one exp2, and
 // the lanes' sums add without rescaling at the end.
 #include "score_common.h"
+#include "select_core.h"
 
 namespace hs2 {
 
@@ -75,11 +83,16 @@ constexpr float kRefMin = -1e30f;           // reference of a lane that has seen
 constexpr float kRescale = 64.f;            // binades a logit may exceed its reference
 constexpr uint64_t kWaitTicks = 100000000;  // 1 s of the 100 MHz constant clock
 constexpr uint64_t kTagMix = 0x9E3779B97F4A7C15ull;
+constexpr uint64_t kTagMix2 = 0xC2B2AE3D27D4EB4Full;
 
 __device__ __forceinline__ uint64_t slot_tag(uint64_t gen) { return gen ^ kTagMix; }
+__device__ __forceinline__ uint64_t slot_tag2(uint64_t gen) { return gen ^ kTagMix2; }
 
 struct OpLds {
-  float4 tile[kOpWaves][kLdsBlocks][4][64];  // kept logit tiles: 16 floats per lane
+  union {
+    float4 tile[kOpWaves][kLdsBlocks][4][64];  // kept logit tiles: 16 floats per lane
+    FilterLds filt;                            // the candidate filter, after phase 2
+  };
   // Phase 2: the workgroup's histogram of the top 12 bits of its pool scores,
   // two 16-bit counts per word (bin 2w in the low half of word w); a
   // workgroup counts at most 4,096 keys, so no count reaches the high half.
@@ -90,10 +103,6 @@ struct OpLds {
   int wflag[2][kOpWaves];  // barrier polling: per-wave verdicts, by iteration parity
 };
 
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc_of(const void* p, uint32_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), 0, bytes, 0x00020000);
-}
-constexpr int kSc1 = 16;  // cache policy: coherent at device scope (sc1)
 
 // a if c else b, as a bit select (an indexed form would make the compiler put
 // the arrays below in memory).
@@ -135,13 +144,16 @@ __device__ __forceinline__ void half_reduce_scatter(const float (&v)[16], const 
   // slot s = 8*b4 + 4*b3 + 2*b2 + b1 = r32 >> 1
 }
 
-template <bool kFp8, bool kHist, int kRegBlocks>
+template <bool kFp8, bool kFilter, int kRegBlocks>
 __global__ __launch_bounds__(kOpThreads) __attribute__((amdgpu_waves_per_eu(1, 1))) void
 score_onepass(const uint16_t* __restrict__ q, const void* __restrict__ k, int64_t kv_stride,
               const int32_t* __restrict__ ctx_len, int cap, int H, float c2, int nwg, int chunk,
               float* __restrict__ stats, uint64_t* __restrict__ sync, float* __restrict__ scores,
-              int64_t score_stride, float* __restrict__ lse_out, uint32_t* __restrict__ hist,
-              int window) {
+              float* __restrict__ lse_out, uint32_t* __restrict__ hist, int window,
+              FilterArgs filt) {
+  // The fused step's variant builds the first-level histogram and runs the
+  // candidate filter; the plain one writes the scores only.
+  constexpr bool kHist = kFilter;
   __shared__ __attribute__((aligned(16))) OpLds S;
   const int b = blockIdx.x / nwg, c = blockIdx.x - b * nwg;
   const int N = clamp_ctx(ctx_len, b, cap);
@@ -152,7 +164,28 @@ score_onepass(const uint16_t* __restrict__ q, const void* __restrict__ k, int64_
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int r32 = lane & 31, hh = lane >> 5;
   uint64_t* const gen_word = sync + b;
-  uint64_t* const slots = sync + (size_t)kOpMaxWg * (1 + b);
+  uint64_t* const slots = sync + (size_t)kOpMaxWg * (1 + 2 * b);
+  uint64_t* const slots2 = sync + (size_t)kOpMaxWg * (2 + 2 * b);
+  float* const out = scores + (size_t)b * cap;
+  const RowGeom rg = row_geom(ctx_len, cap, b, 1, 1, 1, filt.k_top, window);
+  // Slices of the selector's filter: those of the pool, unless the pool fits
+  // the budget (then the final stage takes it whole).
+  const int n_filt = (!kFilter || rg.kk == 0 || rg.kk == rg.pe)
+                         ? 0 : (rg.pe + kSelSlice - 1) / kSelSlice;
+  // After a failed wait: NaN scores for the keys of the filter slices and
+  // empty candidate lists for them.
+  auto fail_filter = [&]() {
+    for (int s = c; s < n_filt; s += nwg) {
+      for (int j = s * kSelSlice + threadIdx.x; j < min(rg.pe, (s + 1) * kSelSlice);
+           j += kOpThreads)
+        out[j] = __builtin_nanf("");
+      if (threadIdx.x == 0) filt.cnt[(size_t)b * filt.nslices + s] = 0u;
+      if (s == 0 && threadIdx.x == 0) {
+        filt.meta[4 * b] = 0u;
+        filt.meta[4 * b + 1] = 0u;
+      }
+    }
+  };
 
   if (threadIdx.x == 0) {
     const uint64_t g = __hip_atomic_load(gen_word, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -320,7 +353,7 @@ score_onepass(const uint16_t* __restrict__ q, const void* __restrict__ k, int64_
         merge_ml(bb.x, bb.y, S.red[w][2 * threadIdx.x + 1].x, S.red[w][2 * threadIdx.x + 1].y);
       }
       const float4 val = make_float4(a.x, a.y, bb.x, bb.y);
-      __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, val), rsrc_of(row, 256),
+      __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, val), buffer_rsrc(row, 256),
                                              threadIdx.x * 16, 0, kSc1);
     }
     __builtin_amdgcn_s_waitcnt(0);  // the row is in memory before the slot says so
@@ -329,17 +362,17 @@ score_onepass(const uint16_t* __restrict__ q, const void* __restrict__ k, int64_
   }
   // ---- barrier: every workgroup of the sequence has written its row --------
   const uint64_t tag = S.tag;
-  {
-    // Thread t checks slot t; each wave posts "all mine arrived" and "past the
-    // time limit", and every wave reads the four posts after one barrier (the
-    // posts alternate between two rows, so a fast wave's next post cannot
-    // overwrite one that a slow wave is still reading).
+  // Thread t checks slot t of sl; each wave posts "all mine arrived" and "past
+  // the time limit", and every wave reads the four posts after one barrier
+  // (the posts alternate between two rows, so a fast wave's next post cannot
+  // overwrite one that a slow wave is still reading).  Returns true when the
+  // time limit passed first.
+  auto wait_all = [&](const uint64_t* sl, uint64_t expect) {
     const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
-    bool timed_out = false;
     for (int it = 0;; ++it) {
       const bool mine = threadIdx.x >= nwg ||
-                        __hip_atomic_load(slots + threadIdx.x, __ATOMIC_RELAXED,
-                                          __HIP_MEMORY_SCOPE_AGENT) == slot_tag(tag);
+                        __hip_atomic_load(sl + threadIdx.x, __ATOMIC_RELAXED,
+                                          __HIP_MEMORY_SCOPE_AGENT) == expect;
       const bool late = __builtin_amdgcn_s_memrealtime() - t0 > kWaitTicks;
       const uint64_t missing = __builtin_amdgcn_ballot_w64(!mine);
       const uint64_t over = __builtin_amdgcn_ballot_w64(late);
@@ -351,19 +384,19 @@ score_onepass(const uint16_t* __restrict__ q, const void* __restrict__ k, int64_
         all &= S.wflag[it & 1][w] & 1;
         any_late |= S.wflag[it & 1][w] & 2;
       }
-      if (all) break;
-      if (any_late) {
-        timed_out = true;
-        break;
-      }
+      if (all) return false;
+      if (any_late) return true;
       __builtin_amdgcn_s_sleep(8);
     }
+  };
+  {
+    const bool timed_out = wait_all(slots, slot_tag(tag));
     if (c == 0 && threadIdx.x == 0)
       __hip_atomic_store(gen_word, tag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     if (timed_out) {
-      float* out = scores + (size_t)b * score_stride;
       for (int i = 0; i < nbw; ++i)
         if (hh == 0 && jb_of(i) + r32 < N) out[jb_of(i) + r32] = __builtin_nanf("");
+      fail_filter();
       return;
     }
   }
@@ -375,7 +408,7 @@ score_onepass(const uint16_t* __restrict__ q, const void* __restrict__ k, int64_
   {
     const int pc = threadIdx.x & 15, r0 = threadIdx.x >> 4;
     const __amdgpu_buffer_rsrc_t rs =
-        rsrc_of(stats + (size_t)b * nwg * 64, (uint32_t)(nwg * 64 * sizeof(float)));
+        buffer_rsrc(stats + (size_t)b * nwg * 64, (uint32_t)(nwg * 64 * sizeof(float)));
     float ma = -INFINITY, la = 0.f, mb = -INFINITY, lb = 0.f;
     for (int base = r0; base < nwg; base += 4 * 16) {
       float4 v[4];
@@ -411,12 +444,16 @@ score_onepass(const uint16_t* __restrict__ q, const void* __restrict__ k, int64_
     }
     __syncthreads();
   }
+  // Scores, and the histogram of the pool ones, of this workgroup's keys.
+  auto phase2 = [&]() {
   if (!any) return;  // workgroup-uniform
   float L[16];
 #pragma unroll
   for (int r = 0; r < 16; ++r) L[r] = S.s_L[8 * (r >> 2) + 4 * hh + (r & 3)];
-  float* out = scores + (size_t)b * score_stride;
   const int pe = N - window;  // decode pool end
+  // With the filter, the scores are read by other workgroups of this launch:
+  // written through at device scope.
+  const __amdgpu_buffer_rsrc_t rs_out = buffer_rsrc(out, (uint32_t)N * 4u);
   if (kHist) {
     for (int i = threadIdx.x; i < kSelBins / 2; i += kOpThreads) S.hist16[i] = 0u;
     __syncthreads();
@@ -448,7 +485,10 @@ score_onepass(const uint16_t* __restrict__ q, const void* __restrict__ k, int64_
     const int i = hh ? ib : ia;
     const int j = jb_of(i) + r32;
     if (i >= 0 && j < N) {
-      out[j] = imp;
+      if (kFilter)
+        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(imp), rs_out, j * 4, 0, kSc1);
+      else
+        out[j] = imp;
       if (kHist && j < pe) {
         const uint32_t bin = order_key(imp) >> 20;
         atomicAdd(&S.hist16[bin >> 1], 1u << (16 * (bin & 1)));
@@ -538,6 +578,30 @@ score_onepass(const uint16_t* __restrict__ q, const void* __restrict__ k, int64_
       if (two >> 16) atomicAdd(&gh[2 * w + 1], two >> 16);
     }
   }
+  };
+  phase2();
+  if constexpr (kFilter) {
+    // ---- second barrier: the sequence's scores and histogram are complete --
+    __builtin_amdgcn_s_waitcnt(0);  // this wave's score stores and atomics are done
+    __syncthreads();
+    if (threadIdx.x == 0)
+      __hip_atomic_store(slots2 + c, slot_tag2(tag), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (wait_all(slots2, slot_tag2(tag))) {
+      fail_filter();
+      return;
+    }
+    // ---- the candidate filter on slices c, c + nwg, ... -----------------------
+    uint32_t* hrow = hist + (size_t)b * kHistRow;
+    for (int s = c; s < n_filt; s += nwg) {
+      uint2* list_s = filt.list + ((size_t)b * filt.nslices + s) * kSelSlice;
+      uint32_t* cnt_r = filt.cnt + (size_t)b * filt.nslices;
+      if (cap % 4 == 0)
+        filter_slice<true, true>(out, cap, rg, s, hrow, cnt_r, filt.meta + 4 * b, list_s, S.filt);
+      else
+        filter_slice<false, true>(out, cap, rg, s, hrow, cnt_r, filt.meta + 4 * b, list_s, S.filt);
+      __syncthreads();
+    }
+  }
 }
 
 }  // namespace
@@ -569,27 +633,31 @@ int device_cu_count() {
 hipError_t launch_score_onepass(const hs2_attn_desc& d, const void* q, const void* k,
                                 int64_t kv_stride, const int32_t* ctx_len, int cap, int nwg,
                                 int chunk, float c2, float* stats, uint64_t* sync, float* scores,
-                                float* lse, uint32_t* hist, hipStream_t st) {
+                                float* lse, uint32_t* hist, const FilterArgs* filt,
+                                hipStream_t st) {
   const auto* qq = static_cast<const uint16_t*>(q);
   const dim3 grid(d.batch * nwg);
   const bool fp8 = d.dtype == HS2_FP8_E4M3;
-  if (fp8 && hist)
-    score_onepass<true, true, kOpRegBlocksFp8><<<grid, kOpThreads, 0, st>>>(qq, k, kv_stride, ctx_len, cap,
-                                                           d.n_heads, c2, nwg, chunk, stats, sync,
-                                                           scores, cap, lse, hist, d.window);
+  FilterArgs fa{};
+  fa.k_top = d.k_top;
+  const bool fused = filt != nullptr && hist != nullptr;
+  if (fused) fa = *filt;
+  if (fp8 && fused)
+    score_onepass<true, true, kOpRegBlocksFp8><<<grid, kOpThreads, 0, st>>>(
+        qq, k, kv_stride, ctx_len, cap, d.n_heads, c2, nwg, chunk, stats, sync, scores, lse, hist,
+        d.window, fa);
   else if (fp8)
-    score_onepass<true, false, kOpRegBlocksFp8><<<grid, kOpThreads, 0, st>>>(qq, k, kv_stride, ctx_len, cap,
-                                                            d.n_heads, c2, nwg, chunk, stats,
-                                                            sync, scores, cap, lse, hist, d.window);
-  else if (hist)
-    score_onepass<false, true, kOpRegBlocksBf16><<<grid, kOpThreads, 0, st>>>(qq, k, kv_stride, ctx_len, cap,
-                                                            d.n_heads, c2, nwg, chunk, stats,
-                                                            sync, scores, cap, lse, hist, d.window);
+    score_onepass<true, false, kOpRegBlocksFp8><<<grid, kOpThreads, 0, st>>>(
+        qq, k, kv_stride, ctx_len, cap, d.n_heads, c2, nwg, chunk, stats, sync, scores, lse, hist,
+        d.window, fa);
+  else if (fused)
+    score_onepass<false, true, kOpRegBlocksBf16><<<grid, kOpThreads, 0, st>>>(
+        qq, k, kv_stride, ctx_len, cap, d.n_heads, c2, nwg, chunk, stats, sync, scores, lse, hist,
+        d.window, fa);
   else
-    score_onepass<false, false, kOpRegBlocksBf16><<<grid, kOpThreads, 0, st>>>(qq, k, kv_stride, ctx_len, cap,
-                                                             d.n_heads, c2, nwg, chunk, stats,
-                                                             sync, scores, cap, lse, hist,
-                                                             d.window);
+    score_onepass<false, false, kOpRegBlocksBf16><<<grid, kOpThreads, 0, st>>>(
+        qq, k, kv_stride, ctx_len, cap, d.n_heads, c2, nwg, chunk, stats, sync, scores, lse, hist,
+        d.window, fa);
   return hipGetLastError();
 }
 

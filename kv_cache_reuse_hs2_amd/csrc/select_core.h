@@ -135,6 +135,121 @@ __device__ void find_bin_regs(const uint32_t (&v)[kPer], uint32_t need, uint32_t
   __syncthreads();
 }
 
+// The candidate filter of one 4,096-key slice s of a row (256 threads): it
+// finds the threshold bin b0 (top 12 key bits) from the row's first-level
+// histogram, writes the slice's keys whose top bits are >= b0, in index
+// order, as (key, index) pairs to list_s and their count to cnt_r[s]
+// (slice 0 also writes b0 and the pool count above b0 to meta_r), and adds
+// key bits 19..8 of its keys in b0 to the row's second-level histogram.
+// kCoherent: the scores and the histogram were written by other workgroups
+// of the same launch, so they are read at device scope (sc1); kVec4: the row
+// is 16-byte aligned (the row length is a multiple of 4).
+constexpr int kFiltPer = kSelSlice / 256;  // keys per thread
+// Above this many threshold-bin keys in a slice, the second-level histogram
+// is merged in LDS first instead of one global atomic per key.
+constexpr uint32_t kDirectHist2 = 256;
+
+struct FilterLds {
+  uint32_t scratch[8];
+  uint32_t res[2];
+  uint32_t h2[kSelBins];
+};
+
+template <bool kVec4, bool kCoherent>
+__device__ void filter_slice(const float* __restrict__ row, int cap, const RowGeom& g, int s,
+                             uint32_t* __restrict__ hrow, uint32_t* __restrict__ cnt_r,
+                             uint32_t* __restrict__ meta_r, uint2* __restrict__ list_s,
+                             FilterLds& L) {
+  static_assert(kSelBins == 16 * 256 && kFiltPer == 16, "sixteen keys and bins per thread");
+  const int s0 = s * kSelSlice;
+  // Thread t owns the 16 consecutive keys s0 + 16t .. s0 + 16t + 15; they are
+  // loaded first so that the loads overlap the threshold search.
+  const int j0 = s0 + kFiltPer * threadIdx.x;
+  uint32_t key[kFiltPer];
+  uint32_t hv[16];
+  if constexpr (kCoherent) {
+    // The row's cap scores (keys past the pool end are loaded, never kept).
+    const __amdgpu_buffer_rsrc_t rs = buffer_rsrc(row, (uint32_t)cap * 4u);
+    const __amdgpu_buffer_rsrc_t rh = buffer_rsrc(hrow, kSelBins * 4u);
+    if (kVec4) {
+#pragma unroll
+      for (int e = 0; e < kFiltPer; e += 4) {
+        const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(rs, (j0 + e) * 4, 0, kSc1);
+#pragma unroll
+        for (int u = 0; u < 4; ++u) key[e + u] = order_key(__uint_as_float(v[u]));
+      }
+    } else {
+#pragma unroll
+      for (int e = 0; e < kFiltPer; ++e)
+        key[e] = order_key(__uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rs, (j0 + e) * 4, 0, kSc1)));
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const u32x4 x = __builtin_amdgcn_raw_buffer_load_b128(rh, (16 * threadIdx.x + 4 * i) * 4, 0, kSc1);
+#pragma unroll
+      for (int u = 0; u < 4; ++u) hv[4 * i + u] = x[u];
+    }
+  } else {
+    if (kVec4 && j0 + kFiltPer <= g.pe) {
+#pragma unroll
+      for (int e = 0; e < kFiltPer; e += 4) {
+        const f32x4 v = *reinterpret_cast<const f32x4*>(row + j0 + e);
+        key[e] = order_key(v.x);
+        key[e + 1] = order_key(v.y);
+        key[e + 2] = order_key(v.z);
+        key[e + 3] = order_key(v.w);
+      }
+    } else {
+#pragma unroll
+      for (int e = 0; e < kFiltPer; ++e) key[e] = (j0 + e < g.pe) ? order_key(row[j0 + e]) : 0u;
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const u32x4 x = *reinterpret_cast<const u32x4*>(hrow + 16 * threadIdx.x + 4 * i);
+      hv[4 * i] = x.x;
+      hv[4 * i + 1] = x.y;
+      hv[4 * i + 2] = x.z;
+      hv[4 * i + 3] = x.w;
+    }
+  }
+  find_bin_regs(hv, (uint32_t)g.kk, L.scratch, L.res);
+  const uint32_t b0 = L.res[0];
+  uint32_t keep = 0, in_b0 = 0;
+#pragma unroll
+  for (int e = 0; e < kFiltPer; ++e) {
+    const bool valid = j0 + e < g.pe;
+    keep += (valid && (key[e] >> 20) >= b0) ? 1u : 0u;
+    in_b0 += (valid && (key[e] >> 20) == b0) ? 1u : 0u;
+  }
+  uint32_t total, total_b0;
+  uint32_t pos = block_prefix_sum(keep, L.scratch, &total);
+  (void)block_prefix_sum(in_b0, L.scratch, &total_b0);
+#pragma unroll
+  for (int e = 0; e < kFiltPer; ++e)
+    if (j0 + e < g.pe && (key[e] >> 20) >= b0) list_s[pos++] = make_uint2(key[e], (uint32_t)(j0 + e));
+  if (threadIdx.x == 0) cnt_r[s] = total;
+  if (s == 0 && threadIdx.x == 0) {
+    meta_r[0] = b0;
+    meta_r[1] = L.res[1];  // pool keys above bin b0
+  }
+  // Second level: key bits 19..8 of this slice's keys in the threshold bin.
+  uint32_t* g2 = hrow + kSelBins;
+  if (total_b0 <= kDirectHist2) {
+#pragma unroll
+    for (int e = 0; e < kFiltPer; ++e)
+      if (j0 + e < g.pe && (key[e] >> 20) == b0) atomicAdd(&g2[(key[e] >> 8) & 0xFFFu], 1u);
+  } else {
+    for (int i = threadIdx.x; i < kSelBins; i += blockDim.x) L.h2[i] = 0u;
+    __syncthreads();
+#pragma unroll
+    for (int e = 0; e < kFiltPer; ++e)
+      if (j0 + e < g.pe && (key[e] >> 20) == b0) atomicAdd(&L.h2[(key[e] >> 8) & 0xFFFu], 1u);
+    __syncthreads();
+    for (int i = threadIdx.x; i < kSelBins; i += blockDim.x)
+      if (L.h2[i] != 0u) atomicAdd(&g2[i], L.h2[i]);
+  }
+}
+
 constexpr int kMaxSlices = 1024;  // pools up to 4,194,304 keys
 constexpr int kStage = 8192;      // list entries held in LDS by the final selection
 

@@ -57,12 +57,6 @@ __global__ __launch_bounds__(256) void sel_hist(const float* __restrict__ scores
     if (h[i] != 0u) atomicAdd(&gh[i], h[i]);
 }
 
-constexpr int kPer = kSelSlice / 256;  // keys per thread in sel_filter
-
-// Above this many threshold-bin keys in a slice, the second-level histogram
-// is merged in LDS first instead of one global atomic per key.
-constexpr uint32_t kDirectHist2 = 256;
-
 template <bool kVec4>
 __global__ __launch_bounds__(256) void sel_filter(const float* __restrict__ scores, int cap,
                                                   const int32_t* __restrict__ ctx_len, int tiles,
@@ -73,77 +67,11 @@ __global__ __launch_bounds__(256) void sel_filter(const float* __restrict__ scor
                                                   uint2* __restrict__ list, int nslices) {
   const int r = blockIdx.y, s = blockIdx.x;
   const RowGeom g = row_geom(ctx_len, cap, r, tiles, n_q, tile_q, k_top, window);
-  const int s0 = s * kSelSlice;
-  if (g.kk == 0 || g.kk == g.pe || s0 >= g.pe) return;
-  // Thread t owns the 16 consecutive keys s0 + 16t .. s0 + 16t + 15; they are
-  // loaded first so that the loads overlap the threshold search.
-  const int j0 = s0 + kPer * threadIdx.x;
-  const float* row = scores + (size_t)r * cap;
-  uint32_t key[kPer];
-  if (kVec4 && j0 + kPer <= g.pe) {
-#pragma unroll
-    for (int e = 0; e < kPer; e += 4) {
-      const f32x4 v = *reinterpret_cast<const f32x4*>(row + j0 + e);
-      key[e] = order_key(v.x);
-      key[e + 1] = order_key(v.y);
-      key[e + 2] = order_key(v.z);
-      key[e + 3] = order_key(v.w);
-    }
-  } else {
-#pragma unroll
-    for (int e = 0; e < kPer; ++e) key[e] = (j0 + e < g.pe) ? order_key(row[j0 + e]) : 0u;
-  }
-  __shared__ uint32_t scratch[8];
-  __shared__ uint32_t res[2];
-  __shared__ uint32_t h2[kSelBins];
-  uint32_t* hrow = hist + (size_t)r * kHistRow;
-  static_assert(kSelBins == 16 * 256, "sixteen bins per thread");
-  uint32_t hv[16];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const u32x4 x = *reinterpret_cast<const u32x4*>(hrow + 16 * threadIdx.x + 4 * i);
-    hv[4 * i] = x.x;
-    hv[4 * i + 1] = x.y;
-    hv[4 * i + 2] = x.z;
-    hv[4 * i + 3] = x.w;
-  }
-  find_bin_regs(hv, (uint32_t)g.kk, scratch, res);
-  const uint32_t b0 = res[0];
-  uint32_t keep = 0, in_b0 = 0;
-#pragma unroll
-  for (int e = 0; e < kPer; ++e) {
-    const bool valid = j0 + e < g.pe;
-    keep += (valid && (key[e] >> 20) >= b0) ? 1u : 0u;
-    in_b0 += (valid && (key[e] >> 20) == b0) ? 1u : 0u;
-  }
-  uint32_t total, total_b0;
-  uint32_t pos = block_prefix_sum(keep, scratch, &total);
-  (void)block_prefix_sum(in_b0, scratch, &total_b0);
-  uint2* out = list + ((size_t)r * nslices + s) * kSelSlice;
-#pragma unroll
-  for (int e = 0; e < kPer; ++e)
-    if (j0 + e < g.pe && (key[e] >> 20) >= b0) out[pos++] = make_uint2(key[e], (uint32_t)(j0 + e));
-  if (threadIdx.x == 0) cnt[(size_t)r * nslices + s] = total;
-  if (s == 0 && threadIdx.x == 0) {
-    meta[4 * r] = b0;
-    meta[4 * r + 1] = res[1];  // pool keys above bin b0
-  }
-  // Second level: key bits 19..8 of this slice's keys in the threshold bin.
-  uint32_t* g2 = hrow + kSelBins;
-  if (total_b0 <= kDirectHist2) {
-#pragma unroll
-    for (int e = 0; e < kPer; ++e)
-      if (j0 + e < g.pe && (key[e] >> 20) == b0) atomicAdd(&g2[(key[e] >> 8) & 0xFFFu], 1u);
-  } else {
-    for (int i = threadIdx.x; i < kSelBins; i += blockDim.x) h2[i] = 0u;
-    __syncthreads();
-#pragma unroll
-    for (int e = 0; e < kPer; ++e)
-      if (j0 + e < g.pe && (key[e] >> 20) == b0) atomicAdd(&h2[(key[e] >> 8) & 0xFFFu], 1u);
-    __syncthreads();
-    for (int i = threadIdx.x; i < kSelBins; i += blockDim.x)
-      if (h2[i] != 0u) atomicAdd(&g2[i], h2[i]);
-  }
+  if (g.kk == 0 || g.kk == g.pe || s * kSelSlice >= g.pe) return;
+  __shared__ FilterLds lds;
+  filter_slice<kVec4, false>(scores + (size_t)r * cap, cap, g, s, hist + (size_t)r * kHistRow,
+                             cnt + (size_t)r * nslices, meta + 4 * r,
+                             list + ((size_t)r * nslices + s) * kSelSlice, lds);
 }
 
 __global__ __launch_bounds__(1024) void sel_final(const int32_t* __restrict__ ctx_len, int cap,
