@@ -38,7 +38,7 @@ GRAPH_ROUNDS = 3  # rounds over the four caches per captured HIP graph (headline
 SCORE_KERNEL = "score_onepass<false, false, 20>"
 # The sources of the headline scoring kernel: its measured traffic is used only
 # while these are unchanged.
-TRAFFIC_SOURCES = ("score_onepass.hip", "score_common.h", "hs2_internal.h", "layout.h")
+TRAFFIC_SOURCES = ("score_onepass.hip", "score_common.h", "select_core.h", "hs2_internal.h", "layout.h")
 MIB = 1 << 20
 
 
