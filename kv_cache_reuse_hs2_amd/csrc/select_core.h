@@ -452,20 +452,25 @@ __device__ int final_select_row(int r, const RowGeom& g, int k_top,
   // consecutive entries.
   uint32_t base;
   if (staged) {
+    // Only the list's chunks are visited (each wave takes chunks wave,
+    // wave + kWaves, ...); the ballots are taken again for the writes rather
+    // than kept per chunk, which would need a register array per possible
+    // chunk.
     const int nchunks = (int)((total + 63) / 64);
     uint32_t* chunk_tau = chunk_wins + kStage / 64;
-    uint64_t mask_a[kStage / 64 / kWaves], mask_t[kStage / 64 / kWaves];
-#pragma unroll
-    for (int u = 0; u < kStage / 64 / kWaves; ++u) {
-      const int ch = wave + kWaves * u;
+    auto ballots = [&](int ch, uint64_t& ma, uint64_t& mt) {
       const uint32_t e = 64u * ch + lane;
-      const uint32_t kx = (ch < nchunks && e < total) ? stage[e].x : 0u;
-      const bool valid = ch < nchunks && e < total;
-      mask_a[u] = __ballot(valid && kx > tau);
-      mask_t[u] = __ballot(valid && kx == tau);
-      if (ch < nchunks && lane == 0) {
-        chunk_wins[ch] = (uint32_t)__popcll(mask_a[u]);
-        chunk_tau[ch] = (uint32_t)__popcll(mask_t[u]);
+      const bool valid = e < total;
+      const uint32_t kx = valid ? stage[e].x : 0u;
+      ma = __ballot(valid && kx > tau);
+      mt = __ballot(valid && kx == tau);
+    };
+    for (int ch = wave; ch < nchunks; ch += kWaves) {
+      uint64_t ma, mt;
+      ballots(ch, ma, mt);
+      if (lane == 0) {
+        chunk_wins[ch] = (uint32_t)__popcll(ma);
+        chunk_tau[ch] = (uint32_t)__popcll(mt);
       }
     }
     __syncthreads();
@@ -502,14 +507,13 @@ __device__ int final_select_row(int r, const RowGeom& g, int k_top,
     __syncthreads();
     base = res_b[0] + min(res_b[1], need2);
     const uint64_t lower = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-#pragma unroll
-    for (int u = 0; u < kStage / 64 / kWaves; ++u) {
-      const int ch = wave + kWaves * u;
-      if (ch >= nchunks) break;
-      const uint32_t a_before = chunk_wins[ch] + (uint32_t)__popcll(mask_a[u] & lower);
-      const uint32_t t_before = chunk_tau[ch] + (uint32_t)__popcll(mask_t[u] & lower);
-      const bool above = (mask_a[u] >> lane) & 1ull;
-      const bool at = ((mask_t[u] >> lane) & 1ull) && t_before < need2;
+    for (int ch = wave; ch < nchunks; ch += kWaves) {
+      uint64_t ma, mt;
+      ballots(ch, ma, mt);
+      const uint32_t a_before = chunk_wins[ch] + (uint32_t)__popcll(ma & lower);
+      const uint32_t t_before = chunk_tau[ch] + (uint32_t)__popcll(mt & lower);
+      const bool above = (ma >> lane) & 1ull;
+      const bool at = ((mt >> lane) & 1ull) && t_before < need2;
       if (above || at) {
         const uint32_t pos = a_before + min(t_before, need2);
         if (pos < (uint32_t)k_top) {
