@@ -73,11 +73,11 @@ namespace {
 
 constexpr int kOpWaves = 4;
 constexpr int kOpThreads = 64 * kOpWaves;
-// 32-key tiles per wave kept in registers: the most that compile without
-// spilling (bf16 K needs more registers in flight than E4M3 K, but the
-// compiler's allocation differs between the two).
+// 32-key tiles per wave kept in registers: the most (in pairs) that compile
+// without spilling; a bf16 block needs twice the registers of an E4M3 block
+// in flight.
 constexpr int kOpRegBlocksBf16 = 20;
-constexpr int kOpRegBlocksFp8 = 16;
+constexpr int kOpRegBlocksFp8 = 22;
 constexpr int kLdsBlocks = 9;   // ... kept in LDS
 constexpr float kRefMin = -1e30f;           // reference of a lane that has seen no key
 constexpr float kRescale = 64.f;            // binades a logit may exceed its reference

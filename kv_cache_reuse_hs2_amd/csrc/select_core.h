@@ -221,9 +221,12 @@ __device__ void filter_slice(const float* __restrict__ row, int cap, const RowGe
     keep += (valid && (key[e] >> 20) >= b0) ? 1u : 0u;
     in_b0 += (valid && (key[e] >> 20) == b0) ? 1u : 0u;
   }
-  uint32_t total, total_b0;
-  uint32_t pos = block_prefix_sum(keep, L.scratch, &total);
-  (void)block_prefix_sum(in_b0, L.scratch, &total_b0);
+  // Both counts in one scan: each is at most kSelSlice = 4,096 over the
+  // block, so they share a word without carries.
+  uint32_t both;
+  const uint32_t pre2 = block_prefix_sum(keep | (in_b0 << 16), L.scratch, &both);
+  uint32_t pos = pre2 & 0xFFFFu;
+  const uint32_t total = both & 0xFFFFu, total_b0 = both >> 16;
 #pragma unroll
   for (int e = 0; e < kFiltPer; ++e)
     if (j0 + e < g.pe && (key[e] >> 20) >= b0) list_s[pos++] = make_uint2(key[e], (uint32_t)(j0 + e));

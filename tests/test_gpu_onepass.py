@@ -42,9 +42,11 @@ def _plan(batch, cap):
     return n, -(-units // n) * 256
 
 
-def _key(chunk, wg, wave, block, offset):
-    """Key index of `offset` within local block `block` of `wave` in workgroup `wg`."""
-    return wg * chunk + 32 * (block * WAVES + wave) + offset
+def _key(nwg, wg, wave, block, offset):
+    """Key index of `offset` within local block `block` of `wave` in workgroup
+    `wg` of a sequence's nwg: workgroup wg takes the 32-key blocks wg,
+    wg + nwg, wg + 2 nwg, ..., its waves in turn."""
+    return 32 * ((block * WAVES + wave) * nwg + wg) + offset
 
 
 def _plant(inp, places, size=100.0):
@@ -92,14 +94,15 @@ def _check_step(hs2, w, inp, ctx):
 
 
 def test_late_reference_move_register_tiles(hs2):
-    # 2 x 9,000 keys: 256 keys per workgroup, two blocks per wave, both kept in
-    # registers.  Key 161 is in wave 1's second block (keys 160..191), met after
-    # the wave kept its first block (32..63).
+    # 2 x 9,000 keys: 36 workgroups of 256 keys per sequence, two blocks per
+    # wave, both kept in registers.  Each planted key is in a wave's second
+    # block, met after the wave kept its first.
     w = WORKLOADS["decode_bf16_64k_b16"].replace(batch=2)
     ctx = [9000, 5000]
     nwg, chunk = _plan(2, 9000)
     assert (nwg, chunk) == (36, 256)
-    places = [(0, _key(chunk, 0, 1, 1, 1)), (1, _key(chunk, 9, 3, 1, 30))]
+    places = [(0, _key(nwg, 0, 1, 1, 1)), (1, _key(nwg, 9, 0, 1, 30))]
+    assert all(j < ctx[b] for b, j in places)
     inp = _plant(make_decode_inputs(w, ctx_lens=ctx, capacity=max(ctx)), places)
     _say(f"late move, register tiles, places={places}")
     _check_step(hs2, w, inp, ctx)
@@ -107,15 +110,16 @@ def test_late_reference_move_register_tiles(hs2):
 
 def test_late_reference_move_lds_tiles(hs2):
     # 16 x 45,056 keys: 2,816 keys per workgroup, 22 blocks per wave; blocks 0
-    # and 1 are kept in LDS, 2..21 in registers.  Planted keys in a register
-    # block (after LDS tiles were kept) and in an LDS block (after block 0).
+    # and 1 are kept in LDS, 2..21 in registers.  Planted keys in register
+    # blocks (after LDS tiles were kept) and in an LDS block (after block 0).
     w = WORKLOADS["decode_bf16_64k_b16"].replace(batch=16)
     cap = 45056
     ctx = [cap] * 15 + [30001]
     nwg, chunk = _plan(16, cap)
     assert (nwg, chunk) == (16, 2816)
-    places = [(0, _key(chunk, 3, 2, 5, 7)), (5, _key(chunk, 0, 0, 1, 0)),
-              (15, _key(chunk, 9, 1, 21, 31))]
+    places = [(0, _key(nwg, 3, 2, 5, 7)), (5, _key(nwg, 0, 0, 1, 0)),
+              (15, _key(nwg, 9, 1, 14, 31))]
+    assert all(j < ctx[b] for b, j in places)
     inp = _plant(make_decode_inputs(w, ctx_lens=ctx, capacity=cap), places)
     _say(f"late move, LDS tiles, places={places}")
     _check_step(hs2, w, inp, ctx)
@@ -123,16 +127,18 @@ def test_late_reference_move_lds_tiles(hs2):
 
 def test_late_reference_move_with_reread_blocks(hs2):
     # 4 x 262,144 keys: 4,096 keys per workgroup, 32 blocks per wave: blocks
-    # 0..2 read again, 3..11 kept in LDS, 12..31 in registers.  One planted key
-    # in a register block (late move: the wave reads all 32 blocks again), one
-    # in block 1 (a move before anything is kept: no fallback).
+    # 0..2 read again, 3..11 kept in LDS, 12..31 in registers.  Planted keys
+    # in an LDS block and in a register block (late moves: those waves read
+    # all 32 blocks again), and in block 1 (a move before anything is kept: no
+    # fallback).
     w = WORKLOADS["decode_bf16_256k_b4"]
     cap = w.ctx_len
     ctx = [cap, cap, cap - 5000, 140000]
     nwg, chunk = _plan(4, cap)
     assert (nwg, chunk) == (64, 4096)
-    places = [(0, _key(chunk, 10, 0, 10, 3)), (1, _key(chunk, 20, 3, 1, 9)),
-              (3, _key(chunk, 33, 2, 31, 0))]
+    places = [(0, _key(nwg, 10, 0, 10, 3)), (1, _key(nwg, 20, 3, 1, 9)),
+              (3, _key(nwg, 33, 0, 16, 0))]
+    assert all(j < ctx[b] for b, j in places)
     inp = _plant(make_decode_inputs(w, ctx_lens=ctx, capacity=cap), places)
     _say(f"late move with read-again blocks, places={places}")
     _check_step(hs2, w, inp, ctx)
@@ -146,7 +152,8 @@ def test_late_reference_move_fp8(hs2):
     w = WORKLOADS["decode_fp8_256k_b4"].replace(batch=2)
     ctx = [9000, 5000]
     nwg, chunk = _plan(2, 9000)
-    places = [(0, _key(chunk, 0, 1, 1, 1)), (1, _key(chunk, 9, 3, 1, 30))]
+    places = [(0, _key(nwg, 0, 1, 1, 1)), (1, _key(nwg, 9, 0, 1, 30))]
+    assert all(j < ctx[b] for b, j in places)
     base = make_decode_inputs(w.replace(dtype="bf16"), ctx_lens=ctx, capacity=max(ctx))
     planted = _plant(base, places)
     k_raw, k_scale = e4m3_codes(planted["k"])
