@@ -60,8 +60,9 @@
  *   compute unit, and those workgroups wait for one another.  So two such
  *   calls must not run at the same time on one GPU, whatever their streams
  *   or workspaces.  Waits are bounded (about 1 s), after which the scores of
- *   the sequences concerned are NaN.  Batches larger than the GPU's compute
- *   unit count take a two-pass path with no such wait.
+ *   the sequences concerned are NaN (and the decode steps' selections and
+ *   sparse outputs for them are undefined).  Batches larger than the GPU's
+ *   compute unit count take a two-pass path with no such wait.
  * - kv_capacity is at most 4,194,304 keys (HS2_EUNSUPPORTED beyond).
  */
 #ifndef HS2_H_
