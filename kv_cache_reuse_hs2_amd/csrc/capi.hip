@@ -146,10 +146,11 @@ hs2_status hs2_decode_step(const hs2_attn_desc* desc, const void* q, const void*
   const WsLayout l = ws_layout(*desc, kv_capacity);
   char* w = static_cast<char*>(ws);
   hipStream_t st = static_cast<hipStream_t>(stream);
-  // bf16 and E4M3: the scoring pass also builds the selector's histogram,
-  // and the one-pass decode kernel also runs the selector's candidate filter.
-  const bool fuse = desc->dtype != HS2_F32;
+  // The scoring pass also builds the selector's histogram (decode, and bf16
+  // or E4M3 prefill), and the one-pass decode kernel also runs the
+  // selector's candidate filter.
   const bool pf = is_prefill(*desc);
+  const bool fuse = !pf || desc->dtype != HS2_F32;
   const SelectWs sw = select_ws(*desc, kv_capacity);
   FilterArgs filt{};
   filt.cnt = reinterpret_cast<uint32_t*>(w + l.select + sw.cnt_off);
@@ -169,7 +170,7 @@ hs2_status hs2_decode_step(const hs2_attn_desc* desc, const void* q, const void*
                              : score_ws(*desc, kv_capacity).hist_off;
   uint32_t* hist = fuse ? reinterpret_cast<uint32_t*>(w + l.score + hist_off) : nullptr;
   // MFMA decode: the final selection runs inside the sparse layer's kernel.
-  const bool tail = fuse && !pf;
+  const bool tail = !pf && desc->dtype != HS2_F32;
   if (!filtered) {
     e = launch_select(*desc, scores, ctx_len, kv_capacity, top_idx, top_cnt, w + l.select, hist,
                       !tail, st);

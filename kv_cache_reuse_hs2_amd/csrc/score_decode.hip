@@ -462,7 +462,7 @@ __global__ __launch_bounds__(kF32Chunk) void score_f32(
     const float* __restrict__ q, const float* __restrict__ k, int64_t kv_stride,
     const int32_t* __restrict__ ctx_len, int cap, int H, float c2,
     float2* __restrict__ stats, int nchunks, const float* __restrict__ lse2,
-    float* __restrict__ scores, int64_t score_stride) {
+    float* __restrict__ scores, int64_t score_stride, uint32_t* __restrict__ hist, int window) {
   const int b = blockIdx.y;
   const int c = (MODE == 1) ? (gridDim.x - 1 - blockIdx.x) : blockIdx.x;
   const int N = clamp_ctx(ctx_len, b, cap);
@@ -502,6 +502,24 @@ __global__ __launch_bounds__(kF32Chunk) void score_f32(
     for (int h = 0; h < kHB; ++h)
       if (h < H) imp += fast_exp2(acc[h] * c2 - lse2[b * kMaxHeads + h]);
     scores[(size_t)b * score_stride + j] = imp;
+    // The selector's first histogram (pool keys only; cleared by
+    // score_reduce_f32 before this pass).  The wave's keys are grouped by
+    // bin first, one atomic per distinct bin: the scores crowd into few bins.
+    if (hist != nullptr) {
+      const uint32_t bin = order_key(imp) >> 20;
+      bool todo = j < N - window;
+      while (__ballot(todo) != 0ull) {  // wave-uniform
+        if (todo) {
+          const uint32_t lead = __builtin_amdgcn_readfirstlane(bin);
+          const uint64_t same = __ballot(bin == lead);
+          if (bin == lead) {
+            todo = false;
+            if ((int)(threadIdx.x & 63) == __ffsll((unsigned long long)same) - 1)
+              atomicAdd(&hist[(size_t)b * kHistRow + lead], (uint32_t)__popcll(same));
+          }
+        }
+      }
+    }
   } else {
     float2* st = stats + ((size_t)b * nchunks + c) * kMaxHeads;
 #pragma unroll
@@ -525,16 +543,19 @@ template <int MODE>
 void launch_score_f32(dim3 grid, hipStream_t st, const float* q, const float* k,
                       int64_t kv_stride, const int32_t* ctx_len, int cap, int H, float c2,
                       float2* stats, int nchunks, const float* lse2, float* scores,
-                      int64_t score_stride) {
+                      int64_t score_stride, uint32_t* hist = nullptr, int window = 0) {
   if (H <= 8)
     score_f32<MODE, 8><<<grid, kF32Chunk, 0, st>>>(q, k, kv_stride, ctx_len, cap, H, c2, stats,
-                                                   nchunks, lse2, scores, score_stride);
+                                                   nchunks, lse2, scores, score_stride, hist,
+                                                   window);
   else if (H <= 16)
     score_f32<MODE, 16><<<grid, kF32Chunk, 0, st>>>(q, k, kv_stride, ctx_len, cap, H, c2, stats,
-                                                    nchunks, lse2, scores, score_stride);
+                                                    nchunks, lse2, scores, score_stride, hist,
+                                                    window);
   else
     score_f32<MODE, 32><<<grid, kF32Chunk, 0, st>>>(q, k, kv_stride, ctx_len, cap, H, c2, stats,
-                                                    nchunks, lse2, scores, score_stride);
+                                                    nchunks, lse2, scores, score_stride, hist,
+                                                    window);
 }
 
 // fp32 path with the full layer's own output: workgroup (c, b) takes keys
@@ -614,8 +635,12 @@ __global__ __launch_bounds__(256) void score_full_f32(
 // Heads beyond H get +inf so that 2^(x - L) vanishes for them.
 __global__ __launch_bounds__(256) void score_reduce_f32(
     const float2* __restrict__ stats, int nchunks, const int32_t* __restrict__ ctx_len, int cap,
-    int H, float* __restrict__ lse2, float* __restrict__ lse_out) {
+    int H, float* __restrict__ lse2, float* __restrict__ lse_out, uint32_t* __restrict__ hist) {
   const int b = blockIdx.x;
+  // The selector histograms of this sequence (both levels) start at zero:
+  // the scores pass and the filter add to them.
+  if (hist != nullptr)
+    for (int i = threadIdx.x; i < kHistRow; i += blockDim.x) hist[(size_t)b * kHistRow + i] = 0u;
   const int N = clamp_ctx(ctx_len, b, cap);
   const int nc = (N + kF32Chunk - 1) / kF32Chunk;
   const int h = threadIdx.x & 31, part = threadIdx.x >> 5;
@@ -672,7 +697,8 @@ hipError_t launch_score_full(const hs2_attn_desc& d, const void* q, const void* 
     const auto* kf = static_cast<const float*>(k);
     launch_score_f32<0>(dim3(nchunks1, d.batch), st, qf, kf, kv_stride, ctx_len, cap, d.n_heads,
                         d.sm_scale * 1.4426950408889634f, stats, nchunks1, nullptr, nullptr, 0);
-    score_reduce_f32<<<d.batch, 256, 0, st>>>(stats, nchunks1, ctx_len, cap, d.n_heads, lse2, lse);
+    score_reduce_f32<<<d.batch, 256, 0, st>>>(stats, nchunks1, ctx_len, cap, d.n_heads, lse2, lse,
+                                              nullptr);
     score_full_f32<<<dim3(nchunks2, d.batch), 256, 0, st>>>(
         qf, kf, static_cast<const float*>(v), kv_stride, ctx_len, cap, d.n_heads,
         d.sm_scale * 1.4426950408889634f, lse2, scores, cap, o_part, nchunks2);
@@ -738,9 +764,11 @@ hipError_t launch_score_decode(const hs2_attn_desc& d, const void* q, const void
     const auto* kf = static_cast<const float*>(k);
     launch_score_f32<0>(grid, st, qf, kf, kv_stride, ctx_len, cap, d.n_heads, c2, stats,
                         nchunks1, nullptr, nullptr, 0);
-    score_reduce_f32<<<d.batch, 256, 0, st>>>(stats, nchunks1, ctx_len, cap, d.n_heads, lse2, lse);
+    uint32_t* hist = with_hist ? reinterpret_cast<uint32_t*>(ws + w.hist_off) : nullptr;
+    score_reduce_f32<<<d.batch, 256, 0, st>>>(stats, nchunks1, ctx_len, cap, d.n_heads, lse2, lse,
+                                              hist);
     launch_score_f32<1>(grid, st, qf, kf, kv_stride, ctx_len, cap, d.n_heads, c2, nullptr,
-                        nchunks1, lse2, scores, cap);
+                        nchunks1, lse2, scores, cap, hist, d.window);
   }
   return hipGetLastError();
 }

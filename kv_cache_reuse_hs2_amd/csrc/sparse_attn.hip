@@ -527,24 +527,33 @@ __global__ __launch_bounds__(kHeadDim) void sparse_combine(const float* __restri
   float den = 0.f, num = 0.f, M = -INFINITY;
   if (nseg <= kCombRegs) {
     // Every load at once (one memory round trip), then the same arithmetic
-    // as the loop below.
-    float2 x[kCombRegs];
+    // as the loop below.  The (max, sum) pairs, the same for every thread,
+    // are loaded one per thread and shared through LDS (as scalar loads they
+    // would need more scalar registers than there are).
+    __shared__ float2 s_ml[kCombRegs];
+    if (d < nseg) s_ml[d] = mlq[(size_t)d * H];
+    // Partials through one buffer resource with per-segment vector offsets
+    // (64-bit addresses per segment would also crowd the scalar registers).
+    // Past the last segment the buffer loads return zero (never used).
     float pv[kCombRegs];
+    const float* p0 = part + ((size_t)bq * nseg * H + h) * kHeadDim;  // uniform
+    const uint32_t seg_bytes = (uint32_t)(H * kHeadDim * sizeof(float));
+    const __amdgpu_buffer_rsrc_t rp = buffer_rsrc(p0, (uint32_t)nseg * seg_bytes);
+#pragma unroll
+    for (int s = 0; s < kCombRegs; ++s)
+      pv[s] = __uint_as_float(
+          __builtin_amdgcn_raw_buffer_load_b32(rp, s * seg_bytes + d * (int)sizeof(float), 0, 0));
+    __syncthreads();
+#pragma unroll
+    for (int s = 0; s < kCombRegs; ++s)
+      if (s < nseg && s_ml[s].y > 0.f) M = fmaxf(M, s_ml[s].x);
 #pragma unroll
     for (int s = 0; s < kCombRegs; ++s)
       if (s < nseg) {
-        x[s] = mlq[(size_t)s * H];
-        pv[s] = pq[(size_t)s * H * kHeadDim];
-      }
-#pragma unroll
-    for (int s = 0; s < kCombRegs; ++s)
-      if (s < nseg && x[s].y > 0.f) M = fmaxf(M, x[s].x);
-#pragma unroll
-    for (int s = 0; s < kCombRegs; ++s)
-      if (s < nseg) {
-        const bool live = x[s].y > 0.f;
-        const float w = live ? fast_exp2(x[s].x - M) : 0.f;
-        den = fmaf(w, live ? x[s].y : 0.f, den);
+        const float2 x = s_ml[s];
+        const bool live = x.y > 0.f;
+        const float w = live ? fast_exp2(x.x - M) : 0.f;
+        den = fmaf(w, live ? x.y : 0.f, den);
         num = live ? fmaf(w, pv[s], num) : num;
       }
   } else {
