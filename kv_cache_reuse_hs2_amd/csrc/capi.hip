@@ -169,7 +169,8 @@ hs2_status hs2_decode_step(const hs2_attn_desc* desc, const void* q, const void*
   const size_t hist_off = pf ? prefill_ws(*desc, kv_capacity).hist_off
                              : score_ws(*desc, kv_capacity).hist_off;
   uint32_t* hist = fuse ? reinterpret_cast<uint32_t*>(w + l.score + hist_off) : nullptr;
-  // MFMA decode: the final selection runs inside the sparse layer's kernel.
+  // MFMA decode: the final selection runs inside the sparse layer's kernel
+  // (with the fp32 segments' 256 threads it was slower than its own launch).
   const bool tail = !pf && desc->dtype != HS2_F32;
   if (!filtered) {
     e = launch_select(*desc, scores, ctx_len, kv_capacity, top_idx, top_cnt, w + l.select, hist,
