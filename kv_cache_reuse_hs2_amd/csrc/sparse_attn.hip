@@ -80,6 +80,7 @@ constexpr int kVtPitch = 40;           // bf16 per transposed V row (32 keys + p
 struct SegLds {
   uint16_t vt[kSegWaves][kHeadDim][kVtPitch];
   float s_m[kSegWaves][32], s_l[kSegWaves][32];
+  float s_sc[kSegWaves][32];  // per wave and head: 2^(wave max - workgroup max)
   float s_o[kSegWaves][32][kHeadDim + 4];
 };
 
@@ -205,6 +206,26 @@ __device__ __forceinline__ void segment_query_bf16(const bf16x8_t (&qreg)[8], in
   }
   __syncthreads();
   if (active) {
+    // This wave's rescale factors, one head per lane of the low half, read
+    // back four heads at a time (they do not depend on P V, so their LDS
+    // round trips overlap the MFMAs below).
+    if (hh == 0) {
+      float M = -INFINITY;
+#pragma unroll
+      for (int w = 0; w < kSegWaves; ++w) M = fmaxf(M, L.s_m[w][r32]);
+      const float mw = L.s_m[wave][r32];
+      L.s_sc[wave][r32] = (mw == -INFINITY) ? 0.f : fast_exp2(mw - M);
+    }
+    wave_lds_sync();
+    float sc[16];
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const float4 x = *reinterpret_cast<const float4*>(&L.s_sc[wave][8 * g + 4 * hh]);
+      sc[4 * g] = x.x;
+      sc[4 * g + 1] = x.y;
+      sc[4 * g + 2] = x.z;
+      sc[4 * g + 3] = x.w;
+    }
     // P V for this wave's 32 keys: k-step s covers the keys of registers
     // 8s..8s+7, i.e. {16s + 4hh + 0..3} and {16s + 8 + 4hh + 0..3}.
     f32x16_t o[4] = {{}, {}, {}, {}};
@@ -235,24 +256,30 @@ __device__ __forceinline__ void segment_query_bf16(const bf16x8_t (&qreg)[8], in
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int h = 8 * (r >> 2) + 4 * hh + (r & 3);
-      float M = -INFINITY;
 #pragma unroll
-      for (int w = 0; w < kSegWaves; ++w) M = fmaxf(M, L.s_m[w][h]);
-      const float mw = L.s_m[wave][h];
-      const float sc = (mw == -INFINITY) ? 0.f : fast_exp2(mw - M);
-#pragma unroll
-      for (int t = 0; t < 4; ++t) L.s_o[wave][h][32 * t + r32] = o[t][r] * sc;
+      for (int t = 0; t < 4; ++t) L.s_o[wave][h][32 * t + r32] = o[t][r] * sc[r];
     }
   }
   __syncthreads();
-  // Merge the waves in order.
-  for (int e = threadIdx.x; e < 32 * kHeadDim; e += blockDim.x) {
-    const int h = e / kHeadDim, d = e % kHeadDim;
-    if (h >= H) continue;
-    float acc_o = 0.f;
+  // Merge the waves in order, four outputs of a thread at a time so that
+  // their LDS reads are in flight together.
+  for (int e0 = threadIdx.x; e0 < 32 * kHeadDim; e0 += 4 * blockDim.x) {
+    float acc_o[4];
 #pragma unroll
-    for (int w = 0; w < kSegWaves; ++w) acc_o += L.s_o[w][h][d];
-    po[(size_t)h * kHeadDim + d] = acc_o;
+    for (int u = 0; u < 4; ++u) {
+      const int e = e0 + u * blockDim.x;
+      const int h = e / kHeadDim, d = e % kHeadDim;
+      acc_o[u] = 0.f;
+      if (e < 32 * kHeadDim)
+#pragma unroll
+        for (int w = 0; w < kSegWaves; ++w) acc_o[u] += L.s_o[w][h][d];
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int e = e0 + u * blockDim.x;
+      const int h = e / kHeadDim, d = e % kHeadDim;
+      if (e < 32 * kHeadDim && h < H) po[(size_t)h * kHeadDim + d] = acc_o[u];
+    }
   }
   if (threadIdx.x < H) {
     const int h = threadIdx.x;
