@@ -80,8 +80,8 @@ __global__ __launch_bounds__(kThreads) void blk_select(
     int tiles, int n_q, int tile_q, int k_top, int window, int block, int piece,
     int32_t* __restrict__ top_idx, int32_t* __restrict__ top_cnt) {
   __shared__ uint32_t hist[4096];
-  __shared__ uint32_t scratch[kScanWaves];
-  __shared__ uint32_t scratch2[kScanWaves];
+  __shared__ uint32_t scratch[kThreads / 64];
+  __shared__ uint32_t scratch2[kThreads / 64];
   __shared__ uint32_t res[2];
   __shared__ int32_t sel[kMaxTop];  // selected blocks, ascending
   const int r = blockIdx.x, t = threadIdx.x;

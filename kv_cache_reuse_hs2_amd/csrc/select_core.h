@@ -27,13 +27,8 @@ __device__ __forceinline__ RowGeom row_geom(const int32_t* ctx_len, int cap, int
   return w;
 }
 
-// Block scans for blocks of at most kScanWaves waves; scratch holds
-// kScanWaves words.  The per-wave totals are read back all at once (a loop
-// of dependent LDS reads would cost one round trip each).
-constexpr int kScanWaves = 16;
-
-// Inclusive suffix sum of v over the block (all threads call).  Returns the
-// sum over threads >= t.
+// Inclusive suffix sum of v over the block (all threads call; scratch holds
+// one word per wave).  Returns the sum over threads >= t.
 __device__ __forceinline__ uint32_t block_suffix_sum(uint32_t v, uint32_t* scratch) {
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6, nw = blockDim.x >> 6;
   uint32_t s = v;
@@ -45,11 +40,7 @@ __device__ __forceinline__ uint32_t block_suffix_sum(uint32_t v, uint32_t* scrat
   if (lane == 0) scratch[wave] = s;
   __syncthreads();
   uint32_t later = 0;
-#pragma unroll
-  for (int w = 0; w < kScanWaves; ++w) {
-    const uint32_t x = (w < nw) ? scratch[w] : 0u;
-    later += (w > wave) ? x : 0u;
-  }
+  for (int w = wave + 1; w < nw; ++w) later += scratch[w];
   __syncthreads();
   return s + later;
 }
@@ -66,11 +57,9 @@ __device__ __forceinline__ uint32_t block_prefix_sum(uint32_t v, uint32_t* scrat
   if (lane == 63) scratch[wave] = s;
   __syncthreads();
   uint32_t before = 0, all = 0;
-#pragma unroll
-  for (int w = 0; w < kScanWaves; ++w) {
-    const uint32_t x = (w < nw) ? scratch[w] : 0u;
-    before += (w < wave) ? x : 0u;
-    all += x;
+  for (int w = 0; w < nw; ++w) {
+    if (w < wave) before += scratch[w];
+    all += scratch[w];
   }
   __syncthreads();
   *total = all;
@@ -161,7 +150,7 @@ constexpr int kFiltPer = kSelSlice / 256;  // keys per thread
 constexpr uint32_t kDirectHist2 = 256;
 
 struct FilterLds {
-  uint32_t scratch[kScanWaves];
+  uint32_t scratch[8];
   uint32_t res[2];
   uint32_t h2[kSelBins];
 };
