@@ -372,7 +372,7 @@ __global__ __launch_bounds__(64 * kSegWaves) void sparse_layers_bf16(
 // into LDS (the first one also writes top_idx and top_cnt), then gathers its
 // segment exactly as sparse_partial_bf16 would from top_idx.
 
-constexpr int kTailThreads = 512;
+constexpr int kTailThreads = 1024;
 
 union TailLds {
   struct {
