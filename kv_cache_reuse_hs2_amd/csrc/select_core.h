@@ -309,6 +309,13 @@ __device__ int final_select_row(int r, const RowGeom& g, int k_top,
     v2[i + 3] = x2.w;
   }
   const uint32_t b0 = meta[4 * r], above0 = meta[4 * r + 1];
+  // Wave 0's slice counts, 64 per chunk, for every chunk the buffers hold
+  // (issued before the heads: the offsets scan waits for these only).
+  constexpr int kCntChunks = kMaxSlices / 64;
+  uint32_t cntv[kCntChunks];
+#pragma unroll
+  for (int c = 0; c < kCntChunks; ++c)
+    cntv[c] = (wave == 0 && 64 * c + lane < nslices) ? cnt[(size_t)r * nslices + 64 * c + lane] : 0u;
   constexpr int kHeads = 8;
   uint2 head[kHeads];
 #pragma unroll
@@ -316,12 +323,6 @@ __device__ int final_select_row(int r, const RowGeom& g, int k_top,
     const int sl = wave + kWaves * u;
     if (sl < nslices) head[u] = lr[(size_t)sl * kSelSlice + lane];
   }
-  // Wave 0's slice counts, 64 per chunk, for every chunk the buffers hold.
-  constexpr int kCntChunks = kMaxSlices / 64;
-  uint32_t cntv[kCntChunks];
-#pragma unroll
-  for (int c = 0; c < kCntChunks; ++c)
-    cntv[c] = (wave == 0 && 64 * c + lane < nslices) ? cnt[(size_t)r * nslices + 64 * c + lane] : 0u;
   if (g.kk == 0 || g.kk == g.pe) {
     for (int i = t; i < k_top; i += blockDim.x) {
       if (out != nullptr) out[i] = i < g.kk ? i : -1;
