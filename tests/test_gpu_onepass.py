@@ -214,3 +214,34 @@ def test_two_pass_path_beyond_the_compute_units(hs2):
     torch.cuda.synchronize()
     for a, b in zip(three, (buf.top_idx, buf.top_cnt, buf.o)):
         assert torch.equal(a, b)
+
+
+@pytest.mark.parametrize("extra,cap", [(0, 1500), (1, 1500), (1, 8192), (None, 1500)],
+                         ids=["two_wg_per_seq", "one_wg_per_seq", "one_wg_long", "batch_eq_cus"])
+def test_few_workgroups_per_sequence(hs2, extra, cap):
+    # Batches near the compute unit count: two workgroups per sequence, one
+    # (each workgroup then takes the whole sequence: at 8,192 keys its waves
+    # keep 29 of their 64 blocks and read the other 35 again), and exactly one
+    # sequence per compute unit.  Same bars; the single call equals the three.
+    from kv_cache_reuse_hs2_amd.torch_api import make_buffers, run_fused_step, run_step
+
+    n_cu = min(torch.cuda.get_device_properties(0).multi_processor_count, 256)
+    bsz = n_cu if extra is None else n_cu // 2 + extra
+    nwg, chunk = _plan(bsz, cap)
+    assert nwg == (2 if extra == 0 else 1) and chunk >= cap // nwg
+    w = WORKLOADS["decode_bf16_64k_b16"].replace(batch=bsz, n_heads=8)
+    rng = np.random.default_rng(1000 + bsz + cap)
+    ctx = rng.integers(1, cap + 1, size=bsz).tolist()
+    ctx[0] = cap
+    inp = make_decode_inputs(w, ctx_lens=ctx, capacity=cap)
+    _say(f"batch {bsz}, {nwg} workgroup(s) per sequence, capacity {cap}")
+    _check_step(hs2, w, inp, ctx)
+    buf = make_buffers(inp, n_heads=w.n_heads, k_top=w.k_top, window=w.window,
+                       sm_scale=w.sm_scale, dtype=w.dtype)
+    run_step(buf)
+    torch.cuda.synchronize()
+    three = [t.clone() for t in (buf.top_idx, buf.top_cnt, buf.o)]
+    run_fused_step(buf)
+    torch.cuda.synchronize()
+    for a, b in zip(three, (buf.top_idx, buf.top_cnt, buf.o)):
+        assert torch.equal(a, b)
