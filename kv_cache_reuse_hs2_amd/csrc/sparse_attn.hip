@@ -436,48 +436,45 @@ __global__ __launch_bounds__(kTailThreads) void decode_tail_bf16(
 constexpr int kSegF = kSparseSeg;     // keys per workgroup
 constexpr int kKPitch = kHeadDim + 4;  // LDS row pitch of K (bank spread)
 
-// LDS of one fp32 segment.
-struct SegF32Lds {
-  float qs[kMaxHeads][kHeadDim];
-  float ks[kSegF][kKPitch];
-  float vs[kSegF][kHeadDim];
-  float ps[kSegF][kMaxHeads];
-  int kidx[kSegF];
-};
-
-// The fp32 partial of the segment at selection position s0 of query row bq
-// (sequence b), 256 threads; key_at(p) is the key at selection position p.
-template <class KeyAt>
-__device__ void segment_partial_f32(const float* __restrict__ q, const float* __restrict__ k,
-                                    const float* __restrict__ v, int64_t kv_stride, int b, int bq,
-                                    int H, float c2, const QueryGeom& qg, int s0, int nseg,
-                                    int seg, KeyAt key_at, SegF32Lds& L,
-                                    float* __restrict__ part, float2* __restrict__ ml) {
+__global__ __launch_bounds__(256) void sparse_partial_f32(
+    const float* __restrict__ q, const float* __restrict__ k, const float* __restrict__ v,
+    int64_t kv_stride, const int32_t* __restrict__ ctx_len, int cap,
+    const int32_t* __restrict__ top_idx, const int32_t* __restrict__ top_cnt, int n_q, int tile_q,
+    int k_top, int window, int H, float c2, float* __restrict__ part, float2* __restrict__ ml,
+    int nseg) {
+  const int seg = blockIdx.x, bq = blockIdx.y;
+  const int b = bq / n_q, i = bq % n_q, g = i / tile_q, tiles = n_q / tile_q;
   const int t = threadIdx.x;
+  const QueryGeom qg = query_geom(ctx_len, top_cnt, cap, b, i, g, tiles, n_q, k_top, window);
+  const int s0 = seg * kSegF;
   float2* mlo = ml + ((size_t)bq * nseg + seg) * H;
   if (s0 >= qg.S) {
     if (t < H) mlo[t] = make_float2(-INFINITY, 0.f);
     return;
   }
   const int nk = min(kSegF, qg.S - s0);
-  if (t < kSegF) L.kidx[t] = key_at(s0 + (t < nk ? t : 0));
+  __shared__ float qs[kMaxHeads][kHeadDim];
+  __shared__ float ks[kSegF][kKPitch];
+  __shared__ float vs[kSegF][kHeadDim];
+  __shared__ float ps[kSegF][kMaxHeads];
+  __shared__ int kidx[kSegF];
+  const int32_t* top_row = top_idx + (size_t)(b * tiles + g) * k_top;
+  if (t < kSegF) kidx[t] = sel_key(qg, top_row, s0 + (t < nk ? t : 0));
   const float* qb = q + (size_t)bq * H * kHeadDim;
   for (int e = t; e < kMaxHeads * kHeadDim / 4; e += blockDim.x) {
     const int h = e / (kHeadDim / 4), c = (e % (kHeadDim / 4)) * 4;
     const float4 qv = h < H ? *reinterpret_cast<const float4*>(qb + h * kHeadDim + c)
                             : make_float4(0.f, 0.f, 0.f, 0.f);
-    *reinterpret_cast<float4*>(&L.qs[h][c]) = qv;
+    *reinterpret_cast<float4*>(&qs[h][c]) = qv;
   }
   __syncthreads();
   {
     const int row = t >> 3, c = (t & 7) * 16;
-    const size_t off = (size_t)b * kv_stride + (size_t)L.kidx[row] * kHeadDim + c;
+    const size_t off = (size_t)b * kv_stride + (size_t)kidx[row] * kHeadDim + c;
 #pragma unroll
     for (int x4 = 0; x4 < 4; ++x4) {
-      *reinterpret_cast<float4*>(&L.ks[row][c + 4 * x4]) =
-          reinterpret_cast<const float4*>(k + off)[x4];
-      *reinterpret_cast<float4*>(&L.vs[row][c + 4 * x4]) =
-          reinterpret_cast<const float4*>(v + off)[x4];
+      *reinterpret_cast<float4*>(&ks[row][c + 4 * x4]) = reinterpret_cast<const float4*>(k + off)[x4];
+      *reinterpret_cast<float4*>(&vs[row][c + 4 * x4]) = reinterpret_cast<const float4*>(v + off)[x4];
     }
   }
   __syncthreads();
@@ -485,10 +482,10 @@ __device__ void segment_partial_f32(const float* __restrict__ q, const float* __
     const int kx = t & 31, hg = t >> 5;
     float acc[4] = {0.f, 0.f, 0.f, 0.f};
     for (int d = 0; d < kHeadDim; d += 4) {
-      const float4 kv = *reinterpret_cast<const float4*>(&L.ks[kx][d]);
+      const float4 kv = *reinterpret_cast<const float4*>(&ks[kx][d]);
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
-        const float4 qv = *reinterpret_cast<const float4*>(&L.qs[hg + 8 * u][d]);
+        const float4 qv = *reinterpret_cast<const float4*>(&qs[hg + 8 * u][d]);
         acc[u] = fmaf(qv.x, kv.x, acc[u]);
         acc[u] = fmaf(qv.y, kv.y, acc[u]);
         acc[u] = fmaf(qv.z, kv.z, acc[u]);
@@ -496,16 +493,16 @@ __device__ void segment_partial_f32(const float* __restrict__ q, const float* __
       }
     }
 #pragma unroll
-    for (int u = 0; u < 4; ++u) L.ps[kx][hg + 8 * u] = (kx < nk) ? acc[u] * c2 : -INFINITY;
+    for (int u = 0; u < 4; ++u) ps[kx][hg + 8 * u] = (kx < nk) ? acc[u] * c2 : -INFINITY;
   }
   __syncthreads();
   if (t < kMaxHeads) {
     float m = -INFINITY;
-    for (int x = 0; x < nk; ++x) m = fmaxf(m, L.ps[x][t]);
+    for (int x = 0; x < nk; ++x) m = fmaxf(m, ps[x][t]);
     float l = 0.f;
     for (int x = 0; x < kSegF; ++x) {
-      const float p = (x < nk) ? fast_exp2(L.ps[x][t] - m) : 0.f;
-      L.ps[x][t] = p;
+      const float p = (x < nk) ? fast_exp2(ps[x][t] - m) : 0.f;
+      ps[x][t] = p;
       l += p;
     }
     if (t < H) mlo[t] = make_float2(m, l);
@@ -517,10 +514,10 @@ __device__ void segment_partial_f32(const float* __restrict__ q, const float* __
 #pragma unroll
     for (int u = 0; u < 16; ++u) o[u] = 0.f;
     for (int x = 0; x < nk; ++x) {
-      const float vx = L.vs[x][d];
+      const float vx = vs[x][d];
 #pragma unroll
       for (int u = 0; u < 16; u += 4) {
-        const float4 p = *reinterpret_cast<const float4*>(&L.ps[x][16 * hh + u]);
+        const float4 p = *reinterpret_cast<const float4*>(&ps[x][16 * hh + u]);
         o[u] = fmaf(p.x, vx, o[u]);
         o[u + 1] = fmaf(p.y, vx, o[u + 1]);
         o[u + 2] = fmaf(p.z, vx, o[u + 2]);
@@ -534,21 +531,6 @@ __device__ void segment_partial_f32(const float* __restrict__ q, const float* __
       if (h < H) po[(size_t)h * kHeadDim + d] = o[u];
     }
   }
-}
-
-__global__ __launch_bounds__(256) void sparse_partial_f32(
-    const float* __restrict__ q, const float* __restrict__ k, const float* __restrict__ v,
-    int64_t kv_stride, const int32_t* __restrict__ ctx_len, int cap,
-    const int32_t* __restrict__ top_idx, const int32_t* __restrict__ top_cnt, int n_q, int tile_q,
-    int k_top, int window, int H, float c2, float* __restrict__ part, float2* __restrict__ ml,
-    int nseg) {
-  const int seg = blockIdx.x, bq = blockIdx.y;
-  const int b = bq / n_q, i = bq % n_q, g = i / tile_q, tiles = n_q / tile_q;
-  const QueryGeom qg = query_geom(ctx_len, top_cnt, cap, b, i, g, tiles, n_q, k_top, window);
-  __shared__ SegF32Lds lds;
-  const int32_t* top_row = top_idx + (size_t)(b * tiles + g) * k_top;
-  segment_partial_f32(q, k, v, kv_stride, b, bq, H, c2, qg, seg * kSegF, nseg, seg,
-                      [&](int p) { return sel_key(qg, top_row, p); }, lds, part, ml);
 }
 
 // ---------------------------------------------------------------------------
