@@ -262,7 +262,7 @@ struct FinalLds {
   uint32_t* pre;         // [kMaxSlices + 1] slice offsets
   uint32_t* chunk_wins;  // [2 * kStage / 64]: per chunk, candidates above and at the threshold
   uint32_t* scratch;     // [16], 16-byte aligned
-  uint32_t* res;         // [6]: three result pairs
+  uint32_t* res;         // [6]: two result pairs, then the long-slice flag
   uint2* stage;          // [kStage] the candidate list
 };
 
@@ -334,14 +334,17 @@ __device__ int final_select_row(int r, const RowGeom& g, int k_top,
   const int ns = (g.pe + kSelSlice - 1) / kSelSlice;
   for (int i = t; i < 256; i += kThreads) h[i] = 0u;  // key bits 7..0, counted while staging
 
-  // Slice offsets: one wave scans the counts 64 at a time.
+  // Slice offsets: one wave scans the counts 64 at a time, and notes whether
+  // any slice holds more entries than its list head (res[4]).
   if (wave == 0) {
     uint32_t carry = 0;
+    bool big = false;
 #pragma unroll
     for (int ci = 0; ci < kCntChunks; ++ci) {
       const int c0 = 64 * ci;
       if (c0 >= ns) break;
       const uint32_t c = (c0 + lane >= ns) ? 0u : cntv[ci];
+      big |= __ballot(c > 64u) != 0ull;
       uint32_t incl = c;
 #pragma unroll
       for (int off = 1; off < 64; off <<= 1) {
@@ -351,7 +354,10 @@ __device__ int final_select_row(int r, const RowGeom& g, int k_top,
       if (c0 + lane < ns) pre[c0 + lane] = carry + incl - c;
       carry += __shfl(incl, 63);
     }
-    if (lane == 0) pre[ns] = carry;
+    if (lane == 0) {
+      pre[ns] = carry;
+      L.res[4] = big ? 1u : 0u;
+    }
   }
 
   // Bits 19..8 of the threshold among the keys of b0.
@@ -383,42 +389,47 @@ __device__ int final_select_row(int r, const RowGeom& g, int k_top,
   };
   if (staged) {
     // Slices wave + kWaves u (u < kHeads): their first 64 entries come from
-    // the heads loaded above, any further ones (rare) by direct loads.
+    // the heads loaded above.
 #pragma unroll
     for (int u = 0; u < kHeads; ++u) {
       const int sl = wave + kWaves * u;
       if (sl >= ns) break;
       const uint32_t n = pre[sl + 1] - pre[sl];
       if ((uint32_t)lane < n) put(pre[sl] + lane, head[u]);
-      for (uint32_t i = 64 + lane; i < n; i += 64) put(pre[sl] + i, lr[(size_t)sl * kSelSlice + i]);
     }
-    // The slices after those (pools above kHeads kWaves slices): every entry
-    // by its list position, the loads of all of a thread's entries issued
-    // before any is stored; an entry's slice is found by binary search over
-    // the slice offsets.
+    // Every other entry (those of the slices after the first kHeads kWaves,
+    // and past the 64th of any slice) by its list position, spread over all
+    // threads, the loads of all of a thread's entries issued before any is
+    // stored; an entry's slice is found by binary search over the slice
+    // offsets.  Without long slices only the later slices' entries are
+    // visited.
     constexpr int kFirst = kHeads * kWaves;
-    if (ns > kFirst) {
+    const bool big = L.res[4] != 0u;
+    if (ns > kFirst || big) {
       constexpr int kPerT = kStage / kThreads;
-      const uint32_t p0 = pre[kFirst];
+      const int s_lo = big ? 0 : kFirst;
+      const uint32_t p0 = pre[s_lo];
       uint2 e[kPerT];
+      bool mine[kPerT];
 #pragma unroll
       for (int k = 0; k < kPerT; ++k) {
         const uint32_t i = p0 + t + (uint32_t)(k * kThreads);
+        mine[k] = false;
         if (i < total) {
-          int lo = kFirst, hi = ns - 1;  // last slice with pre[s] <= i
+          int lo = s_lo, hi = ns - 1;  // last slice with pre[s] <= i
           while (lo < hi) {
             const int mid = (lo + hi + 1) >> 1;
             if (pre[mid] <= i) lo = mid;
             else hi = mid - 1;
           }
-          e[k] = lr[(size_t)lo * kSelSlice + (i - pre[lo])];
+          const uint32_t li = i - pre[lo];
+          mine[k] = lo >= kFirst || li >= 64u;  // else its head put it there
+          if (mine[k]) e[k] = lr[(size_t)lo * kSelSlice + li];
         }
       }
 #pragma unroll
-      for (int k = 0; k < kPerT; ++k) {
-        const uint32_t i = p0 + t + (uint32_t)(k * kThreads);
-        if (i < total) put(i, e[k]);
-      }
+      for (int k = 0; k < kPerT; ++k)
+        if (mine[k]) put(p0 + t + (uint32_t)(k * kThreads), e[k]);
     }
   } else {
     for (uint32_t i = t; i < total; i += blockDim.x) {
