@@ -454,53 +454,70 @@ __global__ __launch_bounds__(32 * kCombGroups) void full_out_combine(
 }
 
 // fp32 VALU kernel: MODE 0 writes per-chunk statistics, MODE 1 importance.
-// One wave, a thread per key; kHB >= H heads are computed (8, 16 or 32; the
-// rows past H are zero), each logit as one fma chain over the 128 dims in
-// order, the same chain score_full_f32 runs, so both write the same bits.
+// A workgroup takes 64 keys (one per lane) and kHB >= H heads (8, 16 or 32;
+// the rows past H are zero), kF32Heads heads per wave, so that a thread runs
+// kF32Heads fma chains rather than all kHB.  Each logit is one fma chain over
+// the 128 dims in order, the same chain score_full_f32 runs; MODE 1 adds a
+// key's head terms in head order in one thread (through LDS), so both write
+// the same importance bits.
+constexpr int kF32Heads = 4;
+
 template <int MODE, int kHB>
-__global__ __launch_bounds__(kF32Chunk) void score_f32(
+__global__ __launch_bounds__(kF32Chunk * kHB / kF32Heads) void score_f32(
     const float* __restrict__ q, const float* __restrict__ k, int64_t kv_stride,
     const int32_t* __restrict__ ctx_len, int cap, int H, float c2,
     float2* __restrict__ stats, int nchunks, const float* __restrict__ lse2,
     float* __restrict__ scores, int64_t score_stride, uint32_t* __restrict__ hist, int window) {
+  static_assert(kF32Chunk == 64 && kHB % kF32Heads == 0, "a key per lane, whole head groups");
   const int b = blockIdx.y;
   const int c = (MODE == 1) ? (gridDim.x - 1 - blockIdx.x) : blockIdx.x;
   const int N = clamp_ctx(ctx_len, b, cap);
   const int j_begin = c * kF32Chunk;
-  if (j_begin >= N) return;
+  if (j_begin >= N) return;  // workgroup-uniform
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int h0 = kF32Heads * wave;  // this wave's heads
   __shared__ float4 qs[kHB][kHeadDim / 4];
+  __shared__ float terms[kF32Chunk][kHB + 1];  // MODE 1: a key's head terms
   const float* qb = q + (size_t)b * H * kHeadDim;
   for (int e = threadIdx.x; e < kHB * kHeadDim / 4; e += blockDim.x) {
     const int h = e / (kHeadDim / 4), d4 = e % (kHeadDim / 4);
-    qs[h][d4] = h < H ? reinterpret_cast<const float4*>(qb + h * kHeadDim)[d4] : make_float4(0.f, 0.f, 0.f, 0.f);
+    qs[h][d4] = h < H ? reinterpret_cast<const float4*>(qb + h * kHeadDim)[d4]
+                      : make_float4(0.f, 0.f, 0.f, 0.f);
   }
   __syncthreads();
-  const int j = j_begin + threadIdx.x;
+  const int j = j_begin + lane;
   const bool valid = j < N;
-  const float4* kp = reinterpret_cast<const float4*>(k + (size_t)b * kv_stride + (size_t)min(j, N - 1) * kHeadDim);
-  float acc[kHB];
+  const float4* kp = reinterpret_cast<const float4*>(k + (size_t)b * kv_stride +
+                                                     (size_t)min(j, N - 1) * kHeadDim);
+  float acc[kF32Heads];
 #pragma unroll
-  for (int h = 0; h < kHB; ++h) acc[h] = 0.f;
+  for (int u = 0; u < kF32Heads; ++u) acc[u] = 0.f;
   // Unrolled so that a thread's row loads are in flight together (the fma
   // order is unchanged).
 #pragma unroll 8
   for (int d4 = 0; d4 < kHeadDim / 4; ++d4) {
     const float4 kv = kp[d4];
 #pragma unroll
-    for (int h = 0; h < kHB; ++h) {
-      const float4 qv = qs[h][d4];
-      acc[h] = fmaf(qv.x, kv.x, acc[h]);
-      acc[h] = fmaf(qv.y, kv.y, acc[h]);
-      acc[h] = fmaf(qv.z, kv.z, acc[h]);
-      acc[h] = fmaf(qv.w, kv.w, acc[h]);
+    for (int u = 0; u < kF32Heads; ++u) {
+      const float4 qv = qs[h0 + u][d4];
+      acc[u] = fmaf(qv.x, kv.x, acc[u]);
+      acc[u] = fmaf(qv.y, kv.y, acc[u]);
+      acc[u] = fmaf(qv.z, kv.z, acc[u]);
+      acc[u] = fmaf(qv.w, kv.w, acc[u]);
     }
   }
   if (MODE == 1) {
-    if (!valid) return;
+#pragma unroll
+    for (int u = 0; u < kF32Heads; ++u) {
+      const int h = h0 + u;
+      terms[lane][h] = h < H ? fast_exp2(acc[u] * c2 - lse2[b * kMaxHeads + h]) : 0.f;
+    }
+    __syncthreads();
+    if (wave != 0 || !valid) return;
     float imp = 0.f;
 #pragma unroll
     for (int h = 0; h < kHB; ++h)
-      if (h < H) imp += fast_exp2(acc[h] * c2 - lse2[b * kMaxHeads + h]);
+      if (h < H) imp += terms[lane][h];
     scores[(size_t)b * score_stride + j] = imp;
     // The selector's first histogram (pool keys only; cleared by
     // score_reduce_f32 before this pass).  The wave's keys are grouped by
@@ -514,7 +531,7 @@ __global__ __launch_bounds__(kF32Chunk) void score_f32(
           const uint64_t same = __ballot(bin == lead);
           if (bin == lead) {
             todo = false;
-            if ((int)(threadIdx.x & 63) == __ffsll((unsigned long long)same) - 1)
+            if (lane == __ffsll((unsigned long long)same) - 1)
               atomicAdd(&hist[(size_t)b * kHistRow + lead], (uint32_t)__popcll(same));
           }
         }
@@ -523,15 +540,15 @@ __global__ __launch_bounds__(kF32Chunk) void score_f32(
   } else {
     float2* st = stats + ((size_t)b * nchunks + c) * kMaxHeads;
 #pragma unroll
-    for (int h = 0; h < kHB; ++h) {
-      const float x = valid ? acc[h] * c2 : -INFINITY;
+    for (int u = 0; u < kF32Heads; ++u) {
+      const float x = valid ? acc[u] * c2 : -INFINITY;
       float m = x;
 #pragma unroll
       for (int o = 32; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o));
       float s = fast_exp2(x - (m == -INFINITY ? 0.f : m));
 #pragma unroll
       for (int o = 32; o > 0; o >>= 1) s += __shfl_xor(s, o);
-      if (threadIdx.x == 0) st[h] = make_float2(m, s);
+      if (lane == 0) st[h0 + u] = make_float2(m, s);
     }
     // Heads past the bucket: neutral statistics (never used for a real head).
     if (threadIdx.x < kMaxHeads - kHB) st[kHB + threadIdx.x] = make_float2(-INFINITY, 0.f);
@@ -544,18 +561,18 @@ void launch_score_f32(dim3 grid, hipStream_t st, const float* q, const float* k,
                       int64_t kv_stride, const int32_t* ctx_len, int cap, int H, float c2,
                       float2* stats, int nchunks, const float* lse2, float* scores,
                       int64_t score_stride, uint32_t* hist = nullptr, int window = 0) {
+  constexpr int kW = kF32Chunk / kF32Heads;  // threads per head of the bucket
   if (H <= 8)
-    score_f32<MODE, 8><<<grid, kF32Chunk, 0, st>>>(q, k, kv_stride, ctx_len, cap, H, c2, stats,
-                                                   nchunks, lse2, scores, score_stride, hist,
-                                                   window);
+    score_f32<MODE, 8><<<grid, 8 * kW, 0, st>>>(q, k, kv_stride, ctx_len, cap, H, c2, stats,
+                                               nchunks, lse2, scores, score_stride, hist, window);
   else if (H <= 16)
-    score_f32<MODE, 16><<<grid, kF32Chunk, 0, st>>>(q, k, kv_stride, ctx_len, cap, H, c2, stats,
-                                                    nchunks, lse2, scores, score_stride, hist,
-                                                    window);
+    score_f32<MODE, 16><<<grid, 16 * kW, 0, st>>>(q, k, kv_stride, ctx_len, cap, H, c2, stats,
+                                                 nchunks, lse2, scores, score_stride, hist,
+                                                 window);
   else
-    score_f32<MODE, 32><<<grid, kF32Chunk, 0, st>>>(q, k, kv_stride, ctx_len, cap, H, c2, stats,
-                                                    nchunks, lse2, scores, score_stride, hist,
-                                                    window);
+    score_f32<MODE, 32><<<grid, 32 * kW, 0, st>>>(q, k, kv_stride, ctx_len, cap, H, c2, stats,
+                                                 nchunks, lse2, scores, score_stride, hist,
+                                                 window);
 }
 
 // fp32 path with the full layer's own output: workgroup (c, b) takes keys
