@@ -477,26 +477,41 @@ __global__ __launch_bounds__(kF32Chunk * kHB / kF32Heads) void score_f32(
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int h0 = kF32Heads * wave;  // this wave's heads
   __shared__ float4 qs[kHB][kHeadDim / 4];
-  __shared__ float terms[kF32Chunk][kHB + 1];  // MODE 1: a key's head terms
+  __shared__ float4 ks[kF32Chunk][kHeadDim / 4 + 1];  // padded: a lane per row
+  __shared__ float terms[kF32Chunk][kHB + 1];         // MODE 1: a key's head terms
   const float* qb = q + (size_t)b * H * kHeadDim;
   for (int e = threadIdx.x; e < kHB * kHeadDim / 4; e += blockDim.x) {
     const int h = e / (kHeadDim / 4), d4 = e % (kHeadDim / 4);
     qs[h][d4] = h < H ? reinterpret_cast<const float4*>(qb + h * kHeadDim)[d4]
                       : make_float4(0.f, 0.f, 0.f, 0.f);
   }
+  // The chunk's K rows through LDS, every load of a thread issued at once
+  // (one round trip), 512 contiguous bytes per 32 threads.
+  {
+    constexpr int kThreads = kF32Chunk * kHB / kF32Heads;
+    constexpr int kPer = kF32Chunk * (kHeadDim / 4) / kThreads;
+    const float* kb = k + (size_t)b * kv_stride;
+    float4 x[kPer];
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+      const int e = threadIdx.x + i * kThreads, r = e / (kHeadDim / 4), d4 = e % (kHeadDim / 4);
+      x[i] = reinterpret_cast<const float4*>(kb + (size_t)min(j_begin + r, N - 1) * kHeadDim)[d4];
+    }
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+      const int e = threadIdx.x + i * kThreads;
+      ks[e / (kHeadDim / 4)][e % (kHeadDim / 4)] = x[i];
+    }
+  }
   __syncthreads();
   const int j = j_begin + lane;
   const bool valid = j < N;
-  const float4* kp = reinterpret_cast<const float4*>(k + (size_t)b * kv_stride +
-                                                     (size_t)min(j, N - 1) * kHeadDim);
   float acc[kF32Heads];
 #pragma unroll
   for (int u = 0; u < kF32Heads; ++u) acc[u] = 0.f;
-  // Unrolled so that a thread's row loads are in flight together (the fma
-  // order is unchanged).
 #pragma unroll 8
   for (int d4 = 0; d4 < kHeadDim / 4; ++d4) {
-    const float4 kv = kp[d4];
+    const float4 kv = ks[lane][d4];
 #pragma unroll
     for (int u = 0; u < kF32Heads; ++u) {
       const float4 qv = qs[h0 + u][d4];
