@@ -453,54 +453,110 @@ __global__ __launch_bounds__(32 * kCombGroups) void full_out_combine(
   }
 }
 
-// fp32 VALU kernel: MODE 0 writes per-chunk statistics, MODE 1 importance.
-// A workgroup takes 64 keys (one per lane) and kHB >= H heads (8, 16 or 32;
-// the rows past H are zero), kF32Heads heads per wave, so that a thread runs
-// kF32Heads fma chains rather than all kHB.  Each logit is one fma chain over
-// the 128 dims in order, the same chain score_full_f32 runs; MODE 1 adds a
-// key's head terms in head order in one thread (through LDS), so both write
-// the same importance bits.
+// L_h = m + log2(l) of sequence b over its nc chunk statistics, for every
+// head slot h < 32: eight interleaved parts (part p merges chunks p, p + 8,
+// ...) are merged in part order.  Any block size; threads t < 32 return L of
+// head t (others 0).  red: LDS [8][32].
+__device__ float reduce_chunk_stats(const float2* __restrict__ stats_b, int nc,
+                                    float2 (*red)[32]) {
+  for (int i = threadIdx.x; i < 8 * 32; i += blockDim.x) {
+    const int h = i & 31, part = i >> 5;
+    float m = -INFINITY, l = 0.f;
+    for (int c = part; c < nc; c += 8) {
+      const float2 s = stats_b[(size_t)c * kMaxHeads + h];
+      merge_ml(m, l, s.x, s.y);
+    }
+    red[part][h] = make_float2(m, l);
+  }
+  __syncthreads();
+  float L = 0.f;
+  if (threadIdx.x < 32) {
+    const int h = threadIdx.x;
+    float m = red[0][h].x, l = red[0][h].y;
+    for (int p = 1; p < 8; ++p) merge_ml(m, l, red[p][h].x, red[p][h].y);
+    L = (l > 0.f) ? m + log2f(l) : -INFINITY;
+  }
+  return L;
+}
+
+// fp32 VALU kernel: MODE 0 writes per-chunk statistics (and its chunk-0
+// workgroup clears the sequence's selector histograms, when given), MODE 1
+// importance: each workgroup first merges the sequence's chunk statistics
+// into L_h itself (as score_reduce_f32 does, the same bits), so no launch
+// sits between the passes; the chunk-0 workgroup also writes the full
+// layer's lse.  A workgroup takes 64 keys (one per lane) and kHB >= H heads
+// (8, 16 or 32; the rows past H are zero), kF32Heads heads per wave, so that
+// a thread runs kF32Heads fma chains rather than all kHB.  Each logit is one
+// fma chain over the 128 dims in order, the same chain score_full_f32 runs;
+// MODE 1 adds a key's head terms in head order in one thread (through LDS),
+// so both write the same importance bits.
 constexpr int kF32Heads = 4;
 
 template <int MODE, int kHB>
 __global__ __launch_bounds__(kF32Chunk * kHB / kF32Heads) void score_f32(
     const float* __restrict__ q, const float* __restrict__ k, int64_t kv_stride,
     const int32_t* __restrict__ ctx_len, int cap, int H, float c2,
-    float2* __restrict__ stats, int nchunks, const float* __restrict__ lse2,
+    float2* __restrict__ stats, int nchunks, float* __restrict__ lse_out,
     float* __restrict__ scores, int64_t score_stride, uint32_t* __restrict__ hist, int window) {
   static_assert(kF32Chunk == 64 && kHB % kF32Heads == 0, "a key per lane, whole head groups");
   const int b = blockIdx.y;
   const int c = (MODE == 1) ? (gridDim.x - 1 - blockIdx.x) : blockIdx.x;
   const int N = clamp_ctx(ctx_len, b, cap);
+  if (MODE == 0 && hist != nullptr && c == 0)
+    for (int i = threadIdx.x; i < kHistRow; i += blockDim.x) hist[(size_t)b * kHistRow + i] = 0u;
   const int j_begin = c * kF32Chunk;
-  if (j_begin >= N) return;  // workgroup-uniform
+  if (j_begin >= N) {  // workgroup-uniform
+    // An empty sequence: no statistics to merge, lse -inf.
+    if (MODE == 1 && N == 0 && c == 0 && lse_out != nullptr && threadIdx.x < H)
+      lse_out[b * H + threadIdx.x] = -INFINITY;
+    return;
+  }
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int h0 = kF32Heads * wave;  // this wave's heads
   __shared__ float4 qs[kHB][kHeadDim / 4];
   __shared__ float4 ks[kF32Chunk][kHeadDim / 4 + 1];  // padded: a lane per row
   __shared__ float terms[kF32Chunk][kHB + 1];         // MODE 1: a key's head terms
-  const float* qb = q + (size_t)b * H * kHeadDim;
-  for (int e = threadIdx.x; e < kHB * kHeadDim / 4; e += blockDim.x) {
-    const int h = e / (kHeadDim / 4), d4 = e % (kHeadDim / 4);
-    qs[h][d4] = h < H ? reinterpret_cast<const float4*>(qb + h * kHeadDim)[d4]
-                      : make_float4(0.f, 0.f, 0.f, 0.f);
-  }
-  // The chunk's K rows through LDS, every load of a thread issued at once
-  // (one round trip), 512 contiguous bytes per 32 threads.
+  __shared__ float2 red[8][32];                        // MODE 1: statistics merge
+  __shared__ float s_L[32];                            // MODE 1: L_h
+  // Q and the chunk's K rows through LDS, every load of a thread issued at
+  // once (one round trip; K 512 contiguous bytes per 32 threads), then the
+  // statistics merge, whose loads overlap those.
   {
     constexpr int kThreads = kF32Chunk * kHB / kF32Heads;
     constexpr int kPer = kF32Chunk * (kHeadDim / 4) / kThreads;
+    constexpr int kPerQ = kHB * (kHeadDim / 4) / kThreads;
     const float* kb = k + (size_t)b * kv_stride;
-    float4 x[kPer];
+    const float* qb = q + (size_t)b * H * kHeadDim;
+    float4 x[kPer], y[kPerQ];
 #pragma unroll
     for (int i = 0; i < kPer; ++i) {
       const int e = threadIdx.x + i * kThreads, r = e / (kHeadDim / 4), d4 = e % (kHeadDim / 4);
       x[i] = reinterpret_cast<const float4*>(kb + (size_t)min(j_begin + r, N - 1) * kHeadDim)[d4];
     }
 #pragma unroll
+    for (int i = 0; i < kPerQ; ++i) {
+      const int e = threadIdx.x + i * kThreads, h = e / (kHeadDim / 4), d4 = e % (kHeadDim / 4);
+      y[i] = h < H ? reinterpret_cast<const float4*>(qb + h * kHeadDim)[d4]
+                   : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+    if (MODE == 1) {
+      const float L = reduce_chunk_stats(stats + (size_t)b * nchunks * kMaxHeads,
+                                         (N + kF32Chunk - 1) / kF32Chunk, red);
+      if (threadIdx.x < 32) {
+        const int h = threadIdx.x;
+        s_L[h] = (h < H) ? L : INFINITY;  // padded heads: 2^-inf = 0
+        if (lse_out != nullptr && c == 0 && h < H) lse_out[b * H + h] = L * 0.69314718055994531f;
+      }
+    }
+#pragma unroll
     for (int i = 0; i < kPer; ++i) {
       const int e = threadIdx.x + i * kThreads;
       ks[e / (kHeadDim / 4)][e % (kHeadDim / 4)] = x[i];
+    }
+#pragma unroll
+    for (int i = 0; i < kPerQ; ++i) {
+      const int e = threadIdx.x + i * kThreads;
+      qs[e / (kHeadDim / 4)][e % (kHeadDim / 4)] = y[i];
     }
   }
   __syncthreads();
@@ -525,7 +581,7 @@ __global__ __launch_bounds__(kF32Chunk * kHB / kF32Heads) void score_f32(
 #pragma unroll
     for (int u = 0; u < kF32Heads; ++u) {
       const int h = h0 + u;
-      terms[lane][h] = h < H ? fast_exp2(acc[u] * c2 - lse2[b * kMaxHeads + h]) : 0.f;
+      terms[lane][h] = h < H ? fast_exp2(acc[u] * c2 - s_L[h]) : 0.f;
     }
     __syncthreads();
     if (wave != 0 || !valid) return;
@@ -534,8 +590,8 @@ __global__ __launch_bounds__(kF32Chunk * kHB / kF32Heads) void score_f32(
     for (int h = 0; h < kHB; ++h)
       if (h < H) imp += terms[lane][h];
     scores[(size_t)b * score_stride + j] = imp;
-    // The selector's first histogram (pool keys only; cleared by
-    // score_reduce_f32 before this pass).  The wave's keys are grouped by
+    // The selector's first histogram (pool keys only; cleared by the
+    // statistics pass).  The wave's keys are grouped by
     // bin first, one atomic per distinct bin: the scores crowd into few bins.
     if (hist != nullptr) {
       const uint32_t bin = order_key(imp) >> 20;
@@ -574,20 +630,20 @@ __global__ __launch_bounds__(kF32Chunk * kHB / kF32Heads) void score_f32(
 template <int MODE>
 void launch_score_f32(dim3 grid, hipStream_t st, const float* q, const float* k,
                       int64_t kv_stride, const int32_t* ctx_len, int cap, int H, float c2,
-                      float2* stats, int nchunks, const float* lse2, float* scores,
+                      float2* stats, int nchunks, float* lse_out, float* scores,
                       int64_t score_stride, uint32_t* hist = nullptr, int window = 0) {
   constexpr int kW = kF32Chunk / kF32Heads;  // threads per head of the bucket
   if (H <= 8)
     score_f32<MODE, 8><<<grid, 8 * kW, 0, st>>>(q, k, kv_stride, ctx_len, cap, H, c2, stats,
-                                               nchunks, lse2, scores, score_stride, hist, window);
+                                               nchunks, lse_out, scores, score_stride, hist, window);
   else if (H <= 16)
     score_f32<MODE, 16><<<grid, 16 * kW, 0, st>>>(q, k, kv_stride, ctx_len, cap, H, c2, stats,
-                                                 nchunks, lse2, scores, score_stride, hist,
-                                                 window);
+                                                 nchunks, lse_out, scores, score_stride,
+                                                 hist, window);
   else
     score_f32<MODE, 32><<<grid, 32 * kW, 0, st>>>(q, k, kv_stride, ctx_len, cap, H, c2, stats,
-                                                 nchunks, lse2, scores, score_stride, hist,
-                                                 window);
+                                                 nchunks, lse_out, scores, score_stride,
+                                                 hist, window);
 }
 
 // fp32 path with the full layer's own output: workgroup (c, b) takes keys
@@ -663,32 +719,22 @@ __global__ __launch_bounds__(256) void score_full_f32(
     if (16 * hg + i < H) dst[(size_t)(16 * hg + i) * kHeadDim] = oacc[i];
 }
 
-// fp32 path: per (sequence, head) L_h = max + log2(sum) over the chunks.
-// Heads beyond H get +inf so that 2^(x - L) vanishes for them.
+// fp32 path with the full layer's own output: per (sequence, head) L_h for
+// score_full_f32 (and the full layer's lse); heads beyond H get +inf so that
+// 2^(x - L) vanishes for them.  Also clears the sequence's selector
+// histograms (both levels), which the scores pass and the filter fill.
 __global__ __launch_bounds__(256) void score_reduce_f32(
     const float2* __restrict__ stats, int nchunks, const int32_t* __restrict__ ctx_len, int cap,
     int H, float* __restrict__ lse2, float* __restrict__ lse_out, uint32_t* __restrict__ hist) {
   const int b = blockIdx.x;
-  // The selector histograms of this sequence (both levels) start at zero:
-  // the scores pass and the filter add to them.
   if (hist != nullptr)
     for (int i = threadIdx.x; i < kHistRow; i += blockDim.x) hist[(size_t)b * kHistRow + i] = 0u;
   const int N = clamp_ctx(ctx_len, b, cap);
   const int nc = (N + kF32Chunk - 1) / kF32Chunk;
-  const int h = threadIdx.x & 31, part = threadIdx.x >> 5;
-  float m = -INFINITY, l = 0.f;
-  for (int c = part; c < nc; c += 8) {
-    const float2 s = stats[((size_t)b * nchunks + c) * kMaxHeads + h];
-    merge_ml(m, l, s.x, s.y);
-  }
   __shared__ float2 red[8][32];
-  red[part][h] = make_float2(m, l);
-  __syncthreads();
+  const float L = reduce_chunk_stats(stats + (size_t)b * nchunks * kMaxHeads, nc, red);
   if (threadIdx.x < 32) {
-    m = red[0][h].x;
-    l = red[0][h].y;
-    for (int p = 1; p < 8; ++p) merge_ml(m, l, red[p][h].x, red[p][h].y);
-    const float L = (l > 0.f) ? m + log2f(l) : -INFINITY;
+    const int h = threadIdx.x;
     lse2[b * kMaxHeads + h] = (h < H) ? L : INFINITY;
     if (lse_out != nullptr && h < H) lse_out[b * H + h] = L * 0.69314718055994531f;
   }
@@ -790,17 +836,14 @@ hipError_t launch_score_decode(const hs2_attn_desc& d, const void* q, const void
       launch_score_mfma<false>(d, q, k, kv_stride, ctx_len, cap, scores, lse, stats, nchunks1,
                                c2, hist, st);
   } else {
-    float* lse2 = reinterpret_cast<float*>(ws + w.lse2_off);
     const dim3 grid(nchunks1, d.batch);
     const auto* qf = static_cast<const float*>(q);
     const auto* kf = static_cast<const float*>(k);
-    launch_score_f32<0>(grid, st, qf, kf, kv_stride, ctx_len, cap, d.n_heads, c2, stats,
-                        nchunks1, nullptr, nullptr, 0);
     uint32_t* hist = with_hist ? reinterpret_cast<uint32_t*>(ws + w.hist_off) : nullptr;
-    score_reduce_f32<<<d.batch, 256, 0, st>>>(stats, nchunks1, ctx_len, cap, d.n_heads, lse2, lse,
-                                              hist);
-    launch_score_f32<1>(grid, st, qf, kf, kv_stride, ctx_len, cap, d.n_heads, c2, nullptr,
-                        nchunks1, lse2, scores, cap, hist, d.window);
+    launch_score_f32<0>(grid, st, qf, kf, kv_stride, ctx_len, cap, d.n_heads, c2, stats,
+                        nchunks1, nullptr, nullptr, 0, hist);
+    launch_score_f32<1>(grid, st, qf, kf, kv_stride, ctx_len, cap, d.n_heads, c2, stats,
+                        nchunks1, lse, scores, cap, hist, d.window);
   }
   return hipGetLastError();
 }
