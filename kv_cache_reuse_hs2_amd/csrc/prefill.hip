@@ -770,23 +770,88 @@ __global__ __launch_bounds__(64 * kSpWaves) void pf_sparse(PfArgs a) {
 
   __shared__ __attribute__((aligned(16))) uint8_t kblk[kBlk * kRowB];
   __shared__ __attribute__((aligned(16))) uint16_t vt[kHeadDim][kVtP];
-  __shared__ int s_key[kBlk];
+  // The list's keys, all read at once (one round trip for both passes).
+  __shared__ int s_keys[(kMaxTop + kMaxWindow + kSpWaves + kBlk - 1) / kBlk * kBlk];
   bf16x8_t qr[8];
   load_q(a.q + ((size_t)b * a.n_q + i) * a.H * kHeadDim, a.H, r32, hh, P >= 0, qr);
+  for (int p = threadIdx.x; p < total; p += blockDim.x) s_keys[p] = key_of(p);
+  __syncthreads();  // every thread's gathers read keys that other threads wrote
   const void* kb = kFp8 ? static_cast<const void*>(reinterpret_cast<const uint8_t*>(a.k) +
                                                    (size_t)b * a.kv_stride)
                         : static_cast<const void*>(a.k + (size_t)b * a.kv_stride);
   const uint16_t* vb = a.v + (size_t)b * a.kv_stride;
   const uint8_t* vb8 = reinterpret_cast<const uint8_t*>(a.v) + (size_t)b * a.kv_stride;
 
+  // K (and in pass B V) rows of list block bi go through registers two blocks
+  // ahead: block bi + 2 is loaded while block bi is in the MFMAs, so a
+  // block's gather latency overlaps the work of the two before it.
+  constexpr int kT = 64 * kSpWaves;
+  constexpr int kPieces = kBlk * (kFp8 ? 8 : 16) / kT;  // 16-byte pieces per thread
+  static_assert(kPieces >= 1 && kBlk * (kFp8 ? 8 : 16) % kT == 0, "whole pieces");
+  const int nblk = (total + kBlk - 1) / kBlk;
+  auto key_at = [&](int bi, int r) { return s_keys[min(bi * kBlk + r, total - 1)]; };
+  auto load_rows = [&](const void* base, int bi, u32x4 (&x)[kPieces]) {
+#pragma unroll
+    for (int it = 0; it < kPieces; ++it) {
+      const int e = threadIdx.x + it * kT;
+      if constexpr (kFp8) {
+        const int r = e >> 3, c = e & 7;
+        x[it] = *reinterpret_cast<const u32x4*>(static_cast<const uint8_t*>(base) +
+                                                (size_t)key_at(bi, r) * kHeadDim + 16 * c);
+      } else {
+        const int r = e >> 4, c = e & 15;
+        x[it] = *reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(base) +
+                                                (size_t)key_at(bi, r) * kHeadDim + 8 * c);
+      }
+    }
+  };
+  auto store_k = [&](const u32x4 (&x)[kPieces]) {
+#pragma unroll
+    for (int it = 0; it < kPieces; ++it) {
+      const int e = threadIdx.x + it * kT;
+      if constexpr (kFp8) {
+        const int r = e >> 3, c = e & 7;
+        *reinterpret_cast<u32x4*>(kblk + r * kRowB + 32 * c) = e4m3x8_to_bf16x8(x[it][0], x[it][1]);
+        *reinterpret_cast<u32x4*>(kblk + r * kRowB + 32 * c + 16) =
+            e4m3x8_to_bf16x8(x[it][2], x[it][3]);
+      } else {
+        const int r = e >> 4, c = e & 15;
+        *reinterpret_cast<u32x4*>(kblk + r * kRowB + 16 * c) = x[it];
+      }
+    }
+  };
+  // V block transposed: vt[d][key] (E4M3 rows widened to bf16).
+  auto store_v = [&](const u32x4 (&y)[kPieces]) {
+#pragma unroll
+    for (int it = 0; it < kPieces; ++it) {
+      const int e = threadIdx.x + it * kT;
+      if constexpr (kFp8) {
+        const int r = e >> 3, c = e & 7;
+        const u32x4 xs[2] = {e4m3x8_to_bf16x8(y[it][0], y[it][1]),
+                             e4m3x8_to_bf16x8(y[it][2], y[it][3])};
+#pragma unroll
+        for (int hf = 0; hf < 2; ++hf)
+#pragma unroll
+          for (int u = 0; u < 4; ++u) {
+            vt[16 * c + 8 * hf + 2 * u][r] = (uint16_t)(xs[hf][u] & 0xFFFFu);
+            vt[16 * c + 8 * hf + 2 * u + 1][r] = (uint16_t)(xs[hf][u] >> 16);
+          }
+      } else {
+        const int r = e >> 4, c = e & 15;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          vt[8 * c + 2 * u][r] = (uint16_t)(y[it][u] & 0xFFFFu);
+          vt[8 * c + 2 * u + 1][r] = (uint16_t)(y[it][u] >> 16);
+        }
+      }
+    }
+  };
+
   // Pass A: row statistics over the list.
   float m = -INFINITY, l = 0.f;
-  for (int p0 = 0; p0 < total; p0 += kBlk) {
-    __syncthreads();
-    if (threadIdx.x < kBlk) s_key[threadIdx.x] = key_of(min(p0 + (int)threadIdx.x, total - 1));
-    __syncthreads();
-    stage_k<kFp8>(kblk, kb, [&](int r) { return s_key[r]; });
-    __syncthreads();
+  auto pass_a = [&](int bi) {
+    const int p0 = bi * kBlk;
+    const int* s_key = s_keys + p0;
 #pragma unroll
     for (int mt = 0; mt < 2; ++mt) {
       f32x16_t acc = {};
@@ -809,43 +874,34 @@ __global__ __launch_bounds__(64 * kSpWaves) void pf_sparse(PfArgs a) {
       l = sum;
       m = mn;
     }
+  };
+  {
+    u32x4 k0[kPieces], k1[kPieces];
+    if (nblk > 0) load_rows(kb, 0, k0);
+    if (nblk > 1) load_rows(kb, 1, k1);
+    for (int bi = 0; bi < nblk; bi += 2) {
+      __syncthreads();
+      store_k(k0);
+      if (bi + 2 < nblk) load_rows(kb, bi + 2, k0);
+      __syncthreads();
+      pass_a(bi);
+      if (bi + 1 >= nblk) break;
+      __syncthreads();
+      store_k(k1);
+      if (bi + 3 < nblk) load_rows(kb, bi + 3, k1);
+      __syncthreads();
+      pass_a(bi + 1);
+    }
   }
   merge_ml(m, l, __shfl_xor(m, 32), __shfl_xor(l, 32));
   const float Lrow = (l > 0.f) ? m + log2f(l) : INFINITY;  // this lane's row (head r32)
 
   // Pass B: O = sum_j 2^(x - L) v_j.
   f32x16_t o[4] = {{}, {}, {}, {}};
-  for (int p0 = 0; p0 < total; p0 += kBlk) {
-    __syncthreads();
-    if (threadIdx.x < kBlk) s_key[threadIdx.x] = key_of(min(p0 + (int)threadIdx.x, total - 1));
-    __syncthreads();
-    stage_k<kFp8>(kblk, kb, [&](int r) { return s_key[r]; });
-    // V block transposed: vt[d][key] (E4M3 rows widened to bf16).
-    if constexpr (kFp8) {
-      for (int e = threadIdx.x; e < kBlk * 8; e += blockDim.x) {
-        const int r = e >> 3, c = e & 7;
-        const u32x4 x8 = *reinterpret_cast<const u32x4*>(vb8 + (size_t)s_key[r] * kHeadDim + 16 * c);
-        const u32x4 xs[2] = {e4m3x8_to_bf16x8(x8[0], x8[1]), e4m3x8_to_bf16x8(x8[2], x8[3])};
-#pragma unroll
-        for (int hf = 0; hf < 2; ++hf)
-#pragma unroll
-          for (int u = 0; u < 4; ++u) {
-            vt[16 * c + 8 * hf + 2 * u][r] = (uint16_t)(xs[hf][u] & 0xFFFFu);
-            vt[16 * c + 8 * hf + 2 * u + 1][r] = (uint16_t)(xs[hf][u] >> 16);
-          }
-      }
-    } else {
-      for (int e = threadIdx.x; e < kBlk * 16; e += blockDim.x) {
-        const int r = e >> 4, c = e & 15;
-        const u32x4 x = *reinterpret_cast<const u32x4*>(vb + (size_t)s_key[r] * kHeadDim + 8 * c);
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          vt[8 * c + 2 * u][r] = (uint16_t)(x[u] & 0xFFFFu);
-          vt[8 * c + 2 * u + 1][r] = (uint16_t)(x[u] >> 16);
-        }
-      }
-    }
-    __syncthreads();
+  const void* vsrc = kFp8 ? static_cast<const void*>(vb8) : static_cast<const void*>(vb);
+  auto pass_b = [&](int bi) {
+    const int p0 = bi * kBlk;
+    const int* s_key = s_keys + p0;
 #pragma unroll
     for (int mt = 0; mt < 2; ++mt) {
       f32x16_t acc = {};
@@ -881,6 +937,38 @@ __global__ __launch_bounds__(64 * kSpWaves) void pf_sparse(PfArgs a) {
           o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(lo), as_bf16x8(bv), o[dt], 0, 0, 0);
         }
       }
+    }
+  };
+  {
+    u32x4 k0[kPieces], k1[kPieces], v0[kPieces], v1[kPieces];
+    if (nblk > 0) {
+      load_rows(kb, 0, k0);
+      load_rows(vsrc, 0, v0);
+    }
+    if (nblk > 1) {
+      load_rows(kb, 1, k1);
+      load_rows(vsrc, 1, v1);
+    }
+    for (int bi = 0; bi < nblk; bi += 2) {
+      __syncthreads();
+      store_k(k0);
+      store_v(v0);
+      if (bi + 2 < nblk) {
+        load_rows(kb, bi + 2, k0);
+        load_rows(vsrc, bi + 2, v0);
+      }
+      __syncthreads();
+      pass_b(bi);
+      if (bi + 1 >= nblk) break;
+      __syncthreads();
+      store_k(k1);
+      store_v(v1);
+      if (bi + 3 < nblk) {
+        load_rows(kb, bi + 3, k1);
+        load_rows(vsrc, bi + 3, v1);
+      }
+      __syncthreads();
+      pass_b(bi + 1);
     }
   }
   // o[dt][r]: row head 8(r/4) + 4hh + r%4, dim 32dt + r32 (already normalised;
