@@ -408,7 +408,7 @@ def extra_measurements(steps: int, warmup: int) -> dict:
         "attention_TFLOPs": round(att_flop / (ms_f * 1e-3) / 1e12, 1),
         "o_full_pass_TFLOPs": round(att_flop / ((ms_f - ms_s) * 1e-3) / 1e12, 1),
         "note": "attention FLOPs count the causal QK^T and P.V once each; the output pass "
-                "recomputes QK^T and multiplies P as a bf16 high and low part"}
+                "recomputes QK^T and multiplies P rounded to bf16"}
     del buf, inp, o_full
     # The same prefill on an E4M3 K/V cache (one scale per cache).
     w8 = WORKLOADS["prefill_fp8_128k_8k"]

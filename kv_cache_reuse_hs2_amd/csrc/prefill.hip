@@ -536,8 +536,9 @@ __global__ __launch_bounds__(64 * kPfWaves) void pf_colsum(PfArgs a) {
 // the block's barrier the workgroup transposes V into vt (wave w: dims
 // 16w .. 16w + 15, lane: key) and a second barrier publishes it.  K is the
 // A operand, so a lane holds one head over 16 keys, which is the B layout of
-// P^T: O^T += V^T P^T with p as a bf16 high and low part (residual below
-// 2^-17 of p).
+// P^T: O^T += V^T P^T with p rounded to bf16 (nearest, ties to even), the
+// MFMA's operand type: each term's relative error is at most 2^-8, so an
+// output moves by at most 2^-8 of sum_j p_j |v_j| beyond the fp32 error.
 constexpr int kOutWaves = 8;
 
 template <bool kFp8>
@@ -648,7 +649,7 @@ __global__ __launch_bounds__(512) void pf_out(PfArgs a, float* __restrict__ o_fu
         // that key's vt column is 32mt + 16sp + 8hh + jj.
 #pragma unroll
         for (int sp = 0; sp < 2; ++sp) {
-          u32x4 phi, plo;
+          u32x4 pb;
 #pragma unroll
           for (int jj = 0; jj < 4; ++jj) {
             float pp[2];
@@ -658,19 +659,13 @@ __global__ __launch_bounds__(512) void pf_out(PfArgs a, float* __restrict__ o_fu
               const int j = kb0 + 32 * mt + 8 * (r >> 2) + 4 * hh + (r & 3);
               pp[u] = (j <= P) ? fast_exp2(fmaf(acc[r], a.c2, -Lh)) : 0.f;
             }
-            const uint16_t h0 = f32_to_bf16_rne(pp[0]), h1 = f32_to_bf16_rne(pp[1]);
-            const uint16_t l0 = f32_to_bf16_rne(pp[0] - bf16_to_f32(h0));
-            const uint16_t l1 = f32_to_bf16_rne(pp[1] - bf16_to_f32(h1));
-            phi[jj] = (uint32_t)h0 | ((uint32_t)h1 << 16);
-            plo[jj] = (uint32_t)l0 | ((uint32_t)l1 << 16);
+            pb[jj] = (uint32_t)f32_to_bf16_rne(pp[0]) | ((uint32_t)f32_to_bf16_rne(pp[1]) << 16);
           }
 #pragma unroll
           for (int t = 0; t < 4; ++t) {
             const u32x4 av =
                 *reinterpret_cast<const u32x4*>(&sm.vt[32 * t + r32][32 * mt + 16 * sp + 8 * hh]);
-            o[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(av), as_bf16x8(phi), o[t],
-                                                           0, 0, 0);
-            o[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(av), as_bf16x8(plo), o[t],
+            o[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(av), as_bf16x8(pb), o[t],
                                                            0, 0, 0);
           }
         }

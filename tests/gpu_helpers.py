@@ -76,3 +76,17 @@ def assert_selection_near_ties(top_gpu, cnt_gpu, top_or, cnt_or, scores_or, ctx_
                 assert np.all(np.abs(imp[diff] - tau) <= 1e-4 * tau), "selection differs beyond near-ties"
                 swaps += diff.size // 2
     return swaps
+
+
+def assert_prefill_out_close(got, o_ref, o_abs, vmax, what):
+    """Prefill o_full against the oracle: 1e-4 * max|v| for the fp32 work plus
+    2^-8 * sum_j p_j |v_j| for p's bf16 rounding, per output; and the bf16
+    path's bar (max abs 2e-2, relative L2 5e-3)."""
+    err = np.abs(got - o_ref)
+    bound = 1e-4 * vmax + 2.0 ** -8 * o_abs
+    worst = float(np.max(err / bound))
+    assert worst <= 1.0, f"{what}: o_full error {worst:.3f} of its bound (max abs {err.max():.3e})"
+    assert err.max() <= 2e-2, f"{what}: o_full max abs {err.max():.3e}"
+    rel = float(np.linalg.norm(got - o_ref) / max(np.linalg.norm(o_ref), 1e-30))
+    assert rel <= 5e-3, f"{what}: o_full relative L2 {rel:.3e}"
+    print(f"[gpu] {what}: max abs {err.max():.3e}, {100 * worst:.1f}% of the bound, rel L2 {rel:.2e}", flush=True)

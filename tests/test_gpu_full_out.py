@@ -7,11 +7,16 @@ sum_j p_hj v_j per 4,096-key chunk; the chunk partials are added in order.
 Prefill: a third pass over K and V, exactly normalised with the first pass's
 statistics, one workgroup per 8 queries over all their keys.
 
-Bar: scores as without o_full (relative 1e-4); o_full max |gpu - oracle| <=
-1e-4 * max|v|.  Both sides use the same stored bf16 (or E4M3-widened) values;
-p enters the MFMA as a bf16 high part plus a bf16 low part (residual below
-2^-17 relative), logits and sums are fp32, so the error is some 1e-5 of the
-largest |v|, a tenth of the bar.
+Bar: scores as without o_full (relative 1e-4).  Decode: o_full max
+|gpu - oracle| <= 1e-4 * max|v|.  Both sides use the same stored bf16 (or
+E4M3-widened) values; in decode p enters the MFMA as a bf16 high part plus a
+bf16 low part (residual below 2^-17 relative), logits and sums are fp32, so
+the error is some 1e-5 of the largest |v|, a tenth of the bar.  Prefill: the
+output pass is bound by the matrix cores, and p enters its P.V MFMA rounded
+once to bf16 (relative error at most 2^-8 per term), so each output may move
+by 2^-8 * sum_j p_j |v_j| more; that sum is the oracle's output for |v|.  The
+prefill outputs must also meet the bf16 path's bar: max abs error 2e-2 and
+relative L2 error 5e-3.
 """
 
 import sys
@@ -21,7 +26,7 @@ import pytest
 import torch
 
 import oracle
-from gpu_helpers import assert_scores_close
+from gpu_helpers import assert_prefill_out_close, assert_scores_close
 from workloads import WORKLOADS, make_decode_inputs, make_prefill_inputs
 
 pytestmark = pytest.mark.gpu
@@ -42,6 +47,7 @@ def _check(buf, o_full, inp, w):
     vmax = max(np.abs(inp["v"]).max(), 1e-30)
     err = np.abs(got - want)
     assert err.max() <= 1e-4 * vmax, f"o_full max abs {err.max():.3e} (max|v| {vmax:.3e})"
+
 
 
 CASES = [
@@ -175,11 +181,12 @@ def test_prefill_full_output_matches_oracle(hs2, name, bsz, heads, ctx, cap, n_q
     assert torch.equal(buf.lse_full, plain_lse)
     ref, o_ref, lse = oracle.full_attn_scores(inp["q"], inp["k"], inp["ctx_len"], tile_q=tile_q,
                                               sm_scale=w.sm_scale, v=inp["v"])
+    _, o_abs, _ = oracle.full_attn_scores(inp["q"], inp["k"], inp["ctx_len"], tile_q=tile_q,
+                                          sm_scale=w.sm_scale, v=np.abs(inp["v"]))
     assert_scores_close(buf.scores.cpu().numpy(), ref, inp["ctx_len"])
     got = o_full.cpu().numpy().astype(np.float64)
     vmax = max(np.abs(inp["v"]).max(), 1e-30)
-    err = np.abs(got - o_ref)
-    assert err.max() <= 1e-4 * vmax, f"o_full max abs {err.max():.3e} (max|v| {vmax:.3e})"
+    assert_prefill_out_close(got, o_ref, o_abs, vmax, name)
     # queries before the cache start see no key: output exactly 0
     dead = ~np.isfinite(lse)
     assert np.all(got[dead] == 0.0)
@@ -211,6 +218,8 @@ def test_prefill_full_output_full_size_sampled(hs2):
         _, o_ref, _ = oracle.full_attn_scores(inp["q"][:, q0:q0 + 16], inp["k"][:, :ctx_t[0]],
                                               ctx_t, tile_q=16, sm_scale=w.sm_scale,
                                               v=inp["v"][:, :ctx_t[0]])
-        err = np.abs(got_all[:, q0:q0 + 16].astype(np.float64) - o_ref)
-        assert err.max() <= 1e-4 * vmax, f"block {blk}: max abs {err.max():.3e}"
-        _say(f"block {blk} ok")
+        _, o_abs, _ = oracle.full_attn_scores(inp["q"][:, q0:q0 + 16], inp["k"][:, :ctx_t[0]],
+                                              ctx_t, tile_q=16, sm_scale=w.sm_scale,
+                                              v=np.abs(inp["v"][:, :ctx_t[0]]))
+        assert_prefill_out_close(got_all[:, q0:q0 + 16].astype(np.float64), o_ref, o_abs, vmax,
+                           f"block {blk}")
