@@ -32,6 +32,8 @@
 //   pf_sparse: 8 queries per workgroup; gathered keys (the tile's selection,
 //              then the window band of the block), a statistics pass then a P.V pass on MFMA with V
 //              transposed through LDS; exact normalisation, no rescaling.
+#include <type_traits>
+
 #include "hs2_internal.h"
 
 namespace hs2 {
@@ -39,6 +41,7 @@ namespace {
 
 typedef __bf16 bf16x8_t __attribute__((__vector_size__(8 * sizeof(__bf16))));
 typedef float f32x16_t __attribute__((__vector_size__(16 * sizeof(float))));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
 
 __device__ __forceinline__ bf16x8_t as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8_t, v); }
 
@@ -636,40 +639,51 @@ __global__ __launch_bounds__(512) void pf_out(PfArgs a, float* __restrict__ o_fu
       asm volatile("" ::: "memory");
       __builtin_amdgcn_sched_barrier(0);
       const int kb0 = bi * kBlk;
+      // Blocks wholly inside the wave's causal range skip the mask.
+      auto block = [&](auto masked) {
+        constexpr bool kMasked = decltype(masked)::value;
 #pragma unroll
-      for (int mt = 0; mt < 2; ++mt) {
-        f32x16_t acc = {};
+        for (int mt = 0; mt < 2; ++mt) {
+          f32x16_t acc = {};
 #pragma unroll
-        for (int e = 0; e < 8; ++e)
-          acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k_opnd_ring(ks, 32 * mt + r32, e, hh),
-                                                        qr[e], acc, 0, 0, 0);
-        // acc[r]: head r32, key kb0 + 32mt + 8(r/4) + 4hh + r%4.  The MFMA
-        // k index 8hh + jj of step sp stands for the lane's p[8sp + jj], key
-        // 32mt + 16sp + 8(jj/4) + 4hh + jj%4, in A (V^T) and B (P^T) alike;
-        // that key's vt column is 32mt + 16sp + 8hh + jj.
+          for (int e = 0; e < 8; ++e)
+            acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k_opnd_ring(ks, 32 * mt + r32, e, hh),
+                                                          qr[e], acc, 0, 0, 0);
+          // acc[r]: head r32, key kb0 + 32mt + 8(r/4) + 4hh + r%4.  The MFMA
+          // k index 8hh + jj of step sp stands for the lane's p[8sp + jj], key
+          // 32mt + 16sp + 8(jj/4) + 4hh + jj%4, in A (V^T) and B (P^T) alike;
+          // that key's vt column is 32mt + 16sp + 8hh + jj.
 #pragma unroll
-        for (int sp = 0; sp < 2; ++sp) {
-          u32x4 pb;
+          for (int sp = 0; sp < 2; ++sp) {
+            u32x4 pb;
 #pragma unroll
-          for (int jj = 0; jj < 4; ++jj) {
-            float pp[2];
+            for (int jj = 0; jj < 4; ++jj) {
+              float pp[2];
 #pragma unroll
-            for (int u = 0; u < 2; ++u) {
-              const int r = 8 * sp + 2 * jj + u;
-              const int j = kb0 + 32 * mt + 8 * (r >> 2) + 4 * hh + (r & 3);
-              pp[u] = (j <= P) ? fast_exp2(fmaf(acc[r], a.c2, -Lh)) : 0.f;
+              for (int u = 0; u < 2; ++u) {
+                const int r = 8 * sp + 2 * jj + u;
+                const int j = kb0 + 32 * mt + 8 * (r >> 2) + 4 * hh + (r & 3);
+                const float e = fast_exp2(fmaf(acc[r], a.c2, -Lh));
+                pp[u] = (!kMasked || j <= P) ? e : 0.f;
+              }
+              // v_cvt_pk_bf16_f32: both to bf16, nearest, ties to even.
+              pb[jj] = __builtin_bit_cast(
+                  uint32_t, __builtin_convertvector((f32x2_t){pp[0], pp[1]}, bf16x2_t));
             }
-            pb[jj] = (uint32_t)f32_to_bf16_rne(pp[0]) | ((uint32_t)f32_to_bf16_rne(pp[1]) << 16);
-          }
 #pragma unroll
-          for (int t = 0; t < 4; ++t) {
-            const u32x4 av =
-                *reinterpret_cast<const u32x4*>(&sm.vt[32 * t + r32][32 * mt + 16 * sp + 8 * hh]);
-            o[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(av), as_bf16x8(pb), o[t],
-                                                           0, 0, 0);
+            for (int t = 0; t < 4; ++t) {
+              const u32x4 av =
+                  *reinterpret_cast<const u32x4*>(&sm.vt[32 * t + r32][32 * mt + 16 * sp + 8 * hh]);
+              o[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(av), as_bf16x8(pb), o[t],
+                                                             0, 0, 0);
+            }
           }
         }
-      }
+      };
+      if (kb0 + kBlk - 1 <= P)
+        block(std::false_type{});
+      else
+        block(std::true_type{});
     }
   }
   // Queries before the cache start and padded heads have p = 0, so O = 0.
