@@ -417,13 +417,17 @@ def extra_measurements(steps: int, warmup: int) -> dict:
                        sm_scale=w8.sm_scale, dtype="fp8", n_q=w8.n_q, tile_q=w8.tile_q)
     ms8 = time_events(lambda: run_fused_step(buf), max(2, steps // 10), 2)
     ms8_s = time_events(lambda: run_scores(buf), max(2, steps // 10), 2)
+    o_full = torch.empty((1, w8.n_q, w8.n_heads, w8.head_dim), dtype=torch.float32, device="cuda")
+    ms8_f = time_events(lambda: run_scores_full(buf, o_full), max(2, steps // 10), 2)
     out[w8.name] = {"ms_per_step": round(ms8, 4), "queries_per_s": round(w8.n_q / (ms8 * 1e-3), 1),
                     "scores_ms": round(ms8_s, 4),
+                    "scores_and_o_full_ms": round(ms8_f, 4),
+                    "o_full_pass_ms": round(ms8_f - ms8_s, 4),
                     "achieved_TFLOPs": round(alg / (ms8 * 1e-3) / 1e12, 1),
                     "mfma_bf16_frac": round(alg / (ms8 * 1e-3) / 2.5e15, 4),
                     "note": "K and V as E4M3 bytes with one fp32 scale each, widened to bf16 "
                             "(exact) on the way into LDS; same FLOP count as the bf16 prefill"}
-    del buf, inp
+    del buf, inp, o_full
     # KV Bridging of 1,048,576 x 2048 hidden states, then decode over the cache.
     w = WORKLOADS["bridge_decode_bf16_1m"]
     g = torch.Generator(device="cuda").manual_seed(w.seed)
